@@ -1,0 +1,468 @@
+"""Plain CPU oracle of HTTM's head-wise temporal token-merged global attention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this module.  It shares no
+code with the HIP path (``token_merged_global_amd``) and never serves as a
+fallback for it.
+
+It is written from "HTTM: Head-wise Temporal Token Merging for Faster VGGT"
+(papernotes.org summary, sections "key design 1-3", "overall framework",
+"training strategy / settings") and the merge formula and index-cache
+description of "LiteVGGT: Boosting Vanilla VGGT via Geometry-aware Cached Token
+Merging" (papernotes.org summary, "key design 3").  Each function cites the
+passage it follows.  Where the pages leave a step open the reading taken is
+stated next to the code and collected in the design notes as R1..R30.
+
+Precision.  Steps whose floating-point result decides an integer (the cosine
+argmax, the top-r order, the deviation that picks outliers) run in fp32, the
+precision the kernels take those decisions in.  Means are fp32 sums taken in
+ascending original token index followed by one fp32 division; deviations are
+fp32 sums of squares taken in ascending channel order followed by a correctly
+rounded square root.  Attention runs in fp64 (it decides nothing).
+
+Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
+(hand example with closed forms, exact attention limits against
+``torch.nn.functional.scaled_dot_product_attention``, brute force on tiny
+blocks, invariants).  Absolute layer outputs at the VGGT-shaped sizes are
+pinned only through those properties ("parity unpinned" for the absolute
+values; see the test module's header).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+EPS_NORM = 1e-12  # R10: F.normalize convention for zero rows
+
+
+# --------------------------------------------------------------------------
+# Parameters and the token map
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class Params:
+    """Layer parameters (HTTM page, "training strategy / settings")."""
+
+    heads: int
+    d_head: int
+    frames: int
+    grid_h: int
+    grid_w: int
+    n_special: int
+    n_s: int
+    n_t: int
+    q_ratio: float
+    kv_ratio: float
+    outlier_pct: float
+    q_dst_stride: int = 0
+    kv_dst_stride: int = 0
+    block_order: int = 0  # 0 frame-major (R3), 1 frame-minor
+    softmax_scale: float = 0.0  # 0 -> 1/sqrt(d_head) (R21)
+
+    @property
+    def tokens_per_frame(self) -> int:
+        return self.n_special + self.grid_h * self.grid_w
+
+    @property
+    def n_tokens(self) -> int:
+        return self.frames * self.tokens_per_frame
+
+    @property
+    def scale(self) -> float:
+        return self.softmax_scale if self.softmax_scale > 0 else 1.0 / math.sqrt(self.d_head)
+
+    @staticmethod
+    def from_workload(w) -> "Params":
+        return Params(heads=w.heads, d_head=w.d_head, frames=w.frames, grid_h=w.grid_h,
+                      grid_w=w.grid_w, n_special=w.n_special, n_s=w.n_s, n_t=w.n_t,
+                      q_ratio=w.q_ratio, kv_ratio=w.kv_ratio, outlier_pct=w.outlier_pct,
+                      q_dst_stride=w.q_dst_stride, kv_dst_stride=w.kv_dst_stride,
+                      softmax_scale=w.softmax_scale)
+
+
+def dst_stride(ratio: float, given: int = 0) -> int:
+    """Destination stride s (R8).
+
+    The configs ask for "dst every 4th" and also a 90 % query merge, which one
+    bipartite round cannot give with a quarter of the tokens as destinations.
+    Reading: s = max(4, ceil(1/(1-ratio) - 1e-9)), so every fourth token stays
+    a destination wherever that is feasible and the 90 % setting gives the
+    page's 20 % final query length (HTTM page, settings).
+    """
+    if given > 0:
+        return int(given)
+    return max(4, int(math.ceil(1.0 / (1.0 - ratio) - 1e-9)))
+
+
+def is_special(p: Params) -> np.ndarray:
+    """Token n = f*T + t is special iff t < n_special (R6)."""
+    t = np.arange(p.n_tokens) % p.tokens_per_frame
+    return t < p.n_special
+
+
+# --------------------------------------------------------------------------
+# Step 1: temporal reordering into spatio-temporal blocks
+# --------------------------------------------------------------------------
+@dataclass
+class Block:
+    g: int  # temporal group
+    a: int  # spatial run
+    f0: int
+    nf: int
+    j0: int
+    run: int
+    tokens: np.ndarray  # original token ids in block order
+
+    @property
+    def n(self) -> int:
+        return len(self.tokens)
+
+
+def blocks(p: Params) -> List[Block]:
+    """Spatio-temporal merge blocks (HTTM page, key design 2).
+
+    Tokens of the same spatial region (a run of n_s raster-order patches, R4)
+    in n_t adjacent frames (R5: the last group may be shorter) are stacked into
+    one block of n_b = n_s * n_t tokens.  Inside a block the stack is
+    frame-major (R3); blocks are ordered by temporal group, then spatial run.
+    Special tokens are not reordered (R6).
+    """
+    HW = p.grid_h * p.grid_w
+    T = p.tokens_per_frame
+    A = -(-HW // p.n_s)
+    G = -(-p.frames // p.n_t)
+    out = []
+    for g in range(G):
+        f0 = g * p.n_t
+        nf = min(p.n_t, p.frames - f0)
+        for a in range(A):
+            j0 = a * p.n_s
+            run = min(p.n_s, HW - j0)
+            f = np.arange(f0, f0 + nf)
+            j = np.arange(j0, j0 + run)
+            if p.block_order == 0:
+                tok = (f[:, None] * T + p.n_special + j[None, :]).reshape(-1)
+            else:
+                tok = (f[None, :] * T + p.n_special + j[:, None]).reshape(-1)
+            out.append(Block(g, a, f0, nf, j0, run, tok.astype(np.int64)))
+    return out
+
+
+def reorder_permutation(p: Params) -> np.ndarray:
+    """pi: reordered position -> original token id, over the patch tokens."""
+    return np.concatenate([b.tokens for b in blocks(p)])
+
+
+# --------------------------------------------------------------------------
+# Steps 2-3: per-head block matching and top-r selection
+# --------------------------------------------------------------------------
+def row_normalize(x: np.ndarray) -> np.ndarray:
+    """RowNorm (HTTM page, key design 1), fp32, zero rows map to zero (R10)."""
+    x = x.astype(np.float32)
+    nrm = np.sqrt(np.sum(x * x, axis=1, dtype=np.float32)).astype(np.float32)
+    return (x / np.maximum(nrm, np.float32(EPS_NORM))[:, None]).astype(np.float32)
+
+
+def match_block(xb: np.ndarray, s: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """Bipartite cosine matching inside one block (HTTM page, key design 1).
+
+    Block positions i with i mod s == 0 are destinations D, the rest sources S
+    (R7, R8).  Sim = RowNorm(S) . RowNorm(D)^T; every source keeps only its
+    most similar destination, ties to the smaller destination position (R11).
+    Returns (dst positions, src positions, matched dst position per src,
+    score per src).
+    """
+    n = xb.shape[0]
+    pos = np.arange(n)
+    dpos = pos[pos % s == 0]
+    spos = pos[pos % s != 0]
+    if len(spos) == 0:
+        return dpos, spos, np.zeros(0, np.int64), np.zeros(0, np.float32)
+    sim = (row_normalize(xb[spos]) @ row_normalize(xb[dpos]).T).astype(np.float32)
+    j = np.argmax(sim, axis=1)  # first maximum = smallest dst position
+    score = sim[np.arange(len(spos)), j] + np.float32(0.0)  # canonical +0
+    return dpos, spos, dpos[j], score.astype(np.float32)
+
+
+def merge_count(ratio: float, n: int, n_src: int) -> int:
+    """r = min(|S|, floor(ratio * n + 1e-9)) in binary64 (R2, R9)."""
+    return min(n_src, int(math.floor(ratio * n + 1e-9)))
+
+
+def select_top_r(score: np.ndarray, spos: np.ndarray, r: int) -> np.ndarray:
+    """Boolean mask of the r sources with the highest score (HTTM page, key design 1).
+
+    Ties go to the smaller source position (R11).
+    """
+    order = np.lexsort((spos, -score.astype(np.float64)))
+    sel = np.zeros(len(spos), dtype=bool)
+    sel[order[:r]] = True
+    return sel
+
+
+@dataclass
+class StreamMatch:
+    """Per-head matching result of one stream (q or k) over all blocks."""
+
+    rep: np.ndarray  # [N] canonical group id = smallest original id in the group
+    match_dst: np.ndarray  # [N] original id of the matched dst for sources, -1 otherwise
+    score: np.ndarray  # [N] score for sources, nan otherwise
+    selected: np.ndarray  # [N] bool, source chosen among the top-r
+    is_src: np.ndarray  # [N] bool
+
+
+def match_stream(x: np.ndarray, p: Params, ratio: float, stride: int) -> StreamMatch:
+    """Steps 2-4 for one head and one stream: match, select, group.
+
+    Groups are {d} u {selected s : m(s) = d} for each destination d, plus one
+    singleton per unselected source and per special token (HTTM page, key
+    design 1; R6, R12).
+    """
+    N = p.n_tokens
+    s = dst_stride(ratio, stride)
+    rep = np.arange(N, dtype=np.int64)
+    mdst = np.full(N, -1, dtype=np.int64)
+    score = np.full(N, np.nan, dtype=np.float32)
+    selected = np.zeros(N, dtype=bool)
+    is_src = np.zeros(N, dtype=bool)
+    for b in blocks(p):
+        tok = b.tokens
+        dpos, spos, mpos, sc = match_block(x[tok], s)
+        r = merge_count(ratio, b.n, len(spos))
+        sel = select_top_r(sc, spos, r)
+        src_tok = tok[spos]
+        dst_of_src = tok[mpos]
+        is_src[src_tok] = True
+        mdst[src_tok] = dst_of_src
+        score[src_tok] = sc
+        selected[src_tok] = sel
+        # group id: the smallest original id among the dst and its selected sources
+        g = tok.copy()  # default: own id
+        g[spos[sel]] = dst_of_src[sel]  # temporarily label by dst id
+        lab = g  # label per block position: dst id for dst and selected src
+        # canonical representative = min original id over members of each label
+        labs, inv = np.unique(lab, return_inverse=True)
+        mins = np.full(len(labs), np.iinfo(np.int64).max, dtype=np.int64)
+        np.minimum.at(mins, inv, tok)
+        rep[tok] = mins[inv]
+    return StreamMatch(rep=rep, match_dst=mdst, score=score, selected=selected, is_src=is_src)
+
+
+# --------------------------------------------------------------------------
+# Partitions and means
+# --------------------------------------------------------------------------
+@dataclass
+class Partition:
+    """Groups of one head: reps (sorted), start offsets, members (ascending ids)."""
+
+    reps: np.ndarray
+    starts: np.ndarray  # len(reps) + 1
+    members: np.ndarray  # original ids, grouped by rep, ascending inside a group
+    group_of: np.ndarray  # [N] index into reps
+
+    @property
+    def sizes(self) -> np.ndarray:
+        return np.diff(self.starts)
+
+
+def partition(rep: np.ndarray) -> Partition:
+    n = np.arange(len(rep))
+    order = np.lexsort((n, rep))
+    r_sorted = rep[order]
+    brk = np.flatnonzero(np.r_[True, r_sorted[1:] != r_sorted[:-1]])
+    starts = np.r_[brk, len(rep)]
+    reps = r_sorted[brk]
+    gid_sorted = np.repeat(np.arange(len(reps)), np.diff(starts))
+    group_of = np.empty(len(rep), dtype=np.int64)
+    group_of[order] = gid_sorted
+    return Partition(reps=reps, starts=starts, members=order.astype(np.int64), group_of=group_of)
+
+
+def group_means(x: np.ndarray, part: Partition) -> np.ndarray:
+    """Mean of each group's members (HTTM page, key design 1; LiteVGGT page, key design 3).
+
+    x_d_up = (x_d + sum_{s in S_d} x_s) / (1 + |S_d|): fp32 sum in ascending
+    original id (R13), then one fp32 division by the member count.
+    """
+    G = len(part.reps)
+    sizes = part.sizes
+    acc = np.zeros((G, x.shape[1]), dtype=np.float32)
+    for rank in range(int(sizes.max()) if G else 0):
+        gs = np.flatnonzero(sizes > rank)
+        acc[gs] = (acc[gs] + x[part.members[part.starts[gs] + rank]]).astype(np.float32)
+    return (acc / sizes.astype(np.float32)[:, None]).astype(np.float32)
+
+
+def deviation(q: np.ndarray, part: Partition, means: np.ndarray) -> np.ndarray:
+    """L2 distance of every query to the mean of its group (HTTM page, key design 3).
+
+    Every member of a group has a deviation, its destination included (R14);
+    unmerged tokens come out exactly 0.  fp32: differences, squares and a
+    running sum over channels in ascending order, then a correctly rounded sqrt.
+    """
+    diff = (q - means[part.group_of]).astype(np.float32)
+    sq = (diff * diff).astype(np.float32)
+    acc = np.zeros(q.shape[0], dtype=np.float32)
+    for c in range(q.shape[1]):
+        acc = (acc + sq[:, c]).astype(np.float32)
+    return np.sqrt(acc).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Step 5: cross-head adaptive outlier filter
+# --------------------------------------------------------------------------
+def outlier_budget(p: Params) -> int:
+    """k_o = floor(p * h * N / 100 + 1e-9), N counting special tokens (R15, R16)."""
+    return int(math.floor(p.outlier_pct * p.heads * p.n_tokens / 100.0 + 1e-9))
+
+
+def select_outliers(delta: np.ndarray, k_o: int) -> np.ndarray:
+    """Global top-k_o deviations over all heads and tokens (HTTM page, key design 3).
+
+    Returns the mask M_o [h][N].  Ties go to the smaller flat index h*N + n (R17).
+    """
+    h, N = delta.shape
+    flat = delta.reshape(-1).astype(np.float32)
+    order = np.lexsort((np.arange(h * N), -flat.astype(np.float64)))
+    m = np.zeros(h * N, dtype=bool)
+    m[order[:k_o]] = True
+    return m.reshape(h, N)
+
+
+def restore_partition(q_rep: np.ndarray, outlier: np.ndarray) -> np.ndarray:
+    """Final query partition after the outlier filter (HTTM page, key design 3).
+
+    Each outlier leaves its group and becomes an independent token; a group
+    keeps its remaining members; a group left empty disappears.  The group id
+    stays the smallest remaining original id.
+    """
+    N = len(q_rep)
+    n = np.arange(N)
+    key = np.where(outlier, N + n, q_rep)  # outliers: own label, disjoint from group labels
+    # recanonicalise the remaining groups to their smallest remaining member
+    labs, inv = np.unique(key, return_inverse=True)
+    mins = np.full(len(labs), np.iinfo(np.int64).max, dtype=np.int64)
+    np.minimum.at(mins, inv, n)
+    return mins[inv]
+
+
+# --------------------------------------------------------------------------
+# Step 6: attention on the shortened sequences, step 7: unmerge
+# --------------------------------------------------------------------------
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+              chunk: int = 2048) -> np.ndarray:
+    """O = softmax(scale * Q K^T) V in fp64 with max subtraction (R20, R21)."""
+    q64 = q.astype(np.float64)
+    k64 = k.astype(np.float64)
+    v64 = v.astype(np.float64)
+    out = np.empty((q.shape[0], v.shape[1]), dtype=np.float64)
+    for i in range(0, q.shape[0], chunk):
+        s = (q64[i:i + chunk] @ k64.T) * scale
+        s -= s.max(axis=1, keepdims=True)
+        e = np.exp(s)
+        out[i:i + chunk] = (e @ v64) / e.sum(axis=1, keepdims=True)
+    return out
+
+
+def unmerge(o: np.ndarray, part: Partition) -> np.ndarray:
+    """Copy each merged output row back to every member, at its original index.
+
+    Unmerge inside the blocks and the inverse reorder compose to this one map
+    (HTTM page, key design 1 and 2; LiteVGGT page, key design 3; R30).
+    """
+    return o[part.group_of]
+
+
+# --------------------------------------------------------------------------
+# The whole layer
+# --------------------------------------------------------------------------
+@dataclass
+class HeadIndex:
+    q_match: StreamMatch
+    k_match: StreamMatch
+
+
+@dataclass
+class Trace:
+    """Every intermediate of a layer, for staged comparison."""
+
+    q_match: List[StreamMatch] = field(default_factory=list)
+    k_match: List[StreamMatch] = field(default_factory=list)
+    delta: Optional[np.ndarray] = None  # [h][N]
+    outlier: Optional[np.ndarray] = None  # [h][N]
+    q_final_rep: List[np.ndarray] = field(default_factory=list)
+    k_rep: List[np.ndarray] = field(default_factory=list)
+    out: Optional[np.ndarray] = None
+
+
+def match_heads(q: np.ndarray, k: np.ndarray, p: Params, heads: Sequence[int]) -> Trace:
+    """Steps 1-4 for every listed head (head-wise merging, HTTM page, key design 1)."""
+    tr = Trace()
+    for i in range(len(heads)):
+        tr.q_match.append(match_stream(q[i], p, p.q_ratio, p.q_dst_stride))
+        tr.k_match.append(match_stream(k[i], p, p.kv_ratio, p.kv_dst_stride))
+        tr.k_rep.append(tr.k_match[-1].rep)
+    return tr
+
+
+def deviations(q: np.ndarray, q_reps: Sequence[np.ndarray]) -> np.ndarray:
+    """delta [h][N] from the initial query partitions (step 5a)."""
+    out = np.empty((len(q_reps), q.shape[1]), dtype=np.float32)
+    for i, rep in enumerate(q_reps):
+        part = partition(rep)
+        out[i] = deviation(q[i], part, group_means(q[i], part))
+    return out
+
+
+def head_output(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_final_rep: np.ndarray,
+                k_rep: np.ndarray, scale: float, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Steps 6-7 for one head: means, attention, unmerge.
+
+    ``rows`` restricts the output to those original token ids (the attention
+    of one output row needs only its own query slot), for large layers.
+    """
+    qp = partition(q_final_rep)
+    kp = partition(k_rep)
+    qt = group_means(q, qp)
+    kt = group_means(k, kp)
+    vt = group_means(v, kp)
+    if rows is None:
+        return unmerge(attention(qt, kt, vt, scale), qp)
+    slots = qp.group_of[rows]
+    return attention(qt[slots], kt, vt, scale)
+
+
+def layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, p: Params,
+          out_heads: Optional[Sequence[int]] = None, rows: Optional[np.ndarray] = None) -> Trace:
+    """One HTTM global-attention layer (HTTM page, overall framework).
+
+    q, k, v: [h][N][d] fp32 (bf16 inputs upcast exactly).  Steps 1-5 run on
+    every head because the outlier budget is shared across heads; steps 6-7
+    run for ``out_heads`` (default all) and, if given, only for ``rows``.
+    """
+    h = q.shape[0]
+    tr = match_heads(q, k, p, list(range(h)))
+    tr.delta = deviations(q, [m.rep for m in tr.q_match])
+    tr.outlier = select_outliers(tr.delta, outlier_budget(p))
+    tr.q_final_rep = [restore_partition(tr.q_match[i].rep, tr.outlier[i]) for i in range(h)]
+    hs = list(range(h)) if out_heads is None else list(out_heads)
+    outs = [head_output(q[i], k[i], v[i], tr.q_final_rep[i], tr.k_rep[i], p.scale, rows) for i in hs]
+    tr.out = np.stack(outs)
+    return tr
+
+
+def layer_cached(q: np.ndarray, k: np.ndarray, v: np.ndarray, p: Params,
+                 q_final_rep: Sequence[np.ndarray], k_rep: Sequence[np.ndarray],
+                 out_heads: Optional[Sequence[int]] = None,
+                 rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """A layer that reuses earlier merge indices (LiteVGGT page, key design 3; R22).
+
+    The reordering, the final query partition (outliers already restored) and
+    the key partition come from the layer that computed them; only the means
+    are recomputed from this layer's q, k, v.
+    """
+    hs = list(range(q.shape[0])) if out_heads is None else list(out_heads)
+    return np.stack([head_output(q[i], k[i], v[i], q_final_rep[i], k_rep[i], p.scale, rows)
+                     for i in hs])
