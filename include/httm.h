@@ -1,0 +1,207 @@
+/*
+ * httm.h -- C ABI of an MI355X (gfx950) implementation of HTTM's head-wise
+ * temporal token-merged global-attention layer.
+ *
+ * What the layer computes ("HTTM: Head-wise Temporal Token Merging for Faster
+ * VGGT", papernotes.org summary, "overall framework" and key designs 1-3):
+ *
+ *   1. temporal reordering: the patch tokens of one spatial region (n_s
+ *      raster-order patches) in n_t adjacent frames form one merge block of
+ *      n_b = n_s * n_t tokens (key design 2);
+ *   2. per head and per stream (Q, then K), inside each block: cosine
+ *      similarity of every source token to every destination token
+ *      (RowNorm(S) RowNorm(D)^T), best destination per source, the r sources
+ *      with the highest similarity merge into their destination, a merged
+ *      token is the mean of its members; V follows K's groups (key design 1);
+ *   3. queries only: L2 deviation of every query to its merged token, a single
+ *      top-d% over all heads and tokens picks outliers, whose contribution is
+ *      subtracted from their merged token and which are restored as separate
+ *      tokens (key design 3);
+ *   4. attention of the shortened, per-head ragged Q~ over K~ / V~;
+ *   5. unmerge: each output row is copied back to every token it stands for,
+ *      at its original index (key designs 1 and 2).
+ *
+ * The cached mode reuses the merge indices of an earlier layer ("LiteVGGT:
+ * Boosting Vanilla VGGT via Geometry-aware Cached Token Merging",
+ * papernotes.org summary, key design 3): only the means are recomputed.
+ *
+ * Conventions
+ *   - q, k, v, out: device memory, contiguous [heads][N][64], N =
+ *     frames * (n_special + grid_h * grid_w), token n = f*T + t with the first
+ *     n_special slots of each frame special (never merged).  Element type is
+ *     params.dtype (fp32 or bf16); out has the same type.  16-byte aligned.
+ *   - Ownership: the caller owns every device buffer (inputs, output,
+ *     workspace, index).  The library never allocates or frees device memory.
+ *     Plans are host objects owned by the caller; they are immutable and may
+ *     be shared between threads.
+ *   - Asynchrony: httm_layer, httm_layer_cached and httm_attention_dense only
+ *     enqueue kernels on `stream` (a hipStream_t; NULL = the default stream)
+ *     and never synchronise.  Arguments are validated on the host before any
+ *     launch; on an error nothing is enqueued and no output is written.  A
+ *     launch failure returns HTTM_ERR_DEVICE; asynchronous device faults
+ *     surface at the caller's next synchronisation.
+ *   - Calls that share a workspace or index buffer must be ordered on one
+ *     stream; concurrent calls need separate buffers.
+ *   - Sizes: validation requires heads * N < 2^31 and n_s * n_t <= 4096.
+ */
+#ifndef HTTM_H_
+#define HTTM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HTTM_OK = 0,
+  HTTM_ERR_INVALID_ARG = 1,    /* out-of-range parameter or NULL pointer */
+  HTTM_ERR_UNSUPPORTED = 2,    /* d_head != 64, block larger than 4096, block_order != 0 on the GPU */
+  HTTM_ERR_WORKSPACE = 3,      /* workspace or index buffer smaller than required */
+  HTTM_ERR_INDEX_MISMATCH = 4, /* index made by another plan, or never filled */
+  HTTM_ERR_DEVICE = 5          /* a HIP call or a kernel launch failed */
+} httm_status;
+
+typedef enum { HTTM_F32 = 0, HTTM_BF16 = 1 } httm_dtype;
+
+/* Layer parameters.  Ratios are binary64 so that r = floor(ratio * n) and
+ * k_o = floor(d * h * N / 100) round exactly as written (0.9f would give
+ * floor(0.9f * 3840) = 3455).  The HTTM page's settings are n_s = 128, n_t = 30, query
+ * merge 90 % with 10 % outliers, key/value merge 70 % (HTTM page, "training
+ * strategy / settings"). */
+typedef struct {
+  int32_t heads;         /* h >= 1 */
+  int32_t d_head;        /* must be 64 */
+  int32_t frames;        /* F >= 1 */
+  int32_t grid_h, grid_w;/* patch grid per frame */
+  int32_t n_special;     /* leading special tokens per frame (never merged) */
+  int32_t n_s;           /* spatial run: consecutive raster-order patches per block */
+  int32_t n_t;           /* temporal group: adjacent frames per block; last group may be shorter */
+  double q_ratio;        /* fraction of each block's queries merged away, [0, 1) */
+  double kv_ratio;       /* fraction of each block's keys merged away, [0, 1) */
+  double outlier_pct;    /* d in [0, 100]: percent of heads*N queries restored */
+  int32_t q_dst_stride;  /* destination stride for Q; 0 = max(4, ceil(1/(1-q_ratio))) */
+  int32_t kv_dst_stride; /* destination stride for K; 0 = max(4, ceil(1/(1-kv_ratio))) */
+  int32_t block_order;   /* 0 = frame-major stacking inside a block (only value supported) */
+  float softmax_scale;   /* 0 = 1/sqrt(d_head) */
+  int32_t dtype;         /* httm_dtype of q, k, v, out */
+} httm_params;
+
+typedef struct httm_plan httm_plan;
+
+/* Cached merge indices (LiteVGGT page, key design 3).  `dev` points to
+ * caller-owned device memory of httm_index_size() bytes.  httm_layer fills it
+ * when given and sets plan_id and valid; httm_layer_cached checks both on the
+ * host. */
+typedef struct {
+  uint64_t plan_id;
+  void* dev;
+  size_t bytes;
+  int32_t valid;
+} httm_index;
+
+/* Sizes that follow from the parameters alone (host-side, no device calls). */
+typedef struct {
+  int64_t n_tokens;      /* N */
+  int64_t n_patch;       /* F * grid_h * grid_w */
+  int32_t n_blocks;
+  int32_t q_stride, kv_stride;
+  int64_t q_groups;      /* G_q: query groups per head before outlier restore, specials included */
+  int64_t kv_len;        /* L_k: merged keys per head, specials included */
+  int64_t n_outliers;    /* k_o = floor(d * heads * N / 100) */
+  int64_t q_capacity;    /* heads * G_q + k_o: upper bound of the packed Q~ rows */
+  int64_t q_src, kv_src; /* source tokens per head (Q stream, K stream) */
+  float softmax_scale;   /* resolved scale */
+} httm_plan_info;
+
+/* Per-block row of the host block table (temporal reordering, HTTM page key
+ * design 2).  Blocks are ordered by temporal group, then spatial run; a
+ * block's tokens occupy reordered positions [start, start + n). */
+typedef struct {
+  int32_t start, n;
+  int32_t f0, nf;        /* frames f0 .. f0+nf-1 */
+  int32_t j0, run;       /* patches j0 .. j0+run-1 of each frame */
+  int32_t q_dst, q_src, q_r;   /* destinations, sources, merged sources (Q) */
+  int32_t kv_dst, kv_src, kv_r;
+  int32_t q_slot0, kv_slot0;   /* first merged slot of this block in its head */
+  int32_t q_src0, kv_src0;     /* first source of this block in its head */
+} httm_block;
+
+/* Validate `params` and build a plan.  Host only; never touches the device.
+ * Returns HTTM_ERR_INVALID_ARG / HTTM_ERR_UNSUPPORTED on bad parameters. */
+httm_status httm_plan_create(const httm_params* params, httm_plan** out);
+void httm_plan_destroy(httm_plan* plan);
+httm_status httm_plan_get_info(const httm_plan* plan, httm_plan_info* info);
+/* Copies min(n_blocks, cap) rows into `rows` (host memory). */
+httm_status httm_plan_get_blocks(const httm_plan* plan, httm_block* rows, int32_t cap);
+
+/* Device bytes the caller must provide as workspace / index buffer. */
+httm_status httm_workspace_size(const httm_plan* plan, size_t* bytes);
+httm_status httm_index_size(const httm_plan* plan, size_t* bytes);
+
+/* One full HTTM layer: q, k, v -> out.  `index` may be NULL; if given, the
+ * merge indices of this layer are written to index->dev for later
+ * httm_layer_cached calls. */
+httm_status httm_layer(const httm_plan* plan, void* ws, size_t ws_bytes,
+                       const void* q, const void* k, const void* v, void* out,
+                       httm_index* index, void* stream);
+
+/* A layer that reuses the reordering, final query partition and key
+ * partition held in `index` (LiteVGGT page, key design 3): means of this
+ * layer's q, k, v over the cached groups, attention, unmerge. */
+httm_status httm_layer_cached(const httm_plan* plan, void* ws, size_t ws_bytes,
+                              const httm_index* index,
+                              const void* q, const void* k, const void* v, void* out,
+                              void* stream);
+
+/* Exact softmax(scale q k^T) v per head with nothing merged, on the same
+ * attention kernel (the unmerged baseline).  Needs
+ * httm_dense_workspace_size() bytes of workspace. */
+httm_status httm_dense_workspace_size(const httm_plan* plan, size_t* bytes);
+httm_status httm_attention_dense(const httm_plan* plan, void* ws, size_t ws_bytes,
+                                 const void* q, const void* k, const void* v, void* out,
+                                 void* stream);
+
+/* Intermediates of the last httm_layer on `ws`, for staged comparison with
+ * an independent implementation.  Synchronises `stream` and copies to host
+ * memory.  Layouts (per head h, all int32 unless noted):
+ *   HTTM_DBG_Q_MATCH / KV_MATCH: [h][src] matched destination as an original
+ *       token id (sources ordered by block, then block position);
+ *   HTTM_DBG_Q_SCORE / KV_SCORE: [h][src] float cosine of that match;
+ *   HTTM_DBG_Q_GROUP / KV_GROUP: [h][N] merged slot of every token before
+ *       outlier restore (query) / final (key);
+ *   HTTM_DBG_DELTA: [h][N] float deviation;
+ *   HTTM_DBG_OUTLIER: [h][N] uint8 outlier mask;
+ *   HTTM_DBG_Q_SLOT: [h][N] packed row of Q~ that token n reads at unmerge;
+ *   HTTM_DBG_CU_Q: [h+1] prefix of per-head Q~ lengths;
+ *   HTTM_DBG_SELECT: [4] uint32 {threshold bits, count above, ties taken, k_o}. */
+typedef enum {
+  HTTM_DBG_Q_MATCH = 0, HTTM_DBG_Q_SCORE, HTTM_DBG_KV_MATCH, HTTM_DBG_KV_SCORE,
+  HTTM_DBG_Q_GROUP, HTTM_DBG_KV_GROUP, HTTM_DBG_DELTA, HTTM_DBG_OUTLIER,
+  HTTM_DBG_Q_SLOT, HTTM_DBG_CU_Q, HTTM_DBG_SELECT, HTTM_DBG_COUNT
+} httm_debug_item;
+httm_status httm_debug_size(const httm_plan* plan, int32_t item, size_t* bytes);
+httm_status httm_debug_read(const httm_plan* plan, const void* ws, int32_t item,
+                            void* host, size_t bytes, void* stream);
+
+/* Launch timing of the last httm_layer / httm_layer_cached / dense call made
+ * with timing enabled: per kernel stage, milliseconds between HIP events
+ * recorded on the call's stream around that stage.  httm_set_timing(1)
+ * creates the events (host side; costs a little launch latency);
+ * httm_get_timing synchronises on the last event. */
+typedef enum {
+  HTTM_T_SIM = 0, HTTM_T_SELECT, HTTM_T_MERGE_KV, HTTM_T_MERGE_Q, HTTM_T_OUTLIER,
+  HTTM_T_RESTORE, HTTM_T_ATTN, HTTM_T_UNMERGE, HTTM_T_COUNT
+} httm_timing_stage;
+httm_status httm_set_timing(int32_t enable);
+httm_status httm_get_timing(float* ms, int32_t n);
+
+const char* httm_status_string(httm_status s);
+/* Last error detail recorded on this thread (empty if none). */
+const char* httm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HTTM_H_ */

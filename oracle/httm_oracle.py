@@ -165,22 +165,30 @@ def row_normalize(x: np.ndarray) -> np.ndarray:
     return (x / np.maximum(nrm, np.float32(EPS_NORM))[:, None]).astype(np.float32)
 
 
-def match_block(xb: np.ndarray, s: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
-    """Bipartite cosine matching inside one block (HTTM page, key design 1).
+def block_similarity(xb: np.ndarray, s: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Sim = RowNorm(S) . RowNorm(D)^T of one block (HTTM page, key design 1).
 
     Block positions i with i mod s == 0 are destinations D, the rest sources S
-    (R7, R8).  Sim = RowNorm(S) . RowNorm(D)^T; every source keeps only its
-    most similar destination, ties to the smaller destination position (R11).
-    Returns (dst positions, src positions, matched dst position per src,
-    score per src).
+    (R7, R8).  Returns (dst positions, src positions, fp32 sim [|S|][|D|]).
     """
     n = xb.shape[0]
     pos = np.arange(n)
     dpos = pos[pos % s == 0]
     spos = pos[pos % s != 0]
+    sim = (row_normalize(xb[spos]) @ row_normalize(xb[dpos]).T).astype(np.float32)
+    return dpos, spos, sim
+
+
+def match_block(xb: np.ndarray, s: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """Bipartite cosine matching inside one block (HTTM page, key design 1).
+
+    Every source keeps only its most similar destination, ties to the smaller
+    destination position (R11).  Returns (dst positions, src positions,
+    matched dst position per src, score per src).
+    """
+    dpos, spos, sim = block_similarity(xb, s)
     if len(spos) == 0:
         return dpos, spos, np.zeros(0, np.int64), np.zeros(0, np.float32)
-    sim = (row_normalize(xb[spos]) @ row_normalize(xb[dpos]).T).astype(np.float32)
     j = np.argmax(sim, axis=1)  # first maximum = smallest dst position
     score = sim[np.arange(len(spos)), j] + np.float32(0.0)  # canonical +0
     return dpos, spos, dpos[j], score.astype(np.float32)

@@ -1,0 +1,195 @@
+"""Staged comparison of an implementation's intermediates with the oracle.
+
+TEST INFRASTRUCTURE ONLY (see httm_oracle).  The caller passes the other
+implementation's intermediates as plain numpy arrays; nothing here imports
+or calls that implementation.
+
+Index decisions are compared exactly, except where the oracle itself finds a
+near-tie (similarity within 1e-5 of the best, or a source score within 1e-5 of
+the r-th score), which is counted.  Every later stage is re-run by the oracle
+on the implementation's own indices, so a counted near-tie never cascades:
+
+  (i)   matches and scores, per block;
+  (ii)  top-r selection and the resulting groups (groups exactly);
+  (iii) deviations on the implementation's query groups, and the global
+        outlier choice on the implementation's deviations (exactly);
+  (iv)  final query partition (exactly) and outputs within tolerance.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+from . import httm_oracle as O
+
+NEAR_TIE = 1e-5
+
+
+class ParityError(AssertionError):
+    pass
+
+
+def canonical(slot: np.ndarray) -> np.ndarray:
+    """Group label -> smallest token id of the group, per token."""
+    slot = np.asarray(slot, dtype=np.int64)
+    n = np.arange(len(slot))
+    u, inv = np.unique(slot, return_inverse=True)
+    mins = np.full(len(u), np.iinfo(np.int64).max, dtype=np.int64)
+    np.minimum.at(mins, inv, n)
+    return mins[inv]
+
+
+@dataclass
+class Report:
+    n_src: int = 0
+    match_near_ties: int = 0
+    select_near_ties: int = 0
+    max_score_err: float = 0.0
+    delta_nonexact: int = 0
+    max_delta_err: float = 0.0
+    outlier_threshold_ties: int = 0
+    max_out_err: float = 0.0
+    out_rms: float = 0.0
+    notes: List[str] = field(default_factory=list)
+
+    def as_dict(self) -> Dict:
+        return dict(self.__dict__)
+
+
+def check_stream(x: np.ndarray, p: O.Params, ratio: float, stride: int, gpu_match: np.ndarray,
+                 gpu_score: np.ndarray, gpu_group: np.ndarray, rep: Report, what: str) -> np.ndarray:
+    """Stages (i)-(ii) for one head and stream; returns the canonical groups.
+
+    gpu_match: destination index (inside its block) per source, sources
+    ordered by block then block position; gpu_score: cosine of that match;
+    gpu_group: merged slot of every token.
+    """
+    s = O.dst_stride(ratio, stride)
+    N = p.n_tokens
+    rep_gpu = canonical(gpu_group)
+    label = np.arange(N, dtype=np.int64)  # group built from the implementation's own decisions
+    k0 = 0
+    for b in O.blocks(p):
+        tok = b.tokens
+        dpos, spos, sim = O.block_similarity(x[tok], s)
+        ns = len(spos)
+        gm = np.asarray(gpu_match[k0:k0 + ns], dtype=np.int64)
+        gs = np.asarray(gpu_score[k0:k0 + ns], dtype=np.float32)
+        k0 += ns
+        if ns == 0:
+            continue
+        if gm.min() < 0 or gm.max() >= len(dpos):
+            raise ParityError(f"{what}: match index out of range in block {b.g},{b.a}")
+        jo = np.argmax(sim, axis=1)
+        rows = np.arange(ns)
+        gap = sim[rows, jo] - sim[rows, gm]
+        bad = (gm != jo) & (gap >= NEAR_TIE)
+        if bad.any():
+            i = int(np.flatnonzero(bad)[0])
+            raise ParityError(f"{what}: block {b.g},{b.a} source {i} matched dst {gm[i]} (sim {sim[i, gm[i]]:.7f})"
+                              f" but best is {jo[i]} (sim {sim[i, jo[i]]:.7f})")
+        rep.match_near_ties += int(((gm != jo) & (gap < NEAR_TIE)).sum())
+        err = np.abs(gs.astype(np.float64) - sim[rows, gm])
+        rep.max_score_err = max(rep.max_score_err, float(err.max()))
+        if err.max() >= NEAR_TIE:
+            raise ParityError(f"{what}: score error {err.max():.3g} in block {b.g},{b.a}")
+        # (ii) selection: a source is merged iff it sits in its match's group
+        src_tok, dst_tok = tok[spos], tok[dpos[gm]]
+        sel = rep_gpu[src_tok] == rep_gpu[dst_tok]
+        r = O.merge_count(ratio, b.n, ns)
+        if int(sel.sum()) != r:
+            raise ParityError(f"{what}: block {b.g},{b.a} merged {int(sel.sum())} sources, expected r={r}")
+        so = sim[rows, jo]
+        osel = O.select_top_r(so, spos, r)
+        if r > 0 and r < ns:
+            thr = np.sort(so)[::-1][r - 1]
+            diff = sel != osel
+            if (diff & (np.abs(so - thr) >= NEAR_TIE)).any():
+                i = int(np.flatnonzero(diff & (np.abs(so - thr) >= NEAR_TIE))[0])
+                raise ParityError(f"{what}: block {b.g},{b.a} selection differs at source {i} "
+                                  f"(score {so[i]:.7f}, r-th {thr:.7f})")
+            rep.select_near_ties += int(diff.sum())
+        elif (sel != osel).any():
+            raise ParityError(f"{what}: block {b.g},{b.a} selection differs with r={r}, |S|={ns}")
+        label[src_tok[sel]] = dst_tok[sel]
+        rep.n_src += ns
+    want = canonical(label)
+    if not np.array_equal(want, rep_gpu):
+        i = int(np.flatnonzero(want != rep_gpu)[0])
+        raise ParityError(f"{what}: groups differ at token {i}: rep {rep_gpu[i]} vs {want[i]}")
+    return rep_gpu
+
+
+def check_layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, p: O.Params, gpu: Dict[str, np.ndarray],
+                out_gpu: np.ndarray, out_heads: Optional[Sequence[int]] = None,
+                rows: Optional[np.ndarray] = None, out_tol: Optional[float] = None,
+                match_heads: Optional[Sequence[int]] = None, rel_tol: Optional[float] = None) -> Report:
+    """Staged parity of one layer.
+
+    gpu: q_match, q_score, kv_match, kv_score ([h][src]), q_group, kv_group,
+    q_slot ([h][N]), delta ([h][N] float32), outlier ([h][N] uint8).
+    out_gpu: [h][N][d] as float64/float32.  Tolerance on the max-abs output
+    error: ``rel_tol`` * RMS(oracle output) if given (bf16: 2e-2), else
+    ``out_tol`` (default 1e-4, fp32).
+    """
+    rep = Report()
+    h, N = q.shape[0], q.shape[1]
+    mh = list(range(h)) if match_heads is None else list(match_heads)
+    nq, nk = gpu["q_match"].shape[1], gpu["kv_match"].shape[1]
+    q_rep = [None] * h
+    k_rep = [None] * h
+    for i in range(h):
+        if i in mh:
+            q_rep[i] = check_stream(q[i], p, p.q_ratio, p.q_dst_stride, gpu["q_match"][i], gpu["q_score"][i],
+                                    gpu["q_group"][i], rep, f"head {i} Q")
+            k_rep[i] = check_stream(k[i], p, p.kv_ratio, p.kv_dst_stride, gpu["kv_match"][i],
+                                    gpu["kv_score"][i], gpu["kv_group"][i], rep, f"head {i} K")
+        else:
+            q_rep[i] = canonical(gpu["q_group"][i])
+            k_rep[i] = canonical(gpu["kv_group"][i])
+    # (iii) deviations on the implementation's query groups
+    delta_o = O.deviations(q, q_rep)
+    dg = gpu["delta"].astype(np.float32)
+    rep.delta_nonexact = int((dg != delta_o).sum())
+    rep.max_delta_err = float(np.abs(dg.astype(np.float64) - delta_o).max())
+    tol = NEAR_TIE * np.maximum(1.0, delta_o)
+    if (np.abs(dg.astype(np.float64) - delta_o) > tol).any():
+        raise ParityError(f"deviation error {rep.max_delta_err:.3g}")
+    k_o = O.outlier_budget(p)
+    mask_gpu = gpu["outlier"].astype(bool)
+    if not np.array_equal(O.select_outliers(dg, k_o), mask_gpu):
+        raise ParityError("outlier mask differs from the global top-k_o of the implementation's deviations")
+    mo = O.select_outliers(delta_o, k_o)
+    if not np.array_equal(mo, mask_gpu):
+        flat = np.sort(delta_o.reshape(-1))[::-1]
+        thr = flat[k_o - 1] if k_o > 0 else np.inf
+        diff = mo != mask_gpu
+        if (np.abs(delta_o[diff] - thr) > NEAR_TIE * max(1.0, thr)).any():
+            raise ParityError("outlier mask differs away from the threshold")
+        rep.outlier_threshold_ties = int(diff.sum())
+    # (iv) final query partition and outputs
+    qf = []
+    for i in range(h):
+        want = O.restore_partition(q_rep[i], mask_gpu[i])
+        got = canonical(gpu["q_slot"][i])
+        if not np.array_equal(want, got):
+            j = int(np.flatnonzero(want != got)[0])
+            raise ParityError(f"head {i}: final query partition differs at token {j}")
+        qf.append(got)
+    hs = list(range(h)) if out_heads is None else list(out_heads)
+    outs = []
+    for i in hs:
+        outs.append(O.head_output(q[i], k[i], v[i], qf[i], k_rep[i], p.scale, rows))
+    ref = np.stack(outs)
+    got = out_gpu[hs] if rows is None else out_gpu[hs][:, rows]
+    rep.out_rms = float(np.sqrt(np.mean(ref ** 2)))
+    rep.max_out_err = float(np.abs(got.astype(np.float64) - ref).max())
+    if rel_tol is not None:
+        out_tol = rel_tol * rep.out_rms
+    elif out_tol is None:
+        out_tol = 1e-4
+    if not rep.max_out_err <= out_tol:
+        raise ParityError(f"output error {rep.max_out_err:.3g} > {out_tol:.3g} (rms {rep.out_rms:.3g})")
+    return rep

@@ -1,0 +1,143 @@
+"""Host-side checks of the C ABI (no GPU needed, no compute calls).
+
+* libhttm.so loads and exports every function ``include/httm.h`` declares;
+* the host plan's block table, strides, merge counts and sizes equal the
+  oracle's independent construction (temporal reordering of the HTTM page,
+  key design 2; counts of key design 1 / settings);
+* validation returns the documented status codes.
+"""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gen
+import oracle as O
+import token_merged_global_amd as H
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "httm.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(httm_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared()
+    assert len(names) >= 15
+    L = H.lib()
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in H.EXPORTS, n
+
+
+def _plans():
+    for name in ["tiny", "vggt30", "vggt100", "vggt200", "vggt500"]:
+        yield name, gen.WORKLOADS[name]
+    w = gen.WORKLOADS["vggt200"]
+    yield "vggt200_kv75", w.with_(kv_ratio=0.75)
+    yield "vggt200_ratio0", w.with_(q_ratio=0.0, kv_ratio=0.0)
+    yield "odd", gen.Workload(name="odd", cfg_id=9, dtype="bf16", heads=3, d_head=64, frames=7, grid_h=5,
+                              grid_w=9, n_special=2, n_s=10, n_t=3, q_ratio=0.6, kv_ratio=0.3,
+                              outlier_pct=7.5)
+
+
+@pytest.mark.parametrize("name,w", list(_plans()))
+def test_plan_matches_oracle_blocks(name, w):
+    plan = H.Plan.from_workload(w)
+    p = O.Params.from_workload(w)
+    ob = O.blocks(p)
+    hb = plan.blocks()
+    assert len(hb) == len(ob) == plan.info["n_blocks"]
+    sq, sk = O.dst_stride(p.q_ratio), O.dst_stride(p.kv_ratio)
+    assert (plan.info["q_stride"], plan.info["kv_stride"]) == (sq, sk)
+    pi = O.reorder_permutation(p)
+    start = 0
+    slots = [0, 0]
+    srcs = [0, 0]
+    for b, (o, h) in enumerate(zip(ob, hb)):
+        assert h["start"] == start and h["n"] == o.n
+        assert (h["f0"], h["nf"], h["j0"], h["run"]) == (o.f0, o.nf, o.j0, o.run)
+        # block position -> token, as the kernels compute it
+        i = np.arange(o.n)
+        tok = (h["f0"] + i // h["run"]) * p.tokens_per_frame + p.n_special + h["j0"] + i % h["run"]
+        assert np.array_equal(tok, pi[start:start + o.n])
+        for st, (s, ratio, pre) in enumerate([(sq, p.q_ratio, "q"), (sk, p.kv_ratio, "kv")]):
+            nd = -(-o.n // s)
+            assert h[f"{pre}_dst"] == nd and h[f"{pre}_src"] == o.n - nd
+            assert h[f"{pre}_r"] == O.merge_count(ratio, o.n, o.n - nd)
+            assert h[f"{pre}_slot0"] == slots[st] and h[f"{pre}_src0"] == srcs[st]
+            slots[st] += o.n - h[f"{pre}_r"]
+            srcs[st] += o.n - nd
+        start += o.n
+    spec = p.frames * p.n_special
+    assert plan.info["q_groups"] == slots[0] + spec
+    assert plan.info["kv_len"] == slots[1] + spec
+    assert plan.info["n_outliers"] == O.outlier_budget(p)
+    assert plan.info["q_capacity"] == p.heads * plan.info["q_groups"] + O.outlier_budget(p)
+    assert plan.info["n_tokens"] == p.n_tokens
+
+
+def test_vggt30_sizes():
+    plan = H.Plan.from_workload(gen.WORKLOADS["vggt30"])
+    assert (plan.info["q_groups"], plan.info["kv_len"], plan.info["n_outliers"]) == (4257, 20685, 65952)
+    assert abs(plan.info["softmax_scale"] - 0.125) < 1e-9
+
+
+def _status(**kw):
+    base = dict(heads=2, frames=4, grid_h=4, grid_w=4, n_special=1, n_s=8, n_t=2, q_ratio=0.5, kv_ratio=0.5,
+                outlier_pct=10.0, dtype="bf16")
+    base.update(kw)
+    try:
+        H.Plan(**base)
+        return 0
+    except H.HttmError as e:
+        return e.status
+
+
+def test_validation_codes():
+    assert _status() == 0
+    assert _status(q_ratio=1.0) == 1
+    assert _status(kv_ratio=-0.1) == 1
+    assert _status(outlier_pct=100.5) == 1
+    assert _status(heads=0) == 1
+    assert _status(q_dst_stride=1) == 1
+    assert _status(d_head=128) == 2
+    assert _status(block_order=1) == 2
+    assert _status(n_s=128, n_t=33) == 2  # block larger than 4096
+    assert _status(softmax_scale=float("inf")) == 1
+
+
+def test_layer_rejects_bad_buffers_before_any_launch():
+    """Host validation paths (no device call is reached)."""
+    L = H.lib()
+    plan = H.Plan(heads=1, frames=2, grid_h=4, grid_w=4, n_special=0, n_s=8, n_t=2, q_ratio=0.5,
+                  kv_ratio=0.5, outlier_pct=10.0, dtype="f32")
+    ws = plan.workspace_bytes
+    fake = 1 << 20  # never dereferenced: validation fails first
+    st = L.httm_layer(plan.handle, fake, ws - 1, fake, fake, fake, fake, None, None)
+    assert st == 3
+    st = L.httm_layer(plan.handle, fake, ws, None, fake, fake, fake, None, None)
+    assert st == 1
+    st = L.httm_layer(plan.handle, fake + 4, ws, fake, fake, fake, fake, None, None)
+    assert st == 1
+    idx = H.Index(0, fake, plan.index_bytes, 0)
+    st = L.httm_layer_cached(plan.handle, fake, ws, ctypes.byref(idx), fake, fake, fake, fake, None)
+    assert st == 4
+    other = H.Plan(heads=1, frames=2, grid_h=4, grid_w=4, n_special=0, n_s=8, n_t=2, q_ratio=0.5,
+                   kv_ratio=0.5, outlier_pct=10.0, dtype="f32")
+    idx2 = H.Index(other.handle.value or 0, fake, plan.index_bytes, 1)
+    st = L.httm_layer_cached(plan.handle, fake, ws, ctypes.byref(idx2), fake, fake, fake, fake, None)
+    assert st == 4
+    small = H.Index(0, fake, plan.index_bytes - 1, 0)
+    st = L.httm_layer(plan.handle, fake, ws, fake, fake, fake, fake, ctypes.byref(small), None)
+    assert st == 3
+    assert L.httm_status_string(4).decode().startswith("index")
+    n = ctypes.c_size_t()
+    assert L.httm_debug_size(plan.handle, 99, ctypes.byref(n)) == 1
+    assert L.httm_debug_size(plan.handle, 10, ctypes.byref(n)) == 0 and n.value == 16

@@ -1,0 +1,582 @@
+// Host side of the HTTM layer library: parameter validation, the plan (block
+// geometry and sizes), workspace / index layouts, and the launch sequence.
+//
+// The launch sequence follows the layer as the HTTM page describes it
+// ("HTTM: Head-wise Temporal Token Merging for Faster VGGT", overall framework):
+// block-local matching of Q and K (key designs 1, 2), top-r merge, mean merge
+// of K and V, query deviation, cross-head outlier selection and restore (key
+// design 3), attention on the shortened sequences, unmerge.  Every per-head
+// ragged length stays on the device; the host only uses bounds that follow
+// from the parameters, so a call never waits for the GPU.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/httm.h"
+#include "geo.h"
+#include "kernels.h"
+
+using namespace httm;
+
+namespace {
+
+thread_local std::string g_err;
+
+httm_status fail(httm_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+std::atomic<uint64_t> g_plan_counter{0x48540000ull};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Region {
+  size_t off = 0, bytes = 0;
+};
+
+struct Layout {
+  Region match[2], score[2];
+  Region q_members, q_off, q_group, k_group;
+  Region qsum, delta, mask, radix, base;
+  Region qt, kt, vt, o;
+  Region index;  // used when the caller passes no index buffer
+  size_t total = 0;
+};
+
+struct IndexLayout {
+  Region k_members, k_off, fmembers, foff, slot, lenq, cu_q;
+  size_t total = 0;
+};
+
+struct Builder {
+  size_t cur = 0;
+  Region take(size_t bytes) {
+    Region r;
+    r.off = cur;
+    r.bytes = bytes;
+    cur = align256(cur + bytes);
+    return r;
+  }
+};
+
+}  // namespace
+
+struct httm_plan {
+  httm_params p;
+  uint64_t id;
+  Geo g;
+  int64_t k_o;
+  int64_t q_cap;
+  int32_t lk_pad;
+  float scale;
+  size_t esize;
+  Layout L;
+  IndexLayout I;
+  size_t dense_ws;
+  std::vector<httm_block> blocks;
+};
+
+namespace {
+
+int stride_of(double ratio, int32_t given) {
+  if (given > 0) return given;
+  const int s = (int)std::ceil(1.0 / (1.0 - ratio) - 1e-9);
+  return s > 4 ? s : 4;
+}
+
+int32_t merge_count(double ratio, int32_t n, int32_t ns) {
+  const int32_t r = (int32_t)std::floor(ratio * (double)n + 1e-9);
+  return r < ns ? r : ns;
+}
+
+httm_status build(const httm_params& p, httm_plan* pl) {
+  if (p.heads < 1 || p.frames < 1 || p.grid_h < 1 || p.grid_w < 1 || p.n_special < 0 || p.n_s < 1 ||
+      p.n_t < 1)
+    return fail(HTTM_ERR_INVALID_ARG, "heads, frames, grid, n_s, n_t must be >= 1 and n_special >= 0");
+  if (!(p.q_ratio >= 0.0 && p.q_ratio < 1.0) || !(p.kv_ratio >= 0.0 && p.kv_ratio < 1.0))
+    return fail(HTTM_ERR_INVALID_ARG, "merge ratios must lie in [0, 1)");
+  if (!(p.outlier_pct >= 0.0 && p.outlier_pct <= 100.0))
+    return fail(HTTM_ERR_INVALID_ARG, "outlier_pct must lie in [0, 100]");
+  if (p.q_dst_stride < 0 || p.kv_dst_stride < 0 || p.q_dst_stride == 1 || p.kv_dst_stride == 1)
+    return fail(HTTM_ERR_INVALID_ARG, "destination strides must be 0 (derived) or >= 2");
+  if (!(p.softmax_scale >= 0.0f) || std::isinf(p.softmax_scale))
+    return fail(HTTM_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  if (p.dtype != HTTM_F32 && p.dtype != HTTM_BF16) return fail(HTTM_ERR_INVALID_ARG, "unknown dtype");
+  if (p.d_head != kD) return fail(HTTM_ERR_UNSUPPORTED, "only d_head == 64 is built");
+  if (p.block_order != 0) return fail(HTTM_ERR_UNSUPPORTED, "only frame-major blocks (block_order 0) are built");
+  if ((int64_t)p.n_s * p.n_t > kMaxBlock) return fail(HTTM_ERR_UNSUPPORTED, "n_s * n_t must be <= 4096");
+  const int64_t T = (int64_t)p.n_special + (int64_t)p.grid_h * p.grid_w;
+  const int64_t N = (int64_t)p.frames * T;
+  if ((int64_t)p.heads * N >= (1ll << 31) || (int64_t)p.heads * N * kD >= (1ll << 40))
+    return fail(HTTM_ERR_INVALID_ARG, "heads * N must be < 2^31");
+
+  pl->p = p;
+  Geo& g = pl->g;
+  std::memset(&g, 0, sizeof(g));
+  g.heads = p.heads;
+  g.F = p.frames;
+  g.HW = p.grid_h * p.grid_w;
+  g.nsp = p.n_special;
+  g.T = (int32_t)T;
+  g.N = (int32_t)N;
+  g.P = p.frames * g.HW;
+  g.n_s = p.n_s < g.HW ? p.n_s : g.HW;
+  g.n_t = p.n_t < p.frames ? p.n_t : p.frames;
+  g.A = ceil_div(g.HW, g.n_s);
+  g.G = ceil_div(g.F, g.n_t);
+  g.nf_last = g.F - (g.G - 1) * g.n_t;
+  g.run_last = g.HW - (g.A - 1) * g.n_s;
+  g.nblocks = g.A * g.G;
+  const double ratio[2] = {p.q_ratio, p.kv_ratio};
+  g.s[0] = stride_of(p.q_ratio, p.q_dst_stride);
+  g.s[1] = stride_of(p.kv_ratio, p.kv_dst_stride);
+  for (int st = 0; st < 2; ++st) {
+    for (int lg = 0; lg < 2; ++lg)
+      for (int lr = 0; lr < 2; ++lr) {
+        const int32_t nf = lg ? g.nf_last : g.n_t;
+        const int32_t run = lr ? g.run_last : g.n_s;
+        const int32_t n = nf * run;
+        const int32_t nd = ceil_div(n, g.s[st]);
+        g.r[st][lg][lr] = merge_count(ratio[st], n, n - nd);
+      }
+    // one full temporal group: (A-1) full runs and the last run, nf = n_t
+    const int32_t nfull = g.n_t * g.n_s, nlast = g.n_t * g.run_last;
+    const int32_t ndf = ceil_div(nfull, g.s[st]), ndl = ceil_div(nlast, g.s[st]);
+    if (g.A > 1) {
+      g.grp_slots[st] = (g.A - 1) * (nfull - g.r[st][0][0]) + (nlast - g.r[st][0][1]);
+      g.grp_src[st] = (g.A - 1) * (nfull - ndf) + (nlast - ndl);
+    } else {
+      g.grp_slots[st] = nlast - g.r[st][0][1];
+      g.grp_src[st] = nlast - ndl;
+    }
+  }
+  // Per-block table (host copy, for callers and for totals); the kernels
+  // recompute the same rows from Geo.
+  pl->blocks.resize(g.nblocks);
+  int64_t slots[2] = {0, 0}, srcs[2] = {0, 0};
+  for (int b = 0; b < g.nblocks; ++b) {
+    const BlockInfo q = block_info(g, b, kQ), k = block_info(g, b, kK);
+    if (q.slot0 != slots[0] || k.slot0 != slots[1] || q.src0 != srcs[0] || k.src0 != srcs[1])
+      return fail(HTTM_ERR_INVALID_ARG, "internal: block prefix mismatch");
+    httm_block& r = pl->blocks[b];
+    r.start = q.start;
+    r.n = q.n;
+    r.f0 = q.f0;
+    r.nf = q.nf;
+    r.j0 = q.j0;
+    r.run = q.run;
+    r.q_dst = q.nd;
+    r.q_src = q.ns;
+    r.q_r = q.r;
+    r.kv_dst = k.nd;
+    r.kv_src = k.ns;
+    r.kv_r = k.r;
+    r.q_slot0 = q.slot0;
+    r.kv_slot0 = k.slot0;
+    r.q_src0 = q.src0;
+    r.kv_src0 = k.src0;
+    slots[0] += q.n - q.r;
+    slots[1] += k.n - k.r;
+    srcs[0] += q.ns;
+    srcs[1] += k.ns;
+  }
+  for (int st = 0; st < 2; ++st) {
+    g.nslots[st] = (int32_t)(slots[st] + (int64_t)g.F * g.nsp);
+    g.nsrc[st] = (int32_t)srcs[st];
+  }
+  pl->k_o = (int64_t)std::floor(p.outlier_pct * (double)p.heads * (double)N / 100.0 + 1e-9);
+  pl->q_cap = (int64_t)p.heads * g.nslots[kQ] + pl->k_o;
+  pl->lk_pad = ceil_div(g.nslots[kK], 64) * 64;
+  pl->scale = p.softmax_scale > 0.0f ? p.softmax_scale : 1.0f / std::sqrt((float)kD);
+  pl->esize = p.dtype == HTTM_BF16 ? 2 : 4;
+
+  const size_t h = (size_t)p.heads, n = (size_t)N, E = pl->esize;
+  // index layout
+  {
+    Builder b;
+    IndexLayout& I = pl->I;
+    I.k_members = b.take(4 * h * n);
+    I.k_off = b.take(4 * h * ((size_t)g.nslots[kK] + 1));
+    I.fmembers = b.take(4 * h * n);
+    I.foff = b.take(4 * h * (n + 1));
+    I.slot = b.take(4 * h * n);
+    I.lenq = b.take(4 * h);
+    I.cu_q = b.take(4 * (h + 1));
+    I.total = b.cur;
+  }
+  {
+    Builder b;
+    Layout& Lw = pl->L;
+    for (int st = 0; st < 2; ++st) {
+      Lw.match[st] = b.take(4 * h * (size_t)g.nsrc[st]);
+      Lw.score[st] = b.take(4 * h * (size_t)g.nsrc[st]);
+    }
+    Lw.q_members = b.take(4 * h * n);
+    Lw.q_off = b.take(4 * h * ((size_t)g.nslots[kQ] + 1));
+    Lw.q_group = b.take(4 * h * n);
+    Lw.k_group = b.take(4 * h * n);
+    Lw.qsum = b.take(4 * h * (size_t)g.nslots[kQ] * kD);
+    Lw.delta = b.take(4 * h * n);
+    Lw.mask = b.take(h * n);
+    Lw.radix = b.take(4 * outlier_scratch_words((int64_t)h * n));
+    Lw.base = b.take(4 * h * (size_t)g.nslots[kQ]);
+    Lw.qt = b.take(E * (size_t)pl->q_cap * kD);
+    Lw.kt = b.take(E * h * (size_t)pl->lk_pad * kD);
+    Lw.vt = b.take(E * h * (size_t)pl->lk_pad * kD);
+    Lw.o = b.take(E * (size_t)pl->q_cap * kD);
+    Lw.index = b.take(pl->I.total);
+    Lw.total = b.cur;
+  }
+  pl->dense_ws = E * h * (size_t)ceil_div(g.N, 64) * 64 * kD;
+  pl->id = ++g_plan_counter;
+  return HTTM_OK;
+}
+
+template <typename P>
+P* at(void* base, const Region& r) {
+  return reinterpret_cast<P*>(reinterpret_cast<char*>(base) + r.off);
+}
+
+// ---------------------------------------------------------------- timing
+struct Timing {
+  bool enabled = false;
+  hipEvent_t ev[2 * HTTM_T_COUNT] = {};
+  bool used[HTTM_T_COUNT] = {};
+  bool created = false;
+};
+Timing g_timing;
+
+void stage_begin(int s, hipStream_t st) {
+  if (g_timing.enabled) {
+    (void)hipEventRecord(g_timing.ev[2 * s], st);
+    g_timing.used[s] = true;
+  }
+}
+void stage_end(int s, hipStream_t st) {
+  if (g_timing.enabled) (void)hipEventRecord(g_timing.ev[2 * s + 1], st);
+}
+void timing_reset() {
+  for (int i = 0; i < HTTM_T_COUNT; ++i) g_timing.used[i] = false;
+}
+
+#define CHECK_LAUNCH(expr)                                                        \
+  do {                                                                            \
+    hipError_t e_ = (expr);                                                       \
+    if (e_ != hipSuccess) return fail(HTTM_ERR_DEVICE, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+httm_status check_common(const httm_plan* plan, void* ws, size_t ws_bytes, const void* q,
+                         const void* k, const void* v, void* out, size_t need) {
+  if (!plan) return fail(HTTM_ERR_INVALID_ARG, "plan is NULL");
+  if (!q || !k || !v || !out) return fail(HTTM_ERR_INVALID_ARG, "q, k, v and out must not be NULL");
+  if (!ws) return fail(HTTM_ERR_INVALID_ARG, "workspace is NULL");
+  if (ws_bytes < need) return fail(HTTM_ERR_WORKSPACE, "workspace smaller than httm_workspace_size()");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)ws) & 15)
+    return fail(HTTM_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+  return HTTM_OK;
+}
+
+// Attention + unmerge, shared by the full and cached layers.
+httm_status attend_unmerge(const httm_plan* pl, void* ws, char* idx, const void* qt,
+                           void* out, hipStream_t st) {
+  const Geo& g = pl->g;
+  const int dt = pl->p.dtype;
+  AttnShape s;
+  s.heads = g.heads;
+  s.lk = g.nslots[kK];
+  s.k_rows = pl->lk_pad;
+  s.vt_pitch = pl->lk_pad;
+  s.lq_uniform = 0;
+  s.q_capacity = pl->q_cap;
+  s.scale = pl->scale;
+  const int32_t* lenq = reinterpret_cast<const int32_t*>(idx + pl->I.lenq.off);
+  stage_begin(HTTM_T_ATTN, st);
+  CHECK_LAUNCH(launch_attention(dt, s, qt, at<void>(ws, pl->L.kt), at<void>(ws, pl->L.vt), lenq,
+                                at<void>(ws, pl->L.o), st));
+  stage_end(HTTM_T_ATTN, st);
+  stage_begin(HTTM_T_UNMERGE, st);
+  CHECK_LAUNCH(launch_unmerge(dt, g.heads, g.N, reinterpret_cast<const int32_t*>(idx + pl->I.slot.off),
+                              at<void>(ws, pl->L.o), out, st));
+  stage_end(HTTM_T_UNMERGE, st);
+  return HTTM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* httm_status_string(httm_status s) {
+  switch (s) {
+    case HTTM_OK: return "ok";
+    case HTTM_ERR_INVALID_ARG: return "invalid argument";
+    case HTTM_ERR_UNSUPPORTED: return "unsupported";
+    case HTTM_ERR_WORKSPACE: return "workspace too small";
+    case HTTM_ERR_INDEX_MISMATCH: return "index does not belong to this plan";
+    case HTTM_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* httm_last_error(void) { return g_err.c_str(); }
+
+httm_status httm_plan_create(const httm_params* params, httm_plan** out) {
+  if (!params || !out) return fail(HTTM_ERR_INVALID_ARG, "params and out must not be NULL");
+  *out = nullptr;
+  httm_plan* pl = new httm_plan();
+  const httm_status s = build(*params, pl);
+  if (s != HTTM_OK) {
+    delete pl;
+    return s;
+  }
+  g_err.clear();
+  *out = pl;
+  return HTTM_OK;
+}
+
+void httm_plan_destroy(httm_plan* plan) { delete plan; }
+
+httm_status httm_plan_get_info(const httm_plan* pl, httm_plan_info* info) {
+  if (!pl || !info) return fail(HTTM_ERR_INVALID_ARG, "NULL argument");
+  info->n_tokens = pl->g.N;
+  info->n_patch = pl->g.P;
+  info->n_blocks = pl->g.nblocks;
+  info->q_stride = pl->g.s[kQ];
+  info->kv_stride = pl->g.s[kK];
+  info->q_groups = pl->g.nslots[kQ];
+  info->kv_len = pl->g.nslots[kK];
+  info->n_outliers = pl->k_o;
+  info->q_capacity = pl->q_cap;
+  info->q_src = pl->g.nsrc[kQ];
+  info->kv_src = pl->g.nsrc[kK];
+  info->softmax_scale = pl->scale;
+  return HTTM_OK;
+}
+
+httm_status httm_plan_get_blocks(const httm_plan* pl, httm_block* rows, int32_t cap) {
+  if (!pl || (!rows && cap > 0) || cap < 0) return fail(HTTM_ERR_INVALID_ARG, "bad arguments");
+  const int32_t n = cap < pl->g.nblocks ? cap : pl->g.nblocks;
+  for (int32_t i = 0; i < n; ++i) rows[i] = pl->blocks[i];
+  return HTTM_OK;
+}
+
+httm_status httm_workspace_size(const httm_plan* pl, size_t* bytes) {
+  if (!pl || !bytes) return fail(HTTM_ERR_INVALID_ARG, "NULL argument");
+  *bytes = pl->L.total;
+  return HTTM_OK;
+}
+
+httm_status httm_index_size(const httm_plan* pl, size_t* bytes) {
+  if (!pl || !bytes) return fail(HTTM_ERR_INVALID_ARG, "NULL argument");
+  *bytes = pl->I.total;
+  return HTTM_OK;
+}
+
+httm_status httm_dense_workspace_size(const httm_plan* pl, size_t* bytes) {
+  if (!pl || !bytes) return fail(HTTM_ERR_INVALID_ARG, "NULL argument");
+  *bytes = pl->dense_ws;
+  return HTTM_OK;
+}
+
+httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const void* q, const void* k,
+                       const void* v, void* out, httm_index* index, void* stream) {
+  httm_status s = check_common(pl, ws, ws_bytes, q, k, v, out, pl ? pl->L.total : 0);
+  if (s != HTTM_OK) return s;
+  if (index && (!index->dev || index->bytes < pl->I.total))
+    return fail(HTTM_ERR_WORKSPACE, "index buffer smaller than httm_index_size()");
+  if (index && ((uintptr_t)index->dev & 15)) return fail(HTTM_ERR_INVALID_ARG, "index must be 16-byte aligned");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const Geo& g = pl->g;
+  const Layout& L = pl->L;
+  const IndexLayout& I = pl->I;
+  const int dt = pl->p.dtype;
+  char* idx = index ? reinterpret_cast<char*>(index->dev) : at<char>(ws, L.index);
+  timing_reset();
+
+  stage_begin(HTTM_T_SIM, st);
+  CHECK_LAUNCH(launch_sim(g, dt, q, k, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
+                          at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), st));
+  stage_end(HTTM_T_SIM, st);
+
+  Csr cq{at<int32_t>(ws, L.q_members), at<int32_t>(ws, L.q_off), at<int32_t>(ws, L.q_group)};
+  Csr ck{reinterpret_cast<int32_t*>(idx + I.k_members.off), reinterpret_cast<int32_t*>(idx + I.k_off.off),
+         at<int32_t>(ws, L.k_group)};
+  stage_begin(HTTM_T_SELECT, st);
+  CHECK_LAUNCH(launch_select(g, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
+                             at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), cq, ck, st));
+  stage_end(HTTM_T_SELECT, st);
+
+  stage_begin(HTTM_T_MERGE_KV, st);
+  CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, k, v, ck.members, ck.off,
+                               at<void>(ws, L.kt), at<void>(ws, L.vt), st));
+  stage_end(HTTM_T_MERGE_KV, st);
+
+  stage_begin(HTTM_T_MERGE_Q, st);
+  CHECK_LAUNCH(launch_merge_q(dt, g.heads, g.N, g.nslots[kQ], q, cq.members, cq.off,
+                              at<float>(ws, L.qsum), at<float>(ws, L.delta), st));
+  stage_end(HTTM_T_MERGE_Q, st);
+
+  stage_begin(HTTM_T_OUTLIER, st);
+  CHECK_LAUNCH(launch_outliers(at<float>(ws, L.delta), (int64_t)g.heads * g.N, pl->k_o,
+                               at<uint8_t>(ws, L.mask), at<uint32_t>(ws, L.radix), st));
+  stage_end(HTTM_T_OUTLIER, st);
+
+  RestoreOut ro;
+  ro.qt = at<void>(ws, L.qt);
+  ro.lenq = reinterpret_cast<int32_t*>(idx + I.lenq.off);
+  ro.cu_q = reinterpret_cast<int32_t*>(idx + I.cu_q.off);
+  ro.base = at<int32_t>(ws, L.base);
+  ro.fmembers = reinterpret_cast<int32_t*>(idx + I.fmembers.off);
+  ro.foff = reinterpret_cast<int32_t*>(idx + I.foff.off);
+  ro.slot = reinterpret_cast<int32_t*>(idx + I.slot.off);
+  stage_begin(HTTM_T_RESTORE, st);
+  CHECK_LAUNCH(launch_restore(dt, g.heads, g.N, g.nslots[kQ], q, cq.members, cq.off,
+                              at<float>(ws, L.qsum), at<uint8_t>(ws, L.mask), ro, st));
+  stage_end(HTTM_T_RESTORE, st);
+
+  s = attend_unmerge(pl, ws, idx, at<void>(ws, L.qt), out, st);
+  if (s != HTTM_OK) return s;
+  if (index) {
+    index->plan_id = pl->id;
+    index->valid = 1;
+  }
+  return HTTM_OK;
+}
+
+httm_status httm_layer_cached(const httm_plan* pl, void* ws, size_t ws_bytes, const httm_index* index,
+                              const void* q, const void* k, const void* v, void* out, void* stream) {
+  httm_status s = check_common(pl, ws, ws_bytes, q, k, v, out, pl ? pl->L.total : 0);
+  if (s != HTTM_OK) return s;
+  if (!index || !index->dev) return fail(HTTM_ERR_INVALID_ARG, "index is NULL");
+  if (index->plan_id != pl->id || !index->valid)
+    return fail(HTTM_ERR_INDEX_MISMATCH, "index was not filled by httm_layer with this plan");
+  if (index->bytes < pl->I.total) return fail(HTTM_ERR_WORKSPACE, "index buffer smaller than httm_index_size()");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const Geo& g = pl->g;
+  const IndexLayout& I = pl->I;
+  const int dt = pl->p.dtype;
+  char* idx = reinterpret_cast<char*>(index->dev);
+  timing_reset();
+  stage_begin(HTTM_T_MERGE_KV, st);
+  CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, k, v,
+                               reinterpret_cast<const int32_t*>(idx + I.k_members.off),
+                               reinterpret_cast<const int32_t*>(idx + I.k_off.off),
+                               at<void>(ws, pl->L.kt), at<void>(ws, pl->L.vt), st));
+  stage_end(HTTM_T_MERGE_KV, st);
+  stage_begin(HTTM_T_MERGE_Q, st);
+  CHECK_LAUNCH(launch_merge_q_cached(dt, g.heads, g.N, pl->q_cap, q,
+                                     reinterpret_cast<const int32_t*>(idx + I.fmembers.off),
+                                     reinterpret_cast<const int32_t*>(idx + I.foff.off),
+                                     reinterpret_cast<const int32_t*>(idx + I.lenq.off),
+                                     at<void>(ws, pl->L.qt), st));
+  stage_end(HTTM_T_MERGE_Q, st);
+  return attend_unmerge(pl, ws, idx, at<void>(ws, pl->L.qt), out, st);
+}
+
+httm_status httm_attention_dense(const httm_plan* pl, void* ws, size_t ws_bytes, const void* q,
+                                 const void* k, const void* v, void* out, void* stream) {
+  httm_status s = check_common(pl, ws, ws_bytes, q, k, v, out, pl ? pl->dense_ws : 0);
+  if (s != HTTM_OK) return s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const Geo& g = pl->g;
+  const int dt = pl->p.dtype;
+  const int pitch = ceil_div(g.N, 64) * 64;
+  timing_reset();
+  stage_begin(HTTM_T_MERGE_KV, st);
+  CHECK_LAUNCH(launch_transpose_v(dt, g.heads, g.N, pitch, v, ws, st));
+  stage_end(HTTM_T_MERGE_KV, st);
+  AttnShape a;
+  a.heads = g.heads;
+  a.lk = g.N;
+  a.k_rows = g.N;
+  a.vt_pitch = pitch;
+  a.lq_uniform = g.N;
+  a.q_capacity = (int64_t)g.heads * g.N;
+  a.scale = pl->scale;
+  stage_begin(HTTM_T_ATTN, st);
+  CHECK_LAUNCH(launch_attention(dt, a, q, k, ws, nullptr, out, st));
+  stage_end(HTTM_T_ATTN, st);
+  return HTTM_OK;
+}
+
+httm_status httm_debug_size(const httm_plan* pl, int32_t item, size_t* bytes) {
+  if (!pl || !bytes) return fail(HTTM_ERR_INVALID_ARG, "NULL argument");
+  const size_t h = pl->g.heads, n = pl->g.N;
+  switch (item) {
+    case HTTM_DBG_Q_MATCH:
+    case HTTM_DBG_Q_SCORE: *bytes = 4 * h * pl->g.nsrc[kQ]; break;
+    case HTTM_DBG_KV_MATCH:
+    case HTTM_DBG_KV_SCORE: *bytes = 4 * h * pl->g.nsrc[kK]; break;
+    case HTTM_DBG_Q_GROUP:
+    case HTTM_DBG_KV_GROUP:
+    case HTTM_DBG_DELTA:
+    case HTTM_DBG_Q_SLOT: *bytes = 4 * h * n; break;
+    case HTTM_DBG_OUTLIER: *bytes = h * n; break;
+    case HTTM_DBG_CU_Q: *bytes = 4 * (h + 1); break;
+    case HTTM_DBG_SELECT: *bytes = 16; break;
+    default: return fail(HTTM_ERR_INVALID_ARG, "unknown debug item");
+  }
+  return HTTM_OK;
+}
+
+httm_status httm_debug_read(const httm_plan* pl, const void* ws, int32_t item, void* host, size_t bytes,
+                            void* stream) {
+  size_t need = 0;
+  httm_status s = httm_debug_size(pl, item, &need);
+  if (s != HTTM_OK) return s;
+  if (!ws || !host) return fail(HTTM_ERR_INVALID_ARG, "NULL buffer");
+  if (bytes < need) return fail(HTTM_ERR_WORKSPACE, "host buffer too small");
+  const Layout& L = pl->L;
+  const char* base = reinterpret_cast<const char*>(ws);
+  const char* idx = base + L.index.off;
+  const char* src = nullptr;
+  switch (item) {
+    case HTTM_DBG_Q_MATCH: src = base + L.match[kQ].off; break;
+    case HTTM_DBG_Q_SCORE: src = base + L.score[kQ].off; break;
+    case HTTM_DBG_KV_MATCH: src = base + L.match[kK].off; break;
+    case HTTM_DBG_KV_SCORE: src = base + L.score[kK].off; break;
+    case HTTM_DBG_Q_GROUP: src = base + L.q_group.off; break;
+    case HTTM_DBG_KV_GROUP: src = base + L.k_group.off; break;
+    case HTTM_DBG_DELTA: src = base + L.delta.off; break;
+    case HTTM_DBG_OUTLIER: src = base + L.mask.off; break;
+    case HTTM_DBG_Q_SLOT: src = idx + pl->I.slot.off; break;
+    case HTTM_DBG_CU_Q: src = idx + pl->I.cu_q.off; break;
+    case HTTM_DBG_SELECT: src = base + L.radix.off + 4 * 3 * 2048; break;
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  CHECK_LAUNCH(hipMemcpyAsync(host, src, need, hipMemcpyDeviceToHost, st));
+  CHECK_LAUNCH(hipStreamSynchronize(st));
+  return HTTM_OK;
+}
+
+httm_status httm_set_timing(int32_t enable) {
+  if (enable && !g_timing.created) {
+    for (int i = 0; i < 2 * HTTM_T_COUNT; ++i)
+      if (hipEventCreate(&g_timing.ev[i]) != hipSuccess) return fail(HTTM_ERR_DEVICE, "hipEventCreate failed");
+    g_timing.created = true;
+  }
+  g_timing.enabled = enable != 0;
+  return HTTM_OK;
+}
+
+httm_status httm_get_timing(float* ms, int32_t n) {
+  if (!ms || n < 0) return fail(HTTM_ERR_INVALID_ARG, "bad arguments");
+  if (!g_timing.created) return fail(HTTM_ERR_INVALID_ARG, "timing was never enabled");
+  for (int i = 0; i < n && i < HTTM_T_COUNT; ++i) {
+    ms[i] = 0.f;
+    if (!g_timing.used[i]) continue;
+    if (hipEventSynchronize(g_timing.ev[2 * i + 1]) != hipSuccess) return fail(HTTM_ERR_DEVICE, "event sync failed");
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]) != hipSuccess)
+      return fail(HTTM_ERR_DEVICE, "event timing failed");
+    ms[i] = t;
+  }
+  return HTTM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,469 @@
+// Memory-bound kernels of the layer: mean merge, query deviation, outlier
+// restore, cached-index merge, unmerge, and the V transpose of the unmerged
+// baseline.
+//
+// "HTTM: Head-wise Temporal Token Merging for Faster VGGT", key design 1: a
+// merged token is the mean of its members, V follows K's groups, unmerge
+// copies the merged output back to every member.  Key design 3: every
+// query's L2 deviation to its merged token; outliers are subtracted from
+// their merged token and restored as separate tokens.  "LiteVGGT", key
+// design 3: x_d_up = (x_d + sum_{s in S_d} x_s) / (1 + |S_d|); cached merge
+// indices are reused by later layers.
+//
+// All reductions are gathers over a CSR member list (no float atomics):
+// sums run in member order (ascending token id) with explicitly rounded fp32
+// operations, so results are deterministic and a mean or deviation equals
+// the same sequence of IEEE operations written in any other language.
+#include "common.h"
+#include "kernels.h"
+
+namespace httm {
+
+namespace {
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* x) { Row8<T>::load(p, x); }
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float* x) { Row8<T>::store(p, x); }
+
+// Merged K and V.  One workgroup = 64 consecutive key slots of one head;
+// 8 lanes per slot, 8 channels per lane.  K~ rows are written directly; V~
+// means go through LDS and are written transposed (vt[h][c][slot]) so that
+// the attention kernel reads V~ along keys with plain row loads.
+template <typename T>
+__global__ __launch_bounds__(256) void merge_kv(int N, int lk, int lk_pad, const T* __restrict__ k,
+                                                const T* __restrict__ v,
+                                                const int32_t* __restrict__ members,
+                                                const int32_t* __restrict__ off, T* __restrict__ kt,
+                                                T* __restrict__ vt) {
+  __shared__ float sV[kD][65];
+  const int tiles = lk_pad / 64;
+  const int head = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int sub = lane >> 3, part = lane & 7;
+  const T* K = k + (size_t)head * N * kD;
+  const T* V = v + (size_t)head * N * kD;
+  const int32_t* mem = members + (size_t)head * N;
+  const int32_t* of = off + (size_t)head * (lk + 1);
+#pragma unroll
+  for (int round = 0; round < 2; ++round) {
+    const int ls = wave * 16 + round * 8 + sub;
+    const int slot = tile * 64 + ls;
+    float km[8], vm[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) km[e] = vm[e] = 0.f;
+    if (slot < lk) {
+      const int m0 = of[slot], m1 = of[slot + 1];
+      for (int m = m0; m < m1; ++m) {
+        const int tok = mem[m];
+        float xk[8], xv[8];
+        load8(K + (size_t)tok * kD + part * 8, xk);
+        load8(V + (size_t)tok * kD + part * 8, xv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          km[e] = __fadd_rn(km[e], xk[e]);
+          vm[e] = __fadd_rn(vm[e], xv[e]);
+        }
+      }
+      const float cnt = (float)(m1 - m0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        km[e] = __fdiv_rn(km[e], cnt);
+        vm[e] = __fdiv_rn(vm[e], cnt);
+      }
+    }
+    store8(kt + ((size_t)head * lk_pad + slot) * kD + part * 8, km);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sV[part * 8 + e][ls] = vm[e];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < kD * 8; idx += 256) {
+    const int c = idx >> 3, j = idx & 7;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = sV[c][j * 8 + e];
+    store8(vt + ((size_t)head * kD + c) * lk_pad + tile * 64 + j * 8, x);
+  }
+}
+
+// Query group sums and deviations.  One workgroup = 64 consecutive query
+// groups of one head.  Phase 1: 8 lanes per group sum the members (fp32,
+// member order) and keep the mean in LDS.  Phase 2: one lane per member
+// computes sqrt(sum_c (q_c - mean_c)^2), the sum over channels in ascending
+// order; members of the 64 groups are contiguous in the CSR, a binary search
+// over the 65 offsets finds each member's group.
+template <typename T>
+__global__ __launch_bounds__(256) void merge_q(int N, int gq, const T* __restrict__ q,
+                                               const int32_t* __restrict__ members,
+                                               const int32_t* __restrict__ off,
+                                               float* __restrict__ qsum,
+                                               float* __restrict__ delta) {
+  __shared__ float sMean[64][kD + 1];
+  __shared__ int sOff[65];
+  const int tiles = ceil_div(gq, 64);
+  const int head = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+  const int g0 = tile * 64;
+  const int ng = min(64, gq - g0);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int sub = lane >> 3, part = lane & 7;
+  const T* Q = q + (size_t)head * N * kD;
+  const int32_t* mem = members + (size_t)head * N;
+  const int32_t* of = off + (size_t)head * (gq + 1);
+  if (tid <= ng) sOff[tid] = of[g0 + tid];
+#pragma unroll
+  for (int round = 0; round < 2; ++round) {
+    const int ls = wave * 16 + round * 8 + sub;
+    if (ls < ng) {
+      const int grp = g0 + ls;
+      const int m0 = of[grp], m1 = of[grp + 1];
+      float sm[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm[e] = 0.f;
+      for (int m = m0; m < m1; ++m) {
+        float x[8];
+        load8(Q + (size_t)mem[m] * kD + part * 8, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm[e] = __fadd_rn(sm[e], x[e]);
+      }
+      Row8<float>::store(qsum + ((size_t)head * gq + grp) * kD + part * 8, sm);
+      const float cnt = (float)(m1 - m0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sMean[ls][part * 8 + e] = __fdiv_rn(sm[e], cnt);
+    }
+  }
+  __syncthreads();
+  const int mb = sOff[0], me = sOff[ng];
+  for (int m = mb + tid; m < me; m += 256) {
+    int lo = 0, hi = ng - 1;  // largest j with sOff[j] <= m
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sOff[mid] <= m) lo = mid; else hi = mid - 1;
+    }
+    const int tok = mem[m];
+    const T* row = Q + (size_t)tok * kD;
+    float acc = 0.f;
+#pragma unroll
+    for (int c8 = 0; c8 < 8; ++c8) {
+      float x[8];
+      load8(row + c8 * 8, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = __fsub_rn(x[e], sMean[lo][c8 * 8 + e]);
+        acc = __fadd_rn(acc, __fmul_rn(t, t));
+      }
+    }
+    delta[(size_t)head * N + tok] = __fsqrt_rn(acc);
+  }
+}
+
+// Exclusive scan of one value per thread over a 1024-thread block.
+__device__ int block_exclusive_scan(int v, int* sh /* >= 16 */, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+      const int t = sh[w];
+      sh[w] = acc;
+      acc += t;
+    }
+    sh[16] = acc;
+  }
+  __syncthreads();
+  total = sh[16];
+  return sh[wave] + x - v;
+}
+
+// Restore, part 1 (one workgroup per head): each initial query group g with
+// c members of which o are outliers yields (c > o) + o final slots; an
+// exclusive scan gives every group its first final slot; the head's final
+// length goes to lenq and closes the final offsets with N.
+__global__ __launch_bounds__(1024) void restore_scan(int N, int gq,
+                                                     const int32_t* __restrict__ members,
+                                                     const int32_t* __restrict__ off,
+                                                     const uint8_t* __restrict__ mask,
+                                                     int32_t* __restrict__ base,
+                                                     int32_t* __restrict__ lenq,
+                                                     int32_t* __restrict__ foff) {
+  __shared__ int sh[17];
+  const int head = blockIdx.x;
+  const int32_t* mem = members + (size_t)head * N;
+  const int32_t* of = off + (size_t)head * (gq + 1);
+  const uint8_t* mk = mask + (size_t)head * N;
+  int32_t* bs = base + (size_t)head * gq;
+  const int per = ceil_div(gq, 1024);
+  const int gb = threadIdx.x * per, ge = min(gq, gb + per);
+  int local = 0;
+  for (int g = gb; g < ge; ++g) {
+    const int m0 = of[g], m1 = of[g + 1];
+    int o = 0;
+    for (int m = m0; m < m1; ++m) o += mk[mem[m]];
+    const int n = ((m1 - m0) > o ? 1 : 0) + o;
+    bs[g] = n;
+    local += n;
+  }
+  int total;
+  int acc = block_exclusive_scan(local, sh, total);
+  for (int g = gb; g < ge; ++g) {
+    const int n = bs[g];
+    bs[g] = acc;
+    acc += n;
+  }
+  if (threadIdx.x == 0) {
+    lenq[head] = total;
+    foff[(size_t)head * (N + 1) + total] = N;
+  }
+}
+
+__device__ __forceinline__ int prefix_len(const int32_t* lenq, int head) {
+  int cu = 0;
+  for (int h = 0; h < head; ++h) cu += lenq[h];
+  return cu;
+}
+
+// Restore, part 2: 8 lanes per initial query group.  Outlier members are
+// subtracted from the group sum and copied to their own rows; the remaining
+// members' mean becomes the group's row (if any remain).  Writes the packed
+// Q~ rows, the final partition (members reordered: remaining first, then
+// outliers) and every token's packed row for unmerge.
+template <typename T>
+__global__ __launch_bounds__(256) void restore_rows(int heads, int N, int gq, const T* __restrict__ q,
+                                                    const int32_t* __restrict__ members,
+                                                    const int32_t* __restrict__ off,
+                                                    const float* __restrict__ qsum,
+                                                    const uint8_t* __restrict__ mask,
+                                                    const int32_t* __restrict__ base,
+                                                    const int32_t* __restrict__ lenq,
+                                                    int32_t* __restrict__ cu_q, T* __restrict__ qt,
+                                                    int32_t* __restrict__ fmembers,
+                                                    int32_t* __restrict__ foff,
+                                                    int32_t* __restrict__ slot) {
+  const int tiles = ceil_div(gq, 32);
+  const int head = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && tid <= heads) cu_q[tid] = prefix_len(lenq, tid);
+  const int g = tile * 32 + (tid >> 3), part = tid & 7;
+  if (g >= gq) return;
+  const int cu = prefix_len(lenq, head);
+  const T* Q = q + (size_t)head * N * kD;
+  const int32_t* mem = members + (size_t)head * N;
+  const uint8_t* mk = mask + (size_t)head * N;
+  const int32_t* of = off + (size_t)head * (gq + 1);
+  int32_t* fm = fmembers + (size_t)head * N;
+  int32_t* fo = foff + (size_t)head * (N + 1);
+  int32_t* sl = slot + (size_t)head * N;
+  const int m0 = of[g], m1 = of[g + 1];
+  int o = 0;
+  for (int m = m0; m < m1; ++m) o += mk[mem[m]];
+  const int nsurv = (m1 - m0) - o;
+  const int surv = nsurv > 0 ? 1 : 0;
+  const int b = cu + base[(size_t)head * gq + g];
+  float sm[8];
+  Row8<float>::load(qsum + ((size_t)head * gq + g) * kD + part * 8, sm);
+  int ro = 0, ri = 0;
+  for (int m = m0; m < m1; ++m) {
+    const int tok = mem[m];
+    if (mk[tok]) {
+      float x[8];
+      load8(Q + (size_t)tok * kD + part * 8, x);
+      if (surv) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm[e] = __fsub_rn(sm[e], x[e]);
+      }
+      const int row = b + surv + ro;
+      store8(qt + (size_t)row * kD + part * 8, x);
+      if (part == 0) {
+        fm[m0 + nsurv + ro] = tok;
+        fo[row - cu] = m0 + nsurv + ro;
+        sl[tok] = row;
+      }
+      ++ro;
+    } else {
+      if (part == 0) {
+        fm[m0 + ri] = tok;
+        sl[tok] = b;
+      }
+      ++ri;
+    }
+  }
+  if (surv) {
+    const float cnt = (float)nsurv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm[e] = __fdiv_rn(sm[e], cnt);
+    store8(qt + (size_t)b * kD + part * 8, sm);
+    if (part == 0) fo[b - cu] = m0;
+  }
+}
+
+// Cached layers: Q~ row R (packed over heads) = mean of the q rows of its
+// final members.  8 lanes per row.
+template <typename T>
+__global__ __launch_bounds__(256) void merge_q_cached(int heads, int N, const T* __restrict__ q,
+                                                      const int32_t* __restrict__ fmembers,
+                                                      const int32_t* __restrict__ foff,
+                                                      const int32_t* __restrict__ lenq,
+                                                      T* __restrict__ qt) {
+  __shared__ int sCu[65];
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int h = 0; h < heads; ++h) {
+      sCu[h] = acc;
+      acc += lenq[h];
+    }
+    sCu[heads] = acc;
+  }
+  __syncthreads();
+  const int R = blockIdx.x * 32 + (threadIdx.x >> 3), part = threadIdx.x & 7;
+  if (R >= sCu[heads]) return;
+  int head = 0;
+  while (sCu[head + 1] <= R) ++head;
+  const int sidx = R - sCu[head];
+  const int32_t* fo = foff + (size_t)head * (N + 1);
+  const int32_t* fm = fmembers + (size_t)head * N;
+  const T* Q = q + (size_t)head * N * kD;
+  const int m0 = fo[sidx], m1 = fo[sidx + 1];
+  float sm[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sm[e] = 0.f;
+  for (int m = m0; m < m1; ++m) {
+    float x[8];
+    load8(Q + (size_t)fm[m] * kD + part * 8, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm[e] = __fadd_rn(sm[e], x[e]);
+  }
+  const float cnt = (float)(m1 - m0);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sm[e] = __fdiv_rn(sm[e], cnt);
+  store8(qt + (size_t)R * kD + part * 8, sm);
+}
+
+// out[h][n][:] = o[slot[h][n]][:], 8 channels per thread (16 B for bf16).
+template <typename T>
+__global__ __launch_bounds__(256) void unmerge(int64_t rows, const int32_t* __restrict__ slot,
+                                               const T* __restrict__ o, T* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = idx >> 3;
+  const int part = (int)(idx & 7);
+  if (row >= rows) return;
+  const T* src = o + (size_t)slot[row] * kD + part * 8;
+  T* dst = out + (size_t)row * kD + part * 8;
+  if (sizeof(T) == 2) {
+    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+  } else {
+    reinterpret_cast<f32x4*>(dst)[0] = reinterpret_cast<const f32x4*>(src)[0];
+    reinterpret_cast<f32x4*>(dst)[1] = reinterpret_cast<const f32x4*>(src)[1];
+  }
+}
+
+// vt[h][c][n] = v[h][n][c] for n < N, 0 for N <= n < pitch.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_v(int N, int pitch, const T* __restrict__ v,
+                                                   T* __restrict__ vt) {
+  __shared__ float sT[kD][65];
+  const int tiles = pitch / 64;
+  const int head = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+  const T* V = v + (size_t)head * N * kD;
+  for (int idx = threadIdx.x; idx < 64 * 8; idx += 256) {
+    const int r = idx >> 3, j = idx & 7;
+    const int n = tile * 64 + r;
+    float x[8];
+    if (n < N) {
+      load8(V + (size_t)n * kD + j * 8, x);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sT[j * 8 + e][r] = x[e];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 64 * 8; idx += 256) {
+    const int c = idx >> 3, j = idx & 7;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = sT[c][j * 8 + e];
+    store8(vt + ((size_t)head * kD + c) * pitch + tile * 64 + j * 8, x);
+  }
+}
+
+}  // namespace
+
+#define HTTM_DISPATCH(dtype, ...)                  \
+  do {                                             \
+    if ((dtype) == 1) {                            \
+      typedef uint16_t T;                          \
+      __VA_ARGS__;                                 \
+    } else {                                       \
+      typedef float T;                             \
+      __VA_ARGS__;                                 \
+    }                                              \
+  } while (0)
+
+hipError_t launch_merge_kv(int dtype, int heads, int N, int lk, int lk_pad, const void* k,
+                           const void* v, const int32_t* members, const int32_t* off, void* kt,
+                           void* vt, hipStream_t stream) {
+  const int grid = heads * (lk_pad / 64);
+  HTTM_DISPATCH(dtype, hipLaunchKernelGGL(merge_kv<T>, dim3(grid), dim3(256), 0, stream, N, lk,
+                                          lk_pad, (const T*)k, (const T*)v, members, off, (T*)kt,
+                                          (T*)vt));
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_q(int dtype, int heads, int N, int gq, const void* q,
+                          const int32_t* members, const int32_t* off, float* qsum, float* delta,
+                          hipStream_t stream) {
+  const int grid = heads * ceil_div(gq, 64);
+  HTTM_DISPATCH(dtype, hipLaunchKernelGGL(merge_q<T>, dim3(grid), dim3(256), 0, stream, N, gq,
+                                          (const T*)q, members, off, qsum, delta));
+  return hipGetLastError();
+}
+
+hipError_t launch_restore(int dtype, int heads, int N, int gq, const void* q,
+                          const int32_t* members, const int32_t* off, const float* qsum,
+                          const uint8_t* mask, RestoreOut o, hipStream_t stream) {
+  hipLaunchKernelGGL(restore_scan, dim3(heads), dim3(1024), 0, stream, N, gq, members, off, mask,
+                     o.base, o.lenq, o.foff);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int grid = heads * ceil_div(gq, 32);
+  HTTM_DISPATCH(dtype, hipLaunchKernelGGL(restore_rows<T>, dim3(grid), dim3(256), 0, stream,
+                                          heads, N, gq, (const T*)q, members, off, qsum, mask,
+                                          o.base, o.lenq, o.cu_q, (T*)o.qt, o.fmembers, o.foff,
+                                          o.slot));
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_q_cached(int dtype, int heads, int N, int64_t q_capacity, const void* q,
+                                 const int32_t* fmembers, const int32_t* foff,
+                                 const int32_t* lenq, void* qt, hipStream_t stream) {
+  const int grid = (int)((q_capacity + 31) / 32);
+  HTTM_DISPATCH(dtype, hipLaunchKernelGGL(merge_q_cached<T>, dim3(grid), dim3(256), 0, stream,
+                                          heads, N, (const T*)q, fmembers, foff, lenq, (T*)qt));
+  return hipGetLastError();
+}
+
+hipError_t launch_unmerge(int dtype, int heads, int N, const int32_t* slot, const void* o,
+                          void* out, hipStream_t stream) {
+  const int64_t rows = (int64_t)heads * N;
+  const int grid = (int)((rows * 8 + 255) / 256);
+  HTTM_DISPATCH(dtype, hipLaunchKernelGGL(unmerge<T>, dim3(grid), dim3(256), 0, stream, rows,
+                                          slot, (const T*)o, (T*)out));
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_v(int dtype, int heads, int N, int pitch, const void* v, void* vt,
+                              hipStream_t stream) {
+  const int grid = heads * (pitch / 64);
+  HTTM_DISPATCH(dtype, hipLaunchKernelGGL(transpose_v<T>, dim3(grid), dim3(256), 0, stream, N,
+                                          pitch, (const T*)v, (T*)vt));
+  return hipGetLastError();
+}
+
+}  // namespace httm

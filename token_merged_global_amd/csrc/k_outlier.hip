@@ -1,0 +1,293 @@
+// Cross-head adaptive outlier selection.
+//
+// "HTTM: Head-wise Temporal Token Merging for Faster VGGT", key design 3: over
+// all heads and tokens, the top-d % largest query deviations are outliers
+// (mask M_o in {0,1}^{h x N}).  Ties go to the smaller flat index h*N + n.
+//
+// Deviations are non-negative floats, so their bit patterns order like their
+// values.  A radix select finds the threshold pattern T = the k_o-th largest
+// in three histogram passes (11, 11, 10 bits); every workgroup recomputes the
+// prefix it needs from the previous histogram in LDS, so no serial "find the
+// bin" kernel sits between the passes.  A marking pass sets values above T and
+// counts values equal to T per chunk; a last pass gives the equal values
+// their rank in flat-index order and keeps the first ones the budget allows.
+// Counts are integer atomics only, so the mask is deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace httm {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPerThread = 16;
+constexpr int kChunk = kThreads * kPerThread;  // elements per workgroup
+constexpr int kBins = 2048;
+
+struct Scratch {
+  uint32_t* h0;   // [2048] bits 31..21
+  uint32_t* h1;   // [2048] bits 20..10 under prefix B0
+  uint32_t* h2;   // [2048] bits 9..0 under prefix (B0, B1)
+  uint32_t* sel;  // [4] threshold, count above, ties taken, k_o
+  uint32_t* ties; // [nchunks]
+};
+
+__device__ __forceinline__ Scratch scratch_of(uint32_t* s) {
+  Scratch r;
+  r.h0 = s;
+  r.h1 = s + kBins;
+  r.h2 = s + 2 * kBins;
+  r.sel = s + 3 * kBins;
+  r.ties = s + 3 * kBins + 4;
+  return r;
+}
+
+__global__ void zero_words(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+__global__ void fill_bytes(uint8_t* p, int64_t n, uint8_t v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// Find bin b with above(b) < k <= above(b) + hist[b], above(b) = sum of bins > b.
+// Writes b and k - above(b) to out[0], out[1].  nb = 2048 or 1024.
+__device__ void find_bin(const uint32_t* hist, int nb, uint32_t k, uint32_t* part, uint32_t* out) {
+  const int per = nb / kThreads;
+  const int t = threadIdx.x;
+  // thread t owns bins [nb - (t+1)*per, nb - t*per), i.e. thread 0 the top bins
+  const int hi = nb - t * per, lo = hi - per;
+  uint32_t s = 0;
+  for (int b = lo; b < hi; ++b) s += hist[b];
+  part[t] = s;
+  __syncthreads();
+  if (t == 0) {
+    uint32_t acc = 0;
+    for (int i = 0; i < kThreads; ++i) {
+      const uint32_t x = part[i];
+      part[i] = acc;  // count strictly above thread i's bins
+      acc += x;
+    }
+  }
+  __syncthreads();
+  const uint32_t above0 = part[t];
+  if (above0 < k && above0 + s >= k) {
+    uint32_t above = above0;
+    for (int b = hi - 1; b >= lo; --b) {
+      if (above + hist[b] >= k) {
+        out[0] = (uint32_t)b;
+        out[1] = k - above;
+        break;
+      }
+      above += hist[b];
+    }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void load_chunk(const float* d, int64_t total, int64_t base, uint32_t* u) {
+  const int64_t i0 = base + (int64_t)threadIdx.x * kPerThread;
+  if (i0 + kPerThread <= total) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(d + i0 + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[4 * q + e] = v[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e)
+      u[e] = (i0 + e < total) ? __float_as_uint(d[i0 + e]) : 0xFFFFFFFFu;  // sentinel: no bin
+  }
+}
+
+// pass 0..2: histogram of bits [shift, shift+width) among values whose higher
+// bits equal the prefix found from the previous histograms.
+template <int PASS>
+__global__ __launch_bounds__(kThreads) void radix_hist(const float* __restrict__ delta, int64_t total,
+                                                       uint32_t k_o, uint32_t* scratch) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t part[kThreads];
+  __shared__ uint32_t res[4];
+  Scratch s = scratch_of(scratch);
+  uint32_t prefix = 0;
+  if (PASS >= 1) {
+    for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = s.h0[i];
+    __syncthreads();
+    find_bin(hist, kBins, k_o, part, res);
+    prefix = res[0];
+    if (PASS == 2) {
+      const uint32_t k1 = res[1];
+      __syncthreads();
+      for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = s.h1[i];
+      __syncthreads();
+      find_bin(hist, kBins, k1, part, res);
+      prefix = (prefix << 11) | res[0];
+    }
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0;
+  __syncthreads();
+  uint32_t u[kPerThread];
+  load_chunk(delta, total, (int64_t)blockIdx.x * kChunk, u);
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    if (u[e] == 0xFFFFFFFFu) continue;
+    if (PASS == 0) {
+      atomicAdd(&hist[u[e] >> 21], 1u);
+    } else if (PASS == 1) {
+      if ((u[e] >> 21) == prefix) atomicAdd(&hist[(u[e] >> 10) & 0x7FFu], 1u);
+    } else {
+      if ((u[e] >> 10) == prefix) atomicAdd(&hist[u[e] & 0x3FFu], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* g = PASS == 0 ? s.h0 : (PASS == 1 ? s.h1 : s.h2);
+  for (int i = threadIdx.x; i < kBins; i += kThreads)
+    if (hist[i]) atomicAdd(&g[i], hist[i]);
+}
+
+__device__ void threshold(const Scratch& s, uint32_t k_o, uint32_t* hist, uint32_t* part,
+                          uint32_t* res, uint32_t& T, uint32_t& need) {
+  for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = s.h0[i];
+  __syncthreads();
+  find_bin(hist, kBins, k_o, part, res);
+  const uint32_t b0 = res[0], k1 = res[1];
+  __syncthreads();
+  for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = s.h1[i];
+  __syncthreads();
+  find_bin(hist, kBins, k1, part, res);
+  const uint32_t b1 = res[0], k2 = res[1];
+  __syncthreads();
+  for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = s.h2[i];
+  __syncthreads();
+  find_bin(hist, 1024, k2, part, res);
+  T = (b0 << 21) | (b1 << 10) | res[0];
+  need = res[1];
+  __syncthreads();
+}
+
+// Marks values above T; counts values equal to T in this chunk.
+__global__ __launch_bounds__(kThreads) void radix_mark(const float* __restrict__ delta, int64_t total,
+                                                       uint32_t k_o, uint32_t* scratch,
+                                                       uint8_t* __restrict__ mask) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t part[kThreads];
+  __shared__ uint32_t res[4];
+  __shared__ uint32_t cnt;
+  Scratch s = scratch_of(scratch);
+  uint32_t T, need;
+  threshold(s, k_o, hist, part, res, T, need);
+  if (threadIdx.x == 0) cnt = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    s.sel[0] = T;
+    s.sel[1] = k_o - need;
+    s.sel[2] = need;
+    s.sel[3] = k_o;
+  }
+  __syncthreads();
+  uint32_t u[kPerThread];
+  const int64_t i0 = (int64_t)blockIdx.x * kChunk + (int64_t)threadIdx.x * kPerThread;
+  load_chunk(delta, total, (int64_t)blockIdx.x * kChunk, u);
+  uint32_t eq = 0;
+  uint8_t m[kPerThread];
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const bool valid = u[e] != 0xFFFFFFFFu;
+    m[e] = (valid && u[e] > T) ? 1 : 0;
+    eq += (valid && u[e] == T) ? 1u : 0u;
+  }
+  if (i0 + kPerThread <= total) {
+    u32x4 w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = (uint32_t)m[4 * q] | ((uint32_t)m[4 * q + 1] << 8) | ((uint32_t)m[4 * q + 2] << 16) |
+             ((uint32_t)m[4 * q + 3] << 24);
+    *reinterpret_cast<u32x4*>(mask + i0) = w;
+  } else {
+    for (int e = 0; e < kPerThread; ++e)
+      if (i0 + e < total) mask[i0 + e] = m[e];
+  }
+  if (eq) atomicAdd(&cnt, eq);
+  __syncthreads();
+  if (threadIdx.x == 0) s.ties[blockIdx.x] = cnt;
+}
+
+// Values equal to T, in flat-index order, take the remaining budget.
+__global__ __launch_bounds__(kThreads) void radix_ties(const float* __restrict__ delta, int64_t total,
+                                                       uint32_t* scratch, uint8_t* __restrict__ mask) {
+  __shared__ uint32_t part[kThreads];
+  __shared__ uint32_t before;
+  Scratch s = scratch_of(scratch);
+  if (s.ties[blockIdx.x] == 0) return;
+  const uint32_t T = s.sel[0], need = s.sel[2];
+  // ties in earlier chunks
+  uint32_t acc = 0;
+  for (int c = threadIdx.x; c < (int)blockIdx.x; c += kThreads) acc += s.ties[c];
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int i = 0; i < kThreads; ++i) t += part[i];
+    before = t;
+  }
+  __syncthreads();
+  if (before >= need) return;
+  uint32_t u[kPerThread];
+  const int64_t i0 = (int64_t)blockIdx.x * kChunk + (int64_t)threadIdx.x * kPerThread;
+  load_chunk(delta, total, (int64_t)blockIdx.x * kChunk, u);
+  uint32_t eq = 0;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) eq += (u[e] == T && u[e] != 0xFFFFFFFFu) ? 1u : 0u;
+  __syncthreads();
+  part[threadIdx.x] = eq;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t a = before;
+    for (int i = 0; i < kThreads; ++i) {
+      const uint32_t x = part[i];
+      part[i] = a;
+      a += x;
+    }
+  }
+  __syncthreads();
+  uint32_t rank = part[threadIdx.x];
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    if (u[e] == T && u[e] != 0xFFFFFFFFu) {
+      if (rank < need) mask[i0 + e] = 1;
+      ++rank;
+    }
+  }
+}
+
+}  // namespace
+
+size_t outlier_scratch_words(int64_t total) {
+  return 3 * kBins + 4 + (size_t)((total + kChunk - 1) / kChunk);
+}
+
+hipError_t launch_outliers(const float* delta, int64_t total, int64_t k_o, uint8_t* mask,
+                           uint32_t* scratch, hipStream_t stream) {
+  if (k_o <= 0 || k_o >= total) {
+    const uint8_t v = k_o <= 0 ? 0 : 1;
+    hipLaunchKernelGGL(fill_bytes, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, mask,
+                       total, v);
+    return hipGetLastError();
+  }
+  const int nchunks = (int)((total + kChunk - 1) / kChunk);
+  const int zw = 3 * kBins + 4;
+  hipLaunchKernelGGL(zero_words, dim3((zw + 255) / 256), dim3(256), 0, stream, scratch, zw);
+  const uint32_t k = (uint32_t)k_o;
+  hipLaunchKernelGGL(radix_hist<0>, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch);
+  hipLaunchKernelGGL(radix_hist<1>, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch);
+  hipLaunchKernelGGL(radix_hist<2>, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch);
+  hipLaunchKernelGGL(radix_mark, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch,
+                     mask);
+  hipLaunchKernelGGL(radix_ties, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, scratch, mask);
+  return hipGetLastError();
+}
+
+}  // namespace httm

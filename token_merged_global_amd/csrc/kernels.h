@@ -1,0 +1,84 @@
+// Host-side launchers of the HIP kernels.  Each enqueues on `stream` and
+// returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "geo.h"
+
+namespace httm {
+
+// Index arrays of one stream's merge partition, per head:
+//   members [h][N]      token ids grouped by slot (ascending inside a slot)
+//   off     [h][L+1]    slot -> first member
+//   group   [h][N]      token -> slot
+struct Csr {
+  int32_t* members;
+  int32_t* off;
+  int32_t* group;
+};
+
+hipError_t launch_sim(const Geo& g, int dtype, const void* q, const void* k, int32_t* match_q,
+                      float* score_q, int32_t* match_k, float* score_k, hipStream_t stream);
+
+hipError_t launch_select(const Geo& g, const int32_t* match_q, const float* score_q,
+                         const int32_t* match_k, const float* score_k, Csr q, Csr k,
+                         hipStream_t stream);
+
+// Means of K and V over the key partition: kt [h][lk_pad][64], vt [h][64][lk_pad].
+hipError_t launch_merge_kv(int dtype, int heads, int N, int lk, int lk_pad, const void* k,
+                           const void* v, const int32_t* members, const int32_t* off, void* kt,
+                           void* vt, hipStream_t stream);
+
+// Query group sums (fp32) and deviation of every query to its group mean.
+hipError_t launch_merge_q(int dtype, int heads, int N, int gq, const void* q,
+                          const int32_t* members, const int32_t* off, float* qsum, float* delta,
+                          hipStream_t stream);
+
+// Global top-k_o of delta [h*N] -> mask; scratch: 3*2048 + 4 + nchunks words.
+size_t outlier_scratch_words(int64_t total);
+hipError_t launch_outliers(const float* delta, int64_t total, int64_t k_o, uint8_t* mask,
+                           uint32_t* scratch, hipStream_t stream);
+
+// Outlier restore: packed Q~ rows, per-head lengths, final partition.
+struct RestoreOut {
+  void* qt;            // [q_capacity][64]
+  int32_t* lenq;       // [h]
+  int32_t* cu_q;       // [h+1]
+  int32_t* base;       // [h][gq] scratch
+  int32_t* fmembers;   // [h][N]
+  int32_t* foff;       // [h][N+1]
+  int32_t* slot;       // [h][N] packed row per token
+};
+hipError_t launch_restore(int dtype, int heads, int N, int gq, const void* q,
+                          const int32_t* members, const int32_t* off, const float* qsum,
+                          const uint8_t* mask, RestoreOut o, hipStream_t stream);
+
+// Cached mode: Q~ rows as means over the final query partition.
+hipError_t launch_merge_q_cached(int dtype, int heads, int N, int64_t q_capacity, const void* q,
+                                 const int32_t* fmembers, const int32_t* foff,
+                                 const int32_t* lenq, void* qt, hipStream_t stream);
+
+// Ragged attention: o[row] = softmax(scale q[row] k_h^T) v_h for the packed
+// rows of every head; lenq == nullptr means every head has `lq_uniform` rows.
+struct AttnShape {
+  int heads;
+  int lk;          // keys per head
+  int k_rows;      // rows per head in the key buffer (>= lk)
+  int vt_pitch;    // keys per row of vt (multiple of 64, >= lk)
+  int lq_uniform;  // used when lenq == nullptr
+  int64_t q_capacity;
+  float scale;
+};
+hipError_t launch_attention(int dtype, const AttnShape& s, const void* q, const void* k,
+                            const void* vt, const int32_t* lenq, void* o, hipStream_t stream);
+
+// out[h][n] = o[slot[h][n]]
+hipError_t launch_unmerge(int dtype, int heads, int N, const int32_t* slot, const void* o,
+                          void* out, hipStream_t stream);
+
+// vt[h][c][n] = v[h][n][c], zero for n in [N, pitch)
+hipError_t launch_transpose_v(int dtype, int heads, int N, int pitch, const void* v, void* vt,
+                              hipStream_t stream);
+
+}  // namespace httm
