@@ -165,7 +165,9 @@ httm_status httm_attention_dense(const httm_plan* plan, void* ws, size_t ws_byte
 
 /* Intermediates of the last httm_layer on `ws`, for staged comparison with
  * an independent implementation.  Synchronises `stream` and copies to host
- * memory.  Layouts (per head h, all int32 unless noted):
+ * memory.  `index` is the index that call filled (NULL if it was given none):
+ * HTTM_DBG_Q_SLOT and HTTM_DBG_CU_Q are read from it.  Layouts (per head h,
+ * all int32 unless noted):
  *   HTTM_DBG_Q_MATCH / KV_MATCH: [h][src] matched destination as an original
  *       token id (sources ordered by block, then block position);
  *   HTTM_DBG_Q_SCORE / KV_SCORE: [h][src] float cosine of that match;
@@ -182,20 +184,23 @@ typedef enum {
   HTTM_DBG_Q_SLOT, HTTM_DBG_CU_Q, HTTM_DBG_SELECT, HTTM_DBG_COUNT
 } httm_debug_item;
 httm_status httm_debug_size(const httm_plan* plan, int32_t item, size_t* bytes);
-httm_status httm_debug_read(const httm_plan* plan, const void* ws, int32_t item,
-                            void* host, size_t bytes, void* stream);
+httm_status httm_debug_read(const httm_plan* plan, const void* ws, const httm_index* index,
+                            int32_t item, void* host, size_t bytes, void* stream);
 
-/* Launch timing of the last httm_layer / httm_layer_cached / dense call made
- * with timing enabled: per kernel stage, milliseconds between HIP events
- * recorded on the call's stream around that stage.  httm_set_timing(1)
- * creates the events (host side; costs a little launch latency);
- * httm_get_timing synchronises on the last event. */
+/* Per-stage launch timing.  httm_set_timing(mask) records HIP events on the
+ * call's stream around every stage whose bit (1 << httm_timing_stage) is set,
+ * for the next calls of httm_layer / httm_layer_cached /
+ * httm_attention_dense (a ring of 32 calls; 0 turns recording off and every
+ * call resets the count).  httm_get_timing writes, per stage, the mean
+ * milliseconds between the events over the recorded calls that ran that
+ * stage (0 if none) and the number of recorded calls; it synchronises on
+ * the events.  Host-side state, not thread-safe. */
 typedef enum {
   HTTM_T_SIM = 0, HTTM_T_SELECT, HTTM_T_MERGE_KV, HTTM_T_MERGE_Q, HTTM_T_OUTLIER,
   HTTM_T_RESTORE, HTTM_T_ATTN, HTTM_T_UNMERGE, HTTM_T_COUNT
 } httm_timing_stage;
-httm_status httm_set_timing(int32_t enable);
-httm_status httm_get_timing(float* ms, int32_t n);
+httm_status httm_set_timing(int32_t stage_mask);
+httm_status httm_get_timing(float* ms, int32_t n, int32_t* calls);
 
 const char* httm_status_string(httm_status s);
 /* Last error detail recorded on this thread (empty if none). */

@@ -165,7 +165,7 @@ def test_cached_layer_matches_oracle_with_same_indices():
     ws = H.workspace(plan)
     out0, idx = H.layer(plan, *dev0, ws=ws, keep_index=True)
     torch.cuda.synchronize()
-    q_slot = H.debug_read(plan, ws, "q_slot").reshape(w.heads, -1)
+    q_slot = H.debug_read(plan, ws, "q_slot", index=idx).reshape(w.heads, -1)
     kv_group = H.debug_read(plan, ws, "kv_group").reshape(w.heads, -1)
     out1 = H.layer_cached(plan, idx, *dev1, ws=ws).float().cpu().numpy()
     qf = [staged.canonical(q_slot[h]) for h in range(w.heads)]

@@ -81,10 +81,11 @@ EXPORTS = {
                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p],
                              ctypes.c_int),
     "httm_debug_size": ([ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
-    "httm_debug_read": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
-                         ctypes.c_void_p], ctypes.c_int),
+    "httm_debug_read": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(Index), ctypes.c_int32, ctypes.c_void_p,
+                         ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "httm_set_timing": ([ctypes.c_int32], ctypes.c_int),
-    "httm_get_timing": ([ctypes.POINTER(ctypes.c_float), ctypes.c_int32], ctypes.c_int),
+    "httm_get_timing": ([ctypes.POINTER(ctypes.c_float), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)],
+                        ctypes.c_int),
     "httm_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "httm_last_error": ([], ctypes.c_char_p),
 }
@@ -252,8 +253,11 @@ def attention_dense(plan: Plan, q, k, v, ws=None, out=None, stream=None):
     return out
 
 
-def debug_read(plan: Plan, ws, item: str, stream=None):
-    """Copy one intermediate of the last ``layer`` on ``ws`` to a numpy array."""
+def debug_read(plan: Plan, ws, item: str, stream=None, index: Optional[CachedIndex] = None):
+    """Copy one intermediate of the last ``layer`` on ``ws`` to a numpy array.
+
+    Pass the ``index`` that call filled, if any (per-token slots live there).
+    """
     import numpy as np
     code = DEBUG_ITEMS.index(item)
     n = ctypes.c_size_t()
@@ -261,16 +265,23 @@ def debug_read(plan: Plan, ws, item: str, stream=None):
     dt = {"q_score": np.float32, "kv_score": np.float32, "delta": np.float32, "outlier": np.uint8,
           "select": np.uint32}.get(item, np.int32)
     arr = np.empty(n.value // np.dtype(dt).itemsize, dtype=dt)
-    _check(lib().httm_debug_read(plan.handle, ws.data_ptr(), code, arr.ctypes.data, arr.nbytes,
-                                 _stream_ptr(stream)))
+    _check(lib().httm_debug_read(plan.handle, ws.data_ptr(), ctypes.byref(index.c) if index is not None else None,
+                                 code, arr.ctypes.data, arr.nbytes, _stream_ptr(stream)))
     return arr
 
 
-def set_timing(enable: bool) -> None:
-    _check(lib().httm_set_timing(1 if enable else 0))
+def set_timing(stages=None) -> None:
+    """Record HIP events around the named stages of the next calls (None: all, []: off)."""
+    names = TIMING_STAGES if stages is None else list(stages)
+    mask = 0
+    for n in names:
+        mask |= 1 << TIMING_STAGES.index(n)
+    _check(lib().httm_set_timing(mask))
 
 
-def get_timing() -> Dict[str, float]:
+def get_timing() -> Tuple[Dict[str, float], int]:
+    """(mean ms per stage over the recorded calls, number of recorded calls)."""
     arr = (ctypes.c_float * len(TIMING_STAGES))()
-    _check(lib().httm_get_timing(arr, len(TIMING_STAGES)))
-    return {s: float(arr[i]) for i, s in enumerate(TIMING_STAGES)}
+    calls = ctypes.c_int32()
+    _check(lib().httm_get_timing(arr, len(TIMING_STAGES), ctypes.byref(calls)))
+    return {s: float(arr[i]) for i, s in enumerate(TIMING_STAGES)}, calls.value

@@ -23,6 +23,9 @@ ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled for all device code (see DESIGN notes on
 # the target); -O3 otherwise.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Sources whose arithmetic must be exactly the written sequence of rounded
+# operations (means and deviations compared bit for bit): no FMA contraction.
+PER_FILE = {"k_merge.hip": ["-ffp-contract=off"]}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
           "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
@@ -41,7 +44,8 @@ def sources():
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"]
-    cmd = [hipcc(), *lang, *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    extra = PER_FILE.get(os.path.basename(src), [])
+    cmd = [hipcc(), *lang, *COMMON, *DEVICE_FLAGS, *extra, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

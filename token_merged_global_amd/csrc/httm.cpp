@@ -244,25 +244,34 @@ P* at(void* base, const Region& r) {
 }
 
 // ---------------------------------------------------------------- timing
+// HIP events around selected stages, for up to kSlots consecutive calls.
+constexpr int kSlots = 32;
 struct Timing {
-  bool enabled = false;
-  hipEvent_t ev[2 * HTTM_T_COUNT] = {};
-  bool used[HTTM_T_COUNT] = {};
+  int32_t mask = 0;
   bool created = false;
+  int calls = 0;
+  hipEvent_t ev[kSlots][2 * HTTM_T_COUNT] = {};
+  bool used[kSlots][HTTM_T_COUNT] = {};
 };
 Timing g_timing;
 
 void stage_begin(int s, hipStream_t st) {
-  if (g_timing.enabled) {
-    (void)hipEventRecord(g_timing.ev[2 * s], st);
-    g_timing.used[s] = true;
+  if ((g_timing.mask >> s) & 1) {
+    const int slot = g_timing.calls % kSlots;
+    (void)hipEventRecord(g_timing.ev[slot][2 * s], st);
+    g_timing.used[slot][s] = true;
   }
 }
 void stage_end(int s, hipStream_t st) {
-  if (g_timing.enabled) (void)hipEventRecord(g_timing.ev[2 * s + 1], st);
+  if ((g_timing.mask >> s) & 1) (void)hipEventRecord(g_timing.ev[g_timing.calls % kSlots][2 * s + 1], st);
 }
-void timing_reset() {
-  for (int i = 0; i < HTTM_T_COUNT; ++i) g_timing.used[i] = false;
+void timing_begin_call() {
+  if (!g_timing.mask) return;
+  const int slot = g_timing.calls % kSlots;
+  for (int i = 0; i < HTTM_T_COUNT; ++i) g_timing.used[slot][i] = false;
+}
+void timing_end_call() {
+  if (g_timing.mask) ++g_timing.calls;
 }
 
 #define CHECK_LAUNCH(expr)                                                        \
@@ -396,7 +405,7 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
   const IndexLayout& I = pl->I;
   const int dt = pl->p.dtype;
   char* idx = index ? reinterpret_cast<char*>(index->dev) : at<char>(ws, L.index);
-  timing_reset();
+  timing_begin_call();
 
   stage_begin(HTTM_T_SIM, st);
   CHECK_LAUNCH(launch_sim(g, dt, q, k, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
@@ -445,6 +454,7 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
     index->plan_id = pl->id;
     index->valid = 1;
   }
+  timing_end_call();
   return HTTM_OK;
 }
 
@@ -461,7 +471,7 @@ httm_status httm_layer_cached(const httm_plan* pl, void* ws, size_t ws_bytes, co
   const IndexLayout& I = pl->I;
   const int dt = pl->p.dtype;
   char* idx = reinterpret_cast<char*>(index->dev);
-  timing_reset();
+  timing_begin_call();
   stage_begin(HTTM_T_MERGE_KV, st);
   CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, k, v,
                                reinterpret_cast<const int32_t*>(idx + I.k_members.off),
@@ -475,7 +485,9 @@ httm_status httm_layer_cached(const httm_plan* pl, void* ws, size_t ws_bytes, co
                                      reinterpret_cast<const int32_t*>(idx + I.lenq.off),
                                      at<void>(ws, pl->L.qt), st));
   stage_end(HTTM_T_MERGE_Q, st);
-  return attend_unmerge(pl, ws, idx, at<void>(ws, pl->L.qt), out, st);
+  s = attend_unmerge(pl, ws, idx, at<void>(ws, pl->L.qt), out, st);
+  if (s == HTTM_OK) timing_end_call();
+  return s;
 }
 
 httm_status httm_attention_dense(const httm_plan* pl, void* ws, size_t ws_bytes, const void* q,
@@ -486,7 +498,7 @@ httm_status httm_attention_dense(const httm_plan* pl, void* ws, size_t ws_bytes,
   const Geo& g = pl->g;
   const int dt = pl->p.dtype;
   const int pitch = ceil_div(g.N, 64) * 64;
-  timing_reset();
+  timing_begin_call();
   stage_begin(HTTM_T_MERGE_KV, st);
   CHECK_LAUNCH(launch_transpose_v(dt, g.heads, g.N, pitch, v, ws, st));
   stage_end(HTTM_T_MERGE_KV, st);
@@ -501,6 +513,7 @@ httm_status httm_attention_dense(const httm_plan* pl, void* ws, size_t ws_bytes,
   stage_begin(HTTM_T_ATTN, st);
   CHECK_LAUNCH(launch_attention(dt, a, q, k, ws, nullptr, out, st));
   stage_end(HTTM_T_ATTN, st);
+  timing_end_call();
   return HTTM_OK;
 }
 
@@ -524,8 +537,8 @@ httm_status httm_debug_size(const httm_plan* pl, int32_t item, size_t* bytes) {
   return HTTM_OK;
 }
 
-httm_status httm_debug_read(const httm_plan* pl, const void* ws, int32_t item, void* host, size_t bytes,
-                            void* stream) {
+httm_status httm_debug_read(const httm_plan* pl, const void* ws, const httm_index* index, int32_t item,
+                            void* host, size_t bytes, void* stream) {
   size_t need = 0;
   httm_status s = httm_debug_size(pl, item, &need);
   if (s != HTTM_OK) return s;
@@ -533,7 +546,9 @@ httm_status httm_debug_read(const httm_plan* pl, const void* ws, int32_t item, v
   if (bytes < need) return fail(HTTM_ERR_WORKSPACE, "host buffer too small");
   const Layout& L = pl->L;
   const char* base = reinterpret_cast<const char*>(ws);
-  const char* idx = base + L.index.off;
+  if (index && (!index->dev || index->plan_id != pl->id))
+    return fail(HTTM_ERR_INDEX_MISMATCH, "index was not filled with this plan");
+  const char* idx = index ? reinterpret_cast<const char*>(index->dev) : base + L.index.off;
   const char* src = nullptr;
   switch (item) {
     case HTTM_DBG_Q_MATCH: src = base + L.match[kQ].off; break;
@@ -554,27 +569,38 @@ httm_status httm_debug_read(const httm_plan* pl, const void* ws, int32_t item, v
   return HTTM_OK;
 }
 
-httm_status httm_set_timing(int32_t enable) {
-  if (enable && !g_timing.created) {
-    for (int i = 0; i < 2 * HTTM_T_COUNT; ++i)
-      if (hipEventCreate(&g_timing.ev[i]) != hipSuccess) return fail(HTTM_ERR_DEVICE, "hipEventCreate failed");
+httm_status httm_set_timing(int32_t stage_mask) {
+  if (stage_mask && !g_timing.created) {
+    for (int k = 0; k < kSlots; ++k)
+      for (int i = 0; i < 2 * HTTM_T_COUNT; ++i)
+        if (hipEventCreate(&g_timing.ev[k][i]) != hipSuccess) return fail(HTTM_ERR_DEVICE, "hipEventCreate failed");
     g_timing.created = true;
   }
-  g_timing.enabled = enable != 0;
+  g_timing.mask = stage_mask & ((1 << HTTM_T_COUNT) - 1);
+  g_timing.calls = 0;
+  for (int k = 0; k < kSlots; ++k)
+    for (int i = 0; i < HTTM_T_COUNT; ++i) g_timing.used[k][i] = false;
   return HTTM_OK;
 }
 
-httm_status httm_get_timing(float* ms, int32_t n) {
+httm_status httm_get_timing(float* ms, int32_t n, int32_t* calls) {
   if (!ms || n < 0) return fail(HTTM_ERR_INVALID_ARG, "bad arguments");
   if (!g_timing.created) return fail(HTTM_ERR_INVALID_ARG, "timing was never enabled");
+  const int nc = g_timing.calls < kSlots ? g_timing.calls : kSlots;
+  if (calls) *calls = nc;
   for (int i = 0; i < n && i < HTTM_T_COUNT; ++i) {
-    ms[i] = 0.f;
-    if (!g_timing.used[i]) continue;
-    if (hipEventSynchronize(g_timing.ev[2 * i + 1]) != hipSuccess) return fail(HTTM_ERR_DEVICE, "event sync failed");
-    float t = 0.f;
-    if (hipEventElapsedTime(&t, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]) != hipSuccess)
-      return fail(HTTM_ERR_DEVICE, "event timing failed");
-    ms[i] = t;
+    double sum = 0.0;
+    int cnt = 0;
+    for (int k = 0; k < nc; ++k) {
+      if (!g_timing.used[k][i]) continue;
+      if (hipEventSynchronize(g_timing.ev[k][2 * i + 1]) != hipSuccess) return fail(HTTM_ERR_DEVICE, "event sync failed");
+      float t = 0.f;
+      if (hipEventElapsedTime(&t, g_timing.ev[k][2 * i], g_timing.ev[k][2 * i + 1]) != hipSuccess)
+        return fail(HTTM_ERR_DEVICE, "event timing failed");
+      sum += t;
+      ++cnt;
+    }
+    ms[i] = cnt ? (float)(sum / cnt) : 0.f;
   }
   return HTTM_OK;
 }

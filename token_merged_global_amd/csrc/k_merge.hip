@@ -11,15 +11,22 @@
 // indices are reused by later layers.
 //
 // All reductions are gathers over a CSR member list (no float atomics):
-// sums run in member order (ascending token id) with explicitly rounded fp32
+// sums run in member order (ascending token id) with separately rounded fp32
 // operations, so results are deterministic and a mean or deviation equals
-// the same sequence of IEEE operations written in any other language.
+// the same sequence of IEEE operations written in any other language.  This
+// file is compiled with -ffp-contract=off so that no add and multiply are
+// fused into an FMA (the rounding helpers are inlined from headers, where a
+// pragma in this file would not reach).  Division and square root use the
+// plain operators, which HIP lowers to correctly rounded sequences
+// (__fsqrt_rn would be the approximate native square root).
 #include "common.h"
 #include "kernels.h"
 
 namespace httm {
 
 namespace {
+
+__device__ __forceinline__ float rn_div(float a, float b) { return a / b; }  // correctly rounded
 
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float* x) { Row8<T>::load(p, x); }
@@ -68,8 +75,8 @@ __global__ __launch_bounds__(256) void merge_kv(int N, int lk, int lk_pad, const
       const float cnt = (float)(m1 - m0);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        km[e] = __fdiv_rn(km[e], cnt);
-        vm[e] = __fdiv_rn(vm[e], cnt);
+        km[e] = rn_div(km[e], cnt);
+        vm[e] = rn_div(vm[e], cnt);
       }
     }
     store8(kt + ((size_t)head * lk_pad + slot) * kD + part * 8, km);
@@ -128,7 +135,7 @@ __global__ __launch_bounds__(256) void merge_q(int N, int gq, const T* __restric
       Row8<float>::store(qsum + ((size_t)head * gq + grp) * kD + part * 8, sm);
       const float cnt = (float)(m1 - m0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sMean[ls][part * 8 + e] = __fdiv_rn(sm[e], cnt);
+      for (int e = 0; e < 8; ++e) sMean[ls][part * 8 + e] = rn_div(sm[e], cnt);
     }
   }
   __syncthreads();
@@ -152,7 +159,7 @@ __global__ __launch_bounds__(256) void merge_q(int N, int gq, const T* __restric
         acc = __fadd_rn(acc, __fmul_rn(t, t));
       }
     }
-    delta[(size_t)head * N + tok] = __fsqrt_rn(acc);
+    delta[(size_t)head * N + tok] = sqrtf(acc);
   }
 }
 
@@ -296,7 +303,7 @@ __global__ __launch_bounds__(256) void restore_rows(int heads, int N, int gq, co
   if (surv) {
     const float cnt = (float)nsurv;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sm[e] = __fdiv_rn(sm[e], cnt);
+    for (int e = 0; e < 8; ++e) sm[e] = rn_div(sm[e], cnt);
     store8(qt + (size_t)b * kD + part * 8, sm);
     if (part == 0) fo[b - cu] = m0;
   }
@@ -340,7 +347,7 @@ __global__ __launch_bounds__(256) void merge_q_cached(int heads, int N, const T*
   }
   const float cnt = (float)(m1 - m0);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) sm[e] = __fdiv_rn(sm[e], cnt);
+  for (int e = 0; e < 8; ++e) sm[e] = rn_div(sm[e], cnt);
   store8(qt + (size_t)R * kD + part * 8, sm);
 }
 
