@@ -29,8 +29,10 @@ bf16 rounding of the fp32 master.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
 from dataclasses import dataclass, field, replace
-from typing import Dict, Iterable, List, Optional, Sequence, Tuple
+from typing import Dict, Iterable, Iterator, List, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -153,21 +155,65 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
+def default_workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def layer_inputs(w: Workload, seed: int = DEFAULT_SEED, layer: int = 0,
-                 heads: Optional[Iterable[int]] = None) -> Dict[str, np.ndarray]:
+                 heads: Optional[Iterable[int]] = None, workers: int = 0) -> Dict[str, np.ndarray]:
     """q, k, v as fp32 arrays [len(heads)][N][d] holding the values both sides consume.
 
     For bf16 workloads the values are bf16-representable (already rounded).
+    Heads are drawn in parallel threads (each head has its own stream).
     """
     hs = list(range(w.heads)) if heads is None else list(heads)
-    out = {}
-    for t in TENSORS:
-        arr = np.empty((len(hs), w.n_tokens, w.d_head), dtype=np.float32)
-        for i, h in enumerate(hs):
-            x = head_tensor(w, t, h, seed=seed, layer=layer)
-            arr[i] = round_bf16(x) if w.dtype == "bf16" else x
-        out[t] = arr
+    out = {t: np.empty((len(hs), w.n_tokens, w.d_head), dtype=np.float32) for t in TENSORS}
+
+    def one(job):
+        t, i, h = job
+        x = head_tensor(w, t, h, seed=seed, layer=layer)
+        out[t][i] = round_bf16(x) if w.dtype == "bf16" else x
+
+    jobs = [(t, i, h) for t in TENSORS for i, h in enumerate(hs)]
+    with cf.ThreadPoolExecutor(max_workers=workers or default_workers()) as ex:
+        list(ex.map(one, jobs))
     return out
+
+
+def layer_stack(w: Workload, seed: int = DEFAULT_SEED, heads: Optional[Iterable[int]] = None,
+                layers: Optional[int] = None, workers: int = 0) -> Iterator[Tuple[int, Dict[str, np.ndarray]]]:
+    """Successive layers (layer, inputs) of a stack: layer l adds N(0, 0.02^2) to l-1.
+
+    Keeps the fp32 masters of the listed heads and adds one noise draw per
+    layer, so layer l costs one draw instead of l (same values as
+    ``layer_inputs(w, seed, layer=l)``).
+    """
+    hs = list(range(w.heads)) if heads is None else list(heads)
+    n_layers = w.layers if layers is None else layers
+    master = {t: np.empty((len(hs), w.n_tokens, w.d_head), dtype=np.float32) for t in TENSORS}
+    pool = cf.ThreadPoolExecutor(max_workers=workers or default_workers())
+    try:
+        def base(job):
+            t, i, h = job
+            master[t][i] = head_tensor(w, t, h, seed=seed, layer=0)
+
+        jobs = [(t, i, h) for t in TENSORS for i, h in enumerate(hs)]
+        list(pool.map(base, jobs))
+        for l in range(n_layers):
+            if l > 0:
+                def step(job, l=l):
+                    t, i, h = job
+                    r = _stream(seed, w.cfg_id, l, TENSORS.index(t), h)
+                    master[t][i] += r.standard_normal(master[t][i].shape, dtype=np.float32) * np.float32(w.sigma_layer)
+
+                list(pool.map(step, jobs))
+            yield l, {t: (round_bf16(master[t]) if w.dtype == "bf16" else master[t].copy()) for t in TENSORS}
+    finally:
+        pool.shutdown()
 
 
 def oracle_heads(w: Workload, seed: int = DEFAULT_SEED, n: int = 2) -> List[int]:

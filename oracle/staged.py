@@ -17,6 +17,7 @@ on the implementation's own indices, so a counted near-tie never cascades:
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Sequence
 
@@ -125,14 +126,16 @@ def check_stream(x: np.ndarray, p: O.Params, ratio: float, stride: int, gpu_matc
 def check_layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, p: O.Params, gpu: Dict[str, np.ndarray],
                 out_gpu: np.ndarray, out_heads: Optional[Sequence[int]] = None,
                 rows: Optional[np.ndarray] = None, out_tol: Optional[float] = None,
-                match_heads: Optional[Sequence[int]] = None, rel_tol: Optional[float] = None) -> Report:
+                match_heads: Optional[Sequence[int]] = None, rel_tol: Optional[float] = None,
+                workers: int = 1) -> Report:
     """Staged parity of one layer.
 
     gpu: q_match, q_score, kv_match, kv_score ([h][src]), q_group, kv_group,
     q_slot ([h][N]), delta ([h][N] float32), outlier ([h][N] uint8).
     out_gpu: [h][N][d] as float64/float32.  Tolerance on the max-abs output
     error: ``rel_tol`` * RMS(oracle output) if given (bf16: 2e-2), else
-    ``out_tol`` (default 1e-4, fp32).
+    ``out_tol`` (default 1e-4, fp32).  ``workers`` threads share the per-head
+    work (numpy releases the GIL in its array kernels).
     """
     rep = Report()
     h, N = q.shape[0], q.shape[1]
@@ -140,17 +143,28 @@ def check_layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, p: O.Params, gpu: D
     nq, nk = gpu["q_match"].shape[1], gpu["kv_match"].shape[1]
     q_rep = [None] * h
     k_rep = [None] * h
-    for i in range(h):
+
+    def per_head(i):
+        r = Report()
         if i in mh:
-            q_rep[i] = check_stream(q[i], p, p.q_ratio, p.q_dst_stride, gpu["q_match"][i], gpu["q_score"][i],
-                                    gpu["q_group"][i], rep, f"head {i} Q")
-            k_rep[i] = check_stream(k[i], p, p.kv_ratio, p.kv_dst_stride, gpu["kv_match"][i],
-                                    gpu["kv_score"][i], gpu["kv_group"][i], rep, f"head {i} K")
+            qr = check_stream(q[i], p, p.q_ratio, p.q_dst_stride, gpu["q_match"][i], gpu["q_score"][i],
+                              gpu["q_group"][i], r, f"head {i} Q")
+            kr = check_stream(k[i], p, p.kv_ratio, p.kv_dst_stride, gpu["kv_match"][i],
+                              gpu["kv_score"][i], gpu["kv_group"][i], r, f"head {i} K")
         else:
-            q_rep[i] = canonical(gpu["q_group"][i])
-            k_rep[i] = canonical(gpu["kv_group"][i])
+            qr, kr = canonical(gpu["q_group"][i]), canonical(gpu["kv_group"][i])
+        return qr, kr, r
+
+    with cf.ThreadPoolExecutor(max_workers=max(1, workers)) as ex:
+        for i, (qr, kr, r) in enumerate(ex.map(per_head, range(h))):
+            q_rep[i], k_rep[i] = qr, kr
+            rep.n_src += r.n_src
+            rep.match_near_ties += r.match_near_ties
+            rep.select_near_ties += r.select_near_ties
+            rep.max_score_err = max(rep.max_score_err, r.max_score_err)
     # (iii) deviations on the implementation's query groups
-    delta_o = O.deviations(q, q_rep)
+    with cf.ThreadPoolExecutor(max_workers=max(1, workers)) as ex:
+        delta_o = np.stack(list(ex.map(lambda i: O.deviations(q[i:i + 1], [q_rep[i]])[0], range(h))))
     dg = gpu["delta"].astype(np.float32)
     rep.delta_nonexact = int((dg != delta_o).sum())
     rep.max_delta_err = float(np.abs(dg.astype(np.float64) - delta_o).max())

@@ -1,0 +1,47 @@
+"""Helpers shared by the GPU parity tests (marshalling only)."""
+import sys
+
+import numpy as np
+import torch
+
+import token_merged_global_amd as H
+
+BF16_REL = 2e-2  # outputs: max-abs error <= 2e-2 * RMS(oracle output) for bf16
+F32_ABS = 1e-4   # outputs: max-abs error <= 1e-4 for fp32
+PER_HEAD = ["q_match", "q_score", "kv_match", "kv_score", "q_group", "kv_group", "delta", "outlier", "q_slot"]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x: np.ndarray, dtype: str):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    t = t.to(torch.bfloat16) if dtype == "bf16" else t
+    return t.cuda()
+
+
+def read_all(plan, ws, heads, index=None):
+    gpu = {it: H.debug_read(plan, ws, it, index=index) for it in H.DEBUG_ITEMS}
+    for it in PER_HEAD:
+        gpu[it] = gpu[it].reshape(heads, -1)
+    return gpu
+
+
+def run_layer(w, inputs, keep_index=False, **plan_kw):
+    plan = H.Plan.from_workload(w, **plan_kw)
+    q, k, v = (to_dev(inputs[t], w.dtype) for t in "qkv")
+    ws = H.workspace(plan)
+    res = H.layer(plan, q, k, v, ws=ws, keep_index=keep_index)
+    out, idx = (res if keep_index else (res, None))
+    torch.cuda.synchronize()
+    gpu = read_all(plan, ws, w.heads, index=idx)
+    o = out.float().cpu().numpy()
+    del out
+    return plan, ws, (q, k, v), o, gpu, idx
+
+
+def sample_rows(n, count, seed):
+    rows = np.random.default_rng(seed).choice(n, count, replace=False)
+    return np.unique(np.r_[rows, [0, 1, n - 1]])

@@ -5,8 +5,6 @@ counted near-ties (|dsim| < 1e-5); outputs within 1e-4 max-abs for fp32 and
 within 2e-2 * RMS(oracle output) max-abs for bf16.  Deviations and outlier
 masks are checked bit-exactly on the GPU's own groups.
 """
-import sys
-
 import numpy as np
 import pytest
 import torch
@@ -18,19 +16,7 @@ import token_merged_global_amd as H
 
 pytestmark = pytest.mark.gpu
 
-BF16_REL = 2e-2
-F32_ABS = 1e-4
-
-
-def _say(*a):
-    print(*a, flush=True)
-    sys.stdout.flush()
-
-
-def to_dev(x: np.ndarray, dtype: str):
-    t = torch.from_numpy(np.ascontiguousarray(x))
-    t = t.to(torch.bfloat16) if dtype == "bf16" else t
-    return t.cuda()
+from gpu_util import BF16_REL, F32_ABS, read_all, say as _say, to_dev
 
 
 def run_layer(w, inputs, **plan_kw):
@@ -39,11 +25,7 @@ def run_layer(w, inputs, **plan_kw):
     ws = H.workspace(plan)
     out = H.layer(plan, q, k, v, ws=ws)
     torch.cuda.synchronize()
-    h = w.heads
-    gpu = {it: H.debug_read(plan, ws, it) for it in H.DEBUG_ITEMS}
-    for it in ["q_match", "q_score", "kv_match", "kv_score", "q_group", "kv_group", "delta", "outlier", "q_slot"]:
-        gpu[it] = gpu[it].reshape(h, -1)
-    return plan, ws, (q, k, v), out.float().cpu().numpy(), gpu
+    return plan, ws, (q, k, v), out.float().cpu().numpy(), read_all(plan, ws, w.heads)
 
 
 def small_bf16(frames=6, heads=4, n_t=3, **kw):

@@ -25,7 +25,10 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # Sources whose arithmetic must be exactly the written sequence of rounded
 # operations (means and deviations compared bit for bit): no FMA contraction.
-PER_FILE = {"k_merge.hip": ["-ffp-contract=off"]}
+PER_FILE = {"k_merge.hip": ["-ffp-contract=off"],
+            # MFMA results in VGPRs: the softmax reads them with plain VALU ops
+            "k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+            "k_sim.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
           "-I", CSRC, "-Wall", "-Wno-unused-function"]
 

@@ -36,6 +36,8 @@ std::atomic<uint64_t> g_plan_counter{0x48540000ull};
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr float kLog2e = 1.4426950408889634f;
+
 struct Region {
   size_t off = 0, bytes = 0;
 };
@@ -79,6 +81,7 @@ struct httm_plan {
   Layout L;
   IndexLayout I;
   size_t dense_ws;
+  size_t dense_vt_bytes;
   std::vector<httm_block> blocks;
 };
 
@@ -233,7 +236,8 @@ httm_status build(const httm_params& p, httm_plan* pl) {
     Lw.index = b.take(pl->I.total);
     Lw.total = b.cur;
   }
-  pl->dense_ws = E * h * (size_t)ceil_div(g.N, 64) * 64 * kD;
+  pl->dense_vt_bytes = align256(E * h * (size_t)ceil_div(g.N, 64) * 64 * kD);
+  pl->dense_ws = pl->dense_vt_bytes + E * h * n * kD;
   pl->id = ++g_plan_counter;
   return HTTM_OK;
 }
@@ -421,7 +425,8 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
   stage_end(HTTM_T_SELECT, st);
 
   stage_begin(HTTM_T_MERGE_KV, st);
-  CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, k, v, ck.members, ck.off,
+  CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
+                               ck.members, ck.off,
                                at<void>(ws, L.kt), at<void>(ws, L.vt), st));
   stage_end(HTTM_T_MERGE_KV, st);
 
@@ -473,7 +478,7 @@ httm_status httm_layer_cached(const httm_plan* pl, void* ws, size_t ws_bytes, co
   char* idx = reinterpret_cast<char*>(index->dev);
   timing_begin_call();
   stage_begin(HTTM_T_MERGE_KV, st);
-  CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, k, v,
+  CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
                                reinterpret_cast<const int32_t*>(idx + I.k_members.off),
                                reinterpret_cast<const int32_t*>(idx + I.k_off.off),
                                at<void>(ws, pl->L.kt), at<void>(ws, pl->L.vt), st));
@@ -498,9 +503,10 @@ httm_status httm_attention_dense(const httm_plan* pl, void* ws, size_t ws_bytes,
   const Geo& g = pl->g;
   const int dt = pl->p.dtype;
   const int pitch = ceil_div(g.N, 64) * 64;
+  char* kc = reinterpret_cast<char*>(ws) + pl->dense_vt_bytes;
   timing_begin_call();
   stage_begin(HTTM_T_MERGE_KV, st);
-  CHECK_LAUNCH(launch_transpose_v(dt, g.heads, g.N, pitch, v, ws, st));
+  CHECK_LAUNCH(launch_prep_dense(dt, g.heads, g.N, pitch, pl->scale * kLog2e, k, v, kc, ws, st));
   stage_end(HTTM_T_MERGE_KV, st);
   AttnShape a;
   a.heads = g.heads;
@@ -511,7 +517,7 @@ httm_status httm_attention_dense(const httm_plan* pl, void* ws, size_t ws_bytes,
   a.q_capacity = (int64_t)g.heads * g.N;
   a.scale = pl->scale;
   stage_begin(HTTM_T_ATTN, st);
-  CHECK_LAUNCH(launch_attention(dt, a, q, k, ws, nullptr, out, st));
+  CHECK_LAUNCH(launch_attention(dt, a, q, kc, ws, nullptr, out, st));
   stage_end(HTTM_T_ATTN, st);
   timing_end_call();
   return HTTM_OK;

@@ -34,11 +34,14 @@ template <typename T>
 __device__ __forceinline__ void store8(T* p, const float* x) { Row8<T>::store(p, x); }
 
 // Merged K and V.  One workgroup = 64 consecutive key slots of one head;
-// 8 lanes per slot, 8 channels per lane.  K~ rows are written directly; V~
-// means go through LDS and are written transposed (vt[h][c][slot]) so that
-// the attention kernel reads V~ along keys with plain row loads.
+// 8 lanes per slot, 8 channels per lane.  K~ rows are written directly,
+// multiplied by kscale (the softmax scale times log2 e, so that the
+// attention kernel's scores come out in exp2 units; the product is rounded
+// once to the storage type with the mean).  V~ means go through LDS and are
+// written transposed (vt[h][c][slot]) so that the attention kernel reads V~
+// along keys with plain row loads.
 template <typename T>
-__global__ __launch_bounds__(256) void merge_kv(int N, int lk, int lk_pad, const T* __restrict__ k,
+__global__ __launch_bounds__(256) void merge_kv(int N, int lk, int lk_pad, float kscale, const T* __restrict__ k,
                                                 const T* __restrict__ v,
                                                 const int32_t* __restrict__ members,
                                                 const int32_t* __restrict__ off, T* __restrict__ kt,
@@ -75,7 +78,7 @@ __global__ __launch_bounds__(256) void merge_kv(int N, int lk, int lk_pad, const
       const float cnt = (float)(m1 - m0);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        km[e] = rn_div(km[e], cnt);
+        km[e] = rn_div(km[e], cnt) * kscale;
         vm[e] = rn_div(vm[e], cnt);
       }
     }
@@ -369,19 +372,26 @@ __global__ __launch_bounds__(256) void unmerge(int64_t rows, const int32_t* __re
   }
 }
 
-// vt[h][c][n] = v[h][n][c] for n < N, 0 for N <= n < pitch.
+// Unmerged baseline inputs: kc[h][n] = k[h][n] * kscale, vt[h][c][n] =
+// v[h][n][c] for n < N and 0 for N <= n < pitch.
 template <typename T>
-__global__ __launch_bounds__(256) void transpose_v(int N, int pitch, const T* __restrict__ v,
-                                                   T* __restrict__ vt) {
+__global__ __launch_bounds__(256) void prep_dense(int N, int pitch, float kscale, const T* __restrict__ k,
+                                                  const T* __restrict__ v, T* __restrict__ kc,
+                                                  T* __restrict__ vt) {
   __shared__ float sT[kD][65];
   const int tiles = pitch / 64;
   const int head = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+  const T* K = k + (size_t)head * N * kD;
   const T* V = v + (size_t)head * N * kD;
   for (int idx = threadIdx.x; idx < 64 * 8; idx += 256) {
     const int r = idx >> 3, j = idx & 7;
     const int n = tile * 64 + r;
     float x[8];
     if (n < N) {
+      load8(K + (size_t)n * kD + j * 8, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= kscale;
+      store8(kc + ((size_t)head * N + n) * kD + j * 8, x);
       load8(V + (size_t)n * kD + j * 8, x);
     } else {
 #pragma unroll
@@ -413,12 +423,12 @@ __global__ __launch_bounds__(256) void transpose_v(int N, int pitch, const T* __
     }                                              \
   } while (0)
 
-hipError_t launch_merge_kv(int dtype, int heads, int N, int lk, int lk_pad, const void* k,
+hipError_t launch_merge_kv(int dtype, int heads, int N, int lk, int lk_pad, float kscale, const void* k,
                            const void* v, const int32_t* members, const int32_t* off, void* kt,
                            void* vt, hipStream_t stream) {
   const int grid = heads * (lk_pad / 64);
   HTTM_DISPATCH(dtype, hipLaunchKernelGGL(merge_kv<T>, dim3(grid), dim3(256), 0, stream, N, lk,
-                                          lk_pad, (const T*)k, (const T*)v, members, off, (T*)kt,
+                                          lk_pad, kscale, (const T*)k, (const T*)v, members, off, (T*)kt,
                                           (T*)vt));
   return hipGetLastError();
 }
@@ -465,11 +475,11 @@ hipError_t launch_unmerge(int dtype, int heads, int N, const int32_t* slot, cons
   return hipGetLastError();
 }
 
-hipError_t launch_transpose_v(int dtype, int heads, int N, int pitch, const void* v, void* vt,
-                              hipStream_t stream) {
+hipError_t launch_prep_dense(int dtype, int heads, int N, int pitch, float kscale, const void* k,
+                             const void* v, void* kc, void* vt, hipStream_t stream) {
   const int grid = heads * (pitch / 64);
-  HTTM_DISPATCH(dtype, hipLaunchKernelGGL(transpose_v<T>, dim3(grid), dim3(256), 0, stream, N,
-                                          pitch, (const T*)v, (T*)vt));
+  HTTM_DISPATCH(dtype, hipLaunchKernelGGL(prep_dense<T>, dim3(grid), dim3(256), 0, stream, N, pitch, kscale,
+                                          (const T*)k, (const T*)v, (T*)kc, (T*)vt));
   return hipGetLastError();
 }
 

@@ -25,8 +25,9 @@ hipError_t launch_select(const Geo& g, const int32_t* match_q, const float* scor
                          const int32_t* match_k, const float* score_k, Csr q, Csr k,
                          hipStream_t stream);
 
-// Means of K and V over the key partition: kt [h][lk_pad][64], vt [h][64][lk_pad].
-hipError_t launch_merge_kv(int dtype, int heads, int N, int lk, int lk_pad, const void* k,
+// Means of K and V over the key partition: kt [h][lk_pad][64] (times kscale),
+// vt [h][64][lk_pad].
+hipError_t launch_merge_kv(int dtype, int heads, int N, int lk, int lk_pad, float kscale, const void* k,
                            const void* v, const int32_t* members, const int32_t* off, void* kt,
                            void* vt, hipStream_t stream);
 
@@ -60,7 +61,8 @@ hipError_t launch_merge_q_cached(int dtype, int heads, int N, int64_t q_capacity
                                  const int32_t* lenq, void* qt, hipStream_t stream);
 
 // Ragged attention: o[row] = softmax(scale q[row] k_h^T) v_h for the packed
-// rows of every head; lenq == nullptr means every head has `lq_uniform` rows.
+// rows of every head, with k already multiplied by scale * log2(e) (scores
+// in exp2 units); lenq == nullptr means every head has `lq_uniform` rows.
 struct AttnShape {
   int heads;
   int lk;          // keys per head
@@ -77,8 +79,9 @@ hipError_t launch_attention(int dtype, const AttnShape& s, const void* q, const 
 hipError_t launch_unmerge(int dtype, int heads, int N, const int32_t* slot, const void* o,
                           void* out, hipStream_t stream);
 
-// vt[h][c][n] = v[h][n][c], zero for n in [N, pitch)
-hipError_t launch_transpose_v(int dtype, int heads, int N, int pitch, const void* v, void* vt,
-                              hipStream_t stream);
+// Unmerged baseline inputs: kc = k * kscale ([h][N][64]); vt[h][c][n] =
+// v[h][n][c], zero for n in [N, pitch).
+hipError_t launch_prep_dense(int dtype, int heads, int N, int pitch, float kscale, const void* k,
+                             const void* v, void* kc, void* vt, hipStream_t stream);
 
 }  // namespace httm
