@@ -74,6 +74,11 @@ def main():
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (HBM counter calibration)")
+    ap.add_argument("--kv-ratio", type=float, default=None, help="override the workload's K/V merge ratio")
+    ap.add_argument("--q-ratio", type=float, default=None, help="override the workload's query merge ratio")
+    ap.add_argument("--outlier-pct", type=float, default=None, help="override the workload's outlier budget")
+    ap.add_argument("--cached-layers", type=int, default=None,
+                    help="also time layers that reuse the merge indices (default: workload layers - 1)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the HTTM layer here runs on a single MI355X "
@@ -84,6 +89,11 @@ def main():
     import token_merged_global_amd as H
 
     w = gen.WORKLOADS[args.workload]
+    over = {k: v for k, v in (("kv_ratio", args.kv_ratio), ("q_ratio", args.q_ratio),
+                                ("outlier_pct", args.outlier_pct)) if v is not None}
+    if over:
+        w = w.with_(**over)
+    n_cached = (w.layers - 1) if args.cached_layers is None else args.cached_layers
     log(f"[bench] generating {describe(w)}")
     x = gen.layer_inputs(w, seed=args.seed)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -129,6 +139,27 @@ def main():
     stages, _ = H.get_timing()
     H.set_timing([])
     torch.cuda.synchronize()
+
+    # layers that reuse this layer's merge indices (LiteVGGT-style cache)
+    cached = None
+    if n_cached > 0:
+        idx = H.CachedIndex(plan)
+        H.layer(plan, q, k, v, ws=ws, out=out, index=idx, stream=stream)
+        H.layer_cached(plan, idx, q, k, v, ws=ws, out=out, stream=stream)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(args.steps):
+            H.layer_cached(plan, idx, q, k, v, ws=ws, out=out, stream=stream)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cms = c0.elapsed_time(c1) / args.steps
+        stack_ms = ms_step + n_cached * cms
+        cached = {"cached_layers": n_cached, "cached_ms_per_layer": cms,
+                  "stack_ms": stack_ms, "stack_tokens_per_s": (1 + n_cached) * w.n_tokens / (stack_ms * 1e-3),
+                  "cached_tokens_per_s": w.n_tokens / (cms * 1e-3)}
+        log(f"[bench] cached layer {cms:.4f} ms; stack of {1 + n_cached}: {stack_ms:.3f} ms")
+        del idx
 
     # speedup over the same engine's unmerged attention
     dense_ms = None
@@ -182,6 +213,7 @@ def main():
                      "avg_launch_ms": attn_ms, "launches_timed": calls},
         "cpu_baseline": cpu,
         "stages_ms": stages,
+        "cached": cached,
         "speedup_vs_unmerged_attention": (dense_ms / ms_step) if dense_ms else None,
         "unmerged_attention_ms": dense_ms,
         "lengths": {"kv_len": lk, "q_len_mean": float(lq.mean()), "q_len_min": int(lq.min()),
