@@ -177,11 +177,14 @@ httm_status httm_attention_dense(const httm_plan* plan, void* ws, size_t ws_byte
  *   HTTM_DBG_OUTLIER: [h][N] uint8 outlier mask;
  *   HTTM_DBG_Q_SLOT: [h][N] packed row of Q~ that token n reads at unmerge;
  *   HTTM_DBG_CU_Q: [h+1] prefix of per-head Q~ lengths;
- *   HTTM_DBG_SELECT: [4] uint32 {threshold bits, count above, ties taken, k_o}. */
+ *   HTTM_DBG_SELECT: [4] uint32 {threshold bits, count above, ties taken, k_o};
+ *   HTTM_DBG_ATTN_FALLBACK: [1] int32 attention work units that the exact
+ *       (running-max) kernel recomputed because their rows' probabilities
+ *       underflowed against the norm bound. */
 typedef enum {
   HTTM_DBG_Q_MATCH = 0, HTTM_DBG_Q_SCORE, HTTM_DBG_KV_MATCH, HTTM_DBG_KV_SCORE,
   HTTM_DBG_Q_GROUP, HTTM_DBG_KV_GROUP, HTTM_DBG_DELTA, HTTM_DBG_OUTLIER,
-  HTTM_DBG_Q_SLOT, HTTM_DBG_CU_Q, HTTM_DBG_SELECT, HTTM_DBG_COUNT
+  HTTM_DBG_Q_SLOT, HTTM_DBG_CU_Q, HTTM_DBG_SELECT, HTTM_DBG_ATTN_FALLBACK, HTTM_DBG_COUNT
 } httm_debug_item;
 httm_status httm_debug_size(const httm_plan* plan, int32_t item, size_t* bytes);
 httm_status httm_debug_read(const httm_plan* plan, const void* ws, const httm_index* index,

@@ -141,3 +141,4 @@ def test_layer_rejects_bad_buffers_before_any_launch():
     n = ctypes.c_size_t()
     assert L.httm_debug_size(plan.handle, 99, ctypes.byref(n)) == 1
     assert L.httm_debug_size(plan.handle, 10, ctypes.byref(n)) == 0 and n.value == 16
+    assert L.httm_debug_size(plan.handle, 11, ctypes.byref(n)) == 0 and n.value == 4

@@ -161,3 +161,48 @@ def test_cached_layer_matches_oracle_with_same_indices():
     other = H.Plan.from_workload(w)
     with pytest.raises(H.HttmError):
         H.layer_cached(other, idx, *dev1)
+
+
+def _orthogonal_offset(x, big=600.0):
+    """Keys confined to channels 0-31; queries get a large constant in channels
+    32-63, orthogonal to every key.  Scores (and the softmax) are unchanged in
+    size, but the norm bound |q| max|k| exceeds every score by far more than
+    60 (log2 units), so every attention unit takes the exact path."""
+    q = x["q"].copy()
+    k = x["k"].copy()
+    k[..., 32:] = 0.0
+    q[..., 32:] = big
+    return {"q": gen.round_bf16(q), "k": gen.round_bf16(k), "v": x["v"]}
+
+
+def test_attention_fallback_exact_path():
+    w = small_bf16(frames=4, heads=2)
+    xs = _orthogonal_offset(gen.layer_inputs(w))
+    p = O.Params.from_workload(w)
+    plan, ws, dev, out, gpu = run_layer(w, xs)
+    fb = int(gpu["attn_fallback"][0])
+    _say(f"[fallback] units recomputed exactly: {fb}")
+    assert fb > 0
+    rep = staged.check_layer(xs["q"], xs["k"], xs["v"], p, gpu, out, rel_tol=BF16_REL)
+    _say("  ", rep.as_dict())
+    # the unmerged path takes the same fallback
+    q, k, v = dev
+    dense = H.attention_dense(plan, q, k, v).float().cpu().numpy()
+    for h in range(w.heads):
+        ref = O.attention(xs["q"][h], xs["k"][h], xs["v"][h], 0.125)
+        assert np.abs(dense[h] - ref).max() <= BF16_REL * np.sqrt((ref ** 2).mean())
+
+
+def test_key_split_matches_single_pass():
+    """The 30-frame layer runs its attention in key splits; cached layers on the
+    same indices and inputs must agree with the full layer to the bf16 tolerance."""
+    w = gen.WORKLOADS["vggt30"].with_(heads=4)
+    x = gen.layer_inputs(w)
+    plan = H.Plan.from_workload(w)
+    q, k, v = (to_dev(x[t], w.dtype) for t in "qkv")
+    ws = H.workspace(plan)
+    out, idx = H.layer(plan, q, k, v, ws=ws, keep_index=True)
+    out2 = H.layer_cached(plan, idx, q, k, v, ws=ws)
+    torch.cuda.synchronize()
+    a, b = out.float().cpu().numpy(), out2.float().cpu().numpy()
+    assert np.abs(a - b).max() <= BF16_REL * np.sqrt((a ** 2).mean())

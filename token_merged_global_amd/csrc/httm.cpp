@@ -47,6 +47,7 @@ struct Layout {
   Region q_members, q_off, q_group, k_group;
   Region qsum, delta, mask, radix, base;
   Region qt, kt, vt, o;
+  Region kmax, fb, opart, lpart, mpart;  // attention: key norms, fallback queue, split partials
   Region index;  // used when the caller passes no index buffer
   size_t total = 0;
 };
@@ -81,7 +82,9 @@ struct httm_plan {
   Layout L;
   IndexLayout I;
   size_t dense_ws;
-  size_t dense_vt_bytes;
+  size_t dense_vt_bytes, dense_kc_bytes;
+  int32_t attn_split;
+  int64_t attn_units;  // upper bound of attention work units (all splits)
   std::vector<httm_block> blocks;
 };
 
@@ -198,6 +201,13 @@ httm_status build(const httm_params& p, httm_plan* pl) {
   pl->lk_pad = ceil_div(g.nslots[kK], 64) * 64;
   pl->scale = p.softmax_scale > 0.0f ? p.softmax_scale : 1.0f / std::sqrt((float)kD);
   pl->esize = p.dtype == HTTM_BF16 ? 2 : 4;
+  pl->attn_split = p.dtype == HTTM_BF16 ? attention_split(pl->q_cap, p.heads) : 1;
+  {
+    const int64_t rows = attention_rows_per_unit();
+    const int64_t dense_units = (int64_t)p.heads * ((N + rows - 1) / rows);
+    const int64_t layer_units = ((pl->q_cap + rows - 1) / rows + p.heads) * pl->attn_split;
+    pl->attn_units = layer_units > dense_units ? layer_units : dense_units;
+  }
 
   const size_t h = (size_t)p.heads, n = (size_t)N, E = pl->esize;
   // index layout
@@ -233,11 +243,19 @@ httm_status build(const httm_params& p, httm_plan* pl) {
     Lw.kt = b.take(E * h * (size_t)pl->lk_pad * kD);
     Lw.vt = b.take(E * h * (size_t)pl->lk_pad * kD);
     Lw.o = b.take(E * (size_t)pl->q_cap * kD);
+    Lw.kmax = b.take(4 * h);
+    Lw.fb = b.take(4 * (1 + (size_t)pl->attn_units));
+    if (pl->attn_split > 1) {
+      Lw.opart = b.take(4 * (size_t)pl->attn_split * pl->q_cap * kD);
+      Lw.lpart = b.take(4 * (size_t)pl->attn_split * pl->q_cap);
+      Lw.mpart = b.take(4 * (size_t)pl->attn_split * pl->q_cap);
+    }
     Lw.index = b.take(pl->I.total);
     Lw.total = b.cur;
   }
   pl->dense_vt_bytes = align256(E * h * (size_t)ceil_div(g.N, 64) * 64 * kD);
-  pl->dense_ws = pl->dense_vt_bytes + E * h * n * kD;
+  pl->dense_kc_bytes = align256(E * h * n * kD);
+  pl->dense_ws = pl->dense_vt_bytes + pl->dense_kc_bytes + pl->L.kmax.bytes + 256 + pl->L.fb.bytes;
   pl->id = ++g_plan_counter;
   return HTTM_OK;
 }
@@ -308,6 +326,13 @@ httm_status attend_unmerge(const httm_plan* pl, void* ws, char* idx, const void*
   s.lq_uniform = 0;
   s.q_capacity = pl->q_cap;
   s.scale = pl->scale;
+  s.split = pl->attn_split;
+  s.opart = pl->attn_split > 1 ? at<float>(ws, pl->L.opart) : nullptr;
+  s.lpart = pl->attn_split > 1 ? at<float>(ws, pl->L.lpart) : nullptr;
+  s.mpart = pl->attn_split > 1 ? at<float>(ws, pl->L.mpart) : nullptr;
+  s.kmax = at<float>(ws, pl->L.kmax);
+  s.fb_count = at<int>(ws, pl->L.fb);
+  s.fb_list = at<int>(ws, pl->L.fb) + 1;
   const int32_t* lenq = reinterpret_cast<const int32_t*>(idx + pl->I.lenq.off);
   stage_begin(HTTM_T_ATTN, st);
   CHECK_LAUNCH(launch_attention(dt, s, qt, at<void>(ws, pl->L.kt), at<void>(ws, pl->L.vt), lenq,
@@ -425,9 +450,10 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
   stage_end(HTTM_T_SELECT, st);
 
   stage_begin(HTTM_T_MERGE_KV, st);
+  CHECK_LAUNCH(launch_attn_init(at<float>(ws, L.kmax), g.heads, at<int>(ws, L.fb), st));
   CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
                                ck.members, ck.off,
-                               at<void>(ws, L.kt), at<void>(ws, L.vt), st));
+                               at<void>(ws, L.kt), at<void>(ws, L.vt), at<float>(ws, L.kmax), st));
   stage_end(HTTM_T_MERGE_KV, st);
 
   stage_begin(HTTM_T_MERGE_Q, st);
@@ -478,10 +504,11 @@ httm_status httm_layer_cached(const httm_plan* pl, void* ws, size_t ws_bytes, co
   char* idx = reinterpret_cast<char*>(index->dev);
   timing_begin_call();
   stage_begin(HTTM_T_MERGE_KV, st);
+  CHECK_LAUNCH(launch_attn_init(at<float>(ws, pl->L.kmax), g.heads, at<int>(ws, pl->L.fb), st));
   CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
                                reinterpret_cast<const int32_t*>(idx + I.k_members.off),
                                reinterpret_cast<const int32_t*>(idx + I.k_off.off),
-                               at<void>(ws, pl->L.kt), at<void>(ws, pl->L.vt), st));
+                               at<void>(ws, pl->L.kt), at<void>(ws, pl->L.vt), at<float>(ws, pl->L.kmax), st));
   stage_end(HTTM_T_MERGE_KV, st);
   stage_begin(HTTM_T_MERGE_Q, st);
   CHECK_LAUNCH(launch_merge_q_cached(dt, g.heads, g.N, pl->q_cap, q,
@@ -504,9 +531,12 @@ httm_status httm_attention_dense(const httm_plan* pl, void* ws, size_t ws_bytes,
   const int dt = pl->p.dtype;
   const int pitch = ceil_div(g.N, 64) * 64;
   char* kc = reinterpret_cast<char*>(ws) + pl->dense_vt_bytes;
+  float* kmax = reinterpret_cast<float*>(kc + pl->dense_kc_bytes);
+  int* fb = reinterpret_cast<int*>(reinterpret_cast<char*>(kmax) + align256(pl->L.kmax.bytes));
   timing_begin_call();
   stage_begin(HTTM_T_MERGE_KV, st);
-  CHECK_LAUNCH(launch_prep_dense(dt, g.heads, g.N, pitch, pl->scale * kLog2e, k, v, kc, ws, st));
+  CHECK_LAUNCH(launch_attn_init(kmax, g.heads, fb, st));
+  CHECK_LAUNCH(launch_prep_dense(dt, g.heads, g.N, pitch, pl->scale * kLog2e, k, v, kc, ws, kmax, st));
   stage_end(HTTM_T_MERGE_KV, st);
   AttnShape a;
   a.heads = g.heads;
@@ -516,6 +546,11 @@ httm_status httm_attention_dense(const httm_plan* pl, void* ws, size_t ws_bytes,
   a.lq_uniform = g.N;
   a.q_capacity = (int64_t)g.heads * g.N;
   a.scale = pl->scale;
+  a.split = 1;
+  a.opart = a.lpart = a.mpart = nullptr;
+  a.kmax = kmax;
+  a.fb_count = fb;
+  a.fb_list = fb + 1;
   stage_begin(HTTM_T_ATTN, st);
   CHECK_LAUNCH(launch_attention(dt, a, q, kc, ws, nullptr, out, st));
   stage_end(HTTM_T_ATTN, st);
@@ -538,6 +573,7 @@ httm_status httm_debug_size(const httm_plan* pl, int32_t item, size_t* bytes) {
     case HTTM_DBG_OUTLIER: *bytes = h * n; break;
     case HTTM_DBG_CU_Q: *bytes = 4 * (h + 1); break;
     case HTTM_DBG_SELECT: *bytes = 16; break;
+    case HTTM_DBG_ATTN_FALLBACK: *bytes = 4; break;
     default: return fail(HTTM_ERR_INVALID_ARG, "unknown debug item");
   }
   return HTTM_OK;
@@ -568,6 +604,7 @@ httm_status httm_debug_read(const httm_plan* pl, const void* ws, const httm_inde
     case HTTM_DBG_Q_SLOT: src = idx + pl->I.slot.off; break;
     case HTTM_DBG_CU_Q: src = idx + pl->I.cu_q.off; break;
     case HTTM_DBG_SELECT: src = base + L.radix.off + 4 * 3 * 2048; break;
+    case HTTM_DBG_ATTN_FALLBACK: src = base + L.fb.off; break;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   CHECK_LAUNCH(hipMemcpyAsync(host, src, need, hipMemcpyDeviceToHost, st));

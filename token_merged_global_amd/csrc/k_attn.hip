@@ -6,21 +6,34 @@
 // outlier budget is shared across heads (key design 3); K~ / V~ have the same
 // length in every head.
 //
-// One workgroup = 128 query rows of one head: 4 waves x 2 tiles of 16 rows,
-// using v_mfma_f32_16x16x32_bf16 (the full-rate bf16 MFMA of gfx950).  Key
-// tiles of 64 rows of K~ and the matching 64 columns of V~^T (stored
-// transposed by the merge kernel) are copied global -> LDS directly
-// (global_load_lds_dwordx4) into a double buffer.  S^T = K~ Q^T puts one query
-// per lane column, so the running max enters the MFMA as its initial
-// accumulator (acc = k.q - m, K~ pre-multiplied by scale * log2 e), the
-// probabilities are exp2(acc), and the lane's probabilities are exactly the B
-// operand of O^T = V~^T P^T.  Row max and row sum cross lanes with VALU lane
-// swaps only; the sum adds the bf16-rounded probabilities (v_dot2) that the
-// PV product uses.  The running max is raised only on the first tile or when
-// a score exceeds it by more than 8 in log2 units, so accumulators are
-// rescaled rarely; the final division makes the result exact.
-// The (head, tile) of a workgroup comes from the per-head lengths on the
-// device, so the host never waits for them.
+// Work unit = (head, tile of 128 query rows, key split).  One workgroup = 2
+// waves x 64 query rows (four 16-row tiles per wave) on
+// v_mfma_f32_16x16x32_bf16, the full-rate bf16 MFMA of gfx950; 64 rows per
+// wave halve the LDS operand bytes per FLOP against 32.  Key tiles of 64 rows
+// of K~ and the matching 64 columns of V~^T (stored transposed by the merge
+// kernel) go global -> LDS directly (global_load_lds_dwordx4), double
+// buffered.  K~ arrives multiplied by scale * log2(e), so scores are in exp2
+// units.
+//
+// Softmax reference.  Cauchy-Schwarz bounds every score of a row by
+// m = |q| * max_k |k~| (max over the head's keys, computed by the K~
+// producer), so with acc = k~.q - m the probabilities exp2(acc) never exceed
+// 1: no running max, no cross-lane max and no rescaling in the key loop.  The
+// bound enters the MFMA as its initial accumulator.  If a row's sum ends
+// below 2^-60 (scores far below the bound: large norms) the unit is queued
+// and recomputed by the exact kernel below, which tracks the running max.
+//
+// Layouts.  S^T tile (16 keys x 16 queries): lane l holds query l%16 and
+// tile rows 4g..4g+3 (g = l/16).  The K~ rows of the two S tiles of a 32-key
+// chunk are permuted so that lane group g holds keys 8g..8g+7 of the chunk:
+// exactly the B operand of the P V MFMA, whose V~^T operand is then one
+// 16-byte LDS read.  The row sum adds the bf16-rounded probabilities that the
+// P V product uses (v_dot2 against 1.0).
+//
+// Key split.  When the query tiles alone do not fill the GPU (small layers),
+// the keys are split in S contiguous ranges; each unit writes its fp32
+// partial O, row sum and reference, and a finalize kernel combines them in
+// split order (deterministic).  With S = 1 the unit writes normalized rows.
 #include "common.h"
 #include "kernels.h"
 
@@ -30,16 +43,27 @@ namespace {
 
 constexpr int kKeyTile = 64;
 constexpr int kRowsF32 = 128;  // fp32 kernel: one thread per query row
+constexpr int kQT = 4;         // 16-row query tiles per wave
+constexpr int kNW = 2;         // waves per workgroup
+constexpr int kRows = kQT * kNW * 16;
+constexpr float kTinySum = 8.673617379884035e-19f;  // 2^-60
 
 struct AttnArgs {
   const void* q;
   const void* k;
   const void* vt;
-  void* o;
+  void* o;                 // normalized output rows (split == 1)
+  float* opart;            // [split][q_capacity][64] partial numerators (split > 1)
+  float* lpart;            // [split][q_capacity] partial row sums
+  float* mpart;            // [split][q_capacity] reference of each partial
+  const float* kmax;       // [heads] max |k~|
+  int* fb_count;           // queued units for the exact kernel
+  int* fb_list;
   const int32_t* lenq;
   int heads, lk, k_rows, vt_pitch, lq_uniform;
+  int split;
+  int64_t q_capacity;
   int total_wg;
-  float scale_log2;  // scale * log2(e), already applied to K~ by its producer
 };
 
 // 16 bytes per lane from global memory straight into LDS: lane i of the wave
@@ -47,62 +71,22 @@ struct AttnArgs {
 __device__ __forceinline__ void lds_copy16(const void* g, u32x4* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
-// LDS tiles are rows of 128 bytes (eight 16-byte chunks); chunk c of row r is
-// stored at chunk c ^ swz(r).  The LDS serves 256 bytes (64 four-byte banks)
-// per cycle, i.e. 16 lanes of a 16-byte read: with this swizzle 16
-// consecutive rows read at one logical chunk hit 16 distinct bank groups
-// (rows of equal parity get distinct chunks, the two parities the two halves).
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Wait until at most N vector-memory operations of this wave are in flight.
-template <int N>
-__device__ __forceinline__ void wait_vm_le() {
-  static_assert(N >= 0 && N <= 63, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
+// LDS tiles are rows of 128 bytes (eight 16-byte chunks); chunk c of row r is
+// stored at chunk c ^ swz(r).  The LDS serves 16 lanes of a 16-byte read per
+// cycle (64 four-byte banks).  V~^T is read by 16 consecutive rows: swzV
+// gives rows of equal parity distinct chunks.  K~ is read by the permuted
+// rows 8(i/4) + 4p + i%4 of a 32-key chunk: swzK does the same for them.
+__device__ __forceinline__ int swzV(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swzK(int row) { return ((row >> 1) & 1) | ((row >> 2) & 6); }
 
 __device__ __forceinline__ int xcd_logical(int bid, int total) {
   const int per = (total + 7) / 8;
   return (bid % 8) * per + bid / 8;
 }
 
-// (head, first packed row of the head, head length, tile) of workgroup w.
-__device__ __forceinline__ bool locate(const AttnArgs& a, int w, int rows_per_wg, int& head, int& cu,
-                                       int& L, int& tile) {
-  int acc = 0;
-  cu = 0;
-  for (int h = 0; h < a.heads; ++h) {
-    const int len = a.lenq ? a.lenq[h] : a.lq_uniform;
-    const int nt = ceil_div(len, rows_per_wg);
-    if (w < acc + nt) {
-      head = h;
-      L = len;
-      tile = w - acc;
-      return true;
-    }
-    acc += nt;
-    cu += len;
-  }
-  return false;
-}
-
-__device__ __forceinline__ float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-// Max over lanes {l, l^32} and {l, l^16} of a wave, with VALU lane swaps
-// (no LDS round trip): after a swap of a register with itself, element 0
-// holds one of the two lanes' values and element 1 the other.
-__device__ __forceinline__ float max_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
+// Sums over lanes {l, l^32} and {l, l^16} with VALU lane swaps.
 __device__ __forceinline__ float sum_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -111,132 +95,313 @@ __device__ __forceinline__ float sum_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
-// 16x16x32 form (full-rate bf16 MFMA on gfx950).  Per wave: QT query tiles of
-// 16 rows.  S^T tile (16 keys x 16 queries): lane l holds query l%16 and keys
-// 4*(l/16) + 0..3, so a lane's four scores share one query and the running
-// max enters as the accumulator's initial value (acc = k.q - m).  PV chunk of
-// 32 keys: lane's B operand holds keys 32*kc + 4g + {0..3} and
-// 32*kc + 16 + 4g + {0..3} (g = l/16), exactly the probabilities it owns.
-template <int QT, int NW>
-__global__ __launch_bounds__(NW * 64) void attn16(AttnArgs a) {
-  constexpr int kRowsPerWg = NW * QT * 16;
+struct Unit {
+  int head, cu, L, tile, split;
+};
+
+// Unit u -> (head, first packed row of the head, head length, query tile,
+// key split); units of one head are ordered split-major so that concurrent
+// units share key tiles.
+__device__ __forceinline__ bool locate(const AttnArgs& a, int u, int rows, Unit& o) {
+  int acc = 0;
+  o.cu = 0;
+  for (int h = 0; h < a.heads; ++h) {
+    const int len = a.lenq ? a.lenq[h] : a.lq_uniform;
+    const int nt = ceil_div(len, rows);
+    const int nu = nt * a.split;
+    if (u < acc + nu) {
+      const int j = u - acc;
+      o.head = h;
+      o.L = len;
+      o.split = j / nt;
+      o.tile = j % nt;
+      return true;
+    }
+    acc += nu;
+    o.cu += len;
+  }
+  return false;
+}
+
+// Shared state of one unit: operands, loaders, output.
+struct UnitCtx {
+  const uint16_t* Kp;
+  const uint16_t* Vp;
+  int t0, t1, ntiles_all;
+  bf16x8 bq[kQT][2];
+  bool valid[kQT];
+  int qrow[kQT];
+};
+
+__device__ __forceinline__ void unit_setup(const AttnArgs& a, const Unit& u, int wave, int g, int l16, UnitCtx& c,
+                                           float* qnorm2) {
+  const uint16_t* Qp = reinterpret_cast<const uint16_t*>(a.q);
+  c.Kp = reinterpret_cast<const uint16_t*>(a.k) + (size_t)u.head * a.k_rows * kD;
+  c.Vp = reinterpret_cast<const uint16_t*>(a.vt) + (size_t)u.head * kD * a.vt_pitch;
+  c.ntiles_all = ceil_div(a.lk, kKeyTile);
+  c.t0 = (int)((int64_t)u.split * c.ntiles_all / a.split);
+  c.t1 = (int)((int64_t)(u.split + 1) * c.ntiles_all / a.split);
+#pragma unroll
+  for (int qt = 0; qt < kQT; ++qt) {
+    const int qr = u.tile * kRows + (wave * kQT + qt) * 16 + l16;
+    c.valid[qt] = qr < u.L;
+    c.qrow[qt] = qr;
+    const size_t r = (size_t)u.cu + (c.valid[qt] ? qr : u.L - 1);
+    float ss = 0.f;
+#pragma unroll
+    for (int dc = 0; dc < 2; ++dc) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(Qp + r * kD + dc * 32 + g * 8);
+      c.bq[qt][dc] = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(v[e] << 16), hi = __uint_as_float(v[e] & 0xFFFF0000u);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+      }
+    }
+    qnorm2[qt] = sum_xor16(sum_xor32(ss));
+  }
+}
+
+// Copy key tile t (64 keys of K~ and V~^T) into LDS buffer buf.  Each wave
+// issues 4 + 4 copies of 64 x 16 bytes; lane i fetches the global chunk that
+// belongs at its swizzled LDS slot.
+__device__ __forceinline__ void load_tile(const AttnArgs& a, const UnitCtx& c, u32x4 (*sK)[kKeyTile * 8],
+                                          u32x4 (*sV)[kD * 8], int t, int buf, int wave, int lane) {
+#pragma unroll
+  for (int rd = 0; rd < 8 / kNW; ++rd) {
+    const int slot = (rd * kNW + wave) * 64;
+    const int p = slot + lane;
+    const int row = p >> 3, pc = p & 7;
+    int key = t * kKeyTile + row;
+    key = key < a.lk ? key : a.lk - 1;
+    lds_copy16(c.Kp + (size_t)key * kD + (pc ^ swzK(row)) * 8, &sK[buf][slot]);
+    lds_copy16(c.Vp + (size_t)row * a.vt_pitch + t * kKeyTile + (pc ^ swzV(row)) * 8, &sV[buf][slot]);
+  }
+}
+
+// S^T - m for one 64-key tile: sacc[qt][kt], kt = 2*kc + p holds keys
+// 32kc + 8g + 4p + r in register r of lane group g.
+__device__ __forceinline__ void scores(const u32x4* sKb, const UnitCtx& c, const f32x4* negm, int g, int l16,
+                                       f32x4 (*sacc)[4]) {
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    const int row = 32 * (kt >> 1) + 8 * (l16 >> 2) + 4 * (kt & 1) + (l16 & 3);
+#pragma unroll
+    for (int dc = 0; dc < 2; ++dc) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, sKb[row * 8 + ((4 * dc + g) ^ swzK(row))]);
+#pragma unroll
+      for (int qt = 0; qt < kQT; ++qt)
+        sacc[qt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, c.bq[qt][dc], dc == 0 ? negm[qt] : sacc[qt][kt],
+                                                                 0, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ void mask_tail(const AttnArgs& a, int t, int g, f32x4 (*sacc)[4]) {
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (t * kKeyTile + 32 * (kt >> 1) + 8 * g + 4 * (kt & 1) + r >= a.lk) {
+#pragma unroll
+        for (int qt = 0; qt < kQT; ++qt) sacc[qt][kt][r] = -INFINITY;
+      }
+}
+
+// p = exp2(acc) as bf16 B operands, and the running row sum of those values.
+__device__ __forceinline__ void probs(f32x4 (*sacc)[4], bf16x8 (*bp)[2], float* lrun) {
+  const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int qt = 0; qt < kQT; ++qt) {
+    float ls0 = lrun[qt], ls1 = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      bf16x8 pb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pb[r] = (__bf16)__builtin_amdgcn_exp2f(sacc[qt][2 * kc][r]);
+        pb[4 + r] = (__bf16)__builtin_amdgcn_exp2f(sacc[qt][2 * kc + 1][r]);
+      }
+      bp[qt][kc] = pb;
+#pragma unroll
+      for (int e = 0; e < 8; e += 4) {
+        const bf16x2 p0 = {pb[e], pb[e + 1]}, p1 = {pb[e + 2], pb[e + 3]};
+        ls0 = __builtin_amdgcn_fdot2_f32_bf16(p0, one2, ls0, false);
+        ls1 = __builtin_amdgcn_fdot2_f32_bf16(p1, one2, ls1, false);
+      }
+    }
+    lrun[qt] = ls0 + ls1;
+  }
+}
+
+// O^T += V~^T P^T for one 64-key tile.
+__device__ __forceinline__ void pv(const u32x4* sVb, bf16x8 (*bp)[2], int g, int l16, f32x4 (*oacc)[4]) {
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int vrow = dt * 16 + l16;
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, sVb[vrow * 8 + ((4 * kc + g) ^ swzV(vrow))]);
+#pragma unroll
+      for (int qt = 0; qt < kQT; ++qt)
+        oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, bp[qt][kc], oacc[qt][dt], 0, 0, 0);
+    }
+  }
+}
+
+// Write one unit's rows: normalized bf16 (split == 1) or fp32 partials.
+__device__ __forceinline__ void store_unit(const AttnArgs& a, const Unit& u, const UnitCtx& c, int g,
+                                           f32x4 (*oacc)[4], const float* lsum, const float* mref) {
+#pragma unroll
+  for (int qt = 0; qt < kQT; ++qt) {
+    if (!c.valid[qt]) continue;
+    const size_t row = (size_t)u.cu + c.qrow[qt];
+    if (a.split == 1) {
+      const float inv = 1.0f / lsum[qt];
+      uint16_t* Op = reinterpret_cast<uint16_t*>(a.o) + row * kD;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        u32x2 w2;
+        w2[0] = (uint32_t)f2bf(oacc[qt][dt][0] * inv) | ((uint32_t)f2bf(oacc[qt][dt][1] * inv) << 16);
+        w2[1] = (uint32_t)f2bf(oacc[qt][dt][2] * inv) | ((uint32_t)f2bf(oacc[qt][dt][3] * inv) << 16);
+        *reinterpret_cast<u32x2*>(Op + dt * 16 + 4 * g) = w2;
+      }
+    } else {
+      const size_t prow = (size_t)u.split * a.q_capacity + row;
+      float* Op = a.opart + prow * kD;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(Op + dt * 16 + 4 * g) = oacc[qt][dt];
+      if (g == 0) {
+        a.lpart[prow] = lsum[qt];
+        a.mpart[prow] = mref[qt];
+      }
+    }
+  }
+}
+
+// Fast path: the Cauchy-Schwarz reference, no running max.
+__global__ __launch_bounds__(kNW * 64) void attn_fast(AttnArgs a) {
   __shared__ u32x4 sK[2][kKeyTile * 8];
   __shared__ u32x4 sV[2][kD * 8];
   const int w = xcd_logical(blockIdx.x, a.total_wg);
-  int head, cu, L, tile;
-  if (!locate(a, w, kRowsPerWg, head, cu, L, tile)) return;
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  Unit u;
+  if (!locate(a, w, kRows, u)) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, l16 = lane & 15;
-  const uint16_t* Qp = reinterpret_cast<const uint16_t*>(a.q);
-  const uint16_t* Kp = reinterpret_cast<const uint16_t*>(a.k) + (size_t)head * a.k_rows * kD;
-  const uint16_t* Vp = reinterpret_cast<const uint16_t*>(a.vt) + (size_t)head * kD * a.vt_pitch;
-
-  bf16x8 bq[QT][2];
-  bool valid[QT];
-  int qrow[QT];
+  UnitCtx c;
+  float qn2[kQT];
+  unit_setup(a, u, wave, g, l16, c, qn2);
+  const float km = a.kmax[u.head];
+  f32x4 negm[kQT];
+  float mref[kQT], lrun[kQT];
+  f32x4 oacc[kQT][4];
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int qr = tile * kRowsPerWg + (wave * QT + qt) * 16 + l16;
-    valid[qt] = qr < L;
-    qrow[qt] = qr;
-    const size_t r = (size_t)cu + (valid[qt] ? qr : L - 1);
-#pragma unroll
-    for (int dc = 0; dc < 2; ++dc)
-      bq[qt][dc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Qp + r * kD + dc * 32 + g * 8));
-  }
-  f32x4 negm[QT];  // -running max, as the S accumulator's initial value
-  float mrun[QT], lrun[QT];
-  f32x4 oacc[QT][4];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    mrun[qt] = 0.f;
+  for (int qt = 0; qt < kQT; ++qt) {
+    mref[qt] = sqrtf(qn2[qt]) * km;
     lrun[qt] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) negm[qt][r] = 0.f;
+    for (int r = 0; r < 4; ++r) negm[qt][r] = -mref[qt];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) oacc[qt][dt][r] = 0.f;
+    for (int dt = 0; dt < 4; ++dt) oacc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-
-  const int ntiles = ceil_div(a.lk, kKeyTile);
-  // Per-lane source of each copy round: row of the 64-row tile and the
-  // logical 16-byte chunk that lands in this lane's LDS slot.
-  int lrow[8 / NW], lchk[8 / NW];
-#pragma unroll
-  for (int rd = 0; rd < 8 / NW; ++rd) {
-    const int p = (rd * NW + wave) * 64 + lane;
-    lrow[rd] = p >> 3;
-    lchk[rd] = (p & 7) ^ swz(p >> 3);
-  }
-  auto load_tile = [&](int t, int buf) {
-#pragma unroll
-    for (int rd = 0; rd < 8 / NW; ++rd) {
-      int key = t * kKeyTile + lrow[rd];
-      key = key < a.lk ? key : a.lk - 1;
-      lds_copy16(Kp + (size_t)key * kD + lchk[rd] * 8, &sK[buf][(rd * NW + wave) * 64]);
-      lds_copy16(Vp + (size_t)lrow[rd] * a.vt_pitch + t * kKeyTile + lchk[rd] * 8,
-                 &sV[buf][(rd * NW + wave) * 64]);
-    }
-  };
-  load_tile(0, 0);
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    wait_vm_le<0>();
+  load_tile(a, c, sK, sV, c.t0, 0, wave, lane);
+  for (int t = c.t0; t < c.t1; ++t) {
+    const int buf = (t - c.t0) & 1;
+    wait_vm();
     __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);
-
-    // S^T - m for 4 key tiles of 16
-    f32x4 sacc[QT][4];
+    if (t + 1 < c.t1) load_tile(a, c, sK, sV, t + 1, buf ^ 1, wave, lane);
+    f32x4 sacc[kQT][4];
+    scores(sK[buf], c, negm, g, l16, sacc);
+    if ((t + 1) * kKeyTile > a.lk) mask_tail(a, t, g, sacc);
+    bf16x8 bp[kQT][2];
+    probs(sacc, bp, lrun);
+    pv(sV[buf], bp, g, l16, oacc);
+  }
+  float lsum[kQT];
+  bool tiny = false;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int arow = kt * 16 + l16;
-#pragma unroll
-      for (int dc = 0; dc < 2; ++dc) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, sK[buf][arow * 8 + ((4 * dc + g) ^ swz(arow))]);
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-          sacc[qt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[qt][dc], dc == 0 ? negm[qt] : sacc[qt][kt], 0, 0, 0);
-      }
+  for (int qt = 0; qt < kQT; ++qt) {
+    lsum[qt] = sum_xor16(sum_xor32(lrun[qt]));
+    tiny |= c.valid[qt] && !(lsum[qt] >= kTinySum);
+  }
+  if (__syncthreads_or(tiny)) {
+    if (tid == 0) {
+      const int slot = atomicAdd(a.fb_count, 1);
+      a.fb_list[slot] = w;
     }
-    if ((t + 1) * kKeyTile > a.lk) {  // ragged key tail: only the last tile
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (t * kKeyTile + kt * 16 + 4 * g + r >= a.lk) {
-#pragma unroll
-            for (int qt = 0; qt < QT; ++qt) sacc[qt][kt][r] = -INFINITY;
-          }
-    }
+    return;
+  }
+  store_unit(a, u, c, g, oacc, lsum, mref);
+}
 
-    bf16x8 bp[QT][2];
+// Exact path for queued units: online max (raised only when a score exceeds
+// it by more than 8 in log2 units; the final division makes it exact).
+__global__ __launch_bounds__(kNW * 64) void attn_exact(AttnArgs a) {
+  __shared__ u32x4 sK[2][kKeyTile * 8];
+  __shared__ u32x4 sV[2][kD * 8];
+  if ((int)blockIdx.x >= *a.fb_count) return;
+  const int w = a.fb_list[blockIdx.x];
+  Unit u;
+  if (!locate(a, w, kRows, u)) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, l16 = lane & 15;
+  UnitCtx c;
+  float qn2[kQT];
+  unit_setup(a, u, wave, g, l16, c, qn2);
+  f32x4 negm[kQT];
+  float mref[kQT], lrun[kQT];
+  f32x4 oacc[kQT][4];
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      // tree of max3 over the lane's 16 scores, then across the 4 lane rows
+  for (int qt = 0; qt < kQT; ++qt) {
+    mref[qt] = 0.f;
+    lrun[qt] = 0.f;
+    negm[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  load_tile(a, c, sK, sV, c.t0, 0, wave, lane);
+  for (int t = c.t0; t < c.t1; ++t) {
+    const int buf = (t - c.t0) & 1;
+    wait_vm();
+    __syncthreads();
+    if (t + 1 < c.t1) load_tile(a, c, sK, sV, t + 1, buf ^ 1, wave, lane);
+    f32x4 sacc[kQT][4];
+    scores(sK[buf], c, negm, g, l16, sacc);
+    if ((t + 1) * kKeyTile > a.lk) mask_tail(a, t, g, sacc);
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) {
       const f32x4* sa = sacc[qt];
       const float m0 = max3(sa[0][0], sa[0][1], sa[0][2]), m1 = max3(sa[0][3], sa[1][0], sa[1][1]);
       const float m2 = max3(sa[1][2], sa[1][3], sa[2][0]), m3 = max3(sa[2][1], sa[2][2], sa[2][3]);
       const float m4 = max3(sa[3][0], sa[3][1], sa[3][2]);
       float mx = fmaxf(max3(m0, m1, m2), max3(m3, m4, sa[3][3]));
       mx = max_xor16(max_xor32(mx));
-      // Raise the running max only on the first tile or when a score exceeds
-      // it by more than 8 (log2 units); the final division makes it exact.
-      const bool grow = (t == 0) || mx > 8.0f;
+      const bool first = (t == c.t0);
+      const bool grow = first || mx > 8.0f;
       if (__any(grow)) {
         float shift = 0.f;
         if (grow) {
-          const float mnew = mrun[qt] + mx;
           shift = mx;
-          mrun[qt] = mnew;
+          mref[qt] += mx;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) negm[qt][r] = -mnew;
+          for (int r = 0; r < 4; ++r) negm[qt][r] = -mref[qt];
         }
-        if (t > 0) {
+        if (!first) {
           const float alpha = __builtin_amdgcn_exp2f(-shift);
           lrun[qt] *= alpha;
 #pragma unroll
@@ -249,65 +414,60 @@ __global__ __launch_bounds__(NW * 64) void attn16(AttnArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) sacc[qt][kt][r] -= shift;
       }
-      // probabilities (bf16) and their sum over the same rounded values,
-      // in four independent partial sums
-      const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-      float ls[4] = {lrun[qt], 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        bf16x8 pb;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pb[r] = (__bf16)__builtin_amdgcn_exp2f(sacc[qt][2 * kc][r]);
-          pb[4 + r] = (__bf16)__builtin_amdgcn_exp2f(sacc[qt][2 * kc + 1][r]);
-        }
-        bp[qt][kc] = pb;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 pr = {pb[e], pb[e + 1]};
-          ls[e >> 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls[e >> 1], false);
-        }
-      }
-      lrun[qt] = (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
+    bf16x8 bp[kQT][2];
+    probs(sacc, bp, lrun);
+    pv(sV[buf], bp, g, l16, oacc);
+  }
+  float lsum[kQT];
+#pragma unroll
+  for (int qt = 0; qt < kQT; ++qt) lsum[qt] = sum_xor16(sum_xor32(lrun[qt]));
+  store_unit(a, u, c, g, oacc, lsum, mref);
+}
 
-    // O^T += V^T P^T
+// Combine the key-split partials of every packed row (split order fixed):
+// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
+__global__ __launch_bounds__(256) void attn_finalize(AttnArgs a) {
+  __shared__ int sTot;
+  if (threadIdx.x == 0) {
+    int t = 0;
+    for (int h = 0; h < a.heads; ++h) t += a.lenq ? a.lenq[h] : a.lq_uniform;
+    sTot = t;
+  }
+  __syncthreads();
+  const int64_t R = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int part = threadIdx.x & 7;
+  if (R >= sTot) return;
+  // splits with an empty key range (or an all-zero sum) carry no weight
+  float M = -INFINITY;
+  for (int s = 0; s < a.split; ++s) {
+    const size_t pr = (size_t)s * a.q_capacity + R;
+    if (a.lpart[pr] > 0.f) M = fmaxf(M, a.mpart[pr]);
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, l = 0.f;
+  for (int s = 0; s < a.split; ++s) {
+    const size_t pr = (size_t)s * a.q_capacity + R;
+    if (!(a.lpart[pr] > 0.f)) continue;
+    const float f = __builtin_amdgcn_exp2f(a.mpart[pr] - M);
+    l = fmaf(f, a.lpart[pr], l);
+    const f32x4* src = reinterpret_cast<const f32x4*>(a.opart + pr * kD + part * 8);
+    const f32x4 x0 = src[0], x1 = src[1];
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int vrow = dt * 16 + l16;
-        const u32x2* base = reinterpret_cast<const u32x2*>(&sV[buf][vrow * 8]);
-        const int c0 = 4 * kc + (g >> 1), c1 = 4 * kc + 2 + (g >> 1);
-        const u32x2 lo = base[2 * (c0 ^ swz(vrow)) + (g & 1)];
-        const u32x2 hi = base[2 * (c1 ^ swz(vrow)) + (g & 1)];
-        u32x4 va;
-        va[0] = lo[0];
-        va[1] = lo[1];
-        va[2] = hi[0];
-        va[3] = hi[1];
-        const bf16x8 vb = __builtin_bit_cast(bf16x8, va);
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-          oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, bp[qt][kc], oacc[qt][dt], 0, 0, 0);
-      }
+    for (int e = 0; e < 4; ++e) {
+      acc[e] = fmaf(f, x0[e], acc[e]);
+      acc[4 + e] = fmaf(f, x1[e], acc[4 + e]);
     }
   }
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] *= inv;
+  Row8<uint16_t>::store(reinterpret_cast<uint16_t*>(a.o) + R * kD + part * 8, acc);
+}
 
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const float inv = 1.0f / sum_xor16(sum_xor32(lrun[qt]));
-    if (valid[qt]) {
-      uint16_t* Op = reinterpret_cast<uint16_t*>(a.o) + ((size_t)cu + qrow[qt]) * kD;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        u32x2 w2;
-        w2[0] = (uint32_t)f2bf(oacc[qt][dt][0] * inv) | ((uint32_t)f2bf(oacc[qt][dt][1] * inv) << 16);
-        w2[1] = (uint32_t)f2bf(oacc[qt][dt][2] * inv) | ((uint32_t)f2bf(oacc[qt][dt][3] * inv) << 16);
-        *reinterpret_cast<u32x2*>(Op + dt * 16 + 4 * g) = w2;
-      }
-    }
-  }
+__global__ void attn_init(float* kmax, int heads, int* fb_count) {
+  const int i = threadIdx.x;
+  if (i < heads) kmax[i] = 0.f;
+  if (i == 0) *fb_count = 0;
 }
 
 // fp32 inputs: one thread per query row, key tiles staged in LDS, fp32
@@ -315,8 +475,9 @@ __global__ __launch_bounds__(NW * 64) void attn16(AttnArgs a) {
 __global__ __launch_bounds__(kRowsF32) void attn_f32(AttnArgs a) {
   __shared__ float sK[kKeyTile][kD + 1];
   __shared__ float sV[kD][kKeyTile + 1];
-  int head, cu, L, tile;
-  if (!locate(a, blockIdx.x, kRowsF32, head, cu, L, tile)) return;
+  Unit u;
+  if (!locate(a, blockIdx.x, kRowsF32, u)) return;
+  const int head = u.head, cu = u.cu, L = u.L, tile = u.tile;
   const float* Qp = reinterpret_cast<const float*>(a.q);
   const float* Kp = reinterpret_cast<const float*>(a.k) + (size_t)head * a.k_rows * kD;
   const float* Vp = reinterpret_cast<const float*>(a.vt) + (size_t)head * kD * a.vt_pitch;
@@ -358,6 +519,22 @@ __global__ __launch_bounds__(kRowsF32) void attn_f32(AttnArgs a) {
 
 }  // namespace
 
+int attention_split(int64_t q_capacity, int heads) {
+  // Enough units for ~4 rounds of resident workgroups on 256 CUs at 4
+  // workgroups each; at most 4 splits.
+  const int64_t units = (q_capacity + kRows - 1) / kRows + heads;
+  const int64_t want = 4 * 1024;
+  int s = (int)((want + units - 1) / units);
+  return s < 1 ? 1 : (s > 4 ? 4 : s);
+}
+
+int attention_rows_per_unit() { return kRows; }
+
+hipError_t launch_attn_init(float* kmax, int heads, int* fb_count, hipStream_t stream) {
+  hipLaunchKernelGGL(attn_init, dim3(1), dim3(64), 0, stream, kmax, heads, fb_count);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(int dtype, const AttnShape& s, const void* q, const void* k,
                             const void* vt, const int32_t* lenq, void* o, hipStream_t stream) {
   AttnArgs a;
@@ -365,18 +542,31 @@ hipError_t launch_attention(int dtype, const AttnShape& s, const void* q, const 
   a.k = k;
   a.vt = vt;
   a.o = o;
+  a.opart = s.opart;
+  a.lpart = s.lpart;
+  a.mpart = s.mpart;
+  a.kmax = s.kmax;
+  a.fb_count = s.fb_count;
+  a.fb_list = s.fb_list;
   a.lenq = lenq;
   a.heads = s.heads;
   a.lk = s.lk;
   a.k_rows = s.k_rows;
   a.vt_pitch = s.vt_pitch;
   a.lq_uniform = s.lq_uniform;
-  a.scale_log2 = s.scale * 1.4426950408889634f;
+  a.split = dtype == 1 ? s.split : 1;
+  a.q_capacity = s.q_capacity;
   if (dtype == 1) {
-    constexpr int kQT = 2, kNW = 4, kRows = kNW * kQT * 16;
-    a.total_wg = (int)((s.q_capacity + kRows - 1) / kRows + s.heads);
+    a.total_wg = (int)(((s.q_capacity + kRows - 1) / kRows + s.heads) * a.split);
     const int grid = ((a.total_wg + 7) / 8) * 8;
-    hipLaunchKernelGGL((attn16<kQT, kNW>), dim3(grid), dim3(kNW * 64), 0, stream, a);
+    hipLaunchKernelGGL(attn_fast, dim3(grid), dim3(kNW * 64), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_exact, dim3(a.total_wg), dim3(kNW * 64), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess || a.split == 1) return e;
+    const int fgrid = (int)((s.q_capacity + 31) / 32);
+    hipLaunchKernelGGL(attn_finalize, dim3(fgrid), dim3(256), 0, stream, a);
   } else {
     a.total_wg = (int)((s.q_capacity + kRowsF32 - 1) / kRowsF32 + s.heads);
     hipLaunchKernelGGL(attn_f32, dim3(a.total_wg), dim3(kRowsF32), 0, stream, a);

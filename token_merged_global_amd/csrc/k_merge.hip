@@ -33,6 +33,40 @@ __device__ __forceinline__ void load8(const T* p, float* x) { Row8<T>::load(p, x
 template <typename T>
 __device__ __forceinline__ void store8(T* p, const float* x) { Row8<T>::store(p, x); }
 
+// Stored value of x in storage type T (what the attention MFMA reads).
+template <typename T>
+__device__ __forceinline__ float stored(float x) {
+  if constexpr (sizeof(T) == 2) return bf2f(f2bf(x));
+  return x;
+}
+
+// 8 consecutive lanes hold one row of T values (8 channels each): the row's
+// L2 norm, valid in every lane of the group.
+template <typename T>
+__device__ __forceinline__ float row_norm8(const float* x) {
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float r = stored<T>(x[e]);
+    ss += r * r;
+  }
+  ss += __shfl_xor(ss, 1);
+  ss += __shfl_xor(ss, 2);
+  ss += __shfl_xor(ss, 4);
+  return sqrtf(ss);
+}
+
+// Workgroup max of per-thread values, then one atomic max into *gmax
+// (non-negative floats order like their bit patterns, so the result does not
+// depend on arrival order).  Every thread of the workgroup must call it.
+__device__ __forceinline__ void wg_atomic_max(float v, unsigned* smax, float* gmax) {
+  if (threadIdx.x == 0) *smax = 0u;
+  __syncthreads();
+  if (v > 0.f) atomicMax(smax, __float_as_uint(v));
+  __syncthreads();
+  if (threadIdx.x == 0 && *smax) atomicMax(reinterpret_cast<unsigned*>(gmax), *smax);
+}
+
 // Merged K and V.  One workgroup = 64 consecutive key slots of one head;
 // 8 lanes per slot, 8 channels per lane.  K~ rows are written directly,
 // multiplied by kscale (the softmax scale times log2 e, so that the
@@ -45,8 +79,9 @@ __global__ __launch_bounds__(256) void merge_kv(int N, int lk, int lk_pad, float
                                                 const T* __restrict__ v,
                                                 const int32_t* __restrict__ members,
                                                 const int32_t* __restrict__ off, T* __restrict__ kt,
-                                                T* __restrict__ vt) {
+                                                T* __restrict__ vt, float* __restrict__ kmax) {
   __shared__ float sV[kD][65];
+  __shared__ unsigned sMax;
   const int tiles = lk_pad / 64;
   const int head = blockIdx.x / tiles, tile = blockIdx.x % tiles;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -55,6 +90,7 @@ __global__ __launch_bounds__(256) void merge_kv(int N, int lk, int lk_pad, float
   const T* V = v + (size_t)head * N * kD;
   const int32_t* mem = members + (size_t)head * N;
   const int32_t* of = off + (size_t)head * (lk + 1);
+  float nmax = 0.f;
 #pragma unroll
   for (int round = 0; round < 2; ++round) {
     const int ls = wave * 16 + round * 8 + sub;
@@ -83,10 +119,12 @@ __global__ __launch_bounds__(256) void merge_kv(int N, int lk, int lk_pad, float
       }
     }
     store8(kt + ((size_t)head * lk_pad + slot) * kD + part * 8, km);
+    const float nrm = row_norm8<T>(km);
+    if (slot < lk) nmax = fmaxf(nmax, nrm);
 #pragma unroll
     for (int e = 0; e < 8; ++e) sV[part * 8 + e][ls] = vm[e];
   }
-  __syncthreads();
+  wg_atomic_max(nmax, &sMax, kmax + head);  // also orders the sV writes before the reads below
   for (int idx = tid; idx < kD * 8; idx += 256) {
     const int c = idx >> 3, j = idx & 7;
     float x[8];
@@ -377,21 +415,30 @@ __global__ __launch_bounds__(256) void unmerge(int64_t rows, const int32_t* __re
 template <typename T>
 __global__ __launch_bounds__(256) void prep_dense(int N, int pitch, float kscale, const T* __restrict__ k,
                                                   const T* __restrict__ v, T* __restrict__ kc,
-                                                  T* __restrict__ vt) {
+                                                  T* __restrict__ vt, float* __restrict__ kmax) {
   __shared__ float sT[kD][65];
+  __shared__ unsigned sMax;
   const int tiles = pitch / 64;
   const int head = blockIdx.x / tiles, tile = blockIdx.x % tiles;
   const T* K = k + (size_t)head * N * kD;
   const T* V = v + (size_t)head * N * kD;
+  float nmax = 0.f;
   for (int idx = threadIdx.x; idx < 64 * 8; idx += 256) {
     const int r = idx >> 3, j = idx & 7;
     const int n = tile * 64 + r;
     float x[8];
-    if (n < N) {
-      load8(K + (size_t)n * kD + j * 8, x);
+    float kx[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] *= kscale;
-      store8(kc + ((size_t)head * N + n) * kD + j * 8, x);
+    for (int e = 0; e < 8; ++e) kx[e] = 0.f;
+    if (n < N) {
+      load8(K + (size_t)n * kD + j * 8, kx);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kx[e] *= kscale;
+      store8(kc + ((size_t)head * N + n) * kD + j * 8, kx);
+    }
+    const float nrm = row_norm8<T>(kx);
+    if (n < N) nmax = fmaxf(nmax, nrm);
+    if (n < N) {
       load8(V + (size_t)n * kD + j * 8, x);
     } else {
 #pragma unroll
@@ -400,7 +447,7 @@ __global__ __launch_bounds__(256) void prep_dense(int N, int pitch, float kscale
 #pragma unroll
     for (int e = 0; e < 8; ++e) sT[j * 8 + e][r] = x[e];
   }
-  __syncthreads();
+  wg_atomic_max(nmax, &sMax, kmax + head);  // also orders the sT writes before the reads below
   for (int idx = threadIdx.x; idx < 64 * 8; idx += 256) {
     const int c = idx >> 3, j = idx & 7;
     float x[8];
@@ -425,11 +472,11 @@ __global__ __launch_bounds__(256) void prep_dense(int N, int pitch, float kscale
 
 hipError_t launch_merge_kv(int dtype, int heads, int N, int lk, int lk_pad, float kscale, const void* k,
                            const void* v, const int32_t* members, const int32_t* off, void* kt,
-                           void* vt, hipStream_t stream) {
+                           void* vt, float* kmax, hipStream_t stream) {
   const int grid = heads * (lk_pad / 64);
   HTTM_DISPATCH(dtype, hipLaunchKernelGGL(merge_kv<T>, dim3(grid), dim3(256), 0, stream, N, lk,
                                           lk_pad, kscale, (const T*)k, (const T*)v, members, off, (T*)kt,
-                                          (T*)vt));
+                                          (T*)vt, kmax));
   return hipGetLastError();
 }
 
@@ -476,10 +523,10 @@ hipError_t launch_unmerge(int dtype, int heads, int N, const int32_t* slot, cons
 }
 
 hipError_t launch_prep_dense(int dtype, int heads, int N, int pitch, float kscale, const void* k,
-                             const void* v, void* kc, void* vt, hipStream_t stream) {
+                             const void* v, void* kc, void* vt, float* kmax, hipStream_t stream) {
   const int grid = heads * (pitch / 64);
   HTTM_DISPATCH(dtype, hipLaunchKernelGGL(prep_dense<T>, dim3(grid), dim3(256), 0, stream, N, pitch, kscale,
-                                          (const T*)k, (const T*)v, (T*)kc, (T*)vt));
+                                          (const T*)k, (const T*)v, (T*)kc, (T*)vt, kmax));
   return hipGetLastError();
 }
 

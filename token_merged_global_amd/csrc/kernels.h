@@ -26,10 +26,11 @@ hipError_t launch_select(const Geo& g, const int32_t* match_q, const float* scor
                          hipStream_t stream);
 
 // Means of K and V over the key partition: kt [h][lk_pad][64] (times kscale),
-// vt [h][64][lk_pad].
+// vt [h][64][lk_pad]; kmax[h] = max over the head's merged keys of |kt row|
+// (atomic max into a zeroed buffer).
 hipError_t launch_merge_kv(int dtype, int heads, int N, int lk, int lk_pad, float kscale, const void* k,
                            const void* v, const int32_t* members, const int32_t* off, void* kt,
-                           void* vt, hipStream_t stream);
+                           void* vt, float* kmax, hipStream_t stream);
 
 // Query group sums (fp32) and deviation of every query to its group mean.
 hipError_t launch_merge_q(int dtype, int heads, int N, int gq, const void* q,
@@ -71,7 +72,19 @@ struct AttnShape {
   int lq_uniform;  // used when lenq == nullptr
   int64_t q_capacity;
   float scale;
+  int split;               // key splits (bf16); partial buffers needed when > 1
+  float* opart;            // [split][q_capacity][64]
+  float* lpart;            // [split][q_capacity]
+  float* mpart;            // [split][q_capacity]
+  const float* kmax;       // [heads] max |k row|
+  int* fb_count;           // [1] units queued for the exact kernel (zeroed by launch_attn_init)
+  int* fb_list;            // [units]
 };
+// Key splits for a layer of q_capacity packed rows; rows per work unit.
+int attention_split(int64_t q_capacity, int heads);
+int attention_rows_per_unit();
+// Zero kmax[heads] and the fallback queue counter (before the K producer runs).
+hipError_t launch_attn_init(float* kmax, int heads, int* fb_count, hipStream_t stream);
 hipError_t launch_attention(int dtype, const AttnShape& s, const void* q, const void* k,
                             const void* vt, const int32_t* lenq, void* o, hipStream_t stream);
 
@@ -82,6 +95,6 @@ hipError_t launch_unmerge(int dtype, int heads, int N, const int32_t* slot, cons
 // Unmerged baseline inputs: kc = k * kscale ([h][N][64]); vt[h][c][n] =
 // v[h][n][c], zero for n in [N, pitch).
 hipError_t launch_prep_dense(int dtype, int heads, int N, int pitch, float kscale, const void* k,
-                             const void* v, void* kc, void* vt, hipStream_t stream);
+                             const void* v, void* kc, void* vt, float* kmax, hipStream_t stream);
 
 }  // namespace httm
