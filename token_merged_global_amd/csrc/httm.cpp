@@ -45,7 +45,7 @@ struct Region {
 struct Layout {
   Region match[2], score[2];
   Region q_members, q_off, q_group, k_group;
-  Region qsum, delta, mask, radix, base;
+  Region qsum, delta, mask, radix, base, ocnt;
   Region qt, kt, vt, o;
   Region kmax, fb, opart, lpart, mpart;  // attention: key norms, fallback queue, split partials
   Region index;  // used when the caller passes no index buffer
@@ -239,6 +239,7 @@ httm_status build(const httm_params& p, httm_plan* pl) {
     Lw.mask = b.take(h * n);
     Lw.radix = b.take(4 * outlier_scratch_words((int64_t)h * n));
     Lw.base = b.take(4 * h * (size_t)g.nslots[kQ]);
+    Lw.ocnt = b.take(4 * h * (size_t)g.nslots[kQ]);
     Lw.qt = b.take(E * (size_t)pl->q_cap * kD);
     Lw.kt = b.take(E * h * (size_t)pl->lk_pad * kD);
     Lw.vt = b.take(E * h * (size_t)pl->lk_pad * kD);
@@ -471,11 +472,12 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
   ro.lenq = reinterpret_cast<int32_t*>(idx + I.lenq.off);
   ro.cu_q = reinterpret_cast<int32_t*>(idx + I.cu_q.off);
   ro.base = at<int32_t>(ws, L.base);
+  ro.ocnt = at<int32_t>(ws, L.ocnt);
   ro.fmembers = reinterpret_cast<int32_t*>(idx + I.fmembers.off);
   ro.foff = reinterpret_cast<int32_t*>(idx + I.foff.off);
   ro.slot = reinterpret_cast<int32_t*>(idx + I.slot.off);
   stage_begin(HTTM_T_RESTORE, st);
-  CHECK_LAUNCH(launch_restore(dt, g.heads, g.N, g.nslots[kQ], q, cq.members, cq.off,
+  CHECK_LAUNCH(launch_restore(dt, g.heads, g.N, g.nslots[kQ], q, cq.members, cq.off, cq.group,
                               at<float>(ws, L.qsum), at<uint8_t>(ws, L.mask), ro, st));
   stage_end(HTTM_T_RESTORE, st);
 

@@ -67,15 +67,49 @@ __device__ __forceinline__ void wg_atomic_max(float v, unsigned* smax, float* gm
   if (threadIdx.x == 0 && *smax) atomicMax(reinterpret_cast<unsigned*>(gmax), *smax);
 }
 
-// Merged K and V.  One workgroup = 64 consecutive key slots of one head;
-// 8 lanes per slot, 8 channels per lane.  K~ rows are written directly,
-// multiplied by kscale (the softmax scale times log2 e, so that the
+// Gather-sum of one CSR segment [m0, m1) of member rows, 8 channels per lane,
+// in member order with separately rounded fp32 adds.  Member ids are fetched
+// C at a time and all C rows are requested before the first add, so a lane
+// keeps up to C row loads (times the number of tensors) in flight instead of
+// one dependent chain per member.  Rows past m1 re-read the segment's first
+// row (already in flight) and are not added.
+template <typename T, int C, int NT>
+__device__ __forceinline__ void gather_sum(const T* const (&X)[NT], const int32_t* __restrict__ mem, int m0,
+                                           int m1, int part, float (&acc)[NT][8]) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
+  for (int mb = m0; mb < m1; mb += C) {
+    int tok[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j) tok[j] = mem[mb + j < m1 ? mb + j : mb];
+    float x[C][NT][8];
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) load8(X[t] + (size_t)tok[j] * kD + part * 8, x[j][t]);
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      if (mb + j < m1) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[t][e] = __fadd_rn(acc[t][e], x[j][t][e]);
+      }
+    }
+  }
+}
+
+// Merged K and V.  One workgroup (512 threads) = 64 consecutive key slots of
+// one head; 8 lanes per slot, 8 channels per lane.  K~ rows are written
+// directly, multiplied by kscale (the softmax scale times log2 e, so that the
 // attention kernel's scores come out in exp2 units; the product is rounded
 // once to the storage type with the mean).  V~ means go through LDS and are
 // written transposed (vt[h][c][slot]) so that the attention kernel reads V~
 // along keys with plain row loads.
 template <typename T>
-__global__ __launch_bounds__(256) void merge_kv(int N, int lk, int lk_pad, float kscale, const T* __restrict__ k,
+__global__ __launch_bounds__(512) void merge_kv(int N, int lk, int lk_pad, float kscale, const T* __restrict__ k,
                                                 const T* __restrict__ v,
                                                 const int32_t* __restrict__ members,
                                                 const int32_t* __restrict__ off, T* __restrict__ kt,
@@ -84,49 +118,35 @@ __global__ __launch_bounds__(256) void merge_kv(int N, int lk, int lk_pad, float
   __shared__ unsigned sMax;
   const int tiles = lk_pad / 64;
   const int head = blockIdx.x / tiles, tile = blockIdx.x % tiles;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int sub = lane >> 3, part = lane & 7;
-  const T* K = k + (size_t)head * N * kD;
-  const T* V = v + (size_t)head * N * kD;
+  const int tid = threadIdx.x;
+  const int ls = tid >> 3, part = tid & 7;
+  const int slot = tile * 64 + ls;
+  const T* const X[2] = {k + (size_t)head * N * kD, v + (size_t)head * N * kD};
   const int32_t* mem = members + (size_t)head * N;
   const int32_t* of = off + (size_t)head * (lk + 1);
+  float acc[2][8];
   float nmax = 0.f;
+  if (slot < lk) {
+    const int m0 = of[slot], m1 = of[slot + 1];
+    gather_sum<T, 4, 2>(X, mem, m0, m1, part, acc);
+    const float cnt = (float)(m1 - m0);
 #pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    const int ls = wave * 16 + round * 8 + sub;
-    const int slot = tile * 64 + ls;
-    float km[8], vm[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) km[e] = vm[e] = 0.f;
-    if (slot < lk) {
-      const int m0 = of[slot], m1 = of[slot + 1];
-      for (int m = m0; m < m1; ++m) {
-        const int tok = mem[m];
-        float xk[8], xv[8];
-        load8(K + (size_t)tok * kD + part * 8, xk);
-        load8(V + (size_t)tok * kD + part * 8, xv);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          km[e] = __fadd_rn(km[e], xk[e]);
-          vm[e] = __fadd_rn(vm[e], xv[e]);
-        }
-      }
-      const float cnt = (float)(m1 - m0);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        km[e] = rn_div(km[e], cnt) * kscale;
-        vm[e] = rn_div(vm[e], cnt);
-      }
+    for (int e = 0; e < 8; ++e) {
+      acc[0][e] = rn_div(acc[0][e], cnt) * kscale;
+      acc[1][e] = rn_div(acc[1][e], cnt);
     }
-    store8(kt + ((size_t)head * lk_pad + slot) * kD + part * 8, km);
-    const float nrm = row_norm8<T>(km);
-    if (slot < lk) nmax = fmaxf(nmax, nrm);
+  } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sV[part * 8 + e][ls] = vm[e];
+    for (int e = 0; e < 8; ++e) acc[0][e] = acc[1][e] = 0.f;
   }
+  store8(kt + ((size_t)head * lk_pad + slot) * kD + part * 8, acc[0]);
+  const float nrm = row_norm8<T>(acc[0]);
+  if (slot < lk) nmax = nrm;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sV[part * 8 + e][ls] = acc[1][e];
   wg_atomic_max(nmax, &sMax, kmax + head);  // also orders the sV writes before the reads below
-  for (int idx = tid; idx < kD * 8; idx += 256) {
-    const int c = idx >> 3, j = idx & 7;
+  {
+    const int c = tid >> 3, j = tid & 7;
     float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = sV[c][j * 8 + e];
@@ -141,7 +161,7 @@ __global__ __launch_bounds__(256) void merge_kv(int N, int lk, int lk_pad, float
 // order; members of the 64 groups are contiguous in the CSR, a binary search
 // over the 65 offsets finds each member's group.
 template <typename T>
-__global__ __launch_bounds__(256) void merge_q(int N, int gq, const T* __restrict__ q,
+__global__ __launch_bounds__(512) void merge_q(int N, int gq, const T* __restrict__ q,
                                                const int32_t* __restrict__ members,
                                                const int32_t* __restrict__ off,
                                                float* __restrict__ qsum,
@@ -152,43 +172,32 @@ __global__ __launch_bounds__(256) void merge_q(int N, int gq, const T* __restric
   const int head = blockIdx.x / tiles, tile = blockIdx.x % tiles;
   const int g0 = tile * 64;
   const int ng = min(64, gq - g0);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int sub = lane >> 3, part = lane & 7;
-  const T* Q = q + (size_t)head * N * kD;
+  const int tid = threadIdx.x;
+  const int ls = tid >> 3, part = tid & 7;
+  const T* const X[1] = {q + (size_t)head * N * kD};
   const int32_t* mem = members + (size_t)head * N;
   const int32_t* of = off + (size_t)head * (gq + 1);
   if (tid <= ng) sOff[tid] = of[g0 + tid];
+  if (ls < ng) {
+    const int grp = g0 + ls;
+    const int m0 = of[grp], m1 = of[grp + 1];
+    float sm[1][8];
+    gather_sum<T, 8, 1>(X, mem, m0, m1, part, sm);
+    Row8<float>::store(qsum + ((size_t)head * gq + grp) * kD + part * 8, sm[0]);
+    const float cnt = (float)(m1 - m0);
 #pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    const int ls = wave * 16 + round * 8 + sub;
-    if (ls < ng) {
-      const int grp = g0 + ls;
-      const int m0 = of[grp], m1 = of[grp + 1];
-      float sm[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm[e] = 0.f;
-      for (int m = m0; m < m1; ++m) {
-        float x[8];
-        load8(Q + (size_t)mem[m] * kD + part * 8, x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sm[e] = __fadd_rn(sm[e], x[e]);
-      }
-      Row8<float>::store(qsum + ((size_t)head * gq + grp) * kD + part * 8, sm);
-      const float cnt = (float)(m1 - m0);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sMean[ls][part * 8 + e] = rn_div(sm[e], cnt);
-    }
+    for (int e = 0; e < 8; ++e) sMean[ls][part * 8 + e] = rn_div(sm[0][e], cnt);
   }
   __syncthreads();
   const int mb = sOff[0], me = sOff[ng];
-  for (int m = mb + tid; m < me; m += 256) {
+  for (int m = mb + tid; m < me; m += 512) {
     int lo = 0, hi = ng - 1;  // largest j with sOff[j] <= m
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (sOff[mid] <= m) lo = mid; else hi = mid - 1;
     }
     const int tok = mem[m];
-    const T* row = Q + (size_t)tok * kD;
+    const T* row = X[0] + (size_t)tok * kD;
     float acc = 0.f;
 #pragma unroll
     for (int c8 = 0; c8 < 8; ++c8) {
@@ -229,40 +238,50 @@ __device__ int block_exclusive_scan(int v, int* sh /* >= 16 */, int& total) {
   return sh[wave] + x - v;
 }
 
+// Restore, part 0: per initial query group, the number of outlier members
+// (integer atomics, one thread per token; the counts do not depend on order).
+__global__ __launch_bounds__(256) void restore_count(int64_t total, int N, int gq,
+                                                     const uint8_t* __restrict__ mask,
+                                                     const int32_t* __restrict__ group,
+                                                     int32_t* __restrict__ ocnt) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total || !mask[i]) return;
+  const int head = (int)(i / N);
+  atomicAdd(&ocnt[(size_t)head * gq + group[i]], 1);
+}
+
+__global__ __launch_bounds__(256) void zero_i32(int32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
 // Restore, part 1 (one workgroup per head): each initial query group g with
 // c members of which o are outliers yields (c > o) + o final slots; an
 // exclusive scan gives every group its first final slot; the head's final
 // length goes to lenq and closes the final offsets with N.
-__global__ __launch_bounds__(1024) void restore_scan(int N, int gq,
-                                                     const int32_t* __restrict__ members,
-                                                     const int32_t* __restrict__ off,
-                                                     const uint8_t* __restrict__ mask,
+__global__ __launch_bounds__(1024) void restore_scan(int N, int gq, const int32_t* __restrict__ off,
+                                                     const int32_t* __restrict__ ocnt,
                                                      int32_t* __restrict__ base,
                                                      int32_t* __restrict__ lenq,
                                                      int32_t* __restrict__ foff) {
   __shared__ int sh[17];
   const int head = blockIdx.x;
-  const int32_t* mem = members + (size_t)head * N;
   const int32_t* of = off + (size_t)head * (gq + 1);
-  const uint8_t* mk = mask + (size_t)head * N;
+  const int32_t* oc = ocnt + (size_t)head * gq;
   int32_t* bs = base + (size_t)head * gq;
   const int per = ceil_div(gq, 1024);
   const int gb = threadIdx.x * per, ge = min(gq, gb + per);
   int local = 0;
   for (int g = gb; g < ge; ++g) {
-    const int m0 = of[g], m1 = of[g + 1];
-    int o = 0;
-    for (int m = m0; m < m1; ++m) o += mk[mem[m]];
-    const int n = ((m1 - m0) > o ? 1 : 0) + o;
-    bs[g] = n;
-    local += n;
+    const int c = of[g + 1] - of[g], o = oc[g];
+    local += (c > o ? 1 : 0) + o;
   }
   int total;
   int acc = block_exclusive_scan(local, sh, total);
   for (int g = gb; g < ge; ++g) {
-    const int n = bs[g];
+    const int c = of[g + 1] - of[g], o = oc[g];
     bs[g] = acc;
-    acc += n;
+    acc += (c > o ? 1 : 0) + o;
   }
   if (threadIdx.x == 0) {
     lenq[head] = total;
@@ -276,8 +295,11 @@ __device__ __forceinline__ int prefix_len(const int32_t* lenq, int head) {
   return cu;
 }
 
-// Restore, part 2: 8 lanes per initial query group.  Outlier members are
-// subtracted from the group sum and copied to their own rows; the remaining
+// Restore, part 2: 8 lanes per initial query group.  The 8 lanes look at 8
+// members at a time: ballots over the group's lanes rank survivors and
+// outliers in member order, so every member's final position is known
+// without a serial walk.  Outlier rows are then subtracted from the group
+// sum (in member order) and copied to their own packed rows; the remaining
 // members' mean becomes the group's row (if any remain).  Writes the packed
 // Q~ rows, the final partition (members reordered: remaining first, then
 // outliers) and every token's packed row for unmerge.
@@ -287,6 +309,7 @@ __global__ __launch_bounds__(256) void restore_rows(int heads, int N, int gq, co
                                                     const int32_t* __restrict__ off,
                                                     const float* __restrict__ qsum,
                                                     const uint8_t* __restrict__ mask,
+                                                    const int32_t* __restrict__ ocnt,
                                                     const int32_t* __restrict__ base,
                                                     const int32_t* __restrict__ lenq,
                                                     int32_t* __restrict__ cu_q, T* __restrict__ qt,
@@ -298,7 +321,8 @@ __global__ __launch_bounds__(256) void restore_rows(int heads, int N, int gq, co
   const int tid = threadIdx.x;
   if (blockIdx.x == 0 && tid <= heads) cu_q[tid] = prefix_len(lenq, tid);
   const int g = tile * 32 + (tid >> 3), part = tid & 7;
-  if (g >= gq) return;
+  const int sub = (tid & 63) >> 3;
+  if (g >= gq) return;  // whole 8-lane groups leave together
   const int cu = prefix_len(lenq, head);
   const T* Q = q + (size_t)head * N * kD;
   const int32_t* mem = members + (size_t)head * N;
@@ -308,38 +332,50 @@ __global__ __launch_bounds__(256) void restore_rows(int heads, int N, int gq, co
   int32_t* fo = foff + (size_t)head * (N + 1);
   int32_t* sl = slot + (size_t)head * N;
   const int m0 = of[g], m1 = of[g + 1];
-  int o = 0;
-  for (int m = m0; m < m1; ++m) o += mk[mem[m]];
+  const int o = ocnt[(size_t)head * gq + g];
   const int nsurv = (m1 - m0) - o;
   const int surv = nsurv > 0 ? 1 : 0;
   const int b = cu + base[(size_t)head * gq + g];
   float sm[8];
-  Row8<float>::load(qsum + ((size_t)head * gq + g) * kD + part * 8, sm);
-  int ro = 0, ri = 0;
-  for (int m = m0; m < m1; ++m) {
-    const int tok = mem[m];
-    if (mk[tok]) {
+  if (surv) Row8<float>::load(qsum + ((size_t)head * gq + g) * kD + part * 8, sm);
+  const uint32_t below = (1u << part) - 1u;
+  int rs = 0, ro = 0;  // survivors / outliers seen so far
+  for (int mb = m0; mb < m1; mb += 8) {
+    const int m = mb + part;
+    const bool valid = m < m1;
+    const int tok = valid ? mem[m] : 0;
+    const bool isout = valid && mk[tok] != 0;
+    const uint32_t bo = (uint32_t)(__ballot(isout) >> (sub * 8)) & 0xFFu;
+    const uint32_t bv = (uint32_t)(__ballot(valid) >> (sub * 8)) & 0xFFu;
+    const uint32_t bs = bv & ~bo;
+    if (isout) {
+      const int j = ro + __popc(bo & below);
+      const int row = b + surv + j;
+      fm[m0 + nsurv + j] = tok;
+      fo[row - cu] = m0 + nsurv + j;
+      sl[tok] = row;
+    } else if (valid) {
+      fm[m0 + rs + __popc(bs & below)] = tok;
+      sl[tok] = b;
+    }
+    // outlier rows of this batch, in member order (all 8 lanes of the group)
+    uint32_t bits = bo;
+    int j = ro;
+    while (bits) {
+      const int src = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      const int t = __shfl(tok, (tid & 63 & ~7) + src);
       float x[8];
-      load8(Q + (size_t)tok * kD + part * 8, x);
+      load8(Q + (size_t)t * kD + part * 8, x);
       if (surv) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) sm[e] = __fsub_rn(sm[e], x[e]);
       }
-      const int row = b + surv + ro;
-      store8(qt + (size_t)row * kD + part * 8, x);
-      if (part == 0) {
-        fm[m0 + nsurv + ro] = tok;
-        fo[row - cu] = m0 + nsurv + ro;
-        sl[tok] = row;
-      }
-      ++ro;
-    } else {
-      if (part == 0) {
-        fm[m0 + ri] = tok;
-        sl[tok] = b;
-      }
-      ++ri;
+      store8(qt + (size_t)(b + surv + j) * kD + part * 8, x);
+      ++j;
     }
+    ro += __popc(bo);
+    rs += __popc(bs);
   }
   if (surv) {
     const float cnt = (float)nsurv;
@@ -474,7 +510,7 @@ hipError_t launch_merge_kv(int dtype, int heads, int N, int lk, int lk_pad, floa
                            const void* v, const int32_t* members, const int32_t* off, void* kt,
                            void* vt, float* kmax, hipStream_t stream) {
   const int grid = heads * (lk_pad / 64);
-  HTTM_DISPATCH(dtype, hipLaunchKernelGGL(merge_kv<T>, dim3(grid), dim3(256), 0, stream, N, lk,
+  HTTM_DISPATCH(dtype, hipLaunchKernelGGL(merge_kv<T>, dim3(grid), dim3(512), 0, stream, N, lk,
                                           lk_pad, kscale, (const T*)k, (const T*)v, members, off, (T*)kt,
                                           (T*)vt, kmax));
   return hipGetLastError();
@@ -484,21 +520,25 @@ hipError_t launch_merge_q(int dtype, int heads, int N, int gq, const void* q,
                           const int32_t* members, const int32_t* off, float* qsum, float* delta,
                           hipStream_t stream) {
   const int grid = heads * ceil_div(gq, 64);
-  HTTM_DISPATCH(dtype, hipLaunchKernelGGL(merge_q<T>, dim3(grid), dim3(256), 0, stream, N, gq,
+  HTTM_DISPATCH(dtype, hipLaunchKernelGGL(merge_q<T>, dim3(grid), dim3(512), 0, stream, N, gq,
                                           (const T*)q, members, off, qsum, delta));
   return hipGetLastError();
 }
 
 hipError_t launch_restore(int dtype, int heads, int N, int gq, const void* q,
-                          const int32_t* members, const int32_t* off, const float* qsum,
-                          const uint8_t* mask, RestoreOut o, hipStream_t stream) {
-  hipLaunchKernelGGL(restore_scan, dim3(heads), dim3(1024), 0, stream, N, gq, members, off, mask,
-                     o.base, o.lenq, o.foff);
+                          const int32_t* members, const int32_t* off, const int32_t* group,
+                          const float* qsum, const uint8_t* mask, RestoreOut o, hipStream_t stream) {
+  const int64_t groups = (int64_t)heads * gq, total = (int64_t)heads * N;
+  hipLaunchKernelGGL(zero_i32, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream, o.ocnt, groups);
+  hipLaunchKernelGGL(restore_count, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, total, N, gq,
+                     mask, group, o.ocnt);
+  hipLaunchKernelGGL(restore_scan, dim3(heads), dim3(1024), 0, stream, N, gq, off, o.ocnt, o.base, o.lenq,
+                     o.foff);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int grid = heads * ceil_div(gq, 32);
   HTTM_DISPATCH(dtype, hipLaunchKernelGGL(restore_rows<T>, dim3(grid), dim3(256), 0, stream,
-                                          heads, N, gq, (const T*)q, members, off, qsum, mask,
+                                          heads, N, gq, (const T*)q, members, off, qsum, mask, o.ocnt,
                                           o.base, o.lenq, o.cu_q, (T*)o.qt, o.fmembers, o.foff,
                                           o.slot));
   return hipGetLastError();

@@ -47,14 +47,15 @@ struct RestoreOut {
   void* qt;            // [q_capacity][64]
   int32_t* lenq;       // [h]
   int32_t* cu_q;       // [h+1]
-  int32_t* base;       // [h][gq] scratch
+  int32_t* base;       // [h][gq] scratch: first final slot of each initial group
+  int32_t* ocnt;       // [h][gq] scratch: outlier members per initial group
   int32_t* fmembers;   // [h][N]
   int32_t* foff;       // [h][N+1]
   int32_t* slot;       // [h][N] packed row per token
 };
 hipError_t launch_restore(int dtype, int heads, int N, int gq, const void* q,
-                          const int32_t* members, const int32_t* off, const float* qsum,
-                          const uint8_t* mask, RestoreOut o, hipStream_t stream);
+                          const int32_t* members, const int32_t* off, const int32_t* group,
+                          const float* qsum, const uint8_t* mask, RestoreOut o, hipStream_t stream);
 
 // Cached mode: Q~ rows as means over the final query partition.
 hipError_t launch_merge_q_cached(int dtype, int heads, int N, int64_t q_capacity, const void* q,
