@@ -84,4 +84,17 @@ GEO_HD int32_t block_token(const Geo& g, const BlockInfo& bi, int32_t i) {
 // Block position of the k-th source (positions with i mod s != 0).
 GEO_HD int32_t src_pos(int32_t k, int32_t s) { return k + k / (s - 1) + 1; }
 
+// Quotient n / d by one float product: with rcp = fl((1 + 2^-20) / d), the
+// rounded product fl(n * rcp) lies in [n/d, n/d + (n/d) 2^-19.8), and the
+// gap from n/d up to the next integer is at least 1/d, so truncation gives
+// the exact quotient for 0 <= n < 2^19 (checked exhaustively for d <= 4096).
+GEO_HD float div_rcp(int32_t d) { return (1.0f + 0x1p-20f) / (float)d; }
+GEO_HD int32_t div_small(int32_t n, float rcp) { return (int32_t)((float)n * rcp); }
+
+// block_token with precomputed div_rcp(bi.run).
+GEO_HD int32_t block_token_r(const Geo& g, const BlockInfo& bi, int32_t i, float rcp_run) {
+  const int32_t q = div_small(i, rcp_run);
+  return (bi.f0 + q) * g.T + g.nsp + bi.j0 + (i - q * bi.run);
+}
+
 }  // namespace httm

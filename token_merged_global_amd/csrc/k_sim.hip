@@ -6,13 +6,23 @@
 //
 // For each (stream in {Q, K}, head, block, chunk of 256 sources) one workgroup
 // of 4 waves streams the block's destination rows through LDS in tiles of 64
-// and multiplies them against the 256 source rows held in registers, with
-// v_mfma_f32_32x32x16_bf16 (exact bf16 products, fp32 accumulation).  The
-// products are never pre-normalised to bf16: the destination's inverse norm
-// (fp32) scales the fp32 dot product in the epilogue, the source's inverse
-// norm scales only the final maximum (it does not change the argmax).
+// and multiplies them against the 64 source rows each wave holds in registers,
+// with v_mfma_f32_16x16x32_bf16 (exact bf16 products, fp32 accumulation).
 // Rows are gathered straight from the [h][N][64] input through the temporal
 // reordering, so no reordered copy is ever written.
+//
+// Argmax epilogue.  Lane (g, l16) of a 16x16 output tile holds destinations
+// 4g..4g+3 of source column l16, so per 64-destination tile a lane sees 16
+// candidates of each of its 4 source columns, in ascending destination order.
+// Each candidate becomes v = dot * inv|d| + |s| (1 + 2^-10) with one FMA: the
+// offset makes every v positive, so its bit pattern orders like its value.
+// The low 4 bits of the pattern are replaced by 15 - (candidate position), and
+// one unsigned max3 tree then yields the maximum and its first position at
+// once (2.5 VALU ops per score).  The replaced bits bound the error of the
+// decision and of the reported cosine by 16 ulp of v (< 4e-6 for |v| < 4|s|):
+// candidates closer than that are near-ties.  Tiles are compared without the
+// position bits, so an earlier tile keeps a tie; the 4 lanes of a source are
+// combined last, ties going to the smaller destination.
 #include "common.h"
 #include "kernels.h"
 
@@ -34,29 +44,100 @@ struct SimArgs {
   int32_t total;
 };
 
-__device__ __forceinline__ void decode(const SimArgs& a, int w, int& st, int& head, int& b, int& chunk) {
-  st = 0;
-  if (w >= a.wgs[0]) { st = 1; w -= a.wgs[0]; }
-  chunk = w % a.chunks[st];
-  const int bh = w / a.chunks[st];
-  b = bh % a.g.nblocks;
-  head = bh / a.g.nblocks;
+// Workgroup -> (stream, head, block, source chunk).  The hardware hands
+// workgroup ids to the 8 XCDs round-robin; XCD x = id % 8 takes the
+// (head, block) pairs [x*HB/8, (x+1)*HB/8) with both streams, the longer
+// K-stream chunks first, so every XCD gets an equal share of the work and the
+// chunks of one block (which read the same destination rows) share its L2.
+__device__ __forceinline__ bool decode(const SimArgs& a, int bid, int& st, int& head, int& b, int& chunk) {
+  const int hb_total = a.g.heads * a.g.nblocks;
+  const int x = bid & 7, j = bid >> 3;
+  const int hb0 = (int)((int64_t)x * hb_total / 8), hb1 = (int)((int64_t)(x + 1) * hb_total / 8);
+  const int nk = (hb1 - hb0) * a.chunks[1];
+  int hb;
+  if (j < nk) {
+    st = 1;
+    hb = hb0 + j / a.chunks[1];
+    chunk = j % a.chunks[1];
+  } else {
+    const int jq = j - nk;
+    if (jq >= (hb1 - hb0) * a.chunks[0]) return false;
+    st = 0;
+    hb = hb0 + jq / a.chunks[0];
+    chunk = jq % a.chunks[0];
+  }
+  b = hb % a.g.nblocks;
+  head = hb / a.g.nblocks;
+  return true;
 }
 
-// Spread consecutive logical workgroups (chunks of one block) over one XCD:
-// hardware hands workgroup ids to the 8 XCDs round-robin.
-__device__ __forceinline__ int xcd_logical(int bid, int total) {
-  const int per = (total + 7) / 8;
-  return (bid % 8) * per + bid / 8;
+// 16-byte chunk c of LDS row r sits at chunk c ^ swz(r): the 16 consecutive
+// rows one A-operand read touches land in distinct bank groups.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// max(a, max(b, c)) on unsigned values lowers to one v_max3_u32.
+__device__ __forceinline__ uint32_t umax3(uint32_t a, uint32_t b, uint32_t c) {
+  const uint32_t m = b > c ? b : c;
+  return a > m ? a : m;
+}
+
+// acc + sum of squares of 8 bf16 values, two per v_dot2.
+__device__ __forceinline__ float sumsq8(const bf16x8 x, float acc) {
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const bf16x2 p = {x[e], x[e + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc, false);
+  }
+  return acc;
+}
+
+// Order of (key without position bits, destination): larger key, then smaller destination.
+__device__ __forceinline__ void take_better(uint32_t& kb, int& db, uint32_t ko, int dob) {
+  if (ko > kb || (ko == kb && dob < db)) {
+    kb = ko;
+    db = dob;
+  }
+}
+
+// Keys of one 64-destination tile: tm[c] = max over the lane's 16
+// candidates of source column tile c (position bits included).  MASK: only
+// destinations below nvalid (tile-relative) count.
+template <bool MASK>
+__device__ __forceinline__ void tile_keys(const u32x4* sDb, const float* sInvb, const bf16x8 (&bs)[4][2],
+                                          const float (&off)[4], int lg, int l16, int nvalid, uint32_t (&tm)[4]) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int arow = dt * 16 + l16;
+    const bf16x8 a0 = __builtin_bit_cast(bf16x8, sDb[arow * 8 + ((0 + lg) ^ swz(arow))]);
+    const bf16x8 a1 = __builtin_bit_cast(bf16x8, sDb[arow * 8 + ((4 + lg) ^ swz(arow))]);
+    const f32x4 inv4 = *reinterpret_cast<const f32x4*>(&sInvb[dt * 16 + 4 * lg]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bs[c][0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bs[c][1], acc, 0, 0, 0);
+      uint32_t key[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = fmaf(acc[r], inv4[r], off[c]);
+        key[r] = (__float_as_uint(v) & ~15u) | (uint32_t)(15 - (4 * dt + r));
+        if (MASK && dt * 16 + 4 * lg + r >= nvalid) key[r] = 0u;
+      }
+      if (dt == 0) {
+        tm[c] = umax3(key[0], key[1], key[2] > key[3] ? key[2] : key[3]);
+      } else {
+        tm[c] = umax3(tm[c], key[0], key[1]);
+        tm[c] = umax3(tm[c], key[2], key[3]);
+      }
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void sim_argmax_bf16(SimArgs a) {
   __shared__ u32x4 sD[2][kDstTile * 8];
   __shared__ __attribute__((aligned(16))) float sInv[2][kDstTile];
-  const int w = xcd_logical(blockIdx.x, a.total);
-  if (w >= a.total) return;
   int st, head, b, chunk;
-  decode(a, w, st, head, b, chunk);
+  if (!decode(a, blockIdx.x, st, head, b, chunk)) return;
   const Geo& g = a.g;
   const BlockInfo bi = block_info(g, b, st);
   const int s = g.s[st];
@@ -65,37 +146,39 @@ __global__ __launch_bounds__(256) void sim_argmax_bf16(SimArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int hf = lane >> 5, l32 = lane & 31;
+  const int lg = lane >> 4, l16 = lane & 15;
+  const float rcp_run = div_rcp(bi.run), rcp_s1 = div_rcp(s - 1);
 
-  // Source operands: lane holds src (wave*64 + c*32 + l32), channels q*16 + 8*hf .. +8.
-  bf16x8 bs[2][4];
-  float invs[2];
-  int ksrc[2];
+  // Source operands: column tile c holds source chunk*256 + wave*64 + 16c + l16,
+  // channels 32kc + 8lg .. +8 for k-chunk kc.
+  bf16x8 bs[4][2];
+  float off[4], invs[4];
+  int ksrc[4];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int k = chunk * kSrcPerWg + wave * kSrcPerWave + c * 32 + l32;
+  for (int c = 0; c < 4; ++c) {
+    const int k = chunk * kSrcPerWg + wave * kSrcPerWave + c * 16 + l16;
     ksrc[c] = k;
     const int kk = k < bi.ns ? k : 0;
-    const int tok = block_token(g, bi, src_pos(kk, s));
+    const int pos = kk + div_small(kk, rcp_s1) + 1;  // src_pos(kk, s)
+    const int tok = block_token_r(g, bi, pos, rcp_run);
     const uint16_t* row = X + (size_t)tok * kD;
     float ss = 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x4 u = *reinterpret_cast<const u32x4*>(row + q * 16 + hf * 8);
-      bs[c][q] = __builtin_bit_cast(bf16x8, u);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = __uint_as_float(u[e] << 16), hi = __uint_as_float(u[e] & 0xFFFF0000u);
-        ss += lo * lo;
-        ss += hi * hi;
-      }
+    for (int kc = 0; kc < 2; ++kc) {
+      const u32x4 u = *reinterpret_cast<const u32x4*>(row + kc * 32 + lg * 8);
+      bs[c][kc] = __builtin_bit_cast(bf16x8, u);
+      ss = sumsq8(bs[c][kc], ss);
     }
+    ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
-    invs[c] = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+    // hardware sqrt / rsq (1 ulp): the offset only has to exceed |s| dot d^,
+    // which its 2^-10 margin guarantees
+    off[c] = __builtin_amdgcn_sqrtf(ss) * (1.0f + 0x1p-10f);
+    invs[c] = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
   }
 
-  float best[2] = {-INFINITY, -INFINITY};
-  int bidx[2] = {0x7fffffff, 0x7fffffff};
+  uint32_t best[4] = {0u, 0u, 0u, 0u}, bestT[4] = {0u, 0u, 0u, 0u};
+  int bt[4] = {0, 0, 0, 0};
 
   // Tile loader: thread loads row tid/4 of the tile, 16-byte chunks 2*(tid%4) and +1.
   const int lrow = tid >> 2, lch = (tid & 3) * 2;
@@ -104,7 +187,7 @@ __global__ __launch_bounds__(256) void sim_argmax_bf16(SimArgs a) {
   auto load_tile = [&](int t) {
     int d = t * kDstTile + lrow;
     d = d < bi.nd ? d : 0;
-    const int tok = block_token(g, bi, d * s);
+    const int tok = block_token_r(g, bi, d * s, rcp_run);
     const u32x4* row = reinterpret_cast<const u32x4*>(X + (size_t)tok * kD);
     pre[0] = row[lch];
     pre[1] = row[lch + 1];
@@ -117,72 +200,52 @@ __global__ __launch_bounds__(256) void sim_argmax_bf16(SimArgs a) {
       float ss = 0.f;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float lo = __uint_as_float(pre[c][e] << 16), hi = __uint_as_float(pre[c][e] & 0xFFFF0000u);
-          ss += lo * lo;
-          ss += hi * hi;
-        }
-        sD[buf][lrow * 8 + ((lch + c) ^ (lrow & 7))] = pre[c];
+        ss = sumsq8(__builtin_bit_cast(bf16x8, pre[c]), ss);
+        sD[buf][lrow * 8 + ((lch + c) ^ swz(lrow))] = pre[c];
       }
       ss += __shfl_xor(ss, 1);
       ss += __shfl_xor(ss, 2);
-      if ((tid & 3) == 0) sInv[buf][lrow] = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+      if ((tid & 3) == 0) sInv[buf][lrow] = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
     }
     __syncthreads();
     if (t + 1 < ntiles) load_tile(t + 1);
 
+    uint32_t tm[4];
+    // destination rows past nd (last tile only) must not win: their keys are 0
+    if ((t + 1) * kDstTile > bi.nd)
+      tile_keys<true>(sD[buf], sInv[buf], bs, off, lg, l16, bi.nd - t * kDstTile, tm);
+    else
+      tile_keys<false>(sD[buf], sInv[buf], bs, off, lg, l16, kDstTile, tm);
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      f32x16 acc[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[c][i] = 0.f;
-      const int arow = rt * 32 + l32;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4 ua = sD[buf][arow * 8 + ((2 * q + hf) ^ (arow & 7))];
-        const bf16x8 av = __builtin_bit_cast(bf16x8, ua);
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bs[c][q], acc[c], 0, 0, 0);
-      }
-      float inv[16];
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const f32x4 v4 = *reinterpret_cast<const f32x4*>(&sInv[buf][rt * 32 + 8 * gq + 4 * hf]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) inv[gq * 4 + j] = v4[j];
-      }
-      const int rbase = t * kDstTile + rt * 32 + 4 * hf;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = rbase + 8 * (i >> 2) + (i & 3);
-          const float v = acc[c][i] * inv[i];
-          if (v > best[c] && row < bi.nd) {
-            best[c] = v;
-            bidx[c] = row;
-          }
-        }
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t tT = tm[c] & ~15u;
+      if (t == 0 || tT > bestT[c]) {
+        best[c] = tm[c];
+        bestT[c] = tT;
+        bt[c] = t;
       }
     }
   }
 
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const float ov = __shfl_xor(best[c], 32);
-    const int oi = __shfl_xor(bidx[c], 32);
-    if (ov > best[c] || (ov == best[c] && oi < bidx[c])) {
-      best[c] = ov;
-      bidx[c] = oi;
+  for (int c = 0; c < 4; ++c) {
+    const int i = 15 - (int)(best[c] & 15u);
+    int d = bt[c] * kDstTile + (i >> 2) * 16 + 4 * lg + (i & 3);
+    uint32_t kb = bestT[c];
+    {
+      const uint32_t ko = (uint32_t)__shfl_xor((int)kb, 16);
+      const int dob = __shfl_xor(d, 16);
+      take_better(kb, d, ko, dob);
     }
-    if (hf == 0 && ksrc[c] < bi.ns) {
+    {
+      const uint32_t ko = (uint32_t)__shfl_xor((int)kb, 32);
+      const int dob = __shfl_xor(d, 32);
+      take_better(kb, d, ko, dob);
+    }
+    if (lg == 0 && ksrc[c] < bi.ns) {
       const size_t o = (size_t)head * g.nsrc[st] + bi.src0 + ksrc[c];
-      a.match[st][o] = bidx[c] < bi.nd ? bidx[c] : 0;  // all-NaN rows: destination 0
-      a.score[st][o] = best[c] * invs[c] + 0.0f;
+      a.match[st][o] = d < bi.nd ? d : 0;
+      a.score[st][o] = (__uint_as_float(kb) - off[c]) * invs[c] + 0.0f;
     }
   }
 }
@@ -192,10 +255,8 @@ __global__ __launch_bounds__(256) void sim_argmax_bf16(SimArgs a) {
 __global__ __launch_bounds__(256) void sim_argmax_f32(SimArgs a) {
   __shared__ float sD[kDstTile][kD + 1];
   __shared__ float sInv[kDstTile];
-  const int w = blockIdx.x;
-  if (w >= a.total) return;
   int st, head, b, chunk;
-  decode(a, w, st, head, b, chunk);
+  if (!decode(a, blockIdx.x, st, head, b, chunk)) return;
   const Geo& g = a.g;
   const BlockInfo bi = block_info(g, b, st);
   const int s = g.s[st];
@@ -269,11 +330,14 @@ hipError_t launch_sim(const Geo& g, int dtype, const void* q, const void* k, int
     a.wgs[st] = g.heads * g.nblocks * a.chunks[st];
   }
   a.total = a.wgs[0] + a.wgs[1];
+  // 8 XCD slices of ceil(HB/8) (head, block) pairs at most
+  const int hb = g.heads * g.nblocks;
+  const int per_xcd = ceil_div(hb, 8) * (a.chunks[0] + a.chunks[1]);
+  const int grid = 8 * per_xcd;
   if (dtype == 1) {
-    const int grid = ((a.total + 7) / 8) * 8;
     hipLaunchKernelGGL(sim_argmax_bf16, dim3(grid), dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(sim_argmax_f32, dim3(a.total), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(sim_argmax_f32, dim3(grid), dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }
