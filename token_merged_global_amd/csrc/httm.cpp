@@ -255,7 +255,7 @@ httm_status build(const httm_params& p, httm_plan* pl) {
     Lw.total = b.cur;
   }
   pl->dense_vt_bytes = align256(E * h * (size_t)ceil_div(g.N, 64) * 64 * kD);
-  pl->dense_kc_bytes = align256(E * h * n * kD);
+  pl->dense_kc_bytes = align256(E * h * (size_t)ceil_div(g.N, 64) * 64 * kD);
   pl->dense_ws = pl->dense_vt_bytes + pl->dense_kc_bytes + pl->L.kmax.bytes + 256 + pl->L.fb.bytes;
   pl->id = ++g_plan_counter;
   return HTTM_OK;
@@ -543,7 +543,7 @@ httm_status httm_attention_dense(const httm_plan* pl, void* ws, size_t ws_bytes,
   AttnShape a;
   a.heads = g.heads;
   a.lk = g.N;
-  a.k_rows = g.N;
+  a.k_rows = pitch;
   a.vt_pitch = pitch;
   a.lq_uniform = g.N;
   a.q_capacity = (int64_t)g.heads * g.N;

@@ -6,14 +6,14 @@
 // outlier budget is shared across heads (key design 3); K~ / V~ have the same
 // length in every head.
 //
-// Work unit = (head, tile of 128 query rows, key split).  One workgroup = 2
+// Work unit = (head, tile of 256 query rows, key split).  One workgroup = 4
 // waves x 64 query rows (four 16-row tiles per wave) on
 // v_mfma_f32_16x16x32_bf16, the full-rate bf16 MFMA of gfx950; 64 rows per
-// wave halve the LDS operand bytes per FLOP against 32.  Key tiles of 64 rows
-// of K~ and the matching 64 columns of V~^T (stored transposed by the merge
-// kernel) go global -> LDS directly (global_load_lds_dwordx4), double
-// buffered.  K~ arrives multiplied by scale * log2(e), so scores are in exp2
-// units.
+// wave halve the LDS operand bytes per FLOP against 32, and 4 waves share
+// each key tile copy.  Key tiles of 64 rows of K~ and the matching 64 columns
+// of V~^T (stored transposed by the merge kernel) go global -> LDS directly
+// (global_load_lds_dwordx4), double buffered.  K~ arrives multiplied by
+// scale * log2(e), so scores are in exp2 units.
 //
 // Softmax reference.  Cauchy-Schwarz bounds every score of a row by
 // m = |q| * max_k |k~| (max over the head's keys, computed by the K~
@@ -28,7 +28,7 @@
 // chunk are permuted so that lane group g holds keys 8g..8g+7 of the chunk:
 // exactly the B operand of the P V MFMA, whose V~^T operand is then one
 // 16-byte LDS read.  The row sum adds the bf16-rounded probabilities that the
-// P V product uses (v_dot2 against 1.0).
+// P V product uses, on the MFMA pipe (a constant all-ones operand row).
 //
 // Key split.  When the query tiles alone do not fill the GPU (small layers),
 // the keys are split in S contiguous ranges; each unit writes its fp32
@@ -44,7 +44,7 @@ namespace {
 constexpr int kKeyTile = 64;
 constexpr int kRowsF32 = 128;  // fp32 kernel: one thread per query row
 constexpr int kQT = 4;         // 16-row query tiles per wave
-constexpr int kNW = 2;         // waves per workgroup
+constexpr int kNW = 4;         // waves per workgroup
 constexpr int kRows = kQT * kNW * 16;
 constexpr float kTinySum = 8.673617379884035e-19f;  // 2^-60
 
@@ -142,6 +142,7 @@ struct UnitCtx {
   const uint16_t* Kp;
   const uint16_t* Vp;
   int t0, t1, ntiles_all;
+  uint32_t koff[8 / kNW], voff[8 / kNW];  // per-lane byte offsets of the tile copies
   bf16x8 bq[kQT][2];
   bool valid[kQT];
   int qrow[kQT];
@@ -153,6 +154,15 @@ __device__ __forceinline__ void unit_setup(const AttnArgs& a, const Unit& u, int
   c.Kp = reinterpret_cast<const uint16_t*>(a.k) + (size_t)u.head * a.k_rows * kD;
   c.Vp = reinterpret_cast<const uint16_t*>(a.vt) + (size_t)u.head * kD * a.vt_pitch;
   c.ntiles_all = ceil_div(a.lk, kKeyTile);
+  // the copy of key tile t reads base(t) + these lane offsets: every key
+  // buffer holds whole 64-key tiles (zero past lk), so no clamp is needed
+#pragma unroll
+  for (int rd = 0; rd < 8 / kNW; ++rd) {
+    const int p = (rd * kNW + wave) * 64 + (threadIdx.x & 63);
+    const int row = p >> 3, pc = p & 7;
+    c.koff[rd] = (uint32_t)(row * kD + (pc ^ swzK(row)) * 8) * 2u;
+    c.voff[rd] = (uint32_t)(row * a.vt_pitch + (pc ^ swzV(row)) * 8) * 2u;
+  }
   c.t0 = (int)((int64_t)u.split * c.ntiles_all / a.split);
   c.t1 = (int)((int64_t)(u.split + 1) * c.ntiles_all / a.split);
 #pragma unroll
@@ -178,19 +188,17 @@ __device__ __forceinline__ void unit_setup(const AttnArgs& a, const Unit& u, int
 }
 
 // Copy key tile t (64 keys of K~ and V~^T) into LDS buffer buf.  Each wave
-// issues 4 + 4 copies of 64 x 16 bytes; lane i fetches the global chunk that
-// belongs at its swizzled LDS slot.
-__device__ __forceinline__ void load_tile(const AttnArgs& a, const UnitCtx& c, u32x4 (*sK)[kKeyTile * 8],
-                                          u32x4 (*sV)[kD * 8], int t, int buf, int wave, int lane) {
+// issues 8/kNW + 8/kNW copies of 64 x 16 bytes; lane i fetches the global
+// chunk that belongs at its swizzled LDS slot (offsets fixed per lane).
+__device__ __forceinline__ void load_tile(const UnitCtx& c, u32x4 (*sK)[kKeyTile * 8], u32x4 (*sV)[kD * 8], int t,
+                                          int buf, int wave) {
+  const char* kb = reinterpret_cast<const char*>(c.Kp) + (size_t)t * (kKeyTile * kD * 2);
+  const char* vb = reinterpret_cast<const char*>(c.Vp) + (size_t)t * (kKeyTile * 2);
 #pragma unroll
   for (int rd = 0; rd < 8 / kNW; ++rd) {
     const int slot = (rd * kNW + wave) * 64;
-    const int p = slot + lane;
-    const int row = p >> 3, pc = p & 7;
-    int key = t * kKeyTile + row;
-    key = key < a.lk ? key : a.lk - 1;
-    lds_copy16(c.Kp + (size_t)key * kD + (pc ^ swzK(row)) * 8, &sK[buf][slot]);
-    lds_copy16(c.Vp + (size_t)row * a.vt_pitch + t * kKeyTile + (pc ^ swzV(row)) * 8, &sV[buf][slot]);
+    lds_copy16(kb + c.koff[rd], &sK[buf][slot]);
+    lds_copy16(vb + c.voff[rd], &sV[buf][slot]);
   }
 }
 
@@ -249,6 +257,35 @@ __device__ __forceinline__ void probs(f32x4 (*sacc)[4], bf16x8 (*bp)[2], float* 
   }
 }
 
+// p = exp2(acc) as bf16 B operands, without row sums (the fast kernel sums
+// them on the MFMA pipe, see psum).
+__device__ __forceinline__ void probs_only(f32x4 (*sacc)[4], bf16x8 (*bp)[2]) {
+#pragma unroll
+  for (int qt = 0; qt < kQT; ++qt)
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      bf16x8 pb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pb[r] = (__bf16)__builtin_amdgcn_exp2f(sacc[qt][2 * kc][r]);
+        pb[4 + r] = (__bf16)__builtin_amdgcn_exp2f(sacc[qt][2 * kc + 1][r]);
+      }
+      bp[qt][kc] = pb;
+    }
+}
+
+// Row sums of the bf16 probabilities on the MFMA pipe: an A operand whose
+// tile row 0 is all ones (lanes with l16 == 0) and zero elsewhere puts
+// sum_k P[k][query] in output row 0, i.e. register 0 of lane group 0.
+// Exact bf16 products, fp32 accumulation, like the P V product itself.
+__device__ __forceinline__ void psum(const bf16x8 ones, bf16x8 (*bp)[2], f32x4* osum) {
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt)
+      osum[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, bp[qt][kc], osum[qt], 0, 0, 0);
+}
+
 // O^T += V~^T P^T for one 64-key tile.
 __device__ __forceinline__ void pv(const u32x4* sVb, bf16x8 (*bp)[2], int g, int l16, f32x4 (*oacc)[4]) {
 #pragma unroll
@@ -262,6 +299,20 @@ __device__ __forceinline__ void pv(const u32x4* sVb, bf16x8 (*bp)[2], int g, int
         oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, bp[qt][kc], oacc[qt][dt], 0, 0, 0);
     }
   }
+}
+
+// One 64-key tile: S^T - m, (tail mask), probabilities, O^T += V~^T P^T.
+template <bool MASK>
+__device__ __forceinline__ void tile_step(const AttnArgs& a, const u32x4* sKb, const u32x4* sVb, const UnitCtx& c,
+                                          const f32x4* negm, int g, int l16, int t, const bf16x8 ones,
+                                          f32x4* osum, f32x4 (*oacc)[4]) {
+  f32x4 sacc[kQT][4];
+  scores(sKb, c, negm, g, l16, sacc);
+  if (MASK) mask_tail(a, t, g, sacc);
+  bf16x8 bp[kQT][2];
+  probs_only(sacc, bp);
+  pv(sVb, bp, g, l16, oacc);
+  psum(ones, bp, osum);
 }
 
 // Write one unit's rows: normalized bf16 (split == 1) or fp32 partials.
@@ -307,36 +358,44 @@ __global__ __launch_bounds__(kNW * 64) void attn_fast(AttnArgs a) {
   float qn2[kQT];
   unit_setup(a, u, wave, g, l16, c, qn2);
   const float km = a.kmax[u.head];
-  f32x4 negm[kQT];
-  float mref[kQT], lrun[kQT];
+  f32x4 negm[kQT], osum[kQT];
+  float mref[kQT];
   f32x4 oacc[kQT][4];
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
     mref[qt] = sqrtf(qn2[qt]) * km;
-    lrun[qt] = 0.f;
+    osum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < 4; ++r) negm[qt][r] = -mref[qt];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  load_tile(a, c, sK, sV, c.t0, 0, wave, lane);
-  for (int t = c.t0; t < c.t1; ++t) {
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)(l16 == 0 ? 1.0f : 0.0f);
+  load_tile(c, sK, sV, c.t0, 0, wave);
+  // only the head's last key tile can be partial: it runs outside the main
+  // loop, so the loop body is one basic block and the exp2 of one key group
+  // can overlap the score MFMAs of the next
+  const int tfull = (c.t1 == c.ntiles_all && a.lk % kKeyTile) ? c.t1 - 1 : c.t1;
+  for (int t = c.t0; t < tfull; ++t) {
     const int buf = (t - c.t0) & 1;
     wait_vm();
     __syncthreads();
-    if (t + 1 < c.t1) load_tile(a, c, sK, sV, t + 1, buf ^ 1, wave, lane);
-    f32x4 sacc[kQT][4];
-    scores(sK[buf], c, negm, g, l16, sacc);
-    if ((t + 1) * kKeyTile > a.lk) mask_tail(a, t, g, sacc);
-    bf16x8 bp[kQT][2];
-    probs(sacc, bp, lrun);
-    pv(sV[buf], bp, g, l16, oacc);
+    if (t + 1 < c.t1) load_tile(c, sK, sV, t + 1, buf ^ 1, wave);
+    tile_step<false>(a, sK[buf], sV[buf], c, negm, g, l16, t, ones, osum, oacc);
+  }
+  if (tfull < c.t1) {
+    const int t = tfull, buf = (t - c.t0) & 1;
+    wait_vm();
+    __syncthreads();
+    tile_step<true>(a, sK[buf], sV[buf], c, negm, g, l16, t, ones, osum, oacc);
   }
   float lsum[kQT];
   bool tiny = false;
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
-    lsum[qt] = sum_xor16(sum_xor32(lrun[qt]));
+    lsum[qt] = __shfl(osum[qt][0], l16);  // from lane group 0
     tiny |= c.valid[qt] && !(lsum[qt] >= kTinySum);
   }
   if (__syncthreads_or(tiny)) {
@@ -374,12 +433,12 @@ __global__ __launch_bounds__(kNW * 64) void attn_exact(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  load_tile(a, c, sK, sV, c.t0, 0, wave, lane);
+  load_tile(c, sK, sV, c.t0, 0, wave);
   for (int t = c.t0; t < c.t1; ++t) {
     const int buf = (t - c.t0) & 1;
     wait_vm();
     __syncthreads();
-    if (t + 1 < c.t1) load_tile(a, c, sK, sV, t + 1, buf ^ 1, wave, lane);
+    if (t + 1 < c.t1) load_tile(c, sK, sV, t + 1, buf ^ 1, wave);
     f32x4 sacc[kQT][4];
     scores(sK[buf], c, negm, g, l16, sacc);
     if ((t + 1) * kKeyTile > a.lk) mask_tail(a, t, g, sacc);

@@ -447,7 +447,7 @@ __global__ __launch_bounds__(256) void unmerge(int64_t rows, const int32_t* __re
 }
 
 // Unmerged baseline inputs: kc[h][n] = k[h][n] * kscale, vt[h][c][n] =
-// v[h][n][c] for n < N and 0 for N <= n < pitch.
+// v[h][n][c] for n < N, both 0 for N <= n < pitch (whole 64-key tiles).
 template <typename T>
 __global__ __launch_bounds__(256) void prep_dense(int N, int pitch, float kscale, const T* __restrict__ k,
                                                   const T* __restrict__ v, T* __restrict__ kc,
@@ -470,8 +470,8 @@ __global__ __launch_bounds__(256) void prep_dense(int N, int pitch, float kscale
       load8(K + (size_t)n * kD + j * 8, kx);
 #pragma unroll
       for (int e = 0; e < 8; ++e) kx[e] *= kscale;
-      store8(kc + ((size_t)head * N + n) * kD + j * 8, kx);
     }
+    store8(kc + ((size_t)head * pitch + n) * kD + j * 8, kx);  // rows past N stay zero
     const float nrm = row_norm8<T>(kx);
     if (n < N) nmax = fmaxf(nmax, nrm);
     if (n < N) {

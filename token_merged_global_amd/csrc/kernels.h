@@ -68,7 +68,7 @@ hipError_t launch_merge_q_cached(int dtype, int heads, int N, int64_t q_capacity
 struct AttnShape {
   int heads;
   int lk;          // keys per head
-  int k_rows;      // rows per head in the key buffer (>= lk)
+  int k_rows;      // rows per head in the key buffer (whole 64-key tiles, zero past lk)
   int vt_pitch;    // keys per row of vt (multiple of 64, >= lk)
   int lq_uniform;  // used when lenq == nullptr
   int64_t q_capacity;
@@ -93,8 +93,8 @@ hipError_t launch_attention(int dtype, const AttnShape& s, const void* q, const 
 hipError_t launch_unmerge(int dtype, int heads, int N, const int32_t* slot, const void* o,
                           void* out, hipStream_t stream);
 
-// Unmerged baseline inputs: kc = k * kscale ([h][N][64]); vt[h][c][n] =
-// v[h][n][c], zero for n in [N, pitch).
+// Unmerged baseline inputs: kc = k * kscale ([h][pitch][64]); vt[h][c][n] =
+// v[h][n][c]; both zero for n in [N, pitch).
 hipError_t launch_prep_dense(int dtype, int heads, int N, int pitch, float kscale, const void* k,
                              const void* v, void* kc, void* vt, float* kmax, hipStream_t stream);
 
