@@ -8,6 +8,11 @@ are already resident in HBM.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload vggt30] [--no-cpu-baseline]
 
+By default W and K are sized from a one-step probe so that the warmup and
+the timed region each cover about 0.5 s of GPU work (clocks ramp up over the
+first few hundred milliseconds of load); the JSON line reports the W and K
+actually used.
+
 Workload default: 30 frames x (37x37 patches + 5 special tokens) = 41,220
 tokens, 16 heads x 64 channels, bf16; blocks n_s=128 x n_t=30; queries merged
 90 % with 10 % outliers restored; keys/values merged 50 %.
@@ -65,8 +70,10 @@ def cpu_baseline(w, x, heads: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=0,
+                    help="timed steps (default: enough for ~0.5 s of GPU work, at least 10)")
+    ap.add_argument("--warmup", type=int, default=0,
+                    help="untimed warmup steps (default: enough for ~0.5 s, at least 3, so clocks have ramped)")
     ap.add_argument("--workload", default="vggt30", choices=sorted(gen.WORKLOADS))
     ap.add_argument("--seed", type=int, default=gen.DEFAULT_SEED)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -104,7 +111,20 @@ def main():
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
 
-    log(f"[bench] warmup {args.warmup}")
+    # step-time probe (untimed for the result): sizes the default warmup and step counts
+    H.layer(plan, q, k, v, ws=ws, out=out, stream=stream)
+    torch.cuda.synchronize()
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
+    H.layer(plan, q, k, v, ws=ws, out=out, stream=stream)
+    p1.record(stream)
+    torch.cuda.synchronize()
+    probe_ms = max(p0.elapsed_time(p1), 1e-3)
+    if args.warmup <= 0:
+        args.warmup = max(3, int(500.0 / probe_ms))
+    if args.steps <= 0:
+        args.steps = max(10, int(500.0 / probe_ms))
+    log(f"[bench] warmup {args.warmup} steps (probe {probe_ms:.3f} ms/step)")
     for _ in range(args.warmup):
         H.layer(plan, q, k, v, ws=ws, out=out, stream=stream)
     torch.cuda.synchronize()

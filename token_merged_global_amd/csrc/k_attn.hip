@@ -144,8 +144,8 @@ struct UnitCtx {
   int t0, t1, ntiles_all;
   uint32_t koff[8 / kNW], voff[8 / kNW];  // per-lane byte offsets of the tile copies
   bf16x8 bq[kQT][2];
-  bool valid[kQT];
-  int qrow[kQT];
+  int qrow0, L;  // this lane's row of query tile 0 inside the head; head length
+  __device__ __forceinline__ bool valid(int qt) const { return qrow0 + qt * 16 < L; }
 };
 
 __device__ __forceinline__ void unit_setup(const AttnArgs& a, const Unit& u, int wave, int g, int l16, UnitCtx& c,
@@ -165,12 +165,12 @@ __device__ __forceinline__ void unit_setup(const AttnArgs& a, const Unit& u, int
   }
   c.t0 = (int)((int64_t)u.split * c.ntiles_all / a.split);
   c.t1 = (int)((int64_t)(u.split + 1) * c.ntiles_all / a.split);
+  c.qrow0 = u.tile * kRows + wave * kQT * 16 + l16;
+  c.L = u.L;
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
-    const int qr = u.tile * kRows + (wave * kQT + qt) * 16 + l16;
-    c.valid[qt] = qr < u.L;
-    c.qrow[qt] = qr;
-    const size_t r = (size_t)u.cu + (c.valid[qt] ? qr : u.L - 1);
+    const int qr = c.qrow0 + qt * 16;
+    const size_t r = (size_t)u.cu + (qr < u.L ? qr : u.L - 1);
     float ss = 0.f;
 #pragma unroll
     for (int dc = 0; dc < 2; ++dc) {
@@ -317,11 +317,11 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, const u32x4* sKb, c
 
 // Write one unit's rows: normalized bf16 (split == 1) or fp32 partials.
 __device__ __forceinline__ void store_unit(const AttnArgs& a, const Unit& u, const UnitCtx& c, int g,
-                                           f32x4 (*oacc)[4], const float* lsum, const float* mref) {
+                                           f32x4 (*oacc)[4], const float* lsum, const f32x4* negm) {
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
-    if (!c.valid[qt]) continue;
-    const size_t row = (size_t)u.cu + c.qrow[qt];
+    if (!c.valid(qt)) continue;
+    const size_t row = (size_t)u.cu + c.qrow0 + qt * 16;
     if (a.split == 1) {
       const float inv = 1.0f / lsum[qt];
       uint16_t* Op = reinterpret_cast<uint16_t*>(a.o) + row * kD;
@@ -339,7 +339,7 @@ __device__ __forceinline__ void store_unit(const AttnArgs& a, const Unit& u, con
       for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(Op + dt * 16 + 4 * g) = oacc[qt][dt];
       if (g == 0) {
         a.lpart[prow] = lsum[qt];
-        a.mpart[prow] = mref[qt];
+        a.mpart[prow] = -negm[qt][0];  // the unit's softmax reference
       }
     }
   }
@@ -359,14 +359,13 @@ __global__ __launch_bounds__(kNW * 64) void attn_fast(AttnArgs a) {
   unit_setup(a, u, wave, g, l16, c, qn2);
   const float km = a.kmax[u.head];
   f32x4 negm[kQT], osum[kQT];
-  float mref[kQT];
   f32x4 oacc[kQT][4];
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
-    mref[qt] = sqrtf(qn2[qt]) * km;
+    const float m = sqrtf(qn2[qt]) * km;
     osum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) negm[qt][r] = -mref[qt];
+    for (int r = 0; r < 4; ++r) negm[qt][r] = -m;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -396,7 +395,7 @@ __global__ __launch_bounds__(kNW * 64) void attn_fast(AttnArgs a) {
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
     lsum[qt] = __shfl(osum[qt][0], l16);  // from lane group 0
-    tiny |= c.valid[qt] && !(lsum[qt] >= kTinySum);
+    tiny |= c.valid(qt) && !(lsum[qt] >= kTinySum);
   }
   if (__syncthreads_or(tiny)) {
     if (tid == 0) {
@@ -405,7 +404,7 @@ __global__ __launch_bounds__(kNW * 64) void attn_fast(AttnArgs a) {
     }
     return;
   }
-  store_unit(a, u, c, g, oacc, lsum, mref);
+  store_unit(a, u, c, g, oacc, lsum, negm);
 }
 
 // Exact path for queued units: online max (raised only when a score exceeds
@@ -481,7 +480,7 @@ __global__ __launch_bounds__(kNW * 64) void attn_exact(AttnArgs a) {
   float lsum[kQT];
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) lsum[qt] = sum_xor16(sum_xor32(lrun[qt]));
-  store_unit(a, u, c, g, oacc, lsum, mref);
+  store_unit(a, u, c, g, oacc, lsum, negm);
 }
 
 // Combine the key-split partials of every packed row (split order fixed):
