@@ -20,8 +20,10 @@ tokens, 16 heads x 64 channels, bf16; blocks n_s=128 x n_t=30; queries merged
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import platform
 import sys
 import time
@@ -41,6 +43,29 @@ MFMA_F32_PEAK_TFLOPS = 157.3
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+ATTN_SRC = os.path.join(ROOT, "token_merged_global_amd", "csrc", "k_attn.hip")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_fast_hbm_traffic_vggt30.md")
+
+
+def measured_traffic(workload: str, dtype: str):
+    """HBM bytes per attn_fast launch from the committed rocprofv3 counter summary.
+
+    Returned only while the attention source is the one the counters were
+    taken with (sha256 recorded in the summary) and for that workload;
+    otherwise None.
+    """
+    if dtype != "bf16" or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    txt = open(TRAFFIC_PROFILE).read()
+    sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", txt)
+    wl = re.search(r"workload:\s*(\S+)", txt)
+    nb = re.search(r"bytes_per_launch:\s*([0-9]+)", txt)
+    if not (sha and wl and nb) or wl.group(1) != workload:
+        return None
+    cur = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    return int(nb.group(1)) if cur == sha.group(1) else None
 
 
 def describe(w) -> str:
@@ -226,9 +251,10 @@ def main():
         "config": {"workload": describe(w), "frames": w.frames, "tokens": w.n_tokens, "heads": w.heads,
                    "d_head": w.d_head, "n_s": w.n_s, "n_t": w.n_t, "q_ratio": w.q_ratio, "kv_ratio": w.kv_ratio,
                    "outlier_pct": w.outlier_pct, "seed": args.seed},
-        "roofline": {"bound": "mfma", "kernel": "attn_bf16" if w.dtype == "bf16" else "attn_f32",
+        "roofline": {"bound": "mfma", "kernel": "attn_fast" if w.dtype == "bf16" else "attn_f32",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": None,
+                     "traffic": measured_traffic(w.name, "bf16" if w.dtype == "bf16" else "f32"),
+                     "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
                      "algorithmic": f"4*d*L_k*sum_h(L_q,h) = 4*{w.d_head}*{lk}*{int(lq.sum())} = {attn_flop:.4g} FLOP per launch",
                      "avg_launch_ms": attn_ms, "launches_timed": calls},
         "cpu_baseline": cpu,

@@ -200,7 +200,11 @@ httm_status httm_debug_read(const httm_plan* plan, const void* ws, const httm_in
  * the events.  Host-side state, not thread-safe. */
 typedef enum {
   HTTM_T_SIM = 0, HTTM_T_SELECT, HTTM_T_MERGE_KV, HTTM_T_MERGE_Q, HTTM_T_OUTLIER,
-  HTTM_T_RESTORE, HTTM_T_ATTN, HTTM_T_UNMERGE, HTTM_T_COUNT
+  HTTM_T_RESTORE,
+  HTTM_T_ATTN,       /* the main attention kernel (one launch) */
+  HTTM_T_UNMERGE,
+  HTTM_T_ATTN_TAIL,  /* exact recompute of queued units + combine of key splits */
+  HTTM_T_COUNT
 } httm_timing_stage;
 httm_status httm_set_timing(int32_t stage_mask);
 httm_status httm_get_timing(float* ms, int32_t n, int32_t* calls);

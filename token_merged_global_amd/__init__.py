@@ -25,7 +25,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
           4: "index mismatch", 5: "device error"}
 DEBUG_ITEMS = ["q_match", "q_score", "kv_match", "kv_score", "q_group", "kv_group", "delta",
                "outlier", "q_slot", "cu_q", "select", "attn_fallback"]
-TIMING_STAGES = ["sim", "select", "merge_kv", "merge_q", "outlier", "restore", "attn", "unmerge"]
+TIMING_STAGES = ["sim", "select", "merge_kv", "merge_q", "outlier", "restore", "attn", "unmerge", "attn_tail"]
 
 
 class HttmError(RuntimeError):

@@ -339,6 +339,10 @@ httm_status attend_unmerge(const httm_plan* pl, void* ws, char* idx, const void*
   CHECK_LAUNCH(launch_attention(dt, s, qt, at<void>(ws, pl->L.kt), at<void>(ws, pl->L.vt), lenq,
                                 at<void>(ws, pl->L.o), st));
   stage_end(HTTM_T_ATTN, st);
+  stage_begin(HTTM_T_ATTN_TAIL, st);
+  CHECK_LAUNCH(launch_attention_tail(dt, s, qt, at<void>(ws, pl->L.kt), at<void>(ws, pl->L.vt), lenq,
+                                     at<void>(ws, pl->L.o), st));
+  stage_end(HTTM_T_ATTN_TAIL, st);
   stage_begin(HTTM_T_UNMERGE, st);
   CHECK_LAUNCH(launch_unmerge(dt, g.heads, g.N, reinterpret_cast<const int32_t*>(idx + pl->I.slot.off),
                               at<void>(ws, pl->L.o), out, st));
@@ -556,6 +560,9 @@ httm_status httm_attention_dense(const httm_plan* pl, void* ws, size_t ws_bytes,
   stage_begin(HTTM_T_ATTN, st);
   CHECK_LAUNCH(launch_attention(dt, a, q, kc, ws, nullptr, out, st));
   stage_end(HTTM_T_ATTN, st);
+  stage_begin(HTTM_T_ATTN_TAIL, st);
+  CHECK_LAUNCH(launch_attention_tail(dt, a, q, kc, ws, nullptr, out, st));
+  stage_end(HTTM_T_ATTN_TAIL, st);
   timing_end_call();
   return HTTM_OK;
 }

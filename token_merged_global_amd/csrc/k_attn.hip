@@ -593,9 +593,10 @@ hipError_t launch_attn_init(float* kmax, int heads, int* fb_count, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_attention(int dtype, const AttnShape& s, const void* q, const void* k,
-                            const void* vt, const int32_t* lenq, void* o, hipStream_t stream) {
-  AttnArgs a;
+namespace {
+AttnArgs make_args(int dtype, const AttnShape& s, const void* q, const void* k, const void* vt,
+                   const int32_t* lenq, void* o) {
+  AttnArgs a{};
   a.q = q;
   a.k = k;
   a.vt = vt;
@@ -614,21 +615,35 @@ hipError_t launch_attention(int dtype, const AttnShape& s, const void* q, const 
   a.lq_uniform = s.lq_uniform;
   a.split = dtype == 1 ? s.split : 1;
   a.q_capacity = s.q_capacity;
-  if (dtype == 1) {
+  if (dtype == 1)
     a.total_wg = (int)(((s.q_capacity + kRows - 1) / kRows + s.heads) * a.split);
+  else
+    a.total_wg = (int)((s.q_capacity + kRowsF32 - 1) / kRowsF32 + s.heads);
+  return a;
+}
+}  // namespace
+
+hipError_t launch_attention(int dtype, const AttnShape& s, const void* q, const void* k,
+                            const void* vt, const int32_t* lenq, void* o, hipStream_t stream) {
+  const AttnArgs a = make_args(dtype, s, q, k, vt, lenq, o);
+  if (dtype == 1) {
     const int grid = ((a.total_wg + 7) / 8) * 8;
     hipLaunchKernelGGL(attn_fast, dim3(grid), dim3(kNW * 64), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_exact, dim3(a.total_wg), dim3(kNW * 64), 0, stream, a);
-    e = hipGetLastError();
-    if (e != hipSuccess || a.split == 1) return e;
-    const int fgrid = (int)((s.q_capacity + 31) / 32);
-    hipLaunchKernelGGL(attn_finalize, dim3(fgrid), dim3(256), 0, stream, a);
   } else {
-    a.total_wg = (int)((s.q_capacity + kRowsF32 - 1) / kRowsF32 + s.heads);
     hipLaunchKernelGGL(attn_f32, dim3(a.total_wg), dim3(kRowsF32), 0, stream, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_tail(int dtype, const AttnShape& s, const void* q, const void* k,
+                                 const void* vt, const int32_t* lenq, void* o, hipStream_t stream) {
+  if (dtype != 1) return hipSuccess;
+  const AttnArgs a = make_args(dtype, s, q, k, vt, lenq, o);
+  hipLaunchKernelGGL(attn_exact, dim3(a.total_wg), dim3(kNW * 64), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.split == 1) return e;
+  const int fgrid = (int)((s.q_capacity + 31) / 32);
+  hipLaunchKernelGGL(attn_finalize, dim3(fgrid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

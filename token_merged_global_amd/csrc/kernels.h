@@ -86,8 +86,12 @@ int attention_split(int64_t q_capacity, int heads);
 int attention_rows_per_unit();
 // Zero kmax[heads] and the fallback queue counter (before the K producer runs).
 hipError_t launch_attn_init(float* kmax, int heads, int* fb_count, hipStream_t stream);
+// The main attention kernel, then the tail: exact recompute of the units the
+// main kernel queued and (key splits > 1) the combine of the partials.
 hipError_t launch_attention(int dtype, const AttnShape& s, const void* q, const void* k,
                             const void* vt, const int32_t* lenq, void* o, hipStream_t stream);
+hipError_t launch_attention_tail(int dtype, const AttnShape& s, const void* q, const void* k,
+                                 const void* vt, const int32_t* lenq, void* o, hipStream_t stream);
 
 // out[h][n] = o[slot[h][n]]
 hipError_t launch_unmerge(int dtype, int heads, int N, const int32_t* slot, const void* o,
