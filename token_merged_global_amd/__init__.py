@@ -94,13 +94,18 @@ _LIB = None
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded library; raises if it was not built (no fallback exists)."""
+    """The loaded library; raises if it was not built (no fallback exists).
+
+    HTTM_LIB, if set, names another build of the same library to load instead
+    (side-by-side comparisons of kernel variants); it must exist too.
+    """
     global _LIB
     if _LIB is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+        path = os.environ.get("HTTM_LIB") or LIB_PATH
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
                                "`python -m token_merged_global_amd.build` (the HTTM layer has no fallback)")
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
         for name, (args, res) in EXPORTS.items():
             f = getattr(L, name)
             f.argtypes = args

@@ -40,15 +40,16 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HTTM library needs the ROCm toolchain to build")
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+def sources(csrc: str = CSRC):
+    return sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+def _compile(src: str, verbose: bool, build_dir: str = BUILD_DIR) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     lang = ["-x", "hip"]
     extra = PER_FILE.get(os.path.basename(src), [])
-    cmd = [hipcc(), *lang, *COMMON, *DEVICE_FLAGS, *extra, "-c", src, "-o", obj]
+    inc = ["-I", os.path.dirname(src)]
+    cmd = [hipcc(), *lang, *COMMON, *inc, *DEVICE_FLAGS, *extra, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -59,20 +60,22 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
+def build(verbose: bool = False, jobs: int = 8, csrc: str = CSRC, out: str = OUT) -> str:
+    """Compile every source of `csrc` for gfx950 and link `out` (default: the in-tree library)."""
+    build_dir = BUILD_DIR if out == OUT else out + ".build"
+    os.makedirs(build_dir, exist_ok=True)
+    srcs = sources(csrc)
     with cf.ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = OUT + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir), srcs))
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"linking libhttm.so failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
-    return OUT
+        raise RuntimeError(f"linking {os.path.basename(out)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

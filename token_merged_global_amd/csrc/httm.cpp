@@ -76,6 +76,7 @@ struct httm_plan {
   Geo g;
   int64_t k_o;
   int64_t q_cap;
+  int64_t attn_units;  // upper bound of attention work units (all key splits; for the exact-path queue)
   int32_t lk_pad;
   float scale;
   size_t esize;
@@ -84,7 +85,6 @@ struct httm_plan {
   size_t dense_ws;
   size_t dense_vt_bytes, dense_kc_bytes;
   int32_t attn_split;
-  int64_t attn_units;  // upper bound of attention work units (all splits)
   std::vector<httm_block> blocks;
 };
 
@@ -245,7 +245,7 @@ httm_status build(const httm_params& p, httm_plan* pl) {
     Lw.vt = b.take(E * h * (size_t)pl->lk_pad * kD);
     Lw.o = b.take(E * (size_t)pl->q_cap * kD);
     Lw.kmax = b.take(4 * h);
-    Lw.fb = b.take(4 * (1 + (size_t)pl->attn_units));
+    Lw.fb = b.take(4 * (1 + (size_t)pl->attn_units));  // exact-path queue: count, then unit ids
     if (pl->attn_split > 1) {
       Lw.opart = b.take(4 * (size_t)pl->attn_split * pl->q_cap * kD);
       Lw.lpart = b.take(4 * (size_t)pl->attn_split * pl->q_cap);
@@ -454,8 +454,12 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
                              at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), cq, ck, st));
   stage_end(HTTM_T_SELECT, st);
 
+  const int64_t hn = (int64_t)g.heads * g.N;
   stage_begin(HTTM_T_MERGE_KV, st);
-  CHECK_LAUNCH(launch_attn_init(at<float>(ws, L.kmax), g.heads, at<int>(ws, L.fb), st));
+  // atomic targets of this layer: key norms, exact-path count, outlier scratch, outlier counts
+  CHECK_LAUNCH(launch_zero_init(at<float>(ws, L.kmax), g.heads, at<int>(ws, L.fb), at<uint32_t>(ws, L.radix),
+                                (int)outlier_scratch_words(hn), at<int32_t>(ws, L.ocnt),
+                                (int64_t)g.heads * g.nslots[kQ], st));
   CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
                                ck.members, ck.off,
                                at<void>(ws, L.kt), at<void>(ws, L.vt), at<float>(ws, L.kmax), st));
@@ -463,12 +467,13 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
 
   stage_begin(HTTM_T_MERGE_Q, st);
   CHECK_LAUNCH(launch_merge_q(dt, g.heads, g.N, g.nslots[kQ], q, cq.members, cq.off,
-                              at<float>(ws, L.qsum), at<float>(ws, L.delta), st));
+                              at<float>(ws, L.qsum), at<float>(ws, L.delta), at<uint32_t>(ws, L.radix), st));
   stage_end(HTTM_T_MERGE_Q, st);
 
   stage_begin(HTTM_T_OUTLIER, st);
-  CHECK_LAUNCH(launch_outliers(at<float>(ws, L.delta), (int64_t)g.heads * g.N, pl->k_o,
-                               at<uint8_t>(ws, L.mask), at<uint32_t>(ws, L.radix), st));
+  CHECK_LAUNCH(launch_outliers(at<float>(ws, L.delta), hn, pl->k_o, at<uint8_t>(ws, L.mask),
+                               at<uint32_t>(ws, L.radix), cq.group, g.N, g.nslots[kQ], at<int32_t>(ws, L.ocnt),
+                               st));
   stage_end(HTTM_T_OUTLIER, st);
 
   RestoreOut ro;
@@ -481,7 +486,7 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
   ro.foff = reinterpret_cast<int32_t*>(idx + I.foff.off);
   ro.slot = reinterpret_cast<int32_t*>(idx + I.slot.off);
   stage_begin(HTTM_T_RESTORE, st);
-  CHECK_LAUNCH(launch_restore(dt, g.heads, g.N, g.nslots[kQ], q, cq.members, cq.off, cq.group,
+  CHECK_LAUNCH(launch_restore(dt, g.heads, g.N, g.nslots[kQ], q, cq.members, cq.off,
                               at<float>(ws, L.qsum), at<uint8_t>(ws, L.mask), ro, st));
   stage_end(HTTM_T_RESTORE, st);
 
@@ -510,7 +515,8 @@ httm_status httm_layer_cached(const httm_plan* pl, void* ws, size_t ws_bytes, co
   char* idx = reinterpret_cast<char*>(index->dev);
   timing_begin_call();
   stage_begin(HTTM_T_MERGE_KV, st);
-  CHECK_LAUNCH(launch_attn_init(at<float>(ws, pl->L.kmax), g.heads, at<int>(ws, pl->L.fb), st));
+  CHECK_LAUNCH(launch_zero_init(at<float>(ws, pl->L.kmax), g.heads, at<int>(ws, pl->L.fb), nullptr, 0, nullptr, 0,
+                                st));
   CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
                                reinterpret_cast<const int32_t*>(idx + I.k_members.off),
                                reinterpret_cast<const int32_t*>(idx + I.k_off.off),
@@ -541,7 +547,7 @@ httm_status httm_attention_dense(const httm_plan* pl, void* ws, size_t ws_bytes,
   int* fb = reinterpret_cast<int*>(reinterpret_cast<char*>(kmax) + align256(pl->L.kmax.bytes));
   timing_begin_call();
   stage_begin(HTTM_T_MERGE_KV, st);
-  CHECK_LAUNCH(launch_attn_init(kmax, g.heads, fb, st));
+  CHECK_LAUNCH(launch_zero_init(kmax, g.heads, fb, nullptr, 0, nullptr, 0, st));
   CHECK_LAUNCH(launch_prep_dense(dt, g.heads, g.N, pitch, pl->scale * kLog2e, k, v, kc, ws, kmax, st));
   stage_end(HTTM_T_MERGE_KV, st);
   AttnShape a;

@@ -522,11 +522,6 @@ __global__ __launch_bounds__(256) void attn_finalize(AttnArgs a) {
   Row8<uint16_t>::store(reinterpret_cast<uint16_t*>(a.o) + R * kD + part * 8, acc);
 }
 
-__global__ void attn_init(float* kmax, int heads, int* fb_count) {
-  const int i = threadIdx.x;
-  if (i < heads) kmax[i] = 0.f;
-  if (i == 0) *fb_count = 0;
-}
 
 // fp32 inputs: one thread per query row, key tiles staged in LDS, fp32
 // online softmax.  For fp32 layers (small correctness workloads).
@@ -577,6 +572,8 @@ __global__ __launch_bounds__(kRowsF32) void attn_f32(AttnArgs a) {
 
 }  // namespace
 
+int attention_rows_per_unit() { return kRows; }
+
 int attention_split(int64_t q_capacity, int heads) {
   // Enough units for ~4 rounds of resident workgroups on 256 CUs at 4
   // workgroups each; at most 4 splits.
@@ -586,12 +583,7 @@ int attention_split(int64_t q_capacity, int heads) {
   return s < 1 ? 1 : (s > 4 ? 4 : s);
 }
 
-int attention_rows_per_unit() { return kRows; }
 
-hipError_t launch_attn_init(float* kmax, int heads, int* fb_count, hipStream_t stream) {
-  hipLaunchKernelGGL(attn_init, dim3(1), dim3(64), 0, stream, kmax, heads, fb_count);
-  return hipGetLastError();
-}
 
 namespace {
 AttnArgs make_args(int dtype, const AttnShape& s, const void* q, const void* k, const void* vt,

@@ -26,6 +26,8 @@ namespace httm {
 
 namespace {
 
+constexpr int kHist0Bins = 2048;  // first radix pass of the outlier select: bits 31..21
+
 __device__ __forceinline__ float rn_div(float a, float b) { return a / b; }  // correctly rounded
 
 template <typename T>
@@ -102,46 +104,110 @@ __device__ __forceinline__ void gather_sum(const T* const (&X)[NT], const int32_
 }
 
 // Merged K and V.  One workgroup (512 threads) = 64 consecutive key slots of
-// one head; 8 lanes per slot, 8 channels per lane.  K~ rows are written
-// directly, multiplied by kscale (the softmax scale times log2 e, so that the
-// attention kernel's scores come out in exp2 units; the product is rounded
-// once to the storage type with the mean).  V~ means go through LDS and are
-// written transposed (vt[h][c][slot]) so that the attention kernel reads V~
-// along keys with plain row loads.
+// one head.  The members of those slots are contiguous in the CSR list; they
+// are staged through LDS in chunks of kStage rows, loaded evenly by all
+// lanes (8 lanes per row, 8 channels each) regardless of group sizes, and
+// then each slot's 8 lanes add their members from LDS in member order
+// (separately rounded fp32 adds, like the oracle's means).  K~ rows are
+// multiplied by kscale (the softmax scale times log2 e, rounded once with
+// the mean); V~ means go through LDS and are written transposed
+// (vt[h][c][slot]) so that the attention kernel reads V~ along keys with plain
+// row loads.
+template <typename T>
+struct KvStage {
+  static constexpr int kRows = sizeof(T) == 2 ? 192 : 96;
+  static constexpr int kChunks = (int)sizeof(T) / 2;  // 16-byte chunks per 8-channel lane part
+};
+
+template <typename T>
+__device__ __forceinline__ void lds_row8_load(const u32x4* p, float* x) {
+  if constexpr (sizeof(T) == 2) {
+    Row8<uint16_t>::load(reinterpret_cast<const uint16_t*>(p), x);
+  } else {
+    Row8<float>::load(reinterpret_cast<const float*>(p), x);
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(512) void merge_kv(int N, int lk, int lk_pad, float kscale, const T* __restrict__ k,
                                                 const T* __restrict__ v,
                                                 const int32_t* __restrict__ members,
                                                 const int32_t* __restrict__ off, T* __restrict__ kt,
                                                 T* __restrict__ vt, float* __restrict__ kmax) {
-  __shared__ float sV[kD][65];
+  constexpr int R = KvStage<T>::kRows, NC = KvStage<T>::kChunks;  // NC 16-byte chunks per lane part
+  __shared__ u32x4 sRow[2][R][8 * NC];  // [tensor][row][lane part * NC + chunk]
+  __shared__ int sOf[65];
   __shared__ unsigned sMax;
   const int tiles = lk_pad / 64;
   const int head = blockIdx.x / tiles, tile = blockIdx.x % tiles;
   const int tid = threadIdx.x;
   const int ls = tid >> 3, part = tid & 7;
   const int slot = tile * 64 + ls;
-  const T* const X[2] = {k + (size_t)head * N * kD, v + (size_t)head * N * kD};
+  const T* K = k + (size_t)head * N * kD;
+  const T* V = v + (size_t)head * N * kD;
   const int32_t* mem = members + (size_t)head * N;
   const int32_t* of = off + (size_t)head * (lk + 1);
+  const int nsl = min(64, lk - tile * 64);  // real slots of this tile (<= 0: padding tile)
+  if (nsl > 0 && tid <= nsl) sOf[tid] = of[tile * 64 + tid];
+  __syncthreads();
+  const int mb = nsl > 0 ? sOf[0] : 0, me = nsl > 0 ? sOf[nsl] : 0;
+  const int m0 = slot < lk ? sOf[ls] : 0, m1 = slot < lk ? sOf[ls + 1] : 0;
   float acc[2][8];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
+  for (int c0 = mb; c0 < me; c0 += R) {
+    const int cnt = min(R, me - c0);
+    // stage rows c0 .. c0 + cnt: row i by the 8 lanes of group ls (i = ls, ls + 64, ...)
+    int tok[(R + 63) / 64];
+#pragma unroll
+    for (int q = 0; q < (R + 63) / 64; ++q) {
+      const int i = ls + 64 * q;
+      tok[q] = i < cnt ? mem[c0 + i] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < (R + 63) / 64; ++q) {
+      const int i = ls + 64 * q;
+      if (tok[q] >= 0) {
+        const u32x4* kr = reinterpret_cast<const u32x4*>(K + (size_t)tok[q] * kD) + part * NC;
+        const u32x4* vr = reinterpret_cast<const u32x4*>(V + (size_t)tok[q] * kD) + part * NC;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+          sRow[0][i][part * NC + cc] = kr[cc];
+          sRow[1][i][part * NC + cc] = vr[cc];
+        }
+      }
+    }
+    __syncthreads();
+    const int a0 = max(m0, c0), a1 = min(m1, c0 + cnt);
+    for (int m = a0; m < a1; ++m) {
+      float xk[8], xv[8];
+      lds_row8_load<T>(&sRow[0][m - c0][part * NC], xk);
+      lds_row8_load<T>(&sRow[1][m - c0][part * NC], xv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        acc[0][e] = __fadd_rn(acc[0][e], xk[e]);
+        acc[1][e] = __fadd_rn(acc[1][e], xv[e]);
+      }
+    }
+    __syncthreads();  // before the next chunk overwrites the rows
+  }
   float nmax = 0.f;
   if (slot < lk) {
-    const int m0 = of[slot], m1 = of[slot + 1];
-    gather_sum<T, 4, 2>(X, mem, m0, m1, part, acc);
-    const float cnt = (float)(m1 - m0);
+    const float c = (float)(m1 - m0);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      acc[0][e] = rn_div(acc[0][e], cnt) * kscale;
-      acc[1][e] = rn_div(acc[1][e], cnt);
+      acc[0][e] = rn_div(acc[0][e], c) * kscale;
+      acc[1][e] = rn_div(acc[1][e], c);
     }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[0][e] = acc[1][e] = 0.f;
   }
   store8(kt + ((size_t)head * lk_pad + slot) * kD + part * 8, acc[0]);
   const float nrm = row_norm8<T>(acc[0]);
   if (slot < lk) nmax = nrm;
+  // transpose V~ through the (now free) staging buffer: float [64 channels][65]
+  float(*sV)[65] = reinterpret_cast<float(*)[65]>(&sRow[0][0][0]);
+  static_assert(sizeof(sRow) >= sizeof(float) * 64 * 65, "staging buffer holds the transpose");
 #pragma unroll
   for (int e = 0; e < 8; ++e) sV[part * 8 + e][ls] = acc[1][e];
   wg_atomic_max(nmax, &sMax, kmax + head);  // also orders the sV writes before the reads below
@@ -155,7 +221,8 @@ __global__ __launch_bounds__(512) void merge_kv(int N, int lk, int lk_pad, float
 }
 
 // Query group sums and deviations.  One workgroup = 64 consecutive query
-// groups of one head.  Phase 1: 8 lanes per group sum the members (fp32,
+// groups of one head.  Every deviation also enters the first histogram of the
+// outlier radix select (bits 31..21 of its non-negative float pattern).  Phase 1: 8 lanes per group sum the members (fp32,
 // member order) and keep the mean in LDS.  Phase 2: one lane per member
 // computes sqrt(sum_c (q_c - mean_c)^2), the sum over channels in ascending
 // order; members of the 64 groups are contiguous in the CSR, a binary search
@@ -165,9 +232,12 @@ __global__ __launch_bounds__(512) void merge_q(int N, int gq, const T* __restric
                                                const int32_t* __restrict__ members,
                                                const int32_t* __restrict__ off,
                                                float* __restrict__ qsum,
-                                               float* __restrict__ delta) {
+                                               float* __restrict__ delta,
+                                               uint32_t* __restrict__ hist0) {
   __shared__ float sMean[64][kD + 1];
   __shared__ int sOff[65];
+  __shared__ uint32_t sHist[kHist0Bins];
+  for (int i = threadIdx.x; i < kHist0Bins; i += 512) sHist[i] = 0;
   const int tiles = ceil_div(gq, 64);
   const int head = blockIdx.x / tiles, tile = blockIdx.x % tiles;
   const int g0 = tile * 64;
@@ -209,8 +279,13 @@ __global__ __launch_bounds__(512) void merge_q(int N, int gq, const T* __restric
         acc = __fadd_rn(acc, __fmul_rn(t, t));
       }
     }
-    delta[(size_t)head * N + tok] = sqrtf(acc);
+    const float d = sqrtf(acc);
+    delta[(size_t)head * N + tok] = d;
+    atomicAdd(&sHist[__float_as_uint(d) >> 21], 1u);
   }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kHist0Bins; i += 512)
+    if (sHist[i]) atomicAdd(&hist0[i], sHist[i]);
 }
 
 // Exclusive scan of one value per thread over a 1024-thread block.
@@ -236,23 +311,6 @@ __device__ int block_exclusive_scan(int v, int* sh /* >= 16 */, int& total) {
   __syncthreads();
   total = sh[16];
   return sh[wave] + x - v;
-}
-
-// Restore, part 0: per initial query group, the number of outlier members
-// (integer atomics, one thread per token; the counts do not depend on order).
-__global__ __launch_bounds__(256) void restore_count(int64_t total, int N, int gq,
-                                                     const uint8_t* __restrict__ mask,
-                                                     const int32_t* __restrict__ group,
-                                                     int32_t* __restrict__ ocnt) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= total || !mask[i]) return;
-  const int head = (int)(i / N);
-  atomicAdd(&ocnt[(size_t)head * gq + group[i]], 1);
-}
-
-__global__ __launch_bounds__(256) void zero_i32(int32_t* p, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0;
 }
 
 // Restore, part 1 (one workgroup per head): each initial query group g with
@@ -518,20 +576,16 @@ hipError_t launch_merge_kv(int dtype, int heads, int N, int lk, int lk_pad, floa
 
 hipError_t launch_merge_q(int dtype, int heads, int N, int gq, const void* q,
                           const int32_t* members, const int32_t* off, float* qsum, float* delta,
-                          hipStream_t stream) {
+                          uint32_t* hist0, hipStream_t stream) {
   const int grid = heads * ceil_div(gq, 64);
   HTTM_DISPATCH(dtype, hipLaunchKernelGGL(merge_q<T>, dim3(grid), dim3(512), 0, stream, N, gq,
-                                          (const T*)q, members, off, qsum, delta));
+                                          (const T*)q, members, off, qsum, delta, hist0));
   return hipGetLastError();
 }
 
 hipError_t launch_restore(int dtype, int heads, int N, int gq, const void* q,
-                          const int32_t* members, const int32_t* off, const int32_t* group,
-                          const float* qsum, const uint8_t* mask, RestoreOut o, hipStream_t stream) {
-  const int64_t groups = (int64_t)heads * gq, total = (int64_t)heads * N;
-  hipLaunchKernelGGL(zero_i32, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream, o.ocnt, groups);
-  hipLaunchKernelGGL(restore_count, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, total, N, gq,
-                     mask, group, o.ocnt);
+                          const int32_t* members, const int32_t* off, const float* qsum,
+                          const uint8_t* mask, RestoreOut o, hipStream_t stream) {
   hipLaunchKernelGGL(restore_scan, dim3(heads), dim3(1024), 0, stream, N, gq, off, o.ocnt, o.base, o.lenq,
                      o.foff);
   hipError_t e = hipGetLastError();

@@ -6,7 +6,8 @@
 //
 // Deviations are non-negative floats, so their bit patterns order like their
 // values.  A radix select finds the threshold pattern T = the k_o-th largest
-// in three histogram passes (11, 11, 10 bits); every workgroup recomputes the
+// in three histogram passes (11, 11, 10 bits; the first is accumulated by the
+// deviation producer as it writes them); every workgroup recomputes the
 // prefix it needs from the previous histogram in LDS, so no serial "find the
 // bin" kernel sits between the passes.  A marking pass sets values above T and
 // counts values equal to T per chunk; a last pass gives the equal values
@@ -32,6 +33,15 @@ struct Scratch {
   uint32_t* ties; // [nchunks]
 };
 
+// Outlier members per initial query group, counted where the mask bits are
+// set (integer atomics: the counts do not depend on order).
+struct OutlierGroups {
+  const int32_t* group;  // [h][N] token -> initial query group
+  int32_t* ocnt;         // [h][gq]
+  int N, gq;
+  __device__ __forceinline__ void add(int64_t i) const { atomicAdd(&ocnt[(i / N) * gq + group[i]], 1); }
+};
+
 __device__ __forceinline__ Scratch scratch_of(uint32_t* s) {
   Scratch r;
   r.h0 = s;
@@ -42,9 +52,21 @@ __device__ __forceinline__ Scratch scratch_of(uint32_t* s) {
   return r;
 }
 
-__global__ void zero_words(uint32_t* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
+// Zero the layer's atomic targets before its producers run (one launch).
+__global__ void zero_init(float* kmax, int heads, int* fb_count, uint32_t* radix, int radix_words,
+                          int32_t* ocnt, int64_t ocnt_words) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < heads) kmax[i] = 0.f;
+  if (i == 0) *fb_count = 0;
+  if (i < radix_words) radix[i] = 0;
+  for (int64_t j = i; j < ocnt_words; j += (int64_t)gridDim.x * blockDim.x) ocnt[j] = 0;
+}
+
+// Every token is an outlier: ocnt[h][g] = size of group g.
+__global__ void count_all(int64_t total, int N, int gq, const int32_t* __restrict__ group,
+                          int32_t* __restrict__ ocnt) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < total) atomicAdd(&ocnt[(i / N) * gq + group[i]], 1);
 }
 
 __global__ void fill_bytes(uint8_t* p, int64_t n, uint8_t v) {
@@ -172,7 +194,7 @@ __device__ void threshold(const Scratch& s, uint32_t k_o, uint32_t* hist, uint32
 // Marks values above T; counts values equal to T in this chunk.
 __global__ __launch_bounds__(kThreads) void radix_mark(const float* __restrict__ delta, int64_t total,
                                                        uint32_t k_o, uint32_t* scratch,
-                                                       uint8_t* __restrict__ mask) {
+                                                       uint8_t* __restrict__ mask, OutlierGroups og) {
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t part[kThreads];
   __shared__ uint32_t res[4];
@@ -210,6 +232,9 @@ __global__ __launch_bounds__(kThreads) void radix_mark(const float* __restrict__
     for (int e = 0; e < kPerThread; ++e)
       if (i0 + e < total) mask[i0 + e] = m[e];
   }
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e)
+    if (m[e]) og.add(i0 + e);
   if (eq) atomicAdd(&cnt, eq);
   __syncthreads();
   if (threadIdx.x == 0) s.ties[blockIdx.x] = cnt;
@@ -217,7 +242,8 @@ __global__ __launch_bounds__(kThreads) void radix_mark(const float* __restrict__
 
 // Values equal to T, in flat-index order, take the remaining budget.
 __global__ __launch_bounds__(kThreads) void radix_ties(const float* __restrict__ delta, int64_t total,
-                                                       uint32_t* scratch, uint8_t* __restrict__ mask) {
+                                                       uint32_t* scratch, uint8_t* __restrict__ mask,
+                                                       OutlierGroups og) {
   __shared__ uint32_t part[kThreads];
   __shared__ uint32_t before;
   Scratch s = scratch_of(scratch);
@@ -257,7 +283,10 @@ __global__ __launch_bounds__(kThreads) void radix_ties(const float* __restrict__
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     if (u[e] == T && u[e] != 0xFFFFFFFFu) {
-      if (rank < need) mask[i0 + e] = 1;
+      if (rank < need) {
+        mask[i0 + e] = 1;
+        og.add(i0 + e);
+      }
       ++rank;
     }
   }
@@ -269,24 +298,39 @@ size_t outlier_scratch_words(int64_t total) {
   return 3 * kBins + 4 + (size_t)((total + kChunk - 1) / kChunk);
 }
 
+hipError_t launch_zero_init(float* kmax, int heads, int* fb_count, uint32_t* radix, int radix_words,
+                            int32_t* ocnt, int64_t ocnt_words, hipStream_t stream) {
+  int64_t n = heads > radix_words ? heads : radix_words;
+  if (ocnt_words > n) n = ocnt_words;
+  int64_t grid = (n + 255) / 256;
+  grid = grid < 1 ? 1 : (grid > 2048 ? 2048 : grid);
+  hipLaunchKernelGGL(zero_init, dim3((unsigned)grid), dim3(256), 0, stream, kmax, heads, fb_count, radix,
+                     radix_words, ocnt, ocnt_words);
+  return hipGetLastError();
+}
+
+int outlier_hist0_words() { return kBins; }
+
 hipError_t launch_outliers(const float* delta, int64_t total, int64_t k_o, uint8_t* mask,
-                           uint32_t* scratch, hipStream_t stream) {
+                           uint32_t* scratch, const int32_t* group, int N, int gq, int32_t* ocnt,
+                           hipStream_t stream) {
+  OutlierGroups og{group, ocnt, N, gq};
   if (k_o <= 0 || k_o >= total) {
     const uint8_t v = k_o <= 0 ? 0 : 1;
     hipLaunchKernelGGL(fill_bytes, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, mask,
                        total, v);
+    if (v) hipLaunchKernelGGL(count_all, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, total, N,
+                              gq, group, ocnt);
     return hipGetLastError();
   }
   const int nchunks = (int)((total + kChunk - 1) / kChunk);
-  const int zw = 3 * kBins + 4;
-  hipLaunchKernelGGL(zero_words, dim3((zw + 255) / 256), dim3(256), 0, stream, scratch, zw);
   const uint32_t k = (uint32_t)k_o;
-  hipLaunchKernelGGL(radix_hist<0>, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch);
+  // pass 0 (bits 31..21) was accumulated by the deviation producer into the zeroed scratch
   hipLaunchKernelGGL(radix_hist<1>, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch);
   hipLaunchKernelGGL(radix_hist<2>, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch);
   hipLaunchKernelGGL(radix_mark, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch,
-                     mask);
-  hipLaunchKernelGGL(radix_ties, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, scratch, mask);
+                     mask, og);
+  hipLaunchKernelGGL(radix_ties, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, scratch, mask, og);
   return hipGetLastError();
 }
 

@@ -32,15 +32,22 @@ hipError_t launch_merge_kv(int dtype, int heads, int N, int lk, int lk_pad, floa
                            const void* v, const int32_t* members, const int32_t* off, void* kt,
                            void* vt, float* kmax, hipStream_t stream);
 
-// Query group sums (fp32) and deviation of every query to its group mean.
+// Query group sums (fp32) and deviation of every query to its group mean;
+// also adds every deviation to hist0 (bits 31..21 of its pattern, the first
+// radix pass of the outlier select; zeroed beforehand).
 hipError_t launch_merge_q(int dtype, int heads, int N, int gq, const void* q,
                           const int32_t* members, const int32_t* off, float* qsum, float* delta,
-                          hipStream_t stream);
+                          uint32_t* hist0, hipStream_t stream);
 
-// Global top-k_o of delta [h*N] -> mask; scratch: 3*2048 + 4 + nchunks words.
+// Global top-k_o of delta [h*N] -> mask, and per initial query group the
+// number of outlier members (ocnt [h][gq], zeroed beforehand; group [h][N] is
+// the token -> group map).  scratch: outlier_scratch_words(total) words,
+// zeroed beforehand, whose first outlier_hist0_words() hold the first pass.
 size_t outlier_scratch_words(int64_t total);
+int outlier_hist0_words();
 hipError_t launch_outliers(const float* delta, int64_t total, int64_t k_o, uint8_t* mask,
-                           uint32_t* scratch, hipStream_t stream);
+                           uint32_t* scratch, const int32_t* group, int N, int gq, int32_t* ocnt,
+                           hipStream_t stream);
 
 // Outlier restore: packed Q~ rows, per-head lengths, final partition.
 struct RestoreOut {
@@ -48,14 +55,14 @@ struct RestoreOut {
   int32_t* lenq;       // [h]
   int32_t* cu_q;       // [h+1]
   int32_t* base;       // [h][gq] scratch: first final slot of each initial group
-  int32_t* ocnt;       // [h][gq] scratch: outlier members per initial group
+  const int32_t* ocnt; // [h][gq] outlier members per initial group (from launch_outliers)
   int32_t* fmembers;   // [h][N]
   int32_t* foff;       // [h][N+1]
   int32_t* slot;       // [h][N] packed row per token
 };
 hipError_t launch_restore(int dtype, int heads, int N, int gq, const void* q,
-                          const int32_t* members, const int32_t* off, const int32_t* group,
-                          const float* qsum, const uint8_t* mask, RestoreOut o, hipStream_t stream);
+                          const int32_t* members, const int32_t* off, const float* qsum,
+                          const uint8_t* mask, RestoreOut o, hipStream_t stream);
 
 // Cached mode: Q~ rows as means over the final query partition.
 hipError_t launch_merge_q_cached(int dtype, int heads, int N, int64_t q_capacity, const void* q,
@@ -78,14 +85,17 @@ struct AttnShape {
   float* lpart;            // [split][q_capacity]
   float* mpart;            // [split][q_capacity]
   const float* kmax;       // [heads] max |k row|
-  int* fb_count;           // [1] units queued for the exact kernel (zeroed by launch_attn_init)
+  int* fb_count;           // [1] units queued for the exact kernel (zeroed by launch_zero_init)
   int* fb_list;            // [units]
 };
 // Key splits for a layer of q_capacity packed rows; rows per work unit.
 int attention_split(int64_t q_capacity, int heads);
 int attention_rows_per_unit();
-// Zero kmax[heads] and the fallback queue counter (before the K producer runs).
-hipError_t launch_attn_init(float* kmax, int heads, int* fb_count, hipStream_t stream);
+// Zero, before a layer's producers run: kmax[heads] (atomic max target of the
+// K~ producer), the exact-path counter, and optionally the outlier radix
+// scratch (radix_words) and the per-group outlier counts (ocnt_words).
+hipError_t launch_zero_init(float* kmax, int heads, int* fb_count, uint32_t* radix, int radix_words,
+                            int32_t* ocnt, int64_t ocnt_words, hipStream_t stream);
 // The main attention kernel, then the tail: exact recompute of the units the
 // main kernel queued and (key splits > 1) the combine of the partials.
 hipError_t launch_attention(int dtype, const AttnShape& s, const void* q, const void* k,
