@@ -177,9 +177,9 @@ def main():
     peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     achieved = attn_flop / (attn_ms * 1e-3) / 1e12
 
-    # per-stage breakdown (separate untimed pass; events around every stage)
+    # per-stage breakdown (separate untimed pass; events around every stage, 30 calls)
     H.set_timing(None)
-    for _ in range(5):
+    for _ in range(30):
         H.layer(plan, q, k, v, ws=ws, out=out, stream=stream)
     stages, _ = H.get_timing()
     H.set_timing([])

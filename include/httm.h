@@ -42,7 +42,8 @@
  *     surface at the caller's next synchronisation.
  *   - Calls that share a workspace or index buffer must be ordered on one
  *     stream; concurrent calls need separate buffers.
- *   - Sizes: validation requires heads * N < 2^31 and n_s * n_t <= 4096.
+ *   - Sizes: validation requires heads * N < 2^31, n_s * n_t <= 4096 and
+ *     heads <= 64 (HTTM_ERR_UNSUPPORTED otherwise).
  */
 #ifndef HTTM_H_
 #define HTTM_H_

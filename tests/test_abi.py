@@ -110,6 +110,8 @@ def test_validation_codes():
     assert _status(d_head=128) == 2
     assert _status(block_order=1) == 2
     assert _status(n_s=128, n_t=33) == 2  # block larger than 4096
+    assert _status(heads=64) == 0
+    assert _status(heads=65) == 2  # per-head prefix tables are sized for 64
     assert _status(softmax_scale=float("inf")) == 1
 
 

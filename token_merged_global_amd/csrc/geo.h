@@ -24,6 +24,7 @@ namespace httm {
 
 constexpr int kD = 64;          // d_head
 constexpr int kMaxBlock = 4096; // largest supported block (fits LDS sorts)
+constexpr int kMaxHeads = 64;   // per-head prefix tables in LDS hold kMaxHeads + 1 entries
 
 enum Stream { kQ = 0, kK = 1 };
 

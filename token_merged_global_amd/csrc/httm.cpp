@@ -115,6 +115,7 @@ httm_status build(const httm_params& p, httm_plan* pl) {
     return fail(HTTM_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
   if (p.dtype != HTTM_F32 && p.dtype != HTTM_BF16) return fail(HTTM_ERR_INVALID_ARG, "unknown dtype");
   if (p.d_head != kD) return fail(HTTM_ERR_UNSUPPORTED, "only d_head == 64 is built");
+  if (p.heads > kMaxHeads) return fail(HTTM_ERR_UNSUPPORTED, "at most 64 heads (per-head prefix tables live in LDS)");
   if (p.block_order != 0) return fail(HTTM_ERR_UNSUPPORTED, "only frame-major blocks (block_order 0) are built");
   if ((int64_t)p.n_s * p.n_t > kMaxBlock) return fail(HTTM_ERR_UNSUPPORTED, "n_s * n_t must be <= 4096");
   const int64_t T = (int64_t)p.n_special + (int64_t)p.grid_h * p.grid_w;

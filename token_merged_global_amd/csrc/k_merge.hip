@@ -452,7 +452,7 @@ __global__ __launch_bounds__(256) void merge_q_cached(int heads, int N, const T*
                                                       const int32_t* __restrict__ foff,
                                                       const int32_t* __restrict__ lenq,
                                                       T* __restrict__ qt) {
-  __shared__ int sCu[65];
+  __shared__ int sCu[kMaxHeads + 1];
   if (threadIdx.x == 0) {
     int acc = 0;
     for (int h = 0; h < heads; ++h) {
