@@ -42,6 +42,11 @@
  *     surface at the caller's next synchronisation.
  *   - Calls that share a workspace or index buffer must be ordered on one
  *     stream; concurrent calls need separate buffers.
+ *   - httm_layer / httm_layer_cached run the K/V merge on a library-owned
+ *     stream of the current device (created on first use, default priority)
+ *     that waits for the caller's stream and is joined back into it with
+ *     events before the attention, so the caller sees one ordered stream.
+ *     Enqueueing is serialised by an internal lock.
  *   - Sizes: validation requires heads * N < 2^31, n_s * n_t <= 4096 and
  *     heads <= 64 (HTTM_ERR_UNSUPPORTED otherwise).
  */

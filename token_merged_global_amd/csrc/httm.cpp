@@ -14,6 +14,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -33,6 +34,18 @@ httm_status fail(httm_status s, const std::string& msg) {
 }
 
 std::atomic<uint64_t> g_plan_counter{0x48540000ull};
+
+// The K/V merge runs on a library stream (one per device, default priority)
+// concurrently with the query path on the caller's stream: forked after the
+// block selection, joined before attention.  The lock makes each call's
+// record/wait pairs on the shared fork/join events atomic.
+constexpr int kMaxDevices = 64;
+struct SideStream {
+  hipStream_t st = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_launch_mu;
+SideStream g_side[kMaxDevices];
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -304,6 +317,22 @@ void timing_end_call() {
     if (e_ != hipSuccess) return fail(HTTM_ERR_DEVICE, std::string(#expr) + ": " + hipGetErrorString(e_)); \
   } while (0)
 
+// Side stream of the current device (created on first use; call with g_launch_mu held).
+httm_status side_stream(SideStream** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(HTTM_ERR_DEVICE, "no usable current device");
+  SideStream& s = g_side[dev];
+  if (!s.st) {
+    if (hipStreamCreateWithFlags(&s.st, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&s.join, hipEventDisableTiming) != hipSuccess)
+      return fail(HTTM_ERR_DEVICE, "creating the library stream failed");
+  }
+  *out = &s;
+  return HTTM_OK;
+}
+
 httm_status check_common(const httm_plan* plan, void* ws, size_t ws_bytes, const void* q,
                          const void* k, const void* v, void* out, size_t need) {
   if (!plan) return fail(HTTM_ERR_INVALID_ARG, "plan is NULL");
@@ -440,6 +469,10 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
   const IndexLayout& I = pl->I;
   const int dt = pl->p.dtype;
   char* idx = index ? reinterpret_cast<char*>(index->dev) : at<char>(ws, L.index);
+  std::lock_guard<std::mutex> lock(g_launch_mu);
+  SideStream* side = nullptr;
+  s = side_stream(&side);
+  if (s != HTTM_OK) return s;
   timing_begin_call();
 
   stage_begin(HTTM_T_SIM, st);
@@ -456,15 +489,19 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
   stage_end(HTTM_T_SELECT, st);
 
   const int64_t hn = (int64_t)g.heads * g.N;
-  stage_begin(HTTM_T_MERGE_KV, st);
   // atomic targets of this layer: key norms, exact-path count, outlier scratch, outlier counts
   CHECK_LAUNCH(launch_zero_init(at<float>(ws, L.kmax), g.heads, at<int>(ws, L.fb), at<uint32_t>(ws, L.radix),
                                 (int)outlier_scratch_words(hn), at<int32_t>(ws, L.ocnt),
                                 (int64_t)g.heads * g.nslots[kQ], st));
+  // K/V merge on the side stream, concurrent with the query path below
+  CHECK_LAUNCH(hipEventRecord(side->fork, st));
+  CHECK_LAUNCH(hipStreamWaitEvent(side->st, side->fork, 0));
+  stage_begin(HTTM_T_MERGE_KV, side->st);
   CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
                                ck.members, ck.off,
-                               at<void>(ws, L.kt), at<void>(ws, L.vt), at<float>(ws, L.kmax), st));
-  stage_end(HTTM_T_MERGE_KV, st);
+                               at<void>(ws, L.kt), at<void>(ws, L.vt), at<float>(ws, L.kmax), side->st));
+  stage_end(HTTM_T_MERGE_KV, side->st);
+  CHECK_LAUNCH(hipEventRecord(side->join, side->st));
 
   stage_begin(HTTM_T_MERGE_Q, st);
   CHECK_LAUNCH(launch_merge_q(dt, g.heads, g.N, g.nslots[kQ], q, cq.members, cq.off,
@@ -491,6 +528,7 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
                               at<float>(ws, L.qsum), at<uint8_t>(ws, L.mask), ro, st));
   stage_end(HTTM_T_RESTORE, st);
 
+  CHECK_LAUNCH(hipStreamWaitEvent(st, side->join, 0));
   s = attend_unmerge(pl, ws, idx, at<void>(ws, L.qt), out, st);
   if (s != HTTM_OK) return s;
   if (index) {
@@ -514,15 +552,22 @@ httm_status httm_layer_cached(const httm_plan* pl, void* ws, size_t ws_bytes, co
   const IndexLayout& I = pl->I;
   const int dt = pl->p.dtype;
   char* idx = reinterpret_cast<char*>(index->dev);
+  std::lock_guard<std::mutex> lock(g_launch_mu);
+  SideStream* side = nullptr;
+  s = side_stream(&side);
+  if (s != HTTM_OK) return s;
   timing_begin_call();
-  stage_begin(HTTM_T_MERGE_KV, st);
   CHECK_LAUNCH(launch_zero_init(at<float>(ws, pl->L.kmax), g.heads, at<int>(ws, pl->L.fb), nullptr, 0, nullptr, 0,
                                 st));
+  CHECK_LAUNCH(hipEventRecord(side->fork, st));
+  CHECK_LAUNCH(hipStreamWaitEvent(side->st, side->fork, 0));
+  stage_begin(HTTM_T_MERGE_KV, side->st);
   CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
                                reinterpret_cast<const int32_t*>(idx + I.k_members.off),
                                reinterpret_cast<const int32_t*>(idx + I.k_off.off),
-                               at<void>(ws, pl->L.kt), at<void>(ws, pl->L.vt), at<float>(ws, pl->L.kmax), st));
-  stage_end(HTTM_T_MERGE_KV, st);
+                               at<void>(ws, pl->L.kt), at<void>(ws, pl->L.vt), at<float>(ws, pl->L.kmax), side->st));
+  stage_end(HTTM_T_MERGE_KV, side->st);
+  CHECK_LAUNCH(hipEventRecord(side->join, side->st));
   stage_begin(HTTM_T_MERGE_Q, st);
   CHECK_LAUNCH(launch_merge_q_cached(dt, g.heads, g.N, pl->q_cap, q,
                                      reinterpret_cast<const int32_t*>(idx + I.fmembers.off),
@@ -530,6 +575,7 @@ httm_status httm_layer_cached(const httm_plan* pl, void* ws, size_t ws_bytes, co
                                      reinterpret_cast<const int32_t*>(idx + I.lenq.off),
                                      at<void>(ws, pl->L.qt), st));
   stage_end(HTTM_T_MERGE_Q, st);
+  CHECK_LAUNCH(hipStreamWaitEvent(st, side->join, 0));
   s = attend_unmerge(pl, ws, idx, at<void>(ws, pl->L.qt), out, st);
   if (s == HTTM_OK) timing_end_call();
   return s;

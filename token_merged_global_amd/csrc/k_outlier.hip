@@ -33,15 +33,6 @@ struct Scratch {
   uint32_t* ties; // [nchunks]
 };
 
-// Outlier members per initial query group, counted where the mask bits are
-// set (integer atomics: the counts do not depend on order).
-struct OutlierGroups {
-  const int32_t* group;  // [h][N] token -> initial query group
-  int32_t* ocnt;         // [h][gq]
-  int N, gq;
-  __device__ __forceinline__ void add(int64_t i) const { atomicAdd(&ocnt[(i / N) * gq + group[i]], 1); }
-};
-
 __device__ __forceinline__ Scratch scratch_of(uint32_t* s) {
   Scratch r;
   r.h0 = s;
@@ -62,11 +53,12 @@ __global__ void zero_init(float* kmax, int heads, int* fb_count, uint32_t* radix
   for (int64_t j = i; j < ocnt_words; j += (int64_t)gridDim.x * blockDim.x) ocnt[j] = 0;
 }
 
-// Every token is an outlier: ocnt[h][g] = size of group g.
-__global__ void count_all(int64_t total, int N, int gq, const int32_t* __restrict__ group,
-                          int32_t* __restrict__ ocnt) {
+// Outlier members per initial query group: one thread per token, integer
+// atomics (the counts do not depend on order).
+__global__ void count_outliers(int64_t total, int N, int gq, const uint8_t* __restrict__ mask,
+                               const int32_t* __restrict__ group, int32_t* __restrict__ ocnt) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < total) atomicAdd(&ocnt[(i / N) * gq + group[i]], 1);
+  if (i < total && mask[i]) atomicAdd(&ocnt[(i / N) * gq + group[i]], 1);
 }
 
 __global__ void fill_bytes(uint8_t* p, int64_t n, uint8_t v) {
@@ -194,7 +186,7 @@ __device__ void threshold(const Scratch& s, uint32_t k_o, uint32_t* hist, uint32
 // Marks values above T; counts values equal to T in this chunk.
 __global__ __launch_bounds__(kThreads) void radix_mark(const float* __restrict__ delta, int64_t total,
                                                        uint32_t k_o, uint32_t* scratch,
-                                                       uint8_t* __restrict__ mask, OutlierGroups og) {
+                                                       uint8_t* __restrict__ mask) {
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t part[kThreads];
   __shared__ uint32_t res[4];
@@ -232,9 +224,6 @@ __global__ __launch_bounds__(kThreads) void radix_mark(const float* __restrict__
     for (int e = 0; e < kPerThread; ++e)
       if (i0 + e < total) mask[i0 + e] = m[e];
   }
-#pragma unroll
-  for (int e = 0; e < kPerThread; ++e)
-    if (m[e]) og.add(i0 + e);
   if (eq) atomicAdd(&cnt, eq);
   __syncthreads();
   if (threadIdx.x == 0) s.ties[blockIdx.x] = cnt;
@@ -242,8 +231,7 @@ __global__ __launch_bounds__(kThreads) void radix_mark(const float* __restrict__
 
 // Values equal to T, in flat-index order, take the remaining budget.
 __global__ __launch_bounds__(kThreads) void radix_ties(const float* __restrict__ delta, int64_t total,
-                                                       uint32_t* scratch, uint8_t* __restrict__ mask,
-                                                       OutlierGroups og) {
+                                                       uint32_t* scratch, uint8_t* __restrict__ mask) {
   __shared__ uint32_t part[kThreads];
   __shared__ uint32_t before;
   Scratch s = scratch_of(scratch);
@@ -283,10 +271,7 @@ __global__ __launch_bounds__(kThreads) void radix_ties(const float* __restrict__
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     if (u[e] == T && u[e] != 0xFFFFFFFFu) {
-      if (rank < need) {
-        mask[i0 + e] = 1;
-        og.add(i0 + e);
-      }
+      if (rank < need) mask[i0 + e] = 1;
       ++rank;
     }
   }
@@ -314,23 +299,21 @@ int outlier_hist0_words() { return kBins; }
 hipError_t launch_outliers(const float* delta, int64_t total, int64_t k_o, uint8_t* mask,
                            uint32_t* scratch, const int32_t* group, int N, int gq, int32_t* ocnt,
                            hipStream_t stream) {
-  OutlierGroups og{group, ocnt, N, gq};
+  const unsigned tgrid = (unsigned)((total + 255) / 256);
   if (k_o <= 0 || k_o >= total) {
     const uint8_t v = k_o <= 0 ? 0 : 1;
-    hipLaunchKernelGGL(fill_bytes, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, mask,
-                       total, v);
-    if (v) hipLaunchKernelGGL(count_all, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, total, N,
-                              gq, group, ocnt);
-    return hipGetLastError();
+    hipLaunchKernelGGL(fill_bytes, dim3(tgrid), dim3(256), 0, stream, mask, total, v);
+  } else {
+    const int nchunks = (int)((total + kChunk - 1) / kChunk);
+    const uint32_t k = (uint32_t)k_o;
+    // pass 0 (bits 31..21) was accumulated by the deviation producer into the zeroed scratch
+    hipLaunchKernelGGL(radix_hist<1>, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch);
+    hipLaunchKernelGGL(radix_hist<2>, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch);
+    hipLaunchKernelGGL(radix_mark, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch, mask);
+    hipLaunchKernelGGL(radix_ties, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, scratch, mask);
   }
-  const int nchunks = (int)((total + kChunk - 1) / kChunk);
-  const uint32_t k = (uint32_t)k_o;
-  // pass 0 (bits 31..21) was accumulated by the deviation producer into the zeroed scratch
-  hipLaunchKernelGGL(radix_hist<1>, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch);
-  hipLaunchKernelGGL(radix_hist<2>, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch);
-  hipLaunchKernelGGL(radix_mark, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch,
-                     mask, og);
-  hipLaunchKernelGGL(radix_ties, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, scratch, mask, og);
+  if (k_o > 0)
+    hipLaunchKernelGGL(count_outliers, dim3(tgrid), dim3(256), 0, stream, total, N, gq, mask, group, ocnt);
   return hipGetLastError();
 }
 
