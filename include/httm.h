@@ -42,10 +42,11 @@
  *     surface at the caller's next synchronisation.
  *   - Calls that share a workspace or index buffer must be ordered on one
  *     stream; concurrent calls need separate buffers.
- *   - httm_layer / httm_layer_cached run the K/V merge on a library-owned
- *     stream of the current device (created on first use, default priority)
- *     that waits for the caller's stream and is joined back into it with
- *     events before the attention, so the caller sees one ordered stream.
+ *   - httm_layer runs the key branch (K similarity, K selection, K/V merge)
+ *     and httm_layer_cached the K/V merge on a library-owned stream of the
+ *     current device (created on first use, default priority) that waits for
+ *     the caller's stream and is joined back into it with events before the
+ *     attention, so the caller sees one ordered stream.
  *     Enqueueing is serialised by an internal lock.
  *   - Sizes: validation requires heads * N < 2^31, n_s * n_t <= 4096 and
  *     heads <= 64 (HTTM_ERR_UNSUPPORTED otherwise).
@@ -204,6 +205,10 @@ httm_status httm_debug_read(const httm_plan* plan, const void* ws, const httm_in
  * milliseconds between the events over the recorded calls that ran that
  * stage (0 if none) and the number of recorded calls; it synchronises on
  * the events.  Host-side state, not thread-safe. */
+/* In httm_layer the key branch (K similarity, K selection, K/V merge) runs on
+ * the library stream concurrently with the query branch: HTTM_T_MERGE_KV
+ * times that whole branch there, HTTM_T_SIM and HTTM_T_SELECT the query
+ * stream's similarity and selection. */
 typedef enum {
   HTTM_T_SIM = 0, HTTM_T_SELECT, HTTM_T_MERGE_KV, HTTM_T_MERGE_Q, HTTM_T_OUTLIER,
   HTTM_T_RESTORE,

@@ -475,33 +475,38 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
   if (s != HTTM_OK) return s;
   timing_begin_call();
 
-  stage_begin(HTTM_T_SIM, st);
-  CHECK_LAUNCH(launch_sim(g, dt, q, k, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
-                          at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), st));
-  stage_end(HTTM_T_SIM, st);
-
   Csr cq{at<int32_t>(ws, L.q_members), at<int32_t>(ws, L.q_off), at<int32_t>(ws, L.q_group)};
   Csr ck{reinterpret_cast<int32_t*>(idx + I.k_members.off), reinterpret_cast<int32_t*>(idx + I.k_off.off),
          at<int32_t>(ws, L.k_group)};
-  stage_begin(HTTM_T_SELECT, st);
-  CHECK_LAUNCH(launch_select(g, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
-                             at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), cq, ck, st));
-  stage_end(HTTM_T_SELECT, st);
-
   const int64_t hn = (int64_t)g.heads * g.N;
   // atomic targets of this layer: key norms, exact-path count, outlier scratch, outlier counts
   CHECK_LAUNCH(launch_zero_init(at<float>(ws, L.kmax), g.heads, at<int>(ws, L.fb), at<uint32_t>(ws, L.radix),
                                 (int)outlier_scratch_words(hn), at<int32_t>(ws, L.ocnt),
                                 (int64_t)g.heads * g.nslots[kQ], st));
-  // K/V merge on the side stream, concurrent with the query path below
+
+  // key branch on the library stream: matching, selection and merge of K / V
   CHECK_LAUNCH(hipEventRecord(side->fork, st));
   CHECK_LAUNCH(hipStreamWaitEvent(side->st, side->fork, 0));
   stage_begin(HTTM_T_MERGE_KV, side->st);
+  CHECK_LAUNCH(launch_sim(g, dt, q, k, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
+                          at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), 2, side->st));
+  CHECK_LAUNCH(launch_select(g, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
+                             at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), cq, ck, 2, side->st));
   CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
                                ck.members, ck.off,
                                at<void>(ws, L.kt), at<void>(ws, L.vt), at<float>(ws, L.kmax), side->st));
   stage_end(HTTM_T_MERGE_KV, side->st);
   CHECK_LAUNCH(hipEventRecord(side->join, side->st));
+
+  // query branch on the caller's stream
+  stage_begin(HTTM_T_SIM, st);
+  CHECK_LAUNCH(launch_sim(g, dt, q, k, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
+                          at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), 1, st));
+  stage_end(HTTM_T_SIM, st);
+  stage_begin(HTTM_T_SELECT, st);
+  CHECK_LAUNCH(launch_select(g, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
+                             at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), cq, ck, 1, st));
+  stage_end(HTTM_T_SELECT, st);
 
   stage_begin(HTTM_T_MERGE_Q, st);
   CHECK_LAUNCH(launch_merge_q(dt, g.heads, g.N, g.nslots[kQ], q, cq.members, cq.off,

@@ -36,6 +36,7 @@ static_assert((1 << kGroupBits) >= kMaxGroups, "group id bits");
 
 struct SelArgs {
   Geo g;
+  int st0;  // first stream handled by this launch
   const int32_t* match[2];
   const float* score[2];
   Csr csr[2];
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void block_select(SelArgs a) {
   __shared__ uint32_t sRes[2];
   const Geo& g = a.g;
   const int per_head = g.nblocks + 1;
-  const int st = blockIdx.x / (g.heads * per_head);
+  const int st = a.st0 + blockIdx.x / (g.heads * per_head);
   const int rem_ = blockIdx.x % (g.heads * per_head);
   const int head = rem_ / per_head;
   const int b = rem_ % per_head;
@@ -265,17 +266,20 @@ __global__ __launch_bounds__(kThreads) void block_select(SelArgs a) {
 }  // namespace
 
 hipError_t launch_select(const Geo& g, const int32_t* match_q, const float* score_q,
-                         const int32_t* match_k, const float* score_k, Csr q, Csr k,
+                         const int32_t* match_k, const float* score_k, Csr q, Csr k, int streams,
                          hipStream_t stream) {
+  if ((streams & 3) == 0) return hipSuccess;
   SelArgs a;
   a.g = g;
+  a.st0 = (streams & 1) ? 0 : 1;
+  const int nst = (streams & 1) + ((streams >> 1) & 1);
   a.match[0] = match_q;
   a.match[1] = match_k;
   a.score[0] = score_q;
   a.score[1] = score_k;
   a.csr[0] = q;
   a.csr[1] = k;
-  const int grid = 2 * g.heads * (g.nblocks + 1);
+  const int grid = nst * g.heads * (g.nblocks + 1);
   hipLaunchKernelGGL(block_select, dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -310,7 +310,7 @@ __global__ __launch_bounds__(256) void sim_argmax_f32(SimArgs a) {
 }  // namespace
 
 hipError_t launch_sim(const Geo& g, int dtype, const void* q, const void* k, int32_t* match_q,
-                      float* score_q, int32_t* match_k, float* score_k, hipStream_t stream) {
+                      float* score_q, int32_t* match_k, float* score_k, int streams, hipStream_t stream) {
   SimArgs a;
   a.g = g;
   a.x[0] = q;
@@ -326,9 +326,10 @@ hipError_t launch_sim(const Geo& g, int dtype, const void* q, const void* k, int
       const BlockInfo bi = block_info(g, b, st);
       mx = bi.ns > mx ? bi.ns : mx;
     }
-    a.chunks[st] = mx > 0 ? ceil_div(mx, kSrcPerWg) : 1;
+    a.chunks[st] = ((streams >> st) & 1) ? (mx > 0 ? ceil_div(mx, kSrcPerWg) : 1) : 0;
     a.wgs[st] = g.heads * g.nblocks * a.chunks[st];
   }
+  if (a.chunks[0] + a.chunks[1] == 0) return hipSuccess;
   a.total = a.wgs[0] + a.wgs[1];
   // 8 XCD slices of ceil(HB/8) (head, block) pairs at most
   const int hb = g.heads * g.nblocks;

@@ -18,11 +18,12 @@ struct Csr {
   int32_t* group;
 };
 
+// streams: bit 0 = the query stream, bit 1 = the key stream (both: 3).
 hipError_t launch_sim(const Geo& g, int dtype, const void* q, const void* k, int32_t* match_q,
-                      float* score_q, int32_t* match_k, float* score_k, hipStream_t stream);
+                      float* score_q, int32_t* match_k, float* score_k, int streams, hipStream_t stream);
 
 hipError_t launch_select(const Geo& g, const int32_t* match_q, const float* score_q,
-                         const int32_t* match_k, const float* score_k, Csr q, Csr k,
+                         const int32_t* match_k, const float* score_k, Csr q, Csr k, int streams,
                          hipStream_t stream);
 
 // Means of K and V over the key partition: kt [h][lk_pad][64] (times kscale),
