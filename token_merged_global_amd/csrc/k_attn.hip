@@ -484,7 +484,11 @@ __global__ __launch_bounds__(kNW * 64) void attn_exact(AttnArgs a) {
 }
 
 // Combine the key-split partials of every packed row (split order fixed):
-// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
+// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s over the
+// splits with l_s > 0 (an empty key range carries no weight).  Every load of
+// a row (up to kMaxSplit row sums, references and partial rows) is issued
+// before the first use.
+constexpr int kMaxSplit = 4;
 __global__ __launch_bounds__(256) void attn_finalize(AttnArgs a) {
   __shared__ int sTot;
   if (threadIdx.x == 0) {
@@ -496,27 +500,40 @@ __global__ __launch_bounds__(256) void attn_finalize(AttnArgs a) {
   const int64_t R = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
   const int part = threadIdx.x & 7;
   if (R >= sTot) return;
-  // splits with an empty key range (or an all-zero sum) carry no weight
-  float M = -INFINITY;
-  for (int s = 0; s < a.split; ++s) {
-    const size_t pr = (size_t)s * a.q_capacity + R;
-    if (a.lpart[pr] > 0.f) M = fmaxf(M, a.mpart[pr]);
-  }
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, l = 0.f;
-  for (int s = 0; s < a.split; ++s) {
-    const size_t pr = (size_t)s * a.q_capacity + R;
-    if (!(a.lpart[pr] > 0.f)) continue;
-    const float f = __builtin_amdgcn_exp2f(a.mpart[pr] - M);
-    l = fmaf(f, a.lpart[pr], l);
-    const f32x4* src = reinterpret_cast<const f32x4*>(a.opart + pr * kD + part * 8);
-    const f32x4 x0 = src[0], x1 = src[1];
+  float l[kMaxSplit], m[kMaxSplit];
+  f32x4 x0[kMaxSplit], x1[kMaxSplit];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[e] = fmaf(f, x0[e], acc[e]);
-      acc[4 + e] = fmaf(f, x1[e], acc[4 + e]);
+  for (int s = 0; s < kMaxSplit; ++s) {
+    if (s < a.split) {
+      const size_t pr = (size_t)s * a.q_capacity + R;
+      l[s] = a.lpart[pr];
+      m[s] = a.mpart[pr];
+      const f32x4* src = reinterpret_cast<const f32x4*>(a.opart + pr * kD + part * 8);
+      x0[s] = src[0];
+      x1[s] = src[1];
+    } else {
+      l[s] = 0.f;
+      m[s] = 0.f;
+      x0[s] = x1[s] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
-  const float inv = 1.0f / l;
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s)
+    if (l[s] > 0.f) M = fmaxf(M, m[s]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, lt = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) {
+    if (!(l[s] > 0.f)) continue;
+    const float f = __builtin_amdgcn_exp2f(m[s] - M);
+    lt = fmaf(f, l[s], lt);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] = fmaf(f, x0[s][e], acc[e]);
+      acc[4 + e] = fmaf(f, x1[s][e], acc[4 + e]);
+    }
+  }
+  const float inv = 1.0f / lt;
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] *= inv;
   Row8<uint16_t>::store(reinterpret_cast<uint16_t*>(a.o) + R * kD + part * 8, acc);
@@ -574,6 +591,7 @@ __global__ __launch_bounds__(kRowsF32) void attn_f32(AttnArgs a) {
 
 int attention_rows_per_unit() { return kRows; }
 
+static_assert(kMaxSplit >= 4, "attention_split returns at most kMaxSplit");
 int attention_split(int64_t q_capacity, int heads) {
   // Four key splits: at 30 frames they fill the GPU (540 units of 256 rows
   // for 512 resident workgroups), and at 100-500 frames four shorter key
