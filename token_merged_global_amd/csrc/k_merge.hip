@@ -316,34 +316,54 @@ __device__ int block_exclusive_scan(int v, int* sh /* >= 16 */, int& total) {
 // Restore, part 1 (one workgroup per head): each initial query group g with
 // c members of which o are outliers yields (c > o) + o final slots; an
 // exclusive scan gives every group its first final slot; the head's final
-// length goes to lenq and closes the final offsets with N.
+// length goes to lenq and closes the final offsets with N.  Groups go through
+// LDS in chunks of 4096 so that global reads and writes are coalesced and
+// every thread scans 4 consecutive groups.
+constexpr int kScanPer = 4;
+constexpr int kScanChunk = 1024 * kScanPer;
 __global__ __launch_bounds__(1024) void restore_scan(int N, int gq, const int32_t* __restrict__ off,
                                                      const int32_t* __restrict__ ocnt,
                                                      int32_t* __restrict__ base,
                                                      int32_t* __restrict__ lenq,
                                                      int32_t* __restrict__ foff) {
   __shared__ int sh[17];
-  const int head = blockIdx.x;
+  __shared__ int sv[kScanChunk];
+  const int head = blockIdx.x, tid = threadIdx.x;
   const int32_t* of = off + (size_t)head * (gq + 1);
   const int32_t* oc = ocnt + (size_t)head * gq;
   int32_t* bs = base + (size_t)head * gq;
-  const int per = ceil_div(gq, 1024);
-  const int gb = threadIdx.x * per, ge = min(gq, gb + per);
-  int local = 0;
-  for (int g = gb; g < ge; ++g) {
-    const int c = of[g + 1] - of[g], o = oc[g];
-    local += (c > o ? 1 : 0) + o;
+  int carry = 0;
+  for (int c0 = 0; c0 < gq; c0 += kScanChunk) {
+    const int n = min(kScanChunk, gq - c0);
+    for (int i = tid; i < n; i += 1024) {
+      const int c = of[c0 + i + 1] - of[c0 + i], o = oc[c0 + i];
+      sv[i] = (c > o ? 1 : 0) + o;
+    }
+    __syncthreads();
+    int v[kScanPer], local = 0;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      const int i = tid * kScanPer + j;
+      v[j] = i < n ? sv[i] : 0;
+      local += v[j];
+    }
+    int total;
+    int acc = carry + block_exclusive_scan(local, sh, total);
+    // every thread read its values before the scan's first barrier, so sv can be overwritten
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      const int i = tid * kScanPer + j;
+      if (i < n) sv[i] = acc;
+      acc += v[j];
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += 1024) bs[c0 + i] = sv[i];
+    carry += total;
+    __syncthreads();
   }
-  int total;
-  int acc = block_exclusive_scan(local, sh, total);
-  for (int g = gb; g < ge; ++g) {
-    const int c = of[g + 1] - of[g], o = oc[g];
-    bs[g] = acc;
-    acc += (c > o ? 1 : 0) + o;
-  }
-  if (threadIdx.x == 0) {
-    lenq[head] = total;
-    foff[(size_t)head * (N + 1) + total] = N;
+  if (tid == 0) {
+    lenq[head] = carry;
+    foff[(size_t)head * (N + 1) + carry] = N;
   }
 }
 

@@ -66,27 +66,41 @@ __global__ void fill_bytes(uint8_t* p, int64_t n, uint8_t v) {
   if (i < n) p[i] = v;
 }
 
+// Exclusive prefix sum over the workgroup's threads (thread order), and the
+// workgroup total; wsum holds one word per wave.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* wsum, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t inc = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(inc, d);
+    if (lane >= d) inc += y;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    const uint32_t t = wsum[w];
+    before += w < wave ? t : 0u;
+    total += t;
+  }
+  __syncthreads();  // wsum may be reused
+  return before + inc - x;
+}
+
 // Find bin b with above(b) < k <= above(b) + hist[b], above(b) = sum of bins > b.
 // Writes b and k - above(b) to out[0], out[1].  nb = 2048 or 1024.
-__device__ void find_bin(const uint32_t* hist, int nb, uint32_t k, uint32_t* part, uint32_t* out) {
+__device__ void find_bin(const uint32_t* hist, int nb, uint32_t k, uint32_t* wsum, uint32_t* out) {
   const int per = nb / kThreads;
   const int t = threadIdx.x;
   // thread t owns bins [nb - (t+1)*per, nb - t*per), i.e. thread 0 the top bins
   const int hi = nb - t * per, lo = hi - per;
   uint32_t s = 0;
   for (int b = lo; b < hi; ++b) s += hist[b];
-  part[t] = s;
-  __syncthreads();
-  if (t == 0) {
-    uint32_t acc = 0;
-    for (int i = 0; i < kThreads; ++i) {
-      const uint32_t x = part[i];
-      part[i] = acc;  // count strictly above thread i's bins
-      acc += x;
-    }
-  }
-  __syncthreads();
-  const uint32_t above0 = part[t];
+  uint32_t total;
+  const uint32_t above0 = block_excl_scan(s, wsum, total);  // count strictly above thread t's bins
   if (above0 < k && above0 + s >= k) {
     uint32_t above = above0;
     for (int b = hi - 1; b >= lo; --b) {
@@ -123,7 +137,7 @@ template <int PASS>
 __global__ __launch_bounds__(kThreads) void radix_hist(const float* __restrict__ delta, int64_t total,
                                                        uint32_t k_o, uint32_t* scratch) {
   __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t part[kThreads];
+  __shared__ uint32_t part[kThreads / 64];
   __shared__ uint32_t res[4];
   Scratch s = scratch_of(scratch);
   uint32_t prefix = 0;
@@ -188,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void radix_mark(const float* __restrict__
                                                        uint32_t k_o, uint32_t* scratch,
                                                        uint8_t* __restrict__ mask) {
   __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t part[kThreads];
+  __shared__ uint32_t part[kThreads / 64];
   __shared__ uint32_t res[4];
   __shared__ uint32_t cnt;
   Scratch s = scratch_of(scratch);
@@ -232,22 +246,15 @@ __global__ __launch_bounds__(kThreads) void radix_mark(const float* __restrict__
 // Values equal to T, in flat-index order, take the remaining budget.
 __global__ __launch_bounds__(kThreads) void radix_ties(const float* __restrict__ delta, int64_t total,
                                                        uint32_t* scratch, uint8_t* __restrict__ mask) {
-  __shared__ uint32_t part[kThreads];
-  __shared__ uint32_t before;
+  __shared__ uint32_t part[kThreads / 64];
   Scratch s = scratch_of(scratch);
   if (s.ties[blockIdx.x] == 0) return;
   const uint32_t T = s.sel[0], need = s.sel[2];
   // ties in earlier chunks
   uint32_t acc = 0;
   for (int c = threadIdx.x; c < (int)blockIdx.x; c += kThreads) acc += s.ties[c];
-  part[threadIdx.x] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t t = 0;
-    for (int i = 0; i < kThreads; ++i) t += part[i];
-    before = t;
-  }
-  __syncthreads();
+  uint32_t before;
+  (void)block_excl_scan(acc, part, before);
   if (before >= need) return;
   uint32_t u[kPerThread];
   const int64_t i0 = (int64_t)blockIdx.x * kChunk + (int64_t)threadIdx.x * kPerThread;
@@ -255,19 +262,8 @@ __global__ __launch_bounds__(kThreads) void radix_ties(const float* __restrict__
   uint32_t eq = 0;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) eq += (u[e] == T && u[e] != 0xFFFFFFFFu) ? 1u : 0u;
-  __syncthreads();
-  part[threadIdx.x] = eq;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t a = before;
-    for (int i = 0; i < kThreads; ++i) {
-      const uint32_t x = part[i];
-      part[i] = a;
-      a += x;
-    }
-  }
-  __syncthreads();
-  uint32_t rank = part[threadIdx.x];
+  uint32_t chunk_total;
+  uint32_t rank = before + block_excl_scan(eq, part, chunk_total);
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     if (u[e] == T && u[e] != 0xFFFFFFFFu) {
