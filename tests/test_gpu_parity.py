@@ -78,6 +78,24 @@ def test_vggt30_layer(seed):
     assert (np.diff(cu) <= plan.info["q_groups"] + plan.info["n_outliers"]).all()
 
 
+def test_xcd_tail_tiles_full_outputs():
+    """A layer whose 256-row query tiles leave partly filled last rounds on the
+    XCDs: tail tiles run with twice the key splits and a separate partial-row
+    region; every output row is checked against the oracle."""
+    w = small_bf16(frames=8, heads=16)
+    x = gen.layer_inputs(w)
+    p = O.Params.from_workload(w)
+    plan, ws, dev, out, gpu = run_layer(w, x)
+    tiles = int(sum(-(-int(n) // 256) for n in np.diff(gpu["cu_q"])))
+    shares = [(i + 1) * tiles // 8 - i * tiles // 8 for i in range(8)]
+    _say(f"[xcd tail] tiles={tiles} per-XCD={shares}")
+    # 16 tiles per full round of an XCD on gfx950 (2 workgroups x 32 CUs, 4 splits)
+    assert any(n > 16 and n % 16 for n in shares)
+    rep = staged.check_layer(x["q"], x["k"], x["v"], p, gpu, out, rel_tol=BF16_REL)
+    _say("  ", rep.as_dict())
+    assert rep.delta_nonexact == 0
+
+
 def test_ratio_zero_is_exact_attention():
     w = small_bf16(frames=4, heads=2, q_ratio=0.0, kv_ratio=0.0)
     x = gen.layer_inputs(w)

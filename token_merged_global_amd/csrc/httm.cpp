@@ -98,6 +98,8 @@ struct httm_plan {
   size_t dense_ws;
   size_t dense_vt_bytes, dense_kc_bytes;
   int32_t attn_split;
+  AttnTail attn_tail;
+  int64_t attn_part_rows;  // rows of each key-split partial buffer
   std::vector<httm_block> blocks;
 };
 
@@ -216,11 +218,25 @@ httm_status build(const httm_params& p, httm_plan* pl) {
   pl->scale = p.softmax_scale > 0.0f ? p.softmax_scale : 1.0f / std::sqrt((float)kD);
   pl->esize = p.dtype == HTTM_BF16 ? 2 : 4;
   pl->attn_split = p.dtype == HTTM_BF16 ? attention_split(pl->q_cap, p.heads) : 1;
+  pl->attn_tail = attention_tail(pl->attn_split);
   {
-    const int64_t rows = attention_rows_per_unit();
-    const int64_t dense_units = (int64_t)p.heads * ((N + rows - 1) / rows);
-    const int64_t layer_units = ((pl->q_cap + rows - 1) / rows + p.heads) * pl->attn_split;
-    pl->attn_units = layer_units > dense_units ? layer_units : dense_units;
+    // exact-path queue capacity: workgroups of the layer's or the unmerged
+    // baseline's attention launch, whichever is larger
+    AttnShape s{};
+    s.heads = p.heads;
+    s.q_capacity = pl->q_cap;
+    s.split = pl->attn_split;
+    s.tail_split = pl->attn_tail.tail_split;
+    s.per_round = pl->attn_tail.per_round;
+    s.tail_rows = pl->attn_tail.tail_rows;
+    const int64_t layer_wgs = attention_workgroups(p.dtype, s);
+    pl->attn_part_rows = pl->attn_split > 1 ? attention_partial_rows(s) : 0;
+    AttnShape d{};
+    d.heads = p.heads;
+    d.q_capacity = (int64_t)p.heads * N;
+    d.split = 1;
+    const int64_t dense_wgs = attention_workgroups(p.dtype, d);
+    pl->attn_units = layer_wgs > dense_wgs ? layer_wgs : dense_wgs;
   }
 
   const size_t h = (size_t)p.heads, n = (size_t)N, E = pl->esize;
@@ -261,9 +277,9 @@ httm_status build(const httm_params& p, httm_plan* pl) {
     Lw.kmax = b.take(4 * h);
     Lw.fb = b.take(4 * (1 + (size_t)pl->attn_units));  // exact-path queue: count, then unit ids
     if (pl->attn_split > 1) {
-      Lw.opart = b.take(4 * (size_t)pl->attn_split * pl->q_cap * kD);
-      Lw.lpart = b.take(4 * (size_t)pl->attn_split * pl->q_cap);
-      Lw.mpart = b.take(4 * (size_t)pl->attn_split * pl->q_cap);
+      Lw.opart = b.take(4 * (size_t)pl->attn_part_rows * kD);
+      Lw.lpart = b.take(4 * (size_t)pl->attn_part_rows);
+      Lw.mpart = b.take(4 * (size_t)pl->attn_part_rows);
     }
     Lw.index = b.take(pl->I.total);
     Lw.total = b.cur;
@@ -349,7 +365,7 @@ httm_status attend_unmerge(const httm_plan* pl, void* ws, char* idx, const void*
                            void* out, hipStream_t st) {
   const Geo& g = pl->g;
   const int dt = pl->p.dtype;
-  AttnShape s;
+  AttnShape s{};
   s.heads = g.heads;
   s.lk = g.nslots[kK];
   s.k_rows = pl->lk_pad;
@@ -358,6 +374,9 @@ httm_status attend_unmerge(const httm_plan* pl, void* ws, char* idx, const void*
   s.q_capacity = pl->q_cap;
   s.scale = pl->scale;
   s.split = pl->attn_split;
+  s.tail_split = pl->attn_tail.tail_split;
+  s.per_round = pl->attn_tail.per_round;
+  s.tail_rows = pl->attn_tail.tail_rows;
   s.opart = pl->attn_split > 1 ? at<float>(ws, pl->L.opart) : nullptr;
   s.lpart = pl->attn_split > 1 ? at<float>(ws, pl->L.lpart) : nullptr;
   s.mpart = pl->attn_split > 1 ? at<float>(ws, pl->L.mpart) : nullptr;
@@ -611,6 +630,9 @@ httm_status httm_attention_dense(const httm_plan* pl, void* ws, size_t ws_bytes,
   a.q_capacity = (int64_t)g.heads * g.N;
   a.scale = pl->scale;
   a.split = 1;
+  a.tail_split = 1;
+  a.per_round = 0;
+  a.tail_rows = 0;
   a.opart = a.lpart = a.mpart = nullptr;
   a.kmax = kmax;
   a.fb_count = fb;

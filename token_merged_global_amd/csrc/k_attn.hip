@@ -30,10 +30,17 @@
 // 16-byte LDS read.  The row sum adds the bf16-rounded probabilities that the
 // P V product uses, on the MFMA pipe (a constant all-ones operand row).
 //
-// Key split.  When the query tiles alone do not fill the GPU (small layers),
-// the keys are split in S contiguous ranges; each unit writes its fp32
-// partial O, row sum and reference, and a finalize kernel combines them in
-// split order (deterministic).  With S = 1 the unit writes normalized rows.
+// Key split.  The keys of every query tile are split in S contiguous ranges;
+// each range writes its fp32 partial O, row sum and reference, and a
+// finalize kernel combines them in split order (deterministic).  With S = 1
+// the unit writes normalized rows.
+//
+// Schedule.  Query tiles are dealt to the 8 XCDs in contiguous ranges (the
+// hardware hands workgroup ids to the XCDs round-robin); each XCD runs its
+// tiles split-major, so the workgroups resident at one time sweep the same
+// key range.  An XCD whose S-split workgroups would end in a partly filled
+// round gives its last (tiles mod tiles-per-round) tiles 2S shorter splits:
+// the final round then holds half-length workgroups.
 #include "common.h"
 #include "kernels.h"
 
@@ -62,7 +69,10 @@ struct AttnArgs {
   const int32_t* lenq;
   int heads, lk, k_rows, vt_pitch, lq_uniform;
   int split;
+  int tail_split;          // splits of an XCD's tail tiles (== split: no tail)
+  int per_round;           // query tiles per full round of one XCD (split-S workgroups)
   int64_t q_capacity;
+  int64_t tail_rows;       // partial rows reserved for splits >= split of tail tiles
   int total_wg;
 };
 
@@ -80,11 +90,6 @@ __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::
 // rows 8(i/4) + 4p + i%4 of a 32-key chunk: swzK does the same for them.
 __device__ __forceinline__ int swzV(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int swzK(int row) { return ((row >> 1) & 1) | ((row >> 2) & 6); }
-
-__device__ __forceinline__ int xcd_logical(int bid, int total) {
-  const int per = (total + 7) / 8;
-  return (bid % 8) * per + bid / 8;
-}
 
 // Sums over lanes {l, l^32} and {l, l^16} with VALU lane swaps.
 __device__ __forceinline__ float sum_xor32(float x) {
@@ -111,7 +116,82 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
 
 struct Unit {
   int head, cu, L, tile, split;
+  int nsplit;  // key splits of this query tile
+  int tord;    // slot among the tail tiles (-1: regular tile)
 };
+
+// Tail tiles per XCD at most (partial rows are reserved for this many).
+constexpr int kMaxTailTiles = 16;
+
+// The XCD share of U query tiles: tiles [u0, u0 + n), the first nr regular
+// (split splits), the rest tail tiles (tail_split splits).
+struct XcdShare {
+  int u0, n, nr;
+};
+__device__ __forceinline__ XcdShare xcd_share(const AttnArgs& a, int U, int x) {
+  XcdShare r;
+  r.u0 = (int)((int64_t)x * U / 8);
+  r.n = (int)((int64_t)(x + 1) * U / 8) - r.u0;
+  const int t = a.per_round > 0 ? r.n % a.per_round : 0;
+  r.nr = r.n - t;
+  return r;
+}
+
+// Query tile ug (over all heads, head-major) -> head, first packed row of
+// the head, head length, tile inside the head.
+__device__ __forceinline__ void tile_of(const AttnArgs& a, int ug, Unit& o) {
+  int acc = 0;
+  o.cu = 0;
+  for (int h = 0; h < a.heads; ++h) {
+    const int len = a.lenq ? a.lenq[h] : a.lq_uniform;
+    const int nt = ceil_div(len, kRows);
+    if (ug < acc + nt) {
+      o.head = h;
+      o.L = len;
+      o.tile = ug - acc;
+      return;
+    }
+    acc += nt;
+    o.cu += len;
+  }
+}
+
+__device__ __forceinline__ int total_tiles(const AttnArgs& a) {
+  int U = 0;
+  for (int h = 0; h < a.heads; ++h) U += ceil_div(a.lenq ? a.lenq[h] : a.lq_uniform, kRows);
+  return U;
+}
+
+// Workgroup id -> unit (see Schedule above); false for workgroups past the work.
+__device__ __forceinline__ bool schedule(const AttnArgs& a, int bid, Unit& o) {
+  const int U = total_tiles(a);
+  const int x = bid & 7, j = bid >> 3;
+  const XcdShare sh = xcd_share(a, U, x);
+  int ug;
+  if (j < a.split * sh.nr) {
+    o.split = j / sh.nr;
+    ug = sh.u0 + j % sh.nr;
+    o.nsplit = a.split;
+    o.tord = -1;
+  } else {
+    const int t = sh.n - sh.nr, jt = j - a.split * sh.nr;
+    if (jt >= a.tail_split * t) return false;
+    o.split = jt / t;
+    o.tord = x * kMaxTailTiles + jt % t;
+    ug = sh.u0 + sh.nr + jt % t;
+    o.nsplit = a.tail_split;
+  }
+  tile_of(a, ug, o);
+  return true;
+}
+
+// Row of the partial buffers for split s of packed row `row` (tile-relative
+// row r) of a unit: splits below `split` are [split][q_capacity]; the extra
+// splits of tail tiles follow as [tail_split - split][tail_rows].
+__device__ __forceinline__ size_t part_row(const AttnArgs& a, int s, size_t row, int tord, int r) {
+  if (s < a.split) return (size_t)s * a.q_capacity + row;
+  return (size_t)a.split * a.q_capacity + (size_t)(s - a.split) * a.tail_rows + (size_t)tord * kRows + r;
+}
 
 // Unit u -> (head, first packed row of the head, head length, query tile,
 // key split); units of one head are ordered split-major so that concurrent
@@ -163,8 +243,8 @@ __device__ __forceinline__ void unit_setup(const AttnArgs& a, const Unit& u, int
     c.koff[rd] = (uint32_t)(row * kD + (pc ^ swzK(row)) * 8) * 2u;
     c.voff[rd] = (uint32_t)(row * a.vt_pitch + (pc ^ swzV(row)) * 8) * 2u;
   }
-  c.t0 = (int)((int64_t)u.split * c.ntiles_all / a.split);
-  c.t1 = (int)((int64_t)(u.split + 1) * c.ntiles_all / a.split);
+  c.t0 = (int)((int64_t)u.split * c.ntiles_all / u.nsplit);
+  c.t1 = (int)((int64_t)(u.split + 1) * c.ntiles_all / u.nsplit);
   c.qrow0 = u.tile * kRows + wave * kQT * 16 + l16;
   c.L = u.L;
 #pragma unroll
@@ -333,7 +413,7 @@ __device__ __forceinline__ void store_unit(const AttnArgs& a, const Unit& u, con
         *reinterpret_cast<u32x2*>(Op + dt * 16 + 4 * g) = w2;
       }
     } else {
-      const size_t prow = (size_t)u.split * a.q_capacity + row;
+      const size_t prow = part_row(a, u.split, row, u.tord, c.qrow0 - u.tile * kRows + qt * 16);
       float* Op = a.opart + prow * kD;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(Op + dt * 16 + 4 * g) = oacc[qt][dt];
@@ -349,9 +429,9 @@ __device__ __forceinline__ void store_unit(const AttnArgs& a, const Unit& u, con
 __global__ __launch_bounds__(kNW * 64) void attn_fast(AttnArgs a) {
   __shared__ u32x4 sK[2][kKeyTile * 8];
   __shared__ u32x4 sV[2][kD * 8];
-  const int w = xcd_logical(blockIdx.x, a.total_wg);
+  const int w = blockIdx.x;
   Unit u;
-  if (!locate(a, w, kRows, u)) return;
+  if (!schedule(a, w, u)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, l16 = lane & 15;
   UnitCtx c;
@@ -415,7 +495,7 @@ __global__ __launch_bounds__(kNW * 64) void attn_exact(AttnArgs a) {
   if ((int)blockIdx.x >= *a.fb_count) return;
   const int w = a.fb_list[blockIdx.x];
   Unit u;
-  if (!locate(a, w, kRows, u)) return;
+  if (!schedule(a, w, u)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, l16 = lane & 15;
   UnitCtx c;
@@ -485,27 +565,53 @@ __global__ __launch_bounds__(kNW * 64) void attn_exact(AttnArgs a) {
 
 // Combine the key-split partials of every packed row (split order fixed):
 // O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s over the
-// splits with l_s > 0 (an empty key range carries no weight).  Every load of
-// a row (up to kMaxSplit row sums, references and partial rows) is issued
-// before the first use.
-constexpr int kMaxSplit = 4;
+// splits with l_s > 0 (an empty key range carries no weight).  A row's split
+// count and partial slots follow from the schedule of its query tile.  Every
+// load of a row (row sums, references and partial rows of all its splits) is
+// issued before the first use.
+constexpr int kMaxSplit = 8;
 __global__ __launch_bounds__(256) void attn_finalize(AttnArgs a) {
-  __shared__ int sTot;
+  __shared__ int sCu[kMaxHeads + 1], sUt[kMaxHeads + 1];
+  __shared__ int sU0[8], sNr[8];
   if (threadIdx.x == 0) {
-    int t = 0;
-    for (int h = 0; h < a.heads; ++h) t += a.lenq ? a.lenq[h] : a.lq_uniform;
-    sTot = t;
+    int acc = 0, ut = 0;
+    for (int h = 0; h < a.heads; ++h) {
+      const int len = a.lenq ? a.lenq[h] : a.lq_uniform;
+      sCu[h] = acc;
+      sUt[h] = ut;
+      acc += len;
+      ut += ceil_div(len, kRows);
+    }
+    sCu[a.heads] = acc;
+    sUt[a.heads] = ut;
+  }
+  __syncthreads();
+  if (threadIdx.x < 8) {
+    const XcdShare sh = xcd_share(a, sUt[a.heads], threadIdx.x);
+    sU0[threadIdx.x] = sh.u0;
+    sNr[threadIdx.x] = sh.nr;
   }
   __syncthreads();
   const int64_t R = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
   const int part = threadIdx.x & 7;
-  if (R >= sTot) return;
+  if (R >= sCu[a.heads]) return;
+  int h = 0;
+  while (sCu[h + 1] <= R) ++h;
+  const int rin = (int)(R - sCu[h]), tile = rin / kRows;
+  const int ug = sUt[h] + tile;
+  int x = 7;
+  while (sU0[x] > ug) --x;  // the XCD whose tile range holds ug
+  int ns = a.split, tord = -1;
+  if (ug >= sU0[x] + sNr[x]) {
+    ns = a.tail_split;
+    tord = x * kMaxTailTiles + (ug - sU0[x] - sNr[x]);
+  }
   float l[kMaxSplit], m[kMaxSplit];
   f32x4 x0[kMaxSplit], x1[kMaxSplit];
 #pragma unroll
   for (int s = 0; s < kMaxSplit; ++s) {
-    if (s < a.split) {
-      const size_t pr = (size_t)s * a.q_capacity + R;
+    if (s < ns) {
+      const size_t pr = part_row(a, s, (size_t)R, tord, rin - tile * kRows);
       l[s] = a.lpart[pr];
       m[s] = a.mpart[pr];
       const f32x4* src = reinterpret_cast<const f32x4*>(a.opart + pr * kD + part * 8);
@@ -591,7 +697,7 @@ __global__ __launch_bounds__(kRowsF32) void attn_f32(AttnArgs a) {
 
 int attention_rows_per_unit() { return kRows; }
 
-static_assert(kMaxSplit >= 4, "attention_split returns at most kMaxSplit");
+static_assert(kMaxSplit >= 8, "attention_split and its tail splits stay within kMaxSplit");
 int attention_split(int64_t q_capacity, int heads) {
   // Four key splits: at 30 frames they fill the GPU (540 units of 256 rows
   // for 512 resident workgroups), and at 100-500 frames four shorter key
@@ -602,7 +708,43 @@ int attention_split(int64_t q_capacity, int heads) {
   return 4;
 }
 
+AttnTail attention_tail(int split) {
+  AttnTail t{split, 0, 0};
+  if (split <= 1) return t;
+  // resident workgroups of the fast kernel per XCD; the gfx950 values
+  // (2 per CU, 32 CUs per XCD) when no device can be queried
+  int occ = 0, cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, attn_fast, kNW * 64, 0) != hipSuccess || occ <= 0 ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    occ = 2;
+    cus = 256;
+  }
+  const int slots = occ * cus / 8;
+  if (cus % 8 || slots % split || slots / split - 1 > kMaxTailTiles) return t;
+  t.tail_split = 2 * split;
+  t.per_round = slots / split;
+  t.tail_rows = (int64_t)8 * kMaxTailTiles * kRows;
+  return t;
+}
 
+int64_t attention_workgroups(int dtype, const AttnShape& s) {
+  if (dtype != 1) return (s.q_capacity + kRowsF32 - 1) / kRowsF32 + s.heads;
+  const int64_t units = (s.q_capacity + kRows - 1) / kRows + s.heads;
+  const int64_t nmax = (units + 7) / 8;
+  int64_t per_xcd = s.split * nmax;
+  if (s.tail_split > s.split && s.per_round > 0) {
+    const int64_t t = nmax < s.per_round - 1 ? nmax : s.per_round - 1;
+    per_xcd += (int64_t)(s.tail_split - s.split) * t;
+  }
+  return 8 * per_xcd;
+}
+
+int64_t attention_partial_rows(const AttnShape& s) {
+  return (int64_t)s.split * s.q_capacity + (int64_t)(s.tail_split > s.split ? s.tail_split - s.split : 0) * s.tail_rows;
+}
 
 namespace {
 AttnArgs make_args(int dtype, const AttnShape& s, const void* q, const void* k, const void* vt,
@@ -625,11 +767,16 @@ AttnArgs make_args(int dtype, const AttnShape& s, const void* q, const void* k, 
   a.vt_pitch = s.vt_pitch;
   a.lq_uniform = s.lq_uniform;
   a.split = dtype == 1 ? s.split : 1;
+  const bool tail = dtype == 1 && a.split > 1 && s.tail_split > a.split && s.per_round > 0;
+  a.tail_split = tail ? s.tail_split : a.split;
+  a.per_round = tail ? s.per_round : 0;
+  a.tail_rows = tail ? s.tail_rows : 0;
   a.q_capacity = s.q_capacity;
-  if (dtype == 1)
-    a.total_wg = (int)(((s.q_capacity + kRows - 1) / kRows + s.heads) * a.split);
-  else
-    a.total_wg = (int)((s.q_capacity + kRowsF32 - 1) / kRowsF32 + s.heads);
+  AttnShape sh = s;
+  sh.split = a.split;
+  sh.tail_split = a.tail_split;
+  sh.per_round = a.per_round;
+  a.total_wg = (int)attention_workgroups(dtype, sh);
   return a;
 }
 }  // namespace
@@ -638,8 +785,7 @@ hipError_t launch_attention(int dtype, const AttnShape& s, const void* q, const 
                             const void* vt, const int32_t* lenq, void* o, hipStream_t stream) {
   const AttnArgs a = make_args(dtype, s, q, k, vt, lenq, o);
   if (dtype == 1) {
-    const int grid = ((a.total_wg + 7) / 8) * 8;
-    hipLaunchKernelGGL(attn_fast, dim3(grid), dim3(kNW * 64), 0, stream, a);
+    hipLaunchKernelGGL(attn_fast, dim3(a.total_wg), dim3(kNW * 64), 0, stream, a);
   } else {
     hipLaunchKernelGGL(attn_f32, dim3(a.total_wg), dim3(kRowsF32), 0, stream, a);
   }

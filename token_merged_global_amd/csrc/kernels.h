@@ -82,9 +82,12 @@ struct AttnShape {
   int64_t q_capacity;
   float scale;
   int split;               // key splits (bf16); partial buffers needed when > 1
-  float* opart;            // [split][q_capacity][64]
-  float* lpart;            // [split][q_capacity]
-  float* mpart;            // [split][q_capacity]
+  int tail_split;          // splits of each XCD's tail query tiles (<= split: none)
+  int per_round;           // query tiles per full round of one XCD (0: no tail splits)
+  int64_t tail_rows;       // partial rows reserved for the tail tiles' extra splits
+  float* opart;            // [attention_partial_rows][64]
+  float* lpart;            // [attention_partial_rows]
+  float* mpart;            // [attention_partial_rows]
   const float* kmax;       // [heads] max |k row|
   int* fb_count;           // [1] units queued for the exact kernel (zeroed by launch_zero_init)
   int* fb_list;            // [units]
@@ -92,6 +95,17 @@ struct AttnShape {
 // Key splits for a layer of q_capacity packed rows; rows per work unit.
 int attention_split(int64_t q_capacity, int heads);
 int attention_rows_per_unit();
+// Tail splitting for `split` key splits on the current device (falls back to
+// the gfx950 figures when no device answers): tail_split == split disables it.
+struct AttnTail {
+  int tail_split, per_round;
+  int64_t tail_rows;
+};
+AttnTail attention_tail(int split);
+// Workgroups of the main attention launch (also the capacity the exact-path
+// queue needs) and rows of each partial buffer, for a shape.
+int64_t attention_workgroups(int dtype, const AttnShape& s);
+int64_t attention_partial_rows(const AttnShape& s);
 // Zero, before a layer's producers run: kmax[heads] (atomic max target of the
 // K~ producer), the exact-path counter, and optionally the outlier radix
 // scratch (radix_words) and the per-group outlier counts (ocnt_words).
