@@ -73,4 +73,34 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Prefix sums over per-head lengths with one head per lane of the calling
+// wave (heads <= 64; every lane of the wave calls it with the same
+// arguments): one load per lane and shuffle scans instead of a serial walk.
+// Lane h gets its head's length and the rows and tiles (tiles of tile_rows
+// rows, 0: none) of heads 0..h-1 and 0..h; totals in every lane.
+struct HeadPrefix {
+  int len, rows_before, tiles_before, tiles_upto, rows_total, tiles_total;
+};
+__device__ __forceinline__ HeadPrefix head_prefix(const int32_t* lenq, int lq_uniform, int heads, int tile_rows) {
+  const int lane = threadIdx.x & 63;
+  HeadPrefix p;
+  p.len = lane < heads ? (lenq ? lenq[lane] : lq_uniform) : 0;
+  const int t = tile_rows > 0 ? ceil_div(p.len, tile_rows) : 0;
+  int r = p.len, u = t;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int r2 = __shfl_up(r, d), u2 = __shfl_up(u, d);
+    if (lane >= d) {
+      r += r2;
+      u += u2;
+    }
+  }
+  p.rows_before = r - p.len;
+  p.tiles_before = u - t;
+  p.tiles_upto = u;
+  p.rows_total = __shfl(r, 63);
+  p.tiles_total = __shfl(u, 63);
+  return p;
+}
+
 }  // namespace httm

@@ -137,34 +137,11 @@ __device__ __forceinline__ XcdShare xcd_share(const AttnArgs& a, int U, int x) {
   return r;
 }
 
-// Query tile ug (over all heads, head-major) -> head, first packed row of
-// the head, head length, tile inside the head.
-__device__ __forceinline__ void tile_of(const AttnArgs& a, int ug, Unit& o) {
-  int acc = 0;
-  o.cu = 0;
-  for (int h = 0; h < a.heads; ++h) {
-    const int len = a.lenq ? a.lenq[h] : a.lq_uniform;
-    const int nt = ceil_div(len, kRows);
-    if (ug < acc + nt) {
-      o.head = h;
-      o.L = len;
-      o.tile = ug - acc;
-      return;
-    }
-    acc += nt;
-    o.cu += len;
-  }
-}
-
-__device__ __forceinline__ int total_tiles(const AttnArgs& a) {
-  int U = 0;
-  for (int h = 0; h < a.heads; ++h) U += ceil_div(a.lenq ? a.lenq[h] : a.lq_uniform, kRows);
-  return U;
-}
-
-// Workgroup id -> unit (see Schedule above); false for workgroups past the work.
+// Workgroup id -> unit (see Schedule above); false for workgroups past the
+// work.  Every lane of the wave takes part (wave-wide scans over the heads).
 __device__ __forceinline__ bool schedule(const AttnArgs& a, int bid, Unit& o) {
-  const int U = total_tiles(a);
+  const HeadPrefix hp = head_prefix(a.lenq, a.lq_uniform, a.heads, kRows);
+  const int U = hp.tiles_total;
   const int x = bid & 7, j = bid >> 3;
   const XcdShare sh = xcd_share(a, U, x);
   int ug;
@@ -181,7 +158,13 @@ __device__ __forceinline__ bool schedule(const AttnArgs& a, int bid, Unit& o) {
     ug = sh.u0 + sh.nr + jt % t;
     o.nsplit = a.tail_split;
   }
-  tile_of(a, ug, o);
+  // the head holding tile ug: heads whose tiles all lie below ug come first
+  const int lane = threadIdx.x & 63;
+  const int h = __popcll(__ballot(lane < a.heads && hp.tiles_upto <= ug));
+  o.head = h;
+  o.L = __shfl(hp.len, h);
+  o.cu = __shfl(hp.rows_before, h);
+  o.tile = ug - __shfl(hp.tiles_before, h);
   return true;
 }
 
@@ -573,17 +556,16 @@ constexpr int kMaxSplit = 8;
 __global__ __launch_bounds__(256) void attn_finalize(AttnArgs a) {
   __shared__ int sCu[kMaxHeads + 1], sUt[kMaxHeads + 1];
   __shared__ int sU0[8], sNr[8];
-  if (threadIdx.x == 0) {
-    int acc = 0, ut = 0;
-    for (int h = 0; h < a.heads; ++h) {
-      const int len = a.lenq ? a.lenq[h] : a.lq_uniform;
-      sCu[h] = acc;
-      sUt[h] = ut;
-      acc += len;
-      ut += ceil_div(len, kRows);
+  if (threadIdx.x < 64) {
+    const HeadPrefix hp = head_prefix(a.lenq, a.lq_uniform, a.heads, kRows);
+    if ((int)threadIdx.x < a.heads) {
+      sCu[threadIdx.x] = hp.rows_before;
+      sUt[threadIdx.x] = hp.tiles_before;
     }
-    sCu[a.heads] = acc;
-    sUt[a.heads] = ut;
+    if (threadIdx.x == 0) {
+      sCu[a.heads] = hp.rows_total;
+      sUt[a.heads] = hp.tiles_total;
+    }
   }
   __syncthreads();
   if (threadIdx.x < 8) {

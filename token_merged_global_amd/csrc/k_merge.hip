@@ -367,11 +367,6 @@ __global__ __launch_bounds__(1024) void restore_scan(int N, int gq, const int32_
   }
 }
 
-__device__ __forceinline__ int prefix_len(const int32_t* lenq, int head) {
-  int cu = 0;
-  for (int h = 0; h < head; ++h) cu += lenq[h];
-  return cu;
-}
 
 // Restore, part 2: 8 lanes per initial query group.  The 8 lanes look at 8
 // members at a time: ballots over the group's lanes rank survivors and
@@ -397,11 +392,15 @@ __global__ __launch_bounds__(256) void restore_rows(int heads, int N, int gq, co
   const int tiles = ceil_div(gq, 32);
   const int head = blockIdx.x / tiles, tile = blockIdx.x % tiles;
   const int tid = threadIdx.x;
-  if (blockIdx.x == 0 && tid <= heads) cu_q[tid] = prefix_len(lenq, tid);
+  const HeadPrefix hp = head_prefix(lenq, 0, heads, 0);  // every wave, before any exit
+  if (blockIdx.x == 0 && tid < 64) {
+    if (tid < heads) cu_q[tid] = hp.rows_before;
+    if (tid == 0) cu_q[heads] = hp.rows_total;
+  }
+  const int cu = __shfl(hp.rows_before, head);
   const int g = tile * 32 + (tid >> 3), part = tid & 7;
   const int sub = (tid & 63) >> 3;
   if (g >= gq) return;  // whole 8-lane groups leave together
-  const int cu = prefix_len(lenq, head);
   const T* Q = q + (size_t)head * N * kD;
   const int32_t* mem = members + (size_t)head * N;
   const uint8_t* mk = mask + (size_t)head * N;
@@ -473,13 +472,10 @@ __global__ __launch_bounds__(256) void merge_q_cached(int heads, int N, const T*
                                                       const int32_t* __restrict__ lenq,
                                                       T* __restrict__ qt) {
   __shared__ int sCu[kMaxHeads + 1];
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int h = 0; h < heads; ++h) {
-      sCu[h] = acc;
-      acc += lenq[h];
-    }
-    sCu[heads] = acc;
+  if (threadIdx.x < 64) {
+    const HeadPrefix hp = head_prefix(lenq, 0, heads, 0);
+    if ((int)threadIdx.x < heads) sCu[threadIdx.x] = hp.rows_before;
+    if (threadIdx.x == 0) sCu[heads] = hp.rows_total;
   }
   __syncthreads();
   const int R = blockIdx.x * 32 + (threadIdx.x >> 3), part = threadIdx.x & 7;
