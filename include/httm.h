@@ -162,6 +162,27 @@ httm_status httm_layer_cached(const httm_plan* plan, void* ws, size_t ws_bytes,
                               const void* q, const void* k, const void* v, void* out,
                               void* stream);
 
+/* Move a filled index through host memory (LiteVGGT page, key design 3:
+ * the merge indices of one layer serve the following layers; exporting them
+ * lets a caller keep or ship them).  Both synchronise `stream`.
+ *
+ * httm_index_export copies httm_index_size() bytes of `index` (filled by
+ * httm_layer with this plan) into `host` (at least that many bytes).  The
+ * bytes start with a header naming the plan's parameters and geometry.
+ * HTTM_ERR_INDEX_MISMATCH if `index` was not filled with this plan.
+ *
+ * httm_index_import copies `host` (exactly httm_index_size() bytes, as
+ * exported by a plan with the same parameters) into index->dev and marks the
+ * index filled for this plan.  The header must match this plan and the
+ * contents must stay in range (offsets rising from 0 to N, token ids below N,
+ * packed rows inside their head), else HTTM_ERR_INDEX_MISMATCH and the index
+ * is left unfilled.  index->dev is caller-owned device memory of at least
+ * httm_index_size() bytes (HTTM_ERR_WORKSPACE otherwise). */
+httm_status httm_index_export(const httm_plan* plan, const httm_index* index, void* host, size_t bytes,
+                              void* stream);
+httm_status httm_index_import(const httm_plan* plan, const void* host, size_t bytes, httm_index* index,
+                              void* stream);
+
 /* Exact softmax(scale q k^T) v per head with nothing merged, on the same
  * attention kernel (the unmerged baseline).  Needs
  * httm_dense_workspace_size() bytes of workspace. */

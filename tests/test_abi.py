@@ -144,3 +144,25 @@ def test_layer_rejects_bad_buffers_before_any_launch():
     assert L.httm_debug_size(plan.handle, 99, ctypes.byref(n)) == 1
     assert L.httm_debug_size(plan.handle, 10, ctypes.byref(n)) == 0 and n.value == 16
     assert L.httm_debug_size(plan.handle, 11, ctypes.byref(n)) == 0 and n.value == 4
+
+
+def test_index_export_import_validation():
+    """Index export/import refuse foreign or malformed bytes before any copy
+    (status codes of include/httm.h; the fake device pointer is never used)."""
+    plan = H.Plan.from_workload(gen.WORKLOADS["tiny"])
+    L = H.lib()
+    n = plan.index_bytes
+    fake = H.Index(0, 0x1000, n, 0)
+    buf = np.zeros(n, dtype=np.uint8)
+    # an index this plan did not fill
+    assert L.httm_index_export(plan.handle, ctypes.byref(fake), buf.ctypes.data, n, None) == 4
+    # NULL arguments
+    assert L.httm_index_export(plan.handle, ctypes.byref(fake), None, n, None) == 1
+    assert L.httm_index_import(plan.handle, None, n, ctypes.byref(fake), None) == 1
+    # wrong size, then the right size with no valid header
+    assert L.httm_index_import(plan.handle, buf.ctypes.data, n - 4, ctypes.byref(fake), None) == 4
+    assert L.httm_index_import(plan.handle, buf.ctypes.data, n, ctypes.byref(fake), None) == 4
+    assert fake.valid == 0
+    # a device buffer smaller than the index
+    small = H.Index(0, 0x1000, n - 1, 0)
+    assert L.httm_index_import(plan.handle, buf.ctypes.data, n, ctypes.byref(small), None) == 3

@@ -224,3 +224,38 @@ def test_key_split_matches_single_pass():
     torch.cuda.synchronize()
     a, b = out.float().cpu().numpy(), out2.float().cpu().numpy()
     assert np.abs(a - b).max() <= BF16_REL * np.sqrt((a ** 2).mean())
+
+
+def test_index_export_import_round_trip():
+    """Cached indices through host memory (LiteVGGT page, key design 3): an
+    exported index, imported into a fresh buffer or by another plan with the
+    same parameters, drives bit-identical cached layers; bytes from other
+    parameters or with out-of-range contents are refused."""
+    w = small_bf16(frames=4, heads=3)
+    x = gen.layer_inputs(w)
+    plan = H.Plan.from_workload(w)
+    q, k, v = (to_dev(x[t], w.dtype) for t in "qkv")
+    ws = H.workspace(plan)
+    _, idx = H.layer(plan, q, k, v, ws=ws, keep_index=True)
+    host = H.index_export(plan, idx)
+    assert host.nbytes == plan.index_bytes
+    o1 = H.layer_cached(plan, idx, q, k, v, ws=ws).clone()
+    o2 = H.layer_cached(plan, H.index_import(plan, host), q, k, v, ws=ws).clone()
+    plan_b = H.Plan.from_workload(w)
+    o3 = H.layer_cached(plan_b, H.index_import(plan_b, host), q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+    # other parameters (same index size): header mismatch
+    plan_c = H.Plan.from_workload(w.with_(outlier_pct=5.0))
+    if plan_c.index_bytes == plan.index_bytes:
+        with pytest.raises(H.HttmError) as e:
+            H.index_import(plan_c, host)
+        assert e.value.status == 4
+    # a token id out of range after a valid header (the first member list
+    # starts at the first 256-byte boundary after the 64-byte header)
+    bad = host.copy()
+    bad.view(np.int32)[256 // 4] = w.n_tokens
+    with pytest.raises(H.HttmError) as e:
+        H.index_import(plan, bad)
+    assert e.value.status == 4

@@ -77,6 +77,10 @@ EXPORTS = {
     "httm_layer_cached": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Index),
                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                            ctypes.c_void_p], ctypes.c_int),
+    "httm_index_export": ([ctypes.c_void_p, ctypes.POINTER(Index), ctypes.c_void_p, ctypes.c_size_t,
+                           ctypes.c_void_p], ctypes.c_int),
+    "httm_index_import": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Index),
+                           ctypes.c_void_p], ctypes.c_int),
     "httm_attention_dense": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p],
                              ctypes.c_int),
@@ -245,6 +249,25 @@ def layer_cached(plan: Plan, index: CachedIndex, q, k, v, ws=None, out=None, str
                                    q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                    _stream_ptr(stream)))
     return out
+
+
+def index_export(plan: Plan, index: CachedIndex, stream=None):
+    """Host copy (numpy uint8) of an index filled by ``layer`` with this plan."""
+    import numpy as np
+    buf = np.empty(plan.index_bytes, dtype=np.uint8)
+    _check(lib().httm_index_export(plan.handle, ctypes.byref(index.c), buf.ctypes.data, buf.nbytes,
+                                   _stream_ptr(stream)))
+    return buf
+
+
+def index_import(plan: Plan, host, stream=None) -> CachedIndex:
+    """A device index holding ``host`` (bytes exported with a plan of the same parameters)."""
+    import numpy as np
+    buf = np.ascontiguousarray(np.frombuffer(memoryview(host), dtype=np.uint8))
+    index = CachedIndex(plan)
+    _check(lib().httm_index_import(plan.handle, buf.ctypes.data, buf.nbytes, ctypes.byref(index.c),
+                                   _stream_ptr(stream)))
+    return index
 
 
 def attention_dense(plan: Plan, q, k, v, ws=None, out=None, stream=None):

@@ -66,8 +66,27 @@ struct Layout {
 };
 
 struct IndexLayout {
-  Region k_members, k_off, fmembers, foff, slot, lenq, cu_q;
+  Region header, k_members, k_off, fmembers, foff, slot, lenq, cu_q;
   size_t total = 0;
+};
+
+constexpr uint32_t kIndexMagic = 0x58495448u;  // "HTIX"
+constexpr uint32_t kIndexVersion = 1;
+
+// FNV-1a, 64-bit, over little-endian words.
+struct Fnv {
+  uint64_t h = 0xcbf29ce484222325ull;
+  void add(uint64_t x) {
+    for (int i = 0; i < 8; ++i) {
+      h ^= (x >> (8 * i)) & 0xffu;
+      h *= 0x100000001b3ull;
+    }
+  }
+  void addd(double x) {
+    uint64_t u;
+    std::memcpy(&u, &x, 8);
+    add(u);
+  }
 };
 
 struct Builder {
@@ -98,6 +117,7 @@ struct httm_plan {
   size_t dense_ws;
   size_t dense_vt_bytes, dense_kc_bytes;
   int32_t attn_split;
+  IndexHeader index_header;  // identity written at the start of every index this plan fills
   AttnTail attn_tail;
   int64_t attn_part_rows;  // rows of each key-split partial buffer
   std::vector<httm_block> blocks;
@@ -244,6 +264,7 @@ httm_status build(const httm_params& p, httm_plan* pl) {
   {
     Builder b;
     IndexLayout& I = pl->I;
+    I.header = b.take(sizeof(IndexHeader));
     I.k_members = b.take(4 * h * n);
     I.k_off = b.take(4 * h * ((size_t)g.nslots[kK] + 1));
     I.fmembers = b.take(4 * h * n);
@@ -288,6 +309,39 @@ httm_status build(const httm_params& p, httm_plan* pl) {
   pl->dense_kc_bytes = align256(E * h * (size_t)ceil_div(g.N, 64) * 64 * kD);
   pl->dense_ws = pl->dense_vt_bytes + pl->dense_kc_bytes + pl->L.kmax.bytes + 256 + pl->L.fb.bytes;
   pl->id = ++g_plan_counter;
+  {
+    // what an index depends on: every parameter and the index geometry
+    Fnv f;
+    f.add((uint64_t)p.heads);
+    f.add((uint64_t)p.d_head);
+    f.add((uint64_t)p.frames);
+    f.add((uint64_t)p.grid_h);
+    f.add((uint64_t)p.grid_w);
+    f.add((uint64_t)p.n_special);
+    f.add((uint64_t)p.n_s);
+    f.add((uint64_t)p.n_t);
+    f.addd(p.q_ratio);
+    f.addd(p.kv_ratio);
+    f.addd(p.outlier_pct);
+    f.add((uint64_t)g.s[kQ]);
+    f.add((uint64_t)g.s[kK]);
+    f.add((uint64_t)p.block_order);
+    f.add((uint64_t)p.dtype);
+    f.add((uint64_t)g.N);
+    f.add((uint64_t)g.nslots[kQ]);
+    f.add((uint64_t)g.nslots[kK]);
+    f.add((uint64_t)pl->I.total);
+    IndexHeader& H = pl->index_header;
+    std::memset(&H, 0, sizeof(H));
+    H.w[0] = kIndexMagic;
+    H.w[1] = kIndexVersion;
+    H.w[2] = (uint32_t)f.h;
+    H.w[3] = (uint32_t)(f.h >> 32);
+    H.w[4] = (uint32_t)pl->I.total;
+    H.w[5] = (uint32_t)((uint64_t)pl->I.total >> 32);
+    H.w[6] = (uint32_t)p.heads;
+    H.w[7] = (uint32_t)g.N;
+  }
   return HTTM_OK;
 }
 
@@ -401,6 +455,38 @@ httm_status attend_unmerge(const httm_plan* pl, void* ws, char* idx, const void*
 
 }  // namespace
 
+// An imported index must keep every kernel that reads it in bounds: offsets
+// rise from 0 to N, member ids and slots stay inside their head, and the
+// per-head lengths fit the packed capacity.
+namespace {
+bool index_payload_ok(const httm_plan* pl, const char* buf) {
+  const Geo& g = pl->g;
+  const IndexLayout& I = pl->I;
+  const int64_t N = g.N, H = g.heads, lk = g.nslots[kK];
+  auto arr = [&](const Region& r) { return reinterpret_cast<const int32_t*>(buf + r.off); };
+  const int32_t *km = arr(I.k_members), *ko = arr(I.k_off), *fm = arr(I.fmembers), *fo = arr(I.foff);
+  const int32_t *sl = arr(I.slot), *lq = arr(I.lenq), *cu = arr(I.cu_q);
+  if (cu[0] != 0) return false;
+  for (int64_t h = 0; h < H; ++h) {
+    const int64_t len = lq[h];
+    if (len < 1 || len > N || cu[h + 1] != cu[h] + len || cu[h + 1] > pl->q_cap) return false;
+    const int32_t* o = ko + h * (lk + 1);
+    if (o[0] != 0 || o[lk] != N) return false;
+    for (int64_t j = 0; j < lk; ++j)
+      if (o[j + 1] <= o[j]) return false;  // every merged key has a member
+    const int32_t* f = fo + h * (N + 1);
+    if (f[0] != 0 || f[len] != N) return false;
+    for (int64_t j = 0; j < len; ++j)
+      if (f[j + 1] <= f[j]) return false;  // every packed query row has a member
+    for (int64_t n = 0; n < N; ++n) {
+      const int32_t a = km[h * N + n], b = fm[h * N + n], c = sl[h * N + n];
+      if (a < 0 || a >= N || b < 0 || b >= N || c < cu[h] || c >= cu[h + 1]) return false;
+    }
+  }
+  return true;
+}
+}  // namespace
+
 extern "C" {
 
 const char* httm_status_string(httm_status s) {
@@ -469,6 +555,39 @@ httm_status httm_index_size(const httm_plan* pl, size_t* bytes) {
   return HTTM_OK;
 }
 
+httm_status httm_index_export(const httm_plan* pl, const httm_index* index, void* host, size_t bytes,
+                              void* stream) {
+  if (!pl || !index || !index->dev || !host) return fail(HTTM_ERR_INVALID_ARG, "NULL argument");
+  if (index->plan_id != pl->id || !index->valid)
+    return fail(HTTM_ERR_INDEX_MISMATCH, "index was not filled by httm_layer with this plan");
+  if (index->bytes < pl->I.total) return fail(HTTM_ERR_WORKSPACE, "index buffer smaller than httm_index_size()");
+  if (bytes < pl->I.total) return fail(HTTM_ERR_INVALID_ARG, "host buffer smaller than httm_index_size()");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(host, index->dev, pl->I.total, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return fail(HTTM_ERR_DEVICE, "index copy to host failed");
+  return HTTM_OK;
+}
+
+httm_status httm_index_import(const httm_plan* pl, const void* host, size_t bytes, httm_index* index,
+                              void* stream) {
+  if (!pl || !host || !index || !index->dev) return fail(HTTM_ERR_INVALID_ARG, "NULL argument");
+  if (index->bytes < pl->I.total) return fail(HTTM_ERR_WORKSPACE, "index buffer smaller than httm_index_size()");
+  if (bytes != pl->I.total) return fail(HTTM_ERR_INDEX_MISMATCH, "buffer size is not this plan's httm_index_size()");
+  const char* buf = reinterpret_cast<const char*>(host);
+  if (std::memcmp(buf + pl->I.header.off, &pl->index_header, sizeof(IndexHeader)) != 0)
+    return fail(HTTM_ERR_INDEX_MISMATCH, "index header does not match this plan");
+  if (!index_payload_ok(pl, buf)) return fail(HTTM_ERR_INDEX_MISMATCH, "index contents out of range");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  index->valid = 0;
+  if (hipMemcpyAsync(index->dev, host, pl->I.total, hipMemcpyHostToDevice, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return fail(HTTM_ERR_DEVICE, "index copy to the device failed");
+  index->plan_id = pl->id;
+  index->valid = 1;
+  return HTTM_OK;
+}
+
 httm_status httm_dense_workspace_size(const httm_plan* pl, size_t* bytes) {
   if (!pl || !bytes) return fail(HTTM_ERR_INVALID_ARG, "NULL argument");
   *bytes = pl->dense_ws;
@@ -501,7 +620,8 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
   // atomic targets of this layer: key norms, exact-path count, outlier scratch, outlier counts
   CHECK_LAUNCH(launch_zero_init(at<float>(ws, L.kmax), g.heads, at<int>(ws, L.fb), at<uint32_t>(ws, L.radix),
                                 (int)outlier_scratch_words(hn), at<int32_t>(ws, L.ocnt),
-                                (int64_t)g.heads * g.nslots[kQ], st));
+                                (int64_t)g.heads * g.nslots[kQ], st, &pl->index_header,
+                                reinterpret_cast<uint32_t*>(idx + I.header.off)));
 
   // key branch on the library stream: matching, selection and merge of K / V
   CHECK_LAUNCH(hipEventRecord(side->fork, st));

@@ -43,10 +43,12 @@ __device__ __forceinline__ Scratch scratch_of(uint32_t* s) {
   return r;
 }
 
-// Zero the layer's atomic targets before its producers run (one launch).
+// Zero the layer's atomic targets before its producers run (one launch);
+// also writes the merge index header when asked.
 __global__ void zero_init(float* kmax, int heads, int* fb_count, uint32_t* radix, int radix_words,
-                          int32_t* ocnt, int64_t ocnt_words) {
+                          int32_t* ocnt, int64_t ocnt_words, IndexHeader hdr, uint32_t* hdr_dst) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (hdr_dst && i < 16) hdr_dst[i] = hdr.w[i];
   if (i < heads) kmax[i] = 0.f;
   if (i == 0) *fb_count = 0;
   if (i < radix_words) radix[i] = 0;
@@ -280,13 +282,16 @@ size_t outlier_scratch_words(int64_t total) {
 }
 
 hipError_t launch_zero_init(float* kmax, int heads, int* fb_count, uint32_t* radix, int radix_words,
-                            int32_t* ocnt, int64_t ocnt_words, hipStream_t stream) {
+                            int32_t* ocnt, int64_t ocnt_words, hipStream_t stream, const IndexHeader* hdr,
+                            uint32_t* hdr_dst) {
   int64_t n = heads > radix_words ? heads : radix_words;
   if (ocnt_words > n) n = ocnt_words;
   int64_t grid = (n + 255) / 256;
   grid = grid < 1 ? 1 : (grid > 2048 ? 2048 : grid);
+  IndexHeader h{};
+  if (hdr) h = *hdr;
   hipLaunchKernelGGL(zero_init, dim3((unsigned)grid), dim3(256), 0, stream, kmax, heads, fb_count, radix,
-                     radix_words, ocnt, ocnt_words);
+                     radix_words, ocnt, ocnt_words, h, hdr ? hdr_dst : nullptr);
   return hipGetLastError();
 }
 

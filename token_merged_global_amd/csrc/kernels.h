@@ -109,8 +109,14 @@ int64_t attention_partial_rows(const AttnShape& s);
 // Zero, before a layer's producers run: kmax[heads] (atomic max target of the
 // K~ producer), the exact-path counter, and optionally the outlier radix
 // scratch (radix_words) and the per-group outlier counts (ocnt_words).
+// Words of the header at the start of a merge index (identity of the plan
+// that filled it; written by the layer's first kernel).
+struct IndexHeader {
+  uint32_t w[16];
+};
 hipError_t launch_zero_init(float* kmax, int heads, int* fb_count, uint32_t* radix, int radix_words,
-                            int32_t* ocnt, int64_t ocnt_words, hipStream_t stream);
+                            int32_t* ocnt, int64_t ocnt_words, hipStream_t stream,
+                            const IndexHeader* hdr = nullptr, uint32_t* hdr_dst = nullptr);
 // The main attention kernel, then the tail: exact recompute of the units the
 // main kernel queued and (key splits > 1) the combine of the partials.
 hipError_t launch_attention(int dtype, const AttnShape& s, const void* q, const void* k,
