@@ -41,6 +41,8 @@
 // key range.  An XCD whose S-split workgroups would end in a partly filled
 // round gives its last (tiles mod tiles-per-round) tiles 2S shorter splits:
 // the final round then holds half-length workgroups.
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -691,34 +693,56 @@ int attention_split(int64_t q_capacity, int heads) {
 }
 
 AttnTail attention_tail(int split) {
+  // host-only: capacities use the bound of kMaxTailTiles tail tiles per XCD;
+  // the device's tiles per round is read at launch (attention_per_round)
   AttnTail t{split, 0, 0};
   if (split <= 1) return t;
-  // resident workgroups of the fast kernel per XCD; the gfx950 values
-  // (2 per CU, 32 CUs per XCD) when no device can be queried
-  int occ = 0, cus = 0, dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, attn_fast, kNW * 64, 0) != hipSuccess || occ <= 0 ||
-      cus <= 0) {
-    (void)hipGetLastError();
-    occ = 2;
-    cus = 256;
-  }
-  const int slots = occ * cus / 8;
-  if (cus % 8 || slots % split || slots / split - 1 > kMaxTailTiles) return t;
   t.tail_split = 2 * split;
-  t.per_round = slots / split;
   t.tail_rows = (int64_t)8 * kMaxTailTiles * kRows;
   return t;
 }
+
+namespace {
+// Query tiles per full round of one XCD for `split` key splits on the current
+// device (resident workgroups of the fast kernel / 8 XCDs / split), queried
+// once per device; 0 disables tail splitting (query failed, or more tail
+// tiles than reserved).
+int attention_per_round(int split) {
+  constexpr int kDevs = 64;
+  static std::atomic<int> slots[kDevs];  // resident workgroups per XCD + 1 (0: not known yet)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int v = slots[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int occ = 0, cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, attn_fast, kNW * 64, 0) != hipSuccess || occ <= 0 ||
+        cus <= 0 || cus % 8) {
+      (void)hipGetLastError();
+      occ = 0;
+      cus = 0;
+    }
+    v = occ * cus / 8 + 1;
+    slots[dev].store(v, std::memory_order_relaxed);
+  }
+  const int slots_xcd = v - 1;
+  if (slots_xcd <= 0 || slots_xcd % split || slots_xcd / split - 1 > kMaxTailTiles) return 0;
+  return slots_xcd / split;
+}
+}  // namespace
 
 int64_t attention_workgroups(int dtype, const AttnShape& s) {
   if (dtype != 1) return (s.q_capacity + kRowsF32 - 1) / kRowsF32 + s.heads;
   const int64_t units = (s.q_capacity + kRows - 1) / kRows + s.heads;
   const int64_t nmax = (units + 7) / 8;
   int64_t per_xcd = s.split * nmax;
-  if (s.tail_split > s.split && s.per_round > 0) {
-    const int64_t t = nmax < s.per_round - 1 ? nmax : s.per_round - 1;
+  if (s.tail_split > s.split) {
+    // tail tiles per XCD: fewer than a round's worth, at most kMaxTailTiles
+    const int64_t cap = s.per_round > 0 ? s.per_round - 1 : kMaxTailTiles;
+    const int64_t t = nmax < cap ? nmax : cap;
     per_xcd += (int64_t)(s.tail_split - s.split) * t;
   }
   return 8 * per_xcd;
@@ -749,9 +773,12 @@ AttnArgs make_args(int dtype, const AttnShape& s, const void* q, const void* k, 
   a.vt_pitch = s.vt_pitch;
   a.lq_uniform = s.lq_uniform;
   a.split = dtype == 1 ? s.split : 1;
-  const bool tail = dtype == 1 && a.split > 1 && s.tail_split > a.split && s.per_round > 0;
+  const int per_round = dtype == 1 && a.split > 1 && s.tail_split > a.split && s.tail_rows > 0
+                            ? (s.per_round > 0 ? s.per_round : attention_per_round(a.split))
+                            : 0;
+  const bool tail = per_round > 0 && per_round - 1 <= kMaxTailTiles;
   a.tail_split = tail ? s.tail_split : a.split;
-  a.per_round = tail ? s.per_round : 0;
+  a.per_round = tail ? per_round : 0;
   a.tail_rows = tail ? s.tail_rows : 0;
   a.q_capacity = s.q_capacity;
   AttnShape sh = s;

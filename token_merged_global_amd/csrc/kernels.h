@@ -83,7 +83,7 @@ struct AttnShape {
   float scale;
   int split;               // key splits (bf16); partial buffers needed when > 1
   int tail_split;          // splits of each XCD's tail query tiles (<= split: none)
-  int per_round;           // query tiles per full round of one XCD (0: no tail splits)
+  int per_round;           // query tiles per full round of one XCD (0: the device's, read at launch)
   int64_t tail_rows;       // partial rows reserved for the tail tiles' extra splits
   float* opart;            // [attention_partial_rows][64]
   float* lpart;            // [attention_partial_rows]
@@ -95,8 +95,9 @@ struct AttnShape {
 // Key splits for a layer of q_capacity packed rows; rows per work unit.
 int attention_split(int64_t q_capacity, int heads);
 int attention_rows_per_unit();
-// Tail splitting for `split` key splits on the current device (falls back to
-// the gfx950 figures when no device answers): tail_split == split disables it.
+// Tail splitting for `split` key splits (host only; tail_split == split
+// disables it).  per_round stays 0: the launch reads the device's tiles per
+// round; capacities assume the most tail tiles the schedule allows.
 struct AttnTail {
   int tail_split, per_round;
   int64_t tail_rows;
