@@ -394,9 +394,11 @@ httm_status side_stream(SideStream** out) {
     return fail(HTTM_ERR_DEVICE, "no usable current device");
   SideStream& s = g_side[dev];
   if (!s.st) {
+    // the fork / join events order two streams of one device: device-scope
+    // release and acquire suffice, without the system-scope cache fences
+    const unsigned ef = hipEventDisableTiming | hipEventDisableSystemFence;
     if (hipStreamCreateWithFlags(&s.st, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&s.join, hipEventDisableTiming) != hipSuccess)
+        hipEventCreateWithFlags(&s.fork, ef) != hipSuccess || hipEventCreateWithFlags(&s.join, ef) != hipSuccess)
       return fail(HTTM_ERR_DEVICE, "creating the library stream failed");
   }
   *out = &s;
