@@ -474,11 +474,10 @@ __global__ __launch_bounds__(kNW * 64) void attn_fast(AttnArgs a) {
 
 // Exact path for queued units: online max (raised only when a score exceeds
 // it by more than 8 in log2 units; the final division makes it exact).
-__global__ __launch_bounds__(kNW * 64) void attn_exact(AttnArgs a) {
-  __shared__ u32x4 sK[2][kKeyTile * 8];
-  __shared__ u32x4 sV[2][kD * 8];
-  if ((int)blockIdx.x >= *a.fb_count) return;
-  const int w = a.fb_list[blockIdx.x];
+// A small grid strides over the queue (usually empty).
+constexpr int kExactGrid = 512;
+__device__ __forceinline__ void exact_unit(const AttnArgs& a, int w, u32x4 (*sK)[kKeyTile * 8],
+                                           u32x4 (*sV)[kD * 8]) {
   Unit u;
   if (!schedule(a, w, u)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -546,6 +545,16 @@ __global__ __launch_bounds__(kNW * 64) void attn_exact(AttnArgs a) {
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) lsum[qt] = sum_xor16(sum_xor32(lrun[qt]));
   store_unit(a, u, c, g, oacc, lsum, negm);
+}
+
+__global__ __launch_bounds__(kNW * 64) void attn_exact(AttnArgs a) {
+  __shared__ u32x4 sK[2][kKeyTile * 8];
+  __shared__ u32x4 sV[2][kD * 8];
+  const int n = *a.fb_count;
+  for (int i = blockIdx.x; i < n; i += gridDim.x) {
+    __syncthreads();  // the previous unit's waves are done with the key buffers
+    exact_unit(a, a.fb_list[i], sK, sV);
+  }
 }
 
 // Combine the key-split partials of every packed row (split order fixed):
@@ -805,7 +814,8 @@ hipError_t launch_attention_tail(int dtype, const AttnShape& s, const void* q, c
                                  const void* vt, const int32_t* lenq, void* o, hipStream_t stream) {
   if (dtype != 1) return hipSuccess;
   const AttnArgs a = make_args(dtype, s, q, k, vt, lenq, o);
-  hipLaunchKernelGGL(attn_exact, dim3(a.total_wg), dim3(kNW * 64), 0, stream, a);
+  hipLaunchKernelGGL(attn_exact, dim3(a.total_wg < kExactGrid ? a.total_wg : kExactGrid), dim3(kNW * 64), 0,
+                     stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.split == 1) return e;
   const int fgrid = (int)((s.q_capacity + 31) / 32);
