@@ -61,6 +61,7 @@ class Workload:
     softmax_scale: float = 0.125
     q_dst_stride: int = 0
     kv_dst_stride: int = 0
+    block_order: int = 0  # 0 frame-major, 1 frame-minor stacking inside a block
     layers: int = 1
     sigma_drift: float = 0.1
     sigma_noise: float = 0.05

@@ -79,7 +79,7 @@ class Params:
                       grid_w=w.grid_w, n_special=w.n_special, n_s=w.n_s, n_t=w.n_t,
                       q_ratio=w.q_ratio, kv_ratio=w.kv_ratio, outlier_pct=w.outlier_pct,
                       q_dst_stride=w.q_dst_stride, kv_dst_stride=w.kv_dst_stride,
-                      softmax_scale=w.softmax_scale)
+                      block_order=getattr(w, "block_order", 0), softmax_scale=w.softmax_scale)
 
 
 def dst_stride(ratio: float, given: int = 0) -> int:

@@ -45,6 +45,9 @@ def _plans():
     yield "odd", gen.Workload(name="odd", cfg_id=9, dtype="bf16", heads=3, d_head=64, frames=7, grid_h=5,
                               grid_w=9, n_special=2, n_s=10, n_t=3, q_ratio=0.6, kv_ratio=0.3,
                               outlier_pct=7.5)
+    yield "odd_frame_minor", gen.Workload(name="odd", cfg_id=9, dtype="bf16", heads=3, d_head=64, frames=7,
+                                          grid_h=5, grid_w=9, n_special=2, n_s=10, n_t=3, q_ratio=0.6,
+                                          kv_ratio=0.3, outlier_pct=7.5, block_order=1)
 
 
 @pytest.mark.parametrize("name,w", list(_plans()))
@@ -65,7 +68,10 @@ def test_plan_matches_oracle_blocks(name, w):
         assert (h["f0"], h["nf"], h["j0"], h["run"]) == (o.f0, o.nf, o.j0, o.run)
         # block position -> token, as the kernels compute it
         i = np.arange(o.n)
-        tok = (h["f0"] + i // h["run"]) * p.tokens_per_frame + p.n_special + h["j0"] + i % h["run"]
+        if p.block_order == 0:
+            tok = (h["f0"] + i // h["run"]) * p.tokens_per_frame + p.n_special + h["j0"] + i % h["run"]
+        else:
+            tok = (h["f0"] + i % h["nf"]) * p.tokens_per_frame + p.n_special + h["j0"] + i // h["nf"]
         assert np.array_equal(tok, pi[start:start + o.n])
         for st, (s, ratio, pre) in enumerate([(sq, p.q_ratio, "q"), (sk, p.kv_ratio, "kv")]):
             nd = -(-o.n // s)
@@ -108,7 +114,8 @@ def test_validation_codes():
     assert _status(heads=0) == 1
     assert _status(q_dst_stride=1) == 1
     assert _status(d_head=128) == 2
-    assert _status(block_order=1) == 2
+    assert _status(block_order=1) == 0
+    assert _status(block_order=2) == 1
     assert _status(n_s=128, n_t=33) == 2  # block larger than 4096
     assert _status(heads=64) == 0
     assert _status(heads=65) == 2  # per-head prefix tables are sized for 64

@@ -96,6 +96,27 @@ def test_xcd_tail_tiles_full_outputs():
     assert rep.delta_nonexact == 0
 
 
+@pytest.mark.parametrize("name", ["tiny", "small", "vggt30"])
+def test_frame_minor_blocks(name):
+    """block_order = 1: frames vary fastest inside a block (the alternative
+    stacking of the HTTM page's temporal reordering); staged parity as for
+    frame-major blocks."""
+    w = {"tiny": gen.WORKLOADS["tiny"], "small": small_bf16(), "vggt30": gen.WORKLOADS["vggt30"]}[name]
+    w = w.with_(block_order=1)
+    _say(f"[frame-minor] {name}")
+    x = gen.layer_inputs(w)
+    p = O.Params.from_workload(w)
+    assert p.block_order == 1
+    plan, ws, dev, out, gpu = run_layer(w, x)
+    kw = {"out_tol": F32_ABS} if w.dtype == "f32" else {"rel_tol": BF16_REL}
+    if name == "vggt30":
+        rows = np.unique(np.r_[np.random.default_rng(5).choice(w.n_tokens, 256, replace=False), 0, w.n_tokens - 1])
+        kw["rows"] = rows
+    rep = staged.check_layer(x["q"], x["k"], x["v"], p, gpu, out, **kw)
+    _say("  ", rep.as_dict())
+    assert rep.delta_nonexact == 0
+
+
 def test_ratio_zero_is_exact_attention():
     w = small_bf16(frames=4, heads=2, q_ratio=0.0, kv_ratio=0.0)
     x = gen.layer_inputs(w)

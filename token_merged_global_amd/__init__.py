@@ -155,7 +155,8 @@ class Plan:
         args = dict(heads=w.heads, frames=w.frames, grid_h=w.grid_h, grid_w=w.grid_w, n_special=w.n_special,
                     n_s=w.n_s, n_t=w.n_t, q_ratio=w.q_ratio, kv_ratio=w.kv_ratio, outlier_pct=w.outlier_pct,
                     dtype=w.dtype, d_head=w.d_head, q_dst_stride=w.q_dst_stride,
-                    kv_dst_stride=w.kv_dst_stride, softmax_scale=w.softmax_scale)
+                    kv_dst_stride=w.kv_dst_stride, softmax_scale=w.softmax_scale,
+                    block_order=getattr(w, "block_order", 0))
         args.update(kw)
         return Plan(**args)
 

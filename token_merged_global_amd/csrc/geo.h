@@ -5,8 +5,9 @@
 //
 // A block is identified by (g, a): temporal group g (frames g*n_t ...), spatial
 // run a (raster patches a*n_s ...).  Blocks are numbered b = g*A + a.  Inside a
-// block the stack is frame-major: position i <-> frame f0 + i / run, patch
-// j0 + i % run.  Every per-block quantity follows in closed form from the
+// block the stack is frame-major by default (the plainest reading of the
+// page's "stacking"): position i <-> frame f0 + i / run, patch j0 + i % run;
+// frame-minor order (order 1) puts patch j0 + i / nf, frame f0 + i % nf.  Every per-block quantity follows in closed form from the
 // block's shape (nf, run), of which there are at most four (full or last
 // temporal group x full or last spatial run), so kernels need no block table:
 // the merge counts r of those four shapes are computed once on the host and
@@ -42,6 +43,7 @@ struct Geo {
   int32_t grp_src[2];     // sources of one full temporal group
   int32_t nslots[2];      // slots per head incl. specials (G_q, L_k)
   int32_t nsrc[2];        // sources per head
+  int32_t order;          // stacking inside a block: 0 frame-major, 1 frame-minor
 };
 
 struct BlockInfo {
@@ -75,10 +77,15 @@ GEO_HD BlockInfo block_info(const Geo& g, int32_t b, int st) {
   return o;
 }
 
+// Divisor that splits a block position into (frame, patch): the run for
+// frame-major stacking, the frame count for frame-minor.
+GEO_HD int32_t block_divisor(const Geo& g, const BlockInfo& bi) { return g.order ? bi.nf : bi.run; }
+
 // Original token id of block position i.
 GEO_HD int32_t block_token(const Geo& g, const BlockInfo& bi, int32_t i) {
-  const int32_t f = bi.f0 + i / bi.run;
-  const int32_t j = bi.j0 + i % bi.run;
+  const int32_t d = block_divisor(g, bi), q = i / d, r = i % d;
+  const int32_t f = bi.f0 + (g.order ? r : q);
+  const int32_t j = bi.j0 + (g.order ? q : r);
   return f * g.T + g.nsp + j;
 }
 
@@ -92,10 +99,11 @@ GEO_HD int32_t src_pos(int32_t k, int32_t s) { return k + k / (s - 1) + 1; }
 GEO_HD float div_rcp(int32_t d) { return (1.0f + 0x1p-20f) / (float)d; }
 GEO_HD int32_t div_small(int32_t n, float rcp) { return (int32_t)((float)n * rcp); }
 
-// block_token with precomputed div_rcp(bi.run).
-GEO_HD int32_t block_token_r(const Geo& g, const BlockInfo& bi, int32_t i, float rcp_run) {
-  const int32_t q = div_small(i, rcp_run);
-  return (bi.f0 + q) * g.T + g.nsp + bi.j0 + (i - q * bi.run);
+// block_token with precomputed rcp = div_rcp(block_divisor(g, bi)).
+GEO_HD int32_t block_token_r(const Geo& g, const BlockInfo& bi, int32_t i, float rcp) {
+  const int32_t d = block_divisor(g, bi);
+  const int32_t q = div_small(i, rcp), r = i - q * d;
+  return (bi.f0 + (g.order ? r : q)) * g.T + g.nsp + bi.j0 + (g.order ? q : r);
 }
 
 }  // namespace httm

@@ -151,7 +151,7 @@ httm_status build(const httm_params& p, httm_plan* pl) {
   if (p.dtype != HTTM_F32 && p.dtype != HTTM_BF16) return fail(HTTM_ERR_INVALID_ARG, "unknown dtype");
   if (p.d_head != kD) return fail(HTTM_ERR_UNSUPPORTED, "only d_head == 64 is built");
   if (p.heads > kMaxHeads) return fail(HTTM_ERR_UNSUPPORTED, "at most 64 heads (per-head prefix tables live in LDS)");
-  if (p.block_order != 0) return fail(HTTM_ERR_UNSUPPORTED, "only frame-major blocks (block_order 0) are built");
+  if (p.block_order != 0 && p.block_order != 1) return fail(HTTM_ERR_INVALID_ARG, "block_order must be 0 or 1");
   if ((int64_t)p.n_s * p.n_t > kMaxBlock) return fail(HTTM_ERR_UNSUPPORTED, "n_s * n_t must be <= 4096");
   const int64_t T = (int64_t)p.n_special + (int64_t)p.grid_h * p.grid_w;
   const int64_t N = (int64_t)p.frames * T;
@@ -175,6 +175,7 @@ httm_status build(const httm_params& p, httm_plan* pl) {
   g.nf_last = g.F - (g.G - 1) * g.n_t;
   g.run_last = g.HW - (g.A - 1) * g.n_s;
   g.nblocks = g.A * g.G;
+  g.order = p.block_order;
   const double ratio[2] = {p.q_ratio, p.kv_ratio};
   g.s[0] = stride_of(p.q_ratio, p.q_dst_stride);
   g.s[1] = stride_of(p.kv_ratio, p.kv_dst_stride);

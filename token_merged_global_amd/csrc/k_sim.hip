@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256) void sim_argmax_bf16(SimArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int lg = lane >> 4, l16 = lane & 15;
-  const float rcp_run = div_rcp(bi.run), rcp_s1 = div_rcp(s - 1);
+  const float rcp_run = div_rcp(block_divisor(g, bi)), rcp_s1 = div_rcp(s - 1);
 
   // Source operands: column tile c holds source chunk*256 + wave*64 + 16c + l16,
   // channels 32kc + 8lg .. +8 for k-chunk kc.
