@@ -92,6 +92,54 @@ def cpu_baseline(w, x, heads: int):
                        f"numpy/BLAS threads {threads}, cpu {platform.processor() or platform.machine()}")}
 
 
+# (n_s, n_t) shapes of the block sweep: block sizes near 256, 800 and 3840
+# tokens, each as spatial-only (n_t = 1) and temporal stacks.
+SWEEP_SHAPES = [(256, 1), (86, 3), (26, 10), (800, 1), (267, 3), (80, 10), (27, 30),
+                (1369, 1), (1280, 3), (384, 10), (128, 30)]
+
+
+def sweep_blocks(args, H, torch) -> None:
+    """Cost and merge quality of block shapes and stackings on one set of inputs.
+
+    HTTM page, key design 2 and its spatial/temporal trade-off: per shape the
+    layer time, the merged lengths, the mean query deviation (how far queries
+    sit from their merged token) and the relative RMS error of the layer
+    output against exact unmerged attention on the same inputs.
+    """
+    base = gen.WORKLOADS[args.workload]
+    x = gen.layer_inputs(base, seed=args.seed)
+    tdt = torch.bfloat16 if base.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x[t]).to(tdt).cuda() for t in "qkv")
+    exact = H.attention_dense(H.Plan.from_workload(base), q, k, v).float()
+    torch.cuda.synchronize()
+    enorm = float(exact.norm())
+    stream = torch.cuda.current_stream()
+    for n_s, n_t in SWEEP_SHAPES:
+        for order in ((0, 1) if n_t > 1 else (0,)):
+            w = base.with_(n_s=n_s, n_t=min(n_t, base.frames), block_order=order)
+            plan = H.Plan.from_workload(w)
+            ws = H.workspace(plan)
+            out = torch.empty_like(q)
+            for _ in range(20):
+                H.layer(plan, q, k, v, ws=ws, out=out, stream=stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 50
+            e0.record(stream)
+            for _ in range(reps):
+                H.layer(plan, q, k, v, ws=ws, out=out, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            delta = H.debug_read(plan, ws, "delta")
+            lq = np.diff(H.debug_read(plan, ws, "cu_q"))
+            err = float((out.float() - exact).norm()) / enorm
+            print(json.dumps({"n_s": n_s, "n_t": w.n_t, "n_b": n_s * w.n_t, "block_order": order,
+                              "ms_per_layer": round(ms, 4), "tokens_per_s": w.n_tokens / (ms * 1e-3),
+                              "q_len_mean": float(lq.mean()), "kv_len": plan.info["kv_len"],
+                              "mean_delta": float(delta.mean()), "out_rel_rms_err": err}), flush=True)
+            del ws, out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +159,8 @@ def main():
     ap.add_argument("--outlier-pct", type=float, default=None, help="override the workload's outlier budget")
     ap.add_argument("--cached-layers", type=int, default=None,
                     help="also time layers that reuse the merge indices (default: workload layers - 1)")
+    ap.add_argument("--sweep-blocks", action="store_true",
+                    help="instead of the benchmark: block shape / stacking sweep (one JSON line per shape)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the HTTM layer here runs on a single MI355X "
@@ -119,6 +169,10 @@ def main():
 
     import torch
     import token_merged_global_amd as H
+
+    if args.sweep_blocks:
+        sweep_blocks(args, H, torch)
+        return
 
     w = gen.WORKLOADS[args.workload]
     over = {k: v for k, v in (("kv_ratio", args.kv_ratio), ("q_ratio", args.q_ratio),
