@@ -60,6 +60,8 @@ class Params:
     kv_dst_stride: int = 0
     block_order: int = 0  # 0 frame-major (R3), 1 frame-minor
     softmax_scale: float = 0.0  # 0 -> 1/sqrt(d_head) (R21)
+    partition: int = 0  # 0 HTTM temporal blocks; 1 geometry-aware three-class partition (R24)
+    protect_pct: float = 10.0  # geometry-aware partition: percent of each frame's patches protected
 
     @property
     def tokens_per_frame(self) -> int:
@@ -79,7 +81,8 @@ class Params:
                       grid_w=w.grid_w, n_special=w.n_special, n_s=w.n_s, n_t=w.n_t,
                       q_ratio=w.q_ratio, kv_ratio=w.kv_ratio, outlier_pct=w.outlier_pct,
                       q_dst_stride=w.q_dst_stride, kv_dst_stride=w.kv_dst_stride,
-                      block_order=getattr(w, "block_order", 0), softmax_scale=w.softmax_scale)
+                      block_order=getattr(w, "block_order", 0), softmax_scale=w.softmax_scale,
+                      partition=getattr(w, "partition", 0), protect_pct=getattr(w, "protect_pct", 10.0))
 
 
 def dst_stride(ratio: float, given: int = 0) -> int:
@@ -259,6 +262,133 @@ def match_stream(x: np.ndarray, p: Params, ratio: float, stride: int) -> StreamM
 
 
 # --------------------------------------------------------------------------
+# Geometry-aware three-class partition (an alternative to steps 2-4)
+# --------------------------------------------------------------------------
+# "LiteVGGT: Boosting Vanilla VGGT via Geometry-aware Cached Token Merging",
+# key designs 1-3: a geometry score per token, three token classes (protected
+# high-score tokens, destinations, sources) and a cosine match of every
+# source to its most similar destination.  Used here, like HTTM's matching,
+# per head and per stream (R1).  Readings R24-R29 (design notes).
+VAR_WINDOW = 1  # R25: 3x3 neighbourhood on the frame's patch grid, clipped at the edges
+
+
+def token_variance_map(x: np.ndarray, p: Params) -> np.ndarray:
+    """Token variance map v (LiteVGGT page, key design 1; variance half, R24).
+
+    Patch tokens of each frame are laid on their grid; v of a token is the
+    mean over channels of the variance of the features in its 3x3
+    neighbourhood (average pooling of x and x^2, windows clipped at the grid
+    edge, R25).  fp32 with a fixed order (R26): window cells row-major
+    (dy, dx = -1..1), per channel s1 = sum x, s2 = sum x*x; var = s2/cnt -
+    (s1/cnt)^2; v = (sum of var over channels in ascending order) / d.
+    Special tokens get 0 (they are never merged).
+    """
+    H_, W_ = p.grid_h, p.grid_w
+    T = p.tokens_per_frame
+    d = x.shape[1]
+    v = np.zeros(p.n_tokens, dtype=np.float32)
+    for f in range(p.frames):
+        g = x[f * T + p.n_special:(f + 1) * T].astype(np.float32).reshape(H_, W_, d)
+        s1 = np.zeros((H_, W_, d), dtype=np.float32)
+        s2 = np.zeros((H_, W_, d), dtype=np.float32)
+        cnt = np.zeros((H_, W_), dtype=np.float32)
+        for dy in range(-VAR_WINDOW, VAR_WINDOW + 1):
+            for dx in range(-VAR_WINDOW, VAR_WINDOW + 1):
+                ys = slice(max(0, -dy), H_ - max(0, dy))  # target rows whose neighbour exists
+                xs = slice(max(0, -dx), W_ - max(0, dx))
+                yn = slice(max(0, dy), H_ + min(0, dy))  # the neighbours
+                xn = slice(max(0, dx), W_ + min(0, dx))
+                nb = g[yn, xn]
+                s1[ys, xs] = (s1[ys, xs] + nb).astype(np.float32)
+                s2[ys, xs] = (s2[ys, xs] + (nb * nb).astype(np.float32)).astype(np.float32)
+                cnt[ys, xs] += 1.0
+        c = cnt[:, :, None]
+        m = (s1 / c).astype(np.float32)
+        var = ((s2 / c).astype(np.float32) - (m * m).astype(np.float32)).astype(np.float32)
+        acc = np.zeros((H_, W_), dtype=np.float32)
+        for ch in range(d):
+            acc = (acc + var[:, :, ch]).astype(np.float32)
+        v[f * T + p.n_special:(f + 1) * T] = (acc / np.float32(d)).astype(np.float32).reshape(-1)
+    return v
+
+
+ROLE_SRC, ROLE_DST, ROLE_PROTECT, ROLE_SPECIAL = 0, 1, 2, 3
+
+
+def ga_roles(v: np.ndarray, p: Params) -> np.ndarray:
+    """Three token classes (LiteVGGT page, key design 2; R27, R28).
+
+    Per frame the k = floor(protect_pct/100 * H*W + 1e-9) patches with the
+    highest score are protected (ties to the smaller patch index).  Every
+    unprotected patch of the first frame is a destination; in every other
+    frame, each 2x2 cell of the grid (clipped at odd edges) contributes its
+    unprotected patch with the lowest score (ties to the smaller patch index),
+    if it has one.  The remaining patches are sources; specials keep their own
+    role.
+    """
+    H_, W_ = p.grid_h, p.grid_w
+    T, HW = p.tokens_per_frame, p.grid_h * p.grid_w
+    k = int(math.floor(p.protect_pct / 100.0 * HW + 1e-9))
+    role = np.full(p.n_tokens, ROLE_SRC, dtype=np.int8)
+    for f in range(p.frames):
+        base = f * T
+        role[base:base + p.n_special] = ROLE_SPECIAL
+        vf = v[base + p.n_special:base + T]
+        j = np.arange(HW)
+        order = np.lexsort((j, -vf.astype(np.float64)))  # score desc, index asc
+        prot = np.zeros(HW, dtype=bool)
+        prot[order[:k]] = True
+        rf = np.full(HW, ROLE_SRC, dtype=np.int8)
+        rf[prot] = ROLE_PROTECT
+        if f == 0:
+            rf[~prot] = ROLE_DST
+        else:
+            for cy in range(0, H_, 2):
+                for cx in range(0, W_, 2):
+                    cell = [y * W_ + x for y in range(cy, min(cy + 2, H_)) for x in range(cx, min(cx + 2, W_))]
+                    cand = [c for c in cell if not prot[c]]
+                    if cand:
+                        best = min(cand, key=lambda c: (float(vf[c]), c))
+                        rf[best] = ROLE_DST
+        role[base + p.n_special:base + T] = rf
+    return role
+
+
+def ga_match_stream(x: np.ndarray, p: Params, chunk: int = 4096) -> StreamMatch:
+    """Geometry-aware grouping of one head and stream (LiteVGGT page, key designs 2-3).
+
+    Every source joins its most similar destination over the whole sequence
+    (cosine of RowNorm rows, fp32; ties to the smaller destination id, R29);
+    groups are each destination with its sources, and singletons for
+    protected and special tokens.
+    """
+    N = p.n_tokens
+    role = ga_roles(token_variance_map(x, p), p)
+    src = np.flatnonzero(role == ROLE_SRC)
+    dst = np.flatnonzero(role == ROLE_DST)
+    rep = np.arange(N, dtype=np.int64)
+    mdst = np.full(N, -1, dtype=np.int64)
+    score = np.full(N, np.nan, dtype=np.float32)
+    if len(src) and len(dst):
+        nd = row_normalize(x[dst])
+        for c0 in range(0, len(src), chunk):
+            sc = src[c0:c0 + chunk]
+            sim = (row_normalize(x[sc]) @ nd.T).astype(np.float32)
+            jj = np.argmax(sim, axis=1)  # first maximum = smallest destination id
+            mdst[sc] = dst[jj]
+            score[sc] = sim[np.arange(len(sc)), jj] + np.float32(0.0)
+        m = mdst[src]
+        # group of a source: its destination's; rep = min id over the group
+        grp = rep.copy()
+        grp[src] = m
+        mins = np.arange(N, dtype=np.int64)
+        np.minimum.at(mins, grp, np.arange(N, dtype=np.int64))
+        rep = mins[grp]
+    is_src = role == ROLE_SRC
+    return StreamMatch(rep=rep, match_dst=mdst, score=score, selected=is_src.copy(), is_src=is_src)
+
+
+# --------------------------------------------------------------------------
 # Partitions and means
 # --------------------------------------------------------------------------
 @dataclass
@@ -409,8 +539,12 @@ def match_heads(q: np.ndarray, k: np.ndarray, p: Params, heads: Sequence[int]) -
     """Steps 1-4 for every listed head (head-wise merging, HTTM page, key design 1)."""
     tr = Trace()
     for i in range(len(heads)):
-        tr.q_match.append(match_stream(q[i], p, p.q_ratio, p.q_dst_stride))
-        tr.k_match.append(match_stream(k[i], p, p.kv_ratio, p.kv_dst_stride))
+        if p.partition == 1:  # geometry-aware three-class partition (R24)
+            tr.q_match.append(ga_match_stream(q[i], p))
+            tr.k_match.append(ga_match_stream(k[i], p))
+        else:
+            tr.q_match.append(match_stream(q[i], p, p.q_ratio, p.q_dst_stride))
+            tr.k_match.append(match_stream(k[i], p, p.kv_ratio, p.kv_dst_stride))
         tr.k_rep.append(tr.k_match[-1].rep)
     return tr
 

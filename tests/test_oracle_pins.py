@@ -403,3 +403,130 @@ def test_generator_shapes_and_bf16():
     # round-to-nearest-even on an exact half-way case
     a = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8], np.float32)
     assert gen.round_bf16(a).tolist() == [1.0, 1.0 + 2 ** -6]
+
+
+# --------------------------------------------------------------------------
+# Geometry-aware three-class partition (LiteVGGT page, key designs 1-3)
+# --------------------------------------------------------------------------
+def _ga_params(**kw):
+    base = dict(heads=1, d_head=64, frames=2, grid_h=4, grid_w=5, n_special=1, n_s=4, n_t=2, q_ratio=0.5,
+                kv_ratio=0.5, outlier_pct=0.0, partition=1, protect_pct=10.0)
+    base.update(kw)
+    return O.Params(**base)
+
+
+def test_variance_map_closed_forms():
+    """Constant field: v = 0.  Channel 0 = column index on a 4x5 grid: the 3x3
+    window of an interior patch holds columns x-1..x+1 (variance 2/3), an edge
+    or corner patch two columns (variance 1/4); v averages over the 64 channels."""
+    p = _ga_params()
+    T = p.tokens_per_frame
+    x = np.ones((p.n_tokens, 64), np.float32)
+    assert np.all(O.token_variance_map(x, p) == 0.0)
+    x = np.zeros((p.n_tokens, 64), np.float32)
+    cols = np.tile(np.arange(5, dtype=np.float32), 4)
+    for f in range(p.frames):
+        x[f * T + 1:(f + 1) * T, 0] = cols
+    v = O.token_variance_map(x, p)
+    for f in range(p.frames):
+        vf = v[f * T + 1:(f + 1) * T].reshape(4, 5)
+        assert v[f * T] == 0.0  # special token
+        assert np.allclose(vf[:, 1:4], (2.0 / 3.0) / 64, rtol=1e-6)
+        assert np.allclose(vf[:, [0, 4]], 0.25 / 64, rtol=1e-6)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_variance_map_brute_force(seed):
+    """Against explicit per-patch windows in fp64 (clipped 3x3 neighbourhoods)."""
+    p = _ga_params(frames=2, grid_h=5, grid_w=6, n_special=2)
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((p.n_tokens, 64)).astype(np.float32)
+    v = O.token_variance_map(x, p)
+    T, H_, W_ = p.tokens_per_frame, p.grid_h, p.grid_w
+    for f in range(p.frames):
+        for y in range(H_):
+            for xx in range(W_):
+                win = [x[f * T + p.n_special + yy * W_ + xc].astype(np.float64)
+                       for yy in range(max(0, y - 1), min(H_, y + 2)) for xc in range(max(0, xx - 1), min(W_, xx + 2))]
+                w = np.stack(win)
+                ref = float(np.mean(w.var(axis=0)))
+                assert abs(float(v[f * T + p.n_special + y * W_ + xx]) - ref) <= 1e-5 * max(1.0, ref)
+
+
+def test_ga_roles_hand_example():
+    """4x4 grid, 2 frames, 10 % protected (k = floor(1.6) = 1 per frame).
+    Frame 0: the top patch is protected, the other 15 are destinations.
+    Frame 1: top patch protected; each 2x2 cell's lowest unprotected patch is
+    a destination (ties to the smaller index); the rest are sources."""
+    p = _ga_params(frames=2, grid_h=4, grid_w=4, n_special=0)
+    v = np.zeros(32, np.float32)
+    v[:16] = np.arange(16, dtype=np.float32)  # frame 0: patch 15 is the top
+    f1 = np.array([5, 1, 2, 9,
+                   3, 7, 2, 2,
+                   4, 4, 8, 6,
+                   4, 0.5, 6, 10], np.float32)  # top: patch 15 (10); cells below
+    v[16:] = f1
+    role = O.ga_roles(v, p)
+    S, D, P = O.ROLE_SRC, O.ROLE_DST, O.ROLE_PROTECT
+    assert role[15] == P and np.all(role[:15] == D)
+    want = np.full(16, S, np.int8)
+    want[15] = P
+    want[1] = D    # cell (0,0), patches {0, 1, 4, 5} with {5, 1, 3, 7} -> patch 1
+    want[2] = D    # cell (0,1), patches {2, 3, 6, 7} with {2, 9, 2, 2} -> 2, 6, 7 tie -> patch 2
+    want[13] = D   # cell (1,0), patches {8, 9, 12, 13} with {4, 4, 4, 0.5} -> patch 13
+    want[11] = D   # cell (1,1), patches {10, 11, 14, 15} with {8, 6, 6, 10 (protected)} -> 11 and 14 tie -> 11
+    assert role[16:].tolist() == want.tolist()
+
+
+def test_ga_roles_full_cell_and_odd_edges():
+    """A cell whose patches are all protected has no destination; on a 3x5
+    grid the last row and column form clipped cells."""
+    p = _ga_params(frames=2, grid_h=3, grid_w=5, n_special=0, protect_pct=27.0)  # k = floor(4.05) = 4
+    v = np.zeros(30, np.float32)
+    f1 = np.array([9, 9, 0, 1, 2,
+                   9, 9, 3, 4, 5,
+                   6, 7, 8, 0.5, 0.25], np.float32)  # top 4: patches 0, 1, 5, 6 (one full cell)
+    v[15:] = f1
+    role = O.ga_roles(v, p)[15:]
+    assert [int(i) for i in np.flatnonzero(role == O.ROLE_PROTECT)] == [0, 1, 5, 6]
+    # cells: (0,0) all protected; (0,1) {0, 1, 3, 4} -> 2; (0,2) {2, 5} -> 4; (1,0) {6, 7} -> 10;
+    # (1,1) {8, 0.5} -> 13; (1,2) {0.25} -> 14
+    assert [int(i) for i in np.flatnonzero(role == O.ROLE_DST)] == [2, 4, 10, 13, 14]
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_ga_match_brute_force(seed):
+    """Every source joins its most similar destination over the whole
+    sequence (fp64 brute force); groups: destination + its sources, protected
+    and special tokens alone."""
+    p = _ga_params(frames=3, grid_h=4, grid_w=6, n_special=1, protect_pct=20.0)
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((p.n_tokens, 64)).astype(np.float32)
+    m = O.ga_match_stream(x, p)
+    role = O.ga_roles(O.token_variance_map(x, p), p)
+    src, dst = np.flatnonzero(role == O.ROLE_SRC), np.flatnonzero(role == O.ROLE_DST)
+    xn = x.astype(np.float64) / np.linalg.norm(x.astype(np.float64), axis=1, keepdims=True)
+    for s_ in src:
+        sims = xn[dst] @ xn[s_]
+        best = dst[int(np.argmax(sims))]
+        if m.match_dst[s_] != best:  # only a float near-tie may differ
+            assert abs(sims.max() - float(xn[m.match_dst[s_]] @ xn[s_])) < 1e-6
+        assert m.rep[s_] == m.rep[m.match_dst[s_]]
+    alone = np.flatnonzero((role == O.ROLE_PROTECT) | (role == O.ROLE_SPECIAL))
+    assert np.all(m.rep[alone] == alone)
+    assert len(np.unique(m.rep)) == len(dst) + len(alone)
+    for d in dst:  # a destination's group is itself and its sources; rep = smallest id
+        mem = np.r_[d, src[m.match_dst[src] == d]]
+        assert np.all(m.rep[mem] == mem.min())
+
+
+def test_ga_protect_all_is_exact_attention():
+    """100 % protected: nothing merges, so the layer is exact attention."""
+    w = gen.WORKLOADS["tiny"].with_(frames=2, grid_h=6, grid_w=6, n_special=1, outlier_pct=10.0)
+    x = gen.layer_inputs(w)
+    p = O.Params.from_workload(w)
+    p = O.Params(**{**p.__dict__, "partition": 1, "protect_pct": 100.0})
+    tr = O.layer(x["q"], x["k"], x["v"], p)
+    for h in range(w.heads):
+        ref = O.attention(x["q"][h], x["k"][h], x["v"][h], p.scale)
+        assert np.abs(tr.out[h] - ref).max() <= 1e-5
