@@ -269,7 +269,17 @@ def match_stream(x: np.ndarray, p: Params, ratio: float, stride: int) -> StreamM
 # high-score tokens, destinations, sources) and a cosine match of every
 # source to its most similar destination.  Used here, like HTTM's matching,
 # per head and per stream (R1).  Readings R24-R29 (design notes).
-VAR_WINDOW = 1  # R25: 3x3 neighbourhood on the frame's patch grid, clipped at the edges
+
+
+def _box3_sum(a: np.ndarray, axis: int) -> np.ndarray:
+    """Sum of each element and its existing neighbours along `axis` (fp32):
+    (left + centre) + right, in ascending order, clipped at the ends."""
+    a = np.moveaxis(a, axis, 0)
+    t = a.copy()
+    if a.shape[0] > 1:
+        t[1:] = (a[:-1] + a[1:]).astype(np.float32)  # left + centre
+        t[:-1] = (t[:-1] + a[1:]).astype(np.float32)  # ... + right
+    return np.moveaxis(t, 0, axis)
 
 
 def token_variance_map(x: np.ndarray, p: Params) -> np.ndarray:
@@ -278,33 +288,27 @@ def token_variance_map(x: np.ndarray, p: Params) -> np.ndarray:
     Patch tokens of each frame are laid on their grid; v of a token is the
     mean over channels of the variance of the features in its 3x3
     neighbourhood (average pooling of x and x^2, windows clipped at the grid
-    edge, R25).  fp32 with a fixed order (R26): window cells row-major
-    (dy, dx = -1..1), per channel s1 = sum x, s2 = sum x*x; var = s2/cnt -
-    (s1/cnt)^2; v = (sum of var over channels in ascending order) / d.
-    Special tokens get 0 (they are never merged).
+    edge, R25).  fp32 in a fixed order (R26): per channel, each row's
+    available cells are summed left to right, then the available rows top to
+    bottom (for x and for x*x); var = s2/cnt - (s1/cnt)^2; v = (sum of var
+    over channels in ascending order) / d.  Special tokens get 0 (they are
+    never merged).
     """
     H_, W_ = p.grid_h, p.grid_w
     T = p.tokens_per_frame
     d = x.shape[1]
+    ncol = np.full(W_, 3.0 if W_ > 2 else float(min(W_, 2)), np.float32)
+    ncol[[0, -1]] = float(min(W_, 2))
+    nrow = np.full(H_, 3.0 if H_ > 2 else float(min(H_, 2)), np.float32)
+    nrow[[0, -1]] = float(min(H_, 2))
+    cnt = (nrow[:, None] * ncol[None, :])[:, :, None].astype(np.float32)
     v = np.zeros(p.n_tokens, dtype=np.float32)
     for f in range(p.frames):
         g = x[f * T + p.n_special:(f + 1) * T].astype(np.float32).reshape(H_, W_, d)
-        s1 = np.zeros((H_, W_, d), dtype=np.float32)
-        s2 = np.zeros((H_, W_, d), dtype=np.float32)
-        cnt = np.zeros((H_, W_), dtype=np.float32)
-        for dy in range(-VAR_WINDOW, VAR_WINDOW + 1):
-            for dx in range(-VAR_WINDOW, VAR_WINDOW + 1):
-                ys = slice(max(0, -dy), H_ - max(0, dy))  # target rows whose neighbour exists
-                xs = slice(max(0, -dx), W_ - max(0, dx))
-                yn = slice(max(0, dy), H_ + min(0, dy))  # the neighbours
-                xn = slice(max(0, dx), W_ + min(0, dx))
-                nb = g[yn, xn]
-                s1[ys, xs] = (s1[ys, xs] + nb).astype(np.float32)
-                s2[ys, xs] = (s2[ys, xs] + (nb * nb).astype(np.float32)).astype(np.float32)
-                cnt[ys, xs] += 1.0
-        c = cnt[:, :, None]
-        m = (s1 / c).astype(np.float32)
-        var = ((s2 / c).astype(np.float32) - (m * m).astype(np.float32)).astype(np.float32)
+        s1 = _box3_sum(_box3_sum(g, 1), 0)
+        s2 = _box3_sum(_box3_sum((g * g).astype(np.float32), 1), 0)
+        m = (s1 / cnt).astype(np.float32)
+        var = ((s2 / cnt).astype(np.float32) - (m * m).astype(np.float32)).astype(np.float32)
         acc = np.zeros((H_, W_), dtype=np.float32)
         for ch in range(d):
             acc = (acc + var[:, :, ch]).astype(np.float32)
