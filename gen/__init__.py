@@ -62,6 +62,8 @@ class Workload:
     q_dst_stride: int = 0
     kv_dst_stride: int = 0
     block_order: int = 0  # 0 frame-major, 1 frame-minor stacking inside a block
+    partition: int = 0  # 0 HTTM temporal blocks, 1 geometry-aware three-class partition
+    protect_pct: float = 10.0  # partition 1: percent of each frame's patches protected
     layers: int = 1
     sigma_drift: float = 0.1
     sigma_noise: float = 0.05

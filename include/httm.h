@@ -90,9 +90,20 @@ typedef struct {
   double outlier_pct;    /* d in [0, 100]: percent of heads*N queries restored */
   int32_t q_dst_stride;  /* destination stride for Q; 0 = max(4, ceil(1/(1-q_ratio))) */
   int32_t kv_dst_stride; /* destination stride for K; 0 = max(4, ceil(1/(1-kv_ratio))) */
-  int32_t block_order;   /* 0 = frame-major stacking inside a block (only value supported) */
+  int32_t block_order;   /* stacking inside a block: 0 = frame-major, 1 = frame-minor */
   float softmax_scale;   /* 0 = 1/sqrt(d_head) */
   int32_t dtype;         /* httm_dtype of q, k, v, out */
+  int32_t partition;     /* 0 = HTTM temporal blocks (default); 1 = geometry-aware three-class
+                            partition (LiteVGGT page, key designs 1-3) of both streams, per
+                            head: q_ratio, kv_ratio, strides and block_order do not apply
+                            (n_s, n_t are still validated); the group count, and with it
+                            the keys per head, varies by head and input, up to the bound
+                            frames * n_special + H*W + (frames - 1) * (protected +
+                            ceil(H/2) * ceil(W/2)) (at most N), which sizes q_groups and
+                            kv_len in httm_plan_info.  Limits: at most 4096 patches per
+                            frame and N < 2^20 */
+  double protect_pct;    /* partition 1: percent of each frame's patches protected, [0, 100]
+                            (the page uses 10); protected = floor(protect_pct / 100 * H*W) */
 } httm_params;
 
 typedef struct httm_plan httm_plan;
@@ -208,11 +219,22 @@ httm_status httm_attention_dense(const httm_plan* plan, void* ws, size_t ws_byte
  *   HTTM_DBG_SELECT: [4] uint32 {threshold bits, count above, ties taken, k_o};
  *   HTTM_DBG_ATTN_FALLBACK: [1] int32 attention work units that the exact
  *       (running-max) kernel recomputed because their rows' probabilities
- *       underflowed against the norm bound. */
+ *       underflowed against the norm bound.
+ * Geometry-aware partition only (the four MATCH / SCORE items above return
+ * HTTM_ERR_UNSUPPORTED there), [2][h][N] with stream 0 = Q, 1 = K:
+ *   HTTM_DBG_GA_VAR: float token variance map (0 for special tokens);
+ *   HTTM_DBG_GA_ROLE: uint8 class: 0 source, 1 destination, 2 protected,
+ *       3 special;
+ *   HTTM_DBG_GA_MATCH: matched destination token of every source, -1 for
+ *       every other token;
+ *   HTTM_DBG_GA_SCORE: float cosine of that match (0 for non-sources);
+ *   HTTM_DBG_KV_LEN: [h] keys per head (the key stream's group count). */
 typedef enum {
   HTTM_DBG_Q_MATCH = 0, HTTM_DBG_Q_SCORE, HTTM_DBG_KV_MATCH, HTTM_DBG_KV_SCORE,
   HTTM_DBG_Q_GROUP, HTTM_DBG_KV_GROUP, HTTM_DBG_DELTA, HTTM_DBG_OUTLIER,
-  HTTM_DBG_Q_SLOT, HTTM_DBG_CU_Q, HTTM_DBG_SELECT, HTTM_DBG_ATTN_FALLBACK, HTTM_DBG_COUNT
+  HTTM_DBG_Q_SLOT, HTTM_DBG_CU_Q, HTTM_DBG_SELECT, HTTM_DBG_ATTN_FALLBACK,
+  HTTM_DBG_GA_VAR, HTTM_DBG_GA_ROLE, HTTM_DBG_GA_MATCH, HTTM_DBG_GA_SCORE, HTTM_DBG_KV_LEN,
+  HTTM_DBG_COUNT
 } httm_debug_item;
 httm_status httm_debug_size(const httm_plan* plan, int32_t item, size_t* bytes);
 httm_status httm_debug_read(const httm_plan* plan, const void* ws, const httm_index* index,

@@ -358,6 +358,12 @@ def ga_roles(v: np.ndarray, p: Params) -> np.ndarray:
     return role
 
 
+def ga_similarity(x: np.ndarray, src: np.ndarray, dst: np.ndarray) -> np.ndarray:
+    """Cosine of every listed source with every listed destination
+    (LiteVGGT page, key design 3): products of RowNorm rows, fp32."""
+    return (row_normalize(x[src]) @ row_normalize(x[dst]).T).astype(np.float32)
+
+
 def ga_match_stream(x: np.ndarray, p: Params, chunk: int = 4096) -> StreamMatch:
     """Geometry-aware grouping of one head and stream (LiteVGGT page, key designs 2-3).
 
@@ -374,10 +380,9 @@ def ga_match_stream(x: np.ndarray, p: Params, chunk: int = 4096) -> StreamMatch:
     mdst = np.full(N, -1, dtype=np.int64)
     score = np.full(N, np.nan, dtype=np.float32)
     if len(src) and len(dst):
-        nd = row_normalize(x[dst])
         for c0 in range(0, len(src), chunk):
             sc = src[c0:c0 + chunk]
-            sim = (row_normalize(x[sc]) @ nd.T).astype(np.float32)
+            sim = ga_similarity(x, sc, dst)
             jj = np.argmax(sim, axis=1)  # first maximum = smallest destination id
             mdst[sc] = dst[jj]
             score[sc] = sim[np.arange(len(sc)), jj] + np.float32(0.0)

@@ -9,7 +9,9 @@ near-tie (similarity within 1e-5 of the best, or a source score within 1e-5 of
 the r-th score), which is counted.  Every later stage is re-run by the oracle
 on the implementation's own indices, so a counted near-tie never cascades:
 
-  (i)   matches and scores, per block;
+  (i)   matches and scores, per block (geometry-aware partition: variance
+        map and classes exactly, then matches and scores over all
+        destinations);
   (ii)  top-r selection and the resulting groups (groups exactly);
   (iii) deviations on the implementation's query groups, and the global
         outlier choice on the implementation's deviations (exactly);
@@ -123,6 +125,70 @@ def check_stream(x: np.ndarray, p: O.Params, ratio: float, stride: int, gpu_matc
     return rep_gpu
 
 
+def check_ga_stream(x: np.ndarray, p: O.Params, gpu_var: np.ndarray, gpu_role: np.ndarray,
+                    gpu_match: np.ndarray, gpu_score: np.ndarray, gpu_group: np.ndarray, rep: Report,
+                    what: str, chunk: int = 2048) -> np.ndarray:
+    """Geometry-aware partition of one head and stream; returns the canonical groups.
+
+    (i) the variance map bit for bit; (ii) the three classes bit for bit,
+    recomputed from the implementation's own map; (iii) every source's
+    destination is the oracle's most similar one or a counted near-tie, its
+    score within 1e-5; (iv) groups exactly: each destination with the
+    sources that the implementation matched to it.
+    gpu_match: matched destination token per token (-1 for non-sources).
+    """
+    N = p.n_tokens
+    v = O.token_variance_map(x, p)
+    gv = np.asarray(gpu_var, dtype=np.float32)
+    if not np.array_equal(v, gv):
+        bad = np.flatnonzero(v != gv)
+        raise ParityError(f"{what}: variance map differs at {len(bad)} tokens (first {bad[0]}: "
+                          f"{gv[bad[0]]!r} vs {v[bad[0]]!r})")
+    role = O.ga_roles(gv, p)
+    gr = np.asarray(gpu_role, dtype=np.int8)
+    if not np.array_equal(role, gr):
+        bad = np.flatnonzero(role != gr)
+        raise ParityError(f"{what}: classes differ at {len(bad)} tokens (first {bad[0]}: {gr[bad[0]]} vs "
+                          f"{role[bad[0]]})")
+    src = np.flatnonzero(role == O.ROLE_SRC)
+    dst = np.flatnonzero(role == O.ROLE_DST)
+    gm = np.asarray(gpu_match, dtype=np.int64)
+    if (gm[role != O.ROLE_SRC] != -1).any():
+        raise ParityError(f"{what}: a token that is not a source carries a match")
+    label = np.arange(N, dtype=np.int64)
+    if len(src):
+        m = gm[src]
+        pos = np.searchsorted(dst, m)
+        if (m < 0).any() or (pos >= len(dst)).any() or (dst[np.minimum(pos, len(dst) - 1)] != m).any():
+            raise ParityError(f"{what}: a source is matched to a token that is not a destination")
+        gs = np.asarray(gpu_score, dtype=np.float32)[src]
+        for c0 in range(0, len(src), chunk):
+            sc = src[c0:c0 + chunk]
+            sim = O.ga_similarity(x, sc, dst)
+            rows = np.arange(len(sc))
+            jo = np.argmax(sim, axis=1)
+            jg = pos[c0:c0 + chunk]
+            gap = sim[rows, jo] - sim[rows, jg]
+            bad = (jg != jo) & (gap >= NEAR_TIE)
+            if bad.any():
+                i = int(np.flatnonzero(bad)[0])
+                raise ParityError(f"{what}: source {sc[i]} matched {dst[jg[i]]} (sim {sim[i, jg[i]]:.7f}) but "
+                                  f"best is {dst[jo[i]]} (sim {sim[i, jo[i]]:.7f})")
+            rep.match_near_ties += int(((jg != jo) & (gap < NEAR_TIE)).sum())
+            err = np.abs(gs[c0:c0 + chunk].astype(np.float64) - sim[rows, jg])
+            rep.max_score_err = max(rep.max_score_err, float(err.max()))
+            if err.max() >= NEAR_TIE:
+                raise ParityError(f"{what}: score error {err.max():.3g}")
+        label[src] = m
+        rep.n_src += len(src)
+    want = canonical(label)
+    got = canonical(gpu_group)
+    if not np.array_equal(want, got):
+        i = int(np.flatnonzero(want != got)[0])
+        raise ParityError(f"{what}: groups differ at token {i}: rep {got[i]} vs {want[i]}")
+    return got
+
+
 def check_layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, p: O.Params, gpu: Dict[str, np.ndarray],
                 out_gpu: np.ndarray, out_heads: Optional[Sequence[int]] = None,
                 rows: Optional[np.ndarray] = None, out_tol: Optional[float] = None,
@@ -131,7 +197,9 @@ def check_layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, p: O.Params, gpu: D
     """Staged parity of one layer.
 
     gpu: q_match, q_score, kv_match, kv_score ([h][src]), q_group, kv_group,
-    q_slot ([h][N]), delta ([h][N] float32), outlier ([h][N] uint8).
+    q_slot ([h][N]), delta ([h][N] float32), outlier ([h][N] uint8); under
+    the geometry-aware partition ga_var, ga_role, ga_match, ga_score
+    ([2][h][N], stream 0 = Q) in place of the four match / score items.
     out_gpu: [h][N][d] as float64/float32.  Tolerance on the max-abs output
     error: ``rel_tol`` * RMS(oracle output) if given (bf16: 2e-2), else
     ``out_tol`` (default 1e-4, fp32).  ``workers`` threads share the per-head
@@ -140,13 +208,21 @@ def check_layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, p: O.Params, gpu: D
     rep = Report()
     h, N = q.shape[0], q.shape[1]
     mh = list(range(h)) if match_heads is None else list(match_heads)
-    nq, nk = gpu["q_match"].shape[1], gpu["kv_match"].shape[1]
     q_rep = [None] * h
     k_rep = [None] * h
 
+    ga = p.partition == 1
+    if ga:
+        ga_items = {it: np.asarray(gpu[it]).reshape(2, h, N) for it in ("ga_var", "ga_role", "ga_match", "ga_score")}
+
     def per_head(i):
         r = Report()
-        if i in mh:
+        if i in mh and ga:
+            qr, kr = (check_ga_stream(x[i], p, ga_items["ga_var"][st, i], ga_items["ga_role"][st, i],
+                                      ga_items["ga_match"][st, i], ga_items["ga_score"][st, i],
+                                      gpu[grp][i], r, f"head {i} {nm}")
+                      for st, (x, grp, nm) in enumerate(((q, "q_group", "Q"), (k, "kv_group", "K"))))
+        elif i in mh:
             qr = check_stream(q[i], p, p.q_ratio, p.q_dst_stride, gpu["q_match"][i], gpu["q_score"][i],
                               gpu["q_group"][i], r, f"head {i} Q")
             kr = check_stream(k[i], p, p.kv_ratio, p.kv_dst_stride, gpu["kv_match"][i],

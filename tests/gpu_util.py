@@ -23,9 +23,10 @@ def to_dev(x: np.ndarray, dtype: str):
 
 
 def read_all(plan, ws, heads, index=None):
-    gpu = {it: H.debug_read(plan, ws, it, index=index) for it in H.DEBUG_ITEMS}
+    gpu = {it: H.debug_read(plan, ws, it, index=index) for it in H.debug_items(plan)}
     for it in PER_HEAD:
-        gpu[it] = gpu[it].reshape(heads, -1)
+        if it in gpu:
+            gpu[it] = gpu[it].reshape(heads, -1)
     return gpu
 
 

@@ -173,3 +173,64 @@ def test_index_export_import_validation():
     # a device buffer smaller than the index
     small = H.Index(0, 0x1000, n - 1, 0)
     assert L.httm_index_import(plan.handle, buf.ctypes.data, n, ctypes.byref(small), None) == 3
+
+
+def _ga_bound(w, pct):
+    hw = w.grid_h * w.grid_w
+    kp = math.floor(pct / 100.0 * hw + 1e-9)
+    cells = ((w.grid_h + 1) // 2) * ((w.grid_w + 1) // 2)
+    return min(w.n_tokens, w.frames * w.n_special + hw + (w.frames - 1) * (kp + cells))
+
+
+@pytest.mark.parametrize("name,pct", [("tiny", 10.0), ("vggt30", 10.0), ("vggt100", 10.0), ("vggt500", 10.0),
+                                      ("vggt30", 0.0), ("vggt30", 100.0)])
+def test_ga_plan_sizes(name, pct):
+    """Geometry-aware plans size every head for the largest possible group
+    count: all first-frame patches, specials, and per later frame the
+    protected patches plus one destination per 2x2 cell."""
+    w = gen.WORKLOADS[name].with_(partition=1, protect_pct=pct)
+    plan = H.Plan.from_workload(w)
+    b = _ga_bound(w, pct)
+    assert plan.info["q_groups"] == plan.info["kv_len"] == b
+    assert plan.info["q_capacity"] == w.heads * b + plan.info["n_outliers"]
+    assert plan.info["q_src"] == plan.info["kv_src"] == (w.frames - 1) * w.grid_h * w.grid_w
+    assert "ga_var" in H.debug_items(plan) and "q_match" not in H.debug_items(plan)
+    n = ctypes.c_size_t()
+    L = H.lib()
+    assert L.httm_debug_size(plan.handle, H.DEBUG_ITEMS.index("q_match"), ctypes.byref(n)) == 2
+    assert L.httm_debug_size(plan.handle, H.DEBUG_ITEMS.index("ga_role"), ctypes.byref(n)) == 0
+    assert n.value == 2 * w.heads * w.n_tokens
+    blk = H.Plan.from_workload(gen.WORKLOADS[name])
+    assert L.httm_debug_size(blk.handle, H.DEBUG_ITEMS.index("ga_var"), ctypes.byref(n)) == 2
+    # the index differs from the block-local plan's: another layout, another fingerprint
+    assert plan.index_bytes > 0
+
+
+def test_ga_group_bound_holds_on_the_oracle():
+    """The plan's bound is never exceeded by the oracle's groups, with
+    protected cells and odd grid edges."""
+    for gh, gw, pct, sp in [(5, 7, 20.0, 2), (4, 4, 0.0, 0), (3, 5, 60.0, 1)]:
+        w = gen.Workload(name="ga", cfg_id=11, dtype="f32", heads=2, d_head=64, frames=5, grid_h=gh, grid_w=gw,
+                         n_special=sp, n_s=8, n_t=2, q_ratio=0.5, kv_ratio=0.5, outlier_pct=10.0, partition=1,
+                         protect_pct=pct)
+        p = O.Params.from_workload(w)
+        x = gen.layer_inputs(w)
+        for t in "qk":
+            for hh in range(w.heads):
+                m = O.ga_match_stream(x[t][hh], p)
+                assert len(np.unique(m.rep)) <= _ga_bound(w, pct)
+
+
+def test_ga_validation_codes():
+    assert _status(partition=1) == 0
+    assert _status(partition=2) == 1
+    assert _status(partition=-1) == 1
+    assert _status(partition=1, protect_pct=-1.0) == 1
+    assert _status(partition=1, protect_pct=100.5) == 1
+    assert _status(partition=1, protect_pct=float("nan")) == 1
+    assert _status(partition=0, protect_pct=-1.0) == 0  # ignored by the block partition
+    assert _status(partition=1, grid_h=64, grid_w=64) == 0
+    assert _status(partition=1, grid_h=64, grid_w=65) == 2  # more than 4096 patches per frame
+    # N = 1000 * 1374 >= 2^20 tokens
+    assert _status(partition=1, frames=1000, grid_h=37, grid_w=37, n_special=5, n_s=128, n_t=30) == 2
+    assert _status(partition=1, frames=500, grid_h=37, grid_w=37, n_special=5, n_s=128, n_t=30) == 0

@@ -165,12 +165,12 @@ def test_repeat_runs_are_bit_identical():
     q, k, v = (to_dev(x[t], w.dtype) for t in "qkv")
     ws = H.workspace(plan)
     o1 = H.layer(plan, q, k, v, ws=ws).clone()
-    d1 = {it: H.debug_read(plan, ws, it) for it in H.DEBUG_ITEMS}
+    d1 = {it: H.debug_read(plan, ws, it) for it in H.debug_items(plan)}
     o2 = H.layer(plan, q, k, v, ws=ws)
-    d2 = {it: H.debug_read(plan, ws, it) for it in H.DEBUG_ITEMS}
+    d2 = {it: H.debug_read(plan, ws, it) for it in H.debug_items(plan)}
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
-    for it in H.DEBUG_ITEMS:
+    for it in d1:
         assert np.array_equal(d1[it], d2[it]), it
 
 

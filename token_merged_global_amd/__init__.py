@@ -24,7 +24,11 @@ HTTM_F32, HTTM_BF16 = 0, 1
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small",
           4: "index mismatch", 5: "device error"}
 DEBUG_ITEMS = ["q_match", "q_score", "kv_match", "kv_score", "q_group", "kv_group", "delta",
-               "outlier", "q_slot", "cu_q", "select", "attn_fallback"]
+               "outlier", "q_slot", "cu_q", "select", "attn_fallback",
+               "ga_var", "ga_role", "ga_match", "ga_score", "kv_len"]
+#: Items that exist only under one partition (block-local / geometry-aware).
+BLOCK_ITEMS = ["q_match", "q_score", "kv_match", "kv_score"]
+GA_ITEMS = ["ga_var", "ga_role", "ga_match", "ga_score", "kv_len"]
 TIMING_STAGES = ["sim", "select", "merge_kv", "merge_q", "outlier", "restore", "attn", "unmerge", "attn_tail"]
 
 
@@ -41,7 +45,7 @@ class Params(ctypes.Structure):
                 ("kv_ratio", ctypes.c_double), ("outlier_pct", ctypes.c_double),
                 ("q_dst_stride", ctypes.c_int32), ("kv_dst_stride", ctypes.c_int32),
                 ("block_order", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("partition", ctypes.c_int32), ("protect_pct", ctypes.c_double)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -138,10 +142,10 @@ class Plan:
     def __init__(self, heads: int, frames: int, grid_h: int, grid_w: int, n_special: int, n_s: int,
                  n_t: int, q_ratio: float, kv_ratio: float, outlier_pct: float, dtype="bf16",
                  d_head: int = 64, q_dst_stride: int = 0, kv_dst_stride: int = 0, block_order: int = 0,
-                 softmax_scale: float = 0.0):
+                 softmax_scale: float = 0.0, partition: int = 0, protect_pct: float = 10.0):
         self.params = Params(heads, d_head, frames, grid_h, grid_w, n_special, n_s, n_t, float(q_ratio),
                              float(kv_ratio), float(outlier_pct), q_dst_stride, kv_dst_stride, block_order,
-                             float(softmax_scale), _dtype_code(dtype))
+                             float(softmax_scale), _dtype_code(dtype), int(partition), float(protect_pct))
         h = ctypes.c_void_p()
         _check(lib().httm_plan_create(ctypes.byref(self.params), ctypes.byref(h)))
         self.handle = h
@@ -156,7 +160,8 @@ class Plan:
                     n_s=w.n_s, n_t=w.n_t, q_ratio=w.q_ratio, kv_ratio=w.kv_ratio, outlier_pct=w.outlier_pct,
                     dtype=w.dtype, d_head=w.d_head, q_dst_stride=w.q_dst_stride,
                     kv_dst_stride=w.kv_dst_stride, softmax_scale=w.softmax_scale,
-                    block_order=getattr(w, "block_order", 0))
+                    block_order=getattr(w, "block_order", 0), partition=getattr(w, "partition", 0),
+                    protect_pct=getattr(w, "protect_pct", 10.0))
         args.update(kw)
         return Plan(**args)
 
@@ -282,6 +287,12 @@ def attention_dense(plan: Plan, q, k, v, ws=None, out=None, stream=None):
     return out
 
 
+def debug_items(plan: Plan) -> List[str]:
+    """The debug items that exist for ``plan``'s partition."""
+    skip = BLOCK_ITEMS if plan.params.partition == 1 else GA_ITEMS
+    return [it for it in DEBUG_ITEMS if it not in skip]
+
+
 def debug_read(plan: Plan, ws, item: str, stream=None, index: Optional[CachedIndex] = None):
     """Copy one intermediate of the last ``layer`` on ``ws`` to a numpy array.
 
@@ -292,7 +303,8 @@ def debug_read(plan: Plan, ws, item: str, stream=None, index: Optional[CachedInd
     n = ctypes.c_size_t()
     _check(lib().httm_debug_size(plan.handle, code, ctypes.byref(n)))
     dt = {"q_score": np.float32, "kv_score": np.float32, "delta": np.float32, "outlier": np.uint8,
-          "select": np.uint32}.get(item, np.int32)
+          "select": np.uint32, "ga_var": np.float32, "ga_role": np.uint8,
+          "ga_score": np.float32}.get(item, np.int32)
     arr = np.empty(n.value // np.dtype(dt).itemsize, dtype=dt)
     _check(lib().httm_debug_read(plan.handle, ws.data_ptr(), ctypes.byref(index.c) if index is not None else None,
                                  code, arr.ctypes.data, arr.nbytes, _stream_ptr(stream)))

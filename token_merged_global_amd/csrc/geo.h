@@ -26,6 +26,7 @@ namespace httm {
 constexpr int kD = 64;          // d_head
 constexpr int kMaxBlock = 4096; // largest supported block (fits LDS sorts)
 constexpr int kMaxHeads = 64;   // per-head prefix tables in LDS hold kMaxHeads + 1 entries
+constexpr int kMaxFrameHW = 4096;  // geometry-aware partition: one frame's patches rank in LDS
 
 enum Stream { kQ = 0, kK = 1 };
 

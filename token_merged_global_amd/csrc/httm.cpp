@@ -61,12 +61,15 @@ struct Layout {
   Region qsum, delta, mask, radix, base, ocnt;
   Region qt, kt, vt, o;
   Region kmax, fb, opart, lpart, mpart;  // attention: key norms, fallback queue, split partials
+  // geometry-aware partition (partition 1 only)
+  Region ga_var, ga_role, ga_fcnt, ga_foff, ga_tot, ga_slot, ga_dlist, ga_dslot, ga_slist;
+  Region ga_gdst, ga_gslot, ga_gscore, ga_cnt, ga_fill, ga_tmp;
   Region index;  // used when the caller passes no index buffer
   size_t total = 0;
 };
 
 struct IndexLayout {
-  Region header, k_members, k_off, fmembers, foff, slot, lenq, cu_q;
+  Region header, k_members, k_off, fmembers, foff, slot, lenq, cu_q, lenk;
   size_t total = 0;
 };
 
@@ -120,6 +123,7 @@ struct httm_plan {
   IndexHeader index_header;  // identity written at the start of every index this plan fills
   AttnTail attn_tail;
   int64_t attn_part_rows;  // rows of each key-split partial buffer
+  int32_t ga_kp = 0, ga_bound = 0, ga_max_src = 0;  // geometry-aware partition sizes
   std::vector<httm_block> blocks;
 };
 
@@ -152,6 +156,9 @@ httm_status build(const httm_params& p, httm_plan* pl) {
   if (p.d_head != kD) return fail(HTTM_ERR_UNSUPPORTED, "only d_head == 64 is built");
   if (p.heads > kMaxHeads) return fail(HTTM_ERR_UNSUPPORTED, "at most 64 heads (per-head prefix tables live in LDS)");
   if (p.block_order != 0 && p.block_order != 1) return fail(HTTM_ERR_INVALID_ARG, "block_order must be 0 or 1");
+  if (p.partition != 0 && p.partition != 1) return fail(HTTM_ERR_INVALID_ARG, "partition must be 0 or 1");
+  if (p.partition == 1 && !(p.protect_pct >= 0.0 && p.protect_pct <= 100.0))
+    return fail(HTTM_ERR_INVALID_ARG, "protect_pct must lie in [0, 100]");
   if ((int64_t)p.n_s * p.n_t > kMaxBlock) return fail(HTTM_ERR_UNSUPPORTED, "n_s * n_t must be <= 4096");
   const int64_t T = (int64_t)p.n_special + (int64_t)p.grid_h * p.grid_w;
   const int64_t N = (int64_t)p.frames * T;
@@ -233,6 +240,22 @@ httm_status build(const httm_params& p, httm_plan* pl) {
     g.nslots[st] = (int32_t)(slots[st] + (int64_t)g.F * g.nsp);
     g.nsrc[st] = (int32_t)srcs[st];
   }
+  if (p.partition == 1) {
+    // groups per head: every anchor (special, protected or destination) is
+    // one; the first frame's patches are all anchors, another frame has its
+    // protected patches and at most one destination per 2x2 cell
+    if (g.HW > kMaxFrameHW) return fail(HTTM_ERR_UNSUPPORTED, "geometry-aware partition: at most 4096 patches per frame");
+    if (N >= (1 << 20)) return fail(HTTM_ERR_UNSUPPORTED, "geometry-aware partition: at most 2^20 - 1 tokens");
+    const int64_t kp = (int64_t)std::floor(p.protect_pct / 100.0 * (double)g.HW + 1e-9);
+    const int64_t cells = (int64_t)((p.grid_h + 1) / 2) * ((p.grid_w + 1) / 2);
+    const int64_t bound = (int64_t)g.F * g.nsp + g.HW + (int64_t)(g.F - 1) * (kp + cells);
+    const int64_t bound_c = bound < N ? bound : N;
+    pl->ga_kp = (int32_t)kp;
+    pl->ga_bound = (int32_t)bound_c;
+    pl->ga_max_src = (int32_t)((int64_t)(g.F - 1) * g.HW);
+    g.nslots[kQ] = g.nslots[kK] = (int32_t)bound_c;
+    g.nsrc[kQ] = g.nsrc[kK] = pl->ga_max_src;
+  }
   pl->k_o = (int64_t)std::floor(p.outlier_pct * (double)p.heads * (double)N / 100.0 + 1e-9);
   pl->q_cap = (int64_t)p.heads * g.nslots[kQ] + pl->k_o;
   pl->lk_pad = ceil_div(g.nslots[kK], 64) * 64;
@@ -273,14 +296,34 @@ httm_status build(const httm_params& p, httm_plan* pl) {
     I.slot = b.take(4 * h * n);
     I.lenq = b.take(4 * h);
     I.cu_q = b.take(4 * (h + 1));
+    I.lenk = b.take(4 * h);  // keys per head (geometry-aware partition)
     I.total = b.cur;
   }
   {
     Builder b;
     Layout& Lw = pl->L;
-    for (int st = 0; st < 2; ++st) {
-      Lw.match[st] = b.take(4 * h * (size_t)g.nsrc[st]);
-      Lw.score[st] = b.take(4 * h * (size_t)g.nsrc[st]);
+    const bool ga = p.partition == 1;
+    for (int st = 0; st < 2; ++st) {  // block-local matches (partition 0)
+      Lw.match[st] = b.take(ga ? 0 : 4 * h * (size_t)g.nsrc[st]);
+      Lw.score[st] = b.take(ga ? 0 : 4 * h * (size_t)g.nsrc[st]);
+    }
+    if (ga) {
+      const size_t sh = 2 * h, F = (size_t)g.F;
+      Lw.ga_var = b.take(4 * sh * n);
+      Lw.ga_role = b.take(sh * n);
+      Lw.ga_fcnt = b.take(4 * sh * F * 3);
+      Lw.ga_foff = b.take(4 * sh * F * 3);
+      Lw.ga_tot = b.take(4 * sh * 3);
+      Lw.ga_slot = b.take(4 * sh * n);
+      Lw.ga_dlist = b.take(4 * sh * n);
+      Lw.ga_dslot = b.take(4 * sh * n);
+      Lw.ga_slist = b.take(4 * sh * n);
+      Lw.ga_gdst = b.take(4 * sh * n);
+      Lw.ga_gslot = b.take(4 * sh * n);
+      Lw.ga_gscore = b.take(4 * sh * n);
+      Lw.ga_cnt = b.take(4 * sh * (size_t)pl->ga_bound);
+      Lw.ga_fill = b.take(4 * sh * (size_t)pl->ga_bound);
+      Lw.ga_tmp = b.take(4 * sh * n);
     }
     Lw.q_members = b.take(4 * h * n);
     Lw.q_off = b.take(4 * h * ((size_t)g.nslots[kQ] + 1));
@@ -332,6 +375,8 @@ httm_status build(const httm_params& p, httm_plan* pl) {
     f.add((uint64_t)g.nslots[kQ]);
     f.add((uint64_t)g.nslots[kK]);
     f.add((uint64_t)pl->I.total);
+    f.add((uint64_t)p.partition);
+    f.addd(p.partition == 1 ? p.protect_pct : 0.0);
     IndexHeader& H = pl->index_header;
     std::memset(&H, 0, sizeof(H));
     H.w[0] = kIndexMagic;
@@ -440,6 +485,7 @@ httm_status attend_unmerge(const httm_plan* pl, void* ws, char* idx, const void*
   s.kmax = at<float>(ws, pl->L.kmax);
   s.fb_count = at<int>(ws, pl->L.fb);
   s.fb_list = at<int>(ws, pl->L.fb) + 1;
+  s.lenk = pl->p.partition == 1 ? reinterpret_cast<const int32_t*>(idx + pl->I.lenk.off) : nullptr;
   const int32_t* lenq = reinterpret_cast<const int32_t*>(idx + pl->I.lenq.off);
   stage_begin(HTTM_T_ATTN, st);
   CHECK_LAUNCH(launch_attention(dt, s, qt, at<void>(ws, pl->L.kt), at<void>(ws, pl->L.vt), lenq,
@@ -468,15 +514,22 @@ bool index_payload_ok(const httm_plan* pl, const char* buf) {
   const int64_t N = g.N, H = g.heads, lk = g.nslots[kK];
   auto arr = [&](const Region& r) { return reinterpret_cast<const int32_t*>(buf + r.off); };
   const int32_t *km = arr(I.k_members), *ko = arr(I.k_off), *fm = arr(I.fmembers), *fo = arr(I.foff);
-  const int32_t *sl = arr(I.slot), *lq = arr(I.lenq), *cu = arr(I.cu_q);
+  const int32_t *sl = arr(I.slot), *lq = arr(I.lenq), *cu = arr(I.cu_q), *lkh = arr(I.lenk);
+  const bool ga = pl->p.partition == 1;
   if (cu[0] != 0) return false;
   for (int64_t h = 0; h < H; ++h) {
     const int64_t len = lq[h];
     if (len < 1 || len > N || cu[h + 1] != cu[h] + len || cu[h + 1] > pl->q_cap) return false;
+    // keys of this head: every slot (block-local matching) or the first lenk
+    // slots, the rest empty (geometry-aware partition)
+    const int64_t nk = ga ? lkh[h] : lk;
+    if (nk < 1 || nk > lk) return false;
     const int32_t* o = ko + h * (lk + 1);
-    if (o[0] != 0 || o[lk] != N) return false;
-    for (int64_t j = 0; j < lk; ++j)
+    if (o[0] != 0 || o[nk] != N) return false;
+    for (int64_t j = 0; j < nk; ++j)
       if (o[j + 1] <= o[j]) return false;  // every merged key has a member
+    for (int64_t j = nk; j < lk; ++j)
+      if (o[j + 1] != N) return false;
     const int32_t* f = fo + h * (N + 1);
     if (f[0] != 0 || f[len] != N) return false;
     for (int64_t j = 0; j < len; ++j)
@@ -626,29 +679,70 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
                                 (int64_t)g.heads * g.nslots[kQ], st, &pl->index_header,
                                 reinterpret_cast<uint32_t*>(idx + I.header.off)));
 
-  // key branch on the library stream: matching, selection and merge of K / V
-  CHECK_LAUNCH(hipEventRecord(side->fork, st));
-  CHECK_LAUNCH(hipStreamWaitEvent(side->st, side->fork, 0));
-  stage_begin(HTTM_T_MERGE_KV, side->st);
-  CHECK_LAUNCH(launch_sim(g, dt, q, k, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
-                          at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), 2, side->st));
-  CHECK_LAUNCH(launch_select(g, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
-                             at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), cq, ck, 2, side->st));
-  CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
-                               ck.members, ck.off,
-                               at<void>(ws, L.kt), at<void>(ws, L.vt), at<float>(ws, L.kmax), side->st));
-  stage_end(HTTM_T_MERGE_KV, side->st);
-  CHECK_LAUNCH(hipEventRecord(side->join, side->st));
+  if (pl->p.partition == 1) {
+    // geometry-aware partition of both streams in one pass on the caller's
+    // stream, then the K / V means on the library stream
+    int32_t* lenk = reinterpret_cast<int32_t*>(idx + I.lenk.off);
+    GaShape gs{g.heads, g.N, g.T, g.nsp, pl->p.grid_h, pl->p.grid_w, g.F, pl->ga_kp, pl->ga_bound, pl->ga_max_src};
+    GaBuffers gb;
+    gb.var = at<float>(ws, L.ga_var);
+    gb.role = at<uint8_t>(ws, L.ga_role);
+    gb.fcnt = at<int32_t>(ws, L.ga_fcnt);
+    gb.foff = at<int32_t>(ws, L.ga_foff);
+    gb.tot = at<int32_t>(ws, L.ga_tot);
+    gb.slot = at<int32_t>(ws, L.ga_slot);
+    gb.dst_list = at<int32_t>(ws, L.ga_dlist);
+    gb.dst_slot = at<int32_t>(ws, L.ga_dslot);
+    gb.src_list = at<int32_t>(ws, L.ga_slist);
+    gb.gdst = at<int32_t>(ws, L.ga_gdst);
+    gb.gslot = at<int32_t>(ws, L.ga_gslot);
+    gb.gscore = at<float>(ws, L.ga_gscore);
+    gb.cnt = at<int32_t>(ws, L.ga_cnt);
+    gb.fill = at<int32_t>(ws, L.ga_fill);
+    gb.tmp = at<int32_t>(ws, L.ga_tmp);
+    gb.grp_q = cq.group;
+    gb.grp_k = ck.group;
+    gb.mem_q = cq.members;
+    gb.mem_k = ck.members;
+    gb.off_q = cq.off;
+    gb.off_k = ck.off;
+    gb.lenk = lenk;
+    stage_begin(HTTM_T_SIM, st);
+    CHECK_LAUNCH(launch_ga_partition(dt, gs, q, k, gb, st));
+    stage_end(HTTM_T_SIM, st);
+    CHECK_LAUNCH(hipEventRecord(side->fork, st));
+    CHECK_LAUNCH(hipStreamWaitEvent(side->st, side->fork, 0));
+    stage_begin(HTTM_T_MERGE_KV, side->st);
+    CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
+                                 ck.members, ck.off, at<void>(ws, L.kt), at<void>(ws, L.vt), at<float>(ws, L.kmax),
+                                 side->st, lenk));
+    stage_end(HTTM_T_MERGE_KV, side->st);
+    CHECK_LAUNCH(hipEventRecord(side->join, side->st));
+  } else {
+    // key branch on the library stream: matching, selection and merge of K / V
+    CHECK_LAUNCH(hipEventRecord(side->fork, st));
+    CHECK_LAUNCH(hipStreamWaitEvent(side->st, side->fork, 0));
+    stage_begin(HTTM_T_MERGE_KV, side->st);
+    CHECK_LAUNCH(launch_sim(g, dt, q, k, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
+                            at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), 2, side->st));
+    CHECK_LAUNCH(launch_select(g, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
+                               at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), cq, ck, 2, side->st));
+    CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
+                                 ck.members, ck.off,
+                                 at<void>(ws, L.kt), at<void>(ws, L.vt), at<float>(ws, L.kmax), side->st));
+    stage_end(HTTM_T_MERGE_KV, side->st);
+    CHECK_LAUNCH(hipEventRecord(side->join, side->st));
 
-  // query branch on the caller's stream
-  stage_begin(HTTM_T_SIM, st);
-  CHECK_LAUNCH(launch_sim(g, dt, q, k, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
-                          at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), 1, st));
-  stage_end(HTTM_T_SIM, st);
-  stage_begin(HTTM_T_SELECT, st);
-  CHECK_LAUNCH(launch_select(g, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
-                             at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), cq, ck, 1, st));
-  stage_end(HTTM_T_SELECT, st);
+    // query branch on the caller's stream
+    stage_begin(HTTM_T_SIM, st);
+    CHECK_LAUNCH(launch_sim(g, dt, q, k, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
+                            at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), 1, st));
+    stage_end(HTTM_T_SIM, st);
+    stage_begin(HTTM_T_SELECT, st);
+    CHECK_LAUNCH(launch_select(g, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
+                               at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), cq, ck, 1, st));
+    stage_end(HTTM_T_SELECT, st);
+  }
 
   stage_begin(HTTM_T_MERGE_Q, st);
   CHECK_LAUNCH(launch_merge_q(dt, g.heads, g.N, g.nslots[kQ], q, cq.members, cq.off,
@@ -712,7 +806,8 @@ httm_status httm_layer_cached(const httm_plan* pl, void* ws, size_t ws_bytes, co
   CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
                                reinterpret_cast<const int32_t*>(idx + I.k_members.off),
                                reinterpret_cast<const int32_t*>(idx + I.k_off.off),
-                               at<void>(ws, pl->L.kt), at<void>(ws, pl->L.vt), at<float>(ws, pl->L.kmax), side->st));
+                               at<void>(ws, pl->L.kt), at<void>(ws, pl->L.vt), at<float>(ws, pl->L.kmax), side->st,
+                               pl->p.partition == 1 ? reinterpret_cast<const int32_t*>(idx + I.lenk.off) : nullptr));
   stage_end(HTTM_T_MERGE_KV, side->st);
   CHECK_LAUNCH(hipEventRecord(side->join, side->st));
   stage_begin(HTTM_T_MERGE_Q, st);
@@ -753,6 +848,7 @@ httm_status httm_attention_dense(const httm_plan* pl, void* ws, size_t ws_bytes,
   a.q_capacity = (int64_t)g.heads * g.N;
   a.scale = pl->scale;
   a.split = 1;
+  a.lenk = nullptr;
   a.tail_split = 1;
   a.per_round = 0;
   a.tail_rows = 0;
@@ -773,7 +869,20 @@ httm_status httm_attention_dense(const httm_plan* pl, void* ws, size_t ws_bytes,
 httm_status httm_debug_size(const httm_plan* pl, int32_t item, size_t* bytes) {
   if (!pl || !bytes) return fail(HTTM_ERR_INVALID_ARG, "NULL argument");
   const size_t h = pl->g.heads, n = pl->g.N;
+  const bool ga = pl->p.partition == 1;
+  const bool ga_item = item == HTTM_DBG_GA_VAR || item == HTTM_DBG_GA_ROLE || item == HTTM_DBG_GA_MATCH ||
+                       item == HTTM_DBG_GA_SCORE || item == HTTM_DBG_KV_LEN;
+  const bool block_item = item == HTTM_DBG_Q_MATCH || item == HTTM_DBG_Q_SCORE || item == HTTM_DBG_KV_MATCH ||
+                          item == HTTM_DBG_KV_SCORE;
+  if (ga ? block_item : ga_item)
+    return fail(HTTM_ERR_UNSUPPORTED, ga ? "block-local matches do not exist under the geometry-aware partition"
+                                         : "geometry-aware items exist only under that partition");
   switch (item) {
+    case HTTM_DBG_GA_VAR:
+    case HTTM_DBG_GA_MATCH:
+    case HTTM_DBG_GA_SCORE: *bytes = 4 * 2 * h * n; break;
+    case HTTM_DBG_GA_ROLE: *bytes = 2 * h * n; break;
+    case HTTM_DBG_KV_LEN: *bytes = 4 * h; break;
     case HTTM_DBG_Q_MATCH:
     case HTTM_DBG_Q_SCORE: *bytes = 4 * h * pl->g.nsrc[kQ]; break;
     case HTTM_DBG_KV_MATCH:
@@ -817,6 +926,11 @@ httm_status httm_debug_read(const httm_plan* pl, const void* ws, const httm_inde
     case HTTM_DBG_CU_Q: src = idx + pl->I.cu_q.off; break;
     case HTTM_DBG_SELECT: src = base + L.radix.off + 4 * 3 * 2048; break;
     case HTTM_DBG_ATTN_FALLBACK: src = base + L.fb.off; break;
+    case HTTM_DBG_GA_VAR: src = base + L.ga_var.off; break;
+    case HTTM_DBG_GA_ROLE: src = base + L.ga_role.off; break;
+    case HTTM_DBG_GA_MATCH: src = base + L.ga_gdst.off; break;
+    case HTTM_DBG_GA_SCORE: src = base + L.ga_gscore.off; break;
+    case HTTM_DBG_KV_LEN: src = idx + pl->I.lenk.off; break;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   CHECK_LAUNCH(hipMemcpyAsync(host, src, need, hipMemcpyDeviceToHost, st));

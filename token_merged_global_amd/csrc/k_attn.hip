@@ -66,6 +66,7 @@ struct AttnArgs {
   float* lpart;            // [split][q_capacity] partial row sums
   float* mpart;            // [split][q_capacity] reference of each partial
   const float* kmax;       // [heads] max |k~|
+  const int32_t* lenk;     // [heads] keys per head when they vary (nullable: lk)
   int* fb_count;           // queued units for the exact kernel
   int* fb_list;
   const int32_t* lenq;
@@ -206,7 +207,7 @@ __device__ __forceinline__ bool locate(const AttnArgs& a, int u, int rows, Unit&
 struct UnitCtx {
   const uint16_t* Kp;
   const uint16_t* Vp;
-  int t0, t1, ntiles_all;
+  int t0, t1, ntiles_all, lk;  // key tiles of this unit, of the head; keys of the head
   uint32_t koff[8 / kNW], voff[8 / kNW];  // per-lane byte offsets of the tile copies
   bf16x8 bq[kQT][2];
   int qrow0, L;  // this lane's row of query tile 0 inside the head; head length
@@ -218,7 +219,8 @@ __device__ __forceinline__ void unit_setup(const AttnArgs& a, const Unit& u, int
   const uint16_t* Qp = reinterpret_cast<const uint16_t*>(a.q);
   c.Kp = reinterpret_cast<const uint16_t*>(a.k) + (size_t)u.head * a.k_rows * kD;
   c.Vp = reinterpret_cast<const uint16_t*>(a.vt) + (size_t)u.head * kD * a.vt_pitch;
-  c.ntiles_all = ceil_div(a.lk, kKeyTile);
+  c.lk = a.lenk ? a.lenk[u.head] : a.lk;
+  c.ntiles_all = ceil_div(c.lk, kKeyTile);
   // the copy of key tile t reads base(t) + these lane offsets: every key
   // buffer holds whole 64-key tiles (zero past lk), so no clamp is needed
 #pragma unroll
@@ -285,12 +287,12 @@ __device__ __forceinline__ void scores(const u32x4* sKb, const UnitCtx& c, const
   }
 }
 
-__device__ __forceinline__ void mask_tail(const AttnArgs& a, int t, int g, f32x4 (*sacc)[4]) {
+__device__ __forceinline__ void mask_tail(int lk, int t, int g, f32x4 (*sacc)[4]) {
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (t * kKeyTile + 32 * (kt >> 1) + 8 * g + 4 * (kt & 1) + r >= a.lk) {
+      if (t * kKeyTile + 32 * (kt >> 1) + 8 * g + 4 * (kt & 1) + r >= lk) {
 #pragma unroll
         for (int qt = 0; qt < kQT; ++qt) sacc[qt][kt][r] = -INFINITY;
       }
@@ -373,7 +375,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, const u32x4* sKb, c
                                           f32x4* osum, f32x4 (*oacc)[4]) {
   f32x4 sacc[kQT][4];
   scores(sKb, c, negm, g, l16, sacc);
-  if (MASK) mask_tail(a, t, g, sacc);
+  if (MASK) mask_tail(c.lk, t, g, sacc);
   bf16x8 bp[kQT][2];
   probs_only(sacc, bp);
   pv(sVb, bp, g, l16, oacc);
@@ -434,6 +436,15 @@ __global__ __launch_bounds__(kNW * 64) void attn_fast(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  if (c.t0 == c.t1) {
+    // a head with fewer key tiles than splits: this split adds nothing (l = 0,
+    // skipped by the combine); no tile load is left in flight
+    float lz[kQT];
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) lz[qt] = 0.f;
+    store_unit(a, u, c, g, oacc, lz, negm);
+    return;
+  }
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)(l16 == 0 ? 1.0f : 0.0f);
@@ -441,7 +452,7 @@ __global__ __launch_bounds__(kNW * 64) void attn_fast(AttnArgs a) {
   // only the head's last key tile can be partial: it runs outside the main
   // loop, so the loop body is one basic block and the exp2 of one key group
   // can overlap the score MFMAs of the next
-  const int tfull = (c.t1 == c.ntiles_all && a.lk % kKeyTile) ? c.t1 - 1 : c.t1;
+  const int tfull = (c.t1 == c.ntiles_all && c.lk % kKeyTile) ? c.t1 - 1 : c.t1;
   for (int t = c.t0; t < tfull; ++t) {
     const int buf = (t - c.t0) & 1;
     wait_vm();
@@ -504,7 +515,7 @@ __device__ __forceinline__ void exact_unit(const AttnArgs& a, int w, u32x4 (*sK)
     if (t + 1 < c.t1) load_tile(c, sK, sV, t + 1, buf ^ 1, wave);
     f32x4 sacc[kQT][4];
     scores(sK[buf], c, negm, g, l16, sacc);
-    if ((t + 1) * kKeyTile > a.lk) mask_tail(a, t, g, sacc);
+    if ((t + 1) * kKeyTile > c.lk) mask_tail(c.lk, t, g, sacc);
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
       const f32x4* sa = sacc[qt];
@@ -647,6 +658,7 @@ __global__ __launch_bounds__(kRowsF32) void attn_f32(AttnArgs a) {
   Unit u;
   if (!locate(a, blockIdx.x, kRowsF32, u)) return;
   const int head = u.head, cu = u.cu, L = u.L, tile = u.tile;
+  const int lk = a.lenk ? a.lenk[head] : a.lk;
   const float* Qp = reinterpret_cast<const float*>(a.q);
   const float* Kp = reinterpret_cast<const float*>(a.k) + (size_t)head * a.k_rows * kD;
   const float* Vp = reinterpret_cast<const float*>(a.vt) + (size_t)head * kD * a.vt_pitch;
@@ -659,16 +671,16 @@ __global__ __launch_bounds__(kRowsF32) void attn_f32(AttnArgs a) {
     acc[c] = 0.f;
   }
   float mrun = -INFINITY, lrun = 0.f;
-  for (int t0 = 0; t0 < a.lk; t0 += kKeyTile) {
+  for (int t0 = 0; t0 < lk; t0 += kKeyTile) {
     __syncthreads();
     for (int e = threadIdx.x; e < kKeyTile * kD; e += blockDim.x) {
       const int r = e / kD, c = e % kD;
-      const int key = t0 + r < a.lk ? t0 + r : a.lk - 1;
+      const int key = t0 + r < lk ? t0 + r : lk - 1;
       sK[r][c] = Kp[(size_t)key * kD + c];
       sV[e / kKeyTile][e % kKeyTile] = Vp[(size_t)(e / kKeyTile) * a.vt_pitch + t0 + e % kKeyTile];
     }
     __syncthreads();
-    const int nt = min(kKeyTile, a.lk - t0);
+    const int nt = min(kKeyTile, lk - t0);
     for (int r = 0; r < nt; ++r) {
       float s = 0.f;
       for (int c = 0; c < kD; ++c) s = fmaf(qv[c], sK[r][c], s);  // K~ carries scale*log2 e
@@ -778,6 +790,7 @@ AttnArgs make_args(int dtype, const AttnShape& s, const void* q, const void* k, 
   a.lenq = lenq;
   a.heads = s.heads;
   a.lk = s.lk;
+  a.lenk = s.lenk;
   a.k_rows = s.k_rows;
   a.vt_pitch = s.vt_pitch;
   a.lq_uniform = s.lq_uniform;

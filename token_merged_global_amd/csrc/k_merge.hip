@@ -133,7 +133,8 @@ __global__ __launch_bounds__(512) void merge_kv(int N, int lk, int lk_pad, float
                                                 const T* __restrict__ v,
                                                 const int32_t* __restrict__ members,
                                                 const int32_t* __restrict__ off, T* __restrict__ kt,
-                                                T* __restrict__ vt, float* __restrict__ kmax) {
+                                                T* __restrict__ vt, float* __restrict__ kmax,
+                                                const int32_t* __restrict__ lenk) {
   constexpr int R = KvStage<T>::kRows, NC = KvStage<T>::kChunks;  // NC 16-byte chunks per lane part
   __shared__ u32x4 sRow[2][R][8 * NC];  // [tensor][row][lane part * NC + chunk]
   __shared__ int sOf[65];
@@ -147,11 +148,13 @@ __global__ __launch_bounds__(512) void merge_kv(int N, int lk, int lk_pad, float
   const T* V = v + (size_t)head * N * kD;
   const int32_t* mem = members + (size_t)head * N;
   const int32_t* of = off + (size_t)head * (lk + 1);
-  const int nsl = min(64, lk - tile * 64);  // real slots of this tile (<= 0: padding tile)
+  // keys of this head: lk, or fewer when the partition is data dependent (lenk)
+  const int lkh = lenk ? lenk[head] : lk;
+  const int nsl = min(64, lkh - tile * 64);  // real slots of this tile (<= 0: padding tile)
   if (nsl > 0 && tid <= nsl) sOf[tid] = of[tile * 64 + tid];
   __syncthreads();
   const int mb = nsl > 0 ? sOf[0] : 0, me = nsl > 0 ? sOf[nsl] : 0;
-  const int m0 = slot < lk ? sOf[ls] : 0, m1 = slot < lk ? sOf[ls + 1] : 0;
+  const int m0 = slot < lkh ? sOf[ls] : 0, m1 = slot < lkh ? sOf[ls + 1] : 0;
   float acc[2][8];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(512) void merge_kv(int N, int lk, int lk_pad, float
     __syncthreads();  // before the next chunk overwrites the rows
   }
   float nmax = 0.f;
-  if (slot < lk) {
+  if (slot < lkh) {
     const float c = (float)(m1 - m0);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(512) void merge_kv(int N, int lk, int lk_pad, float
   }
   store8(kt + ((size_t)head * lk_pad + slot) * kD + part * 8, acc[0]);
   const float nrm = row_norm8<T>(acc[0]);
-  if (slot < lk) nmax = nrm;
+  if (slot < lkh) nmax = nrm;
   // transpose V~ through the (now free) staging buffer: float [64 channels][65]
   float(*sV)[65] = reinterpret_cast<float(*)[65]>(&sRow[0][0][0]);
   static_assert(sizeof(sRow) >= sizeof(float) * 64 * 65, "staging buffer holds the transpose");
@@ -582,11 +585,11 @@ __global__ __launch_bounds__(256) void prep_dense(int N, int pitch, float kscale
 
 hipError_t launch_merge_kv(int dtype, int heads, int N, int lk, int lk_pad, float kscale, const void* k,
                            const void* v, const int32_t* members, const int32_t* off, void* kt,
-                           void* vt, float* kmax, hipStream_t stream) {
+                           void* vt, float* kmax, hipStream_t stream, const int32_t* lenk) {
   const int grid = heads * (lk_pad / 64);
   HTTM_DISPATCH(dtype, hipLaunchKernelGGL(merge_kv<T>, dim3(grid), dim3(512), 0, stream, N, lk,
                                           lk_pad, kscale, (const T*)k, (const T*)v, members, off, (T*)kt,
-                                          (T*)vt, kmax));
+                                          (T*)vt, kmax, lenk));
   return hipGetLastError();
 }
 

@@ -29,9 +29,11 @@ hipError_t launch_select(const Geo& g, const int32_t* match_q, const float* scor
 // Means of K and V over the key partition: kt [h][lk_pad][64] (times kscale),
 // vt [h][64][lk_pad]; kmax[h] = max over the head's merged keys of |kt row|
 // (atomic max into a zeroed buffer).
+// lenk (nullable): per-head key counts when they vary (slots past them stay
+// zero rows); the offsets keep lk + 1 entries per head.
 hipError_t launch_merge_kv(int dtype, int heads, int N, int lk, int lk_pad, float kscale, const void* k,
                            const void* v, const int32_t* members, const int32_t* off, void* kt,
-                           void* vt, float* kmax, hipStream_t stream);
+                           void* vt, float* kmax, hipStream_t stream, const int32_t* lenk = nullptr);
 
 // Query group sums (fp32) and deviation of every query to its group mean;
 // also adds every deviation to hist0 (bits 31..21 of its pattern, the first
@@ -89,9 +91,47 @@ struct AttnShape {
   float* lpart;            // [attention_partial_rows]
   float* mpart;            // [attention_partial_rows]
   const float* kmax;       // [heads] max |k row|
+  const int32_t* lenk;     // [heads] keys per head when they vary (nullable: lk for every head)
   int* fb_count;           // [1] units queued for the exact kernel (zeroed by launch_zero_init)
   int* fb_list;            // [units]
 };
+// Geometry-aware three-class partition (variance map, roles, global match)
+// of both streams, producing per head the same CSR groups as the block-local
+// matching: members / offsets over `bound` slots (trailing slots empty) and
+// the slot of every token.
+struct GaShape {
+  int heads, N, Tf, nsp, H, W, F;
+  int k_protect;  // protected patches per frame
+  int bound;      // slots per head (upper bound of anchors)
+  int max_src;    // upper bound of sources per head
+};
+struct GaBuffers {
+  float* var;          // [2][h][N] variance map
+  uint8_t* role;       // [2][h][N]
+  int32_t* fcnt;       // [2][h][F][3] per frame: anchors, destinations, sources
+  int32_t* foff;       // [2][h][F][3] exclusive prefixes
+  int32_t* tot;        // [2][h][3] totals (anchors = groups)
+  int32_t* slot;       // [2][h][N] slot of anchors, -1 for sources
+  int32_t* dst_list;   // [2][h][N] destination tokens (ascending)
+  int32_t* dst_slot;   // [2][h][N] their slots
+  int32_t* src_list;   // [2][h][N] source tokens (ascending)
+  int32_t* gdst;       // [2][h][N] matched destination token of each source
+  int32_t* gslot;      // [2][h][N] its slot
+  float* gscore;       // [2][h][N] its cosine
+  int32_t* cnt;        // [2][h][bound] members per slot
+  int32_t* fill;       // [2][h][bound] placement counters
+  int32_t* tmp;        // [2][h][N] members in placement order
+  int32_t* grp_q;      // [h][N] slot of every token (query stream)
+  int32_t* grp_k;
+  int32_t* mem_q;      // [h][N] members, grouped by slot, ascending inside a slot
+  int32_t* mem_k;
+  int32_t* off_q;      // [h][bound + 1]
+  int32_t* off_k;
+  int32_t* lenk;       // [h] groups of the key stream (keys per head)
+};
+hipError_t launch_ga_partition(int dtype, const GaShape& s, const void* q, const void* k, const GaBuffers& b,
+                               hipStream_t stream);
+
 // Key splits for a layer of q_capacity packed rows; rows per work unit.
 int attention_split(int64_t q_capacity, int heads);
 int attention_rows_per_unit();

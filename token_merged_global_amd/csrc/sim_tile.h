@@ -1,0 +1,73 @@
+// Cosine-argmax tile of 64 destinations against 64 sources per wave, shared
+// by the block-local similarity kernel and the geometry-aware global match.
+// Argmax keys: see the similarity kernel's header comment.
+#pragma once
+#include "common.h"
+
+namespace httm {
+namespace {
+
+// 16-byte chunk c of LDS row r sits at chunk c ^ swz(r): the 16 consecutive
+// rows one A-operand read touches land in distinct bank groups.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// max(a, max(b, c)) on unsigned values lowers to one v_max3_u32.
+__device__ __forceinline__ uint32_t umax3(uint32_t a, uint32_t b, uint32_t c) {
+  const uint32_t m = b > c ? b : c;
+  return a > m ? a : m;
+}
+
+// acc + sum of squares of 8 bf16 values, two per v_dot2.
+__device__ __forceinline__ float sumsq8(const bf16x8 x, float acc) {
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const bf16x2 p = {x[e], x[e + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc, false);
+  }
+  return acc;
+}
+
+// Order of (key without position bits, destination): larger key, then smaller destination.
+__device__ __forceinline__ void take_better(uint32_t& kb, int& db, uint32_t ko, int dob) {
+  if (ko > kb || (ko == kb && dob < db)) {
+    kb = ko;
+    db = dob;
+  }
+}
+
+// Keys of one 64-destination tile: tm[c] = max over the lane's 16
+// candidates of source column tile c (position bits included).  MASK: only
+// destinations below nvalid (tile-relative) count.
+template <bool MASK>
+__device__ __forceinline__ void tile_keys(const u32x4* sDb, const float* sInvb, const bf16x8 (&bs)[4][2],
+                                          const float (&off)[4], int lg, int l16, int nvalid, uint32_t (&tm)[4]) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int arow = dt * 16 + l16;
+    const bf16x8 a0 = __builtin_bit_cast(bf16x8, sDb[arow * 8 + ((0 + lg) ^ swz(arow))]);
+    const bf16x8 a1 = __builtin_bit_cast(bf16x8, sDb[arow * 8 + ((4 + lg) ^ swz(arow))]);
+    const f32x4 inv4 = *reinterpret_cast<const f32x4*>(&sInvb[dt * 16 + 4 * lg]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bs[c][0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bs[c][1], acc, 0, 0, 0);
+      uint32_t key[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = fmaf(acc[r], inv4[r], off[c]);
+        key[r] = (__float_as_uint(v) & ~15u) | (uint32_t)(15 - (4 * dt + r));
+        if (MASK && dt * 16 + 4 * lg + r >= nvalid) key[r] = 0u;
+      }
+      if (dt == 0) {
+        tm[c] = umax3(key[0], key[1], key[2] > key[3] ? key[2] : key[3]);
+      } else {
+        tm[c] = umax3(tm[c], key[0], key[1]);
+        tm[c] = umax3(tm[c], key[2], key[3]);
+      }
+    }
+  }
+}
+
+}  // namespace
+}  // namespace httm
