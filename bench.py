@@ -69,6 +69,10 @@ def measured_traffic(workload: str, dtype: str):
 
 
 def describe(w) -> str:
+    if getattr(w, "partition", 0) == 1:
+        return (f"{w.name}: {w.frames} frames x ({w.grid_h}x{w.grid_w}+{w.n_special}) = {w.n_tokens} tokens, "
+                f"{w.heads} heads x {w.d_head}, {w.dtype}, geometry-aware partition ({w.protect_pct:g}% "
+                f"protected, global match) + {w.outlier_pct:g}% outliers")
     return (f"{w.name}: {w.frames} frames x ({w.grid_h}x{w.grid_w}+{w.n_special}) = {w.n_tokens} tokens, "
             f"{w.heads} heads x {w.d_head}, {w.dtype}, n_s={w.n_s} n_t={w.n_t}, q merge {w.q_ratio:g} + "
             f"{w.outlier_pct:g}% outliers, kv merge {w.kv_ratio:g}")
@@ -159,6 +163,9 @@ def main():
     ap.add_argument("--outlier-pct", type=float, default=None, help="override the workload's outlier budget")
     ap.add_argument("--cached-layers", type=int, default=None,
                     help="also time layers that reuse the merge indices (default: workload layers - 1)")
+    ap.add_argument("--partition", default="httm", choices=["httm", "ga"],
+                    help="httm: temporal blocks (default); ga: geometry-aware three-class partition")
+    ap.add_argument("--protect-pct", type=float, default=10.0, help="ga: percent of each frame's patches protected")
     ap.add_argument("--sweep-blocks", action="store_true",
                     help="instead of the benchmark: block shape / stacking sweep (one JSON line per shape)")
     args = ap.parse_args()
@@ -179,6 +186,9 @@ def main():
                                 ("outlier_pct", args.outlier_pct)) if v is not None}
     if over:
         w = w.with_(**over)
+    ga = args.partition == "ga"
+    if ga:
+        w = w.with_(name=w.name + "_ga", partition=1, protect_pct=args.protect_pct)
     n_cached = (w.layers - 1) if args.cached_layers is None else args.cached_layers
     log(f"[bench] generating {describe(w)}")
     x = gen.layer_inputs(w, seed=args.seed)
@@ -226,7 +236,17 @@ def main():
     cu = H.debug_read(plan, ws, "cu_q")
     lq = np.diff(cu)
     lk = plan.info["kv_len"]
-    attn_flop = 4.0 * w.d_head * lk * float(lq.sum())
+    lkh = H.debug_read(plan, ws, "kv_len").astype(np.float64) if ga else np.full(w.heads, float(lk))
+    attn_flop = 4.0 * w.d_head * float((lkh * lq).sum())
+    ga_info = None
+    if ga:
+        # global match: 2*d*|S|*|D| per head and stream
+        role = H.debug_read(plan, ws, "ga_role").reshape(2, w.heads, -1)
+        ns = (role == 0).sum(axis=2).astype(np.float64)
+        nd = (role == 1).sum(axis=2).astype(np.float64)
+        ga_info = {"match_flop": float((2.0 * w.d_head * ns * nd).sum()),
+                   "sources_per_head_mean": float(ns.mean()), "destinations_per_head_mean": float(nd.mean()),
+                   "kv_len_min": int(lkh.min()), "kv_len_max": int(lkh.max())}
     attn_ms = attn_t["attn"]
     peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     achieved = attn_flop / (attn_ms * 1e-3) / 1e12
@@ -304,16 +324,19 @@ def main():
         "data": "synthetic: seeded VGGT-shaped tokens (smoothed spatial field + per-frame drift + noise), inputs resident in HBM",
         "config": {"workload": describe(w), "frames": w.frames, "tokens": w.n_tokens, "heads": w.heads,
                    "d_head": w.d_head, "n_s": w.n_s, "n_t": w.n_t, "q_ratio": w.q_ratio, "kv_ratio": w.kv_ratio,
-                   "outlier_pct": w.outlier_pct, "seed": args.seed},
+                   "outlier_pct": w.outlier_pct, "seed": args.seed,
+                   **({"partition": "geometry-aware", "protect_pct": w.protect_pct} if ga else {})},
         "roofline": {"bound": "mfma", "kernel": "attn_fast" if w.dtype == "bf16" else "attn_f32",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": measured_traffic(w.name, "bf16" if w.dtype == "bf16" else "f32"),
                      "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
-                     "algorithmic": f"4*d*L_k*sum_h(L_q,h) = 4*{w.d_head}*{lk}*{int(lq.sum())} = {attn_flop:.4g} FLOP per launch",
+                     "algorithmic": (f"4*d*sum_h(L_k,h*L_q,h) = {attn_flop:.4g} FLOP per launch" if ga else
+                                     f"4*d*L_k*sum_h(L_q,h) = 4*{w.d_head}*{lk}*{int(lq.sum())} = {attn_flop:.4g} FLOP per launch"),
                      "avg_launch_ms": attn_ms, "launches_timed": calls},
         "cpu_baseline": cpu,
         "stages_ms": stages,
         "cached": cached,
+        "geometry_aware": ga_info,
         "speedup_vs_unmerged_attention": (dense_ms / ms_step) if dense_ms else None,
         "unmerged_attention_ms": dense_ms,
         "lengths": {"kv_len": lk, "q_len_mean": float(lq.mean()), "q_len_min": int(lq.min()),

@@ -63,7 +63,7 @@ struct Layout {
   Region kmax, fb, opart, lpart, mpart;  // attention: key norms, fallback queue, split partials
   // geometry-aware partition (partition 1 only)
   Region ga_var, ga_role, ga_fcnt, ga_foff, ga_tot, ga_slot, ga_dlist, ga_dslot, ga_slist;
-  Region ga_gdst, ga_gslot, ga_gscore, ga_cnt, ga_fill, ga_tmp;
+  Region ga_gdst, ga_gslot, ga_gscore, ga_best, ga_snorm, ga_cnt, ga_fill, ga_tmp, ga_dg, ga_dinv;
   Region index;  // used when the caller passes no index buffer
   size_t total = 0;
 };
@@ -124,6 +124,7 @@ struct httm_plan {
   AttnTail attn_tail;
   int64_t attn_part_rows;  // rows of each key-split partial buffer
   int32_t ga_kp = 0, ga_bound = 0, ga_max_src = 0;  // geometry-aware partition sizes
+  int32_t ga_dpitch = 0;  // gathered destination rows per (stream, head)
   std::vector<httm_block> blocks;
 };
 
@@ -253,6 +254,9 @@ httm_status build(const httm_params& p, httm_plan* pl) {
     pl->ga_kp = (int32_t)kp;
     pl->ga_bound = (int32_t)bound_c;
     pl->ga_max_src = (int32_t)((int64_t)(g.F - 1) * g.HW);
+    // destinations: the first frame's unprotected patches, one per 2x2 cell elsewhere
+    const int64_t max_dst = (g.HW - kp) + (int64_t)(g.F - 1) * cells;
+    pl->ga_dpitch = (int32_t)(((max_dst < 1 ? 1 : max_dst) + 63) / 64 * 64);
     g.nslots[kQ] = g.nslots[kK] = (int32_t)bound_c;
     g.nsrc[kQ] = g.nsrc[kK] = pl->ga_max_src;
   }
@@ -321,9 +325,14 @@ httm_status build(const httm_params& p, httm_plan* pl) {
       Lw.ga_gdst = b.take(4 * sh * n);
       Lw.ga_gslot = b.take(4 * sh * n);
       Lw.ga_gscore = b.take(4 * sh * n);
+      Lw.ga_best = b.take(8 * sh * n);
+      Lw.ga_snorm = b.take(4 * sh * n);
       Lw.ga_cnt = b.take(4 * sh * (size_t)pl->ga_bound);
       Lw.ga_fill = b.take(4 * sh * (size_t)pl->ga_bound);
       Lw.ga_tmp = b.take(4 * sh * n);
+      const bool bf = p.dtype == HTTM_BF16;
+      Lw.ga_dg = b.take(bf ? 2 * sh * (size_t)pl->ga_dpitch * kD : 0);
+      Lw.ga_dinv = b.take(bf ? 4 * sh * (size_t)pl->ga_dpitch : 0);
     }
     Lw.q_members = b.take(4 * h * n);
     Lw.q_off = b.take(4 * h * ((size_t)g.nslots[kQ] + 1));
@@ -683,7 +692,8 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
     // geometry-aware partition of both streams in one pass on the caller's
     // stream, then the K / V means on the library stream
     int32_t* lenk = reinterpret_cast<int32_t*>(idx + I.lenk.off);
-    GaShape gs{g.heads, g.N, g.T, g.nsp, pl->p.grid_h, pl->p.grid_w, g.F, pl->ga_kp, pl->ga_bound, pl->ga_max_src};
+    GaShape gs{g.heads, g.N,         g.T,          g.nsp,          pl->p.grid_h,
+               pl->p.grid_w, g.F, pl->ga_kp, pl->ga_bound, pl->ga_max_src, pl->ga_dpitch};
     GaBuffers gb;
     gb.var = at<float>(ws, L.ga_var);
     gb.role = at<uint8_t>(ws, L.ga_role);
@@ -697,6 +707,10 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
     gb.gdst = at<int32_t>(ws, L.ga_gdst);
     gb.gslot = at<int32_t>(ws, L.ga_gslot);
     gb.gscore = at<float>(ws, L.ga_gscore);
+    gb.dg = at<uint16_t>(ws, L.ga_dg);
+    gb.dinv = at<float>(ws, L.ga_dinv);
+    gb.best = at<uint64_t>(ws, L.ga_best);
+    gb.snorm = at<float>(ws, L.ga_snorm);
     gb.cnt = at<int32_t>(ws, L.ga_cnt);
     gb.fill = at<int32_t>(ws, L.ga_fill);
     gb.tmp = at<int32_t>(ws, L.ga_tmp);

@@ -257,15 +257,14 @@ __device__ __forceinline__ void unit_setup(const AttnArgs& a, const Unit& u, int
 // Copy key tile t (64 keys of K~ and V~^T) into LDS buffer buf.  Each wave
 // issues 8/kNW + 8/kNW copies of 64 x 16 bytes; lane i fetches the global
 // chunk that belongs at its swizzled LDS slot (offsets fixed per lane).
-__device__ __forceinline__ void load_tile(const UnitCtx& c, u32x4 (*sK)[kKeyTile * 8], u32x4 (*sV)[kD * 8], int t,
-                                          int buf, int wave) {
+__device__ __forceinline__ void load_tile(const UnitCtx& c, u32x4* sKb, u32x4* sVb, int t, int wave) {
   const char* kb = reinterpret_cast<const char*>(c.Kp) + (size_t)t * (kKeyTile * kD * 2);
   const char* vb = reinterpret_cast<const char*>(c.Vp) + (size_t)t * (kKeyTile * 2);
 #pragma unroll
   for (int rd = 0; rd < 8 / kNW; ++rd) {
     const int slot = (rd * kNW + wave) * 64;
-    lds_copy16(kb + c.koff[rd], &sK[buf][slot]);
-    lds_copy16(vb + c.voff[rd], &sV[buf][slot]);
+    lds_copy16(kb + c.koff[rd], sKb + slot);
+    lds_copy16(vb + c.voff[rd], sVb + slot);
   }
 }
 
@@ -413,9 +412,11 @@ __device__ __forceinline__ void store_unit(const AttnArgs& a, const Unit& u, con
 }
 
 // Fast path: the Cauchy-Schwarz reference, no running max.
-__global__ __launch_bounds__(kNW * 64) void attn_fast(AttnArgs a) {
-  __shared__ u32x4 sK[2][kKeyTile * 8];
-  __shared__ u32x4 sV[2][kD * 8];
+__global__ __launch_bounds__(kNW * 64, 2) void attn_fast(AttnArgs a) {
+  // the two tile buffers are separate LDS objects, so the compiler can see
+  // that reads of one do not wait for the direct-to-LDS copies into the other
+  __shared__ u32x4 sK0[kKeyTile * 8], sK1[kKeyTile * 8];
+  __shared__ u32x4 sV0[kD * 8], sV1[kD * 8];
   const int w = blockIdx.x;
   Unit u;
   if (!schedule(a, w, u)) return;
@@ -448,23 +449,37 @@ __global__ __launch_bounds__(kNW * 64) void attn_fast(AttnArgs a) {
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)(l16 == 0 ? 1.0f : 0.0f);
-  load_tile(c, sK, sV, c.t0, 0, wave);
+  load_tile(c, sK0, sV0, c.t0, wave);
   // only the head's last key tile can be partial: it runs outside the main
   // loop, so the loop body is one basic block and the exp2 of one key group
-  // can overlap the score MFMAs of the next
+  // can overlap the score MFMAs of the next.  Unrolled by two so that every
+  // tile names its buffer statically.
   const int tfull = (c.t1 == c.ntiles_all && c.lk % kKeyTile) ? c.t1 - 1 : c.t1;
-  for (int t = c.t0; t < tfull; ++t) {
-    const int buf = (t - c.t0) & 1;
+  auto step = [&](int t, const u32x4* sKc, const u32x4* sVc, u32x4* sKn, u32x4* sVn) {
+    __builtin_amdgcn_sched_barrier(0);  // the previous tile's work stays before the wait
     wait_vm();
     __syncthreads();
-    if (t + 1 < c.t1) load_tile(c, sK, sV, t + 1, buf ^ 1, wave);
-    tile_step<false>(a, sK[buf], sV[buf], c, negm, g, l16, t, ones, osum, oacc);
+    if (t + 1 < c.t1) load_tile(c, sKn, sVn, t + 1, wave);
+    tile_step<false>(a, sKc, sVc, c, negm, g, l16, t, ones, osum, oacc);
+  };
+  int t = c.t0;
+  for (; t + 1 < tfull; t += 2) {
+    step(t, sK0, sV0, sK1, sV1);
+    step(t + 1, sK1, sV1, sK0, sV0);
   }
-  if (tfull < c.t1) {
-    const int t = tfull, buf = (t - c.t0) & 1;
+  if (t < tfull) {
+    step(t, sK0, sV0, sK1, sV1);
+    ++t;
+  }
+  if (t < c.t1) {
+    // the partial tile sits in buffer (t - t0) & 1
+    __builtin_amdgcn_sched_barrier(0);
     wait_vm();
     __syncthreads();
-    tile_step<true>(a, sK[buf], sV[buf], c, negm, g, l16, t, ones, osum, oacc);
+    if ((t - c.t0) & 1)
+      tile_step<true>(a, sK1, sV1, c, negm, g, l16, t, ones, osum, oacc);
+    else
+      tile_step<true>(a, sK0, sV0, c, negm, g, l16, t, ones, osum, oacc);
   }
   float lsum[kQT];
   bool tiny = false;
@@ -507,12 +522,12 @@ __device__ __forceinline__ void exact_unit(const AttnArgs& a, int w, u32x4 (*sK)
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  load_tile(c, sK, sV, c.t0, 0, wave);
+  load_tile(c, sK[0], sV[0], c.t0, wave);
   for (int t = c.t0; t < c.t1; ++t) {
     const int buf = (t - c.t0) & 1;
     wait_vm();
     __syncthreads();
-    if (t + 1 < c.t1) load_tile(c, sK, sV, t + 1, buf ^ 1, wave);
+    if (t + 1 < c.t1) load_tile(c, sK[buf ^ 1], sV[buf ^ 1], t + 1, wave);
     f32x4 sacc[kQT][4];
     scores(sK[buf], c, negm, g, l16, sacc);
     if ((t + 1) * kKeyTile > c.lk) mask_tail(c.lk, t, g, sacc);

@@ -23,6 +23,8 @@
 // ga_place (every token into its slot's range, any order) -> ga_rank (each
 // member's place inside its range = members with a smaller id).  No sort
 // and no memset: the result does not depend on the order of the atomics.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "sim_tile.h"
@@ -57,34 +59,75 @@ __device__ __forceinline__ void row3(const float* l, const float* c, const float
   }
 }
 
-// Variance map: one thread per patch.  Per channel octet: the three rows'
-// sums (x and x*x) left to right, then top to bottom; var = s2/cnt -
-// (s1/cnt)^2 summed over channels in ascending order, divided by 64.
+// Variance map.  A workgroup takes a tile of R x C patches of one frame
+// (R * C <= 256, one thread per patch) and stages the tile with a one-patch
+// halo in LDS (coalesced 16-byte loads along each grid row).  Per channel
+// octet: the three rows' sums (x and x*x) left to right, then top to
+// bottom; var = s2/cnt - (s1/cnt)^2 summed over channels in ascending order,
+// divided by 64.  Specials get 0.
+constexpr int kVarMaxStage = 340;  // staged patches: (R + 2) * (C + 2) over the tile shapes the host picks
+template <typename T>
+struct VarStage {
+  static constexpr int kChunks = kD * (int)sizeof(T) / 16;  // 16-byte chunks of one patch
+  static constexpr int kPitch = kChunks + 1;               // padded row pitch (16-byte units)
+};
+
+template <typename T>
+__device__ __forceinline__ void lds_load8(const u32x4* row, int c8, float* x) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x4 a = row[c8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(a[i] << 16);
+      x[2 * i + 1] = __uint_as_float(a[i] & 0xFFFF0000u);
+    }
+  } else {
+    const u32x4 a = row[2 * c8], b = row[2 * c8 + 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = __uint_as_float(a[i]);
+      x[4 + i] = __uint_as_float(b[i]);
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void ga_variance(const T* __restrict__ q, const T* __restrict__ k, int heads,
-                                                   int N, int Tf, int nsp, int H, int W,
+                                                   int N, int Tf, int nsp, int H, int W, int R, int C, int tiles_x,
                                                    float* __restrict__ var) {
-  const int HW = H * W;
-  const int j = blockIdx.x * 256 + threadIdx.x;
+  constexpr int P = VarStage<T>::kPitch, NC = VarStage<T>::kChunks;
+  __shared__ u32x4 sX[kVarMaxStage * P];
   const int f = blockIdx.y;
   const int sh = blockIdx.z, st = sh / heads, head = sh % heads;
-  if (j < nsp) var[((size_t)st * heads + head) * N + (size_t)f * Tf + j] = 0.f;  // specials: no score
-  if (j >= HW) return;
-  const T* X = (st == 0 ? q : k) + (size_t)head * N * kD;
-  const int y = j / W, xx = j - y * W;
-  const bool hl = xx > 0, hr = xx + 1 < W, hu = y > 0, hd = y + 1 < H;
+  const int tid = threadIdx.x;
+  float* V = var + ((size_t)st * heads + head) * N + (size_t)f * Tf;
+  if (blockIdx.x == 0)
+    for (int j = tid; j < nsp; j += 256) V[j] = 0.f;  // specials: no score
+  const int y0 = (blockIdx.x / tiles_x) * R, x0 = (blockIdx.x % tiles_x) * C;
+  const int sw = C + 2, nst = (R + 2) * sw;
+  const u32x4* X = reinterpret_cast<const u32x4*>((st == 0 ? q : k) + ((size_t)head * N + (size_t)f * Tf + nsp) * kD);
+  for (int e = tid; e < nst * NC; e += 256) {
+    const int i = e / NC, c = e - i * NC;
+    const int yy = y0 - 1 + i / sw, xx = x0 - 1 + i % sw;
+    if (yy >= 0 && yy < H && xx >= 0 && xx < W) sX[i * P + c] = X[(size_t)(yy * W + xx) * NC + c];
+  }
+  __syncthreads();
+  const int ly = tid / C, lx = tid - ly * C;
+  const int y = y0 + ly, x = x0 + lx;
+  if (ly >= R || y >= H || x >= W) return;
+  const bool hl = x > 0, hr = x + 1 < W, hu = y > 0, hd = y + 1 < H;
   const float cnt = (float)((1 + hl + hr) * (1 + hu + hd));
-  const T* base = X + ((size_t)f * Tf + nsp) * kD;
+  const int centre = (ly + 1) * sw + lx + 1;
   float acc = 0.f;
   for (int c8 = 0; c8 < 8; ++c8) {
     float s1[8], s2[8];
     for (int dy = -1; dy <= 1; ++dy) {
       if ((dy < 0 && !hu) || (dy > 0 && !hd)) continue;
-      const T* row = base + (size_t)((y + dy) * W + xx) * kD + c8 * 8;
+      const int ci = centre + dy * sw;
       float a[8], b[8], c[8], a2[8], b2[8], c2[8];
-      load8(row, b);
-      if (hl) load8(row - kD, a);
-      if (hr) load8(row + kD, c);
+      lds_load8<T>(&sX[ci * P], c8, b);
+      if (hl) lds_load8<T>(&sX[(ci - 1) * P], c8, a);
+      if (hr) lds_load8<T>(&sX[(ci + 1) * P], c8, c);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         a2[e] = hl ? __fmul_rn(a[e], a[e]) : 0.f;
@@ -114,7 +157,7 @@ __global__ __launch_bounds__(256) void ga_variance(const T* __restrict__ q, cons
       acc = __fadd_rn(acc, __fsub_rn(s2[e] / cnt, __fmul_rn(m, m)));
     }
   }
-  var[((size_t)st * heads + head) * N + (size_t)f * Tf + nsp + j] = acc / 64.0f;
+  V[nsp + y * W + x] = acc / 64.0f;
 }
 
 constexpr int kRoleThreads = 256;
@@ -285,7 +328,7 @@ __global__ __launch_bounds__(kRoleThreads) void ga_slots(const uint8_t* __restri
                                                           int32_t* __restrict__ dst_slot,
                                                           int32_t* __restrict__ src_list, int32_t* __restrict__ gdst,
                                                           float* __restrict__ gscore, int32_t* __restrict__ cnt,
-                                                          int32_t* __restrict__ fill) {
+                                                          int32_t* __restrict__ fill, uint64_t* __restrict__ best) {
   __shared__ int wsum[kRoleThreads / 64];
   const int f = blockIdx.x, sh = blockIdx.y;
   const size_t hb = (size_t)sh * N;
@@ -321,14 +364,21 @@ __global__ __launch_bounds__(kRoleThreads) void ga_slots(const uint8_t* __restri
       ++ra;
     } else {
       slot[hb + tok] = -1;
+      best[hb + tok] = 0;  // below every packed (key, destination)
       src_list[hb + rs++] = tok;
     }
   }
 }
 
-// Global match, bf16: per (stream, head, 256 sources) like the block-local
-// similarity kernel, with source and destination rows taken from the lists.
+// Global match, bf16: per (stream, head, 256 sources, destination split)
+// like the block-local similarity kernel, with source and destination rows
+// taken from the lists.  Each split's best (key, destination) of a source
+// goes to one 64-bit atomic max: larger key, then smaller destination index,
+// whatever the order of the splits.
 constexpr int kSrcPerWg = 256, kDstTile = 64;
+// Destination splits per source chunk: four times the workgroups of one
+// split each, so the last round of workgroups is a small part of the launch.
+constexpr int kDstSplits = 4;
 struct GaMatchArgs {
   const void* x[2];
   int heads, N, chunks;
@@ -336,28 +386,148 @@ struct GaMatchArgs {
   const int32_t* dst_list;  // [2][h][N]
   const int32_t* dst_slot;
   const int32_t* src_list;
-  int32_t* gdst;            // [2][h][N] matched destination token (sources)
-  int32_t* gslot;           // [2][h][N] its slot
-  float* gscore;            // [2][h][N] cosine
-  int32_t* cnt;             // [2][h][bound] members per slot (atomic adds)
-  int bound;
+  uint64_t* best;           // [2][h][N] per source: packed (key, ~destination index), atomic max
+  float* snorm;             // [2][h][N] per source: squared norm (bf16) / inverse norm (fp32)
+  int dsplit;               // destination splits per source chunk
+  const uint16_t* dg;       // bf16: [2][h][dpitch][64] gathered destination rows
+  const float* dinv;        // bf16: [2][h][dpitch] their inverse norms
+  int dpitch;               // rows per (stream, head), a multiple of 64
 };
 
+// Positive offset of a source's keys (above |score| * |source|) from its
+// squared norm; the score is (key - off) / |source|.
+__device__ __forceinline__ float ga_off(float ss) { return __builtin_amdgcn_sqrtf(ss) * (1.0f + 0x1p-10f); }
+
+// Destination rows of every (stream, head) gathered into one contiguous
+// matrix (rows past the head's destinations up to the next 64 are zero), with
+// the inverse norm of each row: the match then streams whole tiles with
+// direct-to-LDS copies and no index indirection.  Four lanes per row; the
+// squared norm adds each lane's 16 values, then lanes 0+1 and 2+3, then both.
+__global__ __launch_bounds__(256) void ga_gather(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                 int heads, int N, int dpitch, const int32_t* __restrict__ tot,
+                                                 const int32_t* __restrict__ dst_list, uint16_t* __restrict__ dg,
+                                                 float* __restrict__ dinv) {
+  const int sh = blockIdx.y, st = sh / heads, head = sh % heads;
+  const int nd = tot[sh * 3 + 1];
+  const int d = blockIdx.x * 64 + (threadIdx.x >> 2), part = threadIdx.x & 3;
+  if (blockIdx.x * 64 >= nd) return;  // whole workgroups past the last tile
+  u32x4 v0 = u32x4{0u, 0u, 0u, 0u}, v1 = v0;
+  if (d < nd) {
+    const u32x4* row = reinterpret_cast<const u32x4*>((st == 0 ? q : k) +
+                                                      ((size_t)head * N + dst_list[(size_t)sh * N + d]) * kD);
+    v0 = row[part * 2];
+    v1 = row[part * 2 + 1];
+  }
+  float ss = sumsq8(__builtin_bit_cast(bf16x8, v1), sumsq8(__builtin_bit_cast(bf16x8, v0), 0.f));
+  ss += __shfl_xor(ss, 1);
+  ss += __shfl_xor(ss, 2);
+  u32x4* out = reinterpret_cast<u32x4*>(dg + ((size_t)sh * dpitch + d) * kD);
+  out[part * 2] = v0;
+  out[part * 2 + 1] = v1;
+  if (part == 0) dinv[(size_t)sh * dpitch + d] = d < nd ? __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f)) : 0.f;
+}
+
+__device__ __forceinline__ void ga_lds_copy16(const void* g, u32x4* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void ga_wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Keys of destination block dt (16 rows of the tile) for the 4 source
+// columns, folded into tm: key = score bits with the low 4 bits replaced by
+// 15 - (position of the candidate among the lane's 16), so one unsigned max
+// keeps the larger score and, on equal bits, the smaller destination.
+template <bool MASK>
+__device__ __forceinline__ void ga_keys16(const f32x4 (&acc)[4], const f32x4 inv4, const float (&off)[4], int dt,
+                                          int lg, int nvalid, uint32_t (&tm)[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint32_t key[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = fmaf(acc[c][r], inv4[r], off[c]);
+      key[r] = (__float_as_uint(v) & ~15u) | (uint32_t)(15 - (4 * dt + r));
+      if (MASK && dt * 16 + 4 * lg + r >= nvalid) key[r] = 0u;
+    }
+    if (dt == 0) {
+      tm[c] = umax3(key[0], key[1], key[2] > key[3] ? key[2] : key[3]);
+    } else {
+      tm[c] = umax3(tm[c], key[0], key[1]);
+      tm[c] = umax3(tm[c], key[2], key[3]);
+    }
+  }
+}
+
+// One 64-destination tile: the 8 MFMAs of block dt + 1 are issued between
+// the key updates of block dt, so matrix and vector work overlap in a wave.
+template <bool MASK>
+__device__ __forceinline__ void ga_tile(const u32x4* sDb, const float* sInvb, const bf16x8 (&bs)[4][2],
+                                        const float (&off)[4], int lg, int l16, int nvalid, uint32_t (&tm)[4]) {
+  f32x4 acc[2][4];
+  auto mfma_block = [&](int dt, f32x4 (&o)[4]) {
+    const int arow = dt * 16 + l16;
+    const bf16x8 a0 = __builtin_bit_cast(bf16x8, sDb[arow * 8 + ((0 + lg) ^ swz(arow))]);
+    const bf16x8 a1 = __builtin_bit_cast(bf16x8, sDb[arow * 8 + ((4 + lg) ^ swz(arow))]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bs[c][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bs[c][1], o[c], 0, 0, 0);
+    }
+  };
+  mfma_block(0, acc[0]);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    if (dt + 1 < 4) mfma_block(dt + 1, acc[(dt + 1) & 1]);
+    const f32x4 inv4 = *reinterpret_cast<const f32x4*>(&sInvb[dt * 16 + 4 * lg]);
+    ga_keys16<MASK>(acc[dt & 1], inv4, off, dt, lg, nvalid, tm);
+    if (dt + 1 < 4) {
+      // 8 MFMAs spread over the 40 key instructions
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void ga_match_bf16(GaMatchArgs a) {
-  __shared__ u32x4 sD[2][kDstTile * 8];
-  __shared__ __attribute__((aligned(16))) float sInv[2][kDstTile];
-  const int chunk = blockIdx.x % a.chunks, sh = blockIdx.x / a.chunks;
+  // two tile buffers as separate LDS objects: reads of one need not wait
+  // for the direct-to-LDS copies into the other
+  __shared__ u32x4 sD0[kDstTile * 8], sD1[kDstTile * 8];
+  __shared__ __attribute__((aligned(16))) float sI0[kDstTile], sI1[kDstTile];
+  // chunk fastest: concurrent workgroups stream the same destination tiles
+  const int chunk = blockIdx.x % a.chunks, rest = blockIdx.x / a.chunks;
+  const int split = rest % a.dsplit, sh = rest / a.dsplit;
   const int st = sh / a.heads, head = sh % a.heads;
   const int nd = a.tot[sh * 3 + 1], ns = a.tot[sh * 3 + 2];
-  if (chunk * kSrcPerWg >= ns || nd == 0) return;
+  const int ntiles = ceil_div(nd, kDstTile);
+  const int t0 = (int)((int64_t)split * ntiles / a.dsplit), t1 = (int)((int64_t)(split + 1) * ntiles / a.dsplit);
+  if (chunk * kSrcPerWg >= ns || t0 >= t1) return;
   const size_t hb = (size_t)sh * a.N;
   const uint16_t* X = reinterpret_cast<const uint16_t*>(a.x[st]) + (size_t)head * a.N * kD;
-  const int32_t* DL = a.dst_list + hb;
   const int32_t* SL = a.src_list + hb;
+  const char* Dg = reinterpret_cast<const char*>(a.dg + (size_t)sh * a.dpitch * kD);
+  const char* Di = reinterpret_cast<const char*>(a.dinv + (size_t)sh * a.dpitch);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lg = lane >> 4, l16 = lane & 15;
+  // direct-to-LDS tile copies: the lane at LDS chunk slot p (row p / 8,
+  // stored chunk p % 8) fetches logical chunk (p % 8) ^ swz(row) of that row
+  uint32_t goff[2];
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) {
+    const int p = rd * 256 + wave * 64 + lane, row = p >> 3;
+    goff[rd] = (uint32_t)(row * kD * 2 + (((p & 7) ^ swz(row)) * 16));
+  }
+  auto load_tile = [&](int t, u32x4* sDb, float* sIb) {
+    const char* base = Dg + (size_t)t * kDstTile * kD * 2;
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) ga_lds_copy16(base + goff[rd], sDb + rd * 256 + wave * 64);
+    if (wave == 0 && lane < kDstTile / 4)
+      ga_lds_copy16(Di + ((size_t)t * kDstTile + lane * 4) * 4, reinterpret_cast<u32x4*>(sIb));
+  };
+  load_tile(t0, sD0, sI0);
   bf16x8 bs[4][2];
-  float off[4], invs[4];
+  float off[4];
   int ksrc[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -374,51 +544,54 @@ __global__ __launch_bounds__(256) void ga_match_bf16(GaMatchArgs a) {
     }
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
-    off[c] = __builtin_amdgcn_sqrtf(ss) * (1.0f + 0x1p-10f);
-    invs[c] = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
+    off[c] = ga_off(ss);
+    // the last split is never empty
+    if (split == a.dsplit - 1 && lg == 0 && kidx < ns) a.snorm[hb + tok] = ss;
   }
   uint32_t best[4] = {0u, 0u, 0u, 0u}, bestT[4] = {0u, 0u, 0u, 0u};
   int bt[4] = {0, 0, 0, 0};
-  const int lrow = tid >> 2, lch = (tid & 3) * 2;
-  const int ntiles = ceil_div(nd, kDstTile);
-  u32x4 pre[2];
-  auto load_tile = [&](int t) {
-    int d = t * kDstTile + lrow;
-    d = d < nd ? d : 0;
-    const u32x4* row = reinterpret_cast<const u32x4*>(X + (size_t)DL[d] * kD);
-    pre[0] = row[lch];
-    pre[1] = row[lch + 1];
-  };
-  load_tile(0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    {
-      float ss = 0.f;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        ss = sumsq8(__builtin_bit_cast(bf16x8, pre[c]), ss);
-        sD[buf][lrow * 8 + ((lch + c) ^ swz(lrow))] = pre[c];
-      }
-      ss += __shfl_xor(ss, 1);
-      ss += __shfl_xor(ss, 2);
-      if ((tid & 3) == 0) sInv[buf][lrow] = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
-    }
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1);
-    uint32_t tm[4];
-    if ((t + 1) * kDstTile > nd)
-      tile_keys<true>(sD[buf], sInv[buf], bs, off, lg, l16, nd - t * kDstTile, tm);
-    else
-      tile_keys<false>(sD[buf], sInv[buf], bs, off, lg, l16, kDstTile, tm);
+  auto update = [&](const uint32_t (&tm)[4], int t) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint32_t tT = tm[c] & ~15u;
-      if (t == 0 || tT > bestT[c]) {
+      if (t == t0 || tT > bestT[c]) {
         best[c] = tm[c];
         bestT[c] = tT;
         bt[c] = t;
       }
     }
+  };
+  // only the head's last tile can be partial: it runs after the loop.  The
+  // loop is unrolled by two so that every read names its buffer statically.
+  const int tfull = (t1 == ntiles && nd % kDstTile) ? t1 - 1 : t1;
+  auto step = [&](int t, const u32x4* sDc, const float* sIc, u32x4* sDn, float* sIn) {
+    __builtin_amdgcn_sched_barrier(0);  // the previous tile's work stays before the wait
+    ga_wait_vm();
+    __syncthreads();
+    if (t + 1 < t1) load_tile(t + 1, sDn, sIn);
+    uint32_t tm[4];
+    ga_tile<false>(sDc, sIc, bs, off, lg, l16, kDstTile, tm);
+    update(tm, t);
+  };
+  int t = t0;
+  for (; t + 1 < tfull; t += 2) {
+    step(t, sD0, sI0, sD1, sI1);
+    step(t + 1, sD1, sI1, sD0, sI0);
+  }
+  if (t < tfull) {
+    step(t, sD0, sI0, sD1, sI1);
+    ++t;
+  }
+  if (t < t1) {
+    // the partial tile sits in buffer (t - t0) & 1
+    ga_wait_vm();
+    __syncthreads();
+    uint32_t tm[4];
+    if ((t - t0) & 1)
+      ga_tile<true>(sD1, sI1, bs, off, lg, l16, nd - t * kDstTile, tm);
+    else
+      ga_tile<true>(sD0, sI0, bs, off, lg, l16, nd - t * kDstTile, tm);
+    update(tm, t);
   }
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -436,13 +609,9 @@ __global__ __launch_bounds__(256) void ga_match_bf16(GaMatchArgs a) {
       take_better(kb, d, ko, dob);
     }
     if (lg == 0 && ksrc[c] < ns) {
-      const int dd = d < nd ? d : 0;
-      const size_t o = hb + SL[ksrc[c]];
-      const int ds = a.dst_slot[hb + dd];
-      a.gdst[o] = DL[dd];
-      a.gslot[o] = ds;
-      a.gscore[o] = (__uint_as_float(kb) - off[c]) * invs[c] + 0.0f;
-      atomicAdd(&a.cnt[(size_t)sh * a.bound + ds], 1);
+      const uint32_t dd = (uint32_t)(d < nd ? d : 0);
+      atomicMax(reinterpret_cast<unsigned long long*>(&a.best[hb + SL[ksrc[c]]]),
+                ((unsigned long long)kb << 32) | (unsigned long long)(0xFFFFFFFFu - dd));
     }
   }
 }
@@ -451,10 +620,13 @@ __global__ __launch_bounds__(256) void ga_match_bf16(GaMatchArgs a) {
 __global__ __launch_bounds__(256) void ga_match_f32(GaMatchArgs a) {
   __shared__ float sD[kDstTile][kD + 1];
   __shared__ float sInv[kDstTile];
-  const int chunk = blockIdx.x % a.chunks, sh = blockIdx.x / a.chunks;
+  const int chunk = blockIdx.x % a.chunks, rest = blockIdx.x / a.chunks;
+  const int split = rest % a.dsplit, sh = rest / a.dsplit;
   const int st = sh / a.heads, head = sh % a.heads;
   const int nd = a.tot[sh * 3 + 1], ns = a.tot[sh * 3 + 2];
-  if (chunk * kSrcPerWg >= ns || nd == 0) return;
+  const int ntiles = ceil_div(nd, kDstTile);
+  const int tt0 = (int)((int64_t)split * ntiles / a.dsplit), tt1 = (int)((int64_t)(split + 1) * ntiles / a.dsplit);
+  if (chunk * kSrcPerWg >= ns || tt0 >= tt1) return;
   const size_t hb = (size_t)sh * a.N;
   const float* X = reinterpret_cast<const float*>(a.x[st]) + (size_t)head * a.N * kD;
   const int32_t* DL = a.dst_list + hb;
@@ -469,8 +641,8 @@ __global__ __launch_bounds__(256) void ga_match_f32(GaMatchArgs a) {
   }
   const float inv_src = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
   float bestv = -INFINITY;
-  int bidx = 0;
-  for (int t0 = 0; t0 < nd; t0 += kDstTile) {
+  int bidx = tt0 * kDstTile;
+  for (int t0 = tt0 * kDstTile; t0 < min(nd, tt1 * kDstTile); t0 += kDstTile) {
     __syncthreads();
     for (int e = tid; e < kDstTile * kD; e += blockDim.x) {
       const int r = e / kD, c = e % kD;
@@ -496,13 +668,43 @@ __global__ __launch_bounds__(256) void ga_match_f32(GaMatchArgs a) {
     }
   }
   if (kidx < ns) {
-    const size_t o = hb + stok;
-    const int ds = a.dst_slot[hb + bidx];
-    a.gdst[o] = DL[bidx];
-    a.gslot[o] = ds;
-    a.gscore[o] = bestv * inv_src + 0.0f;
-    atomicAdd(&a.cnt[(size_t)sh * a.bound + ds], 1);
+    if (split == a.dsplit - 1) a.snorm[hb + stok] = inv_src;  // the last split is never empty
+    atomicMax(reinterpret_cast<unsigned long long*>(&a.best[hb + stok]),
+              ((unsigned long long)float_key(bestv + 0.0f) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)bidx));
   }
+}
+
+// Matches from the packed atomic maxima: destination token, its slot, the
+// cosine, and one more member for that slot.
+__global__ __launch_bounds__(256) void ga_decode(int dtype, int heads, int N, int bound,
+                                                 const int32_t* __restrict__ tot, const int32_t* __restrict__ dst_list,
+                                                 const int32_t* __restrict__ dst_slot,
+                                                 const int32_t* __restrict__ src_list,
+                                                 const uint64_t* __restrict__ best, const float* __restrict__ snorm,
+                                                 int32_t* __restrict__ gdst, int32_t* __restrict__ gslot,
+                                                 float* __restrict__ gscore, int32_t* __restrict__ cnt) {
+  const int sh = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= tot[sh * 3 + 2]) return;
+  const size_t hb = (size_t)sh * N;
+  const int tok = src_list[hb + i];
+  const uint64_t b = best[hb + tok];
+  int d = (int)(0xFFFFFFFFu - (uint32_t)b);
+  if ((unsigned)d >= (unsigned)tot[sh * 3 + 1]) d = 0;  // never: every source has a destination
+  const uint32_t kb = (uint32_t)(b >> 32);
+  const int ds = dst_slot[hb + d];
+  gdst[hb + tok] = dst_list[hb + d];
+  gslot[hb + tok] = ds;
+  float sc;
+  if (dtype == 1) {
+    const float ss = snorm[hb + tok];
+    sc = (__uint_as_float(kb) - ga_off(ss)) * __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f)) + 0.0f;
+  } else {
+    const uint32_t u = (kb & 0x80000000u) ? (kb & 0x7FFFFFFFu) : ~kb;  // inverse of float_key
+    sc = __uint_as_float(u) * snorm[hb + tok] + 0.0f;
+  }
+  gscore[hb + tok] = sc;
+  atomicAdd(&cnt[(size_t)sh * bound + ds], 1);
 }
 
 // Slot offsets of one (stream, head): exclusive prefix of the member counts
@@ -584,16 +786,20 @@ hipError_t launch_ga_partition(int dtype, const GaShape& s, const void* q, const
   const int HW = s.H * s.W;
   const int SH = 2 * s.heads;
   {
-    const dim3 grid((unsigned)ceil_div(HW > s.nsp ? HW : s.nsp, 256), (unsigned)s.F, (unsigned)SH);
+    // near-equal tiles of at most 32 columns and 16 rows (<= 256 patches)
+    const int tx = ceil_div(s.W, 32), C = ceil_div(s.W, tx);
+    const int r0 = std::min(16, 256 / C), ty = ceil_div(s.H, r0), R = ceil_div(s.H, ty);
+    if ((R + 2) * (C + 2) > kVarMaxStage) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(tx * ty), (unsigned)s.F, (unsigned)SH);
     HTTM_DISPATCH_T(dtype, hipLaunchKernelGGL(ga_variance<T>, grid, dim3(256), 0, stream, (const T*)q, (const T*)k,
-                                              s.heads, s.N, s.Tf, s.nsp, s.H, s.W, b.var));
+                                              s.heads, s.N, s.Tf, s.nsp, s.H, s.W, R, C, tx, b.var));
   }
   hipLaunchKernelGGL(ga_roles, dim3((unsigned)s.F, (unsigned)SH), dim3(kRoleThreads), 0, stream, b.var, s.heads, s.N,
                      s.Tf, s.nsp, s.H, s.W, s.F, s.k_protect, b.role, b.fcnt);
   hipLaunchKernelGGL(ga_scan, dim3((unsigned)SH), dim3(256), 0, stream, b.fcnt, s.F, s.heads, b.foff, b.tot, b.lenk);
   hipLaunchKernelGGL(ga_slots, dim3((unsigned)s.F, (unsigned)SH), dim3(kRoleThreads), 0, stream, b.role, s.heads, s.N,
                      s.Tf, s.F, s.bound, b.foff, b.slot, b.dst_list, b.dst_slot, b.src_list, b.gdst, b.gscore, b.cnt,
-                     b.fill);
+                     b.fill, b.best);
   GaMatchArgs a;
   a.x[0] = q;
   a.x[1] = k;
@@ -604,15 +810,24 @@ hipError_t launch_ga_partition(int dtype, const GaShape& s, const void* q, const
   a.dst_list = b.dst_list;
   a.dst_slot = b.dst_slot;
   a.src_list = b.src_list;
-  a.gdst = b.gdst;
-  a.gslot = b.gslot;
-  a.gscore = b.gscore;
-  a.cnt = b.cnt;
-  a.bound = s.bound;
-  if (dtype == 1)
-    hipLaunchKernelGGL(ga_match_bf16, dim3((unsigned)(SH * a.chunks)), dim3(256), 0, stream, a);
+  a.best = b.best;
+  a.snorm = b.snorm;
+  a.dsplit = kDstSplits;
+  a.dg = b.dg;
+  a.dinv = b.dinv;
+  a.dpitch = s.dpitch;
+  const unsigned mgrid = (unsigned)(SH * kDstSplits * a.chunks);
+  if (dtype == 1) {
+    hipLaunchKernelGGL(ga_gather, dim3((unsigned)(s.dpitch / 64), (unsigned)SH), dim3(256), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, s.heads, s.N, s.dpitch, b.tot, b.dst_list, b.dg,
+                       b.dinv);
+    hipLaunchKernelGGL(ga_match_bf16, dim3(mgrid), dim3(256), 0, stream, a);
+  }
   else
-    hipLaunchKernelGGL(ga_match_f32, dim3((unsigned)(SH * a.chunks)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(ga_match_f32, dim3(mgrid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(ga_decode, dim3((unsigned)ceil_div(s.max_src, 256), (unsigned)SH), dim3(256), 0, stream, dtype,
+                     s.heads, s.N, s.bound, b.tot, b.dst_list, b.dst_slot, b.src_list, b.best, b.snorm, b.gdst,
+                     b.gslot, b.gscore, b.cnt);
   hipLaunchKernelGGL(ga_offsets, dim3((unsigned)SH), dim3(kRoleThreads), 0, stream, b.cnt, b.tot, s.heads, s.N,
                      s.bound, b.off_q, b.off_k);
   const unsigned grid = (unsigned)(((int64_t)SH * s.N + 255) / 256);

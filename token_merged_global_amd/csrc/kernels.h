@@ -104,6 +104,7 @@ struct GaShape {
   int k_protect;  // protected patches per frame
   int bound;      // slots per head (upper bound of anchors)
   int max_src;    // upper bound of sources per head
+  int dpitch;     // rows of the gathered destination matrix per (stream, head): >= destinations, multiple of 64
 };
 struct GaBuffers {
   float* var;          // [2][h][N] variance map
@@ -118,6 +119,10 @@ struct GaBuffers {
   int32_t* gdst;       // [2][h][N] matched destination token of each source
   int32_t* gslot;      // [2][h][N] its slot
   float* gscore;       // [2][h][N] its cosine
+  uint16_t* dg;        // bf16: [2][h][dpitch][64] destination rows, gathered
+  float* dinv;         // bf16: [2][h][dpitch] their inverse norms
+  uint64_t* best;      // [2][h][N] per source: packed best (key, destination index)
+  float* snorm;        // [2][h][N] per source: norm term of its score
   int32_t* cnt;        // [2][h][bound] members per slot
   int32_t* fill;       // [2][h][bound] placement counters
   int32_t* tmp;        // [2][h][N] members in placement order
