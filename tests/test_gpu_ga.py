@@ -167,3 +167,28 @@ def test_ga_cached_layer_and_index_round_trip():
     if blk.index_bytes == plan.index_bytes:
         with pytest.raises(H.HttmError):
             H.index_import(blk, host)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ga_variance_map_tiny_values(dtype):
+    """Inputs scaled by 2^-66: window sums of squares fall below 2^-125 (the
+    subnormal range), where the variance kernel's fast quotient by 6 hands
+    over to plain division; the map and the classes stay bit-exact."""
+    w = gen.Workload(name="ga_tiny_vals", cfg_id=14, dtype=dtype, heads=2, d_head=64, frames=3, grid_h=7,
+                     grid_w=9, n_special=1, n_s=16, n_t=2, q_ratio=0.5, kv_ratio=0.5, outlier_pct=10.0,
+                     partition=1, protect_pct=10.0)
+    x = gen.layer_inputs(w)
+    xs = {t: (x[t] * np.float32(2.0 ** -66)).astype(np.float32) for t in "qkv"}
+    p = O.Params.from_workload(w)
+    plan, ws, dev, out, gpu, _ = run_layer(w, xs)
+    var = gpu["ga_var"].reshape(2, w.heads, -1)
+    role = gpu["ga_role"].reshape(2, w.heads, -1)
+    tiny = 0
+    for st, t in enumerate("qk"):
+        for h in range(w.heads):
+            want = O.token_variance_map(xs[t][h], p)
+            assert np.array_equal(var[st, h], want), (t, h, np.flatnonzero(var[st, h] != want)[:5])
+            assert np.array_equal(role[st, h], O.ga_roles(want, p)), (t, h)
+            tiny += int(((want > 0) & (want < 2.0 ** -125)).sum())
+    say(f"[ga tiny values {dtype}] variance entries below 2^-125: {tiny}")
+    assert tiny > 0

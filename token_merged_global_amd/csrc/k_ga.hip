@@ -117,6 +117,7 @@ __global__ __launch_bounds__(256) void ga_variance(const T* __restrict__ q, cons
   if (ly >= R || y >= H || x >= W) return;
   const bool hl = x > 0, hr = x + 1 < W, hu = y > 0, hd = y + 1 < H;
   const float cnt = (float)((1 + hl + hr) * (1 + hu + hd));
+  const float rc = 1.0f / cnt;
   const int centre = (ly + 1) * sw + lx + 1;
   float acc = 0.f;
   for (int c8 = 0; c8 < 8; ++c8) {
@@ -151,11 +152,30 @@ __global__ __launch_bounds__(256) void ga_variance(const T* __restrict__ q, cons
         }
       }
     }
+    // s / cnt correctly rounded in three operations: q0 = s * RN(1/cnt), then
+    // one residual correction.  Checked against IEEE division for every
+    // finite float and cnt in {1, 2, 3, 4, 6, 9}: equal except that -0 gives
+    // +0 (harmless: only m * m and s2 >= +0 are used) and, for cnt = 6,
+    // nonzero |s| < 2^-125, which take the plain division below.
+    float var8[8];
+    bool slow = false;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float m = s1[e] / cnt;
-      acc = __fadd_rn(acc, __fsub_rn(s2[e] / cnt, __fmul_rn(m, m)));
+      const float q1 = s1[e] * rc, q2 = s2[e] * rc;
+      const float m = fmaf(fmaf(-q1, cnt, s1[e]), rc, q1);
+      const float v2 = fmaf(fmaf(-q2, cnt, s2[e]), rc, q2);
+      var8[e] = __fsub_rn(v2, __fmul_rn(m, m));
+      slow |= cnt == 6.0f && ((s1[e] != 0.f && fabsf(s1[e]) < 0x1p-125f) || (s2[e] != 0.f && s2[e] < 0x1p-125f));
     }
+    if (slow) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float m = s1[e] / cnt;
+        var8[e] = __fsub_rn(s2[e] / cnt, __fmul_rn(m, m));
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __fadd_rn(acc, var8[e]);
   }
   V[nsp + y * W + x] = acc / 64.0f;
 }
