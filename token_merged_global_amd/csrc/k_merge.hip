@@ -509,17 +509,33 @@ __global__ __launch_bounds__(256) void merge_q_cached(int heads, int N, const T*
 template <typename T>
 __global__ __launch_bounds__(256) void unmerge(int64_t rows, const int32_t* __restrict__ slot,
                                                const T* __restrict__ o, T* __restrict__ out) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = idx >> 3;
-  const int part = (int)(idx & 7);
-  if (row >= rows) return;
-  const T* src = o + (size_t)slot[row] * kD + part * 8;
-  T* dst = out + (size_t)row * kD + part * 8;
+  // 8 lanes per 128-byte row (bf16), 8 rows per lane group: all slot and row
+  // loads are in flight before the first store; the output is written once
+  // and not read here again, so its stores do not allocate in the caches
+  constexpr int kR = 8;
+  const int64_t g8 = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 3;
+  const int part = (int)(threadIdx.x & 7);
+  const int64_t row0 = g8 * kR;
+  int32_t sl[kR];
+#pragma unroll
+  for (int k = 0; k < kR; ++k) sl[k] = row0 + k < rows ? slot[row0 + k] : 0;
   if (sizeof(T) == 2) {
-    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+    u32x4 v[kR];
+#pragma unroll
+    for (int k = 0; k < kR; ++k) v[k] = *reinterpret_cast<const u32x4*>(o + (size_t)sl[k] * kD + part * 8);
+#pragma unroll
+    for (int k = 0; k < kR; ++k)
+      if (row0 + k < rows)
+        __builtin_nontemporal_store(v[k], reinterpret_cast<u32x4*>(out + (size_t)(row0 + k) * kD + part * 8));
   } else {
-    reinterpret_cast<f32x4*>(dst)[0] = reinterpret_cast<const f32x4*>(src)[0];
-    reinterpret_cast<f32x4*>(dst)[1] = reinterpret_cast<const f32x4*>(src)[1];
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      if (row0 + k >= rows) break;
+      const f32x4* src = reinterpret_cast<const f32x4*>(o + (size_t)sl[k] * kD + part * 8);
+      f32x4* dst = reinterpret_cast<f32x4*>(out + (size_t)(row0 + k) * kD + part * 8);
+      dst[0] = src[0];
+      dst[1] = src[1];
+    }
   }
 }
 
@@ -629,7 +645,7 @@ hipError_t launch_merge_q_cached(int dtype, int heads, int N, int64_t q_capacity
 hipError_t launch_unmerge(int dtype, int heads, int N, const int32_t* slot, const void* o,
                           void* out, hipStream_t stream) {
   const int64_t rows = (int64_t)heads * N;
-  const int grid = (int)((rows * 8 + 255) / 256);
+  const int grid = (int)(((rows + 7) / 8 * 8 + 255) / 256);
   HTTM_DISPATCH(dtype, hipLaunchKernelGGL(unmerge<T>, dim3(grid), dim3(256), 0, stream, rows,
                                           slot, (const T*)o, (T*)out));
   return hipGetLastError();
