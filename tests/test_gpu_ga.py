@@ -192,3 +192,50 @@ def test_ga_variance_map_tiny_values(dtype):
             tiny += int(((want > 0) & (want < 2.0 ** -125)).sum())
     say(f"[ga tiny values {dtype}] variance entries below 2^-125: {tiny}")
     assert tiny > 0
+
+
+def _index_regions(h, n, lk):
+    """Byte offsets of the index regions (64-byte header, then each region
+    at the next 256-byte boundary, in the layout order of the library)."""
+    al = lambda x: (x + 255) & ~255
+    sizes = [("header", 64), ("k_members", 4 * h * n), ("k_off", 4 * h * (lk + 1)), ("fmembers", 4 * h * n),
+             ("foff", 4 * h * (n + 1)), ("slot", 4 * h * n), ("lenq", 4 * h), ("cu_q", 4 * (h + 1)),
+             ("lenk", 4 * h)]
+    off, cur = {}, 0
+    for name, size in sizes:
+        off[name] = cur
+        cur = al(cur + size)
+    return off, cur
+
+
+def test_ga_index_import_checks_key_counts():
+    """An imported geometry-aware index is checked on the host: the per-head
+    key counts must lie in [1, kv_len] and the key offsets past them must be
+    empty (equal to N)."""
+    w = small(frames=4, heads=2)
+    x = gen.layer_inputs(w)
+    plan = H.Plan.from_workload(w)
+    q, k, v = (to_dev(x[t], w.dtype) for t in "qkv")
+    ws = H.workspace(plan)
+    _, idx = H.layer(plan, q, k, v, ws=ws, keep_index=True)
+    host = H.index_export(plan, idx)
+    h, n, lk = w.heads, w.n_tokens, plan.info["kv_len"]
+    off, total = _index_regions(h, n, lk)
+    assert total == plan.index_bytes == host.nbytes
+    lenk = host[off["lenk"]:off["lenk"] + 4 * h].view(np.int32)
+    kl = H.debug_read(plan, ws, "kv_len", index=idx)
+    assert np.array_equal(lenk, kl) and (kl < lk).all()
+    ko = host[off["k_off"]:off["k_off"] + 4 * h * (lk + 1)].view(np.int32).reshape(h, lk + 1)
+    assert (ko[0, kl[0]:] == n).all() and ko[0, 0] == 0
+    H.index_import(plan, host)  # the untouched bytes pass
+    for bad in (0, lk + 1):
+        b = host.copy()
+        b[off["lenk"]:off["lenk"] + 4].view(np.int32)[0] = bad
+        with pytest.raises(H.HttmError) as e:
+            H.index_import(plan, b)
+        assert e.value.status == 4
+    b = host.copy()
+    b[off["k_off"]:off["k_off"] + 4 * h * (lk + 1)].view(np.int32).reshape(h, lk + 1)[1, kl[1] + 1] = n - 1
+    with pytest.raises(H.HttmError) as e:
+        H.index_import(plan, b)
+    assert e.value.status == 4
