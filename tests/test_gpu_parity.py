@@ -280,3 +280,23 @@ def test_index_export_import_round_trip():
     with pytest.raises(H.HttmError) as e:
         H.index_import(plan, bad)
     assert e.value.status == 4
+
+
+@pytest.mark.parametrize("dtype,order,qs,ks", [("bf16", 0, 0, 0), ("f32", 0, 0, 0), ("bf16", 1, 5, 3),
+                                               ("f32", 1, 0, 6)])
+def test_odd_geometry_layer(dtype, order, qs, ks):
+    """A grid whose runs and temporal groups do not divide evenly (5 x 9
+    patches, runs of 10, groups of 3 over 7 frames, 2 specials), explicit
+    destination strides and both stacking orders: every index stage and
+    every output row against the oracle."""
+    w = gen.Workload(name="odd", cfg_id=9, dtype=dtype, heads=3, d_head=64, frames=7, grid_h=5, grid_w=9,
+                     n_special=2, n_s=10, n_t=3, q_ratio=0.6, kv_ratio=0.3, outlier_pct=7.5, block_order=order,
+                     q_dst_stride=qs, kv_dst_stride=ks)
+    _say(f"[odd geometry] {dtype} order {order} strides {qs}/{ks}")
+    x = gen.layer_inputs(w)
+    p = O.Params.from_workload(w)
+    plan, ws, dev, out, gpu = run_layer(w, x)
+    kw = dict(rel_tol=BF16_REL) if dtype == "bf16" else dict(out_tol=F32_ABS)
+    rep = staged.check_layer(x["q"], x["k"], x["v"], p, gpu, out, **kw)
+    _say("  ", rep.as_dict())
+    assert rep.delta_nonexact == 0

@@ -13,11 +13,14 @@
 //   2. every block position gets a group: its own index for a destination,
 //      the matched destination for a merged source, and |D| for the other
 //      sources (they follow as singletons);
-//   3. a stable counting sort by group gives the CSR: each wave ranks its
-//      contiguous segment of positions 64 at a time (lanes with equal groups
-//      are found with one ballot per key bit), a scan over (group, wave)
-//      turns per-wave counts into offsets, so members ascend inside a group,
-//      which for frame-major blocks is ascending original token id.
+//   3. a stable counting sort by group gives the CSR: positions are visited
+//      in ascending original token id (block position order for frame-major
+//      blocks; for frame-minor blocks the frame-major enumeration of the same
+//      block), each wave ranks its contiguous segment of that enumeration 64
+//      at a time (lanes with equal groups are found with one ballot per key
+//      bit), and a scan over (group, wave) turns per-wave counts into
+//      offsets, so members ascend by token id inside a group (the order of
+//      the means' sums).
 // Everything is integer work after the float-to-key transform, so the result
 // is deterministic.  Extra workgroups fill the special-token slots.
 #include "common.h"
@@ -199,15 +202,18 @@ __global__ __launch_bounds__(kThreads) void block_select(SelArgs a) {
   __syncthreads();
 
   // 2-3a. group of every position; per-wave stable ranks.  Wave w owns the
-  // contiguous positions [w*pw, (w+1)*pw).
+  // contiguous enumeration indices [w*pw, (w+1)*pw); index u is the u-th
+  // token of the block in ascending token id, at block position pos(u).
   const int pw = ceil_div(bi.n, kThreads) * 64;  // multiple of 64, kWaves * pw >= n
   const int chunks = pw / 64;
+  auto pos = [&](int u) { return g.order ? (u % bi.run) * bi.nf + u / bi.run : u; };
   int grp[kPer], lrank[kPer];
 #pragma unroll
   for (int ch = 0; ch < kPer; ++ch) {
     if (ch >= chunks) break;  // uniform over the workgroup
-    const int i = wave * pw + ch * 64 + lane;
-    const bool valid = i < bi.n;
+    const int u = wave * pw + ch * 64 + lane;
+    const bool valid = u < bi.n;
+    const int i = valid ? pos(u) : 0;
     int gi = 0;
     if (valid) gi = (i % s == 0) ? i / s : sGrp[i - i / s - 1];
     const uint64_t eqm = match_any((uint32_t)gi, valid);
@@ -246,8 +252,9 @@ __global__ __launch_bounds__(kThreads) void block_select(SelArgs a) {
 #pragma unroll
   for (int ch = 0; ch < kPer; ++ch) {
     if (ch >= chunks) break;
-    const int i = wave * pw + ch * 64 + lane;
-    if (i >= bi.n) continue;
+    const int u = wave * pw + ch * 64 + lane;
+    if (u >= bi.n) continue;
+    const int i = pos(u);
     const int gi = grp[ch];
     const int p = (int)sCnt[wave][gi] + lrank[ch];
     const int tok = block_token(g, bi, i);
