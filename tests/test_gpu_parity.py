@@ -300,3 +300,42 @@ def test_odd_geometry_layer(dtype, order, qs, ks):
     rep = staged.check_layer(x["q"], x["k"], x["v"], p, gpu, out, **kw)
     _say("  ", rep.as_dict())
     assert rep.delta_nonexact == 0
+
+
+EDGE_CASES = {
+    # one frame: a single temporal group shorter than n_t
+    "one_frame": dict(frames=1, grid_h=6, grid_w=6, n_special=1, n_s=12, n_t=4),
+    # runs longer than a frame (one spatial run per frame)
+    "run_covers_frame": dict(frames=5, grid_h=3, grid_w=4, n_special=2, n_s=64, n_t=2),
+    # one patch per frame
+    "one_patch": dict(frames=9, grid_h=1, grid_w=1, n_special=3, n_s=1, n_t=4),
+    # no outliers, keys unmerged, queries merged
+    "no_outliers_kv0": dict(frames=4, grid_h=5, grid_w=5, n_special=0, n_s=10, n_t=2, outlier_pct=0.0,
+                            kv_ratio=0.0),
+    # queries unmerged, keys merged hard
+    "q0_kv90": dict(frames=4, grid_h=5, grid_w=5, n_special=1, n_s=25, n_t=4, q_ratio=0.0, kv_ratio=0.9),
+    # many heads of a small layer
+    "heads64": dict(heads=64, frames=2, grid_h=3, grid_w=3, n_special=1, n_s=9, n_t=2),
+}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", sorted(EDGE_CASES))
+def test_edge_geometry_layers(case, dtype):
+    """Degenerate shapes of the method: every index stage and every output
+    row against the oracle."""
+    kw = dict(name="edge", cfg_id=21, dtype=dtype, heads=2, d_head=64, q_ratio=0.5, kv_ratio=0.5,
+              outlier_pct=10.0)
+    kw.update(EDGE_CASES[case])
+    w = gen.Workload(**kw)
+    _say(f"[edge] {case} {dtype} N={w.n_tokens}")
+    x = gen.layer_inputs(w)
+    p = O.Params.from_workload(w)
+    plan, ws, dev, out, gpu = run_layer(w, x)
+    # these tiny layers have outputs up to 7 x their RMS, where rounding the
+    # output to bf16 alone can exceed 2e-2 x RMS: half an ulp of the largest
+    # output is allowed on top (bf16 only)
+    tol = dict(rel_tol=BF16_REL, out_half_ulp=True) if dtype == "bf16" else dict(out_tol=F32_ABS)
+    rep = staged.check_layer(x["q"], x["k"], x["v"], p, gpu, out, **tol)
+    _say("  ", rep.as_dict())
+    assert rep.delta_nonexact == 0

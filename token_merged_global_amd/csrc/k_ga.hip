@@ -837,17 +837,20 @@ hipError_t launch_ga_partition(int dtype, const GaShape& s, const void* q, const
   a.dinv = b.dinv;
   a.dpitch = s.dpitch;
   const unsigned mgrid = (unsigned)(SH * kDstSplits * a.chunks);
-  if (dtype == 1) {
+  if (s.max_src == 0) {
+    // a single frame: no sources, every token is its own group
+  } else if (dtype == 1) {
     hipLaunchKernelGGL(ga_gather, dim3((unsigned)(s.dpitch / 64), (unsigned)SH), dim3(256), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k, s.heads, s.N, s.dpitch, b.tot, b.dst_list, b.dg,
                        b.dinv);
     hipLaunchKernelGGL(ga_match_bf16, dim3(mgrid), dim3(256), 0, stream, a);
-  }
-  else
+  } else {
     hipLaunchKernelGGL(ga_match_f32, dim3(mgrid), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(ga_decode, dim3((unsigned)ceil_div(s.max_src, 256), (unsigned)SH), dim3(256), 0, stream, dtype,
-                     s.heads, s.N, s.bound, b.tot, b.dst_list, b.dst_slot, b.src_list, b.best, b.snorm, b.gdst,
-                     b.gslot, b.gscore, b.cnt);
+  }
+  if (s.max_src > 0)
+    hipLaunchKernelGGL(ga_decode, dim3((unsigned)ceil_div(s.max_src, 256), (unsigned)SH), dim3(256), 0, stream,
+                       dtype, s.heads, s.N, s.bound, b.tot, b.dst_list, b.dst_slot, b.src_list, b.best, b.snorm,
+                       b.gdst, b.gslot, b.gscore, b.cnt);
   hipLaunchKernelGGL(ga_offsets, dim3((unsigned)SH), dim3(kRoleThreads), 0, stream, b.cnt, b.tot, s.heads, s.N,
                      s.bound, b.off_q, b.off_k);
   const unsigned grid = (unsigned)(((int64_t)SH * s.N + 255) / 256);
