@@ -243,17 +243,22 @@ def test_ga_index_import_checks_key_counts():
 
 @pytest.mark.parametrize("case", [dict(frames=1, grid_h=6, grid_w=7, n_special=1),
                                   dict(frames=6, grid_h=1, grid_w=1, n_special=2),
-                                  dict(frames=3, grid_h=2, grid_w=9, n_special=0)])
+                                  dict(frames=3, grid_h=2, grid_w=9, n_special=0),
+                                  dict(frames=2, grid_h=64, grid_w=64, n_special=1, dtype="bf16")])
 def test_ga_edge_geometry(case):
     """One frame (no sources at all: exact attention), one patch per frame,
-    a 2-row grid: the geometry-aware layer against the oracle."""
-    w = gen.Workload(name="ga_edge", cfg_id=22, dtype="f32", heads=2, d_head=64, n_s=4, n_t=2, q_ratio=0.5,
+    a 2-row grid, the largest frame (64 x 64 patches, bf16): the
+    geometry-aware layer against the oracle."""
+    case = dict(case)
+    dtype = case.pop("dtype", "f32")
+    w = gen.Workload(name="ga_edge", cfg_id=22, dtype=dtype, heads=2, d_head=64, n_s=4, n_t=2, q_ratio=0.5,
                      kv_ratio=0.5, outlier_pct=10.0, partition=1, protect_pct=20.0, **case)
     say(f"[ga edge] {case}")
     x = gen.layer_inputs(w)
     p = O.Params.from_workload(w)
     plan, ws, dev, out, gpu, _ = run_layer(w, x)
-    rep = staged.check_layer(x["q"], x["k"], x["v"], p, gpu, out, out_tol=F32_ABS)
+    tol = dict(rel_tol=BF16_REL) if dtype == "bf16" else dict(out_tol=F32_ABS)
+    rep = staged.check_layer(x["q"], x["k"], x["v"], p, gpu, out, workers=4, **tol)
     say("  ", rep.as_dict())
     assert rep.delta_nonexact == 0
     if case["frames"] == 1:
