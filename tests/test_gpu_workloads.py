@@ -112,3 +112,25 @@ def test_vggt500_cached_stack():
             rms = np.sqrt((ref ** 2).mean())
             say(f"  layer {l} head {h}: err {err:.3g} rms {rms:.3g}")
             assert err <= BF16_REL * rms
+
+
+@pytest.mark.timeout(600)
+def test_vggt100_geometry_aware_layer():
+    """The geometry-aware partition at 100 frames (137,400 tokens): variance
+    map, classes and groups of every head and stream; the global match (about
+    86,500 sources against 36,700 destinations per head and stream) against
+    the oracle on two heads; deviations, the outlier choice and the final
+    partition on every head; outputs on sampled rows of the oracle heads."""
+    w = gen.WORKLOADS["vggt100"].with_(partition=1, protect_pct=10.0)
+    say(f"[vggt100 geometry-aware] N={w.n_tokens}")
+    x = gen.layer_inputs(w)
+    p = O.Params.from_workload(w)
+    plan, ws, dev, out, gpu, _ = run_layer(w, x)
+    oh = gen.oracle_heads(w)
+    rows = sample_rows(w.n_tokens, 256, 1)
+    rep = staged.check_layer(x["q"], x["k"], x["v"], p, gpu, out, out_heads=oh, rows=rows, rel_tol=BF16_REL,
+                             match_heads=[0, w.heads - 1], workers=WORKERS)
+    say("  ", rep.as_dict())
+    assert rep.delta_nonexact == 0
+    kl = gpu["kv_len"]
+    assert (kl <= plan.info["kv_len"]).all()
