@@ -5,6 +5,18 @@
 
 #include "geo.h"
 
+// Runs the statement with T = uint16_t (bf16 bits, dtype 1) or T = float.
+#define HTTM_DISPATCH(dtype, ...) \
+  do {                            \
+    if ((dtype) == 1) {           \
+      typedef uint16_t T;         \
+      __VA_ARGS__;                \
+    } else {                      \
+      typedef float T;            \
+      __VA_ARGS__;                \
+    }                             \
+  } while (0)
+
 namespace httm {
 
 typedef __bf16 bf16;

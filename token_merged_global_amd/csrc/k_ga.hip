@@ -33,17 +33,6 @@ namespace httm {
 
 namespace {
 
-#define HTTM_DISPATCH_T(dtype, ...) \
-  do {                              \
-    if ((dtype) == 1) {             \
-      typedef uint16_t T;           \
-      __VA_ARGS__;                  \
-    } else {                        \
-      typedef float T;              \
-      __VA_ARGS__;                  \
-    }                               \
-  } while (0)
-
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float* x) { Row8<T>::load(p, x); }
 
@@ -811,7 +800,7 @@ hipError_t launch_ga_partition(int dtype, const GaShape& s, const void* q, const
     const int r0 = std::min(16, 256 / C), ty = ceil_div(s.H, r0), R = ceil_div(s.H, ty);
     if ((R + 2) * (C + 2) > kVarMaxStage) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(tx * ty), (unsigned)s.F, (unsigned)SH);
-    HTTM_DISPATCH_T(dtype, hipLaunchKernelGGL(ga_variance<T>, grid, dim3(256), 0, stream, (const T*)q, (const T*)k,
+    HTTM_DISPATCH(dtype, hipLaunchKernelGGL(ga_variance<T>, grid, dim3(256), 0, stream, (const T*)q, (const T*)k,
                                               s.heads, s.N, s.Tf, s.nsp, s.H, s.W, R, C, tx, b.var));
   }
   hipLaunchKernelGGL(ga_roles, dim3((unsigned)s.F, (unsigned)SH), dim3(kRoleThreads), 0, stream, b.var, s.heads, s.N,

@@ -588,17 +588,6 @@ __global__ __launch_bounds__(256) void prep_dense(int N, int pitch, float kscale
 
 }  // namespace
 
-#define HTTM_DISPATCH(dtype, ...)                  \
-  do {                                             \
-    if ((dtype) == 1) {                            \
-      typedef uint16_t T;                          \
-      __VA_ARGS__;                                 \
-    } else {                                       \
-      typedef float T;                             \
-      __VA_ARGS__;                                 \
-    }                                              \
-  } while (0)
-
 hipError_t launch_merge_kv(int dtype, int heads, int N, int lk, int lk_pad, float kscale, const void* k,
                            const void* v, const int32_t* members, const int32_t* off, void* kt,
                            void* vt, float* kmax, hipStream_t stream, const int32_t* lenk) {
