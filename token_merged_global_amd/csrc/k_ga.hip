@@ -229,15 +229,36 @@ __global__ __launch_bounds__(kRoleThreads) void ga_roles(const float* __restrict
       if ((key & hmask) == prefix) atomicAdd(&sHist[(key >> shift) & 0xFF], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      uint32_t above = 0;
-      int b = 255;
-      for (; b > 0; --b) {
-        if (above + sHist[b] >= kk) break;
-        above += sHist[b];
+    if (tid < 64) {
+      // the bin of the kk-th largest key: the largest b >= 1 whose suffix
+      // count S(b) = sum of bins >= b reaches kk, else 0; lane l holds bins
+      // 4l .. 4l + 3 and the suffix sums come from one wave scan
+      const int l = tid;
+      const uint32_t h0 = sHist[4 * l], h1 = sHist[4 * l + 1], h2 = sHist[4 * l + 2], h3 = sHist[4 * l + 3];
+      const uint32_t t = h0 + h1 + h2 + h3;
+      uint32_t x = t;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_down((int)x, d);
+        if (l + d < 64) x += y;
       }
-      sSel[0] = prefix | ((uint32_t)b << shift);
-      sSel[1] = kk - above;
+      const uint32_t s3 = x - t + h3, s2 = s3 + h2, s1 = s2 + h1, s0 = s1 + h0;
+      int cand = -1;
+      if (s3 >= kk) cand = 4 * l + 3;
+      else if (s2 >= kk) cand = 4 * l + 2;
+      else if (s1 >= kk) cand = 4 * l + 1;
+      else if (s0 >= kk && l > 0) cand = 4 * l;
+      int bsel = cand;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) bsel = max(bsel, __shfl_xor(bsel, d));
+      bsel = bsel < 0 ? 0 : bsel;
+      if (l == (bsel >> 2)) {
+        const int r = bsel & 3;
+        const uint32_t sb = r == 3 ? s3 : r == 2 ? s2 : r == 1 ? s1 : s0;
+        const uint32_t hb = r == 3 ? h3 : r == 2 ? h2 : r == 1 ? h1 : h0;
+        sSel[0] = prefix | ((uint32_t)bsel << shift);
+        sSel[1] = kk - (sb - hb);  // minus the keys in bins above bsel
+      }
     }
     __syncthreads();
     prefix = sSel[0];
