@@ -115,7 +115,7 @@ __device__ __forceinline__ void gather_sum(const T* const (&X)[NT], const int32_
 // row loads.
 template <typename T>
 struct KvStage {
-  static constexpr int kRows = sizeof(T) == 2 ? 192 : 96;
+  static constexpr int kRows = sizeof(T) == 2 ? 128 : 96;
   static constexpr int kChunks = (int)sizeof(T) / 2;  // 16-byte chunks per 8-channel lane part
 };
 
