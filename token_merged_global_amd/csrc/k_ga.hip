@@ -18,11 +18,13 @@
 //
 // Pipeline: ga_variance -> ga_roles (per frame: radix top-k, 2x2 minima) ->
 // ga_scan (per-frame offsets) -> ga_slots (anchor slots, destination and
-// source lists) -> ga_match (MFMA cosine argmax of sources against all
-// destinations; member counts per slot) -> ga_offsets (slot offsets) ->
-// ga_place (every token into its slot's range, any order) -> ga_rank (each
-// member's place inside its range = members with a smaller id).  No sort
-// and no memset: the result does not depend on the order of the atomics.
+// source lists) -> ga_gather (destination rows and inverse norms, bf16) ->
+// ga_match (MFMA cosine argmax of sources against all destinations, split
+// over destinations, packed 64-bit atomic maxima) -> ga_decode (matches,
+// scores, member counts per slot) -> ga_offsets (slot offsets) -> ga_place
+// (every token into its slot's range, any order) -> ga_rank (each member's
+// place inside its range = members with a smaller id).  No sort and no
+// memset: the result does not depend on the order of the atomics.
 #include <algorithm>
 
 #include "common.h"
