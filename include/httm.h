@@ -251,13 +251,17 @@ httm_status httm_debug_read(const httm_plan* plan, const void* ws, const httm_in
 /* In httm_layer the key branch (K similarity, K selection, K/V merge) runs on
  * the library stream concurrently with the query branch: HTTM_T_MERGE_KV
  * times that whole branch there, HTTM_T_SIM and HTTM_T_SELECT the query
- * stream's similarity and selection. */
+ * stream's similarity and selection.  With partition = 1, HTTM_T_SIM times
+ * the whole geometry-aware partition of both streams (on the caller's
+ * stream) and HTTM_T_GA_MATCH its global cosine match alone (one launch);
+ * HTTM_T_SELECT is not recorded. */
 typedef enum {
   HTTM_T_SIM = 0, HTTM_T_SELECT, HTTM_T_MERGE_KV, HTTM_T_MERGE_Q, HTTM_T_OUTLIER,
   HTTM_T_RESTORE,
   HTTM_T_ATTN,       /* the main attention kernel (one launch) */
   HTTM_T_UNMERGE,
   HTTM_T_ATTN_TAIL,  /* exact recompute of queued units + combine of key splits */
+  HTTM_T_GA_MATCH,   /* partition = 1: the global match kernel (one launch) */
   HTTM_T_COUNT
 } httm_timing_stage;
 httm_status httm_set_timing(int32_t stage_mask);

@@ -29,7 +29,8 @@ DEBUG_ITEMS = ["q_match", "q_score", "kv_match", "kv_score", "q_group", "kv_grou
 #: Items that exist only under one partition (block-local / geometry-aware).
 BLOCK_ITEMS = ["q_match", "q_score", "kv_match", "kv_score"]
 GA_ITEMS = ["ga_var", "ga_role", "ga_match", "ga_score", "kv_len"]
-TIMING_STAGES = ["sim", "select", "merge_kv", "merge_q", "outlier", "restore", "attn", "unmerge", "attn_tail"]
+TIMING_STAGES = ["sim", "select", "merge_kv", "merge_q", "outlier", "restore", "attn", "unmerge", "attn_tail",
+                 "ga_match"]
 
 
 class HttmError(RuntimeError):

@@ -722,7 +722,12 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
     gb.off_k = ck.off;
     gb.lenk = lenk;
     stage_begin(HTTM_T_SIM, st);
-    CHECK_LAUNCH(launch_ga_partition(dt, gs, q, k, gb, st));
+    CHECK_LAUNCH(launch_ga_partition(dt, gs, q, k, gb, st, 0));
+    CHECK_LAUNCH(launch_ga_partition(dt, gs, q, k, gb, st, 1));
+    stage_begin(HTTM_T_GA_MATCH, st);
+    CHECK_LAUNCH(launch_ga_partition(dt, gs, q, k, gb, st, 2));
+    stage_end(HTTM_T_GA_MATCH, st);
+    CHECK_LAUNCH(launch_ga_partition(dt, gs, q, k, gb, st, 3));
     stage_end(HTTM_T_SIM, st);
     CHECK_LAUNCH(hipEventRecord(side->fork, st));
     CHECK_LAUNCH(hipStreamWaitEvent(side->st, side->fork, 0));

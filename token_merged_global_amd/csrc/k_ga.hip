@@ -814,51 +814,58 @@ __global__ __launch_bounds__(256) void ga_rank(const int32_t* __restrict__ tmp, 
 }  // namespace
 
 hipError_t launch_ga_partition(int dtype, const GaShape& s, const void* q, const void* k, const GaBuffers& b,
-                               hipStream_t stream) {
-  const int HW = s.H * s.W;
+                               hipStream_t stream, int phase) {
   const int SH = 2 * s.heads;
-  {
+  if (phase == 0) {
     // near-equal tiles of at most 32 columns and 16 rows (<= 256 patches)
     const int tx = ceil_div(s.W, 32), C = ceil_div(s.W, tx);
     const int r0 = std::min(16, 256 / C), ty = ceil_div(s.H, r0), R = ceil_div(s.H, ty);
     if ((R + 2) * (C + 2) > kVarMaxStage) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(tx * ty), (unsigned)s.F, (unsigned)SH);
     HTTM_DISPATCH(dtype, hipLaunchKernelGGL(ga_variance<T>, grid, dim3(256), 0, stream, (const T*)q, (const T*)k,
-                                              s.heads, s.N, s.Tf, s.nsp, s.H, s.W, R, C, tx, b.var));
+                                            s.heads, s.N, s.Tf, s.nsp, s.H, s.W, R, C, tx, b.var));
+    hipLaunchKernelGGL(ga_roles, dim3((unsigned)s.F, (unsigned)SH), dim3(kRoleThreads), 0, stream, b.var, s.heads,
+                       s.N, s.Tf, s.nsp, s.H, s.W, s.F, s.k_protect, b.role, b.fcnt);
+    hipLaunchKernelGGL(ga_scan, dim3((unsigned)SH), dim3(256), 0, stream, b.fcnt, s.F, s.heads, b.foff, b.tot,
+                       b.lenk);
+    hipLaunchKernelGGL(ga_slots, dim3((unsigned)s.F, (unsigned)SH), dim3(kRoleThreads), 0, stream, b.role, s.heads,
+                       s.N, s.Tf, s.F, s.bound, b.foff, b.slot, b.dst_list, b.dst_slot, b.src_list, b.gdst, b.gscore,
+                       b.cnt, b.fill, b.best);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL(ga_roles, dim3((unsigned)s.F, (unsigned)SH), dim3(kRoleThreads), 0, stream, b.var, s.heads, s.N,
-                     s.Tf, s.nsp, s.H, s.W, s.F, s.k_protect, b.role, b.fcnt);
-  hipLaunchKernelGGL(ga_scan, dim3((unsigned)SH), dim3(256), 0, stream, b.fcnt, s.F, s.heads, b.foff, b.tot, b.lenk);
-  hipLaunchKernelGGL(ga_slots, dim3((unsigned)s.F, (unsigned)SH), dim3(kRoleThreads), 0, stream, b.role, s.heads, s.N,
-                     s.Tf, s.F, s.bound, b.foff, b.slot, b.dst_list, b.dst_slot, b.src_list, b.gdst, b.gscore, b.cnt,
-                     b.fill, b.best);
-  GaMatchArgs a;
-  a.x[0] = q;
-  a.x[1] = k;
-  a.heads = s.heads;
-  a.N = s.N;
-  a.chunks = ceil_div(s.max_src, kSrcPerWg);
-  a.tot = b.tot;
-  a.dst_list = b.dst_list;
-  a.dst_slot = b.dst_slot;
-  a.src_list = b.src_list;
-  a.best = b.best;
-  a.snorm = b.snorm;
-  a.dsplit = kDstSplits;
-  a.dg = b.dg;
-  a.dinv = b.dinv;
-  a.dpitch = s.dpitch;
-  const unsigned mgrid = (unsigned)(SH * kDstSplits * a.chunks);
-  if (s.max_src == 0) {
-    // a single frame: no sources, every token is its own group
-  } else if (dtype == 1) {
-    hipLaunchKernelGGL(ga_gather, dim3((unsigned)(s.dpitch / 64), (unsigned)SH), dim3(256), 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, s.heads, s.N, s.dpitch, b.tot, b.dst_list, b.dg,
-                       b.dinv);
-    hipLaunchKernelGGL(ga_match_bf16, dim3(mgrid), dim3(256), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(ga_match_f32, dim3(mgrid), dim3(256), 0, stream, a);
+  if (s.max_src == 0 && phase < 3) return hipSuccess;  // a single frame: no sources, every token is its own group
+  if (phase == 1) {
+    if (dtype == 1)
+      hipLaunchKernelGGL(ga_gather, dim3((unsigned)(s.dpitch / 64), (unsigned)SH), dim3(256), 0, stream,
+                         (const uint16_t*)q, (const uint16_t*)k, s.heads, s.N, s.dpitch, b.tot, b.dst_list, b.dg,
+                         b.dinv);
+    return hipGetLastError();
   }
+  if (phase == 2) {
+    GaMatchArgs a;
+    a.x[0] = q;
+    a.x[1] = k;
+    a.heads = s.heads;
+    a.N = s.N;
+    a.chunks = ceil_div(s.max_src, kSrcPerWg);
+    a.tot = b.tot;
+    a.dst_list = b.dst_list;
+    a.dst_slot = b.dst_slot;
+    a.src_list = b.src_list;
+    a.best = b.best;
+    a.snorm = b.snorm;
+    a.dsplit = kDstSplits;
+    a.dg = b.dg;
+    a.dinv = b.dinv;
+    a.dpitch = s.dpitch;
+    const unsigned mgrid = (unsigned)(SH * kDstSplits * a.chunks);
+    if (dtype == 1)
+      hipLaunchKernelGGL(ga_match_bf16, dim3(mgrid), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(ga_match_f32, dim3(mgrid), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  if (phase != 3) return hipErrorInvalidValue;
   if (s.max_src > 0)
     hipLaunchKernelGGL(ga_decode, dim3((unsigned)ceil_div(s.max_src, 256), (unsigned)SH), dim3(256), 0, stream,
                        dtype, s.heads, s.N, s.bound, b.tot, b.dst_list, b.dst_slot, b.src_list, b.best, b.snorm,

@@ -134,8 +134,11 @@ struct GaBuffers {
   int32_t* off_k;
   int32_t* lenk;       // [h] groups of the key stream (keys per head)
 };
+// In four phases, enqueued in order: 0 classes (variance, roles, per-frame
+// offsets, anchor slots and lists), 1 destination gather (bf16), 2 the match
+// (one launch), 3 groups (decode, offsets, placement, rank).
 hipError_t launch_ga_partition(int dtype, const GaShape& s, const void* q, const void* k, const GaBuffers& b,
-                               hipStream_t stream);
+                               hipStream_t stream, int phase);
 
 // Key splits for a layer of q_capacity packed rows; rows per work unit.
 int attention_split(int64_t q_capacity, int heads);
