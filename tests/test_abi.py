@@ -36,6 +36,21 @@ def test_library_exports_every_declared_function():
         assert n in H.EXPORTS, n
 
 
+def _enum_names(typedef: str, prefix: str):
+    """Member names of one `typedef enum { ... } <typedef>;` of the header, in order, without COUNT."""
+    txt = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "httm.h")).read(), flags=re.S)
+    body = re.search(r"typedef enum \{([^}]*)\}\s*" + typedef + r"\s*;", txt).group(1)
+    names = [m.split("=")[0].strip() for m in body.split(",") if m.strip()]
+    assert names[-1] == prefix + "COUNT"
+    return [n[len(prefix):].lower() for n in names[:-1]]
+
+
+def test_binding_name_lists_follow_the_header_enums():
+    # the binding indexes the library's tables by position in these lists
+    assert H.TIMING_STAGES == _enum_names("httm_timing_stage", "HTTM_T_")
+    assert H.DEBUG_ITEMS == _enum_names("httm_debug_item", "HTTM_DBG_")
+
+
 def _plans():
     for name in ["tiny", "vggt30", "vggt100", "vggt200", "vggt500"]:
         yield name, gen.WORKLOADS[name]
