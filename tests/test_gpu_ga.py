@@ -263,3 +263,31 @@ def test_ga_edge_geometry(case):
     assert rep.delta_nonexact == 0
     if case["frames"] == 1:
         assert rep.n_src == 0
+
+
+def test_ga_match_timing_stage():
+    """The global match has its own timing stage: recorded for every call
+    under the geometry-aware partition, never under the block-local one,
+    and inside the span of the whole partition (the similarity stage)."""
+    say("[ga timing stage]")
+    for part in (1, 0):
+        w = small(frames=4).with_(partition=part)
+        x = gen.layer_inputs(w, seed=gen.DEFAULT_SEED)
+        plan = H.Plan.from_workload(w)
+        q, k, v = (to_dev(x[t], w.dtype) for t in "qkv")
+        ws = H.workspace(plan)
+        H.set_timing(["sim", "ga_match"])
+        try:
+            for _ in range(3):
+                H.layer(plan, q, k, v, ws=ws)
+            torch.cuda.synchronize()
+            st, calls = H.get_timing()
+        finally:
+            H.set_timing([])
+        say("  ", part, calls, st["sim"], st["ga_match"])
+        assert calls == 3
+        assert st["sim"] > 0
+        if part == 1:
+            assert 0 < st["ga_match"] <= st["sim"]
+        else:
+            assert st["ga_match"] == 0
