@@ -97,11 +97,26 @@ __global__ __launch_bounds__(256) void ga_variance(const T* __restrict__ q, cons
   const int y0 = (blockIdx.x / tiles_x) * R, x0 = (blockIdx.x % tiles_x) * C;
   const int sw = C + 2, nst = (R + 2) * sw;
   const u32x4* X = reinterpret_cast<const u32x4*>((st == 0 ? q : k) + ((size_t)head * N + (size_t)f * Tf + nsp) * kD);
-  for (int e = tid; e < nst * NC; e += 256) {
+  // every load of the tile is issued before the first LDS store (a loop of
+  // load-then-store would wait out one memory latency per iteration);
+  // halo chunks outside the frame are never read and stay unwritten
+  constexpr int kPer = (kVarMaxStage * NC + 255) / 256;
+  u32x4 buf[kPer];
+  int dst[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = tid + j * 256;
     const int i = e / NC, c = e - i * NC;
     const int yy = y0 - 1 + i / sw, xx = x0 - 1 + i % sw;
-    if (yy >= 0 && yy < H && xx >= 0 && xx < W) sX[i * P + c] = X[(size_t)(yy * W + xx) * NC + c];
+    dst[j] = -1;
+    if (e < nst * NC && yy >= 0 && yy < H && xx >= 0 && xx < W) {
+      buf[j] = X[(size_t)(yy * W + xx) * NC + c];
+      dst[j] = i * P + c;
+    }
   }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (dst[j] >= 0) sX[dst[j]] = buf[j];
   __syncthreads();
   const int ly = tid / C, lx = tid - ly * C;
   const int y = y0 + ly, x = x0 + lx;
