@@ -1,0 +1,49 @@
+"""bench.py's output contract on a GPU: one JSON line with the metric, the
+whole-job value, the dominant kernel's roofline (achieved / peak from the
+live launch timing) and the oracle's CPU baseline, for both partitions.
+Run on the small 4-frame workload so that it takes seconds."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.gpu
+
+
+def _bench(*args):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny", "--steps", "3",
+                        "--warmup", "1", "--dense-reps", "0", "--cached-layers", "0", "--cpu-heads", "1", *args],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, r.stdout
+    return json.loads(lines[0])
+
+
+@pytest.mark.parametrize("partition", ["httm", "ga"])
+def test_bench_json_contract(partition):
+    d = _bench("--partition", partition)
+    for key in ["metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"]:
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
+    assert d["value"] > 0 and d["ms_per_step"] > 0 and d["higher_is_better"] is True
+    assert d["vs_baseline"] is None
+    assert isinstance(d["config"]["workload"], str) and d["config"]["tokens"] > 0
+    # whole-job throughput: tokens of one layer per step time
+    assert d["value"] == pytest.approx(d["config"]["tokens"] / (d["ms_per_step"] * 1e-3), rel=1e-9)
+    rf = d["roofline"]
+    assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s"
+    assert rf["avg_launch_ms"] > 0 and rf["launches_timed"] == 3
+    assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"], rel=1e-9)
+    if partition == "ga":
+        assert d["config"]["partition"] == "geometry-aware"
+        assert d["geometry_aware"]["match_flop"] > 0
+        kernels = {rf["kernel"], d["roofline_other_kernel"]["kernel"]}
+        assert any(k.startswith("ga_match") for k in kernels) and any(k.startswith("attn") for k in kernels)
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
