@@ -60,7 +60,7 @@ class Params:
     kv_dst_stride: int = 0
     block_order: int = 0  # 0 frame-major (R3), 1 frame-minor
     softmax_scale: float = 0.0  # 0 -> 1/sqrt(d_head) (R21)
-    partition: int = 0  # 0 HTTM temporal blocks; 1 geometry-aware three-class partition (R24)
+    partition: int = 0  # 0 HTTM temporal blocks; 1 geometry-aware three-class partition (R31)
     protect_pct: float = 10.0  # geometry-aware partition: percent of each frame's patches protected
 
     @property
@@ -268,7 +268,7 @@ def match_stream(x: np.ndarray, p: Params, ratio: float, stride: int) -> StreamM
 # key designs 1-3: a geometry score per token, three token classes (protected
 # high-score tokens, destinations, sources) and a cosine match of every
 # source to its most similar destination.  Used here, like HTTM's matching,
-# per head and per stream (R1).  Readings R24-R29 (design notes).
+# per head and per stream (R1).  Readings R31-R36 (design notes).
 
 
 def _box3_sum(a: np.ndarray, axis: int) -> np.ndarray:
@@ -283,12 +283,12 @@ def _box3_sum(a: np.ndarray, axis: int) -> np.ndarray:
 
 
 def token_variance_map(x: np.ndarray, p: Params) -> np.ndarray:
-    """Token variance map v (LiteVGGT page, key design 1; variance half, R24).
+    """Token variance map v (LiteVGGT page, key design 1; variance half, R31).
 
     Patch tokens of each frame are laid on their grid; v of a token is the
     mean over channels of the variance of the features in its 3x3
     neighbourhood (average pooling of x and x^2, windows clipped at the grid
-    edge, R25).  fp32 in a fixed order (R26): per channel, each row's
+    edge, R32).  fp32 in a fixed order (R33): per channel, each row's
     available cells are summed left to right, then the available rows top to
     bottom (for x and for x*x); var = s2/cnt - (s1/cnt)^2; v = (sum of var
     over channels in ascending order) / d.  Special tokens get 0 (they are
@@ -320,7 +320,7 @@ ROLE_SRC, ROLE_DST, ROLE_PROTECT, ROLE_SPECIAL = 0, 1, 2, 3
 
 
 def ga_roles(v: np.ndarray, p: Params) -> np.ndarray:
-    """Three token classes (LiteVGGT page, key design 2; R27, R28).
+    """Three token classes (LiteVGGT page, key design 2; R34, R35).
 
     Per frame the k = floor(protect_pct/100 * H*W + 1e-9) patches with the
     highest score are protected (ties to the smaller patch index).  Every
@@ -368,7 +368,7 @@ def ga_match_stream(x: np.ndarray, p: Params, chunk: int = 4096) -> StreamMatch:
     """Geometry-aware grouping of one head and stream (LiteVGGT page, key designs 2-3).
 
     Every source joins its most similar destination over the whole sequence
-    (cosine of RowNorm rows, fp32; ties to the smaller destination id, R29);
+    (cosine of RowNorm rows, fp32; ties to the smaller destination id, R36);
     groups are each destination with its sources, and singletons for
     protected and special tokens.
     """
@@ -548,7 +548,7 @@ def match_heads(q: np.ndarray, k: np.ndarray, p: Params, heads: Sequence[int]) -
     """Steps 1-4 for every listed head (head-wise merging, HTTM page, key design 1)."""
     tr = Trace()
     for i in range(len(heads)):
-        if p.partition == 1:  # geometry-aware three-class partition (R24)
+        if p.partition == 1:  # geometry-aware three-class partition (R31)
             tr.q_match.append(ga_match_stream(q[i], p))
             tr.k_match.append(ga_match_stream(k[i], p))
         else:

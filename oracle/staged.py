@@ -13,8 +13,9 @@ on the implementation's own indices, so a counted near-tie never cascades:
         map and classes exactly, then matches and scores over all
         destinations);
   (ii)  top-r selection and the resulting groups (groups exactly);
-  (iii) deviations on the implementation's query groups, and the global
-        outlier choice on the implementation's deviations (exactly);
+  (iii) deviations on the implementation's query groups (bit for bit), and
+        the global outlier choice on the implementation's deviations
+        (exactly);
   (iv)  final query partition (exactly) and outputs within tolerance.
 """
 from __future__ import annotations
@@ -195,7 +196,7 @@ def check_layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, p: O.Params, gpu: D
                 out_gpu: np.ndarray, out_heads: Optional[Sequence[int]] = None,
                 rows: Optional[np.ndarray] = None, out_tol: Optional[float] = None,
                 match_heads: Optional[Sequence[int]] = None, rel_tol: Optional[float] = None,
-                workers: int = 1, out_half_ulp: bool = False) -> Report:
+                workers: int = 1, out_half_ulp: bool = False, delta_exact: bool = True) -> Report:
     """Staged parity of one layer.
 
     gpu: q_match, q_score, kv_match, kv_score ([h][src]), q_group, kv_group,
@@ -210,6 +211,9 @@ def check_layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, p: O.Params, gpu: D
     RMS (tiny or heavily merged layers), since there one rounding step of the
     largest outputs is larger than 2e-2 x RMS.  ``workers`` threads share the
     per-head work (numpy releases the GIL in its array kernels).
+    ``delta_exact`` (default) requires the deviations bit for bit on the
+    implementation's groups (the same fp32 operation sequence); False
+    accepts differences within 1e-5 x max(1, delta) and only counts them.
     """
     rep = Report()
     h, N = q.shape[0], q.shape[1]
@@ -252,6 +256,10 @@ def check_layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, p: O.Params, gpu: D
     dg = gpu["delta"].astype(np.float32)
     rep.delta_nonexact = int((dg != delta_o).sum())
     rep.max_delta_err = float(np.abs(dg.astype(np.float64) - delta_o).max())
+    if delta_exact and rep.delta_nonexact:
+        h0, n0 = (int(a[0]) for a in np.nonzero(dg != delta_o))
+        raise ParityError(f"deviation differs at {rep.delta_nonexact} tokens (first head {h0} token {n0}: "
+                          f"{dg[h0, n0]!r} vs {delta_o[h0, n0]!r})")
     tol = NEAR_TIE * np.maximum(1.0, delta_o)
     if (np.abs(dg.astype(np.float64) - delta_o) > tol).any():
         raise ParityError(f"deviation error {rep.max_delta_err:.3g}")

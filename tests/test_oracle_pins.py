@@ -530,3 +530,77 @@ def test_ga_protect_all_is_exact_attention():
     for h in range(w.heads):
         ref = O.attention(x["q"][h], x["k"][h], x["v"][h], p.scale)
         assert np.abs(tr.out[h] - ref).max() <= 1e-5
+
+
+# --------------------------------------------------------------------------
+# Cached-index layer (LiteVGGT page, key design 3: merge indices of one layer
+# are reused by the next ones; only the means are recomputed)
+# --------------------------------------------------------------------------
+def test_layer_cached_with_the_layers_own_indices_equals_the_layer():
+    """Reusing a layer's own final query partition and key partition on the
+    same inputs reproduces that layer's output bit for bit; swapping the two
+    partitions (a plausible slip) does not."""
+    for part in (0, 1):
+        p = _small(pct=15.0) if part == 0 else _ga_params(heads=2, outlier_pct=15.0)
+        q, k, v = (_rand_qkv(p, 21) if part == 0 else
+                   [np.random.default_rng(21 + i).standard_normal((2, p.n_tokens, 64)).astype(np.float32)
+                    for i in range(3)])
+        tr = O.layer(q, k, v, p)
+        got = O.layer_cached(q, k, v, p, tr.q_final_rep, tr.k_rep)
+        assert np.array_equal(got, tr.out)
+        rows = np.array([0, 3, p.n_tokens - 1])
+        # a row subset runs the fp64 products with other BLAS blocking: equal to rounding
+        assert np.abs(O.layer_cached(q, k, v, p, tr.q_final_rep, tr.k_rep, rows=rows) - tr.out[:, rows]).max() < 1e-12
+        assert np.array_equal(O.layer_cached(q, k, v, p, tr.q_final_rep, tr.k_rep, out_heads=[1]), tr.out[[1]])
+        swapped = O.layer_cached(q, k, v, p, tr.k_rep, tr.q_final_rep)
+        assert not np.allclose(swapped, tr.out)
+
+
+def test_layer_cached_hand_example_scaled_inputs():
+    """On the hand block, the cached layer with the hand-derived partitions
+    (p = 25 %) and inputs scaled by 2 equals SDPA on twice the hand-derived
+    merged rows (means are linear; the scale is exact in fp32)."""
+    ex, p, q, k, v = _hand()
+    e = ex["expected"]
+    rep_of = lambda groups: np.array([min(g) for n in range(8) for g in groups if n in g])
+    qf = rep_of(e["p25"]["final_groups"])
+    kr = rep_of(e["groups"])  # k == q: the key groups are the query groups before outliers
+    got = O.layer_cached(2 * q, 2 * k, 2 * v, p, [qf], [kr])[0]
+    fq = e["p25"]["final_q"]
+    slots = sorted(int(r) for r in fq)
+    Q = 2 * np.array([[_expr(x) for x in fq[str(r)]] for r in slots])
+    kreps = sorted(int(r) for r in e["v_means"])
+    K = 2 * np.array([[_expr(x) for x in e["q_means"][str(r)]] for r in kreps])
+    V = 2 * np.array([[_expr(x) for x in e["v_means"][str(r)]] for r in kreps])
+    o = _sdpa64(Q, K, V, 1.0)
+    want = np.stack([o[slots.index(int(qf[n]))] for n in range(8)])
+    assert np.allclose(got, want, atol=1e-6)
+
+
+def test_layer_cached_value_shift_and_singletons():
+    """A constant added to every value row shifts every output row by that
+    constant (softmax weights sum to one and a mean of shifted rows is the
+    shifted mean); singleton partitions give exact attention (fp64 SDPA)."""
+    p = _small(pct=10.0)
+    q, k, v = _rand_qkv(p, 22)
+    tr = O.layer(q, k, v, p)
+    c = np.float32(0.5)  # exact in fp32 next to values of this size
+    base = O.layer_cached(q, k, v, p, tr.q_final_rep, tr.k_rep)
+    shifted = O.layer_cached(q, k, v + c, p, tr.q_final_rep, tr.k_rep)
+    assert np.abs(shifted - base - c).max() < 1e-6
+    ident = [np.arange(p.n_tokens)] * p.heads
+    single = O.layer_cached(q, k, v, p, ident, ident)
+    for h in range(p.heads):
+        assert np.abs(single[h] - _sdpa64(q[h], k[h], v[h], p.scale)).max() < 1e-12
+
+
+def test_layer_cached_head_permutation():
+    """Heads are independent: permuting the heads of the inputs and of the
+    cached partitions permutes the outputs."""
+    p = _small(heads=3, pct=10.0)
+    q, k, v = _rand_qkv(p, 23)
+    tr = O.layer(q, k, v, p)
+    perm = [2, 0, 1]
+    got = O.layer_cached(q[perm], k[perm], v[perm], p, [tr.q_final_rep[h] for h in perm],
+                         [tr.k_rep[h] for h in perm])
+    assert np.array_equal(got, tr.out[perm])

@@ -13,6 +13,7 @@ fallback: if the library is missing the import of ``lib()`` raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Dict, List, Optional, Tuple
@@ -103,18 +104,13 @@ _LIB = None
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded library; raises if it was not built (no fallback exists).
-
-    HTTM_LIB, if set, names another build of the same library to load instead
-    (side-by-side comparisons of kernel variants); it must exist too.
-    """
+    """The loaded in-tree library; raises if it was not built (no fallback exists)."""
     global _LIB
     if _LIB is None:
-        path = os.environ.get("HTTM_LIB") or LIB_PATH
-        if not os.path.exists(path):
-            raise RuntimeError(f"{path} is missing: build it with "
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m token_merged_global_amd.build` (the HTTM layer has no fallback)")
-        L = ctypes.CDLL(path)
+        L = ctypes.CDLL(LIB_PATH)
         for name, (args, res) in EXPORTS.items():
             f = getattr(L, name)
             f.argtypes = args
@@ -222,6 +218,18 @@ def workspace(plan: Plan, kind: str = "layer"):
     return torch.empty(n, dtype=torch.uint8, device="cuda")
 
 
+def _on(stream):
+    """Allocation context of the stream a call runs on.
+
+    Buffers that a call allocates for itself (a temporary workspace, a fresh
+    output) are taken from the caching allocator under the stream the
+    kernels run on, so that the allocator orders their reuse after that
+    stream's work (a block taken under another stream could be handed out
+    again while this call's kernels still run)."""
+    torch = _torch()
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 class CachedIndex:
     """Device buffer holding the merge indices of one layer (LiteVGGT-style reuse)."""
 
@@ -236,10 +244,11 @@ def layer(plan: Plan, q, k, v, ws=None, out=None, index: Optional[CachedIndex] =
     """One HTTM layer on the GPU.  Returns ``out`` (and the index if ``keep_index``)."""
     torch = _torch()
     _check_qkv(plan, q, k, v)
-    ws = workspace(plan) if ws is None else ws
-    out = torch.empty_like(q) if out is None else out
-    if keep_index and index is None:
-        index = CachedIndex(plan)
+    with _on(stream):
+        ws = workspace(plan) if ws is None else ws
+        out = torch.empty_like(q) if out is None else out
+        if keep_index and index is None:
+            index = CachedIndex(plan)
     _check(lib().httm_layer(plan.handle, ws.data_ptr(), ws.numel(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                             out.data_ptr(), ctypes.byref(index.c) if index is not None else None,
                             _stream_ptr(stream)))
@@ -250,8 +259,9 @@ def layer_cached(plan: Plan, index: CachedIndex, q, k, v, ws=None, out=None, str
     """A layer reusing ``index`` from an earlier ``layer`` call with the same plan."""
     torch = _torch()
     _check_qkv(plan, q, k, v)
-    ws = workspace(plan) if ws is None else ws
-    out = torch.empty_like(q) if out is None else out
+    with _on(stream):
+        ws = workspace(plan) if ws is None else ws
+        out = torch.empty_like(q) if out is None else out
     _check(lib().httm_layer_cached(plan.handle, ws.data_ptr(), ws.numel(), ctypes.byref(index.c),
                                    q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                    _stream_ptr(stream)))
@@ -281,8 +291,9 @@ def attention_dense(plan: Plan, q, k, v, ws=None, out=None, stream=None):
     """Unmerged softmax(scale q k^T) v per head on the same attention kernel."""
     torch = _torch()
     _check_qkv(plan, q, k, v)
-    ws = workspace(plan, "dense") if ws is None else ws
-    out = torch.empty_like(q) if out is None else out
+    with _on(stream):
+        ws = workspace(plan, "dense") if ws is None else ws
+        out = torch.empty_like(q) if out is None else out
     _check(lib().httm_attention_dense(plan.handle, ws.data_ptr(), ws.numel(), q.data_ptr(), k.data_ptr(),
                                       v.data_ptr(), out.data_ptr(), _stream_ptr(stream)))
     return out
