@@ -1,21 +1,31 @@
 #!/usr/bin/env python3
-"""Benchmark of one HTTM global-attention layer (merge + attention + unmerge) on one GPU.
+"""Benchmark of HTTM global-attention layers (merge + attention + unmerge) on one GPU.
 
-A step is one full layer call (httm_layer: similarity + argmax, top-r
+A step is one pass of the whole hot path over one batch of synthetic tokens
+that are already resident in HBM.  For the default workload, the 500-frame
+stack (500 frames x (37x37 patches + 5 special tokens) = 687,000 tokens,
+16 heads x 64 channels, bf16), a step is the stack of six layers the cached
+mode is made for: layer 0 runs the full layer (similarity + argmax, top-r
 grouping, K/V merge, query merge + deviation, cross-head outlier select,
-restore, ragged attention, unmerge) over one batch of synthetic tokens that
-are already resident in HBM.  Prints one JSON line.
+restore, ragged attention, unmerge) and fills the merge index; layers 1-5
+each run on their own inputs and reuse that index (K/V and query means,
+attention, unmerge).  The value is the aggregate layer throughput
+6 N / (time of the six layers); layer 0 and the cached layers are also
+reported on their own.  Single-layer workloads (tiny, vggt30, vggt100,
+vggt200) time one full layer per step.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload vggt30] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload vggt500] [--no-cpu-baseline]
 
-By default W and K are sized from a one-step probe so that the warmup and
-the timed region each cover about 0.5 s of GPU work (clocks ramp up over the
-first few hundred milliseconds of load); the JSON line reports the W and K
-actually used.
+By default W and K are sized from a one-step probe so that the warmup and the
+timed region each cover about 0.5 s of GPU work (clocks ramp up over the
+first few hundred milliseconds of load), at least 3 steps each.
 
-Workload default: 30 frames x (37x37 patches + 5 special tokens) = 41,220
-tokens, 16 heads x 64 channels, bf16; blocks n_s=128 x n_t=30; queries merged
-90 % with 10 % outliers restored; keys/values merged 50 %.
+Besides the headline, the line carries the dominant kernel's roofline (the
+attention kernel, from HIP events on its launch stream over the timed
+region), every other kernel's roofline from a separate pass with events
+around each stage (``rooflines``), the in-run speedup over the same engine's
+unmerged attention, the 30-frame layer as extra keys (``vggt30``), and the
+oracle's time on a bounded sample on the host cores (``cpu_baseline``).
 """
 from __future__ import annotations
 
@@ -39,6 +49,7 @@ METRIC = "HTTM global-attn layer tokens/s (merge+attn+unmerge), 30–500 frames"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MFMA_F32_PEAK_TFLOPS = 157.3
+TRAFFIC_UNIT = "bytes per launch (HBM, rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0)"
 
 
 def log(*a):
@@ -46,28 +57,32 @@ def log(*a):
 
 
 ATTN_SRC = os.path.join(ROOT, "token_merged_global_amd", "csrc", "k_attn.hip")
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_fast_hbm_traffic_vggt30.md")
 GA_SRC = os.path.join(ROOT, "token_merged_global_amd", "csrc", "k_ga.hip")
-GA_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "ga_match_hbm_traffic_vggt30.md")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
-def measured_traffic(workload: str, dtype: str, profile: str = TRAFFIC_PROFILE, src: str = ATTN_SRC):
-    """HBM bytes per launch of a kernel from a committed rocprofv3 counter summary.
+def measured_traffic(workload: str, kernel: str, src: str):
+    """HBM bytes per launch of `kernel` from a committed rocprofv3 counter summary.
 
-    Returned only while the kernel's source is the one the counters were
-    taken with (sha256 recorded in the summary) and for that workload;
-    otherwise None.
+    Summaries under profiles/ record the kernel, the workload, the sha256 of
+    the kernel's source and the scaled bytes per launch.  The value is
+    returned only while the source is unchanged since the counters were
+    taken; otherwise None.
     """
-    if dtype != "bf16" or not os.path.exists(profile):
-        return None
-    txt = open(profile).read()
-    sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", txt)
-    wl = re.search(r"workload:\s*(\S+)", txt)
-    nb = re.search(r"bytes_per_launch:\s*([0-9]+)", txt)
-    if not (sha and wl and nb) or wl.group(1) != workload:
+    if not os.path.isdir(PROFILES):
         return None
     cur = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    return int(nb.group(1)) if cur == sha.group(1) else None
+    for f in sorted(os.listdir(PROFILES)):
+        if not f.endswith(".md"):
+            continue
+        txt = open(os.path.join(PROFILES, f)).read()
+        kn = re.search(r"kernel:\s*(\S+)", txt)
+        sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", txt)
+        wl = re.search(r"workload:\s*(\S+)", txt)
+        nb = re.search(r"bytes_per_launch:\s*([0-9]+)", txt)
+        if kn and sha and wl and nb and kn.group(1) == kernel and wl.group(1) == workload and sha.group(1) == cur:
+            return int(nb.group(1))
+    return None
 
 
 def describe(w) -> str:
@@ -75,29 +90,169 @@ def describe(w) -> str:
         return (f"{w.name}: {w.frames} frames x ({w.grid_h}x{w.grid_w}+{w.n_special}) = {w.n_tokens} tokens, "
                 f"{w.heads} heads x {w.d_head}, {w.dtype}, geometry-aware partition ({w.protect_pct:g}% "
                 f"protected, global match) + {w.outlier_pct:g}% outliers")
+    stack = (f", stack of {w.layers} layers (layer 0 full, layers 1-{w.layers - 1} reuse its merge indices)"
+             if w.layers > 1 else "")
     return (f"{w.name}: {w.frames} frames x ({w.grid_h}x{w.grid_w}+{w.n_special}) = {w.n_tokens} tokens, "
             f"{w.heads} heads x {w.d_head}, {w.dtype}, n_s={w.n_s} n_t={w.n_t}, q merge {w.q_ratio:g} + "
-            f"{w.outlier_pct:g}% outliers, kv merge {w.kv_ratio:g}")
+            f"{w.outlier_pct:g}% outliers, kv merge {w.kv_ratio:g}{stack}")
 
 
-def cpu_baseline(w, x, heads: int):
-    """The oracle, untouched, on a bounded sample: the first `heads` heads of the layer."""
+# --------------------------------------------------------------------------- algorithmic work
+def algorithmic(w, plan, lq: np.ndarray, lkh: np.ndarray):
+    """Algorithmic FLOP / bytes per launch of every kernel of a layer.
+
+    Bytes count each tensor element the step must read or write once (no
+    re-reads, no padding); FLOP count 2 per multiply-add of the algorithm
+    (similarity: 2 d |S_b| |D_b| per block and head; attention:
+    4 d L_k L_q per head).
+    """
+    h, N, d = w.heads, w.n_tokens, w.d_head
+    es = 2 if w.dtype == "bf16" else 4
+    info = plan.info
+    E = h * N * d * es
+    Gq, Lk, ko = info["q_groups"], info["kv_len"], info["n_outliers"]
+    sum_lq = float(lq.sum())
+    a = {}
+    if getattr(w, "partition", 0) != 1:
+        bl = plan.blocks()
+        a["sim_q"] = ("flop", 2.0 * d * h * sum(b["q_src"] * b["q_dst"] for b in bl))
+        a["sim_k"] = ("flop", 2.0 * d * h * sum(b["kv_src"] * b["kv_dst"] for b in bl))
+        # matches + scores read, members + group ids written, offsets written
+        a["select_q"] = ("bytes", 8.0 * h * info["q_src"] + 8.0 * h * N + 4.0 * h * Gq)
+        a["select_k"] = ("bytes", 8.0 * h * info["kv_src"] + 8.0 * h * N + 4.0 * h * Lk)
+    a["merge_kv"] = ("bytes", 2.0 * E + 4.0 * h * N + 4.0 * h * (Lk + 1) + 2.0 * float(lkh.sum()) * d * es)
+    a["merge_q"] = ("bytes", E + 4.0 * h * N + 4.0 * h * (Gq + 1) + 4.0 * h * Gq * d + 4.0 * h * N)
+    # deviations read once, mask written once; per-group outlier counts read the mask and the group ids
+    a["outlier"] = ("bytes", 4.0 * h * N + 1.0 * h * N + 1.0 * h * N + 4.0 * h * N + 4.0 * h * Gq)
+    a["restore"] = ("bytes", 4.0 * h * N + 4.0 * h * (Gq + 1) + 1.0 * h * N + 4.0 * h * Gq + 4.0 * h * Gq * d
+                    + ko * d * es + sum_lq * d * es + 4.0 * h * N + 4.0 * (sum_lq + h) + 4.0 * h * N)
+    a["attn"] = ("flop", 4.0 * d * float((lkh * lq).sum()))
+    a["unmerge"] = ("bytes", 4.0 * h * N + sum_lq * d * es + E)
+    a["merge_q_cached"] = ("bytes", E + 4.0 * h * N + 4.0 * (sum_lq + h) + sum_lq * d * es)
+    return a
+
+
+def roofline_entry(kernel, kind_val, ms, dtype, calls=None):
+    kind, val = kind_val
+    if ms <= 0:
+        return None
+    if kind == "flop":
+        peak = MFMA_BF16_PEAK_TFLOPS if dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+        ach = val / (ms * 1e-3) / 1e12
+        r = {"bound": "mfma", "kernel": kernel, "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+             "frac": ach / peak, "algorithmic_flop": val, "avg_launch_ms": ms}
+    else:
+        ach = val / (ms * 1e-3) / 1e9
+        r = {"bound": "hbm", "kernel": kernel, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": ach / HBM_PEAK_GBS, "algorithmic_bytes": val, "avg_launch_ms": ms}
+    if calls is not None:
+        r["launches_timed"] = calls
+    return r
+
+
+# stage -> (algorithmic key, kernel(s) the stage brackets)
+STAGE_KERNELS = {
+    "sim": ("sim_q", "sim_argmax_bf16 (query stream)"),
+    "sim_k": ("sim_k", "sim_argmax_bf16 (key stream, library stream)"),
+    "select": ("select_q", "block_select (query stream)"),
+    "select_k": ("select_k", "block_select (key stream, library stream)"),
+    "merge_kv": ("merge_kv", "merge_kv (library stream)"),
+    "merge_q": ("merge_q", "merge_q"),
+    "outlier": ("outlier", "radix_hist<1>, radix_hist<2>, radix_mark, radix_ties, count_outliers"),
+    "restore": ("restore", "restore_scan, restore_rows"),
+    "unmerge": ("unmerge", "unmerge"),
+}
+
+
+def stage_rooflines(stages, alg, dtype, cached_stages=None):
+    out = {}
+    for st, (key, kern) in STAGE_KERNELS.items():
+        if key in alg and stages.get(st, 0) > 0:
+            out[key] = roofline_entry(kern, alg[key], stages[st], dtype)
+    if cached_stages:
+        if cached_stages.get("merge_q", 0) > 0:
+            out["merge_q_cached"] = roofline_entry("merge_q_cached", alg["merge_q_cached"],
+                                                   cached_stages["merge_q"], dtype)
+        if cached_stages.get("merge_kv", 0) > 0:
+            out["merge_kv_cached_layer"] = roofline_entry("merge_kv (cached layer, library stream)",
+                                                          alg["merge_kv"], cached_stages["merge_kv"], dtype)
+    return out
+
+
+# --------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(w, x0, xc, n_cached: int, rows: int = 512, head: int = 0):
+    """The oracle, as it stands, timed stage by stage on a bounded sample.
+
+    Sample: one head of the workload.  Matching, top-r, query means and
+    deviations, restore, the final means and unmerge run on the whole
+    sequence of that head; the global outlier choice runs over h x N
+    deviations (that head's, repeated for every head); attention runs for
+    `rows` merged query rows of that head against all of its merged keys.
+    One layer's CPU time is extrapolated as h x (per-head stages) + select +
+    h x (attention per row x merged query rows); a cached layer as
+    h x (final means + unmerge + attention).  The stack is layer 0 plus the
+    cached layers; the value is tokens of the stack per second.
+    """
     import oracle as O
     from threadpoolctl import threadpool_info
 
-    ws = w.with_(heads=heads)
-    p = O.Params.from_workload(ws)
+    p1 = O.Params.from_workload(w.with_(heads=1))
+    pf = O.Params.from_workload(w)
+    q, k, v = (x0[t][head:head + 1] for t in "qkv")
+    T = {}
     t0 = time.perf_counter()
-    O.layer(x["q"][:heads], x["k"][:heads], x["v"][:heads], p)
-    dt = time.perf_counter() - t0
+    tr = O.match_heads(q, k, p1, [0])
+    T["match"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    delta = O.deviations(q, [tr.q_match[0].rep])
+    T["deviation"] = time.perf_counter() - t0
+    tiled = np.tile(delta, (w.heads, 1))
+    t0 = time.perf_counter()
+    mask = O.select_outliers(tiled, O.outlier_budget(pf))
+    T["select"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    fin = O.restore_partition(tr.q_match[0].rep, mask[0])
+    T["restore"] = time.perf_counter() - t0
+
+    def means_attn_unmerge(qq, kk, vv):
+        t0 = time.perf_counter()
+        qp, kp = O.partition(fin), O.partition(tr.k_rep[0])
+        qt, kt, vt = O.group_means(qq, qp), O.group_means(kk, kp), O.group_means(vv, kp)
+        tm = time.perf_counter() - t0
+        sel = np.sort(np.random.default_rng(0).choice(len(qt), min(rows, len(qt)), replace=False))
+        t0 = time.perf_counter()
+        o = O.attention(qt[sel], kt, vt, pf.scale)
+        ta = (time.perf_counter() - t0) * len(qt) / len(sel)
+        full = np.zeros((len(qt), o.shape[1]))
+        t0 = time.perf_counter()
+        O.unmerge(full, qp)
+        tu = time.perf_counter() - t0
+        return tm, ta, tu, len(qt)
+
+    T["means"], T["attention_extrapolated"], T["unmerge"], lq = means_attn_unmerge(q[0], k[0], v[0])
+    h = w.heads
+    layer0 = h * (T["match"] + T["deviation"] + T["restore"] + T["means"] + T["unmerge"] +
+                  T["attention_extrapolated"]) + T["select"]
+    cached = 0.0
+    if n_cached > 0:
+        xq, xk, xv = (xc[t][head] for t in "qkv")
+        tm, ta, tu, _ = means_attn_unmerge(xq, xk, xv)
+        cached = h * (tm + ta + tu)
+    stack = layer0 + n_cached * cached
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    scale = w.heads / heads
-    return {"value": w.n_tokens / (dt * scale), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"full oracle layer on {heads} of {w.heads} heads of the same workload "
-                       f"(outlier budget over those heads), {dt:.2f} s wall, scaled x{scale:g} to {w.heads} heads; "
-                       f"numpy/BLAS threads {threads}, cpu {platform.processor() or platform.machine()}")}
+    measured = sum(v for kk, v in T.items() if kk != "attention_extrapolated")
+    return {"value": (1 + n_cached) * w.n_tokens / stack, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"oracle stages on head {head} of {w.heads} over all {w.n_tokens} tokens (matching, top-r, "
+                       f"deviations, restore, means, unmerge), the global outlier choice over {w.heads}x{w.n_tokens} "
+                       f"deviations, attention for {min(rows, lq)} of {lq} merged query rows; "
+                       f"measured {measured:.1f} s of CPU stages; extrapolated x{h} heads and to all merged rows: "
+                       f"layer 0 {layer0:.0f} s" + (f", cached layer {cached:.0f} s" if n_cached else "")
+                       + f"; numpy/BLAS threads {threads}, cpu {platform.processor() or platform.machine()}"),
+            "stage_seconds": {kk: round(v, 3) for kk, v in T.items()},
+            "layer0_s_extrapolated": layer0, "cached_layer_s_extrapolated": cached if n_cached else None}
 
 
+# --------------------------------------------------------------------------- block sweep
 # (n_s, n_t) shapes of the block sweep: block sizes near 256, 800 and 3840
 # tokens, each as spatial-only (n_t = 1) and temporal stacks.
 SWEEP_SHAPES = [(256, 1), (86, 3), (26, 10), (800, 1), (267, 3), (80, 10), (27, 30),
@@ -112,7 +267,7 @@ def sweep_blocks(args, H, torch) -> None:
     sit from their merged token) and the relative RMS error of the layer
     output against exact unmerged attention on the same inputs.
     """
-    base = gen.WORKLOADS[args.workload]
+    base = gen.WORKLOADS[args.workload].with_(layers=1)
     x = gen.layer_inputs(base, seed=args.seed)
     tdt = torch.bfloat16 if base.dtype == "bf16" else torch.float32
     q, k, v = (torch.from_numpy(x[t]).to(tdt).cuda() for t in "qkv")
@@ -146,25 +301,75 @@ def sweep_blocks(args, H, torch) -> None:
             del ws, out
 
 
+# --------------------------------------------------------------------------- timing helpers
+def timed(torch, stream, fn, reps):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def lengths(H, plan, ws, w, ga):
+    lq = np.diff(H.debug_read(plan, ws, "cu_q")).astype(np.float64)
+    lk = plan.info["kv_len"]
+    lkh = H.debug_read(plan, ws, "kv_len").astype(np.float64) if ga else np.full(w.heads, float(lk))
+    return lq, lkh
+
+
+def single_layer_summary(H, torch, w, seed, reps_floor=10):
+    """tokens/s, attention fraction and stage times of one full layer (extra keys)."""
+    x = gen.layer_inputs(w, seed=seed)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x[t]).to(tdt).cuda() for t in "qkv")
+    del x
+    plan = H.Plan.from_workload(w)
+    ws = H.workspace(plan)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    run = lambda: H.layer(plan, q, k, v, ws=ws, out=out, stream=stream)
+    probe = max(timed(torch, stream, run, 2), 1e-3)
+    reps = max(reps_floor, int(500.0 / probe))
+    timed(torch, stream, run, reps)  # warmup
+    H.set_timing(["attn"])
+    ms = timed(torch, stream, run, reps)
+    at, calls = H.get_timing()
+    H.set_timing(None)
+    timed(torch, stream, run, 30)
+    stages, _ = H.get_timing()
+    H.set_timing([])
+    lq, lkh = lengths(H, plan, ws, w, False)
+    alg = algorithmic(w, plan, lq, lkh)
+    attn = roofline_entry("attn_fast", alg["attn"], at["attn"], w.dtype, calls)
+    return {"workload": describe(w), "tokens": w.n_tokens, "ms_per_layer": ms,
+            "tokens_per_s": w.n_tokens / (ms * 1e-3), "steps": reps, "attn_roofline": attn,
+            "rooflines": stage_rooflines(stages, alg, w.dtype), "stages_ms": stages}
+
+
+# --------------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=0,
-                    help="timed steps (default: enough for ~0.5 s of GPU work, at least 10)")
+                    help="timed steps (default: enough for ~0.5 s of GPU work, at least 3)")
     ap.add_argument("--warmup", type=int, default=0,
                     help="untimed warmup steps (default: enough for ~0.5 s, at least 3, so clocks have ramped)")
-    ap.add_argument("--workload", default="vggt30", choices=sorted(gen.WORKLOADS))
+    ap.add_argument("--workload", default="vggt500", choices=sorted(gen.WORKLOADS))
     ap.add_argument("--seed", type=int, default=gen.DEFAULT_SEED)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=8)
-    ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--cpu-rows", type=int, default=512, help="cpu baseline: merged query rows of attention timed")
+    ap.add_argument("--dense-reps", type=int, default=2)
+    ap.add_argument("--no-extra", action="store_true", help="skip the 30-frame layer reported as extra keys")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (HBM counter calibration)")
     ap.add_argument("--kv-ratio", type=float, default=None, help="override the workload's K/V merge ratio")
     ap.add_argument("--q-ratio", type=float, default=None, help="override the workload's query merge ratio")
     ap.add_argument("--outlier-pct", type=float, default=None, help="override the workload's outlier budget")
     ap.add_argument("--cached-layers", type=int, default=None,
-                    help="also time layers that reuse the merge indices (default: workload layers - 1)")
+                    help="layers per step that reuse layer 0's merge indices (default: workload layers - 1)")
     ap.add_argument("--partition", default="httm", choices=["httm", "ga"],
                     help="httm: temporal blocks (default); ga: geometry-aware three-class partition")
     ap.add_argument("--protect-pct", type=float, default=10.0, help="ga: percent of each frame's patches protected")
@@ -192,135 +397,128 @@ def main():
     if ga:
         w = w.with_(name=w.name + "_ga", partition=1, protect_pct=args.protect_pct)
     n_cached = (w.layers - 1) if args.cached_layers is None else args.cached_layers
-    log(f"[bench] generating {describe(w)}")
-    x = gen.layer_inputs(w, seed=args.seed)
+    w = w.with_(layers=1 + n_cached)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    dev = [torch.from_numpy(x[t]).to(tdt).cuda() for t in "qkv"]
-    q, k, v = dev
+    log(f"[bench] generating {describe(w)}")
+    t0 = time.perf_counter()
+    dev, host0, host1 = [], {}, {}
+    for l, xl in gen.layer_stack(w, seed=args.seed, layers=1 + n_cached):
+        dev.append([torch.from_numpy(xl[t]).to(tdt).cuda() for t in "qkv"])
+        if l <= 1 and not args.no_cpu_baseline:  # the CPU baseline's sample: head 0 of layers 0 and 1
+            (host0 if l == 0 else host1).update({t: xl[t][:1].copy() for t in "qkv"})
+        del xl
+    log(f"[bench] inputs of {1 + n_cached} layer(s) resident in HBM ({time.perf_counter() - t0:.1f} s)")
     plan = H.Plan.from_workload(w)
     ws = H.workspace(plan)
-    out = torch.empty_like(q)
+    idx = H.CachedIndex(plan) if n_cached > 0 else None
+    out = torch.empty_like(dev[0][0])
     stream = torch.cuda.current_stream()
 
+    def step():
+        q, k, v = dev[0]
+        H.layer(plan, q, k, v, ws=ws, out=out, index=idx, stream=stream)
+        for l in range(1, 1 + n_cached):
+            q, k, v = dev[l]
+            H.layer_cached(plan, idx, q, k, v, ws=ws, out=out, stream=stream)
+
     # step-time probe (untimed for the result): sizes the default warmup and step counts
-    H.layer(plan, q, k, v, ws=ws, out=out, stream=stream)
-    torch.cuda.synchronize()
-    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    p0.record(stream)
-    H.layer(plan, q, k, v, ws=ws, out=out, stream=stream)
-    p1.record(stream)
-    torch.cuda.synchronize()
-    probe_ms = max(p0.elapsed_time(p1), 1e-3)
+    step()
+    probe_ms = max(timed(torch, stream, step, 1), 1e-3)
     if args.warmup <= 0:
         args.warmup = max(3, int(500.0 / probe_ms))
     if args.steps <= 0:
-        args.steps = max(10, int(500.0 / probe_ms))
+        args.steps = max(3, int(500.0 / probe_ms))
     log(f"[bench] warmup {args.warmup} steps (probe {probe_ms:.3f} ms/step)")
     for _ in range(args.warmup):
-        H.layer(plan, q, k, v, ws=ws, out=out, stream=stream)
+        step()
     torch.cuda.synchronize()
 
-    # timed region: K layer calls; HIP events around the attention kernel only
-    # (and, with the geometry-aware partition, around its global match kernel)
+    # timed region: K steps; HIP events around every attention launch (and,
+    # with the geometry-aware partition, around its global match kernel)
     H.set_timing(["attn", "ga_match"] if ga else ["attn"])
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        H.layer(plan, q, k, v, ws=ws, out=out, stream=stream)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_total = ev0.elapsed_time(ev1)
+    ms_step = timed(torch, stream, step, args.steps)
     attn_t, calls = H.get_timing()
-    ms_step = ms_total / args.steps
-    value = w.n_tokens / (ms_step * 1e-3)
-    log(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step, {value:.4g} tokens/s, attn {attn_t['attn']:.4f} ms")
+    layers = 1 + n_cached
+    value = layers * w.n_tokens / (ms_step * 1e-3)
+    log(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step ({layers} layer(s)), {value:.4g} tokens/s, "
+        f"attn {attn_t['attn']:.4f} ms per launch")
 
-    cu = H.debug_read(plan, ws, "cu_q")
-    lq = np.diff(cu)
-    lk = plan.info["kv_len"]
-    lkh = H.debug_read(plan, ws, "kv_len").astype(np.float64) if ga else np.full(w.heads, float(lk))
-    attn_flop = 4.0 * w.d_head * float((lkh * lq).sum())
+    # the layers of a stack on their own (untimed for the headline)
+    per_layer = None
+    if n_cached > 0:
+        q, k, v = dev[0]
+        l0 = timed(torch, stream, lambda: H.layer(plan, q, k, v, ws=ws, out=out, index=idx, stream=stream),
+                   max(3, args.steps // 2))
+        q, k, v = dev[1]
+        lc = timed(torch, stream, lambda: H.layer_cached(plan, idx, q, k, v, ws=ws, out=out, stream=stream),
+                   max(3, args.steps // 2))
+        per_layer = {"layer0_ms": l0, "layer0_tokens_per_s": w.n_tokens / (l0 * 1e-3),
+                     "cached_ms_per_layer": lc, "cached_tokens_per_s": w.n_tokens / (lc * 1e-3),
+                     "cached_layers": n_cached, "aggregate_tokens_per_s": value}
+        log(f"[bench] layer 0 {l0:.3f} ms, cached layer {lc:.3f} ms")
+        # leave layer 0's intermediates in the workspace for the reads below
+        H.layer(plan, *dev[0], ws=ws, out=out, index=idx, stream=stream)
+
+    lq, lkh = lengths(H, plan, ws, w, ga)
+    alg = algorithmic(w, plan, lq, lkh)
     ga_info = None
     if ga:
-        # global match: 2*d*|S|*|D| per head and stream
         role = H.debug_read(plan, ws, "ga_role").reshape(2, w.heads, -1)
         ns = (role == 0).sum(axis=2).astype(np.float64)
         nd = (role == 1).sum(axis=2).astype(np.float64)
         ga_info = {"match_flop": float((2.0 * w.d_head * ns * nd).sum()),
                    "sources_per_head_mean": float(ns.mean()), "destinations_per_head_mean": float(nd.mean()),
                    "kv_len_min": int(lkh.min()), "kv_len_max": int(lkh.max())}
-    attn_ms = attn_t["attn"]
-    peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
-    achieved = attn_flop / (attn_ms * 1e-3) / 1e12
-    attn_roof = {"bound": "mfma", "kernel": "attn_fast" if w.dtype == "bf16" else "attn_f32",
-                 "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                 "traffic": measured_traffic(w.name, "bf16" if w.dtype == "bf16" else "f32"),
-                 "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
-                 "algorithmic": (f"4*d*sum_h(L_k,h*L_q,h) = {attn_flop:.4g} FLOP per launch" if ga else
-                                 f"4*d*L_k*sum_h(L_q,h) = 4*{w.d_head}*{lk}*{int(lq.sum())} = {attn_flop:.4g} FLOP per launch"),
-                 "avg_launch_ms": attn_ms, "launches_timed": calls}
+    attn_kernel = "attn_fast" if w.dtype == "bf16" else "attn_f32"
+    attn_roof = roofline_entry(attn_kernel, alg["attn"], attn_t["attn"], w.dtype, calls)
+    attn_roof["traffic"] = measured_traffic(w.name, attn_kernel, ATTN_SRC)
+    attn_roof["traffic_unit"] = TRAFFIC_UNIT
+    attn_roof["algorithmic"] = (f"4*d*sum_h(L_k,h*L_q,h) = {alg['attn'][1]:.4g} FLOP per launch (L_k = "
+                                f"{int(lkh.max())}, sum_h L_q,h = {int(lq.sum())}); the same per launch in "
+                                f"layer 0 and the cached layers")
     roofline, other_roofline = attn_roof, None
     if ga and attn_t["ga_match"] > 0:
         match_ms = attn_t["ga_match"]
-        m_ach = ga_info["match_flop"] / (match_ms * 1e-3) / 1e12
-        match_roof = {"bound": "mfma", "kernel": "ga_match_bf16" if w.dtype == "bf16" else "ga_match_f32",
-                      "achieved": m_ach, "peak": peak, "unit": "TFLOP/s", "frac": m_ach / peak,
-                      "traffic": measured_traffic(w.name, "bf16" if w.dtype == "bf16" else "f32",
-                                                  GA_TRAFFIC_PROFILE, GA_SRC),
-                      "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
-                      "algorithmic": f"2*d*sum_(stream,h)(|S|*|D|) = {ga_info['match_flop']:.4g} FLOP per launch",
-                      "avg_launch_ms": match_ms, "launches_timed": calls}
-        log(f"[bench] global match {match_ms:.4f} ms ({m_ach:.1f} TFLOP/s), attention {attn_ms:.4f} ms")
+        match_roof = roofline_entry("ga_match_bf16" if w.dtype == "bf16" else "ga_match_f32",
+                                    ("flop", ga_info["match_flop"]), match_ms, w.dtype, calls)
+        match_roof["traffic"] = measured_traffic(w.name, match_roof["kernel"], GA_SRC)
+        match_roof["traffic_unit"] = TRAFFIC_UNIT
+        match_roof["algorithmic"] = f"2*d*sum_(stream,h)(|S|*|D|) = {ga_info['match_flop']:.4g} FLOP per launch"
+        log(f"[bench] global match {match_ms:.4f} ms, attention {attn_t['attn']:.4f} ms")
         # the dominant kernel (the longer launch) carries the roofline; the other rides along
-        if match_ms > attn_ms:
+        if match_ms > attn_t["attn"]:
             roofline, other_roofline = match_roof, attn_roof
         else:
             other_roofline = match_roof
 
-    # per-stage breakdown (separate untimed pass; events around every stage, 30 calls)
+    # per-stage breakdown (separate untimed pass; events around every stage)
     H.set_timing(None)
-    for _ in range(30):
-        H.layer(plan, q, k, v, ws=ws, out=out, stream=stream)
+    for _ in range(8):
+        H.layer(plan, *dev[0], ws=ws, out=out, index=idx, stream=stream)
     stages, _ = H.get_timing()
+    cstages = None
+    if n_cached > 0:
+        H.set_timing(None)
+        for _ in range(8):
+            H.layer_cached(plan, idx, *dev[1], ws=ws, out=out, stream=stream)
+        cstages, _ = H.get_timing()
     H.set_timing([])
     torch.cuda.synchronize()
-
-    # layers that reuse this layer's merge indices (LiteVGGT-style cache)
-    cached = None
-    if n_cached > 0:
-        idx = H.CachedIndex(plan)
-        H.layer(plan, q, k, v, ws=ws, out=out, index=idx, stream=stream)
-        H.layer_cached(plan, idx, q, k, v, ws=ws, out=out, stream=stream)
-        torch.cuda.synchronize()
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record(stream)
-        for _ in range(args.steps):
-            H.layer_cached(plan, idx, q, k, v, ws=ws, out=out, stream=stream)
-        c1.record(stream)
-        torch.cuda.synchronize()
-        cms = c0.elapsed_time(c1) / args.steps
-        stack_ms = ms_step + n_cached * cms
-        cached = {"cached_layers": n_cached, "cached_ms_per_layer": cms,
-                  "stack_ms": stack_ms, "stack_tokens_per_s": (1 + n_cached) * w.n_tokens / (stack_ms * 1e-3),
-                  "cached_tokens_per_s": w.n_tokens / (cms * 1e-3)}
-        log(f"[bench] cached layer {cms:.4f} ms; stack of {1 + n_cached}: {stack_ms:.3f} ms")
-        del idx
+    rooflines = stage_rooflines(stages, alg, w.dtype, cstages)
+    for key, r in rooflines.items():
+        if r:
+            log(f"[bench]   {key:22s} {r['avg_launch_ms']:9.4f} ms  {r['achieved']:9.1f} {r['unit']}  "
+                f"frac {r['frac']:.3f}")
 
     # speedup over the same engine's unmerged attention
     dense_ms = None
     if args.dense_reps > 0:
         dws = H.workspace(plan, "dense")
-        dout = torch.empty_like(q)
-        H.attention_dense(plan, q, k, v, ws=dws, out=dout)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.dense_reps):
-            H.attention_dense(plan, q, k, v, ws=dws, out=dout, stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        dense_ms = e0.elapsed_time(e1) / args.dense_reps
+        dout = torch.empty_like(out)
+        q, k, v = dev[0]
+        H.attention_dense(plan, q, k, v, ws=dws, out=dout, stream=stream)
+        dense_ms = timed(torch, stream, lambda: H.attention_dense(plan, q, k, v, ws=dws, out=dout, stream=stream),
+                         args.dense_reps)
         del dws, dout
 
     if args.copy_calibration_mib > 0:
@@ -331,10 +529,21 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: {args.copy_calibration_mib} MiB device copy")
 
+    layer_ms = per_layer["layer0_ms"] if per_layer else ms_step
+    del dev, ws, idx, out
+    torch.cuda.empty_cache()
+
+    extra = None
+    if not args.no_extra and args.workload != "vggt30" and not ga:
+        log("[bench] extra: the 30-frame layer")
+        extra = single_layer_summary(H, torch, gen.WORKLOADS["vggt30"], args.seed)
+        log(f"[bench]   vggt30 {extra['ms_per_layer']:.4f} ms/layer, {extra['tokens_per_s']:.4g} tokens/s")
+
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"[bench] cpu baseline: oracle on {args.cpu_heads} heads")
-        cpu = cpu_baseline(w, x, args.cpu_heads)
+        log("[bench] cpu baseline: oracle stages on one head")
+        cpu = cpu_baseline(w, host0, host1, n_cached, rows=args.cpu_rows)
+        log(f"[bench]   {cpu['sample']}")
 
     res = {
         "metric": METRIC,
@@ -348,22 +557,26 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": "synthetic: seeded VGGT-shaped tokens (smoothed spatial field + per-frame drift + noise), inputs resident in HBM",
+        "data": "synthetic: seeded VGGT-shaped tokens (smoothed spatial field + per-frame drift + noise; each "
+                "later layer of a stack adds N(0, 0.02^2)), inputs resident in HBM",
         "config": {"workload": describe(w), "frames": w.frames, "tokens": w.n_tokens, "heads": w.heads,
                    "d_head": w.d_head, "n_s": w.n_s, "n_t": w.n_t, "q_ratio": w.q_ratio, "kv_ratio": w.kv_ratio,
-                   "outlier_pct": w.outlier_pct, "seed": args.seed,
+                   "outlier_pct": w.outlier_pct, "layers_per_step": layers, "seed": args.seed,
                    **({"partition": "geometry-aware", "protect_pct": w.protect_pct} if ga else {})},
         "roofline": roofline,
         **({"roofline_other_kernel": other_roofline} if other_roofline else {}),
+        "rooflines": rooflines,
         "cpu_baseline": cpu,
+        "stack": per_layer,
         "stages_ms": stages,
-        "cached": cached,
+        "cached_stages_ms": cstages,
         "geometry_aware": ga_info,
-        "speedup_vs_unmerged_attention": (dense_ms / ms_step) if dense_ms else None,
+        "speedup_vs_unmerged_attention": (dense_ms / layer_ms) if dense_ms else None,
         "unmerged_attention_ms": dense_ms,
-        "lengths": {"kv_len": lk, "q_len_mean": float(lq.mean()), "q_len_min": int(lq.min()),
+        "lengths": {"kv_len": int(lkh.max()), "q_len_mean": float(lq.mean()), "q_len_min": int(lq.min()),
                     "q_len_max": int(lq.max()), "q_ratio_final": float(lq.mean() / w.n_tokens),
-                    "kv_ratio_final": lk / w.n_tokens},
+                    "kv_ratio_final": float(lkh.mean() / w.n_tokens)},
+        "vggt30": extra,
     }
     print(json.dumps(res), flush=True)
 

@@ -106,6 +106,9 @@ typedef struct {
                             frame and N < 2^20 */
   double protect_pct;    /* partition 1: percent of each frame's patches protected, [0, 100]
                             (the page uses 10); protected = floor(protect_pct / 100 * H*W) */
+  int32_t attn_split;    /* bf16 attention: key ranges per query tile whose partial results are
+                            combined in a fixed order; 0 = the library's choice (4), else 1, 2, 4
+                            or 8 (fp32 layers always use 1).  Outputs agree to rounding */
 } httm_params;
 
 typedef struct httm_plan httm_plan;
@@ -230,12 +233,20 @@ httm_status httm_attention_dense(const httm_plan* plan, void* ws, size_t ws_byte
  *   HTTM_DBG_GA_MATCH: matched destination token of every source, -1 for
  *       every other token;
  *   HTTM_DBG_GA_SCORE: float cosine of that match (0 for non-sources);
- *   HTTM_DBG_KV_LEN: [h] keys per head (the key stream's group count). */
+ *   HTTM_DBG_KV_LEN: [h] keys per head (the key stream's group count).
+ * Merged rows, in the layer's element type (bf16 bit patterns or fp32), as
+ * the attention kernel reads them (also after httm_layer_cached):
+ *   HTTM_DBG_KT: [h][L_k padded to 64][64] merged keys, each the mean of its
+ *       group multiplied by softmax_scale * log2(e) (rows past L_k are 0);
+ *   HTTM_DBG_VT: [h][64][L_k padded to 64] merged values, transposed;
+ *   HTTM_DBG_QT: [q_capacity][64] packed merged queries, head h's rows at
+ *       [cu_q[h], cu_q[h+1]) (rows past cu_q[h] are unspecified). */
 typedef enum {
   HTTM_DBG_Q_MATCH = 0, HTTM_DBG_Q_SCORE, HTTM_DBG_KV_MATCH, HTTM_DBG_KV_SCORE,
   HTTM_DBG_Q_GROUP, HTTM_DBG_KV_GROUP, HTTM_DBG_DELTA, HTTM_DBG_OUTLIER,
   HTTM_DBG_Q_SLOT, HTTM_DBG_CU_Q, HTTM_DBG_SELECT, HTTM_DBG_ATTN_FALLBACK,
   HTTM_DBG_GA_VAR, HTTM_DBG_GA_ROLE, HTTM_DBG_GA_MATCH, HTTM_DBG_GA_SCORE, HTTM_DBG_KV_LEN,
+  HTTM_DBG_KT, HTTM_DBG_VT, HTTM_DBG_QT,
   HTTM_DBG_COUNT
 } httm_debug_item;
 httm_status httm_debug_size(const httm_plan* plan, int32_t item, size_t* bytes);
@@ -251,12 +262,15 @@ httm_status httm_debug_read(const httm_plan* plan, const void* ws, const httm_in
  * stage (0 if none) and the number of recorded calls; it synchronises on
  * the events.  Host-side state, not thread-safe. */
 /* In httm_layer the key branch (K similarity, K selection, K/V merge) runs on
- * the library stream concurrently with the query branch: HTTM_T_MERGE_KV
- * times that whole branch there, HTTM_T_SIM and HTTM_T_SELECT the query
- * stream's similarity and selection.  With partition = 1, HTTM_T_SIM times
- * the whole geometry-aware partition of both streams (on the caller's
- * stream) and HTTM_T_GA_MATCH its global cosine match alone (one launch);
- * HTTM_T_SELECT is not recorded. */
+ * the library stream concurrently with the query branch: HTTM_T_SIM_K,
+ * HTTM_T_SELECT_K and HTTM_T_MERGE_KV time its three launches there,
+ * HTTM_T_SIM and HTTM_T_SELECT the query stream's similarity and selection.
+ * With partition = 1, HTTM_T_SIM times the whole geometry-aware partition of
+ * both streams (on the caller's stream) and HTTM_T_GA_MATCH its global cosine
+ * match alone (one launch); the two selection stages and HTTM_T_SIM_K are not
+ * recorded.  httm_layer_cached records HTTM_T_MERGE_KV (its K/V merge, on the
+ * library stream) and HTTM_T_MERGE_Q (its query means); httm_attention_dense
+ * records HTTM_T_MERGE_KV for its input preparation. */
 typedef enum {
   HTTM_T_SIM = 0, HTTM_T_SELECT, HTTM_T_MERGE_KV, HTTM_T_MERGE_Q, HTTM_T_OUTLIER,
   HTTM_T_RESTORE,
@@ -264,6 +278,8 @@ typedef enum {
   HTTM_T_UNMERGE,
   HTTM_T_ATTN_TAIL,  /* exact recompute of queued units + combine of key splits */
   HTTM_T_GA_MATCH,   /* partition = 1: the global match kernel (one launch) */
+  HTTM_T_SIM_K,      /* key stream similarity (library stream) */
+  HTTM_T_SELECT_K,   /* key stream selection (library stream) */
   HTTM_T_COUNT
 } httm_timing_stage;
 httm_status httm_set_timing(int32_t stage_mask);

@@ -46,3 +46,29 @@ def run_layer(w, inputs, keep_index=False, **plan_kw):
 def sample_rows(n, count, seed):
     rows = np.random.default_rng(seed).choice(n, count, replace=False)
     return np.unique(np.r_[rows, [0, 1, n - 1]])
+
+
+def tile_rows(q_slot_h: np.ndarray, cu_q: np.ndarray, h: int, tile: int = 256) -> np.ndarray:
+    """One token per `tile`-row query tile of head h: the token whose packed
+    row is the first one at or after the tile's start (every packed row has
+    at least one token)."""
+    order = np.argsort(q_slot_h, kind="stable")
+    srt = q_slot_h[order]
+    starts = np.arange(cu_q[h], cu_q[h + 1], tile)
+    pos = np.searchsorted(srt, starts)
+    assert (pos < len(srt)).all() and (srt[pos] < cu_q[h + 1]).all()
+    return np.unique(order[pos])
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def segment_means(x: np.ndarray, label: np.ndarray, n_seg: int) -> np.ndarray:
+    """fp64 mean of the rows of x sharing each label in [0, n_seg) (label -1: skipped)."""
+    keep = label >= 0
+    s = np.zeros((n_seg, x.shape[1]), np.float64)
+    np.add.at(s, label[keep], x[keep].astype(np.float64))
+    c = np.bincount(label[keep], minlength=n_seg).astype(np.float64)
+    assert (c > 0).all()
+    return s / c[:, None]

@@ -135,6 +135,10 @@ def test_validation_codes():
     assert _status(heads=64) == 0
     assert _status(heads=65) == 2  # per-head prefix tables are sized for 64
     assert _status(softmax_scale=float("inf")) == 1
+    for split in (0, 1, 2, 4, 8):
+        assert _status(attn_split=split) == 0
+    for split in (-1, 3, 16):
+        assert _status(attn_split=split) == 1
 
 
 def test_layer_rejects_bad_buffers_before_any_launch():

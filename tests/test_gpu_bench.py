@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 def _bench(*args):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny", "--steps", "3",
-                        "--warmup", "1", "--dense-reps", "0", "--cached-layers", "0", "--cpu-heads", "1", *args],
+                        "--warmup", "1", "--dense-reps", "0", "--cached-layers", "0", "--no-extra", *args],
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.splitlines() if l.strip()]
@@ -34,7 +34,8 @@ def test_bench_json_contract(partition):
     assert d["value"] > 0 and d["ms_per_step"] > 0 and d["higher_is_better"] is True
     assert d["vs_baseline"] is None
     assert isinstance(d["config"]["workload"], str) and d["config"]["tokens"] > 0
-    # whole-job throughput: tokens of one layer per step time
+    # whole-job throughput: tokens of the step's layers per step time
+    assert d["config"]["layers_per_step"] == 1
     assert d["value"] == pytest.approx(d["config"]["tokens"] / (d["ms_per_step"] * 1e-3), rel=1e-9)
     rf = d["roofline"]
     assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s"
@@ -47,3 +48,22 @@ def test_bench_json_contract(partition):
         assert any(k.startswith("ga_match") for k in kernels) and any(k.startswith("attn") for k in kernels)
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    for key, r in d["rooflines"].items():
+        assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], rel=1e-9), key
+        assert r["bound"] in ("hbm", "mfma"), key
+
+
+def test_bench_cached_stack_contract():
+    """A stack step (layer 0 + cached layers on their own inputs): the value is
+    the aggregate throughput of all layers of the step."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny", "--steps", "3",
+                        "--warmup", "1", "--dense-reps", "1", "--cached-layers", "2", "--no-extra"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    assert d["config"]["layers_per_step"] == 3
+    assert d["value"] == pytest.approx(3 * d["config"]["tokens"] / (d["ms_per_step"] * 1e-3), rel=1e-9)
+    st = d["stack"]
+    assert st["cached_layers"] == 2 and st["layer0_ms"] > 0 and st["cached_ms_per_layer"] > 0
+    assert "merge_q_cached" in d["rooflines"]
+    assert d["speedup_vs_unmerged_attention"] > 0

@@ -16,7 +16,7 @@ import token_merged_global_amd as H
 
 pytestmark = pytest.mark.gpu
 
-from gpu_util import BF16_REL, F32_ABS, read_all, say as _say, to_dev
+from gpu_util import BF16_REL, F32_ABS, bf16_to_f32, read_all, say as _say, segment_means, to_dev
 
 
 def run_layer(w, inputs, **plan_kw):
@@ -232,19 +232,120 @@ def test_attention_fallback_exact_path():
         assert np.abs(dense[h] - ref).max() <= BF16_REL * np.sqrt((ref ** 2).mean())
 
 
-def test_key_split_matches_single_pass():
-    """The 30-frame layer runs its attention in key splits; cached layers on the
-    same indices and inputs must agree with the full layer to the bf16 tolerance."""
-    w = gen.WORKLOADS["vggt30"].with_(heads=4)
+@pytest.mark.parametrize("split", [1, 2, 4, 8])
+def test_attention_key_splits_against_oracle(split):
+    """Attention with its keys split in 1, 2, 4 or 8 ranges (partials combined
+    in a fixed order) against the oracle on every output row of a layer with
+    several query tiles per head and partly filled last rounds on the XCDs."""
+    w = small_bf16(frames=8, heads=16)
+    x = gen.layer_inputs(w)
+    p = O.Params.from_workload(w)
+    plan, ws, dev, out, gpu = run_layer(w, x, attn_split=split)
+    _say(f"[split {split}] q rows per head {np.diff(gpu['cu_q']).tolist()[:4]}...")
+    rep = staged.check_layer(x["q"], x["k"], x["v"], p, gpu, out, rel_tol=BF16_REL)
+    _say("  ", rep.as_dict())
+
+
+def _merged_rows_check(plan, ws, w, x, gpu, what):
+    """Every merged key, value and query row against the fp64 mean of its
+    members (the group the implementation formed), within one rounding of
+    the stored type (bf16: 2^-8 relative, fp32: 1e-6 relative)."""
+    h, N = w.heads, w.n_tokens
+    lkp = -(-plan.info["kv_len"] // 64) * 64
+    lk = plan.info["kv_len"]
+    conv = bf16_to_f32 if w.dtype == "bf16" else (lambda a: a)
+    kt = conv(H.debug_read(plan, ws, "kt")).reshape(h, lkp, 64)
+    vt = conv(H.debug_read(plan, ws, "vt")).reshape(h, 64, lkp)
+    qt = conv(H.debug_read(plan, ws, "qt")).reshape(-1, 64)
+    rel = 2.0 ** -8 if w.dtype == "bf16" else 1e-6
+    kscale = plan.info["softmax_scale"] * 1.4426950408889634
+    cu = gpu["cu_q"]
+    worst = 0.0
+    for i in range(h):
+        km = segment_means(x["k"][i], gpu["kv_group"][i], lk) * kscale
+        vm = segment_means(x["v"][i], gpu["kv_group"][i], lk)
+        qm = segment_means(x["q"][i], gpu["q_slot"][i] - cu[i], cu[i + 1] - cu[i])
+        for got, ref in ((kt[i, :lk], km), (vt[i, :, :lk].T, vm), (qt[cu[i]:cu[i + 1]], qm)):
+            err = np.abs(got - ref) - rel * np.abs(ref) - 2e-6  # + fp32 summation error of the mean
+            worst = max(worst, float((np.abs(got - ref) / (np.abs(ref) + 1e-3)).max()))
+            assert (err <= 0).all(), f"{what} head {i}: merged row off by {np.abs(got - ref).max():.3g}"
+        assert (kt[i, lk:] == 0).all() and (vt[i, :, lk:] == 0).all()
+    _say(f"[merged rows {what}] worst relative error {worst:.3g}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "vggt30"])
+def test_merged_rows_are_group_means(name):
+    """K~ (times scale * log2 e), V~ (transposed) and the packed Q~ rows read
+    back and compared with the fp64 means of their groups (HTTM page, key
+    design 1: a merged token is the mean of its members, V follows K's
+    groups; key design 3: outliers leave their group and become rows of
+    their own); then again after a cached layer on new inputs (LiteVGGT
+    page, key design 3: reused indices, recomputed means)."""
+    w = {"tiny": gen.WORKLOADS["tiny"], "small": small_bf16(), "vggt30": gen.WORKLOADS["vggt30"]}[name]
     x = gen.layer_inputs(w)
     plan = H.Plan.from_workload(w)
     q, k, v = (to_dev(x[t], w.dtype) for t in "qkv")
     ws = H.workspace(plan)
-    out, idx = H.layer(plan, q, k, v, ws=ws, keep_index=True)
-    out2 = H.layer_cached(plan, idx, q, k, v, ws=ws)
+    _, idx = H.layer(plan, q, k, v, ws=ws, keep_index=True)
     torch.cuda.synchronize()
-    a, b = out.float().cpu().numpy(), out2.float().cpu().numpy()
-    assert np.abs(a - b).max() <= BF16_REL * np.sqrt((a ** 2).mean())
+    gpu = read_all(plan, ws, w.heads, index=idx)
+    _merged_rows_check(plan, ws, w, x, gpu, f"{name} layer")
+    x1 = gen.layer_inputs(w, layer=1)
+    for t, d in zip("qkv", (q, k, v)):
+        d.copy_(to_dev(x1[t], w.dtype))
+    H.layer_cached(plan, idx, q, k, v, ws=ws)
+    torch.cuda.synchronize()
+    _merged_rows_check(plan, ws, w, x1, gpu, f"{name} cached layer")
+
+
+def test_vggt30_every_query_slot():
+    """30 frames, 16 heads: after the staged index checks, the output of one
+    token of every merged query row of every head (about 8,400 per head)
+    against the oracle's attention on the implementation's partitions."""
+    w = gen.WORKLOADS["vggt30"]
+    x = gen.layer_inputs(w)
+    p = O.Params.from_workload(w)
+    plan, ws, dev, out, gpu = run_layer(w, x)
+    rows = np.unique(np.r_[np.random.default_rng(3).choice(w.n_tokens, 64, replace=False), 0, w.n_tokens - 1])
+    rep = staged.check_layer(x["q"], x["k"], x["v"], p, gpu, out, rows=rows, rel_tol=BF16_REL,
+                             workers=gen.default_workers())
+    _say("  ", rep.as_dict())
+    worst = 0.0
+    for h in range(w.heads):
+        qf = staged.canonical(gpu["q_slot"][h])
+        kr = staged.canonical(gpu["kv_group"][h])
+        reps = np.unique(qf)  # one token per final query slot
+        ref = O.head_output(x["q"][h], x["k"][h], x["v"][h], qf, kr, p.scale, rows=reps)
+        rms = float(np.sqrt((ref ** 2).mean()))
+        err = float(np.abs(out[h][reps] - ref).max())
+        worst = max(worst, err / rms)
+        assert err <= BF16_REL * rms, f"head {h}: {err:.3g} > {BF16_REL} x {rms:.3g}"
+        assert len(reps) == gpu["cu_q"][h + 1] - gpu["cu_q"][h]
+    _say(f"[vggt30 every slot] worst error / RMS {worst:.4f}")
+
+
+def test_call_on_another_stream_without_workspace():
+    """A layer enqueued on a stream that is not the current one, with no
+    workspace passed: the temporary workspace and the output come from that
+    stream's allocations, so tensors allocated right afterwards on the
+    current stream cannot take them over while the layer runs."""
+    w = small_bf16(frames=6, heads=4)
+    x = gen.layer_inputs(w)
+    plan = H.Plan.from_workload(w)
+    q, k, v = (to_dev(x[t], w.dtype) for t in "qkv")
+    ref = H.layer(plan, q, k, v, ws=H.workspace(plan))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        o = H.layer(plan, q, k, v, stream=s)
+        junk = torch.full((plan.workspace_bytes // 4 + 1024,), 7.0, device="cuda")  # current stream
+        outs.append(o)
+        del junk
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
 
 
 def test_index_export_import_round_trip():

@@ -14,16 +14,25 @@ import gen
 import oracle as O
 from oracle import staged
 import token_merged_global_amd as H
-from gpu_util import BF16_REL, read_all, run_layer, sample_rows, say, to_dev
+from gpu_util import BF16_REL, read_all, run_layer, sample_rows, say, tile_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 WORKERS = gen.default_workers()
 
 
+def _rows(w, gpu, rows_seed):
+    """256 sampled tokens plus one token of every 256-row query tile of the
+    oracle heads (every attention work unit of those heads is checked)."""
+    oh = gen.oracle_heads(w)
+    tiles = [tile_rows(gpu["q_slot"][h], gpu["cu_q"], h) for h in oh]
+    return np.unique(np.concatenate([sample_rows(w.n_tokens, 256, rows_seed)] + tiles))
+
+
 def _check(w, x, gpu, out, p=None, rows_seed=0):
     p = p or O.Params.from_workload(w)
     oh = gen.oracle_heads(w)
-    rows = sample_rows(w.n_tokens, 256, rows_seed)
+    rows = _rows(w, gpu, rows_seed)
+    say(f"   output rows checked per oracle head: {len(rows)}")
     rep = staged.check_layer(x["q"], x["k"], x["v"], p, gpu, out, out_heads=oh, rows=rows,
                              rel_tol=BF16_REL, workers=WORKERS)
     say("  ", rep.as_dict())
@@ -44,7 +53,8 @@ def test_vggt100_layer():
 
 @pytest.mark.timeout(900)
 def test_vggt200_sweep_and_ratio_zero():
-    """K/V merge {0.5, 0.75} x outlier {5, 10, 20} %, plus merge ratio 0."""
+    """K/V merge {0.5, 0.75} x outlier {5, 10, 20} %, every point staged against
+    the oracle, plus merge ratio 0."""
     w = gen.WORKLOADS["vggt200"]
     say(f"[vggt200] N={w.n_tokens}")
     x = gen.layer_inputs(w)
@@ -56,8 +66,7 @@ def test_vggt200_sweep_and_ratio_zero():
             say(f"  kv={kv} p={pct}: q_len/head={np.diff(gpu['cu_q']).mean():.0f} kv_len={plan.info['kv_len']}")
             assert int(gpu["outlier"].sum()) == plan.info["n_outliers"]
             masks[(kv, pct)] = gpu["outlier"].astype(bool)
-            if (kv, pct) in ((0.5, 10.0), (0.75, 20.0)):
-                _check(wk, x, gpu, out, rows_seed=int(pct))
+            _check(wk, x, gpu, out, rows_seed=int(pct))
             del ws, dev
             torch.cuda.empty_cache()
     # nesting: a larger budget keeps every earlier outlier (same query groups)
@@ -94,10 +103,12 @@ def test_vggt500_cached_stack():
     _check(w, x0, gpu, out0)
     qf = {h: staged.canonical(gpu["q_slot"][h]) for h in oh}
     kr = {h: staged.canonical(gpu["kv_group"][h]) for h in oh}
+    stack_rows = _rows(w, gpu, 11)
     q, k, v = dev
     del out0, gpu
     p = O.Params.from_workload(w)
-    rows = sample_rows(w.n_tokens, 256, 11)
+    rows = stack_rows
+    say(f"   cached layers: output rows checked per oracle head: {len(rows)}")
     for l, xl in gen.layer_stack(w, heads=oh):
         if l == 0:
             continue

@@ -26,12 +26,12 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
           4: "index mismatch", 5: "device error"}
 DEBUG_ITEMS = ["q_match", "q_score", "kv_match", "kv_score", "q_group", "kv_group", "delta",
                "outlier", "q_slot", "cu_q", "select", "attn_fallback",
-               "ga_var", "ga_role", "ga_match", "ga_score", "kv_len"]
+               "ga_var", "ga_role", "ga_match", "ga_score", "kv_len", "kt", "vt", "qt"]
 #: Items that exist only under one partition (block-local / geometry-aware).
 BLOCK_ITEMS = ["q_match", "q_score", "kv_match", "kv_score"]
 GA_ITEMS = ["ga_var", "ga_role", "ga_match", "ga_score", "kv_len"]
 TIMING_STAGES = ["sim", "select", "merge_kv", "merge_q", "outlier", "restore", "attn", "unmerge", "attn_tail",
-                 "ga_match"]
+                 "ga_match", "sim_k", "select_k"]
 
 
 class HttmError(RuntimeError):
@@ -47,7 +47,8 @@ class Params(ctypes.Structure):
                 ("kv_ratio", ctypes.c_double), ("outlier_pct", ctypes.c_double),
                 ("q_dst_stride", ctypes.c_int32), ("kv_dst_stride", ctypes.c_int32),
                 ("block_order", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
-                ("dtype", ctypes.c_int32), ("partition", ctypes.c_int32), ("protect_pct", ctypes.c_double)]
+                ("dtype", ctypes.c_int32), ("partition", ctypes.c_int32), ("protect_pct", ctypes.c_double),
+                ("attn_split", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -139,10 +140,11 @@ class Plan:
     def __init__(self, heads: int, frames: int, grid_h: int, grid_w: int, n_special: int, n_s: int,
                  n_t: int, q_ratio: float, kv_ratio: float, outlier_pct: float, dtype="bf16",
                  d_head: int = 64, q_dst_stride: int = 0, kv_dst_stride: int = 0, block_order: int = 0,
-                 softmax_scale: float = 0.0, partition: int = 0, protect_pct: float = 10.0):
+                 softmax_scale: float = 0.0, partition: int = 0, protect_pct: float = 10.0, attn_split: int = 0):
         self.params = Params(heads, d_head, frames, grid_h, grid_w, n_special, n_s, n_t, float(q_ratio),
                              float(kv_ratio), float(outlier_pct), q_dst_stride, kv_dst_stride, block_order,
-                             float(softmax_scale), _dtype_code(dtype), int(partition), float(protect_pct))
+                             float(softmax_scale), _dtype_code(dtype), int(partition), float(protect_pct),
+                             int(attn_split))
         h = ctypes.c_void_p()
         _check(lib().httm_plan_create(ctypes.byref(self.params), ctypes.byref(h)))
         self.handle = h
@@ -299,10 +301,14 @@ def attention_dense(plan: Plan, q, k, v, ws=None, out=None, stream=None):
     return out
 
 
-def debug_items(plan: Plan) -> List[str]:
-    """The debug items that exist for ``plan``'s partition."""
+#: Merged rows (K~, V~^T, Q~): as large as the inputs, read only on request.
+ROW_ITEMS = ["kt", "vt", "qt"]
+
+
+def debug_items(plan: Plan, rows: bool = False) -> List[str]:
+    """The debug items that exist for ``plan``'s partition (merged rows only if ``rows``)."""
     skip = BLOCK_ITEMS if plan.params.partition == 1 else GA_ITEMS
-    return [it for it in DEBUG_ITEMS if it not in skip]
+    return [it for it in DEBUG_ITEMS if it not in skip and (rows or it not in ROW_ITEMS)]
 
 
 def debug_read(plan: Plan, ws, item: str, stream=None, index: Optional[CachedIndex] = None):
@@ -314,9 +320,10 @@ def debug_read(plan: Plan, ws, item: str, stream=None, index: Optional[CachedInd
     code = DEBUG_ITEMS.index(item)
     n = ctypes.c_size_t()
     _check(lib().httm_debug_size(plan.handle, code, ctypes.byref(n)))
+    rows = np.uint16 if plan.dtype == "bf16" else np.float32  # merged rows: bf16 bit patterns or fp32
     dt = {"q_score": np.float32, "kv_score": np.float32, "delta": np.float32, "outlier": np.uint8,
           "select": np.uint32, "ga_var": np.float32, "ga_role": np.uint8,
-          "ga_score": np.float32}.get(item, np.int32)
+          "ga_score": np.float32, "kt": rows, "vt": rows, "qt": rows}.get(item, np.int32)
     arr = np.empty(n.value // np.dtype(dt).itemsize, dtype=dt)
     _check(lib().httm_debug_read(plan.handle, ws.data_ptr(), ctypes.byref(index.c) if index is not None else None,
                                  code, arr.ctypes.data, arr.nbytes, _stream_ptr(stream)))

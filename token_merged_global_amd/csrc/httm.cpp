@@ -161,6 +161,8 @@ httm_status build(const httm_params& p, httm_plan* pl) {
   if (p.partition == 1 && !(p.protect_pct >= 0.0 && p.protect_pct <= 100.0))
     return fail(HTTM_ERR_INVALID_ARG, "protect_pct must lie in [0, 100]");
   if ((int64_t)p.n_s * p.n_t > kMaxBlock) return fail(HTTM_ERR_UNSUPPORTED, "n_s * n_t must be <= 4096");
+  if (p.attn_split != 0 && p.attn_split != 1 && p.attn_split != 2 && p.attn_split != 4 && p.attn_split != 8)
+    return fail(HTTM_ERR_INVALID_ARG, "attn_split must be 0, 1, 2, 4 or 8");
   const int64_t T = (int64_t)p.n_special + (int64_t)p.grid_h * p.grid_w;
   const int64_t N = (int64_t)p.frames * T;
   if ((int64_t)p.heads * N >= (1ll << 31) || (int64_t)p.heads * N * kD >= (1ll << 40))
@@ -265,7 +267,7 @@ httm_status build(const httm_params& p, httm_plan* pl) {
   pl->lk_pad = ceil_div(g.nslots[kK], 64) * 64;
   pl->scale = p.softmax_scale > 0.0f ? p.softmax_scale : 1.0f / std::sqrt((float)kD);
   pl->esize = p.dtype == HTTM_BF16 ? 2 : 4;
-  pl->attn_split = p.dtype == HTTM_BF16 ? attention_split(pl->q_cap, p.heads) : 1;
+  pl->attn_split = p.dtype != HTTM_BF16 ? 1 : (p.attn_split > 0 ? p.attn_split : attention_split(pl->q_cap, p.heads));
   pl->attn_tail = attention_tail(pl->attn_split);
   {
     // exact-path queue capacity: workgroups of the layer's or the unmerged
@@ -741,11 +743,15 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
     // key branch on the library stream: matching, selection and merge of K / V
     CHECK_LAUNCH(hipEventRecord(side->fork, st));
     CHECK_LAUNCH(hipStreamWaitEvent(side->st, side->fork, 0));
-    stage_begin(HTTM_T_MERGE_KV, side->st);
+    stage_begin(HTTM_T_SIM_K, side->st);
     CHECK_LAUNCH(launch_sim(g, dt, q, k, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
                             at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), 2, side->st));
+    stage_end(HTTM_T_SIM_K, side->st);
+    stage_begin(HTTM_T_SELECT_K, side->st);
     CHECK_LAUNCH(launch_select(g, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
                                at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), cq, ck, 2, side->st));
+    stage_end(HTTM_T_SELECT_K, side->st);
+    stage_begin(HTTM_T_MERGE_KV, side->st);
     CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
                                  ck.members, ck.off,
                                  at<void>(ws, L.kt), at<void>(ws, L.vt), at<float>(ws, L.kmax), side->st));
@@ -889,6 +895,7 @@ httm_status httm_debug_size(const httm_plan* pl, int32_t item, size_t* bytes) {
   if (!pl || !bytes) return fail(HTTM_ERR_INVALID_ARG, "NULL argument");
   const size_t h = pl->g.heads, n = pl->g.N;
   const bool ga = pl->p.partition == 1;
+  const size_t E = pl->esize;
   const bool ga_item = item == HTTM_DBG_GA_VAR || item == HTTM_DBG_GA_ROLE || item == HTTM_DBG_GA_MATCH ||
                        item == HTTM_DBG_GA_SCORE || item == HTTM_DBG_KV_LEN;
   const bool block_item = item == HTTM_DBG_Q_MATCH || item == HTTM_DBG_Q_SCORE || item == HTTM_DBG_KV_MATCH ||
@@ -914,6 +921,9 @@ httm_status httm_debug_size(const httm_plan* pl, int32_t item, size_t* bytes) {
     case HTTM_DBG_CU_Q: *bytes = 4 * (h + 1); break;
     case HTTM_DBG_SELECT: *bytes = 16; break;
     case HTTM_DBG_ATTN_FALLBACK: *bytes = 4; break;
+    case HTTM_DBG_KT:
+    case HTTM_DBG_VT: *bytes = E * h * (size_t)pl->lk_pad * kD; break;
+    case HTTM_DBG_QT: *bytes = E * (size_t)pl->q_cap * kD; break;
     default: return fail(HTTM_ERR_INVALID_ARG, "unknown debug item");
   }
   return HTTM_OK;
@@ -950,6 +960,9 @@ httm_status httm_debug_read(const httm_plan* pl, const void* ws, const httm_inde
     case HTTM_DBG_GA_MATCH: src = base + L.ga_gdst.off; break;
     case HTTM_DBG_GA_SCORE: src = base + L.ga_gscore.off; break;
     case HTTM_DBG_KV_LEN: src = idx + pl->I.lenk.off; break;
+    case HTTM_DBG_KT: src = base + L.kt.off; break;
+    case HTTM_DBG_VT: src = base + L.vt.off; break;
+    case HTTM_DBG_QT: src = base + L.qt.off; break;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   CHECK_LAUNCH(hipMemcpyAsync(host, src, need, hipMemcpyDeviceToHost, st));

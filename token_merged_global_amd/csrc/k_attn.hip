@@ -780,7 +780,7 @@ AttnTail attention_tail(int split) {
   // host-only: capacities use the bound of kMaxTailTiles tail tiles per XCD;
   // the device's tiles per round is read at launch (attention_per_round)
   AttnTail t{split, 0, 0};
-  if (split <= 1) return t;
+  if (split <= 1 || 2 * split > kMaxSplit) return t;
   t.tail_split = 2 * split;
   t.tail_rows = (int64_t)8 * kMaxTailTiles * kRows;
   return t;
