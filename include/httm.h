@@ -170,6 +170,21 @@ httm_status httm_layer(const httm_plan* plan, void* ws, size_t ws_bytes,
                        const void* q, const void* k, const void* v, void* out,
                        httm_index* index, void* stream);
 
+/* httm_layer for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same layer, with no workspace argument and no merge index.  Its workspace
+ * is a static device array of httm_noalloc_capacity() bytes (64 MiB) that
+ * the library holds on every GPU it runs on until the process ends; a plan
+ * whose httm_workspace_size() exceeds it gets HTTM_ERR_WORKSPACE before any
+ * launch.  Every launch goes to `stream` (no library stream is created) and
+ * nothing is allocated or freed.  All calls on one GPU share that GPU's
+ * array, which keeps the last call's contents (the layer clears what it
+ * needs zeroed): calls that may overlap on one GPU (other streams, other
+ * threads' streams) race and must be ordered by the caller. */
+httm_status httm_noalloc_capacity(size_t* bytes);
+httm_status httm_layer_noalloc(const httm_plan* plan, const void* q, const void* k, const void* v, void* out,
+                               void* stream);
+
 /* A layer that reuses the reordering, final query partition and key
  * partition held in `index` (LiteVGGT page, key design 3): means of this
  * layer's q, k, v over the cached groups, attention, unmerge. */

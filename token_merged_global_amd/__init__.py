@@ -97,6 +97,9 @@ EXPORTS = {
     "httm_set_timing": ([ctypes.c_int32], ctypes.c_int),
     "httm_get_timing": ([ctypes.POINTER(ctypes.c_float), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)],
                         ctypes.c_int),
+    "httm_noalloc_capacity": ([ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "httm_layer_noalloc": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                            ctypes.c_void_p], ctypes.c_int),
     "httm_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "httm_last_error": ([], ctypes.c_char_p),
 }
@@ -267,6 +270,23 @@ def layer_cached(plan: Plan, index: CachedIndex, q, k, v, ws=None, out=None, str
     _check(lib().httm_layer_cached(plan.handle, ws.data_ptr(), ws.numel(), ctypes.byref(index.c),
                                    q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                    _stream_ptr(stream)))
+    return out
+
+
+def noalloc_capacity() -> int:
+    """Bytes of the library's static device scratch used by ``layer_noalloc``."""
+    n = ctypes.c_size_t()
+    _check(lib().httm_noalloc_capacity(ctypes.byref(n)))
+    return n.value
+
+
+def layer_noalloc(plan: Plan, q, k, v, out, stream=None):
+    """One layer that allocates nothing: the library's static scratch is its
+    workspace (plans up to ``noalloc_capacity()`` bytes of workspace); every
+    launch goes to ``stream``.  ``out`` is the caller's output tensor."""
+    _check_qkv(plan, q, k, v, out)
+    _check(lib().httm_layer_noalloc(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    _stream_ptr(stream)))
     return out
 
 

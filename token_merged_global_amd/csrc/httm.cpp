@@ -554,6 +554,182 @@ bool index_payload_ok(const httm_plan* pl, const char* buf) {
 }
 }  // namespace
 
+namespace {
+
+// Device scratch of httm_layer_noalloc: its workspace (and merge index) on
+// every GPU the library runs on, held until the process ends.  In host code
+// `scratch` only names the symbol; its device address on the current device
+// comes from hipGetSymbolAddress, looked up once per device.
+constexpr size_t kNoAllocBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+void* g_scratch[kMaxDevices];
+
+// Address of the current device's scratch (call with g_launch_mu held).
+httm_status scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(HTTM_ERR_DEVICE, "no usable current device");
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(HTTM_ERR_DEVICE, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return HTTM_OK;
+}
+
+}  // namespace
+
+namespace {
+
+// One full layer enqueued on `st`.  With a library side stream the key branch
+// forks onto it (joined back before the attention); with side == nullptr
+// every launch goes to `st` in order.  Call with g_launch_mu held and the
+// arguments validated.
+httm_status enqueue_layer(const httm_plan* pl, void* ws, httm_index* index, const void* q, const void* k,
+                          const void* v, void* out, hipStream_t st, SideStream* side) {
+  const Geo& g = pl->g;
+  const Layout& L = pl->L;
+  const IndexLayout& I = pl->I;
+  const int dt = pl->p.dtype;
+  char* idx = index ? reinterpret_cast<char*>(index->dev) : at<char>(ws, L.index);
+  hipStream_t kst = side ? side->st : st;  // stream of the key branch
+  httm_status s = HTTM_OK;
+  timing_begin_call();
+
+  Csr cq{at<int32_t>(ws, L.q_members), at<int32_t>(ws, L.q_off), at<int32_t>(ws, L.q_group)};
+  Csr ck{reinterpret_cast<int32_t*>(idx + I.k_members.off), reinterpret_cast<int32_t*>(idx + I.k_off.off),
+         at<int32_t>(ws, L.k_group)};
+  const int64_t hn = (int64_t)g.heads * g.N;
+  // atomic targets of this layer: key norms, exact-path count, outlier scratch, outlier counts
+  CHECK_LAUNCH(launch_zero_init(at<float>(ws, L.kmax), g.heads, at<int>(ws, L.fb), at<uint32_t>(ws, L.radix),
+                                (int)outlier_scratch_words(hn), at<int32_t>(ws, L.ocnt),
+                                (int64_t)g.heads * g.nslots[kQ], st, &pl->index_header,
+                                reinterpret_cast<uint32_t*>(idx + I.header.off)));
+
+  if (pl->p.partition == 1) {
+    // geometry-aware partition of both streams in one pass on the caller's
+    // stream, then the K / V means on the library stream
+    int32_t* lenk = reinterpret_cast<int32_t*>(idx + I.lenk.off);
+    GaShape gs{g.heads, g.N,         g.T,          g.nsp,          pl->p.grid_h,
+               pl->p.grid_w, g.F, pl->ga_kp, pl->ga_bound, pl->ga_max_src, pl->ga_dpitch};
+    GaBuffers gb;
+    gb.var = at<float>(ws, L.ga_var);
+    gb.role = at<uint8_t>(ws, L.ga_role);
+    gb.fcnt = at<int32_t>(ws, L.ga_fcnt);
+    gb.foff = at<int32_t>(ws, L.ga_foff);
+    gb.tot = at<int32_t>(ws, L.ga_tot);
+    gb.slot = at<int32_t>(ws, L.ga_slot);
+    gb.dst_list = at<int32_t>(ws, L.ga_dlist);
+    gb.dst_slot = at<int32_t>(ws, L.ga_dslot);
+    gb.src_list = at<int32_t>(ws, L.ga_slist);
+    gb.gdst = at<int32_t>(ws, L.ga_gdst);
+    gb.gslot = at<int32_t>(ws, L.ga_gslot);
+    gb.gscore = at<float>(ws, L.ga_gscore);
+    gb.dg = at<uint16_t>(ws, L.ga_dg);
+    gb.dinv = at<float>(ws, L.ga_dinv);
+    gb.best = at<uint64_t>(ws, L.ga_best);
+    gb.snorm = at<float>(ws, L.ga_snorm);
+    gb.cnt = at<int32_t>(ws, L.ga_cnt);
+    gb.fill = at<int32_t>(ws, L.ga_fill);
+    gb.tmp = at<int32_t>(ws, L.ga_tmp);
+    gb.grp_q = cq.group;
+    gb.grp_k = ck.group;
+    gb.mem_q = cq.members;
+    gb.mem_k = ck.members;
+    gb.off_q = cq.off;
+    gb.off_k = ck.off;
+    gb.lenk = lenk;
+    stage_begin(HTTM_T_SIM, st);
+    CHECK_LAUNCH(launch_ga_partition(dt, gs, q, k, gb, st, 0));
+    CHECK_LAUNCH(launch_ga_partition(dt, gs, q, k, gb, st, 1));
+    stage_begin(HTTM_T_GA_MATCH, st);
+    CHECK_LAUNCH(launch_ga_partition(dt, gs, q, k, gb, st, 2));
+    stage_end(HTTM_T_GA_MATCH, st);
+    CHECK_LAUNCH(launch_ga_partition(dt, gs, q, k, gb, st, 3));
+    stage_end(HTTM_T_SIM, st);
+    if (side) {
+      CHECK_LAUNCH(hipEventRecord(side->fork, st));
+      CHECK_LAUNCH(hipStreamWaitEvent(kst, side->fork, 0));
+    }
+    stage_begin(HTTM_T_MERGE_KV, kst);
+    CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
+                                 ck.members, ck.off, at<void>(ws, L.kt), at<void>(ws, L.vt), at<float>(ws, L.kmax),
+                                 kst, lenk));
+    stage_end(HTTM_T_MERGE_KV, kst);
+    if (side) CHECK_LAUNCH(hipEventRecord(side->join, kst));
+  } else {
+    // key branch on the library stream (if any): matching, selection and merge of K / V
+    if (side) {
+      CHECK_LAUNCH(hipEventRecord(side->fork, st));
+      CHECK_LAUNCH(hipStreamWaitEvent(kst, side->fork, 0));
+    }
+    stage_begin(HTTM_T_SIM_K, kst);
+    CHECK_LAUNCH(launch_sim(g, dt, q, k, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
+                            at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), 2, kst));
+    stage_end(HTTM_T_SIM_K, kst);
+    stage_begin(HTTM_T_SELECT_K, kst);
+    CHECK_LAUNCH(launch_select(g, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
+                               at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), cq, ck, 2, kst));
+    stage_end(HTTM_T_SELECT_K, kst);
+    stage_begin(HTTM_T_MERGE_KV, kst);
+    CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
+                                 ck.members, ck.off,
+                                 at<void>(ws, L.kt), at<void>(ws, L.vt), at<float>(ws, L.kmax), kst));
+    stage_end(HTTM_T_MERGE_KV, kst);
+    if (side) CHECK_LAUNCH(hipEventRecord(side->join, kst));
+
+    // query branch on the caller's stream
+    stage_begin(HTTM_T_SIM, st);
+    CHECK_LAUNCH(launch_sim(g, dt, q, k, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
+                            at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), 1, st));
+    stage_end(HTTM_T_SIM, st);
+    stage_begin(HTTM_T_SELECT, st);
+    CHECK_LAUNCH(launch_select(g, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
+                               at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), cq, ck, 1, st));
+    stage_end(HTTM_T_SELECT, st);
+  }
+
+  stage_begin(HTTM_T_MERGE_Q, st);
+  CHECK_LAUNCH(launch_merge_q(dt, g.heads, g.N, g.nslots[kQ], q, cq.members, cq.off,
+                              at<float>(ws, L.qsum), at<float>(ws, L.delta), at<uint32_t>(ws, L.radix), st));
+  stage_end(HTTM_T_MERGE_Q, st);
+
+  stage_begin(HTTM_T_OUTLIER, st);
+  CHECK_LAUNCH(launch_outliers(at<float>(ws, L.delta), hn, pl->k_o, at<uint8_t>(ws, L.mask),
+                               at<uint32_t>(ws, L.radix), cq.group, g.N, g.nslots[kQ], at<int32_t>(ws, L.ocnt),
+                               st));
+  stage_end(HTTM_T_OUTLIER, st);
+
+  RestoreOut ro;
+  ro.qt = at<void>(ws, L.qt);
+  ro.lenq = reinterpret_cast<int32_t*>(idx + I.lenq.off);
+  ro.cu_q = reinterpret_cast<int32_t*>(idx + I.cu_q.off);
+  ro.base = at<int32_t>(ws, L.base);
+  ro.ocnt = at<int32_t>(ws, L.ocnt);
+  ro.fmembers = reinterpret_cast<int32_t*>(idx + I.fmembers.off);
+  ro.foff = reinterpret_cast<int32_t*>(idx + I.foff.off);
+  ro.slot = reinterpret_cast<int32_t*>(idx + I.slot.off);
+  stage_begin(HTTM_T_RESTORE, st);
+  CHECK_LAUNCH(launch_restore(dt, g.heads, g.N, g.nslots[kQ], q, cq.members, cq.off,
+                              at<float>(ws, L.qsum), at<uint8_t>(ws, L.mask), ro, st));
+  stage_end(HTTM_T_RESTORE, st);
+
+  if (side) CHECK_LAUNCH(hipStreamWaitEvent(st, side->join, 0));
+  s = attend_unmerge(pl, ws, idx, at<void>(ws, L.qt), out, st);
+  if (s != HTTM_OK) return s;
+  if (index) {
+    index->plan_id = pl->id;
+    index->valid = 1;
+  }
+  timing_end_call();
+  return HTTM_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* httm_status_string(httm_status s) {
@@ -668,141 +844,34 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
   if (index && (!index->dev || index->bytes < pl->I.total))
     return fail(HTTM_ERR_WORKSPACE, "index buffer smaller than httm_index_size()");
   if (index && ((uintptr_t)index->dev & 15)) return fail(HTTM_ERR_INVALID_ARG, "index must be 16-byte aligned");
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const Geo& g = pl->g;
-  const Layout& L = pl->L;
-  const IndexLayout& I = pl->I;
-  const int dt = pl->p.dtype;
-  char* idx = index ? reinterpret_cast<char*>(index->dev) : at<char>(ws, L.index);
   std::lock_guard<std::mutex> lock(g_launch_mu);
   SideStream* side = nullptr;
   s = side_stream(&side);
   if (s != HTTM_OK) return s;
-  timing_begin_call();
+  return enqueue_layer(pl, ws, index, q, k, v, out, reinterpret_cast<hipStream_t>(stream), side);
+}
 
-  Csr cq{at<int32_t>(ws, L.q_members), at<int32_t>(ws, L.q_off), at<int32_t>(ws, L.q_group)};
-  Csr ck{reinterpret_cast<int32_t*>(idx + I.k_members.off), reinterpret_cast<int32_t*>(idx + I.k_off.off),
-         at<int32_t>(ws, L.k_group)};
-  const int64_t hn = (int64_t)g.heads * g.N;
-  // atomic targets of this layer: key norms, exact-path count, outlier scratch, outlier counts
-  CHECK_LAUNCH(launch_zero_init(at<float>(ws, L.kmax), g.heads, at<int>(ws, L.fb), at<uint32_t>(ws, L.radix),
-                                (int)outlier_scratch_words(hn), at<int32_t>(ws, L.ocnt),
-                                (int64_t)g.heads * g.nslots[kQ], st, &pl->index_header,
-                                reinterpret_cast<uint32_t*>(idx + I.header.off)));
-
-  if (pl->p.partition == 1) {
-    // geometry-aware partition of both streams in one pass on the caller's
-    // stream, then the K / V means on the library stream
-    int32_t* lenk = reinterpret_cast<int32_t*>(idx + I.lenk.off);
-    GaShape gs{g.heads, g.N,         g.T,          g.nsp,          pl->p.grid_h,
-               pl->p.grid_w, g.F, pl->ga_kp, pl->ga_bound, pl->ga_max_src, pl->ga_dpitch};
-    GaBuffers gb;
-    gb.var = at<float>(ws, L.ga_var);
-    gb.role = at<uint8_t>(ws, L.ga_role);
-    gb.fcnt = at<int32_t>(ws, L.ga_fcnt);
-    gb.foff = at<int32_t>(ws, L.ga_foff);
-    gb.tot = at<int32_t>(ws, L.ga_tot);
-    gb.slot = at<int32_t>(ws, L.ga_slot);
-    gb.dst_list = at<int32_t>(ws, L.ga_dlist);
-    gb.dst_slot = at<int32_t>(ws, L.ga_dslot);
-    gb.src_list = at<int32_t>(ws, L.ga_slist);
-    gb.gdst = at<int32_t>(ws, L.ga_gdst);
-    gb.gslot = at<int32_t>(ws, L.ga_gslot);
-    gb.gscore = at<float>(ws, L.ga_gscore);
-    gb.dg = at<uint16_t>(ws, L.ga_dg);
-    gb.dinv = at<float>(ws, L.ga_dinv);
-    gb.best = at<uint64_t>(ws, L.ga_best);
-    gb.snorm = at<float>(ws, L.ga_snorm);
-    gb.cnt = at<int32_t>(ws, L.ga_cnt);
-    gb.fill = at<int32_t>(ws, L.ga_fill);
-    gb.tmp = at<int32_t>(ws, L.ga_tmp);
-    gb.grp_q = cq.group;
-    gb.grp_k = ck.group;
-    gb.mem_q = cq.members;
-    gb.mem_k = ck.members;
-    gb.off_q = cq.off;
-    gb.off_k = ck.off;
-    gb.lenk = lenk;
-    stage_begin(HTTM_T_SIM, st);
-    CHECK_LAUNCH(launch_ga_partition(dt, gs, q, k, gb, st, 0));
-    CHECK_LAUNCH(launch_ga_partition(dt, gs, q, k, gb, st, 1));
-    stage_begin(HTTM_T_GA_MATCH, st);
-    CHECK_LAUNCH(launch_ga_partition(dt, gs, q, k, gb, st, 2));
-    stage_end(HTTM_T_GA_MATCH, st);
-    CHECK_LAUNCH(launch_ga_partition(dt, gs, q, k, gb, st, 3));
-    stage_end(HTTM_T_SIM, st);
-    CHECK_LAUNCH(hipEventRecord(side->fork, st));
-    CHECK_LAUNCH(hipStreamWaitEvent(side->st, side->fork, 0));
-    stage_begin(HTTM_T_MERGE_KV, side->st);
-    CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
-                                 ck.members, ck.off, at<void>(ws, L.kt), at<void>(ws, L.vt), at<float>(ws, L.kmax),
-                                 side->st, lenk));
-    stage_end(HTTM_T_MERGE_KV, side->st);
-    CHECK_LAUNCH(hipEventRecord(side->join, side->st));
-  } else {
-    // key branch on the library stream: matching, selection and merge of K / V
-    CHECK_LAUNCH(hipEventRecord(side->fork, st));
-    CHECK_LAUNCH(hipStreamWaitEvent(side->st, side->fork, 0));
-    stage_begin(HTTM_T_SIM_K, side->st);
-    CHECK_LAUNCH(launch_sim(g, dt, q, k, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
-                            at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), 2, side->st));
-    stage_end(HTTM_T_SIM_K, side->st);
-    stage_begin(HTTM_T_SELECT_K, side->st);
-    CHECK_LAUNCH(launch_select(g, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
-                               at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), cq, ck, 2, side->st));
-    stage_end(HTTM_T_SELECT_K, side->st);
-    stage_begin(HTTM_T_MERGE_KV, side->st);
-    CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
-                                 ck.members, ck.off,
-                                 at<void>(ws, L.kt), at<void>(ws, L.vt), at<float>(ws, L.kmax), side->st));
-    stage_end(HTTM_T_MERGE_KV, side->st);
-    CHECK_LAUNCH(hipEventRecord(side->join, side->st));
-
-    // query branch on the caller's stream
-    stage_begin(HTTM_T_SIM, st);
-    CHECK_LAUNCH(launch_sim(g, dt, q, k, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
-                            at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), 1, st));
-    stage_end(HTTM_T_SIM, st);
-    stage_begin(HTTM_T_SELECT, st);
-    CHECK_LAUNCH(launch_select(g, at<int32_t>(ws, L.match[kQ]), at<float>(ws, L.score[kQ]),
-                               at<int32_t>(ws, L.match[kK]), at<float>(ws, L.score[kK]), cq, ck, 1, st));
-    stage_end(HTTM_T_SELECT, st);
-  }
-
-  stage_begin(HTTM_T_MERGE_Q, st);
-  CHECK_LAUNCH(launch_merge_q(dt, g.heads, g.N, g.nslots[kQ], q, cq.members, cq.off,
-                              at<float>(ws, L.qsum), at<float>(ws, L.delta), at<uint32_t>(ws, L.radix), st));
-  stage_end(HTTM_T_MERGE_Q, st);
-
-  stage_begin(HTTM_T_OUTLIER, st);
-  CHECK_LAUNCH(launch_outliers(at<float>(ws, L.delta), hn, pl->k_o, at<uint8_t>(ws, L.mask),
-                               at<uint32_t>(ws, L.radix), cq.group, g.N, g.nslots[kQ], at<int32_t>(ws, L.ocnt),
-                               st));
-  stage_end(HTTM_T_OUTLIER, st);
-
-  RestoreOut ro;
-  ro.qt = at<void>(ws, L.qt);
-  ro.lenq = reinterpret_cast<int32_t*>(idx + I.lenq.off);
-  ro.cu_q = reinterpret_cast<int32_t*>(idx + I.cu_q.off);
-  ro.base = at<int32_t>(ws, L.base);
-  ro.ocnt = at<int32_t>(ws, L.ocnt);
-  ro.fmembers = reinterpret_cast<int32_t*>(idx + I.fmembers.off);
-  ro.foff = reinterpret_cast<int32_t*>(idx + I.foff.off);
-  ro.slot = reinterpret_cast<int32_t*>(idx + I.slot.off);
-  stage_begin(HTTM_T_RESTORE, st);
-  CHECK_LAUNCH(launch_restore(dt, g.heads, g.N, g.nslots[kQ], q, cq.members, cq.off,
-                              at<float>(ws, L.qsum), at<uint8_t>(ws, L.mask), ro, st));
-  stage_end(HTTM_T_RESTORE, st);
-
-  CHECK_LAUNCH(hipStreamWaitEvent(st, side->join, 0));
-  s = attend_unmerge(pl, ws, idx, at<void>(ws, L.qt), out, st);
-  if (s != HTTM_OK) return s;
-  if (index) {
-    index->plan_id = pl->id;
-    index->valid = 1;
-  }
-  timing_end_call();
+httm_status httm_noalloc_capacity(size_t* bytes) {
+  if (!bytes) return fail(HTTM_ERR_INVALID_ARG, "NULL argument");
+  *bytes = kNoAllocBytes;
   return HTTM_OK;
+}
+
+httm_status httm_layer_noalloc(const httm_plan* pl, const void* q, const void* k, const void* v, void* out,
+                               void* stream) {
+  if (!pl) return fail(HTTM_ERR_INVALID_ARG, "plan is NULL");
+  if (pl->L.total > kNoAllocBytes)
+    return fail(HTTM_ERR_WORKSPACE, "the layer needs " + std::to_string(pl->L.total) +
+                                        " bytes of workspace; httm_layer_noalloc holds " +
+                                        std::to_string(kNoAllocBytes) + " (use httm_layer with a workspace)");
+  if (!q || !k || !v || !out) return fail(HTTM_ERR_INVALID_ARG, "q, k, v and out must not be NULL");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15)
+    return fail(HTTM_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+  std::lock_guard<std::mutex> lock(g_launch_mu);
+  void* ws = nullptr;
+  const httm_status s = scratch_ptr(&ws);
+  if (s != HTTM_OK) return s;
+  return enqueue_layer(pl, ws, nullptr, q, k, v, out, reinterpret_cast<hipStream_t>(stream), nullptr);
 }
 
 httm_status httm_layer_cached(const httm_plan* pl, void* ws, size_t ws_bytes, const httm_index* index,
