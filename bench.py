@@ -180,73 +180,90 @@ def stage_rooflines(stages, alg, dtype, cached_stages=None):
 
 
 # --------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(w, x0, xc, n_cached: int, rows: int = 512, head: int = 0):
+def cpu_baseline(w, x0, xc, n_cached: int, rows: int = 2048, heads: int = 2):
     """The oracle, as it stands, timed stage by stage on a bounded sample.
 
-    Sample: one head of the workload.  Matching, top-r, query means and
-    deviations, restore, the final means and unmerge run on the whole
-    sequence of that head; the global outlier choice runs over h x N
-    deviations (that head's, repeated for every head); attention runs for
-    `rows` merged query rows of that head against all of its merged keys.
-    One layer's CPU time is extrapolated as h x (per-head stages) + select +
+    Sample: the first `heads` heads of the workload.  Matching, top-r, query
+    means and deviations, restore, the final means and unmerge run on the
+    whole sequence of each sampled head; the global outlier choice runs over
+    h x N deviations (the sampled heads' deviations, repeated up to h heads);
+    attention runs for `rows` merged query rows of each sampled head against
+    all of its merged keys.  One layer's CPU time is extrapolated as
+    h x (per-head stages, averaged over the sampled heads) + select +
     h x (attention per row x merged query rows); a cached layer as
-    h x (final means + unmerge + attention).  The stack is layer 0 plus the
-    cached layers; the value is tokens of the stack per second.
+    h x (final means + unmerge + attention) on the next layer's inputs.  The
+    stack is layer 0 plus the cached layers; the value is tokens of the stack
+    per second.
     """
     import oracle as O
     from threadpoolctl import threadpool_info
 
+    hs = min(heads, x0["q"].shape[0])
     p1 = O.Params.from_workload(w.with_(heads=1))
     pf = O.Params.from_workload(w)
-    q, k, v = (x0[t][head:head + 1] for t in "qkv")
-    T = {}
-    t0 = time.perf_counter()
-    tr = O.match_heads(q, k, p1, [0])
-    T["match"] = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    delta = O.deviations(q, [tr.q_match[0].rep])
-    T["deviation"] = time.perf_counter() - t0
-    tiled = np.tile(delta, (w.heads, 1))
+    h = w.heads
+    T = {"match": 0.0, "deviation": 0.0, "restore": 0.0, "means": 0.0, "attention_sample": 0.0, "unmerge": 0.0}
+    per_head_layer0, cached_per_head, deltas, parts = 0.0, 0.0, [], []
+    for i in range(hs):
+        q, k = x0["q"][i:i + 1], x0["k"][i:i + 1]
+        t0 = time.perf_counter()
+        tr = O.match_heads(q, k, p1, [0])
+        T["match"] += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        deltas.append(O.deviations(q, [tr.q_match[0].rep])[0])
+        T["deviation"] += time.perf_counter() - t0
+        parts.append(tr)
+    tiled = np.stack([deltas[i % hs] for i in range(h)])
     t0 = time.perf_counter()
     mask = O.select_outliers(tiled, O.outlier_budget(pf))
     T["select"] = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    fin = O.restore_partition(tr.q_match[0].rep, mask[0])
-    T["restore"] = time.perf_counter() - t0
 
-    def means_attn_unmerge(qq, kk, vv):
+    def means_attn_unmerge(fin, krep, qq, kk, vv):
         t0 = time.perf_counter()
-        qp, kp = O.partition(fin), O.partition(tr.k_rep[0])
+        qp, kp = O.partition(fin), O.partition(krep)
         qt, kt, vt = O.group_means(qq, qp), O.group_means(kk, kp), O.group_means(vv, kp)
         tm = time.perf_counter() - t0
         sel = np.sort(np.random.default_rng(0).choice(len(qt), min(rows, len(qt)), replace=False))
         t0 = time.perf_counter()
         o = O.attention(qt[sel], kt, vt, pf.scale)
-        ta = (time.perf_counter() - t0) * len(qt) / len(sel)
+        ts = time.perf_counter() - t0
         full = np.zeros((len(qt), o.shape[1]))
         t0 = time.perf_counter()
         O.unmerge(full, qp)
         tu = time.perf_counter() - t0
-        return tm, ta, tu, len(qt)
+        return tm, ts, ts * len(qt) / len(sel), tu, len(qt), len(sel)
 
-    T["means"], T["attention_extrapolated"], T["unmerge"], lq = means_attn_unmerge(q[0], k[0], v[0])
-    h = w.heads
-    layer0 = h * (T["match"] + T["deviation"] + T["restore"] + T["means"] + T["unmerge"] +
-                  T["attention_extrapolated"]) + T["select"]
-    cached = 0.0
-    if n_cached > 0:
-        xq, xk, xv = (xc[t][head] for t in "qkv")
-        tm, ta, tu, _ = means_attn_unmerge(xq, xk, xv)
-        cached = h * (tm + ta + tu)
+    lq = ns = 0
+    for i in range(hs):
+        t0 = time.perf_counter()
+        fin = O.restore_partition(parts[i].q_match[0].rep, mask[i])
+        tr_ = time.perf_counter() - t0
+        tm, ts, ta, tu, lq, ns = means_attn_unmerge(fin, parts[i].k_rep[0], x0["q"][i], x0["k"][i], x0["v"][i])
+        T["restore"] += tr_
+        T["means"] += tm
+        T["attention_sample"] += ts
+        T["unmerge"] += tu
+        per_head_layer0 += tr_ + tm + ta + tu
+        if n_cached > 0:
+            tm, ts, ta, tu, _, _ = means_attn_unmerge(fin, parts[i].k_rep[0], xc["q"][i], xc["k"][i], xc["v"][i])
+            T["means"] += tm
+            T["attention_sample"] += ts
+            T["unmerge"] += tu
+            cached_per_head += tm + ta + tu
+    per_head_layer0 += T["match"] + T["deviation"]
+    layer0 = h * per_head_layer0 / hs + T["select"]
+    cached = h * cached_per_head / hs
     stack = layer0 + n_cached * cached
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    measured = sum(v for kk, v in T.items() if kk != "attention_extrapolated")
+    measured = sum(T.values())
     return {"value": (1 + n_cached) * w.n_tokens / stack, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"oracle stages on head {head} of {w.heads} over all {w.n_tokens} tokens (matching, top-r, "
+            "sample": (f"oracle stages on {hs} of {w.heads} heads over all {w.n_tokens} tokens (matching, top-r, "
                        f"deviations, restore, means, unmerge), the global outlier choice over {w.heads}x{w.n_tokens} "
-                       f"deviations, attention for {min(rows, lq)} of {lq} merged query rows; "
-                       f"measured {measured:.1f} s of CPU stages; extrapolated x{h} heads and to all merged rows: "
-                       f"layer 0 {layer0:.0f} s" + (f", cached layer {cached:.0f} s" if n_cached else "")
+                       f"deviations, attention for {ns} of {lq} merged query rows per sampled head"
+                       + (f" (layer 0 and one cached layer)" if n_cached else "")
+                       + f"; measured {measured:.1f} s of CPU work; extrapolated x{h}/{hs} heads and to all merged "
+                       f"rows: layer 0 {layer0:.0f} s" + (f", cached layer {cached:.0f} s, stack of {1 + n_cached} "
+                                                           f"{stack:.0f} s" if n_cached else "")
                        + f"; numpy/BLAS threads {threads}, cpu {platform.processor() or platform.machine()}"),
             "stage_seconds": {kk: round(v, 3) for kk, v in T.items()},
             "layer0_s_extrapolated": layer0, "cached_layer_s_extrapolated": cached if n_cached else None}
@@ -313,10 +330,12 @@ def timed(torch, stream, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def lengths(H, plan, ws, w, ga):
-    lq = np.diff(H.debug_read(plan, ws, "cu_q")).astype(np.float64)
+def lengths(H, plan, ws, w, ga, index=None):
+    """Per-head merged query lengths and key counts of the last full layer
+    (read from the merge index when the layer filled one)."""
+    lq = np.diff(H.debug_read(plan, ws, "cu_q", index=index)).astype(np.float64)
     lk = plan.info["kv_len"]
-    lkh = H.debug_read(plan, ws, "kv_len").astype(np.float64) if ga else np.full(w.heads, float(lk))
+    lkh = H.debug_read(plan, ws, "kv_len", index=index).astype(np.float64) if ga else np.full(w.heads, float(lk))
     return lq, lkh
 
 
@@ -337,7 +356,7 @@ def single_layer_summary(H, torch, w, seed, reps_floor=10):
     H.set_timing(["attn"])
     ms = timed(torch, stream, run, reps)
     at, calls = H.get_timing()
-    H.set_timing(None)
+    H.set_timing(None, serial=True)
     timed(torch, stream, run, 30)
     stages, _ = H.get_timing()
     H.set_timing([])
@@ -360,7 +379,8 @@ def main():
     ap.add_argument("--workload", default="vggt500", choices=sorted(gen.WORKLOADS))
     ap.add_argument("--seed", type=int, default=gen.DEFAULT_SEED)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512, help="cpu baseline: merged query rows of attention timed")
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="cpu baseline: merged query rows of attention timed")
+    ap.add_argument("--cpu-heads", type=int, default=2, help="cpu baseline: heads in the oracle's sample")
     ap.add_argument("--dense-reps", type=int, default=2)
     ap.add_argument("--no-extra", action="store_true", help="skip the 30-frame layer reported as extra keys")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -404,8 +424,8 @@ def main():
     dev, host0, host1 = [], {}, {}
     for l, xl in gen.layer_stack(w, seed=args.seed, layers=1 + n_cached):
         dev.append([torch.from_numpy(xl[t]).to(tdt).cuda() for t in "qkv"])
-        if l <= 1 and not args.no_cpu_baseline:  # the CPU baseline's sample: head 0 of layers 0 and 1
-            (host0 if l == 0 else host1).update({t: xl[t][:1].copy() for t in "qkv"})
+        if l <= 1 and not args.no_cpu_baseline:  # the CPU baseline's sample heads of layers 0 and 1
+            (host0 if l == 0 else host1).update({t: xl[t][:args.cpu_heads].copy() for t in "qkv"})
         del xl
     log(f"[bench] inputs of {1 + n_cached} layer(s) resident in HBM ({time.perf_counter() - t0:.1f} s)")
     plan = H.Plan.from_workload(w)
@@ -459,7 +479,7 @@ def main():
         # leave layer 0's intermediates in the workspace for the reads below
         H.layer(plan, *dev[0], ws=ws, out=out, index=idx, stream=stream)
 
-    lq, lkh = lengths(H, plan, ws, w, ga)
+    lq, lkh = lengths(H, plan, ws, w, ga, idx)
     alg = algorithmic(w, plan, lq, lkh)
     ga_info = None
     if ga:
@@ -491,14 +511,15 @@ def main():
         else:
             other_roofline = match_roof
 
-    # per-stage breakdown (separate untimed pass; events around every stage)
-    H.set_timing(None)
+    # per-stage breakdown (separate untimed pass; events around every stage,
+    # every launch on one stream so that each kernel runs alone)
+    H.set_timing(None, serial=True)
     for _ in range(8):
         H.layer(plan, *dev[0], ws=ws, out=out, index=idx, stream=stream)
     stages, _ = H.get_timing()
     cstages = None
     if n_cached > 0:
-        H.set_timing(None)
+        H.set_timing(None, serial=True)
         for _ in range(8):
             H.layer_cached(plan, idx, *dev[1], ws=ws, out=out, stream=stream)
         cstages, _ = H.get_timing()
@@ -541,8 +562,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("[bench] cpu baseline: oracle stages on one head")
-        cpu = cpu_baseline(w, host0, host1, n_cached, rows=args.cpu_rows)
+        log(f"[bench] cpu baseline: oracle stages on {args.cpu_heads} heads")
+        cpu = cpu_baseline(w, host0, host1, n_cached, rows=args.cpu_rows, heads=args.cpu_heads)
         log(f"[bench]   {cpu['sample']}")
 
     res = {
@@ -566,6 +587,9 @@ def main():
         "roofline": roofline,
         **({"roofline_other_kernel": other_roofline} if other_roofline else {}),
         "rooflines": rooflines,
+        "rooflines_note": ("per-kernel achieved / peak from HIP events around each stage in a separate pass of 8 "
+                           "calls with every launch on one stream (kernels alone on the GPU); algorithmic bytes "
+                           "count each element read or written once"),
         "cpu_baseline": cpu,
         "stack": per_layer,
         "stages_ms": stages,

@@ -297,6 +297,12 @@ typedef enum {
   HTTM_T_SELECT_K,   /* key stream selection (library stream) */
   HTTM_T_COUNT
 } httm_timing_stage;
+/* With HTTM_TIMING_SERIAL in the mask (and at least one stage bit), the
+ * timed httm_layer / httm_layer_cached calls enqueue every launch on the
+ * caller's stream instead of forking the key branch onto the library
+ * stream: each stage then times its kernels running alone on the GPU (for
+ * per-kernel rooflines).  Results are bit-identical either way. */
+#define HTTM_TIMING_SERIAL (1 << 30)
 httm_status httm_set_timing(int32_t stage_mask);
 httm_status httm_get_timing(float* ms, int32_t n, int32_t* calls);
 

@@ -443,3 +443,28 @@ def test_edge_geometry_layers(case, dtype):
     rep = staged.check_layer(x["q"], x["k"], x["v"], p, gpu, out, **tol)
     _say("  ", rep.as_dict())
     assert rep.delta_nonexact == 0
+
+
+def test_serial_timing_mode_is_bit_identical():
+    """With the serialized timing mode every launch of a layer (and a cached
+    layer) goes to the caller's stream: the same kernels on the same data, so
+    the same bits as the forked schedule."""
+    w = small_bf16(frames=6, heads=4)
+    x = gen.layer_inputs(w)
+    plan = H.Plan.from_workload(w)
+    q, k, v = (to_dev(x[t], w.dtype) for t in "qkv")
+    ws = H.workspace(plan)
+    o1, idx = H.layer(plan, q, k, v, ws=ws, keep_index=True)
+    c1 = H.layer_cached(plan, idx, q, k, v, ws=ws)
+    o1, c1 = o1.clone(), c1.clone()
+    H.set_timing(None, serial=True)
+    try:
+        o2 = H.layer(plan, q, k, v, ws=ws, index=idx)
+        c2 = H.layer_cached(plan, idx, q, k, v, ws=ws)
+        torch.cuda.synchronize()
+        stages, calls = H.get_timing()
+    finally:
+        H.set_timing([])
+    assert calls == 2 and stages["sim_k"] > 0 and stages["merge_kv"] > 0
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))

@@ -350,12 +350,20 @@ def debug_read(plan: Plan, ws, item: str, stream=None, index: Optional[CachedInd
     return arr
 
 
-def set_timing(stages=None) -> None:
-    """Record HIP events around the named stages of the next calls (None: all, []: off)."""
+TIMING_SERIAL = 1 << 30
+
+
+def set_timing(stages=None, serial: bool = False) -> None:
+    """Record HIP events around the named stages of the next calls (None: all, []: off).
+
+    ``serial``: while timing, layers run every launch on the caller's stream
+    (no concurrent key branch), so each stage times its kernels alone."""
     names = TIMING_STAGES if stages is None else list(stages)
     mask = 0
     for n in names:
         mask |= 1 << TIMING_STAGES.index(n)
+    if serial and mask:
+        mask |= TIMING_SERIAL
     _check(lib().httm_set_timing(mask))
 
 

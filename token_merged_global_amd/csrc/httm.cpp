@@ -412,6 +412,7 @@ P* at(void* base, const Region& r) {
 constexpr int kSlots = 32;
 struct Timing {
   int32_t mask = 0;
+  bool serial = false;
   bool created = false;
   int calls = 0;
   hipEvent_t ev[kSlots][2 * HTTM_T_COUNT] = {};
@@ -437,6 +438,9 @@ void timing_begin_call() {
 void timing_end_call() {
   if (g_timing.mask) ++g_timing.calls;
 }
+// While timing with HTTM_TIMING_SERIAL, layers enqueue every launch on the
+// caller's stream, so that each stage's events bracket kernels running alone.
+bool timing_serial() { return g_timing.serial; }
 
 #define CHECK_LAUNCH(expr)                                                        \
   do {                                                                            \
@@ -846,8 +850,10 @@ httm_status httm_layer(const httm_plan* pl, void* ws, size_t ws_bytes, const voi
   if (index && ((uintptr_t)index->dev & 15)) return fail(HTTM_ERR_INVALID_ARG, "index must be 16-byte aligned");
   std::lock_guard<std::mutex> lock(g_launch_mu);
   SideStream* side = nullptr;
-  s = side_stream(&side);
-  if (s != HTTM_OK) return s;
+  if (!timing_serial()) {
+    s = side_stream(&side);
+    if (s != HTTM_OK) return s;
+  }
   return enqueue_layer(pl, ws, index, q, k, v, out, reinterpret_cast<hipStream_t>(stream), side);
 }
 
@@ -889,21 +895,26 @@ httm_status httm_layer_cached(const httm_plan* pl, void* ws, size_t ws_bytes, co
   char* idx = reinterpret_cast<char*>(index->dev);
   std::lock_guard<std::mutex> lock(g_launch_mu);
   SideStream* side = nullptr;
-  s = side_stream(&side);
-  if (s != HTTM_OK) return s;
+  if (!timing_serial()) {
+    s = side_stream(&side);
+    if (s != HTTM_OK) return s;
+  }
+  hipStream_t kst = side ? side->st : st;  // stream of the K / V merge
   timing_begin_call();
   CHECK_LAUNCH(launch_zero_init(at<float>(ws, pl->L.kmax), g.heads, at<int>(ws, pl->L.fb), nullptr, 0, nullptr, 0,
                                 st));
-  CHECK_LAUNCH(hipEventRecord(side->fork, st));
-  CHECK_LAUNCH(hipStreamWaitEvent(side->st, side->fork, 0));
-  stage_begin(HTTM_T_MERGE_KV, side->st);
+  if (side) {
+    CHECK_LAUNCH(hipEventRecord(side->fork, st));
+    CHECK_LAUNCH(hipStreamWaitEvent(kst, side->fork, 0));
+  }
+  stage_begin(HTTM_T_MERGE_KV, kst);
   CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
                                reinterpret_cast<const int32_t*>(idx + I.k_members.off),
                                reinterpret_cast<const int32_t*>(idx + I.k_off.off),
-                               at<void>(ws, pl->L.kt), at<void>(ws, pl->L.vt), at<float>(ws, pl->L.kmax), side->st,
+                               at<void>(ws, pl->L.kt), at<void>(ws, pl->L.vt), at<float>(ws, pl->L.kmax), kst,
                                pl->p.partition == 1 ? reinterpret_cast<const int32_t*>(idx + I.lenk.off) : nullptr));
-  stage_end(HTTM_T_MERGE_KV, side->st);
-  CHECK_LAUNCH(hipEventRecord(side->join, side->st));
+  stage_end(HTTM_T_MERGE_KV, kst);
+  if (side) CHECK_LAUNCH(hipEventRecord(side->join, kst));
   stage_begin(HTTM_T_MERGE_Q, st);
   CHECK_LAUNCH(launch_merge_q_cached(dt, g.heads, g.N, pl->q_cap, q,
                                      reinterpret_cast<const int32_t*>(idx + I.fmembers.off),
@@ -911,7 +922,7 @@ httm_status httm_layer_cached(const httm_plan* pl, void* ws, size_t ws_bytes, co
                                      reinterpret_cast<const int32_t*>(idx + I.lenq.off),
                                      at<void>(ws, pl->L.qt), st));
   stage_end(HTTM_T_MERGE_Q, st);
-  CHECK_LAUNCH(hipStreamWaitEvent(st, side->join, 0));
+  if (side) CHECK_LAUNCH(hipStreamWaitEvent(st, side->join, 0));
   s = attend_unmerge(pl, ws, idx, at<void>(ws, pl->L.qt), out, st);
   if (s == HTTM_OK) timing_end_call();
   return s;
@@ -1047,6 +1058,7 @@ httm_status httm_set_timing(int32_t stage_mask) {
     g_timing.created = true;
   }
   g_timing.mask = stage_mask & ((1 << HTTM_T_COUNT) - 1);
+  g_timing.serial = g_timing.mask != 0 && (stage_mask & HTTM_TIMING_SERIAL) != 0;
   g_timing.calls = 0;
   for (int k = 0; k < kSlots; ++k)
     for (int i = 0; i < HTTM_T_COUNT; ++i) g_timing.used[k][i] = false;
