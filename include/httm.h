@@ -104,6 +104,14 @@ typedef struct {
                             ceil(H/2) * ceil(W/2)) (at most N), which sizes q_groups and
                             kv_len in httm_plan_info.  Limits: at most 4096 patches per
                             frame and N < 2^20 */
+                         /* 2 = one head-shared partition from global matching (the merging
+                            the HTTM page contrasts itself with, research background and key
+                            designs 1-2): the keys averaged over heads, every patch token in
+                            original order as one block, every 4th a destination, the
+                            floor(kv_ratio * patches) most similar sources merged; the same
+                            groups serve the queries and keys of every head (deviation,
+                            outlier restore, attention and unmerge per head as usual);
+                            q_ratio, strides and block_order do not apply.  Limit: N < 2^20 */
   double protect_pct;    /* partition 1: percent of each frame's patches protected, [0, 100]
                             (the page uses 10); protected = floor(protect_pct / 100 * H*W) */
   int32_t attn_split;    /* bf16 attention: key ranges per query tile whose partial results are
@@ -255,13 +263,19 @@ httm_status httm_attention_dense(const httm_plan* plan, void* ws, size_t ws_byte
  *       group multiplied by softmax_scale * log2(e) (rows past L_k are 0);
  *   HTTM_DBG_VT: [h][64][L_k padded to 64] merged values, transposed;
  *   HTTM_DBG_QT: [q_capacity][64] packed merged queries, head h's rows at
- *       [cu_q[h], cu_q[h+1]) (rows past cu_q[h] are unspecified). */
+ *       [cu_q[h], cu_q[h+1]) (rows past cu_q[h] are unspecified).
+ * Head-shared partition only (partition 2):
+ *   HTTM_DBG_GM_METRIC: [N][64] the head-mean keys matched on (element type);
+ *   HTTM_DBG_GM_MATCH: [N] int32 matched destination token of every source,
+ *       -1 for every other token;
+ *   HTTM_DBG_GM_SCORE: [N] float cosine of that match (0 for non-sources). */
 typedef enum {
   HTTM_DBG_Q_MATCH = 0, HTTM_DBG_Q_SCORE, HTTM_DBG_KV_MATCH, HTTM_DBG_KV_SCORE,
   HTTM_DBG_Q_GROUP, HTTM_DBG_KV_GROUP, HTTM_DBG_DELTA, HTTM_DBG_OUTLIER,
   HTTM_DBG_Q_SLOT, HTTM_DBG_CU_Q, HTTM_DBG_SELECT, HTTM_DBG_ATTN_FALLBACK,
   HTTM_DBG_GA_VAR, HTTM_DBG_GA_ROLE, HTTM_DBG_GA_MATCH, HTTM_DBG_GA_SCORE, HTTM_DBG_KV_LEN,
   HTTM_DBG_KT, HTTM_DBG_VT, HTTM_DBG_QT,
+  HTTM_DBG_GM_METRIC, HTTM_DBG_GM_MATCH, HTTM_DBG_GM_SCORE,
   HTTM_DBG_COUNT
 } httm_debug_item;
 httm_status httm_debug_size(const httm_plan* plan, int32_t item, size_t* bytes);
@@ -283,7 +297,9 @@ httm_status httm_debug_read(const httm_plan* plan, const void* ws, const httm_in
  * With partition = 1, HTTM_T_SIM times the whole geometry-aware partition of
  * both streams (on the caller's stream) and HTTM_T_GA_MATCH its global cosine
  * match alone (one launch); the two selection stages and HTTM_T_SIM_K are not
- * recorded.  httm_layer_cached records HTTM_T_MERGE_KV (its K/V merge, on the
+ * recorded.  With partition = 2 the same two stages time the head-shared
+ * partition (metric, match, top-r, groups, per-head copies) and its global
+ * match kernel.  httm_layer_cached records HTTM_T_MERGE_KV (its K/V merge, on the
  * library stream) and HTTM_T_MERGE_Q (its query means); httm_attention_dense
  * records HTTM_T_MERGE_KV for its input preparation. */
 typedef enum {

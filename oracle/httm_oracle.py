@@ -60,7 +60,8 @@ class Params:
     kv_dst_stride: int = 0
     block_order: int = 0  # 0 frame-major (R3), 1 frame-minor
     softmax_scale: float = 0.0  # 0 -> 1/sqrt(d_head) (R21)
-    partition: int = 0  # 0 HTTM temporal blocks; 1 geometry-aware three-class partition (R31)
+    partition: int = 0  # 0 HTTM temporal blocks; 1 geometry-aware three-class partition (R31);
+    #                     2 one head-shared topology from global matching (R37-R40)
     protect_pct: float = 10.0  # geometry-aware partition: percent of each frame's patches protected
 
     @property
@@ -398,6 +399,80 @@ def ga_match_stream(x: np.ndarray, p: Params, chunk: int = 4096) -> StreamMatch:
 
 
 # --------------------------------------------------------------------------
+# Head-shared global matching (the merging the HTTM page contrasts itself with)
+# --------------------------------------------------------------------------
+# HTTM page, research background and key design 1: ToMe-style merging (as
+# FastVGGT uses it) applies one merge topology to every head and matches over
+# the whole long sequence; key design 2 prices that global matching at about
+# 0.19 N^2 d_head FLOPs for a 25 % destination / 75 % source split.
+# Readings R37-R40 (design notes).
+GM_STRIDE = 4  # R38: every 4th patch token is a destination (25 % / 75 %)
+
+
+def round_bf16_rne(x: np.ndarray) -> np.ndarray:
+    """Nearest bf16 value of each fp32 value (ties to even), as fp32."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def head_shared_metric(k: np.ndarray, bf16: bool) -> np.ndarray:
+    """The token feature one shared topology is matched on (R37): the key
+    vectors averaged over heads -- an fp32 sum in ascending head order and
+    one fp32 division by h -- rounded to bf16 (nearest, ties to even) in a
+    bf16 layer, whose similarity takes bf16 operands."""
+    acc = np.zeros(k.shape[1:], dtype=np.float32)
+    for i in range(k.shape[0]):
+        acc = (acc + k[i]).astype(np.float32)
+    m = (acc / np.float32(k.shape[0])).astype(np.float32)
+    return round_bf16_rne(m) if bf16 else m
+
+
+def global_match(x: np.ndarray, p: Params, ratio: float, chunk: int = 4096) -> StreamMatch:
+    """Bipartite matching over the whole sequence (R38, R39).
+
+    The patch tokens in their original order (frames, then raster patches;
+    no temporal reordering) form one block; positions i = 0, 4, 8, ... are
+    destinations, the rest sources.  Every source keeps its most similar
+    destination (cosine of RowNorm rows, fp32; ties to the smaller position),
+    the r = min(|S|, floor(ratio * P + 1e-9)) sources with the highest score
+    merge (ties to the smaller position), and groups are each destination
+    with its merged sources; other sources and specials stay alone.
+    """
+    N = p.n_tokens
+    tok = np.flatnonzero(~is_special(p))
+    pos = np.arange(len(tok))
+    dpos, spos = pos[pos % GM_STRIDE == 0], pos[pos % GM_STRIDE != 0]
+    rep = np.arange(N, dtype=np.int64)
+    mdst = np.full(N, -1, dtype=np.int64)
+    score = np.full(N, np.nan, dtype=np.float32)
+    selected = np.zeros(N, dtype=bool)
+    is_src = np.zeros(N, dtype=bool)
+    if len(spos) and len(dpos):
+        dn = row_normalize(x[tok[dpos]])
+        m = np.empty(len(spos), dtype=np.int64)
+        sc = np.empty(len(spos), dtype=np.float32)
+        for c0 in range(0, len(spos), chunk):
+            sim = (row_normalize(x[tok[spos[c0:c0 + chunk]]]) @ dn.T).astype(np.float32)
+            j = np.argmax(sim, axis=1)  # first maximum = smallest destination position
+            m[c0:c0 + chunk] = dpos[j]
+            sc[c0:c0 + chunk] = sim[np.arange(len(j)), j] + np.float32(0.0)
+        r = merge_count(ratio, len(tok), len(spos))
+        sel = select_top_r(sc, spos, r)
+        src_tok, dst_of_src = tok[spos], tok[m]
+        is_src[src_tok] = True
+        mdst[src_tok] = dst_of_src
+        score[src_tok] = sc
+        selected[src_tok] = sel
+        lab = np.arange(N, dtype=np.int64)
+        lab[src_tok[sel]] = dst_of_src[sel]
+        mins = np.arange(N, dtype=np.int64)
+        np.minimum.at(mins, lab, np.arange(N, dtype=np.int64))
+        rep = mins[lab]
+    return StreamMatch(rep=rep, match_dst=mdst, score=score, selected=selected, is_src=is_src)
+
+
+# --------------------------------------------------------------------------
 # Partitions and means
 # --------------------------------------------------------------------------
 @dataclass
@@ -544,9 +619,21 @@ class Trace:
     out: Optional[np.ndarray] = None
 
 
-def match_heads(q: np.ndarray, k: np.ndarray, p: Params, heads: Sequence[int]) -> Trace:
-    """Steps 1-4 for every listed head (head-wise merging, HTTM page, key design 1)."""
+def match_heads(q: np.ndarray, k: np.ndarray, p: Params, heads: Sequence[int], bf16: bool = False) -> Trace:
+    """Steps 1-4 for every listed head (head-wise merging, HTTM page, key design 1).
+
+    With the head-shared partition (partition 2) one topology, matched on
+    the listed heads' mean key (R37; ``bf16``: the layer's element type),
+    serves the queries and keys of every head (R40).
+    """
     tr = Trace()
+    if p.partition == 2:
+        shared = global_match(head_shared_metric(k, bf16), p, p.kv_ratio)
+        for _ in heads:
+            tr.q_match.append(shared)
+            tr.k_match.append(shared)
+            tr.k_rep.append(shared.rep)
+        return tr
     for i in range(len(heads)):
         if p.partition == 1:  # geometry-aware three-class partition (R31)
             tr.q_match.append(ga_match_stream(q[i], p))
@@ -586,15 +673,18 @@ def head_output(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_final_rep: np.nda
 
 
 def layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, p: Params,
-          out_heads: Optional[Sequence[int]] = None, rows: Optional[np.ndarray] = None) -> Trace:
+          out_heads: Optional[Sequence[int]] = None, rows: Optional[np.ndarray] = None,
+          bf16: bool = False) -> Trace:
     """One HTTM global-attention layer (HTTM page, overall framework).
 
     q, k, v: [h][N][d] fp32 (bf16 inputs upcast exactly).  Steps 1-5 run on
     every head because the outlier budget is shared across heads; steps 6-7
     run for ``out_heads`` (default all) and, if given, only for ``rows``.
+    ``bf16``: the layer's element type is bf16 (only the head-shared metric
+    of partition 2 depends on it).
     """
     h = q.shape[0]
-    tr = match_heads(q, k, p, list(range(h)))
+    tr = match_heads(q, k, p, list(range(h)), bf16=bf16)
     tr.delta = deviations(q, [m.rep for m in tr.q_match])
     tr.outlier = select_outliers(tr.delta, outlier_budget(p))
     tr.q_final_rep = [restore_partition(tr.q_match[i].rep, tr.outlier[i]) for i in range(h)]

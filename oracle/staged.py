@@ -192,11 +192,86 @@ def check_ga_stream(x: np.ndarray, p: O.Params, gpu_var: np.ndarray, gpu_role: n
     return got
 
 
+def check_gm(k: np.ndarray, p: O.Params, gpu_metric: np.ndarray, gpu_match: np.ndarray, gpu_score: np.ndarray,
+             gpu_group: np.ndarray, rep: Report, bf16: bool, chunk: int = 2048) -> np.ndarray:
+    """Head-shared global matching; returns the canonical shared groups.
+
+    (i) the head-mean metric bit for bit; (ii) every source's destination is
+    the oracle's most similar one or a counted near-tie, its score within
+    1e-5; (iii) r sources merged, the merged set equal to the oracle's top-r
+    except counted ties within 1e-5 of the r-th score, groups exactly what
+    the implementation's own matches and selection imply.
+    gpu_metric: [N][d] float; gpu_match: matched destination token per token
+    (-1 for non-sources); gpu_group: slot of every token (one head's).
+    """
+    N = p.n_tokens
+    m = O.head_shared_metric(k, bf16)
+    gm = np.asarray(gpu_metric, dtype=np.float32)
+    if not np.array_equal(m.view(np.uint32), gm.view(np.uint32)):
+        bad = np.flatnonzero((m != gm).any(axis=1))
+        raise ParityError(f"head-shared metric differs at {len(bad)} tokens (first {bad[0]})")
+    tok = np.flatnonzero(~O.is_special(p))
+    pos = np.arange(len(tok))
+    dpos, spos = pos[pos % O.GM_STRIDE == 0], pos[pos % O.GM_STRIDE != 0]
+    src, dst = tok[spos], tok[dpos]
+    match = np.asarray(gpu_match, dtype=np.int64)
+    if (match[np.setdiff1d(np.arange(N), src)] != -1).any():
+        raise ParityError("head-shared: a token that is not a source carries a match")
+    rep_gpu = canonical(gpu_group)
+    if len(src) == 0:
+        if not np.array_equal(rep_gpu, np.arange(N)):
+            raise ParityError("head-shared: groups without sources")
+        return rep_gpu
+    mj = np.searchsorted(dst, match[src])
+    if (mj >= len(dst)).any() or (dst[np.minimum(mj, len(dst) - 1)] != match[src]).any():
+        raise ParityError("head-shared: a source is matched to a token that is not a destination")
+    gs = np.asarray(gpu_score, dtype=np.float32)[src]
+    dn = O.row_normalize(m[dst])
+    so = np.empty(len(src), dtype=np.float32)
+    for c0 in range(0, len(src), chunk):
+        sim = (O.row_normalize(m[src[c0:c0 + chunk]]) @ dn.T).astype(np.float32)
+        rows = np.arange(sim.shape[0])
+        jo = np.argmax(sim, axis=1)
+        jg = mj[c0:c0 + chunk]
+        gap = sim[rows, jo] - sim[rows, jg]
+        bad = (jg != jo) & (gap >= NEAR_TIE)
+        if bad.any():
+            i = int(np.flatnonzero(bad)[0])
+            raise ParityError(f"head-shared: source {src[c0 + i]} matched {dst[jg[i]]} (sim {sim[i, jg[i]]:.7f}) "
+                              f"but best is {dst[jo[i]]} (sim {sim[i, jo[i]]:.7f})")
+        rep.match_near_ties += int(((jg != jo) & (gap < NEAR_TIE)).sum())
+        err = np.abs(gs[c0:c0 + chunk].astype(np.float64) - sim[rows, jg])
+        rep.max_score_err = max(rep.max_score_err, float(err.max()))
+        if err.max() >= NEAR_TIE:
+            raise ParityError(f"head-shared: score error {err.max():.3g}")
+        so[c0:c0 + chunk] = sim[rows, jo]
+    sel = rep_gpu[src] == rep_gpu[match[src]]
+    r = O.merge_count(p.kv_ratio, len(tok), len(src))
+    if int(sel.sum()) != r:
+        raise ParityError(f"head-shared: {int(sel.sum())} sources merged, expected r={r}")
+    osel = O.select_top_r(so, spos, r)
+    diff = sel != osel
+    if diff.any():
+        thr = np.sort(so)[::-1][r - 1] if r > 0 else np.inf
+        if (np.abs(so[diff] - thr) >= NEAR_TIE).any():
+            raise ParityError("head-shared: merged set differs away from the r-th score")
+        rep.select_near_ties += int(diff.sum())
+    label = np.arange(N, dtype=np.int64)
+    label[src[sel]] = match[src[sel]]
+    want = canonical(label)
+    if not np.array_equal(want, rep_gpu):
+        i = int(np.flatnonzero(want != rep_gpu)[0])
+        raise ParityError(f"head-shared: groups differ at token {i}: rep {rep_gpu[i]} vs {want[i]}")
+    rep.n_src += len(src)
+    return rep_gpu
+
+
 def check_layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, p: O.Params, gpu: Dict[str, np.ndarray],
                 out_gpu: np.ndarray, out_heads: Optional[Sequence[int]] = None,
                 rows: Optional[np.ndarray] = None, out_tol: Optional[float] = None,
                 match_heads: Optional[Sequence[int]] = None, rel_tol: Optional[float] = None,
-                workers: int = 1, out_half_ulp: bool = False, delta_exact: bool = True) -> Report:
+                workers: int = 1, out_half_ulp: bool = False, delta_exact: bool = True,
+                bf16: bool = False) -> Report:
     """Staged parity of one layer.
 
     gpu: q_match, q_score, kv_match, kv_score ([h][src]), q_group, kv_group,
@@ -211,6 +286,10 @@ def check_layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, p: O.Params, gpu: D
     RMS (tiny or heavily merged layers), since there one rounding step of the
     largest outputs is larger than 2e-2 x RMS.  ``workers`` threads share the
     per-head work (numpy releases the GIL in its array kernels).
+    Head-shared partition (partition 2): gm_metric ([N][d] float), gm_match,
+    gm_score ([N]) in place of the match / score items; ``bf16`` states the
+    layer's element type (the metric is rounded to it); every head's query
+    and key groups must be the one shared partition.
     ``delta_exact`` (default) requires the deviations bit for bit on the
     implementation's groups (the same fp32 operation sequence); False
     accepts differences within 1e-5 x max(1, delta) and only counts them.
@@ -224,9 +303,19 @@ def check_layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, p: O.Params, gpu: D
     ga = p.partition == 1
     if ga:
         ga_items = {it: np.asarray(gpu[it]).reshape(2, h, N) for it in ("ga_var", "ga_role", "ga_match", "ga_score")}
+    shared = None
+    if p.partition == 2:
+        shared = check_gm(k, p, np.asarray(gpu["gm_metric"]).reshape(N, -1), gpu["gm_match"], gpu["gm_score"],
+                          gpu["kv_group"][0], rep, bf16)
 
     def per_head(i):
         r = Report()
+        if shared is not None:
+            # one partition for the queries and keys of every head
+            for nm in ("q_group", "kv_group"):
+                if not np.array_equal(canonical(gpu[nm][i]), shared):
+                    raise ParityError(f"head {i}: {nm} is not the shared partition")
+            return shared, shared, r
         if ga:
             # variance map, classes and groups on every head; the argmax of
             # the matches on the match heads

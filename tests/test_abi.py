@@ -139,6 +139,26 @@ def test_validation_codes():
         assert _status(attn_split=split) == 0
     for split in (-1, 3, 16):
         assert _status(attn_split=split) == 1
+    assert _status(partition=2) == 0
+    assert _status(partition=3) == 1
+
+
+@pytest.mark.parametrize("name,kv", [("tiny", 0.5), ("vggt30", 0.5), ("vggt30", 0.75), ("vggt500", 0.5)])
+def test_head_shared_plan_sizes(name, kv):
+    """partition 2: one block of every patch, every 4th a destination, r =
+    min(|S|, floor(kv * P)) merged: N - r groups for queries and keys."""
+    w = gen.WORKLOADS[name].with_(partition=2, kv_ratio=kv)
+    plan = H.Plan.from_workload(w)
+    P = w.frames * w.grid_h * w.grid_w
+    nd = -(-P // 4)
+    r = min(P - nd, int(math.floor(kv * P + 1e-9)))
+    assert plan.info["q_groups"] == plan.info["kv_len"] == w.n_tokens - r
+    assert plan.info["q_src"] == plan.info["kv_src"] == P - nd
+    p = O.Params.from_workload(w)
+    if name == "tiny":
+        q, k, v = (x for x in (np.random.default_rng(1).standard_normal((1, w.n_tokens, 64)).astype(np.float32),) * 3)
+        g = O.global_match(O.head_shared_metric(k, False), p, kv)
+        assert len(np.unique(g.rep)) == w.n_tokens - r
 
 
 def test_layer_rejects_bad_buffers_before_any_launch():
@@ -242,7 +262,7 @@ def test_ga_group_bound_holds_on_the_oracle():
 
 def test_ga_validation_codes():
     assert _status(partition=1) == 0
-    assert _status(partition=2) == 1
+    assert _status(partition=3) == 1
     assert _status(partition=-1) == 1
     assert _status(partition=1, protect_pct=-1.0) == 1
     assert _status(partition=1, protect_pct=100.5) == 1

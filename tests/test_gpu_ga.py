@@ -17,7 +17,7 @@ import oracle as O
 from oracle import staged
 import token_merged_global_amd as H
 
-from gpu_util import BF16_REL, F32_ABS, run_layer, say, to_dev
+from gpu_util import BF16_REL, F32_ABS, read_all, run_layer, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -291,3 +291,32 @@ def test_ga_match_timing_stage():
             assert 0 < st["ga_match"] <= st["sim"]
         else:
             assert st["ga_match"] == 0
+
+
+@pytest.mark.timeout(300)
+def test_ga_constant_tokens_one_huge_group():
+    """Every patch token of q and k the same row (per head): all cosines tie,
+    every source joins the first destination, so one group holds every
+    source (26,187 at 30 frames) and that destination.  The member lists come
+    from a stable sort by slot, linear in N whatever the group sizes."""
+    w = gen.WORKLOADS["vggt30"].with_(heads=2, partition=1, protect_pct=10.0)
+    x = gen.layer_inputs(w)
+    sp = np.arange(w.n_tokens) % w.tokens_per_frame < w.n_special
+    for t in "qk":
+        for h in range(w.heads):
+            x[t][h][~sp] = x[t][h][w.n_special]
+    p = O.Params.from_workload(w)
+    plan = H.Plan.from_workload(w)
+    q, k, v = (to_dev(x[t], w.dtype) for t in "qkv")
+    ws = H.workspace(plan)
+    out = H.layer(plan, q, k, v, ws=ws)
+    torch.cuda.synchronize()
+    gpu = read_all(plan, ws, w.heads)
+    sizes = np.bincount(gpu["kv_group"][0])
+    n_src = int((gpu["ga_role"].reshape(2, w.heads, -1)[1, 0] == O.ROLE_SRC).sum())
+    say(f"[ga constant] largest key group {sizes.max()} of {w.n_tokens} tokens ({n_src} sources)")
+    assert sizes.max() == n_src + 1  # every source joins the first destination
+    rows = np.unique(np.r_[np.random.default_rng(2).choice(w.n_tokens, 128, replace=False), 0, w.n_tokens - 1])
+    rep = staged.check_layer(x["q"], x["k"], x["v"], p, gpu, out.float().cpu().numpy(), rows=rows,
+                             rel_tol=BF16_REL, out_half_ulp=True, match_heads=[0])
+    say("  ", rep.as_dict())

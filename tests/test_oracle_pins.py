@@ -604,3 +604,81 @@ def test_layer_cached_head_permutation():
     got = O.layer_cached(q[perm], k[perm], v[perm], p, [tr.q_final_rep[h] for h in perm],
                          [tr.k_rep[h] for h in perm])
     assert np.array_equal(got, tr.out[perm])
+
+
+# --------------------------------------------------------------------------
+# Head-shared global matching (HTTM page, research background and key designs
+# 1-2: one merge topology for every head, matched over the whole sequence
+# with a 25 % destination / 75 % source split)
+# --------------------------------------------------------------------------
+def _gm_params(**kw):
+    base = dict(heads=2, d_head=8, frames=3, grid_h=3, grid_w=4, n_special=1, n_s=4, n_t=2, q_ratio=0.5,
+                kv_ratio=0.5, outlier_pct=10.0, partition=2)
+    base.update(kw)
+    return O.Params(**base)
+
+
+def test_bf16_rounding_matches_torch():
+    x = np.random.default_rng(31).standard_normal(20000).astype(np.float32) * 3
+    x = np.r_[x, np.float32(1 + 2 ** -8), np.float32(1 + 3 * 2 ** -8), np.float32(-0.0), np.float32(0.0)]
+    want = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(O.round_bf16_rne(x).view(np.uint32), want.view(np.uint32))
+
+
+def test_global_match_is_one_block_over_all_patches():
+    """With one head the shared metric is that head's keys, and global
+    matching equals the block-local matching of the same keys with a single
+    block of every patch in original order (n_s = H*W, n_t = F,
+    frame-major), stride 4 and the same ratio."""
+    for ratio in (0.3, 0.5, 0.75):
+        p2 = _gm_params(heads=1, frames=4, grid_h=5, grid_w=6, kv_ratio=ratio)
+        p0 = O.Params(**{**p2.__dict__, "partition": 0, "n_s": 30, "n_t": 4, "q_dst_stride": 4, "kv_dst_stride": 4,
+                         "q_ratio": ratio})
+        assert len(O.blocks(p0)) == 1
+        q, k, v = _rand_qkv(p2, 41)
+        g = O.global_match(O.head_shared_metric(k, False), p2, ratio)
+        b = O.match_stream(k[0], p0, ratio, 4)
+        for f in ("rep", "match_dst", "selected", "is_src"):
+            assert np.array_equal(getattr(g, f), getattr(b, f)), f
+        assert np.array_equal(g.score[g.is_src], b.score[b.is_src])
+        # with q = k the whole layer is the block-local layer
+        t2 = O.layer(k, k, v, p2)
+        t0 = O.layer(k, k, v, p0)
+        assert np.array_equal(t2.out, t0.out)
+
+
+def test_head_shared_metric_is_the_head_mean():
+    """The metric is the mean key over heads: equal heads give that head back
+    exactly (h = 2), and small integer keys give exact means; every head's
+    query and key partitions are the one shared partition."""
+    p = _gm_params(heads=2)
+    q, k, v = _rand_qkv(p, 42)
+    k2 = np.stack([k[0], k[0]])
+    assert np.array_equal(O.head_shared_metric(k2, False), k[0])
+    ki = np.random.default_rng(43).integers(-8, 8, size=(4, p.n_tokens, 8)).astype(np.float32)
+    assert np.array_equal(O.head_shared_metric(ki, False), ki.astype(np.float64).mean(0).astype(np.float32))
+    tr = O.layer(q, k, v, p)
+    shared = O.global_match(O.head_shared_metric(k, False), p, p.kv_ratio)
+    for h in range(p.heads):
+        assert np.array_equal(tr.k_rep[h], shared.rep)
+        assert np.array_equal(tr.q_match[h].rep, shared.rep)
+    # the outlier restore still acts per head on the shared query groups
+    assert tr.outlier.sum() == O.outlier_budget(p)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_global_match_brute_force(seed):
+    """Double-loop cosine similarity, per-source argmax and exhaustive top-r
+    over all source subsets on a tiny sequence (12 patches)."""
+    rng = np.random.default_rng(200 + seed)
+    p = O.Params(heads=3, d_head=3, frames=3, grid_h=1, grid_w=4, n_special=1, n_s=4, n_t=3, q_ratio=0.5,
+                 kv_ratio=[0.25, 0.5, 0.6, 0.75][seed], outlier_pct=0.0, partition=2)
+    k = rng.integers(-4, 5, size=(3, p.n_tokens, 3)).astype(np.float32)
+    m = O.head_shared_metric(k, False)
+    patches = np.flatnonzero(~O.is_special(p))
+    g = O.global_match(m, p, p.kv_ratio)
+    match, score, sel = _brute_block(m[patches], 4, p.kv_ratio)
+    for i, j in match.items():
+        assert g.match_dst[patches[i]] == patches[j]
+        assert abs(g.score[patches[i]] - score[i]) < 1e-6
+    assert {i for i in range(len(patches)) if g.selected[patches[i]]} == sel

@@ -26,10 +26,12 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
           4: "index mismatch", 5: "device error"}
 DEBUG_ITEMS = ["q_match", "q_score", "kv_match", "kv_score", "q_group", "kv_group", "delta",
                "outlier", "q_slot", "cu_q", "select", "attn_fallback",
-               "ga_var", "ga_role", "ga_match", "ga_score", "kv_len", "kt", "vt", "qt"]
-#: Items that exist only under one partition (block-local / geometry-aware).
+               "ga_var", "ga_role", "ga_match", "ga_score", "kv_len", "kt", "vt", "qt",
+               "gm_metric", "gm_match", "gm_score"]
+#: Items that exist only under one partition (block-local / geometry-aware / head-shared).
 BLOCK_ITEMS = ["q_match", "q_score", "kv_match", "kv_score"]
 GA_ITEMS = ["ga_var", "ga_role", "ga_match", "ga_score", "kv_len"]
+GM_ITEMS = ["gm_metric", "gm_match", "gm_score"]
 TIMING_STAGES = ["sim", "select", "merge_kv", "merge_q", "outlier", "restore", "attn", "unmerge", "attn_tail",
                  "ga_match", "sim_k", "select_k"]
 
@@ -327,7 +329,9 @@ ROW_ITEMS = ["kt", "vt", "qt"]
 
 def debug_items(plan: Plan, rows: bool = False) -> List[str]:
     """The debug items that exist for ``plan``'s partition (merged rows only if ``rows``)."""
-    skip = BLOCK_ITEMS if plan.params.partition == 1 else GA_ITEMS
+    part = plan.params.partition
+    keep = {0: BLOCK_ITEMS, 1: GA_ITEMS, 2: GM_ITEMS}[part]
+    skip = [it for it in BLOCK_ITEMS + GA_ITEMS + GM_ITEMS if it not in keep]
     return [it for it in DEBUG_ITEMS if it not in skip and (rows or it not in ROW_ITEMS)]
 
 
@@ -343,7 +347,8 @@ def debug_read(plan: Plan, ws, item: str, stream=None, index: Optional[CachedInd
     rows = np.uint16 if plan.dtype == "bf16" else np.float32  # merged rows: bf16 bit patterns or fp32
     dt = {"q_score": np.float32, "kv_score": np.float32, "delta": np.float32, "outlier": np.uint8,
           "select": np.uint32, "ga_var": np.float32, "ga_role": np.uint8,
-          "ga_score": np.float32, "kt": rows, "vt": rows, "qt": rows}.get(item, np.int32)
+          "ga_score": np.float32, "kt": rows, "vt": rows, "qt": rows, "gm_metric": rows,
+          "gm_score": np.float32}.get(item, np.int32)
     arr = np.empty(n.value // np.dtype(dt).itemsize, dtype=dt)
     _check(lib().httm_debug_read(plan.handle, ws.data_ptr(), ctypes.byref(index.c) if index is not None else None,
                                  code, arr.ctypes.data, arr.nbytes, _stream_ptr(stream)))

@@ -30,7 +30,9 @@ PER_FILE = {"k_merge.hip": ["-ffp-contract=off"],
             "k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
             "k_sim.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
             # variance map compared bit for bit; MFMA cosine tiles as in k_sim
-            "k_ga.hip": ["-ffp-contract=off", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+            "k_ga.hip": ["-ffp-contract=off", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+            # head-shared metric: fp32 adds in head order and one division
+            "k_global.hip": ["-ffp-contract=off"]}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
           "-I", CSRC, "-Wall", "-Wno-unused-function"]
 

@@ -63,7 +63,11 @@ struct Layout {
   Region kmax, fb, opart, lpart, mpart;  // attention: key norms, fallback queue, split partials
   // geometry-aware partition (partition 1 only)
   Region ga_var, ga_role, ga_fcnt, ga_foff, ga_tot, ga_slot, ga_dlist, ga_dslot, ga_slist;
-  Region ga_gdst, ga_gslot, ga_gscore, ga_best, ga_snorm, ga_cnt, ga_fill, ga_tmp, ga_dg, ga_dinv;
+  Region ga_gdst, ga_gslot, ga_gscore, ga_best, ga_snorm, ga_cnt, ga_tmp, ga_dg, ga_dinv;
+  Region sort_keys, sort_vals, sort_counts;  // stable sort by slot (partitions 1 and 2)
+  // head-shared partition (partition 2 only)
+  Region gm_metric, gm_tot, gm_dlist, gm_slist, gm_dg, gm_dinv, gm_best, gm_snorm, gm_match, gm_score, gm_sel,
+      gm_topk, gm_unsel, gm_urank, gm_sums, gm_keys, gm_members, gm_off, gm_dbg_match, gm_dbg_score;
   Region index;  // used when the caller passes no index buffer
   size_t total = 0;
 };
@@ -125,6 +129,7 @@ struct httm_plan {
   int64_t attn_part_rows;  // rows of each key-split partial buffer
   int32_t ga_kp = 0, ga_bound = 0, ga_max_src = 0;  // geometry-aware partition sizes
   int32_t ga_dpitch = 0;  // gathered destination rows per (stream, head)
+  int32_t gm_nd = 0, gm_ns = 0, gm_r = 0, gm_dpitch = 0;  // head-shared partition sizes
   std::vector<httm_block> blocks;
 };
 
@@ -157,7 +162,7 @@ httm_status build(const httm_params& p, httm_plan* pl) {
   if (p.d_head != kD) return fail(HTTM_ERR_UNSUPPORTED, "only d_head == 64 is built");
   if (p.heads > kMaxHeads) return fail(HTTM_ERR_UNSUPPORTED, "at most 64 heads (per-head prefix tables live in LDS)");
   if (p.block_order != 0 && p.block_order != 1) return fail(HTTM_ERR_INVALID_ARG, "block_order must be 0 or 1");
-  if (p.partition != 0 && p.partition != 1) return fail(HTTM_ERR_INVALID_ARG, "partition must be 0 or 1");
+  if (p.partition < 0 || p.partition > 2) return fail(HTTM_ERR_INVALID_ARG, "partition must be 0, 1 or 2");
   if (p.partition == 1 && !(p.protect_pct >= 0.0 && p.protect_pct <= 100.0))
     return fail(HTTM_ERR_INVALID_ARG, "protect_pct must lie in [0, 100]");
   if ((int64_t)p.n_s * p.n_t > kMaxBlock) return fail(HTTM_ERR_UNSUPPORTED, "n_s * n_t must be <= 4096");
@@ -262,6 +267,18 @@ httm_status build(const httm_params& p, httm_plan* pl) {
     g.nslots[kQ] = g.nslots[kK] = (int32_t)bound_c;
     g.nsrc[kQ] = g.nsrc[kK] = pl->ga_max_src;
   }
+  if (p.partition == 2) {
+    // one block of every patch token in original order, every 4th a
+    // destination; r of the sources merge; N - r groups per head
+    if (N >= (1 << 20)) return fail(HTTM_ERR_UNSUPPORTED, "head-shared partition: at most 2^20 - 1 tokens");
+    const int32_t P = g.P;
+    pl->gm_nd = ceil_div(P, 4);
+    pl->gm_ns = P - pl->gm_nd;
+    pl->gm_r = merge_count(p.kv_ratio, P, pl->gm_ns);
+    pl->gm_dpitch = ceil_div(pl->gm_nd > 0 ? pl->gm_nd : 1, 64) * 64;
+    g.nslots[kQ] = g.nslots[kK] = g.N - pl->gm_r;
+    g.nsrc[kQ] = g.nsrc[kK] = pl->gm_ns;
+  }
   pl->k_o = (int64_t)std::floor(p.outlier_pct * (double)p.heads * (double)N / 100.0 + 1e-9);
   pl->q_cap = (int64_t)p.heads * g.nslots[kQ] + pl->k_o;
   pl->lk_pad = ceil_div(g.nslots[kK], 64) * 64;
@@ -330,11 +347,39 @@ httm_status build(const httm_params& p, httm_plan* pl) {
       Lw.ga_best = b.take(8 * sh * n);
       Lw.ga_snorm = b.take(4 * sh * n);
       Lw.ga_cnt = b.take(4 * sh * (size_t)pl->ga_bound);
-      Lw.ga_fill = b.take(4 * sh * (size_t)pl->ga_bound);
       Lw.ga_tmp = b.take(4 * sh * n);
+      Lw.sort_keys = b.take(4 * sh * n);
+      Lw.sort_vals = b.take(4 * sh * n);
+      Lw.sort_counts = b.take(4 * sort_count_words((int)sh, (int)n));
       const bool bf = p.dtype == HTTM_BF16;
       Lw.ga_dg = b.take(bf ? 2 * sh * (size_t)pl->ga_dpitch * kD : 0);
       Lw.ga_dinv = b.take(bf ? 4 * sh * (size_t)pl->ga_dpitch : 0);
+    }
+    if (p.partition == 2) {
+      const size_t ns = (size_t)pl->gm_ns, dp = (size_t)pl->gm_dpitch;
+      Lw.gm_metric = b.take(E * n * kD);
+      Lw.gm_tot = b.take(4 * 3);
+      Lw.gm_dlist = b.take(4 * dp);
+      Lw.gm_slist = b.take(4 * (ns + 1));
+      Lw.gm_dg = b.take(E == 2 ? 2 * dp * kD : 0);
+      Lw.gm_dinv = b.take(E == 2 ? 4 * dp : 0);
+      Lw.gm_best = b.take(8 * n);
+      Lw.gm_snorm = b.take(4 * n);
+      Lw.gm_match = b.take(4 * (ns + 1));
+      Lw.gm_score = b.take(4 * (ns + 1));
+      Lw.gm_sel = b.take(ns + 16);
+      Lw.gm_topk = b.take(4 * outlier_scratch_words((int64_t)ns));
+      Lw.gm_unsel = b.take(4 * (ns + 1));
+      Lw.gm_urank = b.take(4 * (ns + 1));
+      Lw.gm_sums = b.take(4 * scan_sum_words((int64_t)ns));
+      Lw.gm_keys = b.take(4 * n);
+      Lw.sort_keys = b.take(4 * n);
+      Lw.sort_vals = b.take(4 * n);
+      Lw.sort_counts = b.take(4 * sort_count_words(1, (int)n));
+      Lw.gm_members = b.take(4 * n);
+      Lw.gm_off = b.take(4 * ((size_t)g.nslots[kQ] + 1));
+      Lw.gm_dbg_match = b.take(4 * n);
+      Lw.gm_dbg_score = b.take(4 * n);
     }
     Lw.q_members = b.take(4 * h * n);
     Lw.q_off = b.take(4 * h * ((size_t)g.nslots[kQ] + 1));
@@ -637,8 +682,10 @@ httm_status enqueue_layer(const httm_plan* pl, void* ws, httm_index* index, cons
     gb.best = at<uint64_t>(ws, L.ga_best);
     gb.snorm = at<float>(ws, L.ga_snorm);
     gb.cnt = at<int32_t>(ws, L.ga_cnt);
-    gb.fill = at<int32_t>(ws, L.ga_fill);
     gb.tmp = at<int32_t>(ws, L.ga_tmp);
+    gb.sort_keys = at<int32_t>(ws, L.sort_keys);
+    gb.sort_vals = at<int32_t>(ws, L.sort_vals);
+    gb.sort_counts = at<uint32_t>(ws, L.sort_counts);
     gb.grp_q = cq.group;
     gb.grp_k = ck.group;
     gb.mem_q = cq.members;
@@ -662,6 +709,54 @@ httm_status enqueue_layer(const httm_plan* pl, void* ws, httm_index* index, cons
     CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
                                  ck.members, ck.off, at<void>(ws, L.kt), at<void>(ws, L.vt), at<float>(ws, L.kmax),
                                  kst, lenk));
+    stage_end(HTTM_T_MERGE_KV, kst);
+    if (side) CHECK_LAUNCH(hipEventRecord(side->join, kst));
+  } else if (pl->p.partition == 2) {
+    // one head-shared partition (global matching on the head-mean key) on
+    // the caller's stream, copied to every head's query and key CSR; then
+    // the K / V means on the library stream
+    GmShape gs{g.heads, g.N, g.T, g.nsp, g.HW, pl->gm_nd, pl->gm_ns, pl->gm_r, g.nslots[kQ], pl->gm_dpitch};
+    GmBuffers gb;
+    gb.metric = at<void>(ws, L.gm_metric);
+    gb.tot = at<int32_t>(ws, L.gm_tot);
+    gb.dst_list = at<int32_t>(ws, L.gm_dlist);
+    gb.src_list = at<int32_t>(ws, L.gm_slist);
+    gb.dg = at<uint16_t>(ws, L.gm_dg);
+    gb.dinv = at<float>(ws, L.gm_dinv);
+    gb.best = at<uint64_t>(ws, L.gm_best);
+    gb.snorm = at<float>(ws, L.gm_snorm);
+    gb.match = at<int32_t>(ws, L.gm_match);
+    gb.score = at<float>(ws, L.gm_score);
+    gb.sel = at<uint8_t>(ws, L.gm_sel);
+    gb.topk = at<uint32_t>(ws, L.gm_topk);
+    gb.unsel = at<int32_t>(ws, L.gm_unsel);
+    gb.urank = at<int32_t>(ws, L.gm_urank);
+    gb.scan_sums = at<int32_t>(ws, L.gm_sums);
+    gb.keys = at<int32_t>(ws, L.gm_keys);
+    gb.sort_keys = at<int32_t>(ws, L.sort_keys);
+    gb.sort_vals = at<int32_t>(ws, L.sort_vals);
+    gb.sort_counts = at<uint32_t>(ws, L.sort_counts);
+    gb.members = at<int32_t>(ws, L.gm_members);
+    gb.off = at<int32_t>(ws, L.gm_off);
+    gb.dbg_match = at<int32_t>(ws, L.gm_dbg_match);
+    gb.dbg_score = at<float>(ws, L.gm_dbg_score);
+    gb.q = cq;
+    gb.k = ck;
+    stage_begin(HTTM_T_SIM, st);
+    CHECK_LAUNCH(launch_global_partition(dt, gs, k, gb, st, 0));
+    stage_begin(HTTM_T_GA_MATCH, st);
+    CHECK_LAUNCH(launch_global_partition(dt, gs, k, gb, st, 1));
+    stage_end(HTTM_T_GA_MATCH, st);
+    CHECK_LAUNCH(launch_global_partition(dt, gs, k, gb, st, 2));
+    stage_end(HTTM_T_SIM, st);
+    if (side) {
+      CHECK_LAUNCH(hipEventRecord(side->fork, st));
+      CHECK_LAUNCH(hipStreamWaitEvent(kst, side->fork, 0));
+    }
+    stage_begin(HTTM_T_MERGE_KV, kst);
+    CHECK_LAUNCH(launch_merge_kv(dt, g.heads, g.N, g.nslots[kK], pl->lk_pad, pl->scale * kLog2e, k, v,
+                                 ck.members, ck.off, at<void>(ws, L.kt), at<void>(ws, L.vt), at<float>(ws, L.kmax),
+                                 kst));
     stage_end(HTTM_T_MERGE_KV, kst);
     if (side) CHECK_LAUNCH(hipEventRecord(side->join, kst));
   } else {
@@ -976,13 +1071,14 @@ httm_status httm_debug_size(const httm_plan* pl, int32_t item, size_t* bytes) {
   const size_t h = pl->g.heads, n = pl->g.N;
   const bool ga = pl->p.partition == 1;
   const size_t E = pl->esize;
+  const bool gm = pl->p.partition == 2;
   const bool ga_item = item == HTTM_DBG_GA_VAR || item == HTTM_DBG_GA_ROLE || item == HTTM_DBG_GA_MATCH ||
                        item == HTTM_DBG_GA_SCORE || item == HTTM_DBG_KV_LEN;
   const bool block_item = item == HTTM_DBG_Q_MATCH || item == HTTM_DBG_Q_SCORE || item == HTTM_DBG_KV_MATCH ||
                           item == HTTM_DBG_KV_SCORE;
-  if (ga ? block_item : ga_item)
-    return fail(HTTM_ERR_UNSUPPORTED, ga ? "block-local matches do not exist under the geometry-aware partition"
-                                         : "geometry-aware items exist only under that partition");
+  const bool gm_item = item == HTTM_DBG_GM_METRIC || item == HTTM_DBG_GM_MATCH || item == HTTM_DBG_GM_SCORE;
+  if ((ga_item && !ga) || (block_item && (ga || gm)) || (gm_item && !gm))
+    return fail(HTTM_ERR_UNSUPPORTED, "this debug item does not exist under the plan's partition");
   switch (item) {
     case HTTM_DBG_GA_VAR:
     case HTTM_DBG_GA_MATCH:
@@ -1004,6 +1100,9 @@ httm_status httm_debug_size(const httm_plan* pl, int32_t item, size_t* bytes) {
     case HTTM_DBG_KT:
     case HTTM_DBG_VT: *bytes = E * h * (size_t)pl->lk_pad * kD; break;
     case HTTM_DBG_QT: *bytes = E * (size_t)pl->q_cap * kD; break;
+    case HTTM_DBG_GM_METRIC: *bytes = E * n * kD; break;
+    case HTTM_DBG_GM_MATCH:
+    case HTTM_DBG_GM_SCORE: *bytes = 4 * n; break;
     default: return fail(HTTM_ERR_INVALID_ARG, "unknown debug item");
   }
   return HTTM_OK;
@@ -1043,6 +1142,9 @@ httm_status httm_debug_read(const httm_plan* pl, const void* ws, const httm_inde
     case HTTM_DBG_KT: src = base + L.kt.off; break;
     case HTTM_DBG_VT: src = base + L.vt.off; break;
     case HTTM_DBG_QT: src = base + L.qt.off; break;
+    case HTTM_DBG_GM_METRIC: src = base + L.gm_metric.off; break;
+    case HTTM_DBG_GM_MATCH: src = base + L.gm_dbg_match.off; break;
+    case HTTM_DBG_GM_SCORE: src = base + L.gm_dbg_score.off; break;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   CHECK_LAUNCH(hipMemcpyAsync(host, src, need, hipMemcpyDeviceToHost, st));

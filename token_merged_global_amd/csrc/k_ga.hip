@@ -21,10 +21,10 @@
 // source lists) -> ga_gather (destination rows and inverse norms, bf16) ->
 // ga_match (MFMA cosine argmax of sources against all destinations, split
 // over destinations, packed 64-bit atomic maxima) -> ga_decode (matches,
-// scores, member counts per slot) -> ga_offsets (slot offsets) -> ga_place
-// (every token into its slot's range, any order) -> ga_rank (each member's
-// place inside its range = members with a smaller id).  No sort and no
-// memset: the result does not depend on the order of the atomics.
+// scores, member counts per slot) -> ga_offsets (slot offsets) -> ga_keys
+// (slot of every token) -> a stable sort of the token ids by slot (members
+// ascend inside a slot; linear in N whatever the group sizes).  No memset:
+// the result does not depend on the order of the atomics.
 #include <algorithm>
 
 #include "common.h"
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(kRoleThreads) void ga_slots(const uint8_t* __restri
                                                           int32_t* __restrict__ dst_slot,
                                                           int32_t* __restrict__ src_list, int32_t* __restrict__ gdst,
                                                           float* __restrict__ gscore, int32_t* __restrict__ cnt,
-                                                          int32_t* __restrict__ fill, uint64_t* __restrict__ best) {
+                                                          uint64_t* __restrict__ best) {
   __shared__ int wsum[kRoleThreads / 64];
   const int f = blockIdx.x, sh = blockIdx.y;
   const size_t hb = (size_t)sh * N;
@@ -402,7 +402,6 @@ __global__ __launch_bounds__(kRoleThreads) void ga_slots(const uint8_t* __restri
       gdst[hb + tok] = -1;
       gscore[hb + tok] = 0.f;
       cnt[(size_t)sh * bound + ra] = 1;  // the anchor; ga_match adds the sources
-      fill[(size_t)sh * bound + ra] = 0;
       if (r == kRoleDst) {
         dst_list[hb + rd] = tok;
         dst_slot[hb + rd] = ra;
@@ -788,45 +787,55 @@ __global__ __launch_bounds__(kRoleThreads) void ga_offsets(const int32_t* __rest
   if (threadIdx.x == 0) o[bound] = N;
 }
 
-// Every token into its slot's member range (position from an atomic
-// counter: any order), and its slot in the token -> slot map.
-__global__ __launch_bounds__(256) void ga_place(const uint8_t* __restrict__ role, const int32_t* __restrict__ slot,
-                                                const int32_t* __restrict__ gslot, int heads, int N, int bound,
-                                                const int32_t* __restrict__ off_q, const int32_t* __restrict__ off_k,
-                                                int32_t* __restrict__ fill, int32_t* __restrict__ tmp,
-                                                int32_t* __restrict__ grp_q, int32_t* __restrict__ grp_k) {
+// The token -> slot maps, and the slot of every token as the sort key of its
+// (stream, head) segment: the member lists then come from a stable sort of
+// the token ids by slot (linear in N whatever the group sizes; members
+// ascend by token id inside a slot).
+__global__ __launch_bounds__(256) void ga_keys(const uint8_t* __restrict__ role, const int32_t* __restrict__ slot,
+                                               const int32_t* __restrict__ gslot, int heads, int N,
+                                               int32_t* __restrict__ keys, int32_t* __restrict__ grp_q,
+                                               int32_t* __restrict__ grp_k) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)2 * heads * N) return;
   const int sh = (int)(i / N), tok = (int)(i - (int64_t)sh * N);
   const int st = sh / heads, head = sh % heads;
   const int s = role[i] == kRoleSrc ? gslot[i] : slot[i];
-  const int32_t* o = (st == 0 ? off_q : off_k) + (size_t)head * (bound + 1);
-  const int pos = o[s] + atomicAdd(&fill[(size_t)sh * bound + s], 1);
-  if (pos < N) tmp[(size_t)sh * N + pos] = tok;  // always: the counts sum to N
+  keys[i] = s;
   (st == 0 ? grp_q : grp_k)[(size_t)head * N + tok] = s;
 }
 
-// Members in ascending token order: the member at position p of its slot's
-// range moves to range start + (members of the range with a smaller id).
-__global__ __launch_bounds__(256) void ga_rank(const int32_t* __restrict__ tmp, int heads, int N, int bound,
-                                               const int32_t* __restrict__ off_q, const int32_t* __restrict__ off_k,
-                                               const int32_t* __restrict__ grp_q, const int32_t* __restrict__ grp_k,
-                                               int32_t* __restrict__ mem_q, int32_t* __restrict__ mem_k) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)2 * heads * N) return;
-  const int sh = (int)(i / N);
-  const int st = sh / heads, head = sh % heads;
-  const int32_t* T = tmp + (size_t)sh * N;
-  const int tok = T[i - (int64_t)sh * N];
-  const int s = (st == 0 ? grp_q : grp_k)[(size_t)head * N + tok];
-  const int32_t* o = (st == 0 ? off_q : off_k) + (size_t)head * (bound + 1);
-  const int a = o[s], b = o[s + 1];
-  int rank = 0;
-  for (int q = a; q < b; ++q) rank += T[q] < tok;
-  if (a + rank < N) (st == 0 ? mem_q : mem_k)[(size_t)head * N + a + rank] = tok;
-}
-
 }  // namespace
+
+hipError_t launch_global_match(int dtype, int N, const void* x, const int32_t* tot, const int32_t* dst_list,
+                               const int32_t* src_list, int ns, uint16_t* dg, float* dinv, int dpitch, uint64_t* best,
+                               float* snorm, hipStream_t stream) {
+  if (ns <= 0) return hipSuccess;
+  if (dtype == 1)
+    hipLaunchKernelGGL(ga_gather, dim3((unsigned)(dpitch / 64), 1u), dim3(256), 0, stream, (const uint16_t*)x,
+                       (const uint16_t*)x, 1, N, dpitch, tot, dst_list, dg, dinv);
+  GaMatchArgs a;
+  a.x[0] = x;
+  a.x[1] = x;
+  a.heads = 1;
+  a.N = N;
+  a.chunks = ceil_div(ns, kSrcPerWg);
+  a.tot = tot;
+  a.dst_list = dst_list;
+  a.dst_slot = nullptr;
+  a.src_list = src_list;
+  a.best = best;
+  a.snorm = snorm;
+  a.dsplit = kDstSplits;
+  a.dg = dg;
+  a.dinv = dinv;
+  a.dpitch = dpitch;
+  const unsigned mgrid = (unsigned)(kDstSplits * a.chunks);
+  if (dtype == 1)
+    hipLaunchKernelGGL(ga_match_bf16, dim3(mgrid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(ga_match_f32, dim3(mgrid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_ga_partition(int dtype, const GaShape& s, const void* q, const void* k, const GaBuffers& b,
                                hipStream_t stream, int phase) {
@@ -845,7 +854,7 @@ hipError_t launch_ga_partition(int dtype, const GaShape& s, const void* q, const
                        b.lenk);
     hipLaunchKernelGGL(ga_slots, dim3((unsigned)s.F, (unsigned)SH), dim3(kRoleThreads), 0, stream, b.role, s.heads,
                        s.N, s.Tf, s.F, s.bound, b.foff, b.slot, b.dst_list, b.dst_slot, b.src_list, b.gdst, b.gscore,
-                       b.cnt, b.fill, b.best);
+                       b.cnt, b.best);
     return hipGetLastError();
   }
   if (s.max_src == 0 && phase < 3) return hipSuccess;  // a single frame: no sources, every token is its own group
@@ -888,11 +897,12 @@ hipError_t launch_ga_partition(int dtype, const GaShape& s, const void* q, const
   hipLaunchKernelGGL(ga_offsets, dim3((unsigned)SH), dim3(kRoleThreads), 0, stream, b.cnt, b.tot, s.heads, s.N,
                      s.bound, b.off_q, b.off_k);
   const unsigned grid = (unsigned)(((int64_t)SH * s.N + 255) / 256);
-  hipLaunchKernelGGL(ga_place, dim3(grid), dim3(256), 0, stream, b.role, b.slot, b.gslot, s.heads, s.N, s.bound,
-                     b.off_q, b.off_k, b.fill, b.tmp, b.grp_q, b.grp_k);
-  hipLaunchKernelGGL(ga_rank, dim3(grid), dim3(256), 0, stream, b.tmp, s.heads, s.N, s.bound, b.off_q, b.off_k,
-                     b.grp_q, b.grp_k, b.mem_q, b.mem_k);
-  return hipGetLastError();
+  hipLaunchKernelGGL(ga_keys, dim3(grid), dim3(256), 0, stream, b.role, b.slot, b.gslot, s.heads, s.N, b.tmp,
+                     b.grp_q, b.grp_k);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_sort_by_slot(b.tmp, SH, s.N, b.sort_keys, b.sort_vals, b.sort_counts, b.mem_q, b.mem_k, s.heads,
+                             stream);
 }
 
 }  // namespace httm

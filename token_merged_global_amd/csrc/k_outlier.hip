@@ -117,6 +117,11 @@ __device__ void find_bin(const uint32_t* hist, int nb, uint32_t k, uint32_t* wsu
   __syncthreads();
 }
 
+// Keys of 16 consecutive values: the bit patterns of non-negative values
+// (KEY false: deviations), or the order-preserving float_key of any finite
+// value (KEY true: cosine scores).  0xFFFFFFFF, which no finite value
+// yields, marks positions past the end.
+template <bool KEY>
 __device__ __forceinline__ void load_chunk(const float* d, int64_t total, int64_t base, uint32_t* u) {
   const int64_t i0 = base + (int64_t)threadIdx.x * kPerThread;
   if (i0 + kPerThread <= total) {
@@ -124,18 +129,19 @@ __device__ __forceinline__ void load_chunk(const float* d, int64_t total, int64_
     for (int q = 0; q < 4; ++q) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(d + i0 + 4 * q);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) u[4 * q + e] = v[e];
+      for (int e = 0; e < 4; ++e) u[4 * q + e] = KEY ? float_key(__uint_as_float(v[e]) + 0.0f) : v[e];
     }
   } else {
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e)
-      u[e] = (i0 + e < total) ? __float_as_uint(d[i0 + e]) : 0xFFFFFFFFu;  // sentinel: no bin
+      u[e] = (i0 + e < total) ? (KEY ? float_key(d[i0 + e] + 0.0f) : __float_as_uint(d[i0 + e]))
+                              : 0xFFFFFFFFu;  // sentinel: no bin
   }
 }
 
 // pass 0..2: histogram of bits [shift, shift+width) among values whose higher
 // bits equal the prefix found from the previous histograms.
-template <int PASS>
+template <int PASS, bool KEY>
 __global__ __launch_bounds__(kThreads) void radix_hist(const float* __restrict__ delta, int64_t total,
                                                        uint32_t k_o, uint32_t* scratch) {
   __shared__ uint32_t hist[kBins];
@@ -161,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void radix_hist(const float* __restrict__
   for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0;
   __syncthreads();
   uint32_t u[kPerThread];
-  load_chunk(delta, total, (int64_t)blockIdx.x * kChunk, u);
+  load_chunk<KEY>(delta, total, (int64_t)blockIdx.x * kChunk, u);
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     if (u[e] == 0xFFFFFFFFu) continue;
@@ -200,6 +206,7 @@ __device__ void threshold(const Scratch& s, uint32_t k_o, uint32_t* hist, uint32
 }
 
 // Marks values above T; counts values equal to T in this chunk.
+template <bool KEY>
 __global__ __launch_bounds__(kThreads) void radix_mark(const float* __restrict__ delta, int64_t total,
                                                        uint32_t k_o, uint32_t* scratch,
                                                        uint8_t* __restrict__ mask) {
@@ -220,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void radix_mark(const float* __restrict__
   __syncthreads();
   uint32_t u[kPerThread];
   const int64_t i0 = (int64_t)blockIdx.x * kChunk + (int64_t)threadIdx.x * kPerThread;
-  load_chunk(delta, total, (int64_t)blockIdx.x * kChunk, u);
+  load_chunk<KEY>(delta, total, (int64_t)blockIdx.x * kChunk, u);
   uint32_t eq = 0;
   uint8_t m[kPerThread];
 #pragma unroll
@@ -246,6 +253,7 @@ __global__ __launch_bounds__(kThreads) void radix_mark(const float* __restrict__
 }
 
 // Values equal to T, in flat-index order, take the remaining budget.
+template <bool KEY>
 __global__ __launch_bounds__(kThreads) void radix_ties(const float* __restrict__ delta, int64_t total,
                                                        uint32_t* scratch, uint8_t* __restrict__ mask) {
   __shared__ uint32_t part[kThreads / 64];
@@ -260,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void radix_ties(const float* __restrict__
   if (before >= need) return;
   uint32_t u[kPerThread];
   const int64_t i0 = (int64_t)blockIdx.x * kChunk + (int64_t)threadIdx.x * kPerThread;
-  load_chunk(delta, total, (int64_t)blockIdx.x * kChunk, u);
+  load_chunk<KEY>(delta, total, (int64_t)blockIdx.x * kChunk, u);
   uint32_t eq = 0;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) eq += (u[e] == T && u[e] != 0xFFFFFFFFu) ? 1u : 0u;
@@ -297,6 +305,34 @@ hipError_t launch_zero_init(float* kmax, int heads, int* fb_count, uint32_t* rad
 
 int outlier_hist0_words() { return kBins; }
 
+namespace {
+__global__ void zero_words(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+}  // namespace
+
+hipError_t launch_topk(const float* vals, int64_t total, int64_t k, uint8_t* mask, uint32_t* scratch,
+                       hipStream_t stream) {
+  const unsigned tgrid = (unsigned)((total + 255) / 256);
+  if (total <= 0) return hipSuccess;
+  if (k <= 0 || k >= total) {
+    hipLaunchKernelGGL(fill_bytes, dim3(tgrid), dim3(256), 0, stream, mask, total, (uint8_t)(k <= 0 ? 0 : 1));
+    return hipGetLastError();
+  }
+  const int64_t words = (int64_t)outlier_scratch_words(total);
+  hipLaunchKernelGGL(zero_words, dim3((unsigned)((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024)), dim3(256),
+                     0, stream, scratch, words);
+  const int nchunks = (int)((total + kChunk - 1) / kChunk);
+  const uint32_t kk = (uint32_t)k;
+  hipLaunchKernelGGL((radix_hist<0, true>), dim3(nchunks), dim3(kThreads), 0, stream, vals, total, kk, scratch);
+  hipLaunchKernelGGL((radix_hist<1, true>), dim3(nchunks), dim3(kThreads), 0, stream, vals, total, kk, scratch);
+  hipLaunchKernelGGL((radix_hist<2, true>), dim3(nchunks), dim3(kThreads), 0, stream, vals, total, kk, scratch);
+  hipLaunchKernelGGL(radix_mark<true>, dim3(nchunks), dim3(kThreads), 0, stream, vals, total, kk, scratch, mask);
+  hipLaunchKernelGGL(radix_ties<true>, dim3(nchunks), dim3(kThreads), 0, stream, vals, total, scratch, mask);
+  return hipGetLastError();
+}
+
 hipError_t launch_outliers(const float* delta, int64_t total, int64_t k_o, uint8_t* mask,
                            uint32_t* scratch, const int32_t* group, int N, int gq, int32_t* ocnt,
                            hipStream_t stream) {
@@ -308,10 +344,10 @@ hipError_t launch_outliers(const float* delta, int64_t total, int64_t k_o, uint8
     const int nchunks = (int)((total + kChunk - 1) / kChunk);
     const uint32_t k = (uint32_t)k_o;
     // pass 0 (bits 31..21) was accumulated by the deviation producer into the zeroed scratch
-    hipLaunchKernelGGL(radix_hist<1>, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch);
-    hipLaunchKernelGGL(radix_hist<2>, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch);
-    hipLaunchKernelGGL(radix_mark, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch, mask);
-    hipLaunchKernelGGL(radix_ties, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, scratch, mask);
+    hipLaunchKernelGGL((radix_hist<1, false>), dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch);
+    hipLaunchKernelGGL((radix_hist<2, false>), dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch);
+    hipLaunchKernelGGL(radix_mark<false>, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch, mask);
+    hipLaunchKernelGGL(radix_ties<false>, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, scratch, mask);
   }
   if (k_o > 0)
     hipLaunchKernelGGL(count_outliers, dim3(tgrid), dim3(256), 0, stream, total, N, gq, mask, group, ocnt);

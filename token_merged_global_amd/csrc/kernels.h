@@ -124,8 +124,10 @@ struct GaBuffers {
   uint64_t* best;      // [2][h][N] per source: packed best (key, destination index)
   float* snorm;        // [2][h][N] per source: norm term of its score
   int32_t* cnt;        // [2][h][bound] members per slot
-  int32_t* fill;       // [2][h][bound] placement counters
-  int32_t* tmp;        // [2][h][N] members in placement order
+  int32_t* tmp;        // [2][h][N] slot of every token (sort keys)
+  int32_t* sort_keys;  // [2][h][N] sort scratch
+  int32_t* sort_vals;  // [2][h][N] sort scratch
+  uint32_t* sort_counts;  // sort_count_words(2 h, N)
   int32_t* grp_q;      // [h][N] slot of every token (query stream)
   int32_t* grp_k;
   int32_t* mem_q;      // [h][N] members, grouped by slot, ascending inside a slot
@@ -139,6 +141,73 @@ struct GaBuffers {
 // (one launch), 3 groups (decode, offsets, placement, rank).
 hipError_t launch_ga_partition(int dtype, const GaShape& s, const void* q, const void* k, const GaBuffers& b,
                                hipStream_t stream, int phase);
+
+// Stable sort of token ids by slot, per segment of n tokens (keys [nseg][n],
+// slots < 2^20): out lists the tokens of segment g (g < split: out_a + g*n,
+// else out_b + (g - split)*n) by slot, equal slots in ascending token id.
+// Scratch: tmp_keys, tmp_vals [nseg][n]; counts sort_count_words(nseg, n).
+size_t sort_count_words(int nseg, int n);
+hipError_t launch_sort_by_slot(const int32_t* keys, int nseg, int n, int32_t* tmp_keys, int32_t* tmp_vals,
+                               uint32_t* counts, int32_t* out_a, int32_t* out_b, int split, hipStream_t stream);
+// out[i] = in[0] + ... + in[i-1] for i < n; *total (nullable) = the sum of all.
+// sums: scan_sum_words(n) words of scratch.
+size_t scan_sum_words(int64_t n);
+hipError_t launch_exclusive_scan(const int32_t* in, int64_t n, int32_t* out, int32_t* sums, int32_t* total,
+                                 hipStream_t stream);
+
+// Top-k of n floats: mask[i] = 1 for the k largest values (any finite sign),
+// ties to the smaller index.  scratch: outlier_scratch_words(n) words
+// (cleared by the launch itself).
+hipError_t launch_topk(const float* vals, int64_t n, int64_t k, uint8_t* mask, uint32_t* scratch,
+                       hipStream_t stream);
+// Cosine argmax of `ns` sources over all destinations of one matrix x
+// ([N][64], rows listed by src_list / dst_list, tot = {0, nd, ns}): the
+// geometry-aware partition's gather and match with one head and one stream.
+// best[src token] (zeroed by the caller) receives the packed maximum,
+// snorm[src token] the source norm term.
+hipError_t launch_global_match(int dtype, int N, const void* x, const int32_t* tot, const int32_t* dst_list,
+                               const int32_t* src_list, int ns, uint16_t* dg, float* dinv, int dpitch,
+                               uint64_t* best, float* snorm, hipStream_t stream);
+
+// Head-shared global matching (partition 2): one partition from the keys
+// averaged over heads, copied to the query and key CSR of every head.
+struct GmShape {
+  int heads, N, Tf, nsp, HW;
+  int nd, ns, r;  // destinations, sources, merged sources
+  int L;          // slots (N - r)
+  int dpitch;     // gathered destination rows (multiple of 64)
+};
+struct GmBuffers {
+  void* metric;        // [N][64] element type
+  int32_t* tot;        // [3]
+  int32_t* dst_list;   // [nd]
+  int32_t* src_list;   // [ns]
+  uint16_t* dg;        // bf16: [dpitch][64]
+  float* dinv;         // bf16: [dpitch]
+  uint64_t* best;      // [N]
+  float* snorm;        // [N]
+  int32_t* match;      // [ns] destination index per source
+  float* score;        // [ns]
+  uint8_t* sel;        // [ns] merged sources
+  uint32_t* topk;      // outlier_scratch_words(ns)
+  int32_t* unsel;      // [ns]
+  int32_t* urank;      // [ns]
+  int32_t* scan_sums;  // scan_sum_words(ns)
+  int32_t* keys;       // [N] slot of every token (also the token -> slot map)
+  int32_t* sort_keys;  // [N]
+  int32_t* sort_vals;  // [N]
+  uint32_t* sort_counts;  // sort_count_words(1, N)
+  int32_t* members;    // [N]
+  int32_t* off;        // [L + 1]
+  int32_t* dbg_match;  // [N] matched destination token of every source, -1 otherwise
+  float* dbg_score;    // [N] its cosine, 0 otherwise
+  Csr q, k;            // per-head CSR of both streams (written for every head)
+};
+// Three phases, enqueued in order: 0 metric and lists, 1 the match (one
+// launch on bf16 after the destination gather), 2 scores, top-r, slots,
+// sort, offsets and the per-head copies.
+hipError_t launch_global_partition(int dtype, const GmShape& s, const void* k, const GmBuffers& b,
+                                   hipStream_t stream, int phase);
 
 // Key splits for a layer of q_capacity packed rows; rows per work unit.
 int attention_split(int64_t q_capacity, int heads);
