@@ -86,6 +86,10 @@ def measured_traffic(workload: str, kernel: str, src: str):
 
 
 def describe(w) -> str:
+    if getattr(w, "partition", 0) == 2:
+        return (f"{w.name}: {w.frames} frames x ({w.grid_h}x{w.grid_w}+{w.n_special}) = {w.n_tokens} tokens, "
+                f"{w.heads} heads x {w.d_head}, {w.dtype}, one head-shared topology (head-mean keys, global "
+                f"matching, 25% destinations), merge {w.kv_ratio:g} + {w.outlier_pct:g}% outliers")
     if getattr(w, "partition", 0) == 1:
         return (f"{w.name}: {w.frames} frames x ({w.grid_h}x{w.grid_w}+{w.n_special}) = {w.n_tokens} tokens, "
                 f"{w.heads} heads x {w.d_head}, {w.dtype}, geometry-aware partition ({w.protect_pct:g}% "
@@ -113,7 +117,7 @@ def algorithmic(w, plan, lq: np.ndarray, lkh: np.ndarray):
     Gq, Lk, ko = info["q_groups"], info["kv_len"], info["n_outliers"]
     sum_lq = float(lq.sum())
     a = {}
-    if getattr(w, "partition", 0) != 1:
+    if getattr(w, "partition", 0) == 0:
         bl = plan.blocks()
         a["sim_q"] = ("flop", 2.0 * d * h * sum(b["q_src"] * b["q_dst"] for b in bl))
         a["sim_k"] = ("flop", 2.0 * d * h * sum(b["kv_src"] * b["kv_dst"] for b in bl))
@@ -318,6 +322,71 @@ def sweep_blocks(args, H, torch) -> None:
             del ws, out
 
 
+# --------------------------------------------------------------------------- matching cost
+def compare_matching(args, H, torch) -> None:
+    """Matching and aggregation cost of HTTM's block-local, head-wise matching
+    against head-shared global matching on the same inputs (one JSON line).
+
+    HTTM page, key design 2 and Table 3: global matching over the sequence
+    costs about 0.19 N^2 d_head and dominated FastVGGT's merge time (2.31 s
+    against HTTM's 0.12 s at 1000 frames; merge cost 4.58x lower overall).
+    Matching = similarity, argmax, top-r and groups of both streams of every
+    head (HTTM) or of the one shared topology (head-mean keys, every patch,
+    25 % destinations); aggregation = the K/V and query means.  Stage times
+    come from HIP events with every launch on one stream; the layer time is
+    the ordinary (forked) layer.
+    """
+    base = gen.WORKLOADS[args.workload].with_(layers=1)
+    if args.outlier_pct is not None:
+        base = base.with_(outlier_pct=args.outlier_pct)
+    x = gen.layer_inputs(base, seed=args.seed)
+    tdt = torch.bfloat16 if base.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x[t]).to(tdt).cuda() for t in "qkv")
+    del x
+    stream = torch.cuda.current_stream()
+    res = {"workload": describe(base), "tokens": base.n_tokens}
+    for name, w in (("httm_block_local", base), ("head_shared_global", base.with_(partition=2))):
+        plan = H.Plan.from_workload(w)
+        ws = H.workspace(plan)
+        out = torch.empty_like(q)
+        run = lambda: H.layer(plan, q, k, v, ws=ws, out=out, stream=stream)
+        reps = 5 if w.n_tokens > 200000 else 20
+        timed(torch, stream, run, reps)
+        layer_ms = timed(torch, stream, run, reps)
+        H.set_timing(None, serial=True)
+        for _ in range(reps):
+            run()
+        st, _ = H.get_timing()
+        H.set_timing([])
+        d = w.d_head
+        if w.partition == 2:
+            P = w.frames * w.grid_h * w.grid_w
+            nd = -(-P // 4)
+            flop = 2.0 * d * (P - nd) * nd
+            match_ms = st["sim"]
+            entry = {"matching_ms": match_ms, "match_kernel_ms": st["ga_match"], "matching_flop": flop,
+                     "match_kernel_tflops": flop / (st["ga_match"] * 1e-3) / 1e12 if st["ga_match"] > 0 else None}
+        else:
+            bl = plan.blocks()
+            flop = 2.0 * d * w.heads * sum(b["q_src"] * b["q_dst"] + b["kv_src"] * b["kv_dst"] for b in bl)
+            match_ms = st["sim"] + st["sim_k"] + st["select"] + st["select_k"]
+            entry = {"matching_ms": match_ms, "matching_flop": flop,
+                     "similarity_tflops": flop / ((st["sim"] + st["sim_k"]) * 1e-3) / 1e12}
+        entry.update({"aggregation_ms": st["merge_kv"] + st["merge_q"], "outlier_restore_ms": st["outlier"] + st["restore"],
+                      "attention_ms": st["attn"], "layer_ms": layer_ms, "q_len_mean": float(np.diff(
+                          H.debug_read(plan, ws, "cu_q")).mean()), "kv_len": plan.info["kv_len"]})
+        res[name] = entry
+        log(f"[bench] {name}: matching {entry['matching_ms']:.3f} ms, aggregation {entry['aggregation_ms']:.3f} ms, "
+            f"layer {layer_ms:.3f} ms")
+        del ws, out
+        torch.cuda.empty_cache()
+    a, b = res["head_shared_global"], res["httm_block_local"]
+    res["matching_cost_ratio"] = a["matching_ms"] / b["matching_ms"]
+    res["merge_cost_ratio"] = (a["matching_ms"] + a["aggregation_ms"]) / (b["matching_ms"] + b["aggregation_ms"])
+    res["matching_flop_ratio"] = a["matching_flop"] / b["matching_flop"]
+    print(json.dumps(res), flush=True)
+
+
 # --------------------------------------------------------------------------- timing helpers
 def timed(torch, stream, fn, reps):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -390,8 +459,11 @@ def main():
     ap.add_argument("--outlier-pct", type=float, default=None, help="override the workload's outlier budget")
     ap.add_argument("--cached-layers", type=int, default=None,
                     help="layers per step that reuse layer 0's merge indices (default: workload layers - 1)")
-    ap.add_argument("--partition", default="httm", choices=["httm", "ga"],
-                    help="httm: temporal blocks (default); ga: geometry-aware three-class partition")
+    ap.add_argument("--partition", default="httm", choices=["httm", "ga", "global"],
+                    help="httm: temporal blocks (default); ga: geometry-aware three-class partition; "
+                         "global: one head-shared topology from global matching")
+    ap.add_argument("--compare-matching", action="store_true",
+                    help="instead of the benchmark: matching / aggregation cost, block-local vs head-shared global")
     ap.add_argument("--protect-pct", type=float, default=10.0, help="ga: percent of each frame's patches protected")
     ap.add_argument("--sweep-blocks", action="store_true",
                     help="instead of the benchmark: block shape / stacking sweep (one JSON line per shape)")
@@ -407,6 +479,9 @@ def main():
     if args.sweep_blocks:
         sweep_blocks(args, H, torch)
         return
+    if args.compare_matching:
+        compare_matching(args, H, torch)
+        return
 
     w = gen.WORKLOADS[args.workload]
     over = {k: v for k, v in (("kv_ratio", args.kv_ratio), ("q_ratio", args.q_ratio),
@@ -414,8 +489,11 @@ def main():
     if over:
         w = w.with_(**over)
     ga = args.partition == "ga"
+    gm = args.partition == "global"
     if ga:
         w = w.with_(name=w.name + "_ga", partition=1, protect_pct=args.protect_pct)
+    if gm:
+        w = w.with_(name=w.name + "_global", partition=2)
     n_cached = (w.layers - 1) if args.cached_layers is None else args.cached_layers
     w = w.with_(layers=1 + n_cached)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -455,7 +533,7 @@ def main():
 
     # timed region: K steps; HIP events around every attention launch (and,
     # with the geometry-aware partition, around its global match kernel)
-    H.set_timing(["attn", "ga_match"] if ga else ["attn"])
+    H.set_timing(["attn", "ga_match"] if ga or gm else ["attn"])
     ms_step = timed(torch, stream, step, args.steps)
     attn_t, calls = H.get_timing()
     layers = 1 + n_cached
@@ -482,6 +560,11 @@ def main():
     lq, lkh = lengths(H, plan, ws, w, ga, idx)
     alg = algorithmic(w, plan, lq, lkh)
     ga_info = None
+    if gm:
+        P = w.frames * w.grid_h * w.grid_w
+        nd = -(-P // 4)
+        ga_info = {"match_flop": 2.0 * w.d_head * (P - nd) * nd, "sources": P - nd, "destinations": nd,
+                   "shared_partition": True}
     if ga:
         role = H.debug_read(plan, ws, "ga_role").reshape(2, w.heads, -1)
         ns = (role == 0).sum(axis=2).astype(np.float64)
@@ -497,13 +580,15 @@ def main():
                                 f"{int(lkh.max())}, sum_h L_q,h = {int(lq.sum())}); the same per launch in "
                                 f"layer 0 and the cached layers")
     roofline, other_roofline = attn_roof, None
-    if ga and attn_t["ga_match"] > 0:
+    if (ga or gm) and attn_t["ga_match"] > 0:
         match_ms = attn_t["ga_match"]
         match_roof = roofline_entry("ga_match_bf16" if w.dtype == "bf16" else "ga_match_f32",
                                     ("flop", ga_info["match_flop"]), match_ms, w.dtype, calls)
         match_roof["traffic"] = measured_traffic(w.name, match_roof["kernel"], GA_SRC)
         match_roof["traffic_unit"] = TRAFFIC_UNIT
-        match_roof["algorithmic"] = f"2*d*sum_(stream,h)(|S|*|D|) = {ga_info['match_flop']:.4g} FLOP per launch"
+        match_roof["algorithmic"] = (f"2*d*|S|*|D| (one head-shared topology) = {ga_info['match_flop']:.4g} FLOP per launch"
+                                     if gm else
+                                     f"2*d*sum_(stream,h)(|S|*|D|) = {ga_info['match_flop']:.4g} FLOP per launch")
         log(f"[bench] global match {match_ms:.4f} ms, attention {attn_t['attn']:.4f} ms")
         # the dominant kernel (the longer launch) carries the roofline; the other rides along
         if match_ms > attn_t["attn"]:
@@ -555,7 +640,7 @@ def main():
     torch.cuda.empty_cache()
 
     extra = None
-    if not args.no_extra and args.workload != "vggt30" and not ga:
+    if not args.no_extra and args.workload != "vggt30" and not (ga or gm):
         log("[bench] extra: the 30-frame layer")
         extra = single_layer_summary(H, torch, gen.WORKLOADS["vggt30"], args.seed)
         log(f"[bench]   vggt30 {extra['ms_per_layer']:.4f} ms/layer, {extra['tokens_per_s']:.4g} tokens/s")
@@ -583,7 +668,8 @@ def main():
         "config": {"workload": describe(w), "frames": w.frames, "tokens": w.n_tokens, "heads": w.heads,
                    "d_head": w.d_head, "n_s": w.n_s, "n_t": w.n_t, "q_ratio": w.q_ratio, "kv_ratio": w.kv_ratio,
                    "outlier_pct": w.outlier_pct, "layers_per_step": layers, "seed": args.seed,
-                   **({"partition": "geometry-aware", "protect_pct": w.protect_pct} if ga else {})},
+                   **({"partition": "geometry-aware", "protect_pct": w.protect_pct} if ga else {}),
+                   **({"partition": "head-shared global"} if gm else {})},
         "roofline": roofline,
         **({"roofline_other_kernel": other_roofline} if other_roofline else {}),
         "rooflines": rooflines,
@@ -594,7 +680,7 @@ def main():
         "stack": per_layer,
         "stages_ms": stages,
         "cached_stages_ms": cstages,
-        "geometry_aware": ga_info,
+        "geometry_aware" if not gm else "head_shared": ga_info,
         "speedup_vs_unmerged_attention": (dense_ms / layer_ms) if dense_ms else None,
         "unmerged_attention_ms": dense_ms,
         "lengths": {"kv_len": int(lkh.max()), "q_len_mean": float(lq.mean()), "q_len_min": int(lq.min()),

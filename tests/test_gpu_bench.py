@@ -24,7 +24,7 @@ def _bench(*args):
     return json.loads(lines[0])
 
 
-@pytest.mark.parametrize("partition", ["httm", "ga"])
+@pytest.mark.parametrize("partition", ["httm", "ga", "global"])
 def test_bench_json_contract(partition):
     d = _bench("--partition", partition)
     for key in ["metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
@@ -41,6 +41,9 @@ def test_bench_json_contract(partition):
     assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s"
     assert rf["avg_launch_ms"] > 0 and rf["launches_timed"] == 3
     assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"], rel=1e-9)
+    if partition == "global":
+        assert d["config"]["partition"] == "head-shared global"
+        assert d["head_shared"]["match_flop"] > 0
     if partition == "ga":
         assert d["config"]["partition"] == "geometry-aware"
         assert d["geometry_aware"]["match_flop"] > 0
@@ -67,3 +70,15 @@ def test_bench_cached_stack_contract():
     assert st["cached_layers"] == 2 and st["layer0_ms"] > 0 and st["cached_ms_per_layer"] > 0
     assert "merge_q_cached" in d["rooflines"]
     assert d["speedup_vs_unmerged_attention"] > 0
+
+
+def test_bench_compare_matching():
+    """--compare-matching: matching and aggregation of the block-local layer
+    against the head-shared global layer on the same inputs."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny", "--compare-matching"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    for key in ("httm_block_local", "head_shared_global"):
+        assert d[key]["matching_ms"] > 0 and d[key]["aggregation_ms"] > 0 and d[key]["layer_ms"] > 0
+    assert d["matching_cost_ratio"] > 0 and d["matching_flop_ratio"] > 0
