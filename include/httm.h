@@ -219,6 +219,10 @@ httm_status httm_layer_cached(const httm_plan* plan, void* ws, size_t ws_bytes,
  * httm_index_size() bytes (HTTM_ERR_WORKSPACE otherwise). */
 httm_status httm_index_export(const httm_plan* plan, const httm_index* index, void* host, size_t bytes,
                               void* stream);
+/* The 64-byte header an index of this plan starts with, written to `host`
+ * (at least 64 bytes; host only, no device calls): for callers that
+ * assemble an index in host memory before httm_index_import. */
+httm_status httm_index_header(const httm_plan* plan, void* host, size_t bytes);
 httm_status httm_index_import(const httm_plan* plan, const void* host, size_t bytes, httm_index* index,
                               void* stream);
 
@@ -321,6 +325,13 @@ typedef enum {
 #define HTTM_TIMING_SERIAL (1 << 30)
 httm_status httm_set_timing(int32_t stage_mask);
 httm_status httm_get_timing(float* ms, int32_t n, int32_t* calls);
+
+/* Test hook of the error path: the n-th launch that the library checks
+ * after this call (counting over all following calls; 0 turns it off)
+ * reports HTTM_ERR_DEVICE ("forced launch failure") instead of being
+ * enqueued, once.  The launches before it are enqueued as usual, so a
+ * layer can fail part way; later calls run normally.  Not thread-safe. */
+httm_status httm_debug_fail_launch(int32_t n);
 
 const char* httm_status_string(httm_status s);
 /* Last error detail recorded on this thread (empty if none). */

@@ -273,3 +273,102 @@ def test_ga_validation_codes():
     # N = 1000 * 1374 >= 2^20 tokens
     assert _status(partition=1, frames=1000, grid_h=37, grid_w=37, n_special=5, n_s=128, n_t=30) == 2
     assert _status(partition=1, frames=500, grid_h=37, grid_w=37, n_special=5, n_s=128, n_t=30) == 0
+
+
+def _no_gpu():
+    import torch
+    return not torch.cuda.is_available()
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="checks the error path of a host without a GPU")
+def test_device_error_without_a_gpu():
+    """Valid arguments on a host with no GPU: every entry point that needs the
+    device returns HTTM_ERR_DEVICE with a message (never a crash), and the
+    test hook's forced failure is reported as such."""
+    w = gen.WORKLOADS["tiny"]
+    plan = H.Plan.from_workload(w)
+    L = H.lib()
+    fake = [0x10000 * (i + 1) for i in range(5)]  # aligned, never dereferenced on the host
+    st = L.httm_layer(plan.handle, fake[0], plan.workspace_bytes, fake[1], fake[2], fake[3], fake[4], None, None)
+    assert st == 5 and L.httm_last_error().decode()
+    assert L.httm_layer_noalloc(plan.handle, fake[1], fake[2], fake[3], fake[4], None) == 5
+    assert L.httm_attention_dense(plan.handle, fake[0], plan.dense_workspace_bytes, fake[1], fake[2], fake[3], fake[4],
+                                  None) == 5
+    H.debug_fail_launch(1)
+    st = L.httm_attention_dense(plan.handle, fake[0], plan.dense_workspace_bytes, fake[1], fake[2], fake[3], fake[4],
+                                None)
+    assert st == 5 and "forced launch failure" in L.httm_last_error().decode()
+    H.debug_fail_launch(0)
+
+
+def test_index_import_refuses_bad_payloads():
+    """An index assembled on the host: the size and the header are checked,
+    then the payload (offsets rising from 0 to N, member ids below N, packed
+    rows inside their head, lengths within the packed capacity) before any
+    device copy; garbage behind a valid header is refused."""
+    for name, kw in [("tiny", {}), ("tiny", {"partition": 1}), ("tiny", {"partition": 2}),
+                     ("vggt30", {"heads": 2, "frames": 3})]:
+        w = gen.WORKLOADS[name].with_(**kw)
+        plan = H.Plan.from_workload(w)
+        hdr = H.index_header(plan)
+        assert hdr[:4].view(np.uint32)[0] == 0x58495448  # "HTIX"
+        n = plan.index_bytes
+        rng = np.random.default_rng(3)
+        payloads = {"zeros": np.zeros(n, np.uint8),
+                    "random": rng.integers(0, 256, n).astype(np.uint8),
+                    "plausible": (np.arange(n // 4) % w.n_tokens).astype(np.int32).view(np.uint8)}
+        L = H.lib()
+        idx = H.Index(0, 0x10000, n, 0)  # never written: refused before any copy
+        for what, buf in payloads.items():
+            b = buf.copy()
+            b[:64] = hdr
+            st = L.httm_index_import(plan.handle, b.ctypes.data, n, ctypes.byref(idx), None)
+            assert st == 4 and "out of range" in L.httm_last_error().decode(), (name, kw, what)
+            assert idx.valid == 0
+        b = payloads["zeros"].copy()
+        assert L.httm_index_import(plan.handle, b.ctypes.data, n, ctypes.byref(idx), None) == 4  # no header
+        b[:64] = hdr
+        assert L.httm_index_import(plan.handle, b.ctypes.data, n - 4, ctypes.byref(idx), None) == 4  # size
+
+
+ASAN_SKIP = "sanitized run in progress"
+
+
+@pytest.mark.skipif(os.environ.get("HTTM_SANITIZED_RUN") == "1", reason=ASAN_SKIP)
+def test_abi_host_code_under_asan_and_ubsan(tmp_path):
+    """The host code (validation, plans, layouts, index checks, the error
+    paths) built with AddressSanitizer and UndefinedBehaviorSanitizer, with
+    the same kernel objects, and this module's tests run against it."""
+    import shutil
+    import subprocess
+    import sys
+    from token_merged_global_amd import build as B
+
+    hipcc = B.hipcc()
+    rt = sorted(__import__("glob").glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not rt:
+        pytest.skip("no AddressSanitizer runtime in this toolchain")
+    kernels = [os.path.join(B.BUILD_DIR, f) for f in sorted(os.listdir(B.BUILD_DIR))
+               if f.endswith(".hip.o")] if os.path.isdir(B.BUILD_DIR) else []
+    if len(kernels) < 8:
+        B.build()
+        kernels = [os.path.join(B.BUILD_DIR, f) for f in sorted(os.listdir(B.BUILD_DIR)) if f.endswith(".hip.o")]
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+    obj = str(tmp_path / "httm_asan.o")
+    so = str(tmp_path / "libhttm.so")
+    subprocess.run([hipcc, "-x", "hip", "-O1", "-g", "-std=c++17", "-fPIC", f"--offload-arch={B.ARCH}",
+                    "-I", os.path.join(ROOT, "include"), "-I", B.CSRC, *B.DEVICE_FLAGS, *san, "-c",
+                    os.path.join(B.CSRC, "httm.cpp"), "-o", obj], check=True, capture_output=True, text=True)
+    subprocess.run([hipcc, f"--offload-arch={B.ARCH}", "-shared", "-fPIC", "-shared-libsan", *san, "-o", so, obj,
+                    *kernels], check=True, capture_output=True, text=True)
+    env = dict(os.environ)
+    env["LD_PRELOAD"] = rt[-1] + (":" + env["LD_PRELOAD"] if env.get("LD_PRELOAD") else "")
+    env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1"
+    env["UBSAN_OPTIONS"] = "halt_on_error=1:print_stacktrace=1"
+    env["HTTM_SANITIZED_RUN"] = "1"
+    code = ("import sys, pytest; sys.path.insert(0, %r); import token_merged_global_amd as H; H.LIB_PATH = %r; "
+            "sys.exit(pytest.main(['-q', '-x', '-p', 'no:cacheprovider', %r]))") % (ROOT, so, os.path.abspath(__file__))
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=600, cwd=ROOT)
+    assert r.returncode == 0, (r.stdout[-3000:], r.stderr[-3000:])
+    assert "passed" in r.stdout

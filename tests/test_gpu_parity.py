@@ -468,3 +468,63 @@ def test_serial_timing_mode_is_bit_identical():
     assert calls == 2 and stages["sim_k"] > 0 and stages["merge_kv"] > 0
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
+
+
+def test_forced_launch_failure_then_normal_calls():
+    """The error path part way through a layer (test hook): the n-th launch
+    reports HTTM_ERR_DEVICE, the call returns that status, and the following
+    calls on the same buffers run normally, bit-identical to before."""
+    w = small_bf16(frames=4, heads=2)
+    x = gen.layer_inputs(w)
+    plan = H.Plan.from_workload(w)
+    q, k, v = (to_dev(x[t], w.dtype) for t in "qkv")
+    ws = H.workspace(plan)
+    ref = H.layer(plan, q, k, v, ws=ws).clone()
+    try:
+        for n in (1, 3, 7):
+            H.debug_fail_launch(n)
+            with pytest.raises(H.HttmError) as e:
+                H.layer(plan, q, k, v, ws=ws)
+            assert e.value.status == 5 and "forced launch failure" in str(e.value)
+            torch.cuda.synchronize()
+            out = H.layer(plan, q, k, v, ws=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    finally:
+        H.debug_fail_launch(0)
+
+
+def _guarded(nbytes, guard=4096, fill=0xA5):
+    buf = torch.full((nbytes + 2 * guard,), fill, dtype=torch.uint8, device="cuda")
+    return buf, buf[guard:guard + nbytes]
+
+
+@pytest.mark.parametrize("partition", [0, 1, 2])
+def test_workspace_index_and_output_canaries(partition):
+    """Guard bytes before and after the workspace, the index buffer and the
+    output stay untouched by a layer, a cached layer and the unmerged
+    attention (every kernel writes inside the buffers it is given); the
+    inputs are unchanged."""
+    w = small_bf16(frames=6, heads=3, partition=partition)
+    x = gen.layer_inputs(w)
+    plan = H.Plan.from_workload(w)
+    q, k, v = (to_dev(x[t], w.dtype) for t in "qkv")
+    copies = [t.clone() for t in (q, k, v)]
+    G = 4096
+    wsb, ws = _guarded(plan.workspace_bytes, G)
+    ixb, ix = _guarded(plan.index_bytes, G)
+    n_out = q.numel() * 2
+    outb, outs = _guarded(n_out, G)
+    out = outs.view(torch.bfloat16).view(q.shape)
+    idx = H.CachedIndex.__new__(H.CachedIndex)
+    idx.buf = ix
+    idx.c = H.Index(0, ix.data_ptr(), ix.numel(), 0)
+    H.layer(plan, q, k, v, ws=ws, out=out, index=idx)
+    H.layer_cached(plan, idx, q, k, v, ws=ws, out=out)
+    dwb, dws = _guarded(plan.dense_workspace_bytes, G)
+    H.attention_dense(plan, q, k, v, ws=dws, out=out)
+    torch.cuda.synchronize()
+    for name, b in (("workspace", wsb), ("index", ixb), ("output", outb), ("dense workspace", dwb)):
+        assert bool((b[:G] == 0xA5).all()) and bool((b[-G:] == 0xA5).all()), name
+    for a, c in zip((q, k, v), copies):
+        assert torch.equal(a.view(torch.int16), c.view(torch.int16))

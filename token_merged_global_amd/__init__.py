@@ -102,6 +102,8 @@ EXPORTS = {
     "httm_noalloc_capacity": ([ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "httm_layer_noalloc": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                             ctypes.c_void_p], ctypes.c_int),
+    "httm_index_header": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t], ctypes.c_int),
+    "httm_debug_fail_launch": ([ctypes.c_int32], ctypes.c_int),
     "httm_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "httm_last_error": ([], ctypes.c_char_p),
 }
@@ -290,6 +292,19 @@ def layer_noalloc(plan: Plan, q, k, v, out, stream=None):
     _check(lib().httm_layer_noalloc(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                     _stream_ptr(stream)))
     return out
+
+
+def index_header(plan: Plan):
+    """The 64-byte header (numpy uint8) that an index of ``plan`` starts with."""
+    import numpy as np
+    buf = np.zeros(64, dtype=np.uint8)
+    _check(lib().httm_index_header(plan.handle, buf.ctypes.data, buf.nbytes))
+    return buf
+
+
+def debug_fail_launch(n: int) -> None:
+    """Test hook: the n-th checked launch from now on reports a device error (0: off)."""
+    _check(lib().httm_debug_fail_launch(int(n)))
 
 
 def index_export(plan: Plan, index: CachedIndex, stream=None):

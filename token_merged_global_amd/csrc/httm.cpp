@@ -487,8 +487,19 @@ void timing_end_call() {
 // caller's stream, so that each stage's events bracket kernels running alone.
 bool timing_serial() { return g_timing.serial; }
 
+// Test hook (httm_debug_fail_launch): the n-th checked launch after it is
+// set reports a failure instead of running, once.
+std::atomic<int32_t> g_fail_at{0}, g_fail_tick{0};
+bool forced_failure() {
+  if (g_fail_at.load(std::memory_order_relaxed) <= 0) return false;
+  if (g_fail_tick.fetch_add(1) + 1 != g_fail_at.load()) return false;
+  g_fail_at.store(0);
+  return true;
+}
+
 #define CHECK_LAUNCH(expr)                                                        \
   do {                                                                            \
+    if (forced_failure()) return fail(HTTM_ERR_DEVICE, std::string("forced launch failure before ") + #expr); \
     hipError_t e_ = (expr);                                                       \
     if (e_ != hipSuccess) return fail(HTTM_ERR_DEVICE, std::string(#expr) + ": " + hipGetErrorString(e_)); \
   } while (0)
@@ -654,8 +665,7 @@ httm_status enqueue_layer(const httm_plan* pl, void* ws, httm_index* index, cons
   const int64_t hn = (int64_t)g.heads * g.N;
   // atomic targets of this layer: key norms, exact-path count, outlier scratch, outlier counts
   CHECK_LAUNCH(launch_zero_init(at<float>(ws, L.kmax), g.heads, at<int>(ws, L.fb), at<uint32_t>(ws, L.radix),
-                                (int)outlier_scratch_words(hn), at<int32_t>(ws, L.ocnt),
-                                (int64_t)g.heads * g.nslots[kQ], st, &pl->index_header,
+                                (int)outlier_scratch_words(hn), nullptr, 0, st, &pl->index_header,
                                 reinterpret_cast<uint32_t*>(idx + I.header.off)));
 
   if (pl->p.partition == 1) {
@@ -798,15 +808,14 @@ httm_status enqueue_layer(const httm_plan* pl, void* ws, httm_index* index, cons
 
   stage_begin(HTTM_T_OUTLIER, st);
   CHECK_LAUNCH(launch_outliers(at<float>(ws, L.delta), hn, pl->k_o, at<uint8_t>(ws, L.mask),
-                               at<uint32_t>(ws, L.radix), cq.group, g.N, g.nslots[kQ], at<int32_t>(ws, L.ocnt),
-                               st));
+                               at<uint32_t>(ws, L.radix), st));
   stage_end(HTTM_T_OUTLIER, st);
 
   RestoreOut ro;
   ro.qt = at<void>(ws, L.qt);
   ro.lenq = reinterpret_cast<int32_t*>(idx + I.lenq.off);
   ro.cu_q = reinterpret_cast<int32_t*>(idx + I.cu_q.off);
-  ro.base = at<int32_t>(ws, L.base);
+  ro.tbase = at<int32_t>(ws, L.base);
   ro.ocnt = at<int32_t>(ws, L.ocnt);
   ro.fmembers = reinterpret_cast<int32_t*>(idx + I.fmembers.off);
   ro.foff = reinterpret_cast<int32_t*>(idx + I.foff.off);
@@ -894,6 +903,21 @@ httm_status httm_workspace_size(const httm_plan* pl, size_t* bytes) {
 httm_status httm_index_size(const httm_plan* pl, size_t* bytes) {
   if (!pl || !bytes) return fail(HTTM_ERR_INVALID_ARG, "NULL argument");
   *bytes = pl->I.total;
+  return HTTM_OK;
+}
+
+httm_status httm_index_header(const httm_plan* pl, void* host, size_t bytes) {
+  if (!pl || !host) return fail(HTTM_ERR_INVALID_ARG, "NULL argument");
+  if (bytes < sizeof(IndexHeader)) return fail(HTTM_ERR_INVALID_ARG, "host buffer smaller than the index header");
+  std::memcpy(host, &pl->index_header, sizeof(IndexHeader));
+  return HTTM_OK;
+}
+
+httm_status httm_debug_fail_launch(int32_t n) {
+  if (n < 0) return fail(HTTM_ERR_INVALID_ARG, "n must be >= 0");
+  g_fail_at.store(0);
+  g_fail_tick.store(0);
+  g_fail_at.store(n);
   return HTTM_OK;
 }
 

@@ -478,64 +478,6 @@ __device__ __forceinline__ void ga_lds_copy16(const void* g, u32x4* lds_wave_bas
 }
 __device__ __forceinline__ void ga_wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Keys of destination block dt (16 rows of the tile) for the 4 source
-// columns, folded into tm: key = score bits with the low 4 bits replaced by
-// 15 - (position of the candidate among the lane's 16), so one unsigned max
-// keeps the larger score and, on equal bits, the smaller destination.
-template <bool MASK>
-__device__ __forceinline__ void ga_keys16(const f32x4 (&acc)[4], const f32x4 inv4, const float (&off)[4], int dt,
-                                          int lg, int nvalid, uint32_t (&tm)[4]) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    uint32_t key[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float v = fmaf(acc[c][r], inv4[r], off[c]);
-      key[r] = (__float_as_uint(v) & ~15u) | (uint32_t)(15 - (4 * dt + r));
-      if (MASK && dt * 16 + 4 * lg + r >= nvalid) key[r] = 0u;
-    }
-    if (dt == 0) {
-      tm[c] = umax3(key[0], key[1], key[2] > key[3] ? key[2] : key[3]);
-    } else {
-      tm[c] = umax3(tm[c], key[0], key[1]);
-      tm[c] = umax3(tm[c], key[2], key[3]);
-    }
-  }
-}
-
-// One 64-destination tile: the 8 MFMAs of block dt + 1 are issued between
-// the key updates of block dt, so matrix and vector work overlap in a wave.
-template <bool MASK>
-__device__ __forceinline__ void ga_tile(const u32x4* sDb, const float* sInvb, const bf16x8 (&bs)[4][2],
-                                        const float (&off)[4], int lg, int l16, int nvalid, uint32_t (&tm)[4]) {
-  f32x4 acc[2][4];
-  auto mfma_block = [&](int dt, f32x4 (&o)[4]) {
-    const int arow = dt * 16 + l16;
-    const bf16x8 a0 = __builtin_bit_cast(bf16x8, sDb[arow * 8 + ((0 + lg) ^ swz(arow))]);
-    const bf16x8 a1 = __builtin_bit_cast(bf16x8, sDb[arow * 8 + ((4 + lg) ^ swz(arow))]);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bs[c][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bs[c][1], o[c], 0, 0, 0);
-    }
-  };
-  mfma_block(0, acc[0]);
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    if (dt + 1 < 4) mfma_block(dt + 1, acc[(dt + 1) & 1]);
-    const f32x4 inv4 = *reinterpret_cast<const f32x4*>(&sInvb[dt * 16 + 4 * lg]);
-    ga_keys16<MASK>(acc[dt & 1], inv4, off, dt, lg, nvalid, tm);
-    if (dt + 1 < 4) {
-      // 8 MFMAs spread over the 40 key instructions
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-      }
-    }
-  }
-}
-
 __global__ __launch_bounds__(256) void ga_match_bf16(GaMatchArgs a) {
   // two tile buffers as separate LDS objects: reads of one need not wait
   // for the direct-to-LDS copies into the other
@@ -616,7 +558,7 @@ __global__ __launch_bounds__(256) void ga_match_bf16(GaMatchArgs a) {
     __syncthreads();
     if (t + 1 < t1) load_tile(t + 1, sDn, sIn);
     uint32_t tm[4];
-    ga_tile<false>(sDc, sIc, bs, off, lg, l16, kDstTile, tm);
+    tile_argmax<false>(sDc, sIc, bs, off, lg, l16, kDstTile, tm);
     update(tm, t);
   };
   int t = t0;
@@ -634,9 +576,9 @@ __global__ __launch_bounds__(256) void ga_match_bf16(GaMatchArgs a) {
     __syncthreads();
     uint32_t tm[4];
     if ((t - t0) & 1)
-      ga_tile<true>(sD1, sI1, bs, off, lg, l16, nd - t * kDstTile, tm);
+      tile_argmax<true>(sD1, sI1, bs, off, lg, l16, nd - t * kDstTile, tm);
     else
-      ga_tile<true>(sD0, sI0, bs, off, lg, l16, nd - t * kDstTile, tm);
+      tile_argmax<true>(sD0, sI0, bs, off, lg, l16, nd - t * kDstTile, tm);
     update(tm, t);
   }
 #pragma unroll

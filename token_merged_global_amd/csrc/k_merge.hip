@@ -295,94 +295,90 @@ __global__ __launch_bounds__(8 * G) void merge_q(int N, int gq, const T* __restr
     if (sHist[i]) atomicAdd(&hist0[i], sHist[i]);
 }
 
-// Exclusive scan of one value per thread over a 1024-thread block.
-__device__ int block_exclusive_scan(int v, int* sh /* >= 16 */, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
+// Restore, part 1: 8 lanes per initial query group, 32 groups per
+// workgroup (the tiles of restore_rows).  A group with c members of which
+// o are outliers yields (c > o) + o final slots; o counts the mask over the
+// group's contiguous member list (no atomics).  Writes o per group and the
+// slot total of each tile.
+constexpr int kTileGroups = 32;
+__global__ __launch_bounds__(256) void restore_count(int N, int gq, const int32_t* __restrict__ members,
+                                                     const int32_t* __restrict__ off,
+                                                     const uint8_t* __restrict__ mask,
+                                                     int32_t* __restrict__ ocnt, int32_t* __restrict__ tsum) {
+  __shared__ int sV[kTileGroups];
+  const int tiles = ceil_div(gq, kTileGroups);
+  const int head = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+  const int ls = threadIdx.x >> 3, part = threadIdx.x & 7;
+  const int g = tile * kTileGroups + ls;
+  int v = 0;
+  if (g < gq) {
+    const int32_t* mem = members + (size_t)head * N;
+    const uint8_t* mk = mask + (size_t)head * N;
+    const int32_t* of = off + (size_t)head * (gq + 1);
+    const int m0 = of[g], m1 = of[g + 1];
+    int o = 0;
+    for (int m = m0 + part; m < m1; m += 8) o += mk[mem[m]] ? 1 : 0;
+    o += __shfl_xor(o, 1);
+    o += __shfl_xor(o, 2);
+    o += __shfl_xor(o, 4);
+    if (part == 0) ocnt[(size_t)head * gq + g] = o;
+    v = (m1 - m0 > o ? 1 : 0) + o;
   }
-  if (lane == 63) sh[wave] = x;
+  if (part == 0) sV[ls] = v;
   __syncthreads();
   if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
-      const int t = sh[w];
-      sh[w] = acc;
-      acc += t;
-    }
-    sh[16] = acc;
+    int t = 0;
+    for (int i = 0; i < kTileGroups; ++i) t += sV[i];
+    tsum[(size_t)head * tiles + tile] = t;
   }
+}
+
+// Restore, part 2 (one workgroup per head): exclusive scan of the tile
+// totals into tile bases; the head's final length goes to lenq and closes
+// the final offsets with N.
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void restore_scan(int N, int tiles, int32_t* __restrict__ tsum,
+                                                             int32_t* __restrict__ lenq,
+                                                             int32_t* __restrict__ foff) {
+  __shared__ int wsum[kScanThreads / 64];
+  const int head = blockIdx.x;
+  int32_t* T = tsum + (size_t)head * tiles;
+  const int per = ceil_div(tiles, kScanThreads);
+  const int b0 = threadIdx.x * per, b1 = min(tiles, b0 + per);
+  int local = 0;
+  for (int i = b0; i < b1; ++i) local += T[i];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(inc, d);
+    if (lane >= d) inc += y;
+  }
+  if (lane == 63) wsum[wave] = inc;
   __syncthreads();
-  total = sh[16];
-  return sh[wave] + x - v;
-}
-
-// Restore, part 1 (one workgroup per head): each initial query group g with
-// c members of which o are outliers yields (c > o) + o final slots; an
-// exclusive scan gives every group its first final slot; the head's final
-// length goes to lenq and closes the final offsets with N.  Groups go through
-// LDS in chunks of 4096 so that global reads and writes are coalesced and
-// every thread scans 4 consecutive groups.
-constexpr int kScanPer = 4;
-constexpr int kScanChunk = 1024 * kScanPer;
-__global__ __launch_bounds__(1024) void restore_scan(int N, int gq, const int32_t* __restrict__ off,
-                                                     const int32_t* __restrict__ ocnt,
-                                                     int32_t* __restrict__ base,
-                                                     int32_t* __restrict__ lenq,
-                                                     int32_t* __restrict__ foff) {
-  __shared__ int sh[17];
-  __shared__ int sv[kScanChunk];
-  const int head = blockIdx.x, tid = threadIdx.x;
-  const int32_t* of = off + (size_t)head * (gq + 1);
-  const int32_t* oc = ocnt + (size_t)head * gq;
-  int32_t* bs = base + (size_t)head * gq;
-  int carry = 0;
-  for (int c0 = 0; c0 < gq; c0 += kScanChunk) {
-    const int n = min(kScanChunk, gq - c0);
-    for (int i = tid; i < n; i += 1024) {
-      const int c = of[c0 + i + 1] - of[c0 + i], o = oc[c0 + i];
-      sv[i] = (c > o ? 1 : 0) + o;
-    }
-    __syncthreads();
-    int v[kScanPer], local = 0;
-#pragma unroll
-    for (int j = 0; j < kScanPer; ++j) {
-      const int i = tid * kScanPer + j;
-      v[j] = i < n ? sv[i] : 0;
-      local += v[j];
-    }
-    int total;
-    int acc = carry + block_exclusive_scan(local, sh, total);
-    // every thread read its values before the scan's first barrier, so sv can be overwritten
-#pragma unroll
-    for (int j = 0; j < kScanPer; ++j) {
-      const int i = tid * kScanPer + j;
-      if (i < n) sv[i] = acc;
-      acc += v[j];
-    }
-    __syncthreads();
-    for (int i = tid; i < n; i += 1024) bs[c0 + i] = sv[i];
-    carry += total;
-    __syncthreads();
+  int acc = inc - local;
+  for (int w = 0; w < wave; ++w) acc += wsum[w];
+  for (int i = b0; i < b1; ++i) {
+    const int c = T[i];
+    T[i] = acc;
+    acc += c;
   }
-  if (tid == 0) {
-    lenq[head] = carry;
-    foff[(size_t)head * (N + 1) + carry] = N;
+  if (threadIdx.x == kScanThreads - 1) {
+    lenq[head] = acc;
+    foff[(size_t)head * (N + 1) + acc] = N;
   }
 }
 
 
-// Restore, part 2: 8 lanes per initial query group.  The 8 lanes look at 8
-// members at a time: ballots over the group's lanes rank survivors and
-// outliers in member order, so every member's final position is known
-// without a serial walk.  Outlier rows are then subtracted from the group
-// sum (in member order) and copied to their own packed rows; the remaining
-// members' mean becomes the group's row (if any remain).  Writes the packed
-// Q~ rows, the final partition (members reordered: remaining first, then
-// outliers) and every token's packed row for unmerge.
+// Restore, part 3: 8 lanes per initial query group.  A group's first final
+// slot is its tile's base plus the slots of the tile's earlier groups.  The
+// 8 lanes look at 8 members at a time: ballots over the group's lanes rank
+// survivors and outliers in member order, so every member's final position
+// is known without a serial walk.  Outlier rows are then subtracted from
+// the group sum (in member order) and copied to their own packed rows; the
+// remaining members' mean becomes the group's row (if any remain).  Writes
+// the packed Q~ rows, the final partition (members reordered: remaining
+// first, then outliers) and every token's packed row for unmerge.
 template <typename T>
 __global__ __launch_bounds__(256) void restore_rows(int heads, int N, int gq, const T* __restrict__ q,
                                                     const int32_t* __restrict__ members,
@@ -390,13 +386,14 @@ __global__ __launch_bounds__(256) void restore_rows(int heads, int N, int gq, co
                                                     const float* __restrict__ qsum,
                                                     const uint8_t* __restrict__ mask,
                                                     const int32_t* __restrict__ ocnt,
-                                                    const int32_t* __restrict__ base,
+                                                    const int32_t* __restrict__ tbase,
                                                     const int32_t* __restrict__ lenq,
                                                     int32_t* __restrict__ cu_q, T* __restrict__ qt,
                                                     int32_t* __restrict__ fmembers,
                                                     int32_t* __restrict__ foff,
                                                     int32_t* __restrict__ slot) {
-  const int tiles = ceil_div(gq, 32);
+  __shared__ int sV[kTileGroups];
+  const int tiles = ceil_div(gq, kTileGroups);
   const int head = blockIdx.x / tiles, tile = blockIdx.x % tiles;
   const int tid = threadIdx.x;
   const HeadPrefix hp = head_prefix(lenq, 0, heads, 0);  // every wave, before any exit
@@ -405,21 +402,30 @@ __global__ __launch_bounds__(256) void restore_rows(int heads, int N, int gq, co
     if (tid == 0) cu_q[heads] = hp.rows_total;
   }
   const int cu = __shfl(hp.rows_before, head);
-  const int g = tile * 32 + (tid >> 3), part = tid & 7;
+  const int ls = tid >> 3, part = tid & 7;
+  const int g = tile * kTileGroups + ls;
   const int sub = (tid & 63) >> 3;
+  const int32_t* of = off + (size_t)head * (gq + 1);
+  int m0 = 0, m1 = 0, o = 0;
+  if (g < gq) {
+    m0 = of[g];
+    m1 = of[g + 1];
+    o = ocnt[(size_t)head * gq + g];
+  }
+  const int nsurv = (m1 - m0) - o;
+  const int surv = nsurv > 0 ? 1 : 0;
+  if (part == 0) sV[ls] = g < gq ? surv + o : 0;
+  __syncthreads();
   if (g >= gq) return;  // whole 8-lane groups leave together
+  int before = 0;
+  for (int i = 0; i < ls; ++i) before += sV[i];
   const T* Q = q + (size_t)head * N * kD;
   const int32_t* mem = members + (size_t)head * N;
   const uint8_t* mk = mask + (size_t)head * N;
-  const int32_t* of = off + (size_t)head * (gq + 1);
   int32_t* fm = fmembers + (size_t)head * N;
   int32_t* fo = foff + (size_t)head * (N + 1);
   int32_t* sl = slot + (size_t)head * N;
-  const int m0 = of[g], m1 = of[g + 1];
-  const int o = ocnt[(size_t)head * gq + g];
-  const int nsurv = (m1 - m0) - o;
-  const int surv = nsurv > 0 ? 1 : 0;
-  const int b = cu + base[(size_t)head * gq + g];
+  const int b = cu + tbase[(size_t)head * tiles + tile] + before;
   float sm[8];
   if (surv) Row8<float>::load(qsum + ((size_t)head * gq + g) * kD + part * 8, sm);
   const uint32_t below = (1u << part) - 1u;
@@ -471,7 +477,8 @@ __global__ __launch_bounds__(256) void restore_rows(int heads, int N, int gq, co
 }
 
 // Cached layers: Q~ row R (packed over heads) = mean of the q rows of its
-// final members.  8 lanes per row.
+// final members (in member order).  8 lanes per row, up to 8 member rows in
+// flight per lane.
 template <typename T>
 __global__ __launch_bounds__(256) void merge_q_cached(int heads, int N, const T* __restrict__ q,
                                                       const int32_t* __restrict__ fmembers,
@@ -492,21 +499,14 @@ __global__ __launch_bounds__(256) void merge_q_cached(int heads, int N, const T*
   const int sidx = R - sCu[head];
   const int32_t* fo = foff + (size_t)head * (N + 1);
   const int32_t* fm = fmembers + (size_t)head * N;
-  const T* Q = q + (size_t)head * N * kD;
+  const T* const Q[1] = {q + (size_t)head * N * kD};
   const int m0 = fo[sidx], m1 = fo[sidx + 1];
-  float sm[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) sm[e] = 0.f;
-  for (int m = m0; m < m1; ++m) {
-    float x[8];
-    load8(Q + (size_t)fm[m] * kD + part * 8, x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sm[e] = __fadd_rn(sm[e], x[e]);
-  }
+  float sm[1][8];
+  gather_sum<T, 8, 1>(Q, fm, m0, m1, part, sm);
   const float cnt = (float)(m1 - m0);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) sm[e] = rn_div(sm[e], cnt);
-  store8(qt + (size_t)R * kD + part * 8, sm);
+  for (int e = 0; e < 8; ++e) sm[0][e] = rn_div(sm[0][e], cnt);
+  store8(qt + (size_t)R * kD + part * 8, sm[0]);
 }
 
 // out[h][n][:] = o[slot[h][n]][:], 8 channels per thread (16 B for bf16).
@@ -615,14 +615,15 @@ hipError_t launch_merge_q(int dtype, int heads, int N, int gq, const void* q,
 hipError_t launch_restore(int dtype, int heads, int N, int gq, const void* q,
                           const int32_t* members, const int32_t* off, const float* qsum,
                           const uint8_t* mask, RestoreOut o, hipStream_t stream) {
-  hipLaunchKernelGGL(restore_scan, dim3(heads), dim3(1024), 0, stream, N, gq, off, o.ocnt, o.base, o.lenq,
-                     o.foff);
+  const int tiles = ceil_div(gq, kTileGroups);
+  const int grid = heads * tiles;
+  hipLaunchKernelGGL(restore_count, dim3(grid), dim3(256), 0, stream, N, gq, members, off, mask, o.ocnt, o.tbase);
+  hipLaunchKernelGGL(restore_scan, dim3(heads), dim3(kScanThreads), 0, stream, N, tiles, o.tbase, o.lenq, o.foff);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int grid = heads * ceil_div(gq, 32);
   HTTM_DISPATCH(dtype, hipLaunchKernelGGL(restore_rows<T>, dim3(grid), dim3(256), 0, stream,
                                           heads, N, gq, (const T*)q, members, off, qsum, mask, o.ocnt,
-                                          o.base, o.lenq, o.cu_q, (T*)o.qt, o.fmembers, o.foff,
+                                          o.tbase, o.lenq, o.cu_q, (T*)o.qt, o.fmembers, o.foff,
                                           o.slot));
   return hipGetLastError();
 }

@@ -21,8 +21,12 @@ namespace httm {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPerThread = 16;
-constexpr int kChunk = kThreads * kPerThread;  // elements per workgroup
+// Elements per thread: 16 (small layers: enough workgroups to fill the
+// GPU) or 64 (large layers: a quarter of the workgroups, so each one's
+// threshold prologue covers more data).  One select uses one value.
+constexpr int kPerSmall = 16, kPerLarge = 64;
+constexpr int64_t kLargeFrom = int64_t(1) << 22;
+constexpr int kChunk = kThreads * kPerSmall;  // smallest chunk: sizes the per-chunk tie counts
 constexpr int kBins = 2048;
 
 struct Scratch {
@@ -53,14 +57,6 @@ __global__ void zero_init(float* kmax, int heads, int* fb_count, uint32_t* radix
   if (i == 0) *fb_count = 0;
   if (i < radix_words) radix[i] = 0;
   for (int64_t j = i; j < ocnt_words; j += (int64_t)gridDim.x * blockDim.x) ocnt[j] = 0;
-}
-
-// Outlier members per initial query group: one thread per token, integer
-// atomics (the counts do not depend on order).
-__global__ void count_outliers(int64_t total, int N, int gq, const uint8_t* __restrict__ mask,
-                               const int32_t* __restrict__ group, int32_t* __restrict__ ocnt) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < total && mask[i]) atomicAdd(&ocnt[(i / N) * gq + group[i]], 1);
 }
 
 __global__ void fill_bytes(uint8_t* p, int64_t n, uint8_t v) {
@@ -121,19 +117,19 @@ __device__ void find_bin(const uint32_t* hist, int nb, uint32_t k, uint32_t* wsu
 // (KEY false: deviations), or the order-preserving float_key of any finite
 // value (KEY true: cosine scores).  0xFFFFFFFF, which no finite value
 // yields, marks positions past the end.
-template <bool KEY>
+template <bool KEY, int PER>
 __device__ __forceinline__ void load_chunk(const float* d, int64_t total, int64_t base, uint32_t* u) {
-  const int64_t i0 = base + (int64_t)threadIdx.x * kPerThread;
-  if (i0 + kPerThread <= total) {
+  const int64_t i0 = base + (int64_t)threadIdx.x * PER;
+  if (i0 + PER <= total) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < PER / 4; ++q) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(d + i0 + 4 * q);
 #pragma unroll
       for (int e = 0; e < 4; ++e) u[4 * q + e] = KEY ? float_key(__uint_as_float(v[e]) + 0.0f) : v[e];
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e)
+    for (int e = 0; e < PER; ++e)
       u[e] = (i0 + e < total) ? (KEY ? float_key(d[i0 + e] + 0.0f) : __float_as_uint(d[i0 + e]))
                               : 0xFFFFFFFFu;  // sentinel: no bin
   }
@@ -141,7 +137,7 @@ __device__ __forceinline__ void load_chunk(const float* d, int64_t total, int64_
 
 // pass 0..2: histogram of bits [shift, shift+width) among values whose higher
 // bits equal the prefix found from the previous histograms.
-template <int PASS, bool KEY>
+template <int PASS, bool KEY, int PER>
 __global__ __launch_bounds__(kThreads) void radix_hist(const float* __restrict__ delta, int64_t total,
                                                        uint32_t k_o, uint32_t* scratch) {
   __shared__ uint32_t hist[kBins];
@@ -166,10 +162,10 @@ __global__ __launch_bounds__(kThreads) void radix_hist(const float* __restrict__
   }
   for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0;
   __syncthreads();
-  uint32_t u[kPerThread];
-  load_chunk<KEY>(delta, total, (int64_t)blockIdx.x * kChunk, u);
+  uint32_t u[PER];
+  load_chunk<KEY, PER>(delta, total, (int64_t)blockIdx.x * kThreads * PER, u);
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
+  for (int e = 0; e < PER; ++e) {
     if (u[e] == 0xFFFFFFFFu) continue;
     if (PASS == 0) {
       atomicAdd(&hist[u[e] >> 21], 1u);
@@ -206,7 +202,7 @@ __device__ void threshold(const Scratch& s, uint32_t k_o, uint32_t* hist, uint32
 }
 
 // Marks values above T; counts values equal to T in this chunk.
-template <bool KEY>
+template <bool KEY, int PER>
 __global__ __launch_bounds__(kThreads) void radix_mark(const float* __restrict__ delta, int64_t total,
                                                        uint32_t k_o, uint32_t* scratch,
                                                        uint8_t* __restrict__ mask) {
@@ -225,26 +221,30 @@ __global__ __launch_bounds__(kThreads) void radix_mark(const float* __restrict__
     s.sel[3] = k_o;
   }
   __syncthreads();
-  uint32_t u[kPerThread];
-  const int64_t i0 = (int64_t)blockIdx.x * kChunk + (int64_t)threadIdx.x * kPerThread;
-  load_chunk<KEY>(delta, total, (int64_t)blockIdx.x * kChunk, u);
+  uint32_t u[PER];
+  const int64_t i0 = (int64_t)blockIdx.x * kThreads * PER + (int64_t)threadIdx.x * PER;
+  load_chunk<KEY, PER>(delta, total, (int64_t)blockIdx.x * kThreads * PER, u);
   uint32_t eq = 0;
-  uint8_t m[kPerThread];
+  uint8_t m[PER];
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
+  for (int e = 0; e < PER; ++e) {
     const bool valid = u[e] != 0xFFFFFFFFu;
     m[e] = (valid && u[e] > T) ? 1 : 0;
     eq += (valid && u[e] == T) ? 1u : 0u;
   }
-  if (i0 + kPerThread <= total) {
-    u32x4 w;
+  if (i0 + PER <= total) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      w[q] = (uint32_t)m[4 * q] | ((uint32_t)m[4 * q + 1] << 8) | ((uint32_t)m[4 * q + 2] << 16) |
-             ((uint32_t)m[4 * q + 3] << 24);
-    *reinterpret_cast<u32x4*>(mask + i0) = w;
+    for (int b16 = 0; b16 < PER / 16; ++b16) {
+      u32x4 w;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = 16 * b16 + 4 * q;
+        w[q] = (uint32_t)m[e] | ((uint32_t)m[e + 1] << 8) | ((uint32_t)m[e + 2] << 16) | ((uint32_t)m[e + 3] << 24);
+      }
+      *reinterpret_cast<u32x4*>(mask + i0 + 16 * b16) = w;
+    }
   } else {
-    for (int e = 0; e < kPerThread; ++e)
+    for (int e = 0; e < PER; ++e)
       if (i0 + e < total) mask[i0 + e] = m[e];
   }
   if (eq) atomicAdd(&cnt, eq);
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void radix_mark(const float* __restrict__
 }
 
 // Values equal to T, in flat-index order, take the remaining budget.
-template <bool KEY>
+template <bool KEY, int PER>
 __global__ __launch_bounds__(kThreads) void radix_ties(const float* __restrict__ delta, int64_t total,
                                                        uint32_t* scratch, uint8_t* __restrict__ mask) {
   __shared__ uint32_t part[kThreads / 64];
@@ -266,16 +266,16 @@ __global__ __launch_bounds__(kThreads) void radix_ties(const float* __restrict__
   uint32_t before;
   (void)block_excl_scan(acc, part, before);
   if (before >= need) return;
-  uint32_t u[kPerThread];
-  const int64_t i0 = (int64_t)blockIdx.x * kChunk + (int64_t)threadIdx.x * kPerThread;
-  load_chunk<KEY>(delta, total, (int64_t)blockIdx.x * kChunk, u);
+  uint32_t u[PER];
+  const int64_t i0 = (int64_t)blockIdx.x * kThreads * PER + (int64_t)threadIdx.x * PER;
+  load_chunk<KEY, PER>(delta, total, (int64_t)blockIdx.x * kThreads * PER, u);
   uint32_t eq = 0;
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) eq += (u[e] == T && u[e] != 0xFFFFFFFFu) ? 1u : 0u;
+  for (int e = 0; e < PER; ++e) eq += (u[e] == T && u[e] != 0xFFFFFFFFu) ? 1u : 0u;
   uint32_t chunk_total;
   uint32_t rank = before + block_excl_scan(eq, part, chunk_total);
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
+  for (int e = 0; e < PER; ++e) {
     if (u[e] == T && u[e] != 0xFFFFFFFFu) {
       if (rank < need) mask[i0 + e] = 1;
       ++rank;
@@ -283,6 +283,22 @@ __global__ __launch_bounds__(kThreads) void radix_ties(const float* __restrict__
   }
 }
 
+}  // namespace
+
+namespace {
+// The passes of one select with PER elements per thread; pass 0 only when
+// no producer accumulated it.
+template <bool KEY, int PER>
+void radix_select(const float* vals, int64_t total, uint32_t k, uint32_t* scratch, uint8_t* mask, bool pass0,
+                  hipStream_t stream) {
+  const int nchunks = (int)((total + (int64_t)kThreads * PER - 1) / ((int64_t)kThreads * PER));
+  if (pass0)
+    hipLaunchKernelGGL((radix_hist<0, KEY, PER>), dim3(nchunks), dim3(kThreads), 0, stream, vals, total, k, scratch);
+  hipLaunchKernelGGL((radix_hist<1, KEY, PER>), dim3(nchunks), dim3(kThreads), 0, stream, vals, total, k, scratch);
+  hipLaunchKernelGGL((radix_hist<2, KEY, PER>), dim3(nchunks), dim3(kThreads), 0, stream, vals, total, k, scratch);
+  hipLaunchKernelGGL((radix_mark<KEY, PER>), dim3(nchunks), dim3(kThreads), 0, stream, vals, total, k, scratch, mask);
+  hipLaunchKernelGGL((radix_ties<KEY, PER>), dim3(nchunks), dim3(kThreads), 0, stream, vals, total, scratch, mask);
+}
 }  // namespace
 
 size_t outlier_scratch_words(int64_t total) {
@@ -323,34 +339,28 @@ hipError_t launch_topk(const float* vals, int64_t total, int64_t k, uint8_t* mas
   const int64_t words = (int64_t)outlier_scratch_words(total);
   hipLaunchKernelGGL(zero_words, dim3((unsigned)((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024)), dim3(256),
                      0, stream, scratch, words);
-  const int nchunks = (int)((total + kChunk - 1) / kChunk);
   const uint32_t kk = (uint32_t)k;
-  hipLaunchKernelGGL((radix_hist<0, true>), dim3(nchunks), dim3(kThreads), 0, stream, vals, total, kk, scratch);
-  hipLaunchKernelGGL((radix_hist<1, true>), dim3(nchunks), dim3(kThreads), 0, stream, vals, total, kk, scratch);
-  hipLaunchKernelGGL((radix_hist<2, true>), dim3(nchunks), dim3(kThreads), 0, stream, vals, total, kk, scratch);
-  hipLaunchKernelGGL(radix_mark<true>, dim3(nchunks), dim3(kThreads), 0, stream, vals, total, kk, scratch, mask);
-  hipLaunchKernelGGL(radix_ties<true>, dim3(nchunks), dim3(kThreads), 0, stream, vals, total, scratch, mask);
+  if (total >= kLargeFrom)
+    radix_select<true, kPerLarge>(vals, total, kk, scratch, mask, true, stream);
+  else
+    radix_select<true, kPerSmall>(vals, total, kk, scratch, mask, true, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_outliers(const float* delta, int64_t total, int64_t k_o, uint8_t* mask,
-                           uint32_t* scratch, const int32_t* group, int N, int gq, int32_t* ocnt,
-                           hipStream_t stream) {
+                           uint32_t* scratch, hipStream_t stream) {
   const unsigned tgrid = (unsigned)((total + 255) / 256);
   if (k_o <= 0 || k_o >= total) {
     const uint8_t v = k_o <= 0 ? 0 : 1;
     hipLaunchKernelGGL(fill_bytes, dim3(tgrid), dim3(256), 0, stream, mask, total, v);
   } else {
-    const int nchunks = (int)((total + kChunk - 1) / kChunk);
     const uint32_t k = (uint32_t)k_o;
     // pass 0 (bits 31..21) was accumulated by the deviation producer into the zeroed scratch
-    hipLaunchKernelGGL((radix_hist<1, false>), dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch);
-    hipLaunchKernelGGL((radix_hist<2, false>), dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch);
-    hipLaunchKernelGGL(radix_mark<false>, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, k, scratch, mask);
-    hipLaunchKernelGGL(radix_ties<false>, dim3(nchunks), dim3(kThreads), 0, stream, delta, total, scratch, mask);
+    if (total >= kLargeFrom)
+      radix_select<false, kPerLarge>(delta, total, k, scratch, mask, false, stream);
+    else
+      radix_select<false, kPerSmall>(delta, total, k, scratch, mask, false, stream);
   }
-  if (k_o > 0)
-    hipLaunchKernelGGL(count_outliers, dim3(tgrid), dim3(256), 0, stream, total, N, gq, mask, group, ocnt);
   return hipGetLastError();
 }
 

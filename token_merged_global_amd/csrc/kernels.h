@@ -42,23 +42,21 @@ hipError_t launch_merge_q(int dtype, int heads, int N, int gq, const void* q,
                           const int32_t* members, const int32_t* off, float* qsum, float* delta,
                           uint32_t* hist0, hipStream_t stream);
 
-// Global top-k_o of delta [h*N] -> mask, and per initial query group the
-// number of outlier members (ocnt [h][gq], zeroed beforehand; group [h][N] is
-// the token -> group map).  scratch: outlier_scratch_words(total) words,
-// zeroed beforehand, whose first outlier_hist0_words() hold the first pass.
+// Global top-k_o of delta [h*N] -> mask.  scratch: outlier_scratch_words(total)
+// words, zeroed beforehand, whose first outlier_hist0_words() hold the first
+// pass.
 size_t outlier_scratch_words(int64_t total);
 int outlier_hist0_words();
 hipError_t launch_outliers(const float* delta, int64_t total, int64_t k_o, uint8_t* mask,
-                           uint32_t* scratch, const int32_t* group, int N, int gq, int32_t* ocnt,
-                           hipStream_t stream);
+                           uint32_t* scratch, hipStream_t stream);
 
 // Outlier restore: packed Q~ rows, per-head lengths, final partition.
 struct RestoreOut {
   void* qt;            // [q_capacity][64]
   int32_t* lenq;       // [h]
   int32_t* cu_q;       // [h+1]
-  int32_t* base;       // [h][gq] scratch: first final slot of each initial group
-  const int32_t* ocnt; // [h][gq] outlier members per initial group (from launch_outliers)
+  int32_t* tbase;      // [h][ceil(gq / 32)] scratch: slots of each tile of 32 groups, then its first slot
+  int32_t* ocnt;       // [h][gq] scratch: outlier members per initial group
   int32_t* fmembers;   // [h][N]
   int32_t* foff;       // [h][N+1]
   int32_t* slot;       // [h][N] packed row per token
