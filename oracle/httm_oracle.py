@@ -63,6 +63,7 @@ class Params:
     partition: int = 0  # 0 HTTM temporal blocks; 1 geometry-aware three-class partition (R31);
     #                     2 one head-shared topology from global matching (R37-R40)
     protect_pct: float = 10.0  # geometry-aware partition: percent of each frame's patches protected
+    attn_fp8: bool = False  # attention scores from FP8 (OCP e4m3) queries and keys (R41-R44)
 
     @property
     def tokens_per_frame(self) -> int:
@@ -83,7 +84,8 @@ class Params:
                       q_ratio=w.q_ratio, kv_ratio=w.kv_ratio, outlier_pct=w.outlier_pct,
                       q_dst_stride=w.q_dst_stride, kv_dst_stride=w.kv_dst_stride,
                       block_order=getattr(w, "block_order", 0), softmax_scale=w.softmax_scale,
-                      partition=getattr(w, "partition", 0), protect_pct=getattr(w, "protect_pct", 10.0))
+                      partition=getattr(w, "partition", 0), protect_pct=getattr(w, "protect_pct", 10.0),
+                      attn_fp8=bool(getattr(w, "attn_fp8", False)))
 
 
 def dst_stride(ratio: float, given: int = 0) -> int:
@@ -588,6 +590,97 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     return out
 
 
+# --------------------------------------------------------------------------
+# FP8 attention scores (LiteVGGT page, training strategy and ablations: FP8
+# quantisation for inference; here an OCP e4m3 variant of our own)
+# --------------------------------------------------------------------------
+# Readings R41-R44 (design notes).  R41: e4m3 with 448 as the largest finite
+# magnitude, round to nearest with ties to even.  R42: the merged queries and
+# keys (the score product) are FP8; probabilities and merged values stay
+# bf16; sums are exact here (fp32 on the device).  R43: power-of-two scales,
+# one per query row and one per head's key matrix, each chosen so that the
+# block's largest magnitude lands in [128, 256).  R44: what is quantised is
+# the stored bf16 operand: the query mean, and the key mean times the softmax
+# scale and log2(e) (scores in log2 units, softmax in base 2).
+LOG2E = 1.4426950408889634
+E4M3_MAX = 448.0
+
+
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """Nearest OCP e4m3 value of every element, ties to even (R41), as fp64.
+
+    A normal value in [2^e, 2^(e+1)) (e >= -6) has 3 fraction bits, so its
+    grid spacing is 2^(e-3); below 2^-6 the subnormal spacing is 2^-9.
+    Dividing by the spacing is exact, and numpy's round() takes exact halves
+    to the even integer, which is the even mantissa.  Magnitudes above 448
+    have no finite encoding; the scales of R43 never produce them.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if (a > E4M3_MAX).any():
+        raise ValueError("value beyond the e4m3 range")
+    _, ex = np.frexp(a)  # a = f * 2^ex, f in [0.5, 1): the binade is 2^(ex-1)
+    e = np.maximum(ex - 1, -6)
+    q = np.ldexp(1.0, e - 3)
+    return np.copysign(np.round(a / q) * q, x)
+
+
+def fp8_exponent(amax: np.ndarray) -> np.ndarray:
+    """Scale exponent e of a block whose largest magnitude is amax (R43):
+    amax * 2^e lies in [128, 256), clamped to [-127, 127] (the range of a
+    power-of-two scale byte); an all-zero block takes e = 0."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, ex = np.frexp(amax)
+    e = np.clip(8 - ex, -127, 127)
+    return np.where(amax > 0, e, 0).astype(np.int64)
+
+
+def fp8_quantize(x: np.ndarray, per_row: bool) -> Tuple[np.ndarray, np.ndarray]:
+    """Scaled e4m3 values of x and their exponents: x ~= x8 * 2^-e.
+
+    ``per_row``: one exponent per row of a 2-D x, else one for the whole x.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    amax = np.abs(x).max(axis=1) if per_row else np.abs(x).max(initial=0.0)
+    e = fp8_exponent(amax)
+    scaled = np.ldexp(x, e[:, None] if per_row else e)
+    return e4m3_round(scaled), e
+
+
+def fp8_scores(q: np.ndarray, k2: np.ndarray) -> np.ndarray:
+    """Scores in log2 units from FP8 operands (R42, R43): q rows and the key
+    matrix k2 (already times scale * log2 e) are quantised, multiplied
+    exactly, and the scales removed."""
+    q8, eq = fp8_quantize(q, per_row=True)
+    k8, ek = fp8_quantize(k2, per_row=False)
+    return np.ldexp(q8 @ k8.T, -(eq[:, None] + ek))
+
+
+def attention_fp8(q: np.ndarray, k2: np.ndarray, v: np.ndarray, chunk: int = 2048) -> np.ndarray:
+    """O = softmax_2(S) V with S = fp8_scores(q, k2), in fp64 (R42)."""
+    v64 = np.asarray(v, dtype=np.float64)
+    out = np.empty((q.shape[0], v64.shape[1]), dtype=np.float64)
+    q8, eq = fp8_quantize(q, per_row=True)
+    k8, ek = fp8_quantize(k2, per_row=False)
+    for i in range(0, q.shape[0], chunk):
+        s = np.ldexp(q8[i:i + chunk] @ k8.T, -(eq[i:i + chunk, None] + ek))
+        s -= s.max(axis=1, keepdims=True)
+        e = np.exp2(s)
+        out[i:i + chunk] = (e @ v64) / e.sum(axis=1, keepdims=True)
+    return out
+
+
+def fp8_operands(qm: np.ndarray, km: np.ndarray, vm: np.ndarray, scale: float):
+    """The stored bf16 operands the FP8 scores start from (R44), from fp32
+    means: Q~ rounded to bf16, K~ times the fp32 product of the softmax scale
+    and log2(e) (one fp32 rounding) then rounded to bf16, V~ rounded to bf16."""
+    kscale = np.float32(np.float32(scale) * np.float32(LOG2E))
+    qb = round_bf16_rne(np.asarray(qm, dtype=np.float32))
+    kb = round_bf16_rne((np.asarray(km, dtype=np.float32) * kscale).astype(np.float32))
+    vb = round_bf16_rne(np.asarray(vm, dtype=np.float32))
+    return qb, kb, vb
+
+
 def unmerge(o: np.ndarray, part: Partition) -> np.ndarray:
     """Copy each merged output row back to every member, at its original index.
 
@@ -655,17 +748,24 @@ def deviations(q: np.ndarray, q_reps: Sequence[np.ndarray]) -> np.ndarray:
 
 
 def head_output(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_final_rep: np.ndarray,
-                k_rep: np.ndarray, scale: float, rows: Optional[np.ndarray] = None) -> np.ndarray:
+                k_rep: np.ndarray, scale: float, rows: Optional[np.ndarray] = None,
+                fp8: bool = False) -> np.ndarray:
     """Steps 6-7 for one head: means, attention, unmerge.
 
     ``rows`` restricts the output to those original token ids (the attention
     of one output row needs only its own query slot), for large layers.
+    ``fp8``: scores from FP8 queries and keys (R41-R44).
     """
     qp = partition(q_final_rep)
     kp = partition(k_rep)
     qt = group_means(q, qp)
     kt = group_means(k, kp)
     vt = group_means(v, kp)
+    if fp8:
+        qb, kb, vb = fp8_operands(qt, kt, vt, scale)
+        if rows is None:
+            return unmerge(attention_fp8(qb, kb, vb), qp)
+        return attention_fp8(qb[qp.group_of[rows]], kb, vb)
     if rows is None:
         return unmerge(attention(qt, kt, vt, scale), qp)
     slots = qp.group_of[rows]
@@ -689,7 +789,8 @@ def layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, p: Params,
     tr.outlier = select_outliers(tr.delta, outlier_budget(p))
     tr.q_final_rep = [restore_partition(tr.q_match[i].rep, tr.outlier[i]) for i in range(h)]
     hs = list(range(h)) if out_heads is None else list(out_heads)
-    outs = [head_output(q[i], k[i], v[i], tr.q_final_rep[i], tr.k_rep[i], p.scale, rows) for i in hs]
+    outs = [head_output(q[i], k[i], v[i], tr.q_final_rep[i], tr.k_rep[i], p.scale, rows, p.attn_fp8)
+            for i in hs]
     tr.out = np.stack(outs)
     return tr
 
@@ -705,5 +806,5 @@ def layer_cached(q: np.ndarray, k: np.ndarray, v: np.ndarray, p: Params,
     are recomputed from this layer's q, k, v.
     """
     hs = list(range(q.shape[0])) if out_heads is None else list(out_heads)
-    return np.stack([head_output(q[i], k[i], v[i], q_final_rep[i], k_rep[i], p.scale, rows)
+    return np.stack([head_output(q[i], k[i], v[i], q_final_rep[i], k_rep[i], p.scale, rows, p.attn_fp8)
                      for i in hs])

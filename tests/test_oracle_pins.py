@@ -682,3 +682,164 @@ def test_global_match_brute_force(seed):
         assert g.match_dst[patches[i]] == patches[j]
         assert abs(g.score[patches[i]] - score[i]) < 1e-6
     assert {i for i in range(len(patches)) if g.selected[patches[i]]} == sel
+
+
+# ---------------------------------------------------------------- FP8 scores (R41-R44)
+def _torch_e4m3(x):
+    """Library reference: torch's float8_e4m3fn conversion (nearest, ties to even)."""
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _finite_e4m3():
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return codes[np.isfinite(codes)]
+
+
+def test_e4m3_round_matches_torch():
+    """Against torch's e4m3 conversion: a log-uniform sweep over the normal
+    and subnormal range, every finite code (unchanged) and every midpoint
+    between neighbouring codes (to the even mantissa)."""
+    rng = np.random.default_rng(41)
+    x = (rng.standard_normal(400_000) * np.exp2(rng.uniform(-14, 8, 400_000))).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    assert np.array_equal(O.e4m3_round(x), _torch_e4m3(x))
+    fin = _finite_e4m3()
+    assert len(fin) == 254 and np.array_equal(O.e4m3_round(fin), fin)
+    pos = np.unique(np.abs(fin))
+    mids = np.concatenate([(pos[:-1] + pos[1:]) / 2, -(pos[:-1] + pos[1:]) / 2])
+    assert np.array_equal(O.e4m3_round(mids), _torch_e4m3(mids))
+    with pytest.raises(ValueError):
+        O.e4m3_round(np.array([449.0]))
+
+
+def test_e4m3_round_hand_values():
+    """Hand-derived: spacing 2^-3 in [1, 2), ties to the even mantissa, the
+    subnormal spacing 2^-9 below 2^-6, and the top binade [256, 448]."""
+    cases = [(1.0625, 1.0), (1.1875, 1.25), (1.0625 + 2.0 ** -20, 1.125), (2.0 ** -10, 0.0),
+             (3 * 2.0 ** -10, 2.0 ** -8), (2.0 ** -6 + 2.0 ** -10, 2.0 ** -6), (-0.3, -0.3125),
+             (248.0, 256.0), (240.0, 240.0), (440.0, 448.0), (0.0, 0.0)]
+    x = np.array([c[0] for c in cases])
+    assert O.e4m3_round(x).tolist() == [c[1] for c in cases]
+
+
+def test_fp8_exponent_lands_amax_in_128_256():
+    rng = np.random.default_rng(42)
+    amax = np.concatenate([np.exp2(rng.uniform(-120, 120, 5000)), np.exp2(np.arange(-120, 121.0))])
+    e = O.fp8_exponent(amax)
+    s = np.ldexp(amax, e)
+    assert ((s >= 128) & (s < 256)).all()
+    assert O.fp8_exponent(np.array([0.0, 1.0, 255.9, 256.0])).tolist() == [0, 7, 0, -1]
+    assert O.fp8_exponent(np.array([2.0 ** -130, 2.0 ** 140])).tolist() == [127, -127]  # clamped
+
+
+def _brute_fp8_attention(q, k2, v):
+    """Loops: exponents found by search, elements rounded by torch, exact
+    products (e4m3 products and their sums are exact in fp64 here), base-2
+    softmax."""
+    def expo(amax):
+        if amax == 0:
+            return 0
+        for e in range(-127, 128):
+            if 128 <= amax * 2.0 ** e < 256:
+                return e
+        raise AssertionError
+    ek = expo(float(np.abs(k2).max()))
+    k8 = _torch_e4m3(np.asarray(k2, np.float64) * 2.0 ** ek)
+    out = np.zeros((q.shape[0], v.shape[1]))
+    for i in range(q.shape[0]):
+        eq = expo(float(np.abs(q[i]).max()))
+        q8 = _torch_e4m3(np.asarray(q[i], np.float64) * 2.0 ** eq)
+        s = [sum(float(q8[d]) * float(k8[j, d]) for d in range(q.shape[1])) * 2.0 ** -(eq + ek)
+             for j in range(k2.shape[0])]
+        m = max(s)
+        p = [2.0 ** (x - m) for x in s]
+        out[i] = sum(pj * np.asarray(v[j], np.float64) for j, pj in enumerate(p)) / sum(p)
+    return out
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_attention_fp8_brute_force(seed):
+    rng = np.random.default_rng(43 + seed)
+    q = (rng.standard_normal((6, 16)) * np.exp2(rng.uniform(-3, 3, (6, 1)))).astype(np.float32)
+    k2 = (0.4 * rng.standard_normal((9, 16))).astype(np.float32)
+    v = rng.standard_normal((9, 8)).astype(np.float32)
+    got = O.attention_fp8(q, k2, v)
+    assert np.abs(got - _brute_fp8_attention(q, k2, v)).max() < 1e-12
+    # quantisation is really there: the exact base-2 softmax differs
+    exact = _sdpa64(q, k2.astype(np.float64) * math.log(2.0), v, 1.0)
+    assert np.abs(got - exact).max() > 1e-6
+
+
+def test_attention_fp8_exact_on_representable_operands():
+    """Integers of at most 4 significant bits stay e4m3 values after any
+    power-of-two scale: the FP8 scores are then the exact scores, and the
+    output is the fp64 attention (torch sdpa with scale ln 2 for base 2)."""
+    rng = np.random.default_rng(44)
+    q = rng.integers(-15, 16, (7, 16)).astype(np.float32) * np.exp2(rng.integers(-4, 4, (7, 1))).astype(np.float32)
+    k2 = rng.integers(-15, 16, (11, 16)).astype(np.float32) / 64
+    v = rng.standard_normal((11, 8)).astype(np.float32)
+    assert np.abs(O.attention_fp8(q, k2, v) - _sdpa64(q, k2.astype(np.float64) * math.log(2.0), v, 1.0)).max() < 1e-12
+
+
+def test_attention_fp8_power_of_two_invariance():
+    """Queries times 2^a and keys times 2^-a: every exponent absorbs the
+    factor, no code changes, the output is bit-identical.  A factor that is
+    not a power of two changes codes and the output."""
+    rng = np.random.default_rng(45)
+    q = rng.standard_normal((20, 64)).astype(np.float32)
+    k2 = (0.2 * rng.standard_normal((50, 64))).astype(np.float32)
+    v = rng.standard_normal((50, 64)).astype(np.float32)
+    base = O.attention_fp8(q, k2, v)
+    for a in (-3, 5):
+        assert np.array_equal(O.attention_fp8(q * np.float32(2.0 ** a), k2 * np.float32(2.0 ** -a), v), base)
+    assert not np.array_equal(O.attention_fp8(q * np.float32(1.1), k2 / np.float32(1.1), v), base)
+
+
+def test_fp8_scores_error_bound():
+    """|S8 - S| <= sum_d (|dq_d| |k^_d| + |q_d| |dk_d|), where each element's
+    rounding error is at most 2^-4 of its scaled magnitude plus 2^-10 (half
+    the subnormal spacing), descaled."""
+    rng = np.random.default_rng(46)
+    q = (rng.standard_normal((40, 64)) * np.exp2(rng.uniform(-4, 4, (40, 1)))).astype(np.float64)
+    k2 = (0.3 * rng.standard_normal((70, 64))).astype(np.float64)
+    s8 = O.fp8_scores(q, k2)
+    s = q @ k2.T
+    eq = np.array([math.frexp(a)[1] for a in np.abs(q).max(axis=1)])  # amax in [2^(e-1), 2^e)
+    ek = math.frexp(float(np.abs(k2).max()))[1]
+    dq = 2.0 ** -4 * np.abs(q) + 2.0 ** -10 * 2.0 ** (eq[:, None] - 8)
+    dk = 2.0 ** -4 * np.abs(k2) + 2.0 ** -10 * 2.0 ** (ek - 8)
+    bound = dq @ (np.abs(k2) + dk).T + np.abs(q) @ dk.T
+    assert (np.abs(s8 - s) <= bound).all()
+    assert np.abs(s8 - s).max() > 0
+
+
+def test_layer_fp8_no_merge_is_brute_force_fp8_attention():
+    """Merge ratios 0: every slot is one token, so the FP8 layer's head
+    output is the brute-force FP8 attention of the stored bf16 operands --
+    queries rounded to bf16, keys times fp32(scale) * fp32(log2 e) rounded
+    to bf16 (R44)."""
+    p = _small(heads=1, frames=2, gh=3, gw=3, sp=1, n_s=4, n_t=2, qr=0.0, kr=0.0, pct=0.0,
+               softmax_scale=0.3, attn_fp8=True)
+    p8 = p
+    q, k, v = _rand_qkv(p, 47)
+    tr = O.layer(q, k, v, p8)
+    ks = np.float32(np.float32(0.3) * np.float32(1.4426950408889634))
+    bf = lambda a: torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    ref = _brute_fp8_attention(bf(q[0]), bf((k[0] * ks).astype(np.float32)), bf(v[0]))
+    assert np.abs(tr.out[0] - ref).max() < 1e-12
+    # the bf16 layer on the same inputs differs (the scores are quantised)
+    p16 = O.Params(**{**p.__dict__, "attn_fp8": False})
+    assert np.abs(O.layer(q, k, v, p16).out[0] - tr.out[0]).max() > 1e-5
+
+
+def test_layer_fp8_close_to_bf16_layer():
+    """The FP8 layer's partitions are the bf16 layer's (FP8 enters only the
+    attention scores), and its output stays near it on redundant tokens."""
+    p = _small(pct=10.0, softmax_scale=0.0)
+    q, k, v = _rand_qkv(p, 48)
+    a = O.layer(q, k, v, p)
+    b = O.layer(q, k, v, O.Params(**{**p.__dict__, "attn_fp8": True}))
+    for h in range(p.heads):
+        assert np.array_equal(a.q_final_rep[h], b.q_final_rep[h]) and np.array_equal(a.k_rep[h], b.k_rep[h])
+    rel = np.sqrt(((a.out - b.out) ** 2).mean()) / np.sqrt((a.out ** 2).mean())
+    assert 0 < rel < 0.1
