@@ -49,6 +49,10 @@ METRIC = "HTTM global-attn layer tokens/s (merge+attn+unmerge), 30–500 frames"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MFMA_F32_PEAK_TFLOPS = 157.3
+MFMA_FP8_PEAK_TFLOPS = 5000.0
+# FP8-score attention: half its FLOP (Q K^T) at the fp8 rate, half (P V) at
+# the bf16 rate, so the ideal time is F/2/5.0 + F/2/2.5 PFLOP/s: 3.33 PFLOP/s.
+MFMA_FP8_BF16_MIX_PEAK_TFLOPS = 2.0 / (1.0 / MFMA_FP8_PEAK_TFLOPS + 1.0 / MFMA_BF16_PEAK_TFLOPS)
 TRAFFIC_UNIT = "bytes per launch (HBM, rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0)"
 
 
@@ -181,6 +185,49 @@ def stage_rooflines(stages, alg, dtype, cached_stages=None):
             out["merge_kv_cached_layer"] = roofline_entry("merge_kv (cached layer, library stream)",
                                                           alg["merge_kv"], cached_stages["merge_kv"], dtype)
     return out
+
+
+def fp8_variant(H, torch, w, dev, n_cached, out_bf16, steps, stream):
+    """The same stack with FP8 (e4m3) attention scores: time per step, the
+    attention kernel against the mixed fp8 / bf16 peak, and how far layer 0's
+    output moves from the bf16 layer's (relative RMS)."""
+    w8 = w.with_(attn_fp8=True)
+    plan = H.Plan.from_workload(w8)
+    ws = H.workspace(plan)
+    idx = H.CachedIndex(plan) if n_cached > 0 else None
+    out = torch.empty_like(dev[0][0])
+
+    def step():
+        H.layer(plan, *dev[0], ws=ws, out=out, index=idx, stream=stream)
+        for l in range(1, 1 + n_cached):
+            H.layer_cached(plan, idx, *dev[l], ws=ws, out=out, stream=stream)
+
+    for _ in range(2):
+        step()
+    H.set_timing(["attn", "key_fp8"])
+    ms = timed(torch, stream, step, steps)
+    t, calls = H.get_timing()
+    H.set_timing([])
+    H.layer(plan, *dev[0], ws=ws, out=out, index=idx, stream=stream)
+    torch.cuda.synchronize()
+    a, b = out.float(), out_bf16.float()
+    rel = float(torch.sqrt(((a - b) ** 2).mean()) / torch.sqrt((b ** 2).mean()))
+    lq, lkh = lengths(H, plan, ws, w8, False, idx)
+    flop = 4.0 * w.d_head * float((lkh * lq).sum())
+    ach = flop / (t["attn"] * 1e-3) / 1e12
+    layers = 1 + n_cached
+    res = {"ms_per_step": ms, "tokens_per_s": layers * w.n_tokens / (ms * 1e-3),
+           "attention": {"kernel": "attn_fast8", "bound": "mfma", "avg_launch_ms": t["attn"], "launches_timed": calls,
+                         "achieved": ach, "unit": "TFLOP/s", "peak": MFMA_FP8_BF16_MIX_PEAK_TFLOPS,
+                         "frac": ach / MFMA_FP8_BF16_MIX_PEAK_TFLOPS,
+                         "peak_note": "Q K^T at the fp8 rate (5.0 PFLOP/s) and P V at the bf16 rate (2.5 PFLOP/s)"},
+           "key_quantisation_ms": t["key_fp8"],
+           "layer0_output_rel_rms_vs_bf16": rel,
+           "note": "attention scores from e4m3 queries (per-row power-of-two scale) and keys (per-head scale); "
+                   "probabilities and values bf16; not the headline"}
+    del ws, idx, out
+    torch.cuda.empty_cache()
+    return res
 
 
 # --------------------------------------------------------------------------- CPU baseline
@@ -452,6 +499,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=2, help="cpu baseline: heads in the oracle's sample")
     ap.add_argument("--dense-reps", type=int, default=2)
     ap.add_argument("--no-extra", action="store_true", help="skip the 30-frame layer reported as extra keys")
+    ap.add_argument("--no-fp8", dest="fp8", action="store_false",
+                    help="skip the FP8-score variant reported as extra keys")
+    ap.add_argument("--attn-split", type=int, default=0, help="key splits of the attention (0: the library's)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (HBM counter calibration)")
     ap.add_argument("--kv-ratio", type=float, default=None, help="override the workload's K/V merge ratio")
@@ -506,7 +556,7 @@ def main():
             (host0 if l == 0 else host1).update({t: xl[t][:args.cpu_heads].copy() for t in "qkv"})
         del xl
     log(f"[bench] inputs of {1 + n_cached} layer(s) resident in HBM ({time.perf_counter() - t0:.1f} s)")
-    plan = H.Plan.from_workload(w)
+    plan = H.Plan.from_workload(w, attn_split=args.attn_split)
     ws = H.workspace(plan)
     idx = H.CachedIndex(plan) if n_cached > 0 else None
     out = torch.empty_like(dev[0][0])
@@ -635,6 +685,16 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: {args.copy_calibration_mib} MiB device copy")
 
+    fp8 = None
+    if args.fp8 and w.dtype == "bf16":
+        H.layer(plan, *dev[0], ws=ws, out=out, index=idx, stream=stream)
+        log("[bench] FP8-score variant of the same stack")
+        fp8 = fp8_variant(H, torch, w, dev, n_cached, out, max(3, args.steps), stream)
+        log(f"[bench]   fp8 {fp8['ms_per_step']:.4f} ms/step, {fp8['tokens_per_s']:.4g} tokens/s, attention "
+            f"{fp8['attention']['avg_launch_ms']:.4f} ms ({fp8['attention']['achieved']:.1f} TFLOP/s, frac "
+            f"{fp8['attention']['frac']:.3f} of the mixed peak), output vs bf16 rel RMS "
+            f"{fp8['layer0_output_rel_rms_vs_bf16']:.3g}")
+
     layer_ms = per_layer["layer0_ms"] if per_layer else ms_step
     del dev, ws, idx, out
     torch.cuda.empty_cache()
@@ -687,6 +747,7 @@ def main():
                     "q_len_max": int(lq.max()), "q_ratio_final": float(lq.mean() / w.n_tokens),
                     "kv_ratio_final": float(lkh.mean() / w.n_tokens)},
         "vggt30": extra,
+        "fp8_variant": fp8,
     }
     print(json.dumps(res), flush=True)
 

@@ -64,6 +64,7 @@ class Workload:
     block_order: int = 0  # 0 frame-major, 1 frame-minor stacking inside a block
     partition: int = 0  # 0 HTTM temporal blocks, 1 geometry-aware three-class partition
     protect_pct: float = 10.0  # partition 1: percent of each frame's patches protected
+    attn_fp8: bool = False  # attention scores from FP8 (e4m3) queries and keys
     layers: int = 1
     sigma_drift: float = 0.1
     sigma_noise: float = 0.05

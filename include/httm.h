@@ -117,6 +117,14 @@ typedef struct {
   int32_t attn_split;    /* bf16 attention: key ranges per query tile whose partial results are
                             combined in a fixed order; 0 = the library's choice (4), else 1, 2, 4
                             or 8 (fp32 layers always use 1).  Outputs agree to rounding */
+  int32_t attn_fp8;      /* bf16 layers: 1 = attention scores from FP8 operands (LiteVGGT page,
+                            training strategy and ablations: FP8 quantisation for inference;
+                            our own OCP e4m3 form): every merged query row and every head's
+                            merged keys get a power-of-two scale that puts their largest
+                            magnitude in [128, 256), values round to nearest-even e4m3, the
+                            products and sums are exact / fp32; probabilities and merged
+                            values stay bf16.  0 = bf16 scores (default).  Merge indices do
+                            not depend on it (an index serves both) */
 } httm_params;
 
 typedef struct httm_plan httm_plan;
@@ -272,7 +280,13 @@ httm_status httm_attention_dense(const httm_plan* plan, void* ws, size_t ws_byte
  *   HTTM_DBG_GM_METRIC: [N][64] the head-mean keys matched on (element type);
  *   HTTM_DBG_GM_MATCH: [N] int32 matched destination token of every source,
  *       -1 for every other token;
- *   HTTM_DBG_GM_SCORE: [N] float cosine of that match (0 for non-sources). */
+ *   HTTM_DBG_GM_SCORE: [N] float cosine of that match (0 for non-sources).
+ * FP8 scores only (attn_fp8 = 1), the operands of the last layer's score
+ * product as e4m3 bytes (value = code * 2^-exponent):
+ *   HTTM_DBG_K8: [h][L_k padded to 64][64] merged keys (as HTTM_DBG_KT);
+ *   HTTM_DBG_KEXP: [h] int32 key scale exponent per head;
+ *   HTTM_DBG_Q8: [q_capacity][64] packed merged queries (as HTTM_DBG_QT);
+ *   HTTM_DBG_QEXP: [q_capacity] int32 scale exponent per query row. */
 typedef enum {
   HTTM_DBG_Q_MATCH = 0, HTTM_DBG_Q_SCORE, HTTM_DBG_KV_MATCH, HTTM_DBG_KV_SCORE,
   HTTM_DBG_Q_GROUP, HTTM_DBG_KV_GROUP, HTTM_DBG_DELTA, HTTM_DBG_OUTLIER,
@@ -280,6 +294,7 @@ typedef enum {
   HTTM_DBG_GA_VAR, HTTM_DBG_GA_ROLE, HTTM_DBG_GA_MATCH, HTTM_DBG_GA_SCORE, HTTM_DBG_KV_LEN,
   HTTM_DBG_KT, HTTM_DBG_VT, HTTM_DBG_QT,
   HTTM_DBG_GM_METRIC, HTTM_DBG_GM_MATCH, HTTM_DBG_GM_SCORE,
+  HTTM_DBG_K8, HTTM_DBG_KEXP, HTTM_DBG_Q8, HTTM_DBG_QEXP,
   HTTM_DBG_COUNT
 } httm_debug_item;
 httm_status httm_debug_size(const httm_plan* plan, int32_t item, size_t* bytes);
@@ -315,6 +330,7 @@ typedef enum {
   HTTM_T_GA_MATCH,   /* partition = 1: the global match kernel (one launch) */
   HTTM_T_SIM_K,      /* key stream similarity (library stream) */
   HTTM_T_SELECT_K,   /* key stream selection (library stream) */
+  HTTM_T_KEY_FP8,    /* attn_fp8: the merged keys' scale and e4m3 rounding (two launches) */
   HTTM_T_COUNT
 } httm_timing_stage;
 /* With HTTM_TIMING_SERIAL in the mask (and at least one stage bit), the

@@ -376,7 +376,7 @@ def check_layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, p: O.Params, gpu: D
     hs = list(range(h)) if out_heads is None else list(out_heads)
     outs = []
     for i in hs:
-        outs.append(O.head_output(q[i], k[i], v[i], qf[i], k_rep[i], p.scale, rows))
+        outs.append(O.head_output(q[i], k[i], v[i], qf[i], k_rep[i], p.scale, rows, p.attn_fp8))
     ref = np.stack(outs)
     got = out_gpu[hs] if rows is None else out_gpu[hs][:, rows]
     rep.out_rms = float(np.sqrt(np.mean(ref ** 2)))

@@ -141,6 +141,33 @@ def test_validation_codes():
         assert _status(attn_split=split) == 1
     assert _status(partition=2) == 0
     assert _status(partition=3) == 1
+    assert _status(attn_fp8=True) == 0
+    for part in (1, 2):
+        assert _status(attn_fp8=True, partition=part) == 0
+
+
+def test_fp8_plan_validation_sizes_and_items():
+    """FP8 scores: bf16 layers only; the workspace grows by the e4m3 keys
+    ([h][L_k padded][64] bytes), the e4m3 queries ([q_capacity][64] bytes),
+    their exponents and the key maxima; the FP8 debug items exist only then."""
+    w = gen.WORKLOADS["tiny"]  # fp32 layer
+    with pytest.raises(H.HttmError) as e:
+        H.Plan.from_workload(w, attn_fp8=True)
+    assert e.value.status == 2
+    w30 = gen.WORKLOADS["vggt30"]
+    plan16 = H.Plan.from_workload(w30)
+    plan8 = H.Plan.from_workload(w30, attn_fp8=True)
+    h, lkp, qc = w30.heads, -(-plan8.info["kv_len"] // 64) * 64, plan8.info["q_capacity"]
+    extra = plan8.workspace_bytes - plan16.workspace_bytes
+    need = h * lkp * 64 + qc * 64 + 4 * qc + 4 * h + 4 * h * 64
+    assert need <= extra <= need + 5 * 256
+    assert plan8.index_bytes == plan16.index_bytes
+    assert set(H.FP8_ITEMS) <= set(H.debug_items(plan8, rows=True))
+    assert not set(H.FP8_ITEMS) & set(H.debug_items(plan16, rows=True))
+    n = ctypes.c_size_t()
+    assert H.lib().httm_debug_size(plan16.handle, H.DEBUG_ITEMS.index("k8"), ctypes.byref(n)) == 2
+    assert H.lib().httm_debug_size(plan8.handle, H.DEBUG_ITEMS.index("k8"), ctypes.byref(n)) == 0
+    assert n.value == h * lkp * 64
 
 
 @pytest.mark.parametrize("name,kv", [("tiny", 0.5), ("vggt30", 0.5), ("vggt30", 0.75), ("vggt500", 0.5)])

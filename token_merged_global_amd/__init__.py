@@ -27,13 +27,15 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 DEBUG_ITEMS = ["q_match", "q_score", "kv_match", "kv_score", "q_group", "kv_group", "delta",
                "outlier", "q_slot", "cu_q", "select", "attn_fallback",
                "ga_var", "ga_role", "ga_match", "ga_score", "kv_len", "kt", "vt", "qt",
-               "gm_metric", "gm_match", "gm_score"]
+               "gm_metric", "gm_match", "gm_score", "k8", "kexp", "q8", "qexp"]
+#: Items that exist only with FP8 scores (attn_fp8).
+FP8_ITEMS = ["k8", "kexp", "q8", "qexp"]
 #: Items that exist only under one partition (block-local / geometry-aware / head-shared).
 BLOCK_ITEMS = ["q_match", "q_score", "kv_match", "kv_score"]
 GA_ITEMS = ["ga_var", "ga_role", "ga_match", "ga_score", "kv_len"]
 GM_ITEMS = ["gm_metric", "gm_match", "gm_score"]
 TIMING_STAGES = ["sim", "select", "merge_kv", "merge_q", "outlier", "restore", "attn", "unmerge", "attn_tail",
-                 "ga_match", "sim_k", "select_k"]
+                 "ga_match", "sim_k", "select_k", "key_fp8"]
 
 
 class HttmError(RuntimeError):
@@ -50,7 +52,7 @@ class Params(ctypes.Structure):
                 ("q_dst_stride", ctypes.c_int32), ("kv_dst_stride", ctypes.c_int32),
                 ("block_order", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("dtype", ctypes.c_int32), ("partition", ctypes.c_int32), ("protect_pct", ctypes.c_double),
-                ("attn_split", ctypes.c_int32)]
+                ("attn_split", ctypes.c_int32), ("attn_fp8", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -147,11 +149,12 @@ class Plan:
     def __init__(self, heads: int, frames: int, grid_h: int, grid_w: int, n_special: int, n_s: int,
                  n_t: int, q_ratio: float, kv_ratio: float, outlier_pct: float, dtype="bf16",
                  d_head: int = 64, q_dst_stride: int = 0, kv_dst_stride: int = 0, block_order: int = 0,
-                 softmax_scale: float = 0.0, partition: int = 0, protect_pct: float = 10.0, attn_split: int = 0):
+                 softmax_scale: float = 0.0, partition: int = 0, protect_pct: float = 10.0, attn_split: int = 0,
+                 attn_fp8: bool = False):
         self.params = Params(heads, d_head, frames, grid_h, grid_w, n_special, n_s, n_t, float(q_ratio),
                              float(kv_ratio), float(outlier_pct), q_dst_stride, kv_dst_stride, block_order,
                              float(softmax_scale), _dtype_code(dtype), int(partition), float(protect_pct),
-                             int(attn_split))
+                             int(attn_split), int(bool(attn_fp8)))
         h = ctypes.c_void_p()
         _check(lib().httm_plan_create(ctypes.byref(self.params), ctypes.byref(h)))
         self.handle = h
@@ -167,7 +170,7 @@ class Plan:
                     dtype=w.dtype, d_head=w.d_head, q_dst_stride=w.q_dst_stride,
                     kv_dst_stride=w.kv_dst_stride, softmax_scale=w.softmax_scale,
                     block_order=getattr(w, "block_order", 0), partition=getattr(w, "partition", 0),
-                    protect_pct=getattr(w, "protect_pct", 10.0))
+                    protect_pct=getattr(w, "protect_pct", 10.0), attn_fp8=getattr(w, "attn_fp8", False))
         args.update(kw)
         return Plan(**args)
 
@@ -347,7 +350,9 @@ def debug_items(plan: Plan, rows: bool = False) -> List[str]:
     part = plan.params.partition
     keep = {0: BLOCK_ITEMS, 1: GA_ITEMS, 2: GM_ITEMS}[part]
     skip = [it for it in BLOCK_ITEMS + GA_ITEMS + GM_ITEMS if it not in keep]
-    return [it for it in DEBUG_ITEMS if it not in skip and (rows or it not in ROW_ITEMS)]
+    if not plan.params.attn_fp8:
+        skip += FP8_ITEMS
+    return [it for it in DEBUG_ITEMS if it not in skip and (rows or it not in ROW_ITEMS + FP8_ITEMS)]
 
 
 def debug_read(plan: Plan, ws, item: str, stream=None, index: Optional[CachedIndex] = None):
@@ -363,7 +368,7 @@ def debug_read(plan: Plan, ws, item: str, stream=None, index: Optional[CachedInd
     dt = {"q_score": np.float32, "kv_score": np.float32, "delta": np.float32, "outlier": np.uint8,
           "select": np.uint32, "ga_var": np.float32, "ga_role": np.uint8,
           "ga_score": np.float32, "kt": rows, "vt": rows, "qt": rows, "gm_metric": rows,
-          "gm_score": np.float32}.get(item, np.int32)
+          "gm_score": np.float32, "k8": np.uint8, "q8": np.uint8}.get(item, np.int32)
     arr = np.empty(n.value // np.dtype(dt).itemsize, dtype=dt)
     _check(lib().httm_debug_read(plan.handle, ws.data_ptr(), ctypes.byref(index.c) if index is not None else None,
                                  code, arr.ctypes.data, arr.nbytes, _stream_ptr(stream)))

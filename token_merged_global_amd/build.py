@@ -28,6 +28,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 PER_FILE = {"k_merge.hip": ["-ffp-contract=off"],
             # MFMA results in VGPRs: the softmax reads them with plain VALU ops
             "k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+            "k_attn8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
             "k_sim.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
             # variance map compared bit for bit; MFMA cosine tiles as in k_sim
             "k_ga.hip": ["-ffp-contract=off", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],

@@ -61,6 +61,7 @@ struct Layout {
   Region qsum, delta, mask, radix, base, ocnt;
   Region qt, kt, vt, o;
   Region kmax, fb, opart, lpart, mpart;  // attention: key norms, fallback queue, split partials
+  Region k8, kpart, kexp, q8, qexp;       // FP8 scores: e4m3 keys, key maxima, exponents, queries
   // geometry-aware partition (partition 1 only)
   Region ga_var, ga_role, ga_fcnt, ga_foff, ga_tot, ga_slot, ga_dlist, ga_dslot, ga_slist;
   Region ga_gdst, ga_gslot, ga_gscore, ga_best, ga_snorm, ga_cnt, ga_tmp, ga_dg, ga_dinv;
@@ -168,6 +169,8 @@ httm_status build(const httm_params& p, httm_plan* pl) {
   if ((int64_t)p.n_s * p.n_t > kMaxBlock) return fail(HTTM_ERR_UNSUPPORTED, "n_s * n_t must be <= 4096");
   if (p.attn_split != 0 && p.attn_split != 1 && p.attn_split != 2 && p.attn_split != 4 && p.attn_split != 8)
     return fail(HTTM_ERR_INVALID_ARG, "attn_split must be 0, 1, 2, 4 or 8");
+  if (p.attn_fp8 != 0 && p.attn_fp8 != 1) return fail(HTTM_ERR_INVALID_ARG, "attn_fp8 must be 0 or 1");
+  if (p.attn_fp8 && p.dtype != HTTM_BF16) return fail(HTTM_ERR_UNSUPPORTED, "FP8 scores need a bf16 layer");
   const int64_t T = (int64_t)p.n_special + (int64_t)p.grid_h * p.grid_w;
   const int64_t N = (int64_t)p.frames * T;
   if ((int64_t)p.heads * N >= (1ll << 31) || (int64_t)p.heads * N * kD >= (1ll << 40))
@@ -402,6 +405,13 @@ httm_status build(const httm_params& p, httm_plan* pl) {
       Lw.lpart = b.take(4 * (size_t)pl->attn_part_rows);
       Lw.mpart = b.take(4 * (size_t)pl->attn_part_rows);
     }
+    if (p.attn_fp8) {
+      Lw.k8 = b.take(h * (size_t)pl->lk_pad * kD);
+      Lw.kpart = b.take(4 * h * (size_t)kKeyAmaxChunks);
+      Lw.kexp = b.take(4 * h);
+      Lw.q8 = b.take((size_t)pl->q_cap * kD);
+      Lw.qexp = b.take(4 * (size_t)pl->q_cap);
+    }
     Lw.index = b.take(pl->I.total);
     Lw.total = b.cur;
   }
@@ -558,6 +568,16 @@ httm_status attend_unmerge(const httm_plan* pl, void* ws, char* idx, const void*
   s.fb_list = at<int>(ws, pl->L.fb) + 1;
   s.lenk = pl->p.partition == 1 ? reinterpret_cast<const int32_t*>(idx + pl->I.lenk.off) : nullptr;
   const int32_t* lenq = reinterpret_cast<const int32_t*>(idx + pl->I.lenq.off);
+  if (pl->p.attn_fp8) {
+    s.k8 = at<uint8_t>(ws, pl->L.k8);
+    s.kexp = at<int32_t>(ws, pl->L.kexp);
+    s.q8 = at<uint8_t>(ws, pl->L.q8);
+    s.qexp = at<int32_t>(ws, pl->L.qexp);
+    stage_begin(HTTM_T_KEY_FP8, st);
+    CHECK_LAUNCH(launch_quantize_keys(g.heads, pl->lk_pad, at<void>(ws, pl->L.kt), at<float>(ws, pl->L.kpart),
+                                      at<uint8_t>(ws, pl->L.k8), at<int32_t>(ws, pl->L.kexp), st));
+    stage_end(HTTM_T_KEY_FP8, st);
+  }
   stage_begin(HTTM_T_ATTN, st);
   CHECK_LAUNCH(launch_attention(dt, s, qt, at<void>(ws, pl->L.kt), at<void>(ws, pl->L.vt), lenq,
                                 at<void>(ws, pl->L.o), st));
@@ -1063,7 +1083,7 @@ httm_status httm_attention_dense(const httm_plan* pl, void* ws, size_t ws_bytes,
   CHECK_LAUNCH(launch_zero_init(kmax, g.heads, fb, nullptr, 0, nullptr, 0, st));
   CHECK_LAUNCH(launch_prep_dense(dt, g.heads, g.N, pitch, pl->scale * kLog2e, k, v, kc, ws, kmax, st));
   stage_end(HTTM_T_MERGE_KV, st);
-  AttnShape a;
+  AttnShape a{};
   a.heads = g.heads;
   a.lk = g.N;
   a.k_rows = pitch;
@@ -1101,8 +1121,10 @@ httm_status httm_debug_size(const httm_plan* pl, int32_t item, size_t* bytes) {
   const bool block_item = item == HTTM_DBG_Q_MATCH || item == HTTM_DBG_Q_SCORE || item == HTTM_DBG_KV_MATCH ||
                           item == HTTM_DBG_KV_SCORE;
   const bool gm_item = item == HTTM_DBG_GM_METRIC || item == HTTM_DBG_GM_MATCH || item == HTTM_DBG_GM_SCORE;
+  const bool fp8_item = item == HTTM_DBG_K8 || item == HTTM_DBG_KEXP || item == HTTM_DBG_Q8 || item == HTTM_DBG_QEXP;
   if ((ga_item && !ga) || (block_item && (ga || gm)) || (gm_item && !gm))
     return fail(HTTM_ERR_UNSUPPORTED, "this debug item does not exist under the plan's partition");
+  if (fp8_item && !pl->p.attn_fp8) return fail(HTTM_ERR_UNSUPPORTED, "FP8 items need attn_fp8 = 1");
   switch (item) {
     case HTTM_DBG_GA_VAR:
     case HTTM_DBG_GA_MATCH:
@@ -1127,6 +1149,10 @@ httm_status httm_debug_size(const httm_plan* pl, int32_t item, size_t* bytes) {
     case HTTM_DBG_GM_METRIC: *bytes = E * n * kD; break;
     case HTTM_DBG_GM_MATCH:
     case HTTM_DBG_GM_SCORE: *bytes = 4 * n; break;
+    case HTTM_DBG_K8: *bytes = h * (size_t)pl->lk_pad * kD; break;
+    case HTTM_DBG_KEXP: *bytes = 4 * h; break;
+    case HTTM_DBG_Q8: *bytes = (size_t)pl->q_cap * kD; break;
+    case HTTM_DBG_QEXP: *bytes = 4 * (size_t)pl->q_cap; break;
     default: return fail(HTTM_ERR_INVALID_ARG, "unknown debug item");
   }
   return HTTM_OK;
@@ -1169,6 +1195,10 @@ httm_status httm_debug_read(const httm_plan* pl, const void* ws, const httm_inde
     case HTTM_DBG_GM_METRIC: src = base + L.gm_metric.off; break;
     case HTTM_DBG_GM_MATCH: src = base + L.gm_dbg_match.off; break;
     case HTTM_DBG_GM_SCORE: src = base + L.gm_dbg_score.off; break;
+    case HTTM_DBG_K8: src = base + L.k8.off; break;
+    case HTTM_DBG_KEXP: src = base + L.kexp.off; break;
+    case HTTM_DBG_Q8: src = base + L.q8.off; break;
+    case HTTM_DBG_QEXP: src = base + L.qexp.off; break;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   CHECK_LAUNCH(hipMemcpyAsync(host, src, need, hipMemcpyDeviceToHost, st));

@@ -41,143 +41,11 @@
 // key range.  An XCD whose S-split workgroups would end in a partly filled
 // round gives its last (tiles mod tiles-per-round) tiles 2S shorter splits:
 // the final round then holds half-length workgroups.
-#include <atomic>
-
-#include "common.h"
-#include "kernels.h"
+#include "attn_common.h"
 
 namespace httm {
 
 namespace {
-
-constexpr int kKeyTile = 64;
-constexpr int kRowsF32 = 128;  // fp32 kernel: one thread per query row
-constexpr int kQT = 4;         // 16-row query tiles per wave
-constexpr int kNW = 4;         // waves per workgroup
-constexpr int kRows = kQT * kNW * 16;
-constexpr float kTinySum = 8.673617379884035e-19f;  // 2^-60
-
-struct AttnArgs {
-  const void* q;
-  const void* k;
-  const void* vt;
-  void* o;                 // normalized output rows (split == 1)
-  float* opart;            // [split][q_capacity][64] partial numerators (split > 1)
-  float* lpart;            // [split][q_capacity] partial row sums
-  float* mpart;            // [split][q_capacity] reference of each partial
-  const float* kmax;       // [heads] max |k~|
-  const int32_t* lenk;     // [heads] keys per head when they vary (nullable: lk)
-  int* fb_count;           // queued units for the exact kernel
-  int* fb_list;
-  const int32_t* lenq;
-  int heads, lk, k_rows, vt_pitch, lq_uniform;
-  int split;
-  int tail_split;          // splits of an XCD's tail tiles (== split: no tail)
-  int per_round;           // query tiles per full round of one XCD (split-S workgroups)
-  int64_t q_capacity;
-  int64_t tail_rows;       // partial rows reserved for splits >= split of tail tiles
-  int total_wg;
-};
-
-// 16 bytes per lane from global memory straight into LDS: lane i of the wave
-// writes lds_wave_base + 16*i (the base must be the same for the whole wave).
-__device__ __forceinline__ void lds_copy16(const void* g, u32x4* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
-}
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// LDS tiles are rows of 128 bytes (eight 16-byte chunks); chunk c of row r is
-// stored at chunk c ^ swz(r).  The LDS serves 16 lanes of a 16-byte read per
-// cycle (64 four-byte banks).  V~^T is read by 16 consecutive rows: swzV
-// gives rows of equal parity distinct chunks.  K~ is read by the permuted
-// rows 8(i/4) + 4p + i%4 of a 32-key chunk: swzK does the same for them.
-__device__ __forceinline__ int swzV(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int swzK(int row) { return ((row >> 1) & 1) | ((row >> 2) & 6); }
-
-// Sums over lanes {l, l^32} and {l, l^16} with VALU lane swaps.
-__device__ __forceinline__ float sum_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float sum_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float max_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-struct Unit {
-  int head, cu, L, tile, split;
-  int nsplit;  // key splits of this query tile
-  int tord;    // slot among the tail tiles (-1: regular tile)
-};
-
-// Tail tiles per XCD at most (partial rows are reserved for this many).
-constexpr int kMaxTailTiles = 16;
-
-// The XCD share of U query tiles: tiles [u0, u0 + n), the first nr regular
-// (split splits), the rest tail tiles (tail_split splits).
-struct XcdShare {
-  int u0, n, nr;
-};
-__device__ __forceinline__ XcdShare xcd_share(const AttnArgs& a, int U, int x) {
-  XcdShare r;
-  r.u0 = (int)((int64_t)x * U / 8);
-  r.n = (int)((int64_t)(x + 1) * U / 8) - r.u0;
-  const int t = a.per_round > 0 ? r.n % a.per_round : 0;
-  r.nr = r.n - t;
-  return r;
-}
-
-// Workgroup id -> unit (see Schedule above); false for workgroups past the
-// work.  Every lane of the wave takes part (wave-wide scans over the heads).
-__device__ __forceinline__ bool schedule(const AttnArgs& a, int bid, Unit& o) {
-  const HeadPrefix hp = head_prefix(a.lenq, a.lq_uniform, a.heads, kRows);
-  const int U = hp.tiles_total;
-  const int x = bid & 7, j = bid >> 3;
-  const XcdShare sh = xcd_share(a, U, x);
-  int ug;
-  if (j < a.split * sh.nr) {
-    o.split = j / sh.nr;
-    ug = sh.u0 + j % sh.nr;
-    o.nsplit = a.split;
-    o.tord = -1;
-  } else {
-    const int t = sh.n - sh.nr, jt = j - a.split * sh.nr;
-    if (jt >= a.tail_split * t) return false;
-    o.split = jt / t;
-    o.tord = x * kMaxTailTiles + jt % t;
-    ug = sh.u0 + sh.nr + jt % t;
-    o.nsplit = a.tail_split;
-  }
-  // the head holding tile ug: heads whose tiles all lie below ug come first
-  const int lane = threadIdx.x & 63;
-  const int h = __popcll(__ballot(lane < a.heads && hp.tiles_upto <= ug));
-  o.head = h;
-  o.L = __shfl(hp.len, h);
-  o.cu = __shfl(hp.rows_before, h);
-  o.tile = ug - __shfl(hp.tiles_before, h);
-  return true;
-}
-
-// Row of the partial buffers for split s of packed row `row` (tile-relative
-// row r) of a unit: splits below `split` are [split][q_capacity]; the extra
-// splits of tail tiles follow as [tail_split - split][tail_rows].
-__device__ __forceinline__ size_t part_row(const AttnArgs& a, int s, size_t row, int tord, int r) {
-  if (s < a.split) return (size_t)s * a.q_capacity + row;
-  return (size_t)a.split * a.q_capacity + (size_t)(s - a.split) * a.tail_rows + (size_t)tord * kRows + r;
-}
 
 // Unit u -> (head, first packed row of the head, head length, query tile,
 // key split); units of one head are ordered split-major so that concurrent
@@ -429,34 +297,13 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, const u32x4* sKb, c
   psum_half(ones, bp, 1, osum);
 }
 
-// Write one unit's rows: normalized bf16 (split == 1) or fp32 partials.
+// Write one unit's rows (reference -negm per query tile).
 __device__ __forceinline__ void store_unit(const AttnArgs& a, const Unit& u, const UnitCtx& c, int g,
                                            f32x4 (*oacc)[4], const float* lsum, const f32x4* negm) {
+  float mref[kQT];
 #pragma unroll
-  for (int qt = 0; qt < kQT; ++qt) {
-    if (!c.valid(qt)) continue;
-    const size_t row = (size_t)u.cu + c.qrow0 + qt * 16;
-    if (a.split == 1) {
-      const float inv = 1.0f / lsum[qt];
-      uint16_t* Op = reinterpret_cast<uint16_t*>(a.o) + row * kD;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        u32x2 w2;
-        w2[0] = (uint32_t)f2bf(oacc[qt][dt][0] * inv) | ((uint32_t)f2bf(oacc[qt][dt][1] * inv) << 16);
-        w2[1] = (uint32_t)f2bf(oacc[qt][dt][2] * inv) | ((uint32_t)f2bf(oacc[qt][dt][3] * inv) << 16);
-        *reinterpret_cast<u32x2*>(Op + dt * 16 + 4 * g) = w2;
-      }
-    } else {
-      const size_t prow = part_row(a, u.split, row, u.tord, c.qrow0 - u.tile * kRows + qt * 16);
-      float* Op = a.opart + prow * kD;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(Op + dt * 16 + 4 * g) = oacc[qt][dt];
-      if (g == 0) {
-        a.lpart[prow] = lsum[qt];
-        a.mpart[prow] = -negm[qt][0];  // the unit's softmax reference
-      }
-    }
-  }
+  for (int qt = 0; qt < kQT; ++qt) mref[qt] = -negm[qt][0];
+  store_rows(a, u, c.qrow0, c.L, g, oacc, lsum, mref);
 }
 
 // Fast path: the Cauchy-Schwarz reference, no running max.
@@ -778,7 +625,7 @@ int attention_split(int64_t q_capacity, int heads) {
 
 AttnTail attention_tail(int split) {
   // host-only: capacities use the bound of kMaxTailTiles tail tiles per XCD;
-  // the device's tiles per round is read at launch (attention_per_round)
+  // the device's tiles per round is read at launch (per_round_for)
   AttnTail t{split, 0, 0};
   if (split <= 1 || 2 * split > kMaxSplit) return t;
   t.tail_split = 2 * split;
@@ -786,37 +633,6 @@ AttnTail attention_tail(int split) {
   return t;
 }
 
-namespace {
-// Query tiles per full round of one XCD for `split` key splits on the current
-// device (resident workgroups of the fast kernel / 8 XCDs / split), queried
-// once per device; 0 disables tail splitting (query failed, or more tail
-// tiles than reserved).
-int attention_per_round(int split) {
-  constexpr int kDevs = 64;
-  static std::atomic<int> slots[kDevs];  // resident workgroups per XCD + 1 (0: not known yet)
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  int v = slots[dev].load(std::memory_order_relaxed);
-  if (v == 0) {
-    int occ = 0, cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, attn_fast, kNW * 64, 0) != hipSuccess || occ <= 0 ||
-        cus <= 0 || cus % 8) {
-      (void)hipGetLastError();
-      occ = 0;
-      cus = 0;
-    }
-    v = occ * cus / 8 + 1;
-    slots[dev].store(v, std::memory_order_relaxed);
-  }
-  const int slots_xcd = v - 1;
-  if (slots_xcd <= 0 || slots_xcd % split || slots_xcd / split - 1 > kMaxTailTiles) return 0;
-  return slots_xcd / split;
-}
-}  // namespace
 
 int64_t attention_workgroups(int dtype, const AttnShape& s) {
   if (dtype != 1) return (s.q_capacity + kRowsF32 - 1) / kRowsF32 + s.heads;
@@ -836,48 +652,11 @@ int64_t attention_partial_rows(const AttnShape& s) {
   return (int64_t)s.split * s.q_capacity + (int64_t)(s.tail_split > s.split ? s.tail_split - s.split : 0) * s.tail_rows;
 }
 
-namespace {
-AttnArgs make_args(int dtype, const AttnShape& s, const void* q, const void* k, const void* vt,
-                   const int32_t* lenq, void* o) {
-  AttnArgs a{};
-  a.q = q;
-  a.k = k;
-  a.vt = vt;
-  a.o = o;
-  a.opart = s.opart;
-  a.lpart = s.lpart;
-  a.mpart = s.mpart;
-  a.kmax = s.kmax;
-  a.fb_count = s.fb_count;
-  a.fb_list = s.fb_list;
-  a.lenq = lenq;
-  a.heads = s.heads;
-  a.lk = s.lk;
-  a.lenk = s.lenk;
-  a.k_rows = s.k_rows;
-  a.vt_pitch = s.vt_pitch;
-  a.lq_uniform = s.lq_uniform;
-  a.split = dtype == 1 ? s.split : 1;
-  const int per_round = dtype == 1 && a.split > 1 && s.tail_split > a.split && s.tail_rows > 0
-                            ? (s.per_round > 0 ? s.per_round : attention_per_round(a.split))
-                            : 0;
-  const bool tail = per_round > 0 && per_round - 1 <= kMaxTailTiles;
-  a.tail_split = tail ? s.tail_split : a.split;
-  a.per_round = tail ? per_round : 0;
-  a.tail_rows = tail ? s.tail_rows : 0;
-  a.q_capacity = s.q_capacity;
-  AttnShape sh = s;
-  sh.split = a.split;
-  sh.tail_split = a.tail_split;
-  sh.per_round = a.per_round;
-  a.total_wg = (int)attention_workgroups(dtype, sh);
-  return a;
-}
-}  // namespace
 
 hipError_t launch_attention(int dtype, const AttnShape& s, const void* q, const void* k,
                             const void* vt, const int32_t* lenq, void* o, hipStream_t stream) {
-  const AttnArgs a = make_args(dtype, s, q, k, vt, lenq, o);
+  if (dtype == 1 && s.k8) return launch_attention_fp8(s, q, vt, lenq, o, stream);
+  const AttnArgs a = make_attn_args(dtype, s, q, k, vt, lenq, o, per_round_for<attn_fast>);
   if (dtype == 1) {
     hipLaunchKernelGGL(attn_fast, dim3(a.total_wg), dim3(kNW * 64), 0, stream, a);
   } else {
@@ -889,10 +668,17 @@ hipError_t launch_attention(int dtype, const AttnShape& s, const void* q, const 
 hipError_t launch_attention_tail(int dtype, const AttnShape& s, const void* q, const void* k,
                                  const void* vt, const int32_t* lenq, void* o, hipStream_t stream) {
   if (dtype != 1) return hipSuccess;
-  const AttnArgs a = make_args(dtype, s, q, k, vt, lenq, o);
-  hipLaunchKernelGGL(attn_exact, dim3(a.total_wg < kExactGrid ? a.total_wg : kExactGrid), dim3(kNW * 64), 0,
-                     stream, a);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  AttnArgs a{};
+  if (s.k8) {
+    e = launch_attention_fp8_exact(s, q, vt, lenq, o, stream);
+    a = make_attn_args(dtype, s, q, k, vt, lenq, o, attention_fp8_per_round);
+  } else {
+    a = make_attn_args(dtype, s, q, k, vt, lenq, o, per_round_for<attn_fast>);
+    hipLaunchKernelGGL(attn_exact, dim3(a.total_wg < kExactGrid ? a.total_wg : kExactGrid), dim3(kNW * 64), 0,
+                       stream, a);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess || a.split == 1) return e;
   const int fgrid = (int)((s.q_capacity + 31) / 32);
   hipLaunchKernelGGL(attn_finalize, dim3(fgrid), dim3(256), 0, stream, a);

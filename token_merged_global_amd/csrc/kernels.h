@@ -92,6 +92,11 @@ struct AttnShape {
   const int32_t* lenk;     // [heads] keys per head when they vary (nullable: lk for every head)
   int* fb_count;           // [1] units queued for the exact kernel (zeroed by launch_zero_init)
   int* fb_list;            // [units]
+  // FP8 scores (bf16 layers): non-null k8 selects them
+  const uint8_t* k8 = nullptr;    // [heads][k_rows][64] e4m3 keys (launch_quantize_keys)
+  const int32_t* kexp = nullptr;  // [heads] their scale exponents
+  uint8_t* q8 = nullptr;          // [q_capacity][64] e4m3 queries as the kernel quantised them (nullable)
+  int32_t* qexp = nullptr;        // [q_capacity] their exponents (nullable)
 };
 // Geometry-aware three-class partition (variance map, roles, global match)
 // of both streams, producing per head the same CSR groups as the block-local
@@ -239,6 +244,21 @@ hipError_t launch_attention(int dtype, const AttnShape& s, const void* q, const 
                             const void* vt, const int32_t* lenq, void* o, hipStream_t stream);
 hipError_t launch_attention_tail(int dtype, const AttnShape& s, const void* q, const void* k,
                                  const void* vt, const int32_t* lenq, void* o, hipStream_t stream);
+
+// FP8 (OCP e4m3) scores.  Keys: a power-of-two scale per head puts the
+// head's largest |K~| in [128, 256); partial maxima first (kpart: [heads]
+// [kKeyAmaxChunks]), then every element of kt [heads][k_rows][64] (bf16)
+// rounded to nearest-even e4m3 into k8, and kexp[h] the exponent.
+constexpr int kKeyAmaxChunks = 64;
+hipError_t launch_quantize_keys(int heads, int k_rows, const void* kt, float* kpart, uint8_t* k8,
+                                int32_t* kexp, hipStream_t stream);
+// The FP8 main and exact attention kernels (called by launch_attention /
+// launch_attention_tail when s.k8 is set).
+int attention_fp8_per_round(int split);
+hipError_t launch_attention_fp8(const AttnShape& s, const void* q, const void* vt, const int32_t* lenq, void* o,
+                                hipStream_t stream);
+hipError_t launch_attention_fp8_exact(const AttnShape& s, const void* q, const void* vt, const int32_t* lenq,
+                                      void* o, hipStream_t stream);
 
 // out[h][n] = o[slot[h][n]]
 hipError_t launch_unmerge(int dtype, int heads, int N, const int32_t* slot, const void* o,
