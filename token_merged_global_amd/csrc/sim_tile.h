@@ -11,10 +11,12 @@ namespace {
 // rows one A-operand read touches land in distinct bank groups.
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-// max(a, max(b, c)) on unsigned values lowers to one v_max3_u32.
+// max(a, b, c) on unsigned values as one v_max3_u32 (written out: from the
+// plain form the compiler emitted two v_max_u32 for a quarter of the trees).
 __device__ __forceinline__ uint32_t umax3(uint32_t a, uint32_t b, uint32_t c) {
-  const uint32_t m = b > c ? b : c;
-  return a > m ? a : m;
+  uint32_t r;
+  asm("v_max3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 // acc + sum of squares of 8 bf16 values, two per v_dot2.
