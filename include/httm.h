@@ -48,8 +48,9 @@
  *     the caller's stream and is joined back into it with events before the
  *     attention, so the caller sees one ordered stream.
  *     Enqueueing is serialised by an internal lock.
- *   - Sizes: validation requires heads * N < 2^31, n_s * n_t <= 4096 and
- *     heads <= 64 (HTTM_ERR_UNSUPPORTED otherwise).
+ *   - Sizes: validation requires heads * N < 2^31, N < 2^24 (32-bit offsets
+ *     into a head's merged keys), n_s * n_t <= 4096 and heads <= 64
+ *     (HTTM_ERR_UNSUPPORTED otherwise).
  */
 #ifndef HTTM_H_
 #define HTTM_H_

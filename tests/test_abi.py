@@ -134,6 +134,9 @@ def test_validation_codes():
     assert _status(n_s=128, n_t=33) == 2  # block larger than 4096
     assert _status(heads=64) == 0
     assert _status(heads=65) == 2  # per-head prefix tables are sized for 64
+    # one head of 2^24 tokens: 32-bit offsets into a head's merged keys
+    assert _status(heads=1, frames=4096, grid_h=64, grid_w=64, n_special=0, n_s=64, n_t=1) == 2
+    assert _status(heads=1, frames=4095, grid_h=64, grid_w=64, n_special=0, n_s=64, n_t=1) == 0
     assert _status(softmax_scale=float("inf")) == 1
     for split in (0, 1, 2, 4, 8):
         assert _status(attn_split=split) == 0

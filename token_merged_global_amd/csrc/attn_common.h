@@ -52,6 +52,25 @@ struct AttnArgs {
 __device__ __forceinline__ void lds_copy16(const void* g, u32x4* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
+// The same through a buffer resource: a fixed per-lane byte offset voff and
+// a wave-uniform soff (scalar register), so that advancing to the next tile
+// costs no vector instruction.  Reads past the resource's `bytes` return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+// A pointer every lane holds, as a wave-uniform (scalar) value.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void lds_copy16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                               u32x4* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff,
+                                           soff, 0, 0);
+}
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // LDS tiles are rows of 128 bytes (eight 16-byte chunks); chunk c of row r is
@@ -136,6 +155,15 @@ __device__ __forceinline__ bool schedule(const AttnArgs& a, int bid, Unit& o) {
   o.L = __shfl(hp.len, h);
   o.cu = __shfl(hp.rows_before, h);
   o.tile = ug - __shfl(hp.tiles_before, h);
+  // every lane computed the same unit: keep it in scalar registers (buffer
+  // resources and tile offsets built from it must be wave-uniform)
+  o.head = __builtin_amdgcn_readfirstlane(o.head);
+  o.cu = __builtin_amdgcn_readfirstlane(o.cu);
+  o.L = __builtin_amdgcn_readfirstlane(o.L);
+  o.tile = __builtin_amdgcn_readfirstlane(o.tile);
+  o.split = __builtin_amdgcn_readfirstlane(o.split);
+  o.nsplit = __builtin_amdgcn_readfirstlane(o.nsplit);
+  o.tord = __builtin_amdgcn_readfirstlane(o.tord);
   return true;
 }
 

@@ -175,6 +175,8 @@ httm_status build(const httm_params& p, httm_plan* pl) {
   const int64_t N = (int64_t)p.frames * T;
   if ((int64_t)p.heads * N >= (1ll << 31) || (int64_t)p.heads * N * kD >= (1ll << 40))
     return fail(HTTM_ERR_INVALID_ARG, "heads * N must be < 2^31");
+  if (N >= (1ll << 24))
+    return fail(HTTM_ERR_UNSUPPORTED, "N must be < 2^24 (a head's merged keys are addressed with 32-bit offsets)");
 
   pl->p = p;
   Geo& g = pl->g;

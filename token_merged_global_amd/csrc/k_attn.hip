@@ -75,6 +75,7 @@ __device__ __forceinline__ bool locate(const AttnArgs& a, int u, int rows, Unit&
 struct UnitCtx {
   const uint16_t* Kp;
   const uint16_t* Vp;
+  uint32_t kbytes, vbytes;  // sizes of the head's K~ rows and V~^T rows (buffer bounds)
   int t0, t1, ntiles_all, lk;  // key tiles of this unit, of the head; keys of the head
   uint32_t koff[8 / kNW], voff[8 / kNW];  // per-lane byte offsets of the tile copies
   bf16x8 bq[kQT][2];
@@ -85,12 +86,14 @@ struct UnitCtx {
 __device__ __forceinline__ void unit_setup(const AttnArgs& a, const Unit& u, int wave, int g, int l16, UnitCtx& c,
                                            float* qnorm2) {
   const uint16_t* Qp = reinterpret_cast<const uint16_t*>(a.q);
-  c.Kp = reinterpret_cast<const uint16_t*>(a.k) + (size_t)u.head * a.k_rows * kD;
-  c.Vp = reinterpret_cast<const uint16_t*>(a.vt) + (size_t)u.head * kD * a.vt_pitch;
-  c.lk = a.lenk ? a.lenk[u.head] : a.lk;
+  c.Kp = uniform_ptr(reinterpret_cast<const uint16_t*>(a.k) + (size_t)u.head * a.k_rows * kD);
+  c.Vp = uniform_ptr(reinterpret_cast<const uint16_t*>(a.vt) + (size_t)u.head * kD * a.vt_pitch);
+  c.kbytes = (uint32_t)a.k_rows * (kD * 2);
+  c.vbytes = (uint32_t)kD * a.vt_pitch * 2;
+  c.lk = __builtin_amdgcn_readfirstlane(a.lenk ? a.lenk[u.head] : a.lk);
   c.ntiles_all = ceil_div(c.lk, kKeyTile);
-  // the copy of key tile t reads base(t) + these lane offsets: every key
-  // buffer holds whole 64-key tiles (zero past lk), so no clamp is needed
+  // the copy of key tile t reads tile offset(t) + these lane offsets: every
+  // key buffer holds whole 64-key tiles (zero past lk), so no clamp is needed
 #pragma unroll
   for (int rd = 0; rd < 8 / kNW; ++rd) {
     const int p = (rd * kNW + wave) * 64 + (threadIdx.x & 63);
@@ -98,8 +101,8 @@ __device__ __forceinline__ void unit_setup(const AttnArgs& a, const Unit& u, int
     c.koff[rd] = (uint32_t)(row * kD + (pc ^ swzK(row)) * 8) * 2u;
     c.voff[rd] = (uint32_t)(row * a.vt_pitch + (pc ^ swzV(row)) * 8) * 2u;
   }
-  c.t0 = (int)((int64_t)u.split * c.ntiles_all / u.nsplit);
-  c.t1 = (int)((int64_t)(u.split + 1) * c.ntiles_all / u.nsplit);
+  c.t0 = __builtin_amdgcn_readfirstlane((int)((int64_t)u.split * c.ntiles_all / u.nsplit));
+  c.t1 = __builtin_amdgcn_readfirstlane((int)((int64_t)(u.split + 1) * c.ntiles_all / u.nsplit));
   c.qrow0 = u.tile * kRows + wave * kQT * 16 + l16;
   c.L = u.L;
 #pragma unroll
@@ -126,13 +129,13 @@ __device__ __forceinline__ void unit_setup(const AttnArgs& a, const Unit& u, int
 // issues 8/kNW + 8/kNW copies of 64 x 16 bytes; lane i fetches the global
 // chunk that belongs at its swizzled LDS slot (offsets fixed per lane).
 __device__ __forceinline__ void load_tile(const UnitCtx& c, u32x4* sKb, u32x4* sVb, int t, int wave) {
-  const char* kb = reinterpret_cast<const char*>(c.Kp) + (size_t)t * (kKeyTile * kD * 2);
-  const char* vb = reinterpret_cast<const char*>(c.Vp) + (size_t)t * (kKeyTile * 2);
+  const uint32_t ks = (uint32_t)t * (kKeyTile * kD * 2), vs = (uint32_t)t * (kKeyTile * 2);
+  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(c.Kp, c.kbytes), rv = buffer_rsrc(c.Vp, c.vbytes);
 #pragma unroll
   for (int rd = 0; rd < 8 / kNW; ++rd) {
     const int slot = (rd * kNW + wave) * 64;
-    lds_copy16(kb + c.koff[rd], sKb + slot);
-    lds_copy16(vb + c.voff[rd], sVb + slot);
+    lds_copy16_buf(rk, c.koff[rd], ks, sKb + slot);
+    lds_copy16_buf(rv, c.voff[rd], vs, sVb + slot);
   }
 }
 
@@ -315,7 +318,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void attn_fast(AttnArgs a) {
   const int w = blockIdx.x;
   Unit u;
   if (!schedule(a, w, u)) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, l16 = lane & 15;
   UnitCtx c;
   float qn2[kQT];
@@ -401,7 +404,7 @@ __device__ __forceinline__ void exact_unit(const AttnArgs& a, int w, u32x4 (*sK)
                                            u32x4 (*sV)[kD * 8]) {
   Unit u;
   if (!schedule(a, w, u)) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, l16 = lane & 15;
   UnitCtx c;
   float qn2[kQT];

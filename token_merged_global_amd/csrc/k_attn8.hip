@@ -64,6 +64,7 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 struct Ctx8 {
   const uint8_t* K8;
   const uint16_t* Vp;
+  uint32_t kbytes, vbytes;  // sizes of the head's e4m3 key rows and V~^T rows (buffer bounds)
   int t0, t1, ntiles_all, lk;
   uint32_t koff, voff[2];  // per-lane byte offsets of the tile copies
   i32x8 bq[2];             // fp8 query operands of the wave's two 32-query blocks
@@ -79,9 +80,11 @@ struct Ctx8 {
 // and exponents (a.q8 / a.qexp) for inspection.
 __device__ __forceinline__ void setup8(const AttnArgs& a, const Unit& u, int wave, int lane, Ctx8& c) {
   const uint16_t* Qp = reinterpret_cast<const uint16_t*>(a.q);
-  c.K8 = a.k8 + (size_t)u.head * a.k_rows * kD;
-  c.Vp = reinterpret_cast<const uint16_t*>(a.vt) + (size_t)u.head * kD * a.vt_pitch;
-  c.lk = a.lenk ? a.lenk[u.head] : a.lk;
+  c.K8 = uniform_ptr(a.k8 + (size_t)u.head * a.k_rows * kD);
+  c.Vp = uniform_ptr(reinterpret_cast<const uint16_t*>(a.vt) + (size_t)u.head * kD * a.vt_pitch);
+  c.kbytes = (uint32_t)a.k_rows * kD;
+  c.vbytes = (uint32_t)kD * a.vt_pitch * 2;
+  c.lk = __builtin_amdgcn_readfirstlane(a.lenk ? a.lenk[u.head] : a.lk);
   c.ntiles_all = ceil_div(c.lk, kKeyTile);
   {
     // key tile: 256 slots of 16 bytes, one per lane of the workgroup
@@ -95,8 +98,8 @@ __device__ __forceinline__ void setup8(const AttnArgs& a, const Unit& u, int wav
     const int row = p >> 3, pc = p & 7;
     c.voff[rd] = (uint32_t)(row * a.vt_pitch + (pc ^ swzV(row)) * 8) * 2u;
   }
-  c.t0 = (int)((int64_t)u.split * c.ntiles_all / u.nsplit);
-  c.t1 = (int)((int64_t)(u.split + 1) * c.ntiles_all / u.nsplit);
+  c.t0 = __builtin_amdgcn_readfirstlane((int)((int64_t)u.split * c.ntiles_all / u.nsplit));
+  c.t1 = __builtin_amdgcn_readfirstlane((int)((int64_t)(u.split + 1) * c.ntiles_all / u.nsplit));
   c.qrow0 = u.tile * kRows + wave * kQT * 16 + (lane & 15);
   c.L = u.L;
   c.ks = 127 - a.kexp[u.head];
@@ -146,11 +149,11 @@ __device__ __forceinline__ void setup8(const AttnArgs& a, const Unit& u, int wav
 }
 
 __device__ __forceinline__ void load_tile8(const Ctx8& c, u32x4* sKb, u32x4* sVb, int t, int wave) {
-  const char* kb = reinterpret_cast<const char*>(c.K8) + (size_t)t * (kKeyTile * kD);
-  const char* vb = reinterpret_cast<const char*>(c.Vp) + (size_t)t * (kKeyTile * 2);
-  lds_copy16(kb + c.koff, sKb + wave * 64);
+  const uint32_t ks = (uint32_t)t * (kKeyTile * kD), vs = (uint32_t)t * (kKeyTile * 2);
+  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(c.K8, c.kbytes), rv = buffer_rsrc(c.Vp, c.vbytes);
+  lds_copy16_buf(rk, c.koff, ks, sKb + wave * 64);
 #pragma unroll
-  for (int rd = 0; rd < 8 / kNW; ++rd) lds_copy16(vb + c.voff[rd], sVb + (rd * kNW + wave) * 64);
+  for (int rd = 0; rd < 8 / kNW; ++rd) lds_copy16_buf(rv, c.voff[rd], vs, sVb + (rd * kNW + wave) * 64);
 }
 
 // Scores of key block kb for both query blocks: s[qb] = S^T - m (lane l:
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void attn_fast8(AttnArgs a) {
   const int w = blockIdx.x;
   Unit u;
   if (!schedule(a, w, u)) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, l16 = lane & 15;
   Ctx8 c;
   setup8(a, u, wave, lane, c);
@@ -335,7 +338,7 @@ __device__ __forceinline__ void exact_unit8(const AttnArgs& a, int w, u32x4 (*sK
                                             u32x4 (*sV)[kD * 8]) {
   Unit u;
   if (!schedule(a, w, u)) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, h = lane >> 5, g = lane >> 4, l16 = lane & 15;
   Ctx8 c;
   setup8(a, u, wave, lane, c);

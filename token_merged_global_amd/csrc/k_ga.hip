@@ -473,8 +473,15 @@ __global__ __launch_bounds__(256) void ga_gather(const uint16_t* __restrict__ q,
   if (part == 0) dinv[(size_t)sh * dpitch + d] = d < nd ? __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f)) : 0.f;
 }
 
-__device__ __forceinline__ void ga_lds_copy16(const void* g, u32x4* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+// 16 bytes per lane straight into LDS (lane i -> lds_wave_base + 16 i) from a
+// buffer resource of `bytes` bytes at p: fixed per-lane offset voff,
+// wave-uniform offset soff (no vector instruction per tile).
+__device__ __forceinline__ void ga_lds_copy16_buf(const void* p, uint32_t bytes, uint32_t voff, uint32_t soff,
+                                                  u32x4* lds_wave_base) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                                                     0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff,
+                                           soff, 0, 0);
 }
 __device__ __forceinline__ void ga_wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -496,7 +503,7 @@ __global__ __launch_bounds__(256) void ga_match_bf16(GaMatchArgs a) {
   const int32_t* SL = a.src_list + hb;
   const char* Dg = reinterpret_cast<const char*>(a.dg + (size_t)sh * a.dpitch * kD);
   const char* Di = reinterpret_cast<const char*>(a.dinv + (size_t)sh * a.dpitch);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lg = lane >> 4, l16 = lane & 15;
   // direct-to-LDS tile copies: the lane at LDS chunk slot p (row p / 8,
   // stored chunk p % 8) fetches logical chunk (p % 8) ^ swz(row) of that row
@@ -506,12 +513,13 @@ __global__ __launch_bounds__(256) void ga_match_bf16(GaMatchArgs a) {
     const int p = rd * 256 + wave * 64 + lane, row = p >> 3;
     goff[rd] = (uint32_t)(row * kD * 2 + (((p & 7) ^ swz(row)) * 16));
   }
+  const uint32_t dbytes = (uint32_t)a.dpitch * kD * 2, ibytes = (uint32_t)a.dpitch * 4;
   auto load_tile = [&](int t, u32x4* sDb, float* sIb) {
-    const char* base = Dg + (size_t)t * kDstTile * kD * 2;
+    const uint32_t ts = (uint32_t)t * kDstTile * kD * 2;
 #pragma unroll
-    for (int rd = 0; rd < 2; ++rd) ga_lds_copy16(base + goff[rd], sDb + rd * 256 + wave * 64);
+    for (int rd = 0; rd < 2; ++rd) ga_lds_copy16_buf(Dg, dbytes, goff[rd], ts, sDb + rd * 256 + wave * 64);
     if (wave == 0 && lane < kDstTile / 4)
-      ga_lds_copy16(Di + ((size_t)t * kDstTile + lane * 4) * 4, reinterpret_cast<u32x4*>(sIb));
+      ga_lds_copy16_buf(Di, ibytes, (uint32_t)lane * 16, (uint32_t)t * kDstTile * 4, reinterpret_cast<u32x4*>(sIb));
   };
   load_tile(t0, sD0, sI0);
   bf16x8 bs[4][2];
