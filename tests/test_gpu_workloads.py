@@ -145,3 +145,25 @@ def test_vggt100_geometry_aware_layer():
     assert rep.delta_nonexact == 0
     kl = gpu["kv_len"]
     assert (kl <= plan.info["kv_len"]).all()
+
+
+@pytest.mark.timeout(900)
+def test_largest_head_at_the_offset_limit():
+    """One head of 4,095 frames x 64x64 patches (N = 16,773,120, just under the
+    2^24 limit) with no key merge: the head's K~ and V~^T span just under 2^31
+    bytes, the end of the attention kernels' 32-bit buffer offsets.  Index
+    stages on the whole head against the oracle, outputs on sampled rows."""
+    w = gen.WORKLOADS["vggt30"].with_(name="maxhead", cfg_id=12, heads=1, frames=4095, grid_h=64, grid_w=64,
+                                      n_special=0, n_s=128, n_t=30, kv_ratio=0.0)
+    assert w.n_tokens == 16773120
+    say(f"[maxhead] N={w.n_tokens}")
+    x = gen.layer_inputs(w)
+    plan, ws, dev, out, gpu, _ = run_layer(w, x)
+    assert plan.info["kv_len"] == w.n_tokens
+    del ws, dev
+    torch.cuda.empty_cache()
+    rows = np.unique(np.r_[sample_rows(w.n_tokens, 48, 5), np.arange(w.n_tokens - 64, w.n_tokens, 16)])
+    rep = staged.check_layer(x["q"], x["k"], x["v"], O.Params.from_workload(w), gpu, out, rows=rows,
+                             rel_tol=BF16_REL, workers=WORKERS)
+    say("  ", rep.as_dict())
+    assert rep.delta_nonexact == 0
