@@ -14,14 +14,14 @@ from gpu_util import say, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _small(partition):
-    w = gen.WORKLOADS["vggt30"].with_(name="small", cfg_id=7, frames=4, heads=3, n_t=2)
+def _small(partition, fp8=False):
+    w = gen.WORKLOADS["vggt30"].with_(name="small", cfg_id=7, frames=4, heads=3, n_t=2, attn_fp8=fp8)
     return w.with_(partition=1, protect_pct=10.0) if partition else w
 
 
-@pytest.mark.parametrize("partition", [0, 1])
-def test_graph_replays_match_eager(partition):
-    w = _small(partition)
+@pytest.mark.parametrize("partition,fp8", [(0, False), (1, False), (0, True)])
+def test_graph_replays_match_eager(partition, fp8):
+    w = _small(partition, fp8)
     x = gen.layer_inputs(w)
     x2 = gen.layer_inputs(w, seed=gen.DEFAULT_SEED + 9)
     plan = H.Plan.from_workload(w)
@@ -54,4 +54,4 @@ def test_graph_replays_match_eager(partition):
         # the program's own eager work between replays, on other buffers
         H.layer(plan, q2, k2, v2, ws=ws2, out=out2)
         torch.cuda.synchronize()
-    say(f"[graph partition {partition}] 4 replays equal to eager")
+    say(f"[graph partition {partition} fp8 {fp8}] 4 replays equal to eager")

@@ -39,6 +39,7 @@ def test_noalloc_matches_layer_two_calls_second_smaller():
     _pair(_small(6, 4, 3), gen.DEFAULT_SEED)       # 8,244 tokens x 4 heads
     _pair(_small(4, 2, 2), gen.DEFAULT_SEED + 1)   # then a smaller layer: 5,496 tokens x 2 heads
     _pair(gen.WORKLOADS["tiny"], gen.DEFAULT_SEED)  # and the fp32 layer
+    _pair(_small(4, 2, 2, attn_fp8=True), gen.DEFAULT_SEED)  # and FP8 scores
 
 
 def test_noalloc_refuses_a_layer_beyond_its_scratch():
