@@ -73,6 +73,16 @@ __device__ __forceinline__ void lds_copy16_buf(__amdgpu_buffer_rsrc_t r, uint32_
 }
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Two probabilities as one bf16 pair, each truncated to bf16 (its upper 16
+// bits), in one v_perm_b32 instead of a rounding v_cvt_pk_bf16_f32.  The row
+// sum adds the same truncated values, so the common part of their downward
+// bias cancels in the normalisation and what remains spreads like rounding
+// error (uniform over half an ulp either side).  Used by the FP8-score kernel,
+// where it is faster; in the bf16 kernel's schedule it measured slower.
+__device__ __forceinline__ uint32_t pack_bf16_trunc(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
 // LDS tiles are rows of 128 bytes (eight 16-byte chunks); chunk c of row r is
 // stored at chunk c ^ swz(r).  The LDS serves 16 lanes of a 16-byte read per
 // cycle (64 four-byte banks).  V~^T is read by 16 consecutive rows: swzV

@@ -187,13 +187,12 @@ __device__ __forceinline__ void mask8(int lk, int t, int kb, int h, f32x16* s) {
 __device__ __forceinline__ void probs8(const f32x16* s, bf16x8 (*bp)[2], int kb) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    bf16x8 lo, hi;
+    u32x4 x, y;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      lo[r] = (__bf16)__builtin_amdgcn_exp2f(s[qb][r]);
-      hi[r] = (__bf16)__builtin_amdgcn_exp2f(s[qb][8 + r]);
+    for (int d = 0; d < 4; ++d) {
+      x[d] = pack_bf16_trunc(__builtin_amdgcn_exp2f(s[qb][2 * d]), __builtin_amdgcn_exp2f(s[qb][2 * d + 1]));
+      y[d] = pack_bf16_trunc(__builtin_amdgcn_exp2f(s[qb][8 + 2 * d]), __builtin_amdgcn_exp2f(s[qb][9 + 2 * d]));
     }
-    u32x4 x = __builtin_bit_cast(u32x4, lo), y = __builtin_bit_cast(u32x4, hi);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const auto r = __builtin_amdgcn_permlane16_swap(x[d], y[d], false, false);
