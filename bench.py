@@ -446,6 +446,43 @@ def timed(torch, stream, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def measured_peaks(H, torch, stream, copy_mib: int = 1024):
+    """Peaks measured on this GPU, the counterparts of the published ones:
+    the MFMA micro-benchmark (httm_peak_mfma: 8 independent 16x16x32 bf16
+    MFMA chains per wave on every SIMD, ~50 ms per launch after warm-up so that the clock
+    settles under matrix load) and a plain device copy (read + write bytes)."""
+    grid, iters = 2048, 120000
+    buf = torch.empty(grid * H.PEAK_THREADS, dtype=torch.float32, device="cuda")
+    flop = H.peak_mfma(iters, grid, buf, stream=stream)
+    timed(torch, stream, lambda: H.peak_mfma(iters, grid, buf, stream=stream), 4)  # warm-up (~0.4 s)
+    ms = timed(torch, stream, lambda: H.peak_mfma(iters, grid, buf, stream=stream), 3)
+    n = copy_mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    with torch.cuda.stream(stream):
+        copy = lambda: b.copy_(a)
+        timed(torch, stream, copy, 20)
+        cms = timed(torch, stream, copy, 50)
+    del a, b, buf
+    return {"mfma_bf16": {"achieved": flop / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "launch_ms": ms,
+                          "flop_per_launch": flop,
+                          "kernel": f"httm_peak_mfma: {grid} x {H.PEAK_THREADS} lanes, {iters} x 8 independent "
+                                    "16x16x32 bf16 MFMAs per lane, no memory traffic"},
+            "hbm_copy": {"achieved": 2 * n / (cms * 1e-3) / 1e9, "unit": "GB/s", "launch_ms": cms,
+                         "kernel": f"device copy of {copy_mib} MiB (read + write bytes)"}}
+
+
+def with_measured(r, peaks):
+    """A roofline entry with its fraction of the measured peak of its bound."""
+    if not r or not peaks:
+        return r
+    if r["bound"] == "mfma" and r.get("unit") == "TFLOP/s" and r["peak"] == MFMA_BF16_PEAK_TFLOPS:
+        return {**r, "frac_measured_peak": r["achieved"] / peaks["mfma_bf16"]["achieved"]}
+    if r["bound"] == "hbm":
+        return {**r, "frac_measured_peak": r["achieved"] / peaks["hbm_copy"]["achieved"]}
+    return r
+
+
 def lengths(H, plan, ws, w, ga, index=None):
     """Per-head merged query lengths and key counts of the last full layer
     (read from the merge index when the layer filled one)."""
@@ -502,6 +539,8 @@ def main():
     ap.add_argument("--no-fp8", dest="fp8", action="store_false",
                     help="skip the FP8-score variant reported as extra keys")
     ap.add_argument("--attn-split", type=int, default=0, help="key splits of the attention (0: the library's)")
+    ap.add_argument("--no-peaks", dest="peaks", action="store_false",
+                    help="skip the measured MFMA and copy peaks (micro-benchmarks, ~1.5 s)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (HBM counter calibration)")
     ap.add_argument("--kv-ratio", type=float, default=None, help="override the workload's K/V merge ratio")
@@ -685,6 +724,20 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: {args.copy_calibration_mib} MiB device copy")
 
+    peaks = None
+    if args.peaks:
+        peaks = measured_peaks(H, torch, stream)
+        log(f"[bench] measured peaks: MFMA bf16 {peaks['mfma_bf16']['achieved']:.1f} TFLOP/s "
+            f"({peaks['mfma_bf16']['launch_ms']:.2f} ms per launch), device copy "
+            f"{peaks['hbm_copy']['achieved']:.1f} GB/s")
+        rooflines = {k: with_measured(r, peaks) for k, r in rooflines.items()}
+        roofline = with_measured(roofline, peaks)
+        other_roofline = with_measured(other_roofline, peaks)
+        if roofline and roofline.get("bound") == "mfma" and roofline.get("peak") == MFMA_BF16_PEAK_TFLOPS:
+            peaks["dominant_kernel_frac_of_measured"] = roofline["achieved"] / peaks["mfma_bf16"]["achieved"]
+            log(f"[bench]   {roofline.get('kernel', 'attention')}: {peaks['dominant_kernel_frac_of_measured']:.3f} "
+                f"of the measured MFMA peak")
+
     fp8 = None
     if args.fp8 and w.dtype == "bf16":
         H.layer(plan, *dev[0], ws=ws, out=out, index=idx, stream=stream)
@@ -737,6 +790,7 @@ def main():
                            "calls with every launch on one stream (kernels alone on the GPU); algorithmic bytes "
                            "count each element read or written once"),
         "cpu_baseline": cpu,
+        "measured_peaks": peaks,
         "stack": per_layer,
         "stages_ms": stages,
         "cached_stages_ms": cstages,

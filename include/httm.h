@@ -350,6 +350,19 @@ httm_status httm_get_timing(float* ms, int32_t n, int32_t* calls);
  * layer can fail part way; later calls run normally.  Not thread-safe. */
 httm_status httm_debug_fail_launch(int32_t n);
 
+/* Measured-peak micro-benchmark (not part of a layer): `grid` workgroups of
+ * 256 lanes, every lane `iters` x 8 independent v_mfma_f32_16x16x32_bf16 on
+ * operands whose elements are all bf16(a) and bf16(b), with no memory
+ * traffic in the loop, enqueued on `stream`.  `out` (device, caller-owned)
+ * receives grid * 256 floats, each 1024 * bf16(a) * bf16(b) * iters (exact
+ * while below 2^24).  *flop (nullable) = the launch's MFMA FLOP
+ * (grid * iters * 524,288).  Warm launches of tens of milliseconds measure
+ * the matrix rate the GPU sustains, against which kernel fractions are also
+ * reported.  iters in [1, 2^30], grid in [1, 2^20]; else
+ * HTTM_ERR_INVALID_ARG, with nothing enqueued. */
+httm_status httm_peak_mfma(int32_t iters, int32_t grid, float a, float b, float* out, void* stream,
+                           double* flop);
+
 const char* httm_status_string(httm_status s);
 /* Last error detail recorded on this thread (empty if none). */
 const char* httm_last_error(void);

@@ -331,6 +331,29 @@ def test_device_error_without_a_gpu():
     H.debug_fail_launch(0)
 
 
+def test_peak_mfma_validation():
+    """The micro-benchmark entry point refuses a NULL output and iteration or
+    grid counts out of range before anything is enqueued (no device needed)."""
+    L = H.lib()
+    fake = 0x10000
+    flop = ctypes.c_double(-1.0)
+    assert L.httm_peak_mfma(10, 4, 1.0, 1.0, None, None, ctypes.byref(flop)) == 1
+    assert L.httm_peak_mfma(0, 4, 1.0, 1.0, fake, None, ctypes.byref(flop)) == 1
+    assert L.httm_peak_mfma((1 << 30) + 1, 4, 1.0, 1.0, fake, None, ctypes.byref(flop)) == 1
+    assert L.httm_peak_mfma(10, 0, 1.0, 1.0, fake, None, ctypes.byref(flop)) == 1
+    assert L.httm_peak_mfma(10, (1 << 20) + 1, 1.0, 1.0, fake, None, ctypes.byref(flop)) == 1
+    assert flop.value == -1.0 and L.httm_last_error().decode()
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="checks the error path of a host without a GPU")
+def test_peak_mfma_without_a_gpu():
+    """Valid arguments on a host with no GPU: the launch is reported as a
+    device error, and the FLOP count follows from the arguments alone."""
+    flop = ctypes.c_double(0.0)
+    assert H.lib().httm_peak_mfma(3, 5, 1.0, 1.0, 0x10000, None, ctypes.byref(flop)) == 5
+    assert flop.value == 3 * 5 * 4 * 8 * (2 * 16 * 16 * 32)
+
+
 def test_index_import_refuses_bad_payloads():
     """An index assembled on the host: the size and the header are checked,
     then the payload (offsets rising from 0 to N, member ids below N, packed

@@ -106,6 +106,8 @@ EXPORTS = {
                             ctypes.c_void_p], ctypes.c_int),
     "httm_index_header": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t], ctypes.c_int),
     "httm_debug_fail_launch": ([ctypes.c_int32], ctypes.c_int),
+    "httm_peak_mfma": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+                        ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
     "httm_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "httm_last_error": ([], ctypes.c_char_p),
 }
@@ -308,6 +310,23 @@ def index_header(plan: Plan):
 def debug_fail_launch(n: int) -> None:
     """Test hook: the n-th checked launch from now on reports a device error (0: off)."""
     _check(lib().httm_debug_fail_launch(int(n)))
+
+
+PEAK_THREADS = 256  # lanes per workgroup of httm_peak_mfma
+
+
+def peak_mfma(iters: int, grid: int, out, a: float = 1.0, b: float = 1.0, stream=None) -> float:
+    """Enqueue the MFMA peak micro-benchmark (httm_peak_mfma) into ``out``
+    (contiguous cuda float32, at least grid * PEAK_THREADS elements); returns
+    the launch's MFMA FLOP."""
+    torch = _torch()
+    if not out.is_cuda or out.dtype != torch.float32 or not out.is_contiguous() or \
+            out.numel() < int(grid) * PEAK_THREADS:
+        raise ValueError(f"out must be a contiguous cuda float32 tensor of at least {int(grid) * PEAK_THREADS} elements")
+    flop = ctypes.c_double(0.0)
+    _check(lib().httm_peak_mfma(int(iters), int(grid), float(a), float(b), out.data_ptr(), _stream_ptr(stream),
+                                ctypes.byref(flop)))
+    return flop.value
 
 
 def index_export(plan: Plan, index: CachedIndex, stream=None):

@@ -30,6 +30,8 @@ PER_FILE = {"k_merge.hip": ["-ffp-contract=off"],
             "k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
             "k_attn8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
             "k_sim.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+            # without it the accumulators live in AGPRs and the loop copies them every iteration
+            "k_peak.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
             # variance map compared bit for bit; MFMA cosine tiles as in k_sim
             "k_ga.hip": ["-ffp-contract=off", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
             # head-shared metric: fp32 adds in head order and one division

@@ -269,4 +269,13 @@ hipError_t launch_unmerge(int dtype, int heads, int N, const int32_t* slot, cons
 hipError_t launch_prep_dense(int dtype, int heads, int N, int pitch, float kscale, const void* k,
                              const void* v, void* kc, void* vt, float* kmax, hipStream_t stream);
 
+
+// Measured-peak micro-benchmark: `grid` workgroups of peak_threads() lanes,
+// each lane `iters` x 8 independent 16x16x32 bf16 MFMAs on operands a and b
+// (every element of them); out[grid * peak_threads()] receives each lane's
+// accumulator sum, 1024 a b iters (exact in fp32 while it stays below 2^24).
+int peak_threads();
+double peak_flop_per_iter_wg();
+hipError_t launch_mfma_peak(int iters, int grid, float a, float b, float* out, hipStream_t stream);
+
 }  // namespace httm
