@@ -351,15 +351,20 @@ httm_status httm_get_timing(float* ms, int32_t n, int32_t* calls);
 httm_status httm_debug_fail_launch(int32_t n);
 
 /* Measured-peak micro-benchmark (not part of a layer): `grid` workgroups of
- * 256 lanes, every lane `iters` x 8 independent v_mfma_f32_16x16x32_bf16 on
- * operands whose elements are all bf16(a) and bf16(b), with no memory
- * traffic in the loop, enqueued on `stream`.  `out` (device, caller-owned)
- * receives grid * 256 floats, each 1024 * bf16(a) * bf16(b) * iters (exact
- * while below 2^24).  *flop (nullable) = the launch's MFMA FLOP
- * (grid * iters * 524,288).  Warm launches of tens of milliseconds measure
- * the matrix rate the GPU sustains, against which kernel fractions are also
- * reported.  iters in [1, 2^30], grid in [1, 2^20]; else
- * HTTM_ERR_INVALID_ARG, with nothing enqueued. */
+ * 256 lanes, every lane `iters` x 8 independent v_mfma_f32_16x16x32_bf16,
+ * with no memory traffic in the loop, enqueued on `stream`.  Operands: lane
+ * g (global id) holds 8 pairs (A_j, B_j) of 8 bf16 values; with
+ * h = hash(64 g + 8 j + e) (the xorshift-multiply hash in k_peak.hip),
+ * A_j[e] = bf16(a * ((h & 0xffff) - 32768) / 32768) and
+ * B_j[e] = bf16(b * ((h >> 16) - 32768) / 32768); in every group of 8
+ * iterations, step s accumulates A_j times B_((j + s) mod 8) into chain j
+ * (operands change from one MFMA to the next, as real data does).  `out`
+ * (device, caller-owned) receives grid * 256 floats, each lane's sum of its
+ * 8 chains' 4 accumulator elements.  *flop (nullable) = the launch's MFMA
+ * FLOP (grid * iters * 524,288).  Warm launches of tens of milliseconds
+ * measure the matrix rate the GPU sustains, against which kernel fractions
+ * are also reported.  iters a multiple of 8 in [8, 2^30], grid in
+ * [1, 2^20]; else HTTM_ERR_INVALID_ARG, with nothing enqueued. */
 httm_status httm_peak_mfma(int32_t iters, int32_t grid, float a, float b, float* out, void* stream,
                            double* flop);
 

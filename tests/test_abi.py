@@ -337,11 +337,12 @@ def test_peak_mfma_validation():
     L = H.lib()
     fake = 0x10000
     flop = ctypes.c_double(-1.0)
-    assert L.httm_peak_mfma(10, 4, 1.0, 1.0, None, None, ctypes.byref(flop)) == 1
+    assert L.httm_peak_mfma(16, 4, 1.0, 1.0, None, None, ctypes.byref(flop)) == 1
     assert L.httm_peak_mfma(0, 4, 1.0, 1.0, fake, None, ctypes.byref(flop)) == 1
+    assert L.httm_peak_mfma(12, 4, 1.0, 1.0, fake, None, ctypes.byref(flop)) == 1  # not a multiple of 8
     assert L.httm_peak_mfma((1 << 30) + 1, 4, 1.0, 1.0, fake, None, ctypes.byref(flop)) == 1
-    assert L.httm_peak_mfma(10, 0, 1.0, 1.0, fake, None, ctypes.byref(flop)) == 1
-    assert L.httm_peak_mfma(10, (1 << 20) + 1, 1.0, 1.0, fake, None, ctypes.byref(flop)) == 1
+    assert L.httm_peak_mfma(16, 0, 1.0, 1.0, fake, None, ctypes.byref(flop)) == 1
+    assert L.httm_peak_mfma(16, (1 << 20) + 1, 1.0, 1.0, fake, None, ctypes.byref(flop)) == 1
     assert flop.value == -1.0 and L.httm_last_error().decode()
 
 
@@ -350,8 +351,8 @@ def test_peak_mfma_without_a_gpu():
     """Valid arguments on a host with no GPU: the launch is reported as a
     device error, and the FLOP count follows from the arguments alone."""
     flop = ctypes.c_double(0.0)
-    assert H.lib().httm_peak_mfma(3, 5, 1.0, 1.0, 0x10000, None, ctypes.byref(flop)) == 5
-    assert flop.value == 3 * 5 * 4 * 8 * (2 * 16 * 16 * 32)
+    assert H.lib().httm_peak_mfma(24, 5, 1.0, 1.0, 0x10000, None, ctypes.byref(flop)) == 5
+    assert flop.value == 24 * 5 * 4 * 8 * (2 * 16 * 16 * 32)
 
 
 def test_index_import_refuses_bad_payloads():

@@ -946,7 +946,8 @@ httm_status httm_debug_fail_launch(int32_t n) {
 httm_status httm_peak_mfma(int32_t iters, int32_t grid, float a, float b, float* out, void* stream,
                            double* flop) {
   if (!out) return fail(HTTM_ERR_INVALID_ARG, "out is NULL");
-  if (iters < 1 || iters > (1 << 30)) return fail(HTTM_ERR_INVALID_ARG, "iters must be in [1, 2^30]");
+  if (iters < 8 || iters > (1 << 30) || iters % 8)
+    return fail(HTTM_ERR_INVALID_ARG, "iters must be a multiple of 8 in [8, 2^30]");
   if (grid < 1 || grid > (1 << 20)) return fail(HTTM_ERR_INVALID_ARG, "grid must be in [1, 2^20]");
   if (flop) *flop = peak_flop_per_iter_wg() * (double)grid * (double)iters;
   CHECK_LAUNCH(launch_mfma_peak(iters, grid, a, b, out, reinterpret_cast<hipStream_t>(stream)));

@@ -271,9 +271,9 @@ hipError_t launch_prep_dense(int dtype, int heads, int N, int pitch, float kscal
 
 
 // Measured-peak micro-benchmark: `grid` workgroups of peak_threads() lanes,
-// each lane `iters` x 8 independent 16x16x32 bf16 MFMAs on operands a and b
-// (every element of them); out[grid * peak_threads()] receives each lane's
-// accumulator sum, 1024 a b iters (exact in fp32 while it stays below 2^24).
+// each lane `iters` (a multiple of 8) x 8 independent 16x16x32 bf16 MFMAs on
+// pseudo-random operands scaled by a and b; out[grid * peak_threads()]
+// receives each lane's accumulator sum (layout in k_peak.hip).
 int peak_threads();
 double peak_flop_per_iter_wg();
 hipError_t launch_mfma_peak(int iters, int grid, float a, float b, float* out, hipStream_t stream);
