@@ -51,9 +51,14 @@ def test_bench_json_contract(partition):
         assert any(k.startswith("ga_match") for k in kernels) and any(k.startswith("attn") for k in kernels)
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    mp = d["measured_peaks"]
+    assert mp["mfma_bf16"]["achieved"] > 0 and mp["hbm_copy"]["achieved"] > 0
+    assert mp["mfma_bf16"]["flop_per_launch"] == 2048 * 120000 * 524288
     for key, r in d["rooflines"].items():
         assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], rel=1e-9), key
         assert r["bound"] in ("hbm", "mfma"), key
+        if r["bound"] == "hbm":
+            assert r["frac_measured_peak"] == pytest.approx(r["achieved"] / mp["hbm_copy"]["achieved"], rel=1e-9)
 
 
 def test_bench_cached_stack_contract():
