@@ -445,6 +445,32 @@ def test_edge_geometry_layers(case, dtype):
     assert rep.delta_nonexact == 0
 
 
+@pytest.mark.parametrize("variant", ["f32", "bf16", "fp8"])
+def test_degenerate_values(variant):
+    """Zero and extreme-magnitude tokens.  Head 0: every query and key is zero
+    (every cosine is 0, so ties alone decide matches and selection; every
+    deviation is 0; attention is uniform over the merged keys).  Head 1: keys
+    scaled by 2^-40 and queries by 2^40 (norms far from 1; with FP8 scores,
+    scale exponents far from 0).  Index stages and every output row against
+    the oracle."""
+    dtype = "f32" if variant == "f32" else "bf16"
+    w = gen.WORKLOADS["vggt30"].with_(name="degenerate", cfg_id=22, frames=4, heads=3, n_t=2, dtype=dtype,
+                                      attn_fp8=(variant == "fp8"))
+    x = gen.layer_inputs(w)
+    x["q"][0] = 0.0
+    x["k"][0] = 0.0
+    x["q"][1] *= np.float32(2.0 ** 40)
+    x["k"][1] *= np.float32(2.0 ** -40)
+    p = O.Params.from_workload(w)
+    _say(f"[degenerate] {variant} N={w.n_tokens}")
+    plan, ws, dev, out, gpu = run_layer(w, x)
+    assert np.isfinite(out).all()
+    tol = dict(rel_tol=BF16_REL) if dtype == "bf16" else dict(out_tol=F32_ABS)
+    rep = staged.check_layer(x["q"], x["k"], x["v"], p, gpu, out, **tol)
+    _say("  ", rep.as_dict())
+    assert rep.delta_nonexact == 0
+
+
 def test_serial_timing_mode_is_bit_identical():
     """With the serialized timing mode every launch of a layer (and a cached
     layer) goes to the caller's stream: the same kernels on the same data, so
