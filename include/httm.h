@@ -65,9 +65,10 @@ extern "C" {
 typedef enum {
   HTTM_OK = 0,
   HTTM_ERR_INVALID_ARG = 1,    /* out-of-range parameter or NULL pointer */
-  HTTM_ERR_UNSUPPORTED = 2,    /* d_head != 64, n_s * n_t > 4096, heads > 64; partition 1: more
-                                  than 4096 patches per frame or N >= 2^20; a debug item that the
-                                  plan's partition does not produce */
+  HTTM_ERR_UNSUPPORTED = 2,    /* d_head != 64, n_s * n_t > 4096, heads > 64, N >= 2^24,
+                                  attn_fp8 on an fp32 layer; partitions 1 and 2: N >= 2^20, and
+                                  for partition 1 more than 4096 patches per frame; a debug item
+                                  that the plan's partition (or attn_fp8 = 0) does not produce */
   HTTM_ERR_WORKSPACE = 3,      /* workspace or index buffer smaller than required */
   HTTM_ERR_INDEX_MISMATCH = 4, /* index made by another plan, or never filled */
   HTTM_ERR_DEVICE = 5          /* a HIP call or a kernel launch failed */
