@@ -417,6 +417,11 @@ EDGE_CASES = {
     "q0_kv90": dict(frames=4, grid_h=5, grid_w=5, n_special=1, n_s=25, n_t=4, q_ratio=0.0, kv_ratio=0.9),
     # many heads of a small layer
     "heads64": dict(heads=64, frames=2, grid_h=3, grid_w=3, n_special=1, n_s=9, n_t=2),
+    # the largest block with explicit stride 2 for keys (2048 destinations: more than the block-resident
+    # similarity holds in LDS, so that stream takes the per-chunk kernel) and the derived stride 4 for
+    # queries (1024 destinations: the most the block-resident kernel holds)
+    "block4096_strides_4_2": dict(heads=1, frames=2, grid_h=64, grid_w=64, n_special=1, n_s=4096, n_t=1,
+                                  q_ratio=0.5, kv_ratio=0.5, kv_dst_stride=2),
     # the largest block (4096 tokens: one 64 x 64 frame) and the largest stride (merge 95 %)
     "max_block": dict(heads=1, frames=2, grid_h=64, grid_w=64, n_special=1, n_s=4096, n_t=1, q_ratio=0.95,
                       kv_ratio=0.75),
