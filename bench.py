@@ -448,14 +448,20 @@ def timed(torch, stream, fn, reps):
 
 def measured_peaks(H, torch, stream, copy_mib: int = 1024):
     """Peaks measured on this GPU, the counterparts of the published ones:
-    the MFMA micro-benchmark (httm_peak_mfma: 8 independent 16x16x32 bf16
-    MFMA chains per wave on every SIMD, ~50 ms per launch after warm-up so that the clock
-    settles under matrix load) and a plain device copy (read + write bytes)."""
+    the MFMA micro-benchmarks (httm_peak_mfma: 8 independent 16x16x32 bf16
+    MFMA chains per wave on every SIMD; httm_peak_mfma_fp8: 4 scaled
+    32x32x64 e4m3 chains; operands changing every instruction, ~50 ms per
+    launch after warm-up so that the clock settles under matrix load) and a
+    plain device copy (read + write bytes)."""
     grid, iters = 2048, 120000
     buf = torch.empty(grid * H.PEAK_THREADS, dtype=torch.float32, device="cuda")
     flop = H.peak_mfma(iters, grid, buf, stream=stream)
     timed(torch, stream, lambda: H.peak_mfma(iters, grid, buf, stream=stream), 4)  # warm-up (~0.4 s)
     ms = timed(torch, stream, lambda: H.peak_mfma(iters, grid, buf, stream=stream), 3)
+    iters8 = 40000
+    flop8 = H.peak_mfma_fp8(iters8, grid, buf, stream=stream)
+    timed(torch, stream, lambda: H.peak_mfma_fp8(iters8, grid, buf, stream=stream), 4)
+    ms8 = timed(torch, stream, lambda: H.peak_mfma_fp8(iters8, grid, buf, stream=stream), 3)
     n = copy_mib << 20
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
@@ -468,6 +474,10 @@ def measured_peaks(H, torch, stream, copy_mib: int = 1024):
                           "flop_per_launch": flop,
                           "kernel": f"httm_peak_mfma: {grid} x {H.PEAK_THREADS} lanes, {iters} x 8 independent "
                                     "16x16x32 bf16 MFMAs per lane, no memory traffic"},
+            "mfma_fp8": {"achieved": flop8 / (ms8 * 1e-3) / 1e12, "unit": "TFLOP/s", "launch_ms": ms8,
+                         "flop_per_launch": flop8,
+                         "kernel": f"httm_peak_mfma_fp8: {grid} x {H.PEAK_THREADS} lanes, {iters8} x 4 independent "
+                                   "scaled 32x32x64 e4m3 MFMAs per lane, no memory traffic"},
             "hbm_copy": {"achieved": 2 * n / (cms * 1e-3) / 1e9, "unit": "GB/s", "launch_ms": cms,
                          "kernel": f"device copy of {copy_mib} MiB (read + write bytes)"}}
 
@@ -728,8 +738,8 @@ def main():
     if args.peaks:
         peaks = measured_peaks(H, torch, stream)
         log(f"[bench] measured peaks: MFMA bf16 {peaks['mfma_bf16']['achieved']:.1f} TFLOP/s "
-            f"({peaks['mfma_bf16']['launch_ms']:.2f} ms per launch), device copy "
-            f"{peaks['hbm_copy']['achieved']:.1f} GB/s")
+            f"({peaks['mfma_bf16']['launch_ms']:.2f} ms per launch), MFMA fp8 {peaks['mfma_fp8']['achieved']:.1f} "
+            f"TFLOP/s, device copy {peaks['hbm_copy']['achieved']:.1f} GB/s")
         rooflines = {k: with_measured(r, peaks) for k, r in rooflines.items()}
         roofline = with_measured(roofline, peaks)
         other_roofline = with_measured(other_roofline, peaks)
@@ -743,6 +753,11 @@ def main():
         H.layer(plan, *dev[0], ws=ws, out=out, index=idx, stream=stream)
         log("[bench] FP8-score variant of the same stack")
         fp8 = fp8_variant(H, torch, w, dev, n_cached, out, max(3, args.steps), stream)
+        if peaks:
+            # Q K^T at the measured fp8 rate and P V at the measured bf16 rate (equal FLOP)
+            mixed = 2.0 / (1.0 / peaks["mfma_fp8"]["achieved"] + 1.0 / peaks["mfma_bf16"]["achieved"])
+            fp8["attention"]["measured_peak"] = mixed
+            fp8["attention"]["frac_measured_peak"] = fp8["attention"]["achieved"] / mixed
         log(f"[bench]   fp8 {fp8['ms_per_step']:.4f} ms/step, {fp8['tokens_per_s']:.4g} tokens/s, attention "
             f"{fp8['attention']['avg_launch_ms']:.4f} ms ({fp8['attention']['achieved']:.1f} TFLOP/s, frac "
             f"{fp8['attention']['frac']:.3f} of the mixed peak), output vs bf16 rel RMS "

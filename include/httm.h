@@ -369,6 +369,17 @@ httm_status httm_debug_fail_launch(int32_t n);
 httm_status httm_peak_mfma(int32_t iters, int32_t grid, float a, float b, float* out, void* stream,
                            double* flop);
 
+/* The FP8 counterpart: every lane `iters` x 4 independent
+ * v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e4m3, unit E8M0 scales).  Lane g
+ * holds 4 pairs (A_j, B_j) of 32 bytes: dword w of A_j is
+ * hash(128 g + 16 j + w) and of B_j hash(128 g + 16 j + 8 + w), each byte
+ * with bit 6 cleared (no NaN codes); in every group of 4 iterations, step s
+ * accumulates A_j times B_((j + s) mod 4) into chain j.  `out` receives each
+ * lane's sum of its 4 chains' 16 accumulator elements.  *flop (nullable) =
+ * grid * iters * 524,288.  iters a multiple of 4 in [4, 2^30], grid in
+ * [1, 2^20]; else HTTM_ERR_INVALID_ARG, with nothing enqueued. */
+httm_status httm_peak_mfma_fp8(int32_t iters, int32_t grid, float* out, void* stream, double* flop);
+
 const char* httm_status_string(httm_status s);
 /* Last error detail recorded on this thread (empty if none). */
 const char* httm_last_error(void);

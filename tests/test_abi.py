@@ -344,6 +344,10 @@ def test_peak_mfma_validation():
     assert L.httm_peak_mfma(16, 0, 1.0, 1.0, fake, None, ctypes.byref(flop)) == 1
     assert L.httm_peak_mfma(16, (1 << 20) + 1, 1.0, 1.0, fake, None, ctypes.byref(flop)) == 1
     assert flop.value == -1.0 and L.httm_last_error().decode()
+    assert L.httm_peak_mfma_fp8(16, 4, None, None, ctypes.byref(flop)) == 1
+    assert L.httm_peak_mfma_fp8(6, 4, fake, None, ctypes.byref(flop)) == 1  # not a multiple of 4
+    assert L.httm_peak_mfma_fp8(16, 0, fake, None, ctypes.byref(flop)) == 1
+    assert flop.value == -1.0
 
 
 @pytest.mark.skipif(not _no_gpu(), reason="checks the error path of a host without a GPU")

@@ -54,6 +54,8 @@ def test_bench_json_contract(partition):
     mp = d["measured_peaks"]
     assert mp["mfma_bf16"]["achieved"] > 0 and mp["hbm_copy"]["achieved"] > 0
     assert mp["mfma_bf16"]["flop_per_launch"] == 2048 * 120000 * 524288
+    assert mp["mfma_fp8"]["achieved"] > 0
+    assert mp["mfma_fp8"]["flop_per_launch"] == 2048 * 40000 * 4 * 4 * (2 * 32 * 32 * 64)
     for key, r in d["rooflines"].items():
         assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], rel=1e-9), key
         assert r["bound"] in ("hbm", "mfma"), key

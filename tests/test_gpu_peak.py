@@ -71,3 +71,47 @@ def test_peak_mfma_refuses_a_short_buffer():
     out = torch.empty(255, dtype=torch.float32, device="cuda")
     with pytest.raises(ValueError):
         H.peak_mfma(16, 1, out)
+
+
+def _expected_fp8(grid, iters):
+    """Lane sums of the FP8 micro-benchmark: e4m3 operands in the 32x32x64 MFMA
+    lane layout (lane l, half h = l / 32: byte b < 16 is k = 16 h + b, byte
+    b >= 16 is k = 32 + 16 h + b - 16; A row / B column l % 32; C rows
+    8 (r / 4) + 4 h + r % 4 of column l % 32 in accumulator r)."""
+    import torch
+    n = grid * H.PEAK_THREADS
+    g = np.arange(n, dtype=np.uint64)
+    idx = g[:, None] * 128 + np.arange(64, dtype=np.uint64)[None, :]
+    words = (_hash(idx) & 0xBFBFBFBF).astype(np.uint32)  # [lane][16 j + w]: A_j words 0-7, B_j words 8-15
+    byts = words.view(np.uint8).reshape(n, 4, 2, 32)  # [lane][j][A or B][byte]
+    vals = torch.from_numpy(np.ascontiguousarray(byts)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    b = np.arange(32)
+    out = np.empty((n // 64, 64))
+    lanes = np.arange(64)
+    h = lanes // 32
+    kmap = np.where(b[None, :] < 16, 16 * h[:, None] + b[None, :], 32 + 16 * h[:, None] + b[None, :] - 16)  # [lane][byte]
+    for w in range(n // 64):
+        A = np.zeros((4, 32, 64))
+        Bm = np.zeros((4, 64, 32))
+        for l in range(64):
+            A[:, l % 32, kmap[l]] = vals[64 * w + l, :, 0, :]
+            Bm[:, kmap[l], l % 32] = vals[64 * w + l, :, 1, :]
+        C = (iters // 4) * np.einsum("jmk,kn->jmn", A, Bm.sum(axis=0))
+        r = np.arange(16)
+        rows = 8 * (r // 4)[None, :] + 4 * h[:, None] + (r % 4)[None, :]  # [lane][r]
+        out[w] = C[:, rows, (lanes % 32)[:, None]].sum(axis=(0, 2))
+    return out.reshape(n), (iters // 4) * 4 * 4 * 16 * 64 * 1.875 ** 2
+
+
+@pytest.mark.parametrize("iters,grid", [(4, 1), (64, 2)])
+def test_peak_mfma_fp8_values(iters, grid):
+    import torch
+    n = grid * H.PEAK_THREADS
+    out = torch.full((n + 512,), 7.0, dtype=torch.float32, device="cuda")
+    flop = H.peak_mfma_fp8(iters, grid, out)
+    torch.cuda.synchronize()
+    assert flop == grid * iters * 4 * 4 * (2 * 32 * 32 * 64)
+    want, bound = _expected_fp8(grid, iters)
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.abs(got[:n] - want).max() <= 1e-5 * bound, np.abs(got[:n] - want).max()
+    assert (got[n:] == 7.0).all()

@@ -108,6 +108,8 @@ EXPORTS = {
     "httm_debug_fail_launch": ([ctypes.c_int32], ctypes.c_int),
     "httm_peak_mfma": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
                         ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
+    "httm_peak_mfma_fp8": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                            ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
     "httm_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "httm_last_error": ([], ctypes.c_char_p),
 }
@@ -326,6 +328,17 @@ def peak_mfma(iters: int, grid: int, out, a: float = 1.0, b: float = 1.0, stream
     flop = ctypes.c_double(0.0)
     _check(lib().httm_peak_mfma(int(iters), int(grid), float(a), float(b), out.data_ptr(), _stream_ptr(stream),
                                 ctypes.byref(flop)))
+    return flop.value
+
+
+def peak_mfma_fp8(iters: int, grid: int, out, stream=None) -> float:
+    """Enqueue the FP8 MFMA peak micro-benchmark (httm_peak_mfma_fp8); returns the launch's FLOP."""
+    torch = _torch()
+    if not out.is_cuda or out.dtype != torch.float32 or not out.is_contiguous() or \
+            out.numel() < int(grid) * PEAK_THREADS:
+        raise ValueError(f"out must be a contiguous cuda float32 tensor of at least {int(grid) * PEAK_THREADS} elements")
+    flop = ctypes.c_double(0.0)
+    _check(lib().httm_peak_mfma_fp8(int(iters), int(grid), out.data_ptr(), _stream_ptr(stream), ctypes.byref(flop)))
     return flop.value
 
 

@@ -954,6 +954,16 @@ httm_status httm_peak_mfma(int32_t iters, int32_t grid, float a, float b, float*
   return HTTM_OK;
 }
 
+httm_status httm_peak_mfma_fp8(int32_t iters, int32_t grid, float* out, void* stream, double* flop) {
+  if (!out) return fail(HTTM_ERR_INVALID_ARG, "out is NULL");
+  if (iters < 4 || iters > (1 << 30) || iters % 4)
+    return fail(HTTM_ERR_INVALID_ARG, "iters must be a multiple of 4 in [4, 2^30]");
+  if (grid < 1 || grid > (1 << 20)) return fail(HTTM_ERR_INVALID_ARG, "grid must be in [1, 2^20]");
+  if (flop) *flop = peak_flop_per_iter_wg_fp8() * (double)grid * (double)iters;
+  CHECK_LAUNCH(launch_mfma_peak_fp8(iters, grid, out, reinterpret_cast<hipStream_t>(stream)));
+  return HTTM_OK;
+}
+
 httm_status httm_index_export(const httm_plan* pl, const httm_index* index, void* host, size_t bytes,
                               void* stream) {
   if (!pl || !index || !index->dev || !host) return fail(HTTM_ERR_INVALID_ARG, "NULL argument");

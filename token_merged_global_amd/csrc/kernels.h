@@ -277,5 +277,9 @@ hipError_t launch_prep_dense(int dtype, int heads, int N, int pitch, float kscal
 int peak_threads();
 double peak_flop_per_iter_wg();
 hipError_t launch_mfma_peak(int iters, int grid, float a, float b, float* out, hipStream_t stream);
+// The same for v_mfma_scale_f32_32x32x64_f8f6f4 on e4m3 operands (4 chains
+// per wave, `iters` a multiple of 4; layout in k_peak.hip).
+double peak_flop_per_iter_wg_fp8();
+hipError_t launch_mfma_peak_fp8(int iters, int grid, float* out, hipStream_t stream);
 
 }  // namespace httm
